@@ -1,0 +1,399 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` instance and raises
+AssertionError when the oracle disagrees with:
+
+* a library routine that computes the same definition (numpy's float16
+  conversion; torch fp64 ``rms_norm``, ``native_layer_norm``,
+  ``_fused_rms_norm`` and autograd),
+* central finite differences of the oracle's own forward functions,
+* closed forms for constant, zero and hand-derivable rows (including the
+  LayerNorm example of the meTile contract page),
+* invariants every row satisfies whatever its values.
+
+The functions are shared by ``test_oracle_pins.py`` (the real oracle must pass
+all of them) and ``test_oracle_mutants.py`` (each planted mistake must fail at
+least one of them).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    err = np.abs(a - b)
+    lim = atol + rtol * np.abs(b)
+    bad = ~(err <= lim)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {a.size} differ, max err "
+                           f"{float(np.nanmax(err)):.3e}")
+
+
+def _f64(a):
+    return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# binary16 codec versus numpy
+# ---------------------------------------------------------------------------
+
+def pin_codec_decode(o):
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = o.f16_to_f64(bits.view(np.float16))
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all(), "NaN patterns decode differently"
+    assert (got[~nan] == ref[~nan]).all(), "finite or infinite patterns decode differently"
+    assert (np.signbit(got[~nan]) == np.signbit(ref[~nan])).all(), "sign of zero differs"
+
+
+def _encode_probe_values():
+    finite = np.arange(65536, dtype=np.uint16).view(np.float16)
+    finite = finite[np.isfinite(finite)].astype(np.float64)
+    pos = np.unique(np.abs(finite))
+    mids = (pos[:-1] + pos[1:]) / 2.0               # exact ties between neighbours
+    up = np.nextafter(mids, np.inf)
+    down = np.nextafter(mids, -np.inf)
+    rng = np.random.default_rng(123)
+    rnd = np.exp2(rng.uniform(-30.0, 17.0, 200000)) * rng.choice([-1.0, 1.0], 200000)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 65504.0, 65519.99, 65520.0, 65536.0,
+                        1e6, -65520.0, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -26, 2.0 ** -14,
+                        2.0 ** -14 - 2.0 ** -25, 1e-30, -1e-30])
+    return np.concatenate([finite, mids, -mids, up, down, rnd, special])
+
+
+def pin_codec_encode(o):
+    v = _encode_probe_values()
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    got = o.f64_to_f16(v).view(np.uint16)
+    bad = ref != got
+    assert not bad.any(), (f"{int(bad.sum())} encodings differ from numpy, e.g. "
+                           f"{v[bad][:4]} -> {got[bad][:4]} vs {ref[bad][:4]}")
+    nan = o.f64_to_f16(np.array([np.nan]))
+    assert np.isnan(nan[0]), "NaN does not encode to NaN"
+
+
+# ---------------------------------------------------------------------------
+# torch fp64 library routines and autograd
+# ---------------------------------------------------------------------------
+
+_SHAPES = [(1, 1), (3, 2), (4, 7), (5, 64), (3, 257), (2, 1024)]
+
+
+def _torch_case(kind, N, D, seed):
+    d = workloads.random_case(kind, N, D, seed, x_loc=0.3 if kind == "ln" else 0.0)
+    t = {k: torch.tensor(_f64(v)) for k, v in d.items()}
+    return d, t
+
+
+def pin_torch_rmsnorm(o):
+    for i, (N, D) in enumerate(_SHAPES):
+        eps = [1e-5, 1e-6, 0.1][i % 3]
+        d, t = _torch_case("rms", N, D, 10 + i)
+        Y, rstd = o.rmsnorm_forward(d["X"], d["gamma"], eps)
+        x = t["X"].clone().requires_grad_(True)
+        g = t["gamma"].clone().requires_grad_(True)
+        ty = F.rms_norm(x, (D,), g, eps)
+        _, trstd = torch.ops.aten._fused_rms_norm(t["X"], [D], t["gamma"], eps)
+        _close(Y, ty.detach().numpy(), 1e-12, 1e-15, f"rms Y {N}x{D}")
+        _close(rstd, trstd.reshape(-1).numpy(), 1e-12, 0, f"rms rstd {N}x{D}")
+        (ty * t["dY"]).sum().backward()
+        dX, dg = o.rmsnorm_backward(d["X"], d["gamma"], d["dY"], eps)
+        _close(dX, x.grad.numpy(), 1e-10, 1e-12, f"rms dX {N}x{D}")
+        _close(dg, g.grad.numpy(), 1e-10, 1e-12, f"rms dgamma {N}x{D}")
+
+
+def pin_torch_layernorm(o):
+    for i, (N, D) in enumerate(_SHAPES):
+        eps = [1e-5, 1e-6, 0.1][i % 3]
+        d, t = _torch_case("ln", N, D, 20 + i)
+        Y, mean, rstd = o.layernorm_forward(d["X"], d["gamma"], d["beta"], eps)
+        ty, tmean, trstd = torch.native_layer_norm(t["X"], [D], t["gamma"], t["beta"], eps)
+        _close(Y, ty.numpy(), 1e-12, 1e-14, f"ln Y {N}x{D}")
+        _close(mean, tmean.reshape(-1).numpy(), 1e-12, 1e-15, f"ln mean {N}x{D}")
+        _close(rstd, trstd.reshape(-1).numpy(), 1e-12, 0, f"ln rstd {N}x{D}")
+        x = t["X"].clone().requires_grad_(True)
+        g = t["gamma"].clone().requires_grad_(True)
+        b = t["beta"].clone().requires_grad_(True)
+        (F.layer_norm(x, (D,), g, b, eps) * t["dY"]).sum().backward()
+        dX, dg, db = o.layernorm_backward(d["X"], d["gamma"], d["dY"], eps)
+        _close(dX, x.grad.numpy(), 1e-9, 1e-12, f"ln dX {N}x{D}")
+        _close(dg, g.grad.numpy(), 1e-10, 1e-12, f"ln dgamma {N}x{D}")
+        _close(db, b.grad.numpy(), 1e-12, 1e-14, f"ln dbeta {N}x{D}")
+
+
+def pin_torch_add_rmsnorm(o):
+    for i, (N, D) in enumerate(_SHAPES):
+        eps = [1e-5, 1e-6, 0.1][i % 3]
+        d, t = _torch_case("add", N, D, 30 + i)
+        S, H, Y, rstd = o.add_rmsnorm_forward(d["X"], d["R"], d["gamma"], eps)
+        x = t["X"].clone().requires_grad_(True)
+        r = t["R"].clone().requires_grad_(True)
+        g = t["gamma"].clone().requires_grad_(True)
+        s = x + r
+        ty = F.rms_norm(s, (D,), g, eps)
+        _close(S, s.detach().numpy(), 0, 0, f"add S {N}x{D}")
+        ref_h = (_f64(d["X"]) + _f64(d["R"])).astype(np.float16)
+        assert (H.view(np.uint16) == ref_h.view(np.uint16)).all(), f"add H {N}x{D}"
+        _close(Y, ty.detach().numpy(), 1e-12, 1e-15, f"add Y {N}x{D}")
+        _, trstd = torch.ops.aten._fused_rms_norm(s.detach(), [D], t["gamma"], eps)
+        _close(rstd, trstd.reshape(-1).numpy(), 1e-12, 0, f"add rstd {N}x{D}")
+        ((ty * t["dY"]).sum() + (s * t["dH"]).sum()).backward()
+        dX, dg = o.add_rmsnorm_backward(d["X"], d["R"], d["gamma"], d["dY"], d["dH"], eps)
+        _close(dX, x.grad.numpy(), 1e-10, 1e-12, f"add dX {N}x{D}")
+        _close(dX, r.grad.numpy(), 1e-10, 1e-12, f"add dR {N}x{D}")
+        _close(dg, g.grad.numpy(), 1e-10, 1e-12, f"add dgamma {N}x{D}")
+
+
+# ---------------------------------------------------------------------------
+# Central finite differences of the oracle's own forward (fp64 inputs)
+# ---------------------------------------------------------------------------
+
+def _fd(f, v, j):
+    h = 1e-6 * max(1.0, abs(v.flat[j]))
+    a = v.copy(); a.flat[j] += h
+    b = v.copy(); b.flat[j] -= h
+    return (f(a) - f(b)) / (2 * h)
+
+
+def _fd_check(name, f, v, grad):
+    for j in range(v.size):
+        num = _fd(f, v, j)
+        ana = grad.flat[j]
+        assert abs(num - ana) <= 1e-6 * max(1.0, abs(ana)), (
+            f"{name}[{j}]: finite difference {num:.9g} vs analytic {ana:.9g}")
+
+
+def pin_finite_differences(o):
+    rng = np.random.default_rng(5)
+    for N, D in [(1, 1), (2, 2), (3, 3), (2, 5), (1, 7), (2, 9)]:
+        eps = 1e-3
+        x = rng.standard_normal((N, D)) + 0.2
+        r = 2 * rng.standard_normal((N, D))
+        g = 1 + 0.3 * rng.standard_normal(D)
+        b = 0.3 * rng.standard_normal(D)
+        dy = rng.standard_normal((N, D))
+        dh = rng.standard_normal((N, D))
+
+        loss = lambda xx, gg: float((o.rmsnorm_forward(xx, gg, eps, f64=True)[0] * dy).sum())
+        dX, dg = o.rmsnorm_backward(x, g, dy, eps, f64=True)
+        _fd_check(f"rms dX {N}x{D}", lambda v: loss(v, g), x, dX)
+        _fd_check(f"rms dgamma {N}x{D}", lambda v: loss(x, v), g, dg)
+
+        lloss = lambda xx, gg, bb: float(
+            (o.layernorm_forward(xx, gg, bb, eps, f64=True)[0] * dy).sum())
+        dX, dg, db = o.layernorm_backward(x, g, dy, eps, f64=True)
+        _fd_check(f"ln dX {N}x{D}", lambda v: lloss(v, g, b), x, dX)
+        _fd_check(f"ln dgamma {N}x{D}", lambda v: lloss(x, v, b), g, dg)
+        _fd_check(f"ln dbeta {N}x{D}", lambda v: lloss(x, g, v), b, db)
+
+        def aloss(xx, rr, gg):
+            S, _, Y, _ = o.add_rmsnorm_forward(xx, rr, gg, eps, f64=True)
+            return float((Y * dy).sum() + (S * dh).sum())
+
+        dX, dg = o.add_rmsnorm_backward(x, r, g, dy, dh, eps, f64=True)
+        _fd_check(f"add dX {N}x{D}", lambda v: aloss(v, r, g), x, dX)
+        _fd_check(f"add dR {N}x{D}", lambda v: aloss(x, v, g), r, dX)
+        _fd_check(f"add dgamma {N}x{D}", lambda v: aloss(x, r, v), g, dg)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+def pin_constant_rows(o):
+    rng = np.random.default_rng(9)
+    for D in (1, 2, 7, 128, 257, 4096, 8192):
+        cs = np.array([0.0, 1.0, -1.0, 0.5, -3.25, 100.0, 2.0 ** -10], dtype=np.float16)
+        X = np.repeat(cs[:, None], D, axis=1)
+        gam = (1 + 0.1 * rng.standard_normal(D)).astype(np.float16)
+        bet = (0.1 * rng.standard_normal(D)).astype(np.float16)
+        dY = rng.standard_normal((len(cs), D)).astype(np.float16)
+        eps = 1e-5
+        c = _f64(cs)[:, None]
+        g64, b64, dy64 = _f64(gam)[None, :], _f64(bet)[None, :], _f64(dY)
+        # LayerNorm: the centred row is exactly zero, so y = beta exactly and
+        # rstd = 1/sqrt(eps); dX = (g - mean(g)) / sqrt(eps) since xhat = 0.
+        Y, mean, rstd = o.layernorm_forward(X, gam, bet, eps)
+        assert (Y == np.broadcast_to(b64, Y.shape)).all(), f"ln constant row y != beta, D={D}"
+        assert (mean == c[:, 0]).all(), f"ln constant row mean, D={D}"
+        _close(rstd, np.full(len(cs), 1 / np.sqrt(eps)), 1e-15, 0, f"ln const rstd D={D}")
+        dX, _, _ = o.layernorm_backward(X, gam, dY, eps)
+        gg = dy64 * g64
+        _close(dX, (gg - gg.mean(axis=1, keepdims=True)) / np.sqrt(eps), 1e-12, 1e-9,
+               f"ln const dX D={D}")
+        # RMSNorm: y = c * gamma / sqrt(c^2 + eps), which tends to sign(c) * gamma.
+        Y, rstd = o.rmsnorm_forward(X, gam, eps)
+        _close(Y, c * g64 / np.sqrt(c * c + eps), 1e-14, 1e-300, f"rms const Y D={D}")
+        big = np.abs(cs) >= 0.5
+        _close(Y[big], (np.sign(c) * g64 * np.ones_like(Y))[big], 1e-4, 0,
+               f"rms const sign*gamma D={D}")
+        # dX = rstd * (g - xhat^2 * mean(g)) with xhat = c * rstd for every column.
+        dX, _ = o.rmsnorm_backward(X, gam, dY, eps)
+        rs = 1 / np.sqrt(c * c + eps)
+        xh = c * rs
+        _close(dX, rs * (gg - xh * xh * gg.mean(axis=1, keepdims=True)), 1e-11, 1e-9,
+               f"rms const dX D={D}")
+
+
+def pin_zero_rows(o):
+    D = 33
+    X = np.zeros((2, D), dtype=np.float16)
+    rng = np.random.default_rng(3)
+    gam = (1 + 0.1 * rng.standard_normal(D)).astype(np.float16)
+    dY = rng.standard_normal((2, D)).astype(np.float16)
+    eps = 1e-6
+    Y, rstd = o.rmsnorm_forward(X, gam, eps)
+    assert (Y == 0).all()
+    _close(rstd, np.full(2, 1 / np.sqrt(eps)), 1e-15, 0, "zero-row rstd")
+    dX, dg = o.rmsnorm_backward(X, gam, dY, eps)
+    _close(dX, _f64(dY) * _f64(gam) / np.sqrt(eps), 1e-12, 0, "zero-row rms dX = g/sqrt(eps)")
+    assert (dg == 0).all(), "zero rows give zero dgamma"
+
+
+def pin_worked_example(o):
+    with open(os.path.join(GOLDEN, "layernorm_worked_example.json")) as f:
+        ex = json.load(f)
+    R, C, div, eps = ex["rows"], ex["cols"], ex["arange_divisor"], ex["epsilon"]
+    vals = (np.arange(R * C, dtype=np.float32).reshape(R, C) / np.float32(div)).astype(np.float64)
+    w = np.ones(C)
+    b = np.zeros(C)
+    dy = np.full((R, C), ex["cotangent_value"])
+    Y, mean, rstd = o.layernorm_forward(vals, w, b, eps, f64=True)
+    dX, dg, db = o.layernorm_backward(vals, w, dy, eps, f64=True)
+    assert list(Y.shape) == ex["asserted_shapes"]["output"]
+    assert list(dX.shape) == ex["asserted_shapes"]["source_gradient"]
+    assert list(dg.shape) == ex["asserted_shapes"]["weight_gradient"]
+    assert list(db.shape) == ex["asserted_shapes"]["bias_gradient"]
+    # Closed form from the decimal values (float32 storage perturbs them by
+    # about 1e-8 relative, hence the tolerances).
+    _close(mean, 0.7 * np.arange(R) + 0.3, 1e-7, 0, "example mean")
+    rs = 1 / np.sqrt(0.04 + eps)
+    _close(rstd, np.full(R, rs), 1e-6, 0, "example rstd")
+    yrow = (np.arange(C) - 3) * 0.1 * rs
+    _close(Y, np.broadcast_to(yrow, (R, C)), 0, 1e-6, "example y")
+    _close(dX, np.zeros((R, C)), 0, 1e-9, "example source gradient")
+    _close(db, np.full(C, 3.0), 0, 0, "example bias gradient")
+    _close(dg, 3 * yrow, 0, 3e-6, "example weight gradient")
+    # The same example at arange(21)/8, where every input is exact in fp16:
+    # mean = (7 i + 3) / 8, variance = 1/16 exactly.
+    v16 = (np.arange(R * C).reshape(R, C) / 8.0).astype(np.float16)
+    Y, mean, rstd = o.layernorm_forward(v16, np.ones(C, np.float16), np.zeros(C, np.float16), eps)
+    rs = 1 / np.sqrt(1 / 16 + eps)
+    _close(mean, (7 * np.arange(R) + 3) / 8, 0, 0, "example/8 mean")
+    _close(rstd, np.full(R, rs), 1e-15, 0, "example/8 rstd")
+    _close(Y, np.broadcast_to((np.arange(C) - 3) / 8 * rs, (R, C)), 1e-15, 1e-16, "example/8 y")
+    dX, dg, db = o.layernorm_backward(v16, np.ones(C, np.float16),
+                                      np.ones((R, C), np.float16), eps)
+    _close(dX, np.zeros((R, C)), 0, 1e-12, "example/8 dX")
+    _close(dg, 3 * (np.arange(C) - 3) / 8 * rs, 1e-14, 1e-15, "example/8 dgamma")
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+
+def pin_invariants(o):
+    for seed, (N, D) in enumerate([(6, 257), (4, 1024), (3, 4096), (8, 7)]):
+        eps = 1e-2 if D == 7 else 1e-5
+        d = workloads.random_case("ln", N, D, 40 + seed, x_loc=0.5)
+        X, gam, bet, dY = d["X"], d["gamma"], d["beta"], d["dY"]
+        ones = np.ones(D, np.float16)
+        zeros = np.zeros(D, np.float16)
+        # LayerNorm with unit weight and zero bias: rows of y sum to zero and
+        # mean(y^2) = var / (var + eps) = 1 - eps * rstd^2.
+        Y1, mean, rstd = o.layernorm_forward(X, ones, zeros, eps)
+        _close(Y1.sum(axis=1), np.zeros(N), 0, 1e-11 * D, "ln sum(xhat) = 0")
+        _close((Y1 * Y1).mean(axis=1), 1 - eps * rstd ** 2, 1e-12, 0, "ln mean(xhat^2)")
+        # Backward: sum(dX) = 0 and <dX, x - mean> = eps * rstd^2 * <dY, y - beta>.
+        Y, mean, rstd = o.layernorm_forward(X, gam, bet, eps)
+        dX, dg, db = o.layernorm_backward(X, gam, dY, eps)
+        scale = np.abs(dX).sum(axis=1)
+        _close(dX.sum(axis=1), np.zeros(N), 0, 1e-12 * scale.max(), "ln sum(dX) = 0")
+        lhs = (dX * (_f64(X) - mean[:, None])).sum(axis=1)
+        rhs = eps * rstd ** 2 * (_f64(dY) * (Y - _f64(bet)[None, :])).sum(axis=1)
+        _close(lhs, rhs, 1e-6, 1e-11 * scale.max(), "ln <dX, x - mean>")
+        _close(db, _f64(dY).sum(axis=0), 1e-13, 1e-13, "ln dbeta = column sums of dY")
+        # RMSNorm: mean(y^2) = 1 - eps * rstd^2 at unit weight, and
+        # <dX, x> = eps * rstd^2 * <dY, y>.
+        Y1, rstd = o.rmsnorm_forward(X, ones, eps)
+        _close((Y1 * Y1).mean(axis=1), 1 - eps * rstd ** 2, 1e-12, 0, "rms mean(xhat^2)")
+        Y, rstd = o.rmsnorm_forward(X, gam, eps)
+        dX, dg = o.rmsnorm_backward(X, gam, dY, eps)
+        scale = np.abs(dX * _f64(X)).sum(axis=1)
+        lhs = (dX * _f64(X)).sum(axis=1)
+        rhs = eps * rstd ** 2 * (_f64(dY) * Y).sum(axis=1)
+        _close(lhs, rhs, 1e-6, 1e-12 * scale.max(), "rms <dX, x>")
+        # dgamma is linear in dY (float64 inputs).
+        rng = np.random.default_rng(seed)
+        a = rng.standard_normal((N, D))
+        b = rng.standard_normal((N, D))
+        x64 = _f64(X); g64 = _f64(gam)
+        for fn in (lambda dy: o.rmsnorm_backward(x64, g64, dy, eps, f64=True)[1],
+                   lambda dy: o.layernorm_backward(x64, g64, dy, eps, f64=True)[1]):
+            _close(fn(a + 2 * b), fn(a) + 2 * fn(b), 1e-9, 1e-11, "dgamma linear in dY")
+
+
+def pin_scaling(o):
+    # RMSNorm(2x; 4 eps) = RMSNorm(x; eps) exactly (power-of-two scaling is
+    # exact in binary arithmetic) and rstd halves; the same for LayerNorm
+    # after a shift, up to rounding.
+    rng = np.random.default_rng(11)
+    D = 100
+    x = rng.standard_normal((4, D))
+    g = 1 + 0.1 * rng.standard_normal(D)
+    b = 0.1 * rng.standard_normal(D)
+    eps = 1e-4
+    Y1, r1 = o.rmsnorm_forward(x, g, eps, f64=True)
+    Y2, r2 = o.rmsnorm_forward(2 * x, g, 4 * eps, f64=True)
+    assert (Y1 == Y2).all() and (r2 == r1 / 2).all(), "rms not scale-equivariant (eps placement)"
+    Y1, m1, r1 = o.layernorm_forward(x, g, b, eps, f64=True)
+    Y2, m2, r2 = o.layernorm_forward(3 * x + 1.5, g, b, 9 * eps, f64=True)
+    _close(Y2, Y1, 1e-12, 1e-13, "ln affine invariance (eps placement)")
+    _close(m2, 3 * m1 + 1.5, 1e-14, 1e-14, "ln mean shift")
+    _close(r2, r1 / 3, 1e-12, 0, "ln rstd scale")
+
+
+def pin_fused_special_cases(o):
+    d = workloads.random_case("add", 5, 96, 77)
+    X, R, gam, dY, dH = d["X"], d["R"], d["gamma"], d["dY"], d["dH"]
+    eps = 1e-5
+    Z = np.zeros_like(X)
+    # R = 0: H = X, and the fused forward equals the plain RMSNorm forward.
+    S, H, Y, rstd = o.add_rmsnorm_forward(X, Z, gam, eps)
+    Yr, rr = o.rmsnorm_forward(X, gam, eps)
+    assert (H.view(np.uint16) == X.view(np.uint16)).all(), "H != X when R = 0"
+    assert (Y == Yr).all() and (rstd == rr).all(), "fused(R=0) != rmsnorm"
+    dXa, dga = o.add_rmsnorm_backward(X, Z, gam, dY, None, eps)
+    dXr, dgr = o.rmsnorm_backward(X, gam, dY, eps)
+    assert (dXa == dXr).all() and (dga == dgr).all(), "fused bwd(R=0, dH=0) != rmsnorm bwd"
+    # dY = 0: the gradient is exactly dH.
+    dX, dg = o.add_rmsnorm_backward(X, R, gam, Z, dH, eps)
+    assert (dX == _f64(dH)).all() and (dg == 0).all(), "dY = 0 must give dX = dH"
+    # A missing dH is a zero cotangent.
+    a, _ = o.add_rmsnorm_backward(X, R, gam, dY, None, eps)
+    b, _ = o.add_rmsnorm_backward(X, R, gam, dY, Z, eps)
+    assert (a == b).all(), "dH = None differs from dH = 0"
+    # The fused sum is the source: fused(X, R) == rmsnorm(fp64 sum) on f64 inputs.
+    S, H, Y, rstd = o.add_rmsnorm_forward(X, R, gam, eps)
+    Y2, r2 = o.rmsnorm_forward(_f64(X) + _f64(R), _f64(gam), eps, f64=True)
+    assert (Y == Y2).all() and (rstd == r2).all(), "fused forward is not rmsnorm of x + r"
+
+
+ALL_PINS = [
+    pin_codec_decode, pin_codec_encode, pin_torch_rmsnorm, pin_torch_layernorm,
+    pin_torch_add_rmsnorm, pin_finite_differences, pin_constant_rows, pin_zero_rows,
+    pin_worked_example, pin_invariants, pin_scaling, pin_fused_special_cases,
+]

@@ -1,0 +1,158 @@
+"""Seeded synthetic inputs for the row-wise normalization training pair.
+
+This module is shared by the tests, the benchmark and the smoke check. It
+holds the workload table (shapes, epsilon, value distributions) and the
+seeded generators, and nothing of the normalization arithmetic itself: both
+the CPU oracle and the HIP library receive the arrays it returns.
+
+Recipe (fixed, so that every run sees the same bits):
+
+* ``numpy.random.default_rng(seed)`` (PCG64); seed 0 unless a test says
+  otherwise.
+* Tensors are drawn in the order the workload lists them, as float64
+  ``standard_normal`` values, optionally in row chunks (the chunked stream
+  equals the whole-array stream; a CPU test checks this).
+* ``loc + scale * z`` is applied in float64, then the value is rounded
+  directly to fp16 (round to nearest, ties to even; numpy converts float64 to
+  float16 without passing through float32).
+* The Llama-shape RMSNorm workload marks 1 % of its 4096 channels as outliers:
+  41 channels drawn without replacement from ``default_rng(1)`` and sorted;
+  those X columns are multiplied by 20 before rounding.
+
+The pages publish no dataset for this path; these synthetic tensors stand in
+for activations and cotangents of the stated shapes and distributions.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+# Rows drawn per chunk when materialising large tensors (keeps the float64
+# temporary at 32 MiB for D = 8192).
+_CHUNK_ELEMS = 1 << 22
+
+
+@dataclass(frozen=True)
+class TensorSpec:
+    name: str
+    per_row: bool          # True: shape [N, D]; False: shape [D]
+    loc: float = 0.0
+    scale: float = 1.0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str              # "rms", "ln" or "add"
+    N: int
+    D: int
+    eps: float
+    tensors: Tuple[TensorSpec, ...]
+    outlier_frac: float = 0.0
+    outlier_gain: float = 1.0
+    outlier_seed: int = 1
+    note: str = ""
+
+    def outlier_channels(self) -> np.ndarray:
+        if self.outlier_frac <= 0.0:
+            return np.zeros(0, dtype=np.int64)
+        k = int(np.ceil(self.outlier_frac * self.D))
+        rng = np.random.default_rng(self.outlier_seed)
+        return np.sort(rng.choice(self.D, k, replace=False))
+
+
+def _spec(kind: str, x=(0.0, 1.0), dy=(0.0, 1.0), r=(0.0, 2.0), dh=(0.0, 0.01)):
+    """Tensor list in draw order for one kind of norm."""
+    X = TensorSpec("X", True, *x)
+    G = TensorSpec("gamma", False, 1.0, 0.1)
+    B = TensorSpec("beta", False, 0.0, 0.1)
+    DY = TensorSpec("dY", True, *dy)
+    if kind == "rms":
+        return (X, G, DY)
+    if kind == "ln":
+        return (X, G, B, DY)
+    if kind == "add":
+        return (X, TensorSpec("R", True, *r), G, DY, TensorSpec("dH", True, *dh))
+    raise ValueError(kind)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in (
+        Workload("rms_17x257", "rms", 17, 257, 1e-6, _spec("rms"),
+                 note="ragged width RMSNorm"),
+        Workload("ln_128x1024", "ln", 128, 1024, 1e-5, _spec("ln", x=(0.5, 1.0)),
+                 note="LayerNorm, offset mean"),
+        Workload("rms_16384x4096", "rms", 16384, 4096, 1e-5,
+                 _spec("rms", dy=(0.0, 0.01)), outlier_frac=0.01, outlier_gain=20.0,
+                 note="Llama-8B training shape (8 x 2048 tokens), 1 % outlier channels"),
+        Workload("add_rms_32768x8192", "add", 32768, 8192, 1e-5,
+                 _spec("add", dy=(0.0, 0.01), r=(0.0, 2.0), dh=(0.0, 0.01)),
+                 note="fused residual-add + RMSNorm, both cotangents"),
+        Workload("rms_1048576x128", "rms", 1048576, 128, 1e-6, _spec("rms"),
+                 note="per-head QK-norm, B=8 x H=32 x S=4096 rows of 128"),
+        Workload("ln_16384x4096", "ln", 16384, 4096, 1e-5, _spec("ln", x=(0.5, 1.0)),
+                 note="supplemental LayerNorm at the Llama shape, offset-mean distributions"),
+    )
+}
+
+# The workload the benchmark's headline line is measured on.
+HEADLINE = "rms_16384x4096"
+
+
+def _fill_rows(rng, out: np.ndarray, spec: TensorSpec, outliers: np.ndarray, gain: float):
+    n, d = out.shape
+    rows = max(1, _CHUNK_ELEMS // max(d, 1))
+    buf = np.empty((min(rows, n), d), dtype=np.float64)
+    for r0 in range(0, n, rows):
+        r1 = min(n, r0 + rows)
+        v = buf[: r1 - r0]
+        rng.standard_normal(out=v)
+        v *= spec.scale
+        v += spec.loc
+        if outliers.size:
+            v[:, outliers] *= gain
+        out[r0:r1] = v  # float64 -> float16 assignment rounds to nearest even
+
+
+def generate(w: Workload, seed: int = 0, N: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Materialise every input tensor of ``w`` as contiguous fp16 numpy arrays.
+
+    ``N`` overrides the row count (same distributions, same draw order), used
+    by tests that want a workload's statistics at a smaller size.
+    """
+    n = w.N if N is None else int(N)
+    rng = np.random.default_rng(seed)
+    outliers = w.outlier_channels()
+    out: Dict[str, np.ndarray] = {}
+    for spec in w.tensors:
+        if spec.per_row:
+            a = np.empty((n, w.D), dtype=np.float16)
+            _fill_rows(rng, a, spec, outliers if spec.name == "X" else np.zeros(0, np.int64),
+                       w.outlier_gain)
+        else:
+            a = (spec.loc + spec.scale * rng.standard_normal(w.D)).astype(np.float16)
+        out[spec.name] = a
+    return out
+
+
+def random_case(kind: str, N: int, D: int, seed: int, x_loc: float = 0.0, x_scale: float = 1.0,
+                dy_scale: float = 1.0, r_scale: float = 2.0, dh_scale: float = 0.5,
+                ) -> Dict[str, np.ndarray]:
+    """Inputs for an arbitrary (kind, N, D) test case with the default recipe."""
+    w = Workload(f"case_{kind}_{N}x{D}", kind, N, D, 1e-5,
+                 _spec(kind, x=(x_loc, x_scale), dy=(0.0, dy_scale), r=(0.0, r_scale),
+                       dh=(0.0, dh_scale)))
+    return generate(w, seed)
+
+
+def sample_rows(N: int, k: int, seed: int = 7) -> np.ndarray:
+    """Sorted sample of ``k`` distinct row indices that always contains the
+    first and last rows (ragged tails live there)."""
+    if k >= N:
+        return np.arange(N)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, N - 1), max(0, k - 2), replace=False)
+    return np.unique(np.concatenate([[0, N - 1], mid]))
