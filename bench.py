@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark: RMSNorm forward + backward at the Llama-8B training shape
+(16384 rows x 4096 columns, fp16 storage, fp32 arithmetic) on one MI355X.
+
+One step is one pass of the whole training pair over one batch: the forward
+(Y, rstd) of one batch and the backward (dX, dgamma, via the row kernel and
+the column reduce) of one batch. Inputs are resident in HBM before timing.
+Several buffer sets rotate so that no kernel reads data another kernel of
+the same step has just touched: step k runs the forward on set k mod S and
+the backward on set (k - 1) mod S (whose forward ran one step earlier),
+which keeps the Infinity Cache from serving re-reads.
+
+Printed: one JSON line with the whole-step throughput (algorithmic HBM bytes
+per second: every tensor read or written once, workspace excluded), rows/s,
+per-kernel device times from HIP events on the launch stream, the roofline of
+the dominant kernel, and the CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
+KERNEL_SRCS = [os.path.join(ROOT, "row_wise_normalization_amd", "csrc", f)
+               for f in ("mn_kernels.hpp", "mn_kernels.hip")]
+
+
+def alg_bytes(kind: str, N: int, D: int):
+    """Algorithmic bytes (each tensor read or written once) of the forward,
+    the backward row kernel and the column reduce."""
+    if kind == "rms":
+        fwd = 4 * N * D + 2 * D + 4 * N
+        bwd = 6 * N * D + 6 * D + 4 * N
+    elif kind == "ln":
+        fwd = 4 * N * D + 4 * D + 8 * N
+        bwd = 6 * N * D + 10 * D + 8 * N
+    else:
+        fwd = 8 * N * D + 2 * D + 4 * N
+        bwd = 10 * N * D + 6 * D + 4 * N
+    return fwd, bwd
+
+
+def kernel_hash() -> str:
+    """Hash of the kernel sources (templates and launch tables)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, d, budget_s: float):
+    """The oracle (single-threaded C, fp64) on this host: full forward and
+    backward passes over a bounded number of rows of the same workload."""
+    import oracle
+
+    fwd_b, bwd_b = alg_bytes(w.kind, w.N, w.D)
+    rows = w.N
+    X, g, dY = d["X"], d["gamma"], d["dY"]
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        if w.kind == "rms":
+            oracle.rmsnorm_forward(X, g, w.eps)
+            oracle.rmsnorm_backward(X, g, dY, w.eps)
+        elif w.kind == "ln":
+            oracle.layernorm_forward(X, g, d["beta"], w.eps)
+            oracle.layernorm_backward(X, g, dY, w.eps)
+        else:
+            oracle.add_rmsnorm_forward(X, d["R"], g, w.eps)
+            oracle.add_rmsnorm_backward(X, d["R"], g, dY, d["dH"], w.eps)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per = el / reps
+    return {
+        "value": round((fwd_b + bwd_b) / per / 1e9, 4),
+        "unit": "GB/s",
+        "rows_per_s": round(rows / per, 1),
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{reps} full forward+backward passes over all {w.N}x{w.D} rows "
+                  f"({el:.1f} s), single-threaded C fp64",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the CPU baseline (0: skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the normalization pair is "
+              "row-local and this build measures one GPU's share", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import row_wise_normalization_amd as mn
+
+    w = workloads.WORKLOADS[args.workload]
+    N, D, kind = w.N, w.D, w.kind
+    print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
+    d = workloads.generate(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    S = max(2, args.sets)
+    up = {k: torch.from_numpy(v).to(dev) for k, v in d.items()}
+    sets = []
+    for s in range(S):
+        b = {"X": up["X"] if s == 0 else up["X"].clone(),
+             "dY": up["dY"] if s == 0 else up["dY"].clone(),
+             "Y": torch.empty(N, D, dtype=torch.float16, device=dev),
+             "dX": torch.empty(N, D, dtype=torch.float16, device=dev),
+             "rstd": torch.empty(N, dtype=torch.float32, device=dev),
+             "dgamma": torch.empty(D, dtype=torch.float32, device=dev)}
+        if kind == "ln":
+            b["mean"] = torch.empty(N, dtype=torch.float32, device=dev)
+            b["dbeta"] = torch.empty(D, dtype=torch.float32, device=dev)
+        if kind == "add":
+            b["R"] = up["R"] if s == 0 else up["R"].clone()
+            b["dH"] = up["dH"] if s == 0 else up["dH"].clone()
+            b["H"] = torch.empty(N, D, dtype=torch.float16, device=dev)
+        b["ws"] = mn.new_workspace({"rms": 0, "ln": 1, "add": 2}[kind], N, D, dev)
+        sets.append(b)
+    gamma = up["gamma"]
+    beta = up.get("beta")
+    kcode = {"rms": mn.MN_RMSNORM, "ln": mn.MN_LAYERNORM, "add": mn.MN_ADD_RMSNORM}[kind]
+
+    def fwd(b):
+        if kind == "rms":
+            mn.mn_rmsnorm_forward(b["X"], gamma, b["Y"], b["rstd"], w.eps, stream)
+        elif kind == "ln":
+            mn.mn_layernorm_forward(b["X"], gamma, beta, b["Y"], b["mean"], b["rstd"], w.eps, stream)
+        else:
+            mn.mn_add_rmsnorm_forward(b["X"], b["R"], gamma, b["H"], b["Y"], b["rstd"], w.eps, stream)
+
+    def bwd_rows(b):
+        if kind == "rms":
+            mn.mn_rmsnorm_backward_rows(b["X"], gamma, b["rstd"], b["dY"], b["dX"], b["ws"], stream)
+        elif kind == "ln":
+            mn.mn_layernorm_backward_rows(b["X"], gamma, b["mean"], b["rstd"], b["dY"], b["dX"],
+                                          b["ws"], stream)
+        else:
+            mn.mn_add_rmsnorm_backward_rows(b["X"], b["R"], gamma, b["rstd"], b["dY"], b["dH"],
+                                            b["dX"], b["ws"], stream)
+
+    def reduce(b):
+        mn.mn_norm_reduce_partials(kcode, N, D, b["ws"], b["dgamma"], b.get("dbeta"), stream)
+
+    K, W = args.steps, args.warmup
+    fwd_b, bwd_b = alg_bytes(kind, N, D)
+    # The dominant kernel (most algorithmic bytes per launch) is the backward
+    # row kernel; the timed loop brackets only it with events, so that the
+    # step wall time carries two event records per step.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+
+    def step(k, rows_events=None):
+        f = sets[k % S]
+        bk = sets[(k - 1) % S]
+        fwd(f)
+        if rows_events: rows_events[0].record(stream)
+        bwd_rows(bk)
+        if rows_events: rows_events[1].record(stream)
+        reduce(bk)
+
+    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    for b in sets:
+        fwd(b)
+    for k in range(W):
+        step(k)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(W + k, ev[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    rows_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # Diagnostic pass (not the timed region): every kernel bracketed.
+    dg = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for k in range(K):
+        f = sets[k % S]
+        bk = sets[(k - 1) % S]
+        dg[k][0].record(stream); fwd(f); dg[k][1].record(stream); bwd_rows(bk)
+        dg[k][2].record(stream); reduce(bk); dg[k][3].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in dg]))
+    red_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in dg]))
+
+    step_bytes = fwd_b + bwd_b
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    kernels = {
+        "forward": {"avg_ms": fwd_ms, "bytes": fwd_b},
+        "backward_rows": {"avg_ms": rows_ms, "bytes": bwd_b},
+        "reduce_partials": {"avg_ms": red_ms, "bytes": None},
+    }
+    dom = "backward_rows"
+    achieved = bwd_b / (rows_ms * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm",
+        "kernel": dom,
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(w.name, dom),
+    }
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print(f"[bench] cpu baseline (oracle, {args.cpu_budget:.0f} s budget)", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(w, d, args.cpu_budget)
+
+    line = {
+        "metric": "achieved HBM GB/s (% of peak) + rows/s for norm fwd+bwd, RMSNorm 16384x4096",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "N": N, "D": D, "eps": w.eps, "io_dtype": "f16",
+            "norm": {"rms": "RMSNorm", "ln": "LayerNorm", "add": "fused add + RMSNorm"}[kind],
+            "step": "forward + backward rows + column reduce", "buffer_sets": S,
+        },
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(N / (ms_step * 1e-3), 1),
+        "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kernels.items()},
+        "kernels_ms_note": "backward_rows from the timed loop; forward and reduce_partials "
+                           "from an event-bracketed pass after it; event brackets include "
+                           "the dispatch latency of the launch",
+        "kernel_gbs": {k: (round(v["bytes"] / (v["avg_ms"] * 1e-3) / 1e9, 1) if v["bytes"] else None)
+                       for k, v in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * mn_norm.h -- C ABI of the MI355X (gfx950) row-wise normalization training
+ * library: RMSNorm, LayerNorm and fused residual-add + RMSNorm, forward and
+ * backward, over row-major [N, D] binary16 activations.
+ *
+ * Sources of the semantics (web pages, cited by title and section):
+ *   [meTile]     "Kernel coverage and training scope", section "Exact native
+ *                normalization contract": formulas, the unrounded fused sum,
+ *                both cotangents of the fused add, bounds (positive rows,
+ *                1..8192 columns, positive finite epsilon), FP32 statistics
+ *                and parameter gradients, no accumulation into existing
+ *                gradient buffers, no in-place mutation, deterministic
+ *                parameter reduction without atomics.
+ *   [tensorcore] "Training kernels", sections "RMSnorm -- Llama-style" and
+ *                "LayerNorm -- standard": argument order (X, gamma, [beta],
+ *                Y, saved statistics, N, D, eps), fp16 X/gamma/beta/Y/dY/dX,
+ *                fp32 saved rstd/mean [N] and fp32 dgamma [D], status return.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a device pointer owned by the caller. The
+ *     library allocates nothing and frees nothing.
+ *   - Row-major, contiguous: element (i, j) of an [N, D] tensor is at i*D + j.
+ *     gamma, beta, dgamma, dbeta are [D]; mean and rstd are [N].
+ *   - mn_f16 is an IEEE binary16 bit pattern. Arithmetic inside is fp32;
+ *     fp16 results are rounded to nearest, ties to even.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ *     Work is enqueued asynchronously; no call synchronizes the host.
+ *   - Validation happens before anything is enqueued; on any error nothing
+ *     is written and nothing is launched:
+ *       MN_ERR_NULL      a required pointer is NULL
+ *       MN_ERR_SHAPE     N < 1, or D outside [1, MN_MAX_COLS]
+ *       MN_ERR_EPS       eps is not a positive finite float
+ *       MN_ERR_ALIAS     an output's byte range overlaps an input's or
+ *                        another output's ([meTile]: no in-place mutation)
+ *       MN_ERR_WORKSPACE workspace NULL, smaller than
+ *                        mn_norm_workspace_bytes(), or not 16-byte aligned
+ *       MN_ERR_DEVICE    the HIP runtime rejected a launch
+ *   - Results are bitwise deterministic for a given (N, D), pointer
+ *     alignment class and device: every reduction has a fixed order and no
+ *     floating-point atomics are used.
+ *   - Rows whose binary16 pointers are all 16-byte aligned with D % 8 == 0
+ *     take the 128-bit vector kernels; any other call takes the element-wise
+ *     kernels (same results up to fp32 summation order).
+ */
+#ifndef MN_NORM_H
+#define MN_NORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t mn_f16;
+
+typedef enum {
+    MN_OK = 0,
+    MN_ERR_NULL = 1,
+    MN_ERR_SHAPE = 2,
+    MN_ERR_EPS = 3,
+    MN_ERR_ALIAS = 4,
+    MN_ERR_WORKSPACE = 5,
+    MN_ERR_DEVICE = 6
+} mn_status;
+
+typedef enum {
+    MN_RMSNORM = 0,
+    MN_LAYERNORM = 1,
+    MN_ADD_RMSNORM = 2
+} mn_norm_kind;
+
+/* [meTile] contract bound: 1..8192 columns. */
+#define MN_MAX_COLS 8192
+
+/* ---------------------------------------------------------------------------
+ * RMSNorm. [meTile] contract, rms_norm_forward; [tensorcore] RMSnorm Math:
+ *   rstd[i] = 1 / sqrt(mean_j(X[i,j]^2) + eps)
+ *   Y[i,j]  = fp16(X[i,j] * rstd[i] * gamma[j])
+ * Inputs X [N,D], gamma [D]; outputs Y [N,D] fp16, rstd [N] fp32 (saved for
+ * the backward).
+ * ------------------------------------------------------------------------- */
+mn_status mn_rmsnorm_forward(const mn_f16* X, const mn_f16* gamma, mn_f16* Y, float* rstd,
+                             int64_t N, int64_t D, float eps, void* stream);
+
+/* RMSNorm backward. [meTile] contract (norm_backward differentiates the
+ * real-valued formula using the saved FP32 statistics); [tensorcore]
+ * tc_rmsnorm_backward. With xhat = X*rstd and g = dY*gamma:
+ *   dX[i,j]   = fp16(rstd[i] * (g[i,j] - xhat[i,j] * mean_j(g*xhat)))
+ *   dgamma[j] = sum_i dY[i,j] * xhat[i,j]      (fp32, overwritten)
+ * rstd is the forward's saved array; X and rstd must be unchanged since the
+ * forward. dgamma is reduced in two fixed-order stages through `workspace`
+ * (caller-owned device memory of at least
+ * mn_norm_workspace_bytes(MN_RMSNORM, N, D) bytes, contents on entry
+ * ignored, clobbered on exit). */
+mn_status mn_rmsnorm_backward(const mn_f16* X, const mn_f16* gamma, const float* rstd,
+                              const mn_f16* dY, mn_f16* dX, float* dgamma,
+                              int64_t N, int64_t D, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* ---------------------------------------------------------------------------
+ * LayerNorm. [meTile] contract, layer_norm_forward (centre by the mean, then
+ * the population variance of the centred values); [tensorcore] LayerNorm:
+ *   mean[i] = sum_j X[i,j] / D
+ *   rstd[i] = 1 / sqrt(sum_j (X[i,j] - mean[i])^2 / D + eps)
+ *   Y[i,j]  = fp16((X[i,j] - mean[i]) * rstd[i] * gamma[j] + beta[j])
+ * ------------------------------------------------------------------------- */
+mn_status mn_layernorm_forward(const mn_f16* X, const mn_f16* gamma, const mn_f16* beta,
+                               mn_f16* Y, float* mean, float* rstd,
+                               int64_t N, int64_t D, float eps, void* stream);
+
+/* LayerNorm backward ([meTile] contract: source, weight and bias gradients).
+ * With xhat = (X - mean)*rstd and g = dY*gamma:
+ *   dX[i,j]   = fp16(rstd[i] * (g - mean_j(g) - xhat * mean_j(g*xhat)))
+ *   dgamma[j] = sum_i dY[i,j] * xhat[i,j];  dbeta[j] = sum_i dY[i,j]
+ * Workspace: mn_norm_workspace_bytes(MN_LAYERNORM, N, D). */
+mn_status mn_layernorm_backward(const mn_f16* X, const mn_f16* gamma, const float* mean,
+                                const float* rstd, const mn_f16* dY, mn_f16* dX,
+                                float* dgamma, float* dbeta, int64_t N, int64_t D,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused residual-add + RMSNorm. [meTile] contract, add_rms_norm_forward: the
+ * sum s = X + R is formed in fp32 and normalised without rounding to fp16;
+ * the sum rounded to fp16 is returned as H (the next residual stream):
+ *   H[i,j]  = fp16(X[i,j] + R[i,j])        (exactly rounded binary16 sum)
+ *   rstd[i] = 1 / sqrt(mean_j(s[i,j]^2) + eps)
+ *   Y[i,j]  = fp16(s[i,j] * rstd[i] * gamma[j])
+ * ------------------------------------------------------------------------- */
+mn_status mn_add_rmsnorm_forward(const mn_f16* X, const mn_f16* R, const mn_f16* gamma,
+                                 mn_f16* H, mn_f16* Y, float* rstd,
+                                 int64_t N, int64_t D, float eps, void* stream);
+
+/* Fused add backward with both output cotangents ([meTile] contract: the
+ * residual-output cotangent defaults to zero and is added to both the source
+ * and the residual gradient). The gradient is taken at the unrounded sum
+ * s = X + R, re-formed from X and R (H is not read):
+ *   dX[i,j] = dR[i,j] = fp16(dH[i,j] + rstd*(g - shat * mean_j(g*shat)))
+ * with shat = s*rstd, g = dY*gamma; dH == NULL means a zero cotangent. One
+ * output array serves as both dX and dR.
+ *   dgamma[j] = sum_i dY[i,j] * shat[i,j]
+ * Workspace: mn_norm_workspace_bytes(MN_ADD_RMSNORM, N, D). */
+mn_status mn_add_rmsnorm_backward(const mn_f16* X, const mn_f16* R, const mn_f16* gamma,
+                                  const float* rstd, const mn_f16* dY, const mn_f16* dH,
+                                  mn_f16* dX, float* dgamma, int64_t N, int64_t D,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Workspace and diagnostics.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of device workspace the backward of `kind` needs at (N, D): the
+ * per-block fp32 parameter-gradient partials (two arrays for LayerNorm).
+ * Depends only on (kind, N, D). Returns 0 for invalid arguments. */
+size_t mn_norm_workspace_bytes(mn_norm_kind kind, int64_t N, int64_t D);
+
+/* Static description of a status code. */
+const char* mn_status_string(mn_status s);
+
+/* Text of the last HIP runtime error seen by this thread's MN_ERR_DEVICE
+ * return ("" if none). */
+const char* mn_last_device_error(void);
+
+/* ---------------------------------------------------------------------------
+ * The two stages of every backward, exported for callers that schedule them
+ * separately (for instance to time the row kernel on its own, or to overlap
+ * the parameter reduction with other work). Calling stage 1 then stage 2 on
+ * the same stream with the same workspace is exactly the corresponding
+ * mn_*_backward call.
+ *
+ * Stage 1 (row kernel): writes dX and the per-block fp32 partials of dgamma
+ * (and dbeta) into `workspace`. Arguments and validation as the full call,
+ * minus the gradient vectors. */
+mn_status mn_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const float* rstd,
+                                   const mn_f16* dY, mn_f16* dX, int64_t N, int64_t D,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+mn_status mn_layernorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const float* mean,
+                                     const float* rstd, const mn_f16* dY, mn_f16* dX,
+                                     int64_t N, int64_t D, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+mn_status mn_add_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* R, const mn_f16* gamma,
+                                       const float* rstd, const mn_f16* dY, const mn_f16* dH,
+                                       mn_f16* dX, int64_t N, int64_t D, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* Stage 2 (column reduce): dgamma[j] = sum over partial rows p of
+ * partial[p][j] in ascending p order (dbeta likewise for LayerNorm; pass
+ * dbeta = NULL otherwise). Overwrites dgamma/dbeta. `kind`, N and D must be
+ * those of the stage-1 call that filled `workspace`. */
+mn_status mn_norm_reduce_partials(mn_norm_kind kind, int64_t N, int64_t D,
+                                  const void* workspace, size_t workspace_bytes,
+                                  float* dgamma, float* dbeta, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MN_NORM_H */

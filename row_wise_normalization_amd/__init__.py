@@ -1,0 +1,281 @@
+"""Python binding of libmn_norm.so, the gfx950 row-wise normalization library.
+
+Every ``mn_*`` function here has the name and pointer-argument order of the C
+entry point declared in ``include/mn_norm.h``; the binding only checks torch
+tensors (device, dtype, contiguity, shapes), passes their device pointers,
+derives N and D from X, and raises ``MnError`` on a non-zero status. All
+arithmetic runs in the library's HIP kernels; there is no fallback: if the
+library is missing or cannot be loaded the call raises.
+
+The helpers without the ``mn_`` prefix allocate outputs and workspace with
+torch (device memory plumbing only) and call the same entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmn_norm.so")
+
+MN_RMSNORM, MN_LAYERNORM, MN_ADD_RMSNORM = 0, 1, 2
+MAX_COLS = 8192
+
+STATUS = {
+    0: "MN_OK", 1: "MN_ERR_NULL", 2: "MN_ERR_SHAPE", 3: "MN_ERR_EPS", 4: "MN_ERR_ALIAS",
+    5: "MN_ERR_WORKSPACE", 6: "MN_ERR_DEVICE",
+}
+
+
+class MnError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "mn_rmsnorm_forward": [_P, _P, _P, _P, _I64, _I64, _F, _P],
+    "mn_rmsnorm_backward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
+    "mn_layernorm_forward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P],
+    "mn_layernorm_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
+    "mn_add_rmsnorm_forward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P],
+    "mn_add_rmsnorm_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
+    "mn_rmsnorm_backward_rows": [_P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
+    "mn_layernorm_backward_rows": [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
+    "mn_add_rmsnorm_backward_rows": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
+    "mn_norm_reduce_partials": [ctypes.c_int, _I64, _I64, _P, _SZ, _P, _P, _P],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmn_norm.so from this package directory (raises if absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m row_wise_normalization_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    for name, argtypes in _SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_int
+    L.mn_norm_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64]
+    L.mn_norm_workspace_bytes.restype = _SZ
+    L.mn_status_string.argtypes = [ctypes.c_int]
+    L.mn_status_string.restype = ctypes.c_char_p
+    L.mn_last_device_error.argtypes = []
+    L.mn_last_device_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+# --- marshalling -------------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check_t(name: str, t: Optional[torch.Tensor], dtype, shape, optional: bool = False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _nd(X: torch.Tensor) -> Tuple[int, int]:
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise ValueError("X must be a 2-D [N, D] tensor")
+    return int(X.shape[0]), int(X.shape[1])
+
+
+def _call(name: str, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        text = lib().mn_status_string(st).decode()
+        if st == 6:
+            text += ": " + lib().mn_last_device_error().decode()
+        raise MnError(name, st, text)
+
+
+H, F32 = torch.float16, torch.float32
+
+
+def workspace_bytes(kind: int, N: int, D: int) -> int:
+    return int(lib().mn_norm_workspace_bytes(int(kind), int(N), int(D)))
+
+
+# --- the C entry points ------------------------------------------------------
+
+def mn_rmsnorm_forward(X, gamma, Y, rstd, eps: float, stream=None):
+    N, D = _nd(X)
+    _check_t("X", X, H, (N, D)); _check_t("gamma", gamma, H, (D,))
+    _check_t("Y", Y, H, (N, D)); _check_t("rstd", rstd, F32, (N,))
+    _call("mn_rmsnorm_forward", _ptr(X), _ptr(gamma), _ptr(Y), _ptr(rstd), N, D, float(eps),
+          _stream(stream))
+
+
+def mn_rmsnorm_backward(X, gamma, rstd, dY, dX, dgamma, workspace, stream=None):
+    N, D = _nd(X)
+    _check_t("X", X, H, (N, D)); _check_t("gamma", gamma, H, (D,))
+    _check_t("rstd", rstd, F32, (N,)); _check_t("dY", dY, H, (N, D))
+    _check_t("dX", dX, H, (N, D)); _check_t("dgamma", dgamma, F32, (D,))
+    _call("mn_rmsnorm_backward", _ptr(X), _ptr(gamma), _ptr(rstd), _ptr(dY), _ptr(dX),
+          _ptr(dgamma), N, D, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def mn_layernorm_forward(X, gamma, beta, Y, mean, rstd, eps: float, stream=None):
+    N, D = _nd(X)
+    _check_t("X", X, H, (N, D)); _check_t("gamma", gamma, H, (D,)); _check_t("beta", beta, H, (D,))
+    _check_t("Y", Y, H, (N, D)); _check_t("mean", mean, F32, (N,)); _check_t("rstd", rstd, F32, (N,))
+    _call("mn_layernorm_forward", _ptr(X), _ptr(gamma), _ptr(beta), _ptr(Y), _ptr(mean),
+          _ptr(rstd), N, D, float(eps), _stream(stream))
+
+
+def mn_layernorm_backward(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, workspace, stream=None):
+    N, D = _nd(X)
+    _check_t("X", X, H, (N, D)); _check_t("gamma", gamma, H, (D,))
+    _check_t("mean", mean, F32, (N,)); _check_t("rstd", rstd, F32, (N,))
+    _check_t("dY", dY, H, (N, D)); _check_t("dX", dX, H, (N, D))
+    _check_t("dgamma", dgamma, F32, (D,)); _check_t("dbeta", dbeta, F32, (D,))
+    _call("mn_layernorm_backward", _ptr(X), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dY),
+          _ptr(dX), _ptr(dgamma), _ptr(dbeta), N, D, _ptr(workspace), _ws_bytes(workspace),
+          _stream(stream))
+
+
+def mn_add_rmsnorm_forward(X, R, gamma, H_out, Y, rstd, eps: float, stream=None):
+    N, D = _nd(X)
+    _check_t("X", X, H, (N, D)); _check_t("R", R, H, (N, D)); _check_t("gamma", gamma, H, (D,))
+    _check_t("H", H_out, H, (N, D)); _check_t("Y", Y, H, (N, D)); _check_t("rstd", rstd, F32, (N,))
+    _call("mn_add_rmsnorm_forward", _ptr(X), _ptr(R), _ptr(gamma), _ptr(H_out), _ptr(Y),
+          _ptr(rstd), N, D, float(eps), _stream(stream))
+
+
+def mn_add_rmsnorm_backward(X, R, gamma, rstd, dY, dH, dX, dgamma, workspace, stream=None):
+    N, D = _nd(X)
+    _check_t("X", X, H, (N, D)); _check_t("R", R, H, (N, D)); _check_t("gamma", gamma, H, (D,))
+    _check_t("rstd", rstd, F32, (N,)); _check_t("dY", dY, H, (N, D))
+    _check_t("dH", dH, H, (N, D), optional=True); _check_t("dX", dX, H, (N, D))
+    _check_t("dgamma", dgamma, F32, (D,))
+    _call("mn_add_rmsnorm_backward", _ptr(X), _ptr(R), _ptr(gamma), _ptr(rstd), _ptr(dY),
+          _ptr(dH), _ptr(dX), _ptr(dgamma), N, D, _ptr(workspace), _ws_bytes(workspace),
+          _stream(stream))
+
+
+def mn_rmsnorm_backward_rows(X, gamma, rstd, dY, dX, workspace, stream=None):
+    N, D = _nd(X)
+    _call("mn_rmsnorm_backward_rows", _ptr(X), _ptr(gamma), _ptr(rstd), _ptr(dY), _ptr(dX), N, D,
+          _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def mn_layernorm_backward_rows(X, gamma, mean, rstd, dY, dX, workspace, stream=None):
+    N, D = _nd(X)
+    _call("mn_layernorm_backward_rows", _ptr(X), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dY),
+          _ptr(dX), N, D, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def mn_add_rmsnorm_backward_rows(X, R, gamma, rstd, dY, dH, dX, workspace, stream=None):
+    N, D = _nd(X)
+    _call("mn_add_rmsnorm_backward_rows", _ptr(X), _ptr(R), _ptr(gamma), _ptr(rstd), _ptr(dY),
+          _ptr(dH), _ptr(dX), N, D, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def mn_norm_reduce_partials(kind: int, N: int, D: int, workspace, dgamma, dbeta=None, stream=None):
+    _call("mn_norm_reduce_partials", int(kind), int(N), int(D), _ptr(workspace),
+          _ws_bytes(workspace), _ptr(dgamma), _ptr(dbeta), _stream(stream))
+
+
+def _ws_bytes(workspace: Optional[torch.Tensor]) -> int:
+    if workspace is None:
+        return 0
+    return workspace.numel() * workspace.element_size()
+
+
+# --- allocating helpers -------------------------------------------------------
+
+def new_workspace(kind: int, N: int, D: int, device=None) -> torch.Tensor:
+    nbytes = max(16, workspace_bytes(kind, N, D))
+    return torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=device or "cuda")
+
+
+def rmsnorm_forward(X, gamma, eps: float = 1e-5, stream=None):
+    N, D = _nd(X)
+    Y = torch.empty_like(X)
+    rstd = torch.empty(N, dtype=F32, device=X.device)
+    mn_rmsnorm_forward(X, gamma, Y, rstd, eps, stream)
+    return Y, rstd
+
+
+def rmsnorm_backward(X, gamma, rstd, dY, stream=None):
+    N, D = _nd(X)
+    dX = torch.empty_like(X)
+    dgamma = torch.empty(D, dtype=F32, device=X.device)
+    ws = new_workspace(MN_RMSNORM, N, D, X.device)
+    mn_rmsnorm_backward(X, gamma, rstd, dY, dX, dgamma, ws, stream)
+    return dX, dgamma
+
+
+def layernorm_forward(X, gamma, beta, eps: float = 1e-5, stream=None):
+    N, D = _nd(X)
+    Y = torch.empty_like(X)
+    mean = torch.empty(N, dtype=F32, device=X.device)
+    rstd = torch.empty(N, dtype=F32, device=X.device)
+    mn_layernorm_forward(X, gamma, beta, Y, mean, rstd, eps, stream)
+    return Y, mean, rstd
+
+
+def layernorm_backward(X, gamma, mean, rstd, dY, stream=None):
+    N, D = _nd(X)
+    dX = torch.empty_like(X)
+    dgamma = torch.empty(D, dtype=F32, device=X.device)
+    dbeta = torch.empty(D, dtype=F32, device=X.device)
+    ws = new_workspace(MN_LAYERNORM, N, D, X.device)
+    mn_layernorm_backward(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, ws, stream)
+    return dX, dgamma, dbeta
+
+
+def add_rmsnorm_forward(X, R, gamma, eps: float = 1e-5, stream=None):
+    N, D = _nd(X)
+    Hs = torch.empty_like(X)
+    Y = torch.empty_like(X)
+    rstd = torch.empty(N, dtype=F32, device=X.device)
+    mn_add_rmsnorm_forward(X, R, gamma, Hs, Y, rstd, eps, stream)
+    return Hs, Y, rstd
+
+
+def add_rmsnorm_backward(X, R, gamma, rstd, dY, dH=None, stream=None):
+    N, D = _nd(X)
+    dX = torch.empty_like(X)
+    dgamma = torch.empty(D, dtype=F32, device=X.device)
+    ws = new_workspace(MN_ADD_RMSNORM, N, D, X.device)
+    mn_add_rmsnorm_backward(X, R, gamma, rstd, dY, dH, dX, dgamma, ws, stream)
+    return dX, dgamma

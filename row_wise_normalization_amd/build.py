@@ -1,0 +1,64 @@
+"""Build libmn_norm.so (gfx950) in-tree with hipcc.
+
+Usage: python -m row_wise_normalization_amd.build  (or call build()).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libmn_norm.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+
+SOURCES = ["mn_kernels.hip", "mn_api.cpp"]
+ARCH = "gfx950"
+
+# Device-code flags. Packed fp32 instructions are disabled on purpose; no
+# fast-math and no denormal flushing (IEEE fp32 division and square root).
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmn_norm.so)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared library; always rebuilds."""
+    objs = []
+    build_dir = os.path.join(PKG, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    cc = hipcc()
+    for src in SOURCES:
+        obj = os.path.join(build_dir, src + ".o")
+        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
+    tmp = LIB_PATH + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,179 @@
+// mn_kernels.hip -- launch tables of the gfx950 normalization kernels
+// (templates in mn_kernels.hpp): which template instance serves which width,
+// the grid of every launch, and the dispatch from the C ABI layer.
+#include "mn_kernels.hpp"
+
+namespace mn {
+namespace {
+
+using kern::bwd_kernel;
+using kern::fwd_kernel;
+using kern::reduce_kernel;
+
+constexpr int kReduceCQ = 16;  // 64 columns per block, 64 segments
+
+// ---------------------------------------------------------------------------
+// Variant tables.
+// ---------------------------------------------------------------------------
+
+// Chosen by the smallest max_d >= D. Shapes come from timing sweeps on
+// MI355X at 16384x4096, 32768x8192 and 1048576x128: the forward runs one
+// tile per workgroup (many small workgroups keep the most reads in flight);
+// the backward runs fewer, long-lived workgroups (each owns one partial row
+// of dgamma) and prefetches the next tile. Non-temporal stores throughout.
+//
+// Forward, 128-bit path (D % 8 == 0).
+//   id   T  VEC CPT  U  BLOCK  PF NT  max_d
+#define MN_FWD_VEC_TABLE(X)                  \
+    X(0, 8, 8, 1, 4, 256, 0, 1, 64)          \
+    X(1, 16, 8, 1, 2, 256, 0, 1, 128)        \
+    X(2, 32, 8, 1, 2, 256, 0, 1, 256)        \
+    X(3, 64, 8, 1, 2, 256, 0, 1, 512)        \
+    X(4, 128, 8, 1, 1, 256, 0, 1, 1024)      \
+    X(5, 256, 8, 1, 1, 256, 0, 1, 2048)      \
+    X(6, 256, 8, 2, 1, 256, 0, 1, 4096)      \
+    X(7, 512, 8, 2, 1, 512, 0, 1, 8192)
+// Element-wise path (any D, any alignment).
+#define MN_FWD_GEN_TABLE(X)                  \
+    X(8, 64, 1, 16, 1, 256, 0, 1, 1024)      \
+    X(9, 256, 1, 16, 1, 256, 0, 1, 4096)     \
+    X(10, 512, 1, 16, 1, 512, 0, 1, 8192)
+
+#define MN_BWD_VEC_TABLE(X)                  \
+    X(0, 8, 8, 1, 8, 256, 1, 1, 64)          \
+    X(1, 16, 8, 1, 8, 256, 1, 1, 128)        \
+    X(2, 32, 8, 1, 4, 256, 1, 1, 256)        \
+    X(3, 64, 8, 1, 2, 256, 1, 1, 512)        \
+    X(4, 128, 8, 1, 1, 512, 1, 1, 1024)      \
+    X(5, 256, 8, 1, 1, 512, 1, 1, 2048)      \
+    X(6, 256, 8, 2, 1, 512, 1, 1, 4096)      \
+    X(7, 1024, 8, 1, 1, 1024, 1, 1, 8192)
+#define MN_BWD_GEN_TABLE(X)                  \
+    X(8, 64, 1, 16, 1, 256, 1, 1, 1024)      \
+    X(9, 256, 1, 16, 1, 256, 1, 1, 4096)     \
+    X(10, 512, 1, 16, 1, 512, 1, 1, 8192)
+
+struct VariantRow {
+    Variant v;
+    int max_d;
+};
+
+#define MN_ROW(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) {{id, T, VEC, CPT, U, BLOCK}, MAXD},
+const VariantRow kFwdVec[] = {MN_FWD_VEC_TABLE(MN_ROW)};
+const VariantRow kFwdGen[] = {MN_FWD_GEN_TABLE(MN_ROW)};
+const VariantRow kBwdVec[] = {MN_BWD_VEC_TABLE(MN_ROW)};
+const VariantRow kBwdGen[] = {MN_BWD_GEN_TABLE(MN_ROW)};
+#undef MN_ROW
+
+template <size_t K>
+Variant pick(const VariantRow (&t)[K], int32_t D)
+{
+    for (size_t i = 0; i < K; ++i)
+        if (D <= t[i].max_d) return t[i].v;
+    return t[K - 1].v;
+}
+
+template <typename Kernel, typename Args>
+hipError_t launch(Kernel k, dim3 grid, dim3 block, size_t shmem, hipStream_t s, const Args& a)
+{
+    void* args[] = {const_cast<Args*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, shmem, s);
+}
+
+template <int KIND>
+hipError_t launch_fwd_kind(const FwdPlan& p, const FwdArgs& a, hipStream_t s)
+{
+    const dim3 grid((unsigned)p.grid);
+    switch (p.v.id) {
+#define MN_CASE(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) \
+    case id:                                             \
+        return launch(fwd_kernel<KIND, T, VEC, CPT, U, BLOCK, PF, NT>, grid, dim3(BLOCK), 0, s, a);
+        MN_FWD_VEC_TABLE(MN_CASE)
+        MN_FWD_GEN_TABLE(MN_CASE)
+#undef MN_CASE
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int KIND>
+hipError_t launch_bwd_kind(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
+{
+    const dim3 grid((unsigned)p.P);
+    switch (p.v.id) {
+#define MN_CASE(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) \
+    case id:                                             \
+        return launch(bwd_kernel<KIND, T, VEC, CPT, U, BLOCK, PF, NT>, grid, dim3(BLOCK), p.shmem, s, a);
+        MN_BWD_VEC_TABLE(MN_CASE)
+        MN_BWD_GEN_TABLE(MN_CASE)
+#undef MN_CASE
+    }
+    return hipErrorInvalidValue;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workgroups (= partial rows) of the backward: one long-lived workgroup per
+// CU of the 256 (two for the widest fused-add rows, whose 1024-lane
+// workgroups are shorter-lived), each owning a contiguous range of rows.
+int64_t bwd_blocks(int kind, int32_t D) { return (kind == ADD && D > 4096) ? 512 : 256; }
+
+}  // namespace
+
+int32_t partial_stride(int32_t D) { return (D + 3) & ~3; }
+
+int64_t bwd_partial_rows(int kind, int64_t N, int32_t D)
+{
+    const int64_t rb = ceil_div(N, bwd_blocks(kind, D));
+    return ceil_div(N, rb);
+}
+
+FwdPlan plan_forward(int kind, int64_t N, int32_t D, bool vec_ok)
+{
+    (void)kind;
+    FwdPlan p;
+    p.v = vec_ok ? pick(kFwdVec, D) : pick(kFwdGen, D);
+    // one tile of RPB*U rows per workgroup
+    p.rows_per_block = (int64_t)(p.v.BLOCK / p.v.T) * p.v.U;
+    p.grid = ceil_div(N, p.rows_per_block);
+    return p;
+}
+
+BwdPlan plan_backward(int kind, int64_t N, int32_t D, bool vec_ok)
+{
+    BwdPlan p;
+    p.v = vec_ok ? pick(kBwdVec, D) : pick(kBwdGen, D);
+    p.rows_per_block = ceil_div(N, bwd_blocks(kind, D));
+    p.P = ceil_div(N, p.rows_per_block);
+    p.Dp = partial_stride(D);
+    const int rpb = p.v.BLOCK / p.v.T;
+    p.shmem = (rpb > 1) ? (size_t)D * sizeof(float) * (kind == LN ? 2 : 1) : 0;
+    return p;
+}
+
+hipError_t launch_forward(int kind, const FwdPlan& p, const FwdArgs& a, hipStream_t s)
+{
+    switch (kind) {
+    case RMS: return launch_fwd_kind<RMS>(p, a, s);
+    case LN: return launch_fwd_kind<LN>(p, a, s);
+    case ADD: return launch_fwd_kind<ADD>(p, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_backward_rows(int kind, const BwdPlan& p, const BwdArgs& a, hipStream_t s)
+{
+    switch (kind) {
+    case RMS: return launch_bwd_kind<RMS>(p, a, s);
+    case LN: return launch_bwd_kind<LN>(p, a, s);
+    case ADD: return launch_bwd_kind<ADD>(p, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s)
+{
+    const dim3 grid((unsigned)ceil_div(a.Dp, 4 * kReduceCQ), a.part_b ? 2u : 1u);
+    return launch(reduce_kernel<kReduceCQ>, grid, dim3(1024), 0, s, a);
+}
+
+}  // namespace mn

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/mn_norm.h declares, and rejects bad arguments
+before touching the device (validation never dereferences the pointers, so
+placeholder addresses are enough)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import row_wise_normalization_amd as mn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mn_norm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mn.LIB_PATH),
+                                reason="libmn_norm.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(mn_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("mn_rmsnorm_forward", "mn_rmsnorm_backward", "mn_layernorm_forward",
+              "mn_layernorm_backward", "mn_add_rmsnorm_forward", "mn_add_rmsnorm_backward",
+              "mn_norm_workspace_bytes", "mn_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", mn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s(mn_\w+)$", out, re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    L = mn.lib()
+    for n in declared_functions():
+        getattr(L, n)
+
+
+def test_status_strings():
+    L = mn.lib()
+    for code in range(7):
+        assert len(L.mn_status_string(code)) > 0
+    assert L.mn_last_device_error() == b""
+
+
+P = ctypes.c_void_p
+A = P(0x100000)   # placeholder addresses far apart (never dereferenced)
+B = P(0x20000000)
+C = P(0x40000000)
+Dp = P(0x60000000)
+E = P(0x80000000)
+F = P(0xA0000000)
+G = P(0xC0000000)
+NULL = None
+S = None  # stream
+
+
+def rms_fwd(X=A, g=B, Y=C, r=Dp, N=16, D=64, eps=1e-5):
+    return mn.lib().mn_rmsnorm_forward(X, g, Y, r, N, D, ctypes.c_float(eps), S)
+
+
+def test_forward_validation():
+    assert rms_fwd(X=NULL) == 1
+    assert rms_fwd(Y=NULL) == 1
+    assert rms_fwd(r=NULL) == 1
+    assert rms_fwd(N=0) == 2
+    assert rms_fwd(N=-3) == 2
+    assert rms_fwd(D=0) == 2
+    assert rms_fwd(D=8193) == 2
+    for eps in (0.0, -1e-5, float("nan"), float("inf")):
+        assert rms_fwd(eps=eps) == 3, eps
+    assert rms_fwd(Y=A) == 4                      # Y is X
+    assert rms_fwd(Y=P(0x100000 + 16 * 64 * 2 - 2)) == 4   # Y overlaps X's last element
+    assert rms_fwd(r=P(0x100000 + 64)) == 4       # rstd inside X
+    assert rms_fwd(r=C) == 4                      # rstd overlaps Y
+    L = mn.lib()
+    f = ctypes.c_float(1e-5)
+    assert L.mn_layernorm_forward(A, B, NULL, C, Dp, E, 4, 64, f, S) == 1
+    assert L.mn_layernorm_forward(A, B, C, Dp, NULL, E, 4, 64, f, S) == 1
+    assert L.mn_add_rmsnorm_forward(A, NULL, B, C, Dp, E, 4, 64, f, S) == 1
+    assert L.mn_add_rmsnorm_forward(A, B, C, NULL, Dp, E, 4, 64, f, S) == 1
+    assert L.mn_add_rmsnorm_forward(A, B, C, Dp, Dp, E, 4, 64, f, S) == 4  # H is Y
+
+
+def test_backward_validation():
+    L = mn.lib()
+    N, D = 16, 64
+    ws = mn.workspace_bytes(mn.MN_RMSNORM, N, D)
+    W = P(0xE0000000)
+    assert ws > 0
+    call = lambda **k: L.mn_rmsnorm_backward(
+        k.get("X", A), k.get("g", B), k.get("r", C), k.get("dY", Dp), k.get("dX", E),
+        k.get("dg", F), k.get("N", N), k.get("D", D), k.get("W", W), k.get("ws", ws), S)
+    assert call(dg=NULL) == 1
+    assert call(r=NULL) == 1
+    assert call(N=0) == 2
+    assert call(D=9000) == 2
+    assert call(W=NULL) == 5
+    assert call(ws=ws - 1) == 5
+    assert call(W=P(0xE0000004)) == 5             # not 16-byte aligned
+    assert call(dX=A) == 4                        # dX is X
+    assert call(dX=Dp) == 4                       # dX is dY
+    assert call(dg=W) == 4                        # dgamma inside the workspace
+    assert call(W=P(0x100000)) == 5 or call(W=P(0x100000)) == 4
+    assert L.mn_layernorm_backward(A, B, NULL, C, Dp, E, F, G, N, D, W,
+                                   mn.workspace_bytes(mn.MN_LAYERNORM, N, D), S) == 1
+    assert L.mn_layernorm_backward(A, B, P(0x30000000), C, Dp, E, F, NULL, N, D, W,
+                                   mn.workspace_bytes(mn.MN_LAYERNORM, N, D), S) == 1
+    assert L.mn_add_rmsnorm_backward(A, NULL, B, C, Dp, NULL, E, F, N, D, W, ws, S) == 1
+    assert L.mn_norm_reduce_partials(1, N, D, W, ws, F, NULL, S) == 1
+
+
+def test_workspace_bytes():
+    for kind in (mn.MN_RMSNORM, mn.MN_LAYERNORM, mn.MN_ADD_RMSNORM):
+        assert mn.workspace_bytes(kind, 0, 64) == 0
+        assert mn.workspace_bytes(kind, 4, 0) == 0
+        assert mn.workspace_bytes(kind, 4, 8193) == 0
+        for N, D in ((1, 1), (17, 257), (16384, 4096), (1048576, 128), (32768, 8192)):
+            b = mn.workspace_bytes(kind, N, D)
+            assert b > 0 and b % 16 == 0
+            # at most 512 partial rows of round_up(D, 4) floats (two arrays for LayerNorm)
+            assert b <= 512 * ((D + 3) // 4 * 4) * 4 * (2 if kind == mn.MN_LAYERNORM else 1)
+    assert mn.workspace_bytes(3, 16, 64) == 0
+
+
+def test_product_and_oracle_are_independent():
+    """Neither side imports, includes or links the other."""
+    pkg = os.path.join(ROOT, "row_wise_normalization_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                with open(os.path.join(dirpath, fn)) as f:
+                    src = f.read()
+                assert not re.search(r"\boracle\b|mn_oracle|mno_", src), f"{fn} refers to the oracle"
+    for fn in os.listdir(os.path.join(ROOT, "oracle")):
+        if fn.endswith((".py", ".c", ".h")):
+            with open(os.path.join(ROOT, "oracle", fn)) as f:
+                src = f.read()
+            assert "row_wise_normalization_amd" not in src and "mn_norm.h" not in src, fn

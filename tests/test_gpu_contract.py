@@ -1,0 +1,182 @@
+"""Contract properties on the GPU: determinism, row independence, closed-form
+rows, the fused add's special cases, non-finite locality, no writes outside
+the outputs, the two-stage backward, and error returns."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import row_wise_normalization_amd as mn
+import workloads
+from gpu_cases import dev, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(a):
+    return a.view(np.uint32 if a.dtype == np.float32 else np.uint16)
+
+
+def _same(a, b, what):
+    assert a.shape == b.shape, what
+    assert (_bits(a) == _bits(b)).all(), f"{what}: {int((_bits(a) != _bits(b)).sum())} bits differ"
+
+
+@pytest.mark.parametrize("kind,N,D", [("rms", 16384, 4096), ("ln", 4096, 1024),
+                                      ("add", 2048, 8192), ("rms", 65536, 128),
+                                      ("rms", 17, 257)])
+def test_reruns_bitwise_identical(kind, N, D):
+    say(f"[contract] determinism {kind} {N}x{D}")
+    d = workloads.random_case(kind, N, D, seed=8)
+    runs = [run_gpu(kind, d, 1e-5) for _ in range(3)]
+    for r in runs[1:]:
+        for k in runs[0]:
+            _same(runs[0][k], r[k], f"{kind} {k}")
+
+
+def test_row_subset_reproduces_rows():
+    # rows are independent: a call on a slice gives the same bits for those rows
+    for kind in ("rms", "ln", "add"):
+        d = workloads.random_case(kind, 512, 2048, seed=9)
+        full = run_gpu(kind, d, 1e-5)
+        sub = {k: (np.ascontiguousarray(v[100:300]) if v.ndim == 2 else v) for k, v in d.items()}
+        part = run_gpu(kind, sub, 1e-5)
+        for k in ("Y", "dX", "rstd") + (("mean",) if kind == "ln" else ()) + (("H",) if kind == "add" else ()):
+            _same(full[k][100:300], part[k], f"{kind} {k} rows 100..299")
+
+
+@pytest.mark.parametrize("D", [1, 7, 8, 257, 1024, 4096, 8192])
+def test_constant_rows(D):
+    cs = np.array([0.0, 1.0, -1.0, 0.5, -3.25, 100.0, 2.0 ** -10, 65504.0 / 64], dtype=np.float16)
+    X = np.repeat(cs[:, None], D, axis=1)
+    rng = np.random.default_rng(D)
+    d = {"X": X, "gamma": (1 + 0.1 * rng.standard_normal(D)).astype(np.float16),
+         "beta": (0.1 * rng.standard_normal(D)).astype(np.float16),
+         "dY": rng.standard_normal((len(cs), D)).astype(np.float16)}
+    g = run_gpu("ln", d, 1e-5)
+    # LayerNorm: the centred row is exactly zero, so y = beta bit for bit
+    _same(g["Y"], np.broadcast_to(d["beta"], X.shape).copy(), f"ln constant rows D={D}")
+    assert (g["mean"] == cs.astype(np.float32)).all()
+    # RMSNorm: y = c * gamma / sqrt(c^2 + eps) ~ sign(c) * gamma
+    g = run_gpu("rms", {k: d[k] for k in ("X", "gamma", "dY")}, 1e-5)
+    c = cs.astype(np.float64)[:, None]
+    ref = c * d["gamma"].astype(np.float64) / np.sqrt(c * c + 1e-5)
+    parity.check_f16(g["Y"], ref, f"rms constant rows D={D}")
+
+
+def test_fused_special_cases():
+    d = workloads.random_case("add", 777, 4096, seed=10)
+    Z = np.zeros_like(d["X"])
+    # R = 0: H = X and the fused forward equals plain RMSNorm bit for bit
+    a = run_gpu("add", dict(d, R=Z), 1e-5, use_dh=False)
+    r = run_gpu("rms", {k: d[k] for k in ("X", "gamma", "dY")}, 1e-5)
+    _same(a["H"], d["X"], "H = X when R = 0")
+    # the forwards evaluate the same fp32 operations: bitwise equal
+    for k in ("Y", "rstd"):
+        _same(a[k], r[k], f"fused(R=0) {k} == rmsnorm {k}")
+    # the backward kernels are separate instances (the fused one also adds
+    # dH); fp32 contraction may differ, so compare within 1 fp16 ulp
+    ulp = parity.ulp16(r["dX"])
+    diff = np.abs(a["dX"].astype(np.float64) - r["dX"].astype(np.float64))
+    say(f"[contract] fused(R=0) vs rmsnorm dX: {int((diff > 0).sum())} elements differ, "
+        f"max {float((diff / ulp).max()):.1f} ulp")
+    assert (diff <= ulp).all()
+    parity.check_grad(a["dgamma"], r["dgamma"].astype(np.float64), "fused(R=0) dgamma",
+                      atol=1e-6, rtol=1e-6)
+    # dY = 0: dX = dH exactly (as values; a zero may change sign)
+    b = run_gpu("add", dict(d, dY=Z), 1e-5)
+    assert (b["dX"].astype(np.float64) == d["dH"].astype(np.float64)).all()
+    assert (b["dgamma"] == 0).all()
+
+
+def test_nonfinite_input_stays_in_its_row():
+    d = workloads.random_case("rms", 64, 1024, seed=11)
+    clean = run_gpu("rms", d, 1e-5)
+    X = d["X"].copy()
+    X[5, 17] = np.float16(np.nan)
+    X[9, 3] = np.float16(np.inf)
+    dirty = run_gpu("rms", dict(d, X=X), 1e-5)
+    other = np.setdiff1d(np.arange(64), [5, 9])
+    for k in ("Y", "dX", "rstd"):
+        _same(clean[k][other], dirty[k][other], f"{k} of finite rows")
+    assert np.isnan(dirty["Y"][5]).all() and np.isnan(dirty["dX"][5]).all()
+    assert np.isnan(dirty["dgamma"]).all()
+
+
+def test_no_writes_outside_outputs():
+    N, D = 300, 1000
+    d = workloads.random_case("ln", N, D, seed=12)
+    X, g, b, dY = (dev(d[k]) for k in ("X", "gamma", "beta", "dY"))
+    guard = 4096
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * guard,), 7, dtype=dtype, device="cuda")
+        return buf, buf[guard:guard + n]
+    Yb, Y = guarded(N * D, torch.float16)
+    mb, mean = guarded(N, torch.float32)
+    rb, rstd = guarded(N, torch.float32)
+    dXb, dX = guarded(N * D, torch.float16)
+    gb, dgamma = guarded(D, torch.float32)
+    bb, dbeta = guarded(D, torch.float32)
+    mn.mn_layernorm_forward(X, g, b, Y.view(N, D), mean, rstd, 1e-5)
+    ws = mn.new_workspace(mn.MN_LAYERNORM, N, D)
+    mn.mn_layernorm_backward(X, g, mean, rstd, dY, dX.view(N, D), dgamma, dbeta, ws)
+    torch.cuda.synchronize()
+    for name, buf in (("Y", Yb), ("mean", mb), ("rstd", rb), ("dX", dXb), ("dgamma", gb),
+                      ("dbeta", bb)):
+        h = buf.cpu()
+        assert (h[:guard] == 7).all() and (h[-guard:] == 7).all(), f"write outside {name}"
+
+
+def test_two_stage_backward_equals_full_call():
+    N, D = 1000, 2048
+    for kind in ("rms", "ln", "add"):
+        d = workloads.random_case(kind, N, D, seed=13)
+        full = run_gpu(kind, d, 1e-5)
+        X, g, dY = dev(d["X"]), dev(d["gamma"]), dev(d["dY"])
+        rstd = torch.from_numpy(full["rstd"]).cuda()
+        dX = torch.empty_like(X)
+        dgamma = torch.empty(D, dtype=torch.float32, device="cuda")
+        dbeta = torch.empty(D, dtype=torch.float32, device="cuda")
+        if kind == "rms":
+            ws = mn.new_workspace(mn.MN_RMSNORM, N, D)
+            mn.mn_rmsnorm_backward_rows(X, g, rstd, dY, dX, ws)
+            mn.mn_norm_reduce_partials(mn.MN_RMSNORM, N, D, ws, dgamma)
+        elif kind == "ln":
+            mean = torch.from_numpy(full["mean"]).cuda()
+            ws = mn.new_workspace(mn.MN_LAYERNORM, N, D)
+            mn.mn_layernorm_backward_rows(X, g, mean, rstd, dY, dX, ws)
+            mn.mn_norm_reduce_partials(mn.MN_LAYERNORM, N, D, ws, dgamma, dbeta)
+        else:
+            R, dH = dev(d["R"]), dev(d["dH"])
+            ws = mn.new_workspace(mn.MN_ADD_RMSNORM, N, D)
+            mn.mn_add_rmsnorm_backward_rows(X, R, g, rstd, dY, dH, dX, ws)
+            mn.mn_norm_reduce_partials(mn.MN_ADD_RMSNORM, N, D, ws, dgamma)
+        torch.cuda.synchronize()
+        _same(full["dX"], dX.cpu().numpy(), f"{kind} staged dX")
+        _same(full["dgamma"], dgamma.cpu().numpy(), f"{kind} staged dgamma")
+        if kind == "ln":
+            _same(full["dbeta"], dbeta.cpu().numpy(), "ln staged dbeta")
+
+
+def test_error_returns_on_device():
+    N, D = 64, 256
+    X = torch.zeros(N, D, dtype=torch.float16, device="cuda")
+    g = torch.ones(D, dtype=torch.float16, device="cuda")
+    Y = torch.empty_like(X)
+    rstd = torch.empty(N, dtype=torch.float32, device="cuda")
+    with pytest.raises(mn.MnError, match="MN_ERR_EPS"):
+        mn.mn_rmsnorm_forward(X, g, Y, rstd, 0.0)
+    with pytest.raises(mn.MnError, match="MN_ERR_ALIAS"):
+        mn.mn_rmsnorm_forward(X, g, X, rstd, 1e-5)
+    dX = torch.empty_like(X)
+    dgamma = torch.empty(D, dtype=torch.float32, device="cuda")
+    small = torch.empty(8, dtype=torch.float32, device="cuda")
+    with pytest.raises(mn.MnError, match="MN_ERR_WORKSPACE"):
+        mn.mn_rmsnorm_backward(X, g, rstd, X, dX, dgamma, small)
+    # the failed calls launched nothing: outputs keep their contents
+    Y.fill_(3.0)
+    with pytest.raises(mn.MnError):
+        mn.mn_rmsnorm_forward(X, g, Y, rstd, float("nan"))
+    torch.cuda.synchronize()
+    assert (Y == 3.0).all()

@@ -4,23 +4,26 @@ import numpy as np
 import workloads
 
 
-def test_chunked_stream_equals_whole_draw(monkeypatch):
+def test_blocks_independent_of_threads_and_prefix(monkeypatch):
     w = workloads.WORKLOADS["rms_17x257"]
-    whole = workloads.generate(w)
-    monkeypatch.setattr(workloads, "_CHUNK_ELEMS", 257 * 3)   # 3-row chunks
-    chunked = workloads.generate(w)
-    for k in whole:
-        assert (whole[k].view(np.uint16) == chunked[k].view(np.uint16)).all(), k
+    monkeypatch.setattr(workloads, "_CHUNK_ELEMS", 257 * 3)   # 3-row blocks
+    a = workloads.generate(w)
+    monkeypatch.setattr(workloads, "_THREADS", 1)
+    b = workloads.generate(w)
+    c = workloads.generate(w, N=7)
+    for k in a:
+        assert (a[k].view(np.uint16) == b[k].view(np.uint16)).all(), k
+        if a[k].ndim == 2:
+            assert (a[k][:7].view(np.uint16) == c[k].view(np.uint16)).all(), k
 
 
 def test_recipe_matches_plain_numpy():
     w = workloads.WORKLOADS["ln_128x1024"]
     got = workloads.generate(w)
-    rng = np.random.default_rng(0)
-    X = (0.5 + rng.standard_normal((128, 1024))).astype(np.float16)
-    g = (1 + 0.1 * rng.standard_normal(1024)).astype(np.float16)
-    b = (0.1 * rng.standard_normal(1024)).astype(np.float16)
-    dY = rng.standard_normal((128, 1024)).astype(np.float16)
+    X = (0.5 + np.random.default_rng([0, 0, 0]).standard_normal((128, 1024))).astype(np.float16)
+    g = (1 + 0.1 * np.random.default_rng([0, 1]).standard_normal(1024)).astype(np.float16)
+    b = (0.1 * np.random.default_rng([0, 2]).standard_normal(1024)).astype(np.float16)
+    dY = np.random.default_rng([0, 3, 0]).standard_normal((128, 1024)).astype(np.float16)
     for k, v in (("X", X), ("gamma", g), ("beta", b), ("dY", dY)):
         assert (got[k].view(np.uint16) == v.view(np.uint16)).all(), k
 

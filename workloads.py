@@ -7,11 +7,13 @@ the CPU oracle and the HIP library receive the arrays it returns.
 
 Recipe (fixed, so that every run sees the same bits):
 
-* ``numpy.random.default_rng(seed)`` (PCG64); seed 0 unless a test says
-  otherwise.
-* Tensors are drawn in the order the workload lists them, as float64
-  ``standard_normal`` values, optionally in row chunks (the chunked stream
-  equals the whole-array stream; a CPU test checks this).
+* Tensors are drawn in the order the workload lists them (tensor index t),
+  as float64 ``standard_normal`` values from PCG64 streams: a [D] vector from
+  ``default_rng([seed, t])``; an [N, D] tensor in fixed blocks of
+  ``rows_per_chunk(D)`` rows, block c from ``default_rng([seed, t, c])``.
+  Blocks are independent streams, so they are drawn on several threads and
+  the values do not depend on the thread count; a smaller N yields a prefix
+  of the same rows. Seed 0 unless a test says otherwise.
 * ``loc + scale * z`` is applied in float64, then the value is rounded
   directly to fp16 (round to nearest, ties to even; numpy converts float64 to
   float16 without passing through float32).
@@ -24,14 +26,18 @@ for activations and cotangents of the stated shapes and distributions.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
 from typing import Dict, Optional, Tuple
 
 import numpy as np
 
-# Rows drawn per chunk when materialising large tensors (keeps the float64
-# temporary at 32 MiB for D = 8192).
+# Elements per independently seeded block of an [N, D] tensor (a 32 MiB
+# float64 temporary per block).
 _CHUNK_ELEMS = 1 << 22
+# Worker threads for drawing blocks (numpy releases the GIL while filling).
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
 @dataclass(frozen=True)
@@ -102,38 +108,51 @@ WORKLOADS: Dict[str, Workload] = {
 HEADLINE = "rms_16384x4096"
 
 
-def _fill_rows(rng, out: np.ndarray, spec: TensorSpec, outliers: np.ndarray, gain: float):
+def rows_per_chunk(D: int) -> int:
+    return max(1, _CHUNK_ELEMS // max(int(D), 1))
+
+
+def _fill_rows(seed: int, t: int, out: np.ndarray, spec: TensorSpec, outliers: np.ndarray,
+               gain: float):
     n, d = out.shape
-    rows = max(1, _CHUNK_ELEMS // max(d, 1))
-    buf = np.empty((min(rows, n), d), dtype=np.float64)
-    for r0 in range(0, n, rows):
+    rows = rows_per_chunk(d)
+
+    def block(c: int):
+        r0 = c * rows
         r1 = min(n, r0 + rows)
-        v = buf[: r1 - r0]
-        rng.standard_normal(out=v)
+        v = np.random.default_rng([seed, t, c]).standard_normal((r1 - r0, d))
         v *= spec.scale
         v += spec.loc
         if outliers.size:
             v[:, outliers] *= gain
         out[r0:r1] = v  # float64 -> float16 assignment rounds to nearest even
 
+    nblocks = (n + rows - 1) // rows
+    if nblocks <= 1:
+        for c in range(nblocks):
+            block(c)
+        return
+    with ThreadPoolExecutor(max_workers=min(_THREADS, nblocks)) as ex:
+        list(ex.map(block, range(nblocks)))
+
 
 def generate(w: Workload, seed: int = 0, N: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Materialise every input tensor of ``w`` as contiguous fp16 numpy arrays.
 
-    ``N`` overrides the row count (same distributions, same draw order), used
-    by tests that want a workload's statistics at a smaller size.
+    ``N`` overrides the row count (same distributions; the rows are a prefix
+    of the full workload's rows).
     """
     n = w.N if N is None else int(N)
-    rng = np.random.default_rng(seed)
     outliers = w.outlier_channels()
     out: Dict[str, np.ndarray] = {}
-    for spec in w.tensors:
+    for t, spec in enumerate(w.tensors):
         if spec.per_row:
             a = np.empty((n, w.D), dtype=np.float16)
-            _fill_rows(rng, a, spec, outliers if spec.name == "X" else np.zeros(0, np.int64),
+            _fill_rows(seed, t, a, spec, outliers if spec.name == "X" else np.zeros(0, np.int64),
                        w.outlier_gain)
         else:
-            a = (spec.loc + spec.scale * rng.standard_normal(w.D)).astype(np.float16)
+            z = np.random.default_rng([seed, t]).standard_normal(w.D)
+            a = (spec.loc + spec.scale * z).astype(np.float16)
         out[spec.name] = a
     return out
 
