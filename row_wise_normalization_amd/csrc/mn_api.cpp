@@ -154,7 +154,6 @@ mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, void* ws
     a.N = N;
     a.D = (int32_t)D;
     a.Dp = plan.Dp;
-    a.rows_per_block = plan.rows_per_block;
     return device_status(mn::launch_backward_rows(kind, plan, a, as_stream(stream)));
 }
 

@@ -40,7 +40,6 @@ struct BwdArgs {
     int64_t N;
     int32_t D;
     int32_t Dp;              // partial row stride (D rounded up to 4)
-    int64_t rows_per_block;
 };
 
 // Column-reduce (stage 2) arguments.
@@ -71,7 +70,6 @@ struct FwdPlan {
 struct BwdPlan {
     Variant v;
     int64_t P;               // workgroups == partial rows
-    int64_t rows_per_block;
     int32_t Dp;
     size_t shmem;            // dynamic LDS bytes of the block-level fold
 };

@@ -19,8 +19,9 @@ constexpr int kReduceCQ = 16;  // 64 columns per block, 64 segments
 // Chosen by the smallest max_d >= D. Shapes come from timing sweeps on
 // MI355X at 16384x4096, 32768x8192 and 1048576x128: the forward runs one
 // tile per workgroup (many small workgroups keep the most reads in flight);
-// the backward runs fewer, long-lived workgroups (each owns one partial row
-// of dgamma) and prefetches the next tile. Non-temporal stores throughout.
+// the backward runs 256 long-lived workgroups (each owns one partial row of
+// dgamma and the tiles b, b+256, ...) and prefetches its next tile.
+// Non-temporal stores throughout.
 //
 // Forward, 128-bit path (D % 8 == 0).
 //   id   T  VEC CPT  U  BLOCK  PF NT  max_d
@@ -40,14 +41,14 @@ constexpr int kReduceCQ = 16;  // 64 columns per block, 64 segments
     X(10, 512, 1, 16, 1, 512, 0, 1, 8192)
 
 #define MN_BWD_VEC_TABLE(X)                  \
-    X(0, 8, 8, 1, 8, 256, 1, 1, 64)          \
-    X(1, 16, 8, 1, 8, 256, 1, 1, 128)        \
+    X(0, 8, 8, 1, 4, 256, 1, 1, 64)          \
+    X(1, 16, 8, 1, 4, 256, 1, 1, 128)        \
     X(2, 32, 8, 1, 4, 256, 1, 1, 256)        \
     X(3, 64, 8, 1, 2, 256, 1, 1, 512)        \
     X(4, 128, 8, 1, 1, 512, 1, 1, 1024)      \
     X(5, 256, 8, 1, 1, 512, 1, 1, 2048)      \
-    X(6, 256, 8, 2, 1, 512, 1, 1, 4096)      \
-    X(7, 1024, 8, 1, 1, 1024, 1, 1, 8192)
+    X(6, 512, 8, 1, 1, 512, 1, 1, 4096)      \
+    X(7, 512, 8, 2, 1, 512, 1, 1, 8192)
 #define MN_BWD_GEN_TABLE(X)                  \
     X(8, 64, 1, 16, 1, 256, 1, 1, 1024)      \
     X(9, 256, 1, 16, 1, 256, 1, 1, 4096)     \
@@ -113,9 +114,13 @@ hipError_t launch_bwd_kind(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Workgroups (= partial rows) of the backward: one long-lived workgroup per
-// CU of the 256 (two for the widest fused-add rows, whose 1024-lane
-// workgroups are shorter-lived), each owning a contiguous range of rows.
-int64_t bwd_blocks(int kind, int32_t D) { return (kind == ADD && D > 4096) ? 512 : 256; }
+// CU of the 256, never more than there are rows.
+int64_t bwd_blocks(int kind, int32_t D)
+{
+    (void)kind;
+    (void)D;
+    return 256;
+}
 
 }  // namespace
 
@@ -123,8 +128,7 @@ int32_t partial_stride(int32_t D) { return (D + 3) & ~3; }
 
 int64_t bwd_partial_rows(int kind, int64_t N, int32_t D)
 {
-    const int64_t rb = ceil_div(N, bwd_blocks(kind, D));
-    return ceil_div(N, rb);
+    return N < bwd_blocks(kind, D) ? N : bwd_blocks(kind, D);
 }
 
 FwdPlan plan_forward(int kind, int64_t N, int32_t D, bool vec_ok)
@@ -142,8 +146,7 @@ BwdPlan plan_backward(int kind, int64_t N, int32_t D, bool vec_ok)
 {
     BwdPlan p;
     p.v = vec_ok ? pick(kBwdVec, D) : pick(kBwdGen, D);
-    p.rows_per_block = ceil_div(N, bwd_blocks(kind, D));
-    p.P = ceil_div(N, p.rows_per_block);
+    p.P = bwd_partial_rows(kind, N, D);
     p.Dp = partial_stride(D);
     const int rpb = p.v.BLOCK / p.v.T;
     p.shmem = (rpb > 1) ? (size_t)D * sizeof(float) * (kind == LN ? 2 : 1) : 0;

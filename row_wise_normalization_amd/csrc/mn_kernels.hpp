@@ -16,11 +16,14 @@
 //     chunks a lane owns are the same in every row. VEC = 8 (one 128-bit
 //     load per chunk) needs D % 8 == 0 and 16-byte aligned rows; VEC = 1 is
 //     the element-wise path for every other call.
-//   * Each workgroup owns one contiguous range of rows and walks it in tiles
-//     of RPB*U rows (RPB row groups per workgroup, U rows per group per
-//     step). With PF = 1 the loads of the next tile are issued before the
-//     current tile is reduced, so HBM reads stay in flight while a wave
-//     reduces and writes.
+//   * Rows are processed in tiles of RPB*U rows (RPB row groups per
+//     workgroup, U rows per group per step). The forward gives each
+//     workgroup a contiguous range of rows (one tile in the shipped plans);
+//     the backward gives workgroup b the tiles b, b+P, b+2P, ..., so the
+//     workgroups in flight always cover one contiguous band of rows. With
+//     PF = 1 the loads of the next tile are issued before the current tile
+//     is reduced, so HBM reads stay in flight while a wave reduces and
+//     writes.
 //   * Row sums are reduced inside a wave by DPP (quad permutes, half-row and
 //     row mirrors) and lane exchanges across 16-lane rows; row groups wider
 //     than a wave combine their per-wave sums through LDS in wave order.
@@ -337,8 +340,12 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
     const int g = tid / T;
     const int l = tid % T;
     const int D = a.D;
-    const int64_t begin = (int64_t)blockIdx.x * a.rows_per_block;
-    const int64_t end = min(a.N, begin + a.rows_per_block);
+    // Workgroup b owns tiles b, b + P, b + 2P, ... (P = gridDim.x): a fixed
+    // set of rows, so its dgamma partial is reproducible, while the P
+    // workgroups running together touch one contiguous band of rows.
+    const int64_t end = a.N;
+    const int64_t ntiles = (a.N + TILE - 1) / TILE;
+    const int64_t tstride = (int64_t)gridDim.x * TILE;
 
     int coff[CPT];
     bool cval[CPT];
@@ -385,10 +392,12 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
     const float fD = (float)D;
     int phase = 0;
     Tile cur;
-    if constexpr (PF) load_tile(cur, begin);
-    for (int64_t base = begin; base < end; base += TILE) {
+    const int64_t first = (int64_t)blockIdx.x * TILE;
+    const int64_t stop = ntiles * TILE;  // uniform loop bound for the workgroup
+    if constexpr (PF) load_tile(cur, first);
+    for (int64_t base = first; base < stop; base += tstride) {
         Tile nxt;
-        if constexpr (PF) load_tile(nxt, base + TILE);
+        if constexpr (PF) load_tile(nxt, base + tstride);
         else load_tile(cur, base);
 
         // c1 = sum(g * xhat), c2 = sum(g), g = dY * gamma

@@ -125,8 +125,8 @@ def test_workspace_bytes():
         for N, D in ((1, 1), (17, 257), (16384, 4096), (1048576, 128), (32768, 8192)):
             b = mn.workspace_bytes(kind, N, D)
             assert b > 0 and b % 16 == 0
-            # at most 512 partial rows of round_up(D, 4) floats (two arrays for LayerNorm)
-            assert b <= 512 * ((D + 3) // 4 * 4) * 4 * (2 if kind == mn.MN_LAYERNORM else 1)
+            # at most 256 partial rows of round_up(D, 4) floats (two arrays for LayerNorm)
+            assert b <= 256 * ((D + 3) // 4 * 4) * 4 * (2 if kind == mn.MN_LAYERNORM else 1)
     assert mn.workspace_bytes(3, 16, 64) == 0
 
 
