@@ -16,40 +16,65 @@ constexpr int kReduceCQ = 16;  // 64 columns per block, 64 segments
 // Variant tables.
 // ---------------------------------------------------------------------------
 
-// Chosen by the smallest max_d >= D. Shapes come from timing sweeps on
-// MI355X at 16384x4096, 32768x8192 and 1048576x128: the forward runs one
-// tile per workgroup (many small workgroups keep the most reads in flight);
-// the backward runs 256 long-lived workgroups (each owns one partial row of
-// dgamma and the tiles b, b+256, ...) and prefetches its next tile.
-// Non-temporal stores throughout.
+// Variant tables, one per norm kind and direction; a row is chosen by the
+// smallest max_d >= D. Shapes come from timing sweeps on MI355X at
+// 16384x4096, 32768x8192 and 1048576x128:
+//   * the forward runs one tile per workgroup (many small workgroups keep
+//     the most reads in flight);
+//   * the backward runs 256 long-lived workgroups (each owns one partial
+//     row of dgamma and the tiles b, b+256, ...), prefetches its next tile
+//     and keeps two rows per row group in flight;
+//   * streamed outputs use non-temporal stores (NT bit 0) and streamed
+//     inputs non-temporal loads (NT bit 1), except the LayerNorm forward,
+//     which measured slower with non-temporal loads.
+// Ids are unique within a kind; 8..10 are the element-wise variants (any D,
+// any alignment) shared by all kinds.
 //
-// Forward, 128-bit path (D % 8 == 0).
 //   id   T  VEC CPT  U  BLOCK  PF NT  max_d
-#define MN_FWD_VEC_TABLE(X)                  \
+#define MN_FWD_RMS(X)                        \
+    X(0, 8, 8, 1, 4, 256, 0, 3, 64)          \
+    X(1, 16, 8, 1, 2, 256, 0, 3, 128)        \
+    X(2, 32, 8, 1, 2, 256, 0, 3, 256)        \
+    X(3, 64, 8, 1, 2, 256, 0, 3, 512)        \
+    X(4, 128, 8, 1, 1, 256, 0, 3, 1024)      \
+    X(5, 256, 8, 1, 1, 256, 0, 3, 2048)      \
+    X(6, 256, 8, 2, 1, 256, 0, 3, 4096)      \
+    X(7, 1024, 8, 1, 1, 1024, 0, 3, 8192)
+#define MN_FWD_LN(X)                         \
     X(0, 8, 8, 1, 4, 256, 0, 1, 64)          \
     X(1, 16, 8, 1, 2, 256, 0, 1, 128)        \
     X(2, 32, 8, 1, 2, 256, 0, 1, 256)        \
     X(3, 64, 8, 1, 2, 256, 0, 1, 512)        \
     X(4, 128, 8, 1, 1, 256, 0, 1, 1024)      \
     X(5, 256, 8, 1, 1, 256, 0, 1, 2048)      \
-    X(6, 256, 8, 2, 1, 256, 0, 1, 4096)      \
-    X(7, 512, 8, 2, 1, 512, 0, 1, 8192)
-// Element-wise path (any D, any alignment).
-#define MN_FWD_GEN_TABLE(X)                  \
+    X(6, 256, 8, 2, 2, 256, 0, 1, 4096)      \
+    X(7, 1024, 8, 1, 1, 1024, 0, 1, 8192)
+#define MN_FWD_ADD(X) MN_FWD_RMS(X)
+#define MN_FWD_GEN(X)                        \
     X(8, 64, 1, 16, 1, 256, 0, 1, 1024)      \
     X(9, 256, 1, 16, 1, 256, 0, 1, 4096)     \
     X(10, 512, 1, 16, 1, 512, 0, 1, 8192)
 
-#define MN_BWD_VEC_TABLE(X)                  \
-    X(0, 8, 8, 1, 4, 256, 1, 1, 64)          \
-    X(1, 16, 8, 1, 4, 256, 1, 1, 128)        \
-    X(2, 32, 8, 1, 4, 256, 1, 1, 256)        \
-    X(3, 64, 8, 1, 2, 256, 1, 1, 512)        \
-    X(4, 128, 8, 1, 1, 512, 1, 1, 1024)      \
-    X(5, 256, 8, 1, 1, 512, 1, 1, 2048)      \
-    X(6, 512, 8, 1, 1, 512, 1, 1, 4096)      \
-    X(7, 512, 8, 2, 1, 512, 1, 1, 8192)
-#define MN_BWD_GEN_TABLE(X)                  \
+#define MN_BWD_RMS(X)                        \
+    X(0, 8, 8, 1, 4, 256, 1, 3, 64)          \
+    X(1, 16, 8, 1, 4, 256, 1, 3, 128)        \
+    X(2, 32, 8, 1, 4, 256, 1, 3, 256)        \
+    X(3, 64, 8, 1, 2, 256, 1, 3, 512)        \
+    X(4, 128, 8, 1, 2, 512, 1, 3, 1024)      \
+    X(5, 256, 8, 1, 2, 512, 1, 3, 2048)      \
+    X(6, 512, 8, 1, 2, 512, 1, 3, 4096)      \
+    X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
+#define MN_BWD_LN(X)                         \
+    X(0, 8, 8, 1, 4, 256, 1, 3, 64)          \
+    X(1, 16, 8, 1, 4, 256, 1, 3, 128)        \
+    X(2, 32, 8, 1, 4, 256, 1, 3, 256)        \
+    X(3, 64, 8, 1, 2, 256, 1, 3, 512)        \
+    X(4, 64, 8, 2, 2, 256, 1, 3, 1024)       \
+    X(5, 128, 8, 2, 2, 512, 1, 3, 2048)      \
+    X(6, 256, 8, 2, 2, 512, 1, 3, 4096)      \
+    X(7, 512, 8, 2, 1, 512, 1, 3, 8192)
+#define MN_BWD_ADD(X) MN_BWD_RMS(X)
+#define MN_BWD_GEN(X)                        \
     X(8, 64, 1, 16, 1, 256, 1, 1, 1024)      \
     X(9, 256, 1, 16, 1, 256, 1, 1, 4096)     \
     X(10, 512, 1, 16, 1, 512, 1, 1, 8192)
@@ -60,10 +85,10 @@ struct VariantRow {
 };
 
 #define MN_ROW(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) {{id, T, VEC, CPT, U, BLOCK}, MAXD},
-const VariantRow kFwdVec[] = {MN_FWD_VEC_TABLE(MN_ROW)};
-const VariantRow kFwdGen[] = {MN_FWD_GEN_TABLE(MN_ROW)};
-const VariantRow kBwdVec[] = {MN_BWD_VEC_TABLE(MN_ROW)};
-const VariantRow kBwdGen[] = {MN_BWD_GEN_TABLE(MN_ROW)};
+const VariantRow kFwdVec[3][8] = {{MN_FWD_RMS(MN_ROW)}, {MN_FWD_LN(MN_ROW)}, {MN_FWD_ADD(MN_ROW)}};
+const VariantRow kBwdVec[3][8] = {{MN_BWD_RMS(MN_ROW)}, {MN_BWD_LN(MN_ROW)}, {MN_BWD_ADD(MN_ROW)}};
+const VariantRow kFwdGen[] = {MN_FWD_GEN(MN_ROW)};
+const VariantRow kBwdGen[] = {MN_BWD_GEN(MN_ROW)};
 #undef MN_ROW
 
 template <size_t K>
@@ -81,35 +106,72 @@ hipError_t launch(Kernel k, dim3 grid, dim3 block, size_t shmem, hipStream_t s, 
     return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, shmem, s);
 }
 
-template <int KIND>
-hipError_t launch_fwd_kind(const FwdPlan& p, const FwdArgs& a, hipStream_t s)
-{
-    const dim3 grid((unsigned)p.grid);
-    switch (p.v.id) {
-#define MN_CASE(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) \
-    case id:                                             \
+#define MN_FWD_CASE(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) \
+    case id:                                                 \
         return launch(fwd_kernel<KIND, T, VEC, CPT, U, BLOCK, PF, NT>, grid, dim3(BLOCK), 0, s, a);
-        MN_FWD_VEC_TABLE(MN_CASE)
-        MN_FWD_GEN_TABLE(MN_CASE)
-#undef MN_CASE
-    }
+#define MN_BWD_CASE(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) \
+    case id:                                                 \
+        return launch(bwd_kernel<KIND, T, VEC, CPT, U, BLOCK, PF, NT>, grid, dim3(BLOCK), p.shmem, s, a);
+
+template <int KIND> hipError_t launch_fwd_kind(const FwdPlan& p, const FwdArgs& a, hipStream_t s);
+template <int KIND> hipError_t launch_bwd_kind(const BwdPlan& p, const BwdArgs& a, hipStream_t s);
+
+template <>
+hipError_t launch_fwd_kind<RMS>(const FwdPlan& p, const FwdArgs& a, hipStream_t s)
+{
+    constexpr int KIND = RMS;
+    const dim3 grid((unsigned)p.grid);
+    switch (p.v.id) { MN_FWD_RMS(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
     return hipErrorInvalidValue;
 }
 
-template <int KIND>
-hipError_t launch_bwd_kind(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
+template <>
+hipError_t launch_fwd_kind<LN>(const FwdPlan& p, const FwdArgs& a, hipStream_t s)
 {
-    const dim3 grid((unsigned)p.P);
-    switch (p.v.id) {
-#define MN_CASE(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) \
-    case id:                                             \
-        return launch(bwd_kernel<KIND, T, VEC, CPT, U, BLOCK, PF, NT>, grid, dim3(BLOCK), p.shmem, s, a);
-        MN_BWD_VEC_TABLE(MN_CASE)
-        MN_BWD_GEN_TABLE(MN_CASE)
-#undef MN_CASE
-    }
+    constexpr int KIND = LN;
+    const dim3 grid((unsigned)p.grid);
+    switch (p.v.id) { MN_FWD_LN(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
     return hipErrorInvalidValue;
 }
+
+template <>
+hipError_t launch_fwd_kind<ADD>(const FwdPlan& p, const FwdArgs& a, hipStream_t s)
+{
+    constexpr int KIND = ADD;
+    const dim3 grid((unsigned)p.grid);
+    switch (p.v.id) { MN_FWD_ADD(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
+    return hipErrorInvalidValue;
+}
+
+template <>
+hipError_t launch_bwd_kind<RMS>(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
+{
+    constexpr int KIND = RMS;
+    const dim3 grid((unsigned)p.P);
+    switch (p.v.id) { MN_BWD_RMS(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
+    return hipErrorInvalidValue;
+}
+
+template <>
+hipError_t launch_bwd_kind<LN>(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
+{
+    constexpr int KIND = LN;
+    const dim3 grid((unsigned)p.P);
+    switch (p.v.id) { MN_BWD_LN(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
+    return hipErrorInvalidValue;
+}
+
+template <>
+hipError_t launch_bwd_kind<ADD>(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
+{
+    constexpr int KIND = ADD;
+    const dim3 grid((unsigned)p.P);
+    switch (p.v.id) { MN_BWD_ADD(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
+    return hipErrorInvalidValue;
+}
+
+#undef MN_FWD_CASE
+#undef MN_BWD_CASE
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -133,9 +195,8 @@ int64_t bwd_partial_rows(int kind, int64_t N, int32_t D)
 
 FwdPlan plan_forward(int kind, int64_t N, int32_t D, bool vec_ok)
 {
-    (void)kind;
     FwdPlan p;
-    p.v = vec_ok ? pick(kFwdVec, D) : pick(kFwdGen, D);
+    p.v = vec_ok ? pick(kFwdVec[kind], D) : pick(kFwdGen, D);
     // one tile of RPB*U rows per workgroup
     p.rows_per_block = (int64_t)(p.v.BLOCK / p.v.T) * p.v.U;
     p.grid = ceil_div(N, p.rows_per_block);
@@ -145,7 +206,7 @@ FwdPlan plan_forward(int kind, int64_t N, int32_t D, bool vec_ok)
 BwdPlan plan_backward(int kind, int64_t N, int32_t D, bool vec_ok)
 {
     BwdPlan p;
-    p.v = vec_ok ? pick(kBwdVec, D) : pick(kBwdGen, D);
+    p.v = vec_ok ? pick(kBwdVec[kind], D) : pick(kBwdGen, D);
     p.P = bwd_partial_rows(kind, N, D);
     p.Dp = partial_stride(D);
     const int rpb = p.v.BLOCK / p.v.T;

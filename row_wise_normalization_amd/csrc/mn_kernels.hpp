@@ -34,8 +34,9 @@
 //     fp32 partial row per workgroup. A second kernel reduces the partial
 //     rows of each column in a fixed order. No floating-point atomics
 //     anywhere, so every result is bitwise reproducible.
-//   * NT = 1 writes the streamed outputs (Y, H, dX) with non-temporal
-//     stores, which are not kept in the caches.
+//   * NT is a bit mask: bit 0 writes the streamed outputs (Y, H, dX) with
+//     non-temporal stores, bit 1 reads the streamed inputs (X, R, dY, dH)
+//     with non-temporal loads; neither is kept in the caches.
 #pragma once
 
 #include "mn_internal.hpp"
@@ -65,11 +66,21 @@ __device__ __forceinline__ typename HVec<VEC>::type hload(const _Float16* p)
     return *reinterpret_cast<const typename HVec<VEC>::type*>(p);
 }
 
+// Load of a streamed input row (read once per launch); NT bit 1 marks it
+// non-temporal so it does not displace reusable lines in the caches.
+template <int VEC, int NT>
+__device__ __forceinline__ typename HVec<VEC>::type sload(const _Float16* p)
+{
+    typedef typename HVec<VEC>::type HV;
+    if constexpr ((NT & 2) != 0) return __builtin_nontemporal_load(reinterpret_cast<const HV*>(p));
+    else return *reinterpret_cast<const HV*>(p);
+}
+
 template <int VEC, int NT>
 __device__ __forceinline__ void hstore(_Float16* p, const typename HVec<VEC>::type& v)
 {
     typedef typename HVec<VEC>::type HV;
-    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<HV*>(p));
+    if constexpr ((NT & 1) != 0) __builtin_nontemporal_store(v, reinterpret_cast<HV*>(p));
     else *reinterpret_cast<HV*>(p) = v;
 }
 
@@ -211,8 +222,8 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 const bool ok = row < end && cval[k];
-                t.x[u][k] = ok ? hload<VEC>(a.X + ro + coff[k]) : hzero<VEC>();
-                if constexpr (KIND == ADD) t.r[u][k] = ok ? hload<VEC>(a.R + ro + coff[k]) : hzero<VEC>();
+                t.x[u][k] = ok ? sload<VEC, NT>(a.X + ro + coff[k]) : hzero<VEC>();
+                if constexpr (KIND == ADD) t.r[u][k] = ok ? sload<VEC, NT>(a.R + ro + coff[k]) : hzero<VEC>();
             }
         }
     };
@@ -382,9 +393,9 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 const bool ok = rok && cval[k];
-                t.x[u][k] = ok ? hload<VEC>(a.X + ro + coff[k]) : hzero<VEC>();
-                if constexpr (KIND == ADD) t.r[u][k] = ok ? hload<VEC>(a.R + ro + coff[k]) : hzero<VEC>();
-                t.dy[u][k] = ok ? hload<VEC>(a.dY + ro + coff[k]) : hzero<VEC>();
+                t.x[u][k] = ok ? sload<VEC, NT>(a.X + ro + coff[k]) : hzero<VEC>();
+                if constexpr (KIND == ADD) t.r[u][k] = ok ? sload<VEC, NT>(a.R + ro + coff[k]) : hzero<VEC>();
+                t.dy[u][k] = ok ? sload<VEC, NT>(a.dY + ro + coff[k]) : hzero<VEC>();
             }
         }
     };
@@ -443,7 +454,7 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                 const bool ok = rok && cval[k];
                 HV dh = hzero<VEC>();
                 if constexpr (KIND == ADD) {
-                    if (ok && a.dH != nullptr) dh = hload<VEC>(a.dH + ro + coff[k]);
+                    if (ok && a.dH != nullptr) dh = sload<VEC, NT>(a.dH + ro + coff[k]);
                 }
                 HV o;
 #pragma unroll
