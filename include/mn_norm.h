@@ -83,8 +83,8 @@ typedef enum {
 mn_status mn_rmsnorm_forward(const mn_f16* X, const mn_f16* gamma, mn_f16* Y, float* rstd,
                              int64_t N, int64_t D, float eps, void* stream);
 
-/* RMSNorm backward. [meTile] contract (norm_backward differentiates the
- * real-valued formula using the saved FP32 statistics); [tensorcore]
+/* RMSNorm backward. [meTile] contract (the derivative of the exact formula,
+ * evaluated with the forward's saved fp32 statistics); [tensorcore]
  * tc_rmsnorm_backward. With xhat = X*rstd and g = dY*gamma:
  *   dX[i,j]   = fp16(rstd[i] * (g[i,j] - xhat[i,j] * mean_j(g*xhat)))
  *   dgamma[j] = sum_i dY[i,j] * xhat[i,j]      (fp32, overwritten)
@@ -132,9 +132,9 @@ mn_status mn_add_rmsnorm_forward(const mn_f16* X, const mn_f16* R, const mn_f16*
                                  int64_t N, int64_t D, float eps, void* stream);
 
 /* Fused add backward with both output cotangents ([meTile] contract: the
- * residual-output cotangent defaults to zero and is added to both the source
- * and the residual gradient). The gradient is taken at the unrounded sum
- * s = X + R, re-formed from X and R (H is not read):
+ * residual-output cotangent is zero when absent, and its contribution goes
+ * into both the source and the residual gradient). The gradient is taken at
+ * the unrounded sum s = X + R, re-formed from X and R (H is not read):
  *   dX[i,j] = dR[i,j] = fp16(dH[i,j] + rstd*(g - shat * mean_j(g*shat)))
  * with shat = s*rstd, g = dY*gamma; dH == NULL means a zero cotangent. One
  * output array serves as both dX and dR.

@@ -20,10 +20,10 @@
  * Outputs are doubles; rounding to binary16 for comparison is a separate step
  * (mno_f64_to_f16, round to nearest, ties to even, straight from double).
  *
- * Backward functions recompute their statistics in fp64 from X; they take no
- * saved statistics, because the derivative of the real-valued formula is what
- * is defined ([meTile] contract: the backward differentiates the real-valued
- * formula and there is no gradient with respect to epsilon).
+ * Backward functions recompute their statistics in fp64 from X and take no
+ * saved statistics: what they define is the exact derivative of the forward
+ * formula with respect to its inputs and parameters (the [meTile] contract
+ * ignores the rounding of casts and gives no epsilon gradient).
  *
  * Pins (tests/test_oracle_pins.py): torch fp64 layer_norm / rms_norm and
  * autograd on random inputs, central finite differences, closed forms for
@@ -269,8 +269,8 @@ static int ln_forward(operand X, operand G, operand B, int64_t N, int64_t D, dou
  * ------------------------------------------------------------------------- */
 
 /* RMSNorm backward at x (or at the unrounded sum x + residual when R is
- * present, [meTile] contract: the backward differentiates the real-valued
- * formula). For the fused add the residual-output cotangent dH (zero when
+ * present: the [meTile] contract takes the derivative of the exact formula,
+ * not of the rounded H). For the fused add the residual-output cotangent dH (zero when
  * absent) is added, and the result is both the source and the residual
  * gradient ([meTile] contract: its contribution goes to both). */
 static int rms_backward(operand X, operand R, operand G, operand DY, operand DH,
