@@ -1,0 +1,64 @@
+/*
+ * abi_check.c -- compiles against include/mn_norm.h as plain C (no HIP
+ * headers), links libmn_norm.so and exercises the host-side validation paths,
+ * which return before anything touches a GPU. Exit status 0 on success.
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "mn_norm.h"
+
+static int failures = 0;
+
+#define EXPECT(expr, want)                                                        \
+    do {                                                                          \
+        mn_status got_ = (expr);                                                  \
+        if (got_ != (want)) {                                                     \
+            fprintf(stderr, "%s:%d: %s -> %d (%s), want %d\n", __FILE__, __LINE__, \
+                    #expr, (int)got_, mn_status_string(got_), (int)(want));        \
+            ++failures;                                                           \
+        }                                                                         \
+    } while (0)
+
+int main(void)
+{
+    /* placeholder device addresses, far apart; validation never dereferences */
+    mn_f16* X = (mn_f16*)(uintptr_t)0x100000;
+    mn_f16* G = (mn_f16*)(uintptr_t)0x20000000;
+    mn_f16* Y = (mn_f16*)(uintptr_t)0x40000000;
+    float* r = (float*)(uintptr_t)0x60000000;
+    mn_f16* dY = (mn_f16*)(uintptr_t)0x80000000;
+    mn_f16* dX = (mn_f16*)(uintptr_t)0xA0000000;
+    float* dg = (float*)(uintptr_t)0xC0000000;
+    void* ws = (void*)(uintptr_t)0xE0000000;
+    const int64_t N = 64, D = 512;
+
+    size_t need = mn_norm_workspace_bytes(MN_RMSNORM, N, D);
+    if (need == 0 || need % 16 != 0) {
+        fprintf(stderr, "workspace bytes %zu\n", need);
+        ++failures;
+    }
+    if (mn_norm_workspace_bytes(MN_LAYERNORM, N, D) != 2 * need) {
+        fprintf(stderr, "LayerNorm workspace is not two partial arrays\n");
+        ++failures;
+    }
+    EXPECT(mn_rmsnorm_forward(NULL, G, Y, r, N, D, 1e-5f, NULL), MN_ERR_NULL);
+    EXPECT(mn_rmsnorm_forward(X, G, Y, r, 0, D, 1e-5f, NULL), MN_ERR_SHAPE);
+    EXPECT(mn_rmsnorm_forward(X, G, Y, r, N, MN_MAX_COLS + 1, 1e-5f, NULL), MN_ERR_SHAPE);
+    EXPECT(mn_rmsnorm_forward(X, G, Y, r, N, D, -1.0f, NULL), MN_ERR_EPS);
+    EXPECT(mn_rmsnorm_forward(X, G, X, r, N, D, 1e-5f, NULL), MN_ERR_ALIAS);
+    EXPECT(mn_rmsnorm_backward(X, G, r, dY, dX, dg, N, D, ws, need - 16, NULL), MN_ERR_WORKSPACE);
+    EXPECT(mn_rmsnorm_backward(X, G, r, dY, dY, dg, N, D, ws, need, NULL), MN_ERR_ALIAS);
+    EXPECT(mn_layernorm_forward(X, G, NULL, Y, r, r + 4096, N, D, 1e-5f, NULL), MN_ERR_NULL);
+    EXPECT(mn_add_rmsnorm_backward(X, NULL, G, r, dY, NULL, dX, dg, N, D, ws, need, NULL),
+           MN_ERR_NULL);
+    EXPECT(mn_norm_reduce_partials(MN_LAYERNORM, N, D, ws, 2 * need, dg, NULL, NULL), MN_ERR_NULL);
+    if (strlen(mn_status_string(MN_ERR_DEVICE)) == 0) ++failures;
+    if (failures) {
+        fprintf(stderr, "%d failures\n", failures);
+        return 1;
+    }
+    printf("ok\n");
+    return 0;
+}
