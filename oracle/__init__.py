@@ -6,10 +6,11 @@ imports nothing from the product. The arithmetic lives in ``mn_oracle.c``
 (plain C, double precision, one row at a time, sums in ascending order); this
 module builds it with gcc and marshals numpy arrays through ctypes.
 
-Inputs are fp16 numpy arrays (the path's storage type) or, through the
-``*_f64`` functions, float64 arrays (used by the finite-difference pins).
-Outputs are float64 arrays; ``f64_to_f16`` rounds them to fp16 (nearest, ties
-to even, straight from double) for comparison with fp16 results.
+Inputs are numpy arrays whose dtype names their storage type: float16,
+uint16 (bfloat16 bit patterns), float32, or float64 (used by the
+finite-difference pins). Outputs are float64 arrays; ``round_to`` rounds them
+once to a storage type (nearest, ties to even, straight from double) for
+comparison with GPU results.
 """
 from __future__ import annotations
 
@@ -53,8 +54,20 @@ def _nd(X: np.ndarray) -> Tuple[int, int]:
     return int(X.shape[0]), int(X.shape[1])
 
 
+# Storage-type codes of the C oracle (MNO_F16, MNO_BF16, MNO_F32, MNO_F64).
+# bfloat16 arrays are carried as numpy uint16 bit patterns.
+_TYPE = {np.dtype(np.float16): 0, np.dtype(np.uint16): 1, np.dtype(np.float32): 2,
+         np.dtype(np.float64): 3}
+_VP = ctypes.c_void_p
+
+
 class Oracle:
-    """ctypes view of one build of mn_oracle.c."""
+    """ctypes view of one build of mn_oracle.c.
+
+    Inputs are numpy arrays whose dtype names their storage type: float16,
+    uint16 (bfloat16 bit patterns), float32 or float64. X and R share a type,
+    gamma and beta share one, dY and dH share one. ``f64=True`` converts
+    every input to float64 first (used by the finite-difference pins)."""
 
     def __init__(self, lib_path: str = LIB_PATH):
         lib = ctypes.CDLL(lib_path)
@@ -62,54 +75,62 @@ class Oracle:
         lib.mno_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.mno_f64_to_f16.restype = ctypes.c_uint16
         lib.mno_f64_to_f16.argtypes = [_DBL]
-        lib.mno_decode_f16.argtypes = [_P16, _PD, _I64]
-        lib.mno_encode_f16.argtypes = [_PD, _P16, _I64]
-        for suffix, P in (("", _P16), ("_f64", _PD)):
-            sig = {
-                "mno_rmsnorm_forward": [P, P, _I64, _I64, _DBL, _PD, _PD],
-                "mno_layernorm_forward": [P, P, P, _I64, _I64, _DBL, _PD, _PD, _PD],
-                "mno_add_rmsnorm_forward": [P, P, P, _I64, _I64, _DBL, _PD, _PD, _PD],
-                "mno_rmsnorm_backward": [P, P, P, _I64, _I64, _DBL, _PD, _PD],
-                "mno_layernorm_backward": [P, P, P, _I64, _I64, _DBL, _PD, _PD, _PD],
-                "mno_add_rmsnorm_backward": [P, P, P, P, P, _I64, _I64, _DBL, _PD, _PD],
-            }
-            for name, argtypes in sig.items():
-                fn = getattr(lib, name + suffix)
-                fn.argtypes = argtypes
-                fn.restype = ctypes.c_int
+        lib.mno_bf16_to_f64.restype = _DBL
+        lib.mno_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.mno_f64_to_bf16.restype = ctypes.c_uint16
+        lib.mno_f64_to_bf16.argtypes = [_DBL]
+        for name in ("mno_decode_f16", "mno_decode_bf16"):
+            getattr(lib, name).argtypes = [_P16, _PD, _I64]
+        for name in ("mno_encode_f16", "mno_encode_bf16"):
+            getattr(lib, name).argtypes = [_PD, _P16, _I64]
+        I = ctypes.c_int
+        sig = {
+            "mno_rmsnorm_forward_t": [_VP, I, _VP, I, _I64, _I64, _DBL, _PD, _PD],
+            "mno_layernorm_forward_t": [_VP, I, _VP, _VP, I, _I64, _I64, _DBL, _PD, _PD, _PD],
+            "mno_add_rmsnorm_forward_t": [_VP, _VP, I, _VP, I, _I64, _I64, _DBL, _PD, _PD, _PD],
+            "mno_rmsnorm_backward_t": [_VP, I, _VP, I, _VP, I, _I64, _I64, _DBL, _PD, _PD],
+            "mno_layernorm_backward_t": [_VP, I, _VP, I, _VP, I, _I64, _I64, _DBL, _PD, _PD,
+                                         _PD],
+            "mno_add_rmsnorm_backward_t": [_VP, _VP, I, _VP, I, _VP, _VP, I, _I64, _I64, _DBL,
+                                           _PD, _PD],
+        }
+        for name, argtypes in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = argtypes
+            fn.restype = ctypes.c_int
         self.lib = lib
 
     # -- marshalling -------------------------------------------------------
 
     @staticmethod
-    def _in(a: Optional[np.ndarray], f64: bool):
-        if a is None:
-            return None
-        if f64:
-            a = np.ascontiguousarray(a, dtype=np.float64)
-            return a.ctypes.data_as(_PD), a
-        if a.dtype != np.float16 or not a.flags.c_contiguous:
-            raise TypeError("oracle fp16 inputs must be C-contiguous float16 arrays")
-        return a.ctypes.data_as(_P16), a
+    def _group(arrays, f64: bool):
+        """Pointers and the shared storage-type code of one operand group."""
+        keep, ptrs, code = [], [], None
+        for a in arrays:
+            if a is None:
+                ptrs.append(None)
+                continue
+            a = np.ascontiguousarray(a, dtype=np.float64) if f64 else a
+            if not a.flags.c_contiguous or a.dtype not in _TYPE:
+                raise TypeError("oracle inputs must be C-contiguous float16, uint16 (bfloat16), "
+                                "float32 or float64 arrays")
+            c = _TYPE[a.dtype]
+            if code is not None and c != code:
+                raise TypeError("operands of one group must share a storage type")
+            code = c
+            keep.append(a)
+            ptrs.append(a.ctypes.data_as(_VP))
+        return ptrs, (3 if code is None else code), keep
 
-    def _call(self, name: str, f64: bool, ins, tail):
-        fn = getattr(self.lib, name + ("_f64" if f64 else ""))
-        keep = []
-        args = []
-        for a in ins:
-            m = self._in(a, f64)
-            if m is None:
-                args.append(None)
-            else:
-                args.append(m[0])
-                keep.append(m[1])
-        args += [None if t is None else (t.ctypes.data_as(_PD) if isinstance(t, np.ndarray) else t)
-                 for t in tail]
-        rc = fn(*args)
+    @staticmethod
+    def _out(a):
+        return None if a is None else a.ctypes.data_as(_PD)
+
+    def _check(self, name, rc):
         if rc != 0:
             raise RuntimeError(f"{name} returned {rc}")
 
-    # -- binary16 codec ----------------------------------------------------
+    # -- storage-type codecs ----------------------------------------------
 
     def f16_to_f64(self, a: np.ndarray) -> np.ndarray:
         a = np.ascontiguousarray(a, dtype=np.float16)
@@ -124,58 +145,103 @@ class Oracle:
         self.lib.mno_encode_f16(a.ctypes.data_as(_PD), out.ctypes.data_as(_P16), a.size)
         return out.view(np.float16)
 
+    def bf16_to_f64(self, bits: np.ndarray) -> np.ndarray:
+        bits = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(bits.shape, dtype=np.float64)
+        self.lib.mno_decode_bf16(bits.ctypes.data_as(_P16), out.ctypes.data_as(_PD), bits.size)
+        return out
+
+    def f64_to_bf16(self, a: np.ndarray) -> np.ndarray:
+        """Round float64 values to bfloat16 (bit patterns), nearest, ties to even."""
+        a = np.ascontiguousarray(a, dtype=np.float64)
+        out = np.empty(a.shape, dtype=np.uint16)
+        self.lib.mno_encode_bf16(a.ctypes.data_as(_PD), out.ctypes.data_as(_P16), a.size)
+        return out
+
+    def round_to(self, a: np.ndarray, like: np.dtype) -> np.ndarray:
+        """Round float64 values once to the storage type `like` (float16,
+        uint16 = bfloat16 bits, or float32)."""
+        like = np.dtype(like)
+        if like == np.float16:
+            return self.f64_to_f16(a)
+        if like == np.uint16:
+            return self.f64_to_bf16(a)
+        if like == np.float32:
+            return np.ascontiguousarray(a, dtype=np.float64).astype(np.float32)
+        raise TypeError(like)
+
     # -- forward -----------------------------------------------------------
 
     def rmsnorm_forward(self, X, gamma, eps, f64: bool = False):
         """(Y [N, D], rstd [N]), float64."""
         N, D = _nd(X)
+        (x,), tx, k1 = self._group([X], f64)
+        (g,), tg, k2 = self._group([gamma], f64)
         Y = np.empty((N, D)); rstd = np.empty(N)
-        self._call("mno_rmsnorm_forward", f64, (X, gamma), (N, D, float(eps), Y, rstd))
+        self._check("rmsnorm_forward", self.lib.mno_rmsnorm_forward_t(
+            x, tx, g, tg, N, D, float(eps), self._out(Y), self._out(rstd)))
         return Y, rstd
 
     def layernorm_forward(self, X, gamma, beta, eps, f64: bool = False):
         """(Y [N, D], mean [N], rstd [N]), float64."""
         N, D = _nd(X)
+        (x,), tx, k1 = self._group([X], f64)
+        (g, b), tg, k2 = self._group([gamma, beta], f64)
         Y = np.empty((N, D)); mean = np.empty(N); rstd = np.empty(N)
-        self._call("mno_layernorm_forward", f64, (X, gamma, beta),
-                   (N, D, float(eps), Y, mean, rstd))
+        self._check("layernorm_forward", self.lib.mno_layernorm_forward_t(
+            x, tx, g, b, tg, N, D, float(eps), self._out(Y), self._out(mean), self._out(rstd)))
         return Y, mean, rstd
 
     def add_rmsnorm_forward(self, X, R, gamma, eps, f64: bool = False):
-        """(S = x + r unrounded, H = fp16(S), Y, rstd); all float64 but H."""
+        """(S = x + r unrounded, H = S rounded to X's storage type, Y, rstd);
+        S, Y, rstd float64. H is float16 for float16 inputs, bfloat16 bits
+        for uint16 inputs, float32 for float32 inputs, float64 for float64."""
         N, D = _nd(X)
+        (x, r), tx, k1 = self._group([X, R], f64)
+        (g,), tg, k2 = self._group([gamma], f64)
         S = np.empty((N, D)); Y = np.empty((N, D)); rstd = np.empty(N)
-        self._call("mno_add_rmsnorm_forward", f64, (X, R, gamma),
-                   (N, D, float(eps), S, Y, rstd))
-        return S, self.f64_to_f16(S), Y, rstd
+        self._check("add_rmsnorm_forward", self.lib.mno_add_rmsnorm_forward_t(
+            x, r, tx, g, tg, N, D, float(eps), self._out(S), self._out(Y), self._out(rstd)))
+        H = S if tx == 3 else self.round_to(S, {0: np.float16, 1: np.uint16, 2: np.float32}[tx])
+        return S, H, Y, rstd
 
     # -- backward ----------------------------------------------------------
 
     def rmsnorm_backward(self, X, gamma, dY, eps, want_dx: bool = True, f64: bool = False):
         """(dX [N, D] or None, dgamma [D]), float64."""
         N, D = _nd(X)
+        (x,), tx, k1 = self._group([X], f64)
+        (g,), tg, k2 = self._group([gamma], f64)
+        (dy,), ty, k3 = self._group([dY], f64)
         dX = np.empty((N, D)) if want_dx else None
         dg = np.empty(D)
-        self._call("mno_rmsnorm_backward", f64, (X, gamma, dY), (N, D, float(eps), dX, dg))
+        self._check("rmsnorm_backward", self.lib.mno_rmsnorm_backward_t(
+            x, tx, g, tg, dy, ty, N, D, float(eps), self._out(dX), self._out(dg)))
         return dX, dg
 
     def layernorm_backward(self, X, gamma, dY, eps, want_dx: bool = True, f64: bool = False):
         """(dX or None, dgamma, dbeta), float64."""
         N, D = _nd(X)
+        (x,), tx, k1 = self._group([X], f64)
+        (g,), tg, k2 = self._group([gamma], f64)
+        (dy,), ty, k3 = self._group([dY], f64)
         dX = np.empty((N, D)) if want_dx else None
         dg = np.empty(D); db = np.empty(D)
-        self._call("mno_layernorm_backward", f64, (X, gamma, dY),
-                   (N, D, float(eps), dX, dg, db))
+        self._check("layernorm_backward", self.lib.mno_layernorm_backward_t(
+            x, tx, g, tg, dy, ty, N, D, float(eps), self._out(dX), self._out(dg), self._out(db)))
         return dX, dg, db
 
     def add_rmsnorm_backward(self, X, R, gamma, dY, dH, eps, want_dx: bool = True,
                              f64: bool = False):
         """(dX = dR or None, dgamma), float64. dH None means a zero cotangent."""
         N, D = _nd(X)
+        (x, r), tx, k1 = self._group([X, R], f64)
+        (g,), tg, k2 = self._group([gamma], f64)
+        (dy, dh), ty, k3 = self._group([dY, dH], f64)
         dX = np.empty((N, D)) if want_dx else None
         dg = np.empty(D)
-        self._call("mno_add_rmsnorm_backward", f64, (X, R, gamma, dY, dH),
-                   (N, D, float(eps), dX, dg))
+        self._check("add_rmsnorm_backward", self.lib.mno_add_rmsnorm_backward_t(
+            x, r, tx, g, tg, dy, dh, ty, N, D, float(eps), self._out(dX), self._out(dg)))
         return dX, dg
 
 

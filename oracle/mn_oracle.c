@@ -16,9 +16,10 @@
  *   [tensorcore] "Training kernels", sections "RMSnorm -- Llama-style" (Math)
  *            and "LayerNorm -- standard" (buffers and saved statistics).
  *
- * Inputs are IEEE binary16 bit patterns (uint16_t), widened exactly to double.
- * Outputs are doubles; rounding to binary16 for comparison is a separate step
- * (mno_f64_to_f16, round to nearest, ties to even, straight from double).
+ * Inputs are IEEE binary16 or bfloat16 bit patterns (uint16_t), binary32 or
+ * binary64 values, widened exactly to double. Outputs are doubles; rounding
+ * to a storage type for comparison is a separate step (mno_f64_to_f16,
+ * mno_f64_to_bf16: round to nearest, ties to even, straight from double).
  *
  * Backward functions recompute their statistics in fp64 from X and take no
  * saved statistics: what they define is the exact derivative of the forward
@@ -28,8 +29,10 @@
  * Pins (tests/test_oracle_pins.py): torch fp64 layer_norm / rms_norm and
  * autograd on random inputs, central finite differences, closed forms for
  * constant and zero rows, the LayerNorm worked example of the [meTile]
- * contract, row invariants, and the binary16 codec against numpy over every
- * bit pattern. No function here is "parity unpinned".
+ * contract, row invariants, the binary16 codec against numpy and the
+ * bfloat16 codec against torch over every bit pattern, and agreement of the
+ * typed entry points across storage types on values all types represent.
+ * No function here is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -72,29 +75,72 @@ static double round_half_even(double q)
     return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
 }
 
-uint16_t mno_f64_to_f16(double v)
+/* Round a double to a binary format with `mbits` stored fraction bits and
+ * exponents emin..emax (normal range), to nearest with ties to even, and
+ * return its bit pattern (1 sign bit, then exponent with bias -emin + 1,
+ * then fraction), as IEEE 754 defines binary16 and bfloat16 does binary32's
+ * upper half. Subnormals below 2^emin are multiples of 2^(emin - mbits);
+ * values that round beyond the largest finite number become infinity. */
+static uint32_t encode_binary(double v, int mbits, int emin, int emax)
 {
-    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    const uint32_t inf_exp = (uint32_t)(emax - emin + 2); /* biased exponent of inf */
+    int ewidth = 0;                                        /* exponent field width */
+    while ((1u << ewidth) <= inf_exp) ++ewidth;
+    const uint32_t sign = signbit(v) ? (1u << (mbits + ewidth)) : 0u;
+    const uint32_t inf = inf_exp << mbits;
     double a = fabs(v);
-    if (isnan(v)) return (uint16_t)(sign | 0x7e00);
-    if (isinf(v)) return (uint16_t)(sign | 0x7c00);
+    if (isnan(v)) return sign | inf | (1u << (mbits - 1));
+    if (isinf(v)) return sign | inf;
     if (a == 0.0) return sign;
     int e2;
     frexp(a, &e2);          /* a = m * 2^e2, m in [0.5, 1) */
     int e = e2 - 1;         /* a in [2^e, 2^(e+1)) */
-    if (e < -14) {
-        /* subnormal range: value = q * 2^-24 with q an integer in [0, 1024];
-         * q = 1024 is the smallest normal, whose encoding is also 1024 */
-        double q = round_half_even(ldexp(a, 24));
-        return (uint16_t)(sign | (uint16_t)q);
+    if (e < emin) {
+        /* subnormal range: value = q * 2^(emin - mbits), q an integer in
+         * [0, 2^mbits]; q = 2^mbits is the smallest normal, same encoding */
+        double q = round_half_even(ldexp(a, mbits - emin));
+        return sign | (uint32_t)q;
     }
-    double m = round_half_even(ldexp(a, 10 - e)); /* in [1024, 2048] */
-    if (m == 2048.0) {
-        m = 1024.0;
+    double m = round_half_even(ldexp(a, mbits - e)); /* in [2^mbits, 2^(mbits+1)] */
+    if (m == ldexp(1.0, mbits + 1)) {
+        m = ldexp(1.0, mbits);
         e += 1;
     }
-    if (e > 15) return (uint16_t)(sign | 0x7c00); /* overflow rounds to inf */
-    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(m - 1024.0));
+    if (e > emax) return sign | inf;                  /* overflow rounds to inf */
+    return sign | ((uint32_t)(e - emin + 1) << mbits) | (uint32_t)(m - ldexp(1.0, mbits));
+}
+
+uint16_t mno_f64_to_f16(double v) { return (uint16_t)encode_binary(v, 10, -14, 15); }
+
+/* bfloat16: the upper half of an IEEE binary32 -- 1 sign bit, 8 exponent
+ * bits (bias 127), 7 fraction bits; exponent 0 encodes zero and subnormals
+ * (fraction * 2^-133), exponent 255 infinities and NaNs. */
+double mno_bf16_to_f64(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xff;
+    int f = b & 0x7f;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -133);
+    } else if (e == 255) {
+        v = (f == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(128 + f), e - 134);
+    }
+    return sign ? -v : v;
+}
+
+uint16_t mno_f64_to_bf16(double v) { return (uint16_t)encode_binary(v, 7, -126, 127); }
+
+void mno_decode_bf16(const uint16_t* b, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = mno_bf16_to_f64(b[i]);
+}
+
+void mno_encode_bf16(const double* v, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = mno_f64_to_bf16(v[i]);
 }
 
 void mno_decode_f16(const uint16_t* h, double* out, int64_t n)
@@ -136,39 +182,69 @@ static void ln_stats(const double* x, int64_t D, double eps, double* mean, doubl
     *rstd = 1.0 / sqrt(v / (double)D + eps);
 }
 
-/* Widening table: entry h is mno_f16_to_f64(h), filled on first use so the
- * per-element decode in the row loops is a lookup. */
+/* Widening tables: entry h is mno_f16_to_f64(h) (resp. mno_bf16_to_f64(h)),
+ * filled on first use so the per-element decode in the row loops is a
+ * lookup. */
 static double f16_table[65536];
-static int f16_table_ready = 0;
+static double bf16_table[65536];
+static int tables_ready = 0;
 
-static double widen(uint16_t h)
+static void fill_tables(void)
 {
-    if (!f16_table_ready) {
-        for (int k = 0; k < 65536; ++k) f16_table[k] = mno_f16_to_f64((uint16_t)k);
-        f16_table_ready = 1;
+    if (tables_ready) return;
+    for (int k = 0; k < 65536; ++k) {
+        f16_table[k] = mno_f16_to_f64((uint16_t)k);
+        bf16_table[k] = mno_bf16_to_f64((uint16_t)k);
     }
-    return f16_table[h];
+    tables_ready = 1;
 }
 
-/* An input operand: either binary16 bits or doubles (exactly one of h, d is
- * set), or absent (both NULL). The fp64 entry points let the finite-difference
- * pins perturb inputs by amounts binary16 cannot represent. */
+/* Storage types of an input operand. */
+#define MNO_F16 0
+#define MNO_BF16 1
+#define MNO_F32 2
+#define MNO_F64 3
+
+/* An input operand: a pointer and its storage type, or absent (p == NULL).
+ * The fp64 type lets the finite-difference pins perturb inputs by amounts
+ * no 16-bit type can represent. */
 typedef struct {
-    const uint16_t* h;
-    const double* d;
+    const void* p;
+    int type;
 } operand;
 
-static operand op16(const uint16_t* p) { operand o = {p, NULL}; return o; }
-static operand op64(const double* p) { operand o = {NULL, p}; return o; }
-static int present(operand a) { return a.h != NULL || a.d != NULL; }
+static operand opt(const void* p, int type) { operand o = {p, type}; return o; }
+static operand op16(const uint16_t* p) { return opt(p, MNO_F16); }
+static operand op64(const double* p) { return opt(p, MNO_F64); }
+static int present(operand a) { return a.p != NULL; }
+static int type_ok(int t) { return t == MNO_F16 || t == MNO_BF16 || t == MNO_F32 || t == MNO_F64; }
 
-/* Row i of an [N, D] operand (or the [D] vector when i = 0), widened. */
+/* Row i of an [N, D] operand (or the [D] vector when i = 0), widened exactly
+ * to double. */
 static void get_row(operand a, int64_t i, int64_t D, double* dst)
 {
-    if (a.h) {
-        for (int64_t j = 0; j < D; ++j) dst[j] = widen(a.h[i * D + j]);
-    } else {
-        for (int64_t j = 0; j < D; ++j) dst[j] = a.d[i * D + j];
+    const int64_t o = i * D;
+    switch (a.type) {
+    case MNO_F16: {
+        const uint16_t* h = (const uint16_t*)a.p + o;
+        for (int64_t j = 0; j < D; ++j) dst[j] = f16_table[h[j]];
+        break;
+    }
+    case MNO_BF16: {
+        const uint16_t* b = (const uint16_t*)a.p + o;
+        for (int64_t j = 0; j < D; ++j) dst[j] = bf16_table[b[j]];
+        break;
+    }
+    case MNO_F32: {
+        const float* f = (const float*)a.p + o;
+        for (int64_t j = 0; j < D; ++j) dst[j] = (double)f[j];
+        break;
+    }
+    default: {
+        const double* d = (const double*)a.p + o;
+        for (int64_t j = 0; j < D; ++j) dst[j] = d[j];
+        break;
+    }
     }
 }
 
@@ -192,8 +268,13 @@ static void rows_free(rows* w)
 }
 
 /* The row being normalised: x, or for the fused add the unrounded sum
- * x + residual (exact in double for binary16 operands: both are multiples of
- * 2^-24 below 2^16 in magnitude, so the sum has at most 41 significant bits). */
+ * x + residual. For binary16 operands the double sum is exact (both are
+ * multiples of 2^-24 below 2^16 in magnitude, so the sum has at most 41
+ * significant bits). For bfloat16 and binary32 operands it is exact unless
+ * the exponents differ by more than 45 (resp. 29) binades; then the smaller
+ * operand is below 2^-45 (2^-29) of the larger's unit in the last place, far
+ * from any rounding boundary of the storage type, so rounding the double sum
+ * to the storage type still gives the correctly rounded exact sum. */
 static void source_row(operand X, operand R, int64_t i, int64_t D, rows* w)
 {
     get_row(X, i, D, w->x);
@@ -216,6 +297,7 @@ static int rms_forward(operand X, operand R, operand G, int64_t N, int64_t D, do
                        double* S, double* Y, double* rstd)
 {
     if (bad_shape(N, D)) return MNO_ERR_ARG;
+    fill_tables();
     rows w;
     if (!rows_alloc(&w, D)) { rows_free(&w); return MNO_ERR_MEM; }
     get_row(G, 0, D, w.g);
@@ -239,6 +321,7 @@ static int ln_forward(operand X, operand G, operand B, int64_t N, int64_t D, dou
                       double* Y, double* mean, double* rstd)
 {
     if (bad_shape(N, D)) return MNO_ERR_ARG;
+    fill_tables();
     rows w;
     if (!rows_alloc(&w, D)) { rows_free(&w); return MNO_ERR_MEM; }
     get_row(G, 0, D, w.g);
@@ -277,6 +360,7 @@ static int rms_backward(operand X, operand R, operand G, operand DY, operand DH,
                         int64_t N, int64_t D, double eps, double* dX, double* dgamma)
 {
     if (bad_shape(N, D)) return MNO_ERR_ARG;
+    fill_tables();
     rows w;
     if (!rows_alloc(&w, D)) { rows_free(&w); return MNO_ERR_MEM; }
     get_row(G, 0, D, w.g);
@@ -310,6 +394,7 @@ static int ln_backward(operand X, operand G, operand DY, int64_t N, int64_t D, d
                        double* dX, double* dgamma, double* dbeta)
 {
     if (bad_shape(N, D)) return MNO_ERR_ARG;
+    fill_tables();
     rows w;
     if (!rows_alloc(&w, D)) { rows_free(&w); return MNO_ERR_MEM; }
     get_row(G, 0, D, w.g);
@@ -431,4 +516,55 @@ int mno_add_rmsnorm_backward_f64(const double* X, const double* R, const double*
     if (!R) return MNO_ERR_ARG;
     return rms_backward(op64(X), op64(R), op64(gamma), op64(dY), op64(dH), N, D, eps, dX,
                         dgamma);
+}
+
+/* Entry points with a storage type per operand group (MNO_F16, MNO_BF16,
+ * MNO_F32, MNO_F64): tx for the activations X (and R), tg for gamma (and
+ * beta), ty for the cotangents dY (and dH). */
+int mno_rmsnorm_forward_t(const void* X, int tx, const void* gamma, int tg, int64_t N, int64_t D,
+                          double eps, double* Y, double* rstd)
+{
+    if (!type_ok(tx) || !type_ok(tg)) return MNO_ERR_ARG;
+    return rms_forward(opt(X, tx), opt(NULL, tx), opt(gamma, tg), N, D, eps, NULL, Y, rstd);
+}
+
+int mno_layernorm_forward_t(const void* X, int tx, const void* gamma, const void* beta, int tg,
+                            int64_t N, int64_t D, double eps, double* Y, double* mean,
+                            double* rstd)
+{
+    if (!type_ok(tx) || !type_ok(tg)) return MNO_ERR_ARG;
+    return ln_forward(opt(X, tx), opt(gamma, tg), opt(beta, tg), N, D, eps, Y, mean, rstd);
+}
+
+int mno_add_rmsnorm_forward_t(const void* X, const void* R, int tx, const void* gamma, int tg,
+                              int64_t N, int64_t D, double eps, double* S, double* Y,
+                              double* rstd)
+{
+    if (!type_ok(tx) || !type_ok(tg) || !R) return MNO_ERR_ARG;
+    return rms_forward(opt(X, tx), opt(R, tx), opt(gamma, tg), N, D, eps, S, Y, rstd);
+}
+
+int mno_rmsnorm_backward_t(const void* X, int tx, const void* gamma, int tg, const void* dY,
+                           int ty, int64_t N, int64_t D, double eps, double* dX, double* dgamma)
+{
+    if (!type_ok(tx) || !type_ok(tg) || !type_ok(ty)) return MNO_ERR_ARG;
+    return rms_backward(opt(X, tx), opt(NULL, tx), opt(gamma, tg), opt(dY, ty), opt(NULL, ty),
+                        N, D, eps, dX, dgamma);
+}
+
+int mno_layernorm_backward_t(const void* X, int tx, const void* gamma, int tg, const void* dY,
+                             int ty, int64_t N, int64_t D, double eps, double* dX,
+                             double* dgamma, double* dbeta)
+{
+    if (!type_ok(tx) || !type_ok(tg) || !type_ok(ty)) return MNO_ERR_ARG;
+    return ln_backward(opt(X, tx), opt(gamma, tg), opt(dY, ty), N, D, eps, dX, dgamma, dbeta);
+}
+
+int mno_add_rmsnorm_backward_t(const void* X, const void* R, int tx, const void* gamma, int tg,
+                               const void* dY, const void* dH, int ty, int64_t N, int64_t D,
+                               double eps, double* dX, double* dgamma)
+{
+    if (!type_ok(tx) || !type_ok(tg) || !type_ok(ty) || !R) return MNO_ERR_ARG;
+    return rms_backward(opt(X, tx), opt(R, tx), opt(gamma, tg), opt(dY, ty), opt(dH, ty), N, D,
+                        eps, dX, dgamma);
 }

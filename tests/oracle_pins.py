@@ -4,12 +4,14 @@ Each ``pin_*`` function takes an ``oracle.Oracle`` instance and raises
 AssertionError when the oracle disagrees with:
 
 * a library routine that computes the same definition (numpy's float16
-  conversion; torch fp64 ``rms_norm``, ``native_layer_norm``,
-  ``_fused_rms_norm`` and autograd),
+  conversion; torch's bfloat16 conversion and addition; torch fp64
+  ``rms_norm``, ``native_layer_norm``, ``_fused_rms_norm`` and autograd),
 * central finite differences of the oracle's own forward functions,
 * closed forms for constant, zero and hand-derivable rows (including the
   LayerNorm example of the meTile contract page),
-* invariants every row satisfies whatever its values.
+* invariants every row satisfies whatever its values,
+* agreement of the typed entry points across storage types on values that
+  every type represents exactly.
 
 The functions are shared by ``test_oracle_pins.py`` (the real oracle must pass
 all of them) and ``test_oracle_mutants.py`` (each planted mistake must fail at
@@ -392,8 +394,124 @@ def pin_fused_special_cases(o):
     assert (Y == Y2).all() and (rstd == r2).all(), "fused forward is not rmsnorm of x + r"
 
 
+# ---------------------------------------------------------------------------
+# bfloat16 codec versus torch, and the typed entry points
+# ---------------------------------------------------------------------------
+
+def _torch_bf16_bits(v32: np.ndarray) -> np.ndarray:
+    """torch's float32 -> bfloat16 conversion (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(v32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def pin_bf16_codec_decode(o):
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = o.bf16_to_f64(bits)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all(), "bf16 NaN patterns decode differently"
+    assert (got[~nan] == ref[~nan]).all(), "bf16 patterns decode differently from torch"
+    assert (np.signbit(got[~nan]) == np.signbit(ref[~nan])).all(), "bf16 sign of zero differs"
+
+
+def pin_bf16_codec_encode(o):
+    # float32-representable probes, where torch rounds once (float32 -> bf16)
+    bits = np.arange(65536, dtype=np.uint16)
+    vals = o.bf16_to_f64(bits)
+    fin = np.unique(np.abs(vals[np.isfinite(vals)]))
+    mids = (fin[:-1] + fin[1:]) / 2.0                 # ties, exact in float32
+    m32 = mids.astype(np.float32)
+    assert (m32.astype(np.float64) == mids).all()
+    up = np.nextafter(m32, np.float32(np.inf))
+    down = np.nextafter(m32, np.float32(-np.inf))
+    rng = np.random.default_rng(321)
+    rnd = (np.exp2(rng.uniform(-140.0, 129.0, 200000)) *
+           rng.choice([-1.0, 1.0], 200000)).astype(np.float32)
+    probe = np.concatenate([fin.astype(np.float32), m32, -m32, up, down, rnd,
+                            np.array([0.0, -0.0, np.inf, -np.inf, 3.4e38, -3.4e38],
+                                     dtype=np.float32)])
+    got = o.f64_to_bf16(probe.astype(np.float64))
+    ref = _torch_bf16_bits(probe)
+    bad = got != ref
+    assert not bad.any(), (f"{int(bad.sum())} bf16 encodings differ from torch, e.g. "
+                           f"{probe[bad][:4]} -> {got[bad][:4]} vs {ref[bad][:4]}")
+    # doubles off the float32 grid: the encoding is the nearer bf16 neighbour
+    # (ties to even), checked by brute force on exact double distances
+    v = np.exp2(rng.uniform(-120.0, 120.0, 50000)) * rng.choice([-1.0, 1.0], 50000)
+    b = o.f64_to_bf16(v)
+    here = o.bf16_to_f64(b)
+    lo = o.bf16_to_f64((b.astype(np.int32) - 1).astype(np.uint16))
+    hi = o.bf16_to_f64((b.astype(np.int32) + 1).astype(np.uint16))
+    d0 = np.abs(v - here)
+    assert (d0 <= np.abs(v - lo)).all() and (d0 <= np.abs(v - hi)).all(), \
+        "bf16 encoding is not the nearest value"
+
+
+def pin_storage_types_agree(o):
+    """Values every storage type holds exactly give identical fp64 results
+    through the binary16, bfloat16, binary32 and binary64 entry points."""
+    rng = np.random.default_rng(17)
+    N, D = 5, 96
+    xs = rng.integers(-96, 97, (N, D)) / 16.0          # 7 significant bits at most
+    rs = rng.integers(-64, 65, (N, D)) / 8.0
+    gs = 1 + rng.integers(-16, 17, D) / 64.0
+    bs = rng.integers(-16, 17, D) / 32.0
+    dys = rng.integers(-128, 129, (N, D)) / 64.0
+    dhs = rng.integers(-32, 33, (N, D)) / 32.0
+
+    def as_type(a, t):
+        if t == "f16":
+            return a.astype(np.float16)
+        if t == "bf16":
+            return o.f64_to_bf16(a)
+        if t == "f32":
+            return a.astype(np.float32)
+        return np.ascontiguousarray(a, dtype=np.float64)
+
+    results = {}
+    for t in ("f64", "f16", "bf16", "f32"):
+        X, R, g, b = as_type(xs, t), as_type(rs, t), as_type(gs, t), as_type(bs, t)
+        dY, dH = as_type(dys, t), as_type(dhs, t)
+        r = []
+        r += list(o.rmsnorm_forward(X, g, 1e-5))
+        r += list(o.layernorm_forward(X, g, b, 1e-5))
+        S, H, Y, rs_ = o.add_rmsnorm_forward(X, R, g, 1e-5)
+        r += [S, Y, rs_]
+        r += list(o.rmsnorm_backward(X, g, dY, 1e-5))
+        r += list(o.layernorm_backward(X, g, dY, 1e-5))
+        r += list(o.add_rmsnorm_backward(X, R, g, dY, dH, 1e-5))
+        results[t] = r
+    for t in ("f16", "bf16", "f32"):
+        for i, (a, b_) in enumerate(zip(results["f64"], results[t])):
+            assert (a == b_).all(), f"{t} entry points differ from f64 (output {i})"
+    # mixed types per group: bf16 activations, f32 parameters, f16 cotangents
+    dX, dg = o.rmsnorm_backward(as_type(xs, "bf16"), as_type(gs, "f32"), as_type(dys, "f16"),
+                                1e-5)
+    assert (dX == results["f64"][8]).all() and (dg == results["f64"][9]).all(), \
+        "mixed storage types differ"
+
+
+def pin_bf16_fused_sum(o):
+    """The fused add's H for bfloat16 inputs is the bfloat16 rounding of the
+    exact sum: torch's bf16 addition agrees wherever its float32 sum is
+    exact (exponents within 16 binades)."""
+    rng = np.random.default_rng(23)
+    N, D = 64, 257
+    x = o.f64_to_bf16(rng.standard_normal((N, D)) * np.exp2(rng.integers(-6, 7, (N, D))))
+    r = o.f64_to_bf16(rng.standard_normal((N, D)) * np.exp2(rng.integers(-6, 7, (N, D))))
+    g = o.f64_to_bf16(1 + 0.1 * rng.standard_normal(D))
+    S, H, Y, rstd = o.add_rmsnorm_forward(x, r, g, 1e-5)
+    tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    tr = torch.from_numpy(r.view(np.int16)).view(torch.bfloat16)
+    ref = (tx + tr).view(torch.int16).numpy().view(np.uint16)
+    same = (H == ref) | (((H | ref) & 0x7FFF) == 0)
+    assert same.all(), f"bf16 H differs from torch in {int((~same).sum())} elements"
+    assert (S == o.bf16_to_f64(x) + o.bf16_to_f64(r)).all(), "S is not the exact sum"
+
+
 ALL_PINS = [
     pin_codec_decode, pin_codec_encode, pin_torch_rmsnorm, pin_torch_layernorm,
     pin_torch_add_rmsnorm, pin_finite_differences, pin_constant_rows, pin_zero_rows,
     pin_worked_example, pin_invariants, pin_scaling, pin_fused_special_cases,
+    pin_bf16_codec_decode, pin_bf16_codec_encode, pin_storage_types_agree, pin_bf16_fused_sum,
 ]

@@ -42,6 +42,14 @@ MUTANTS = {
                                   "ldexp((double)(1024 + f), e - 24)"),
     "codec_ties_away": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
     "codec_subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    "bf16_decode_exponent": ("v = ldexp((double)(128 + f), e - 134);",
+                             "v = ldexp((double)(128 + f), e - 133);"),
+    "bf16_encode_mantissa": ("return (uint16_t)encode_binary(v, 7, -126, 127);",
+                             "return (uint16_t)encode_binary(v, 7, -125, 127);"),
+    "f32_operand_stride": ("const float* f = (const float*)a.p + o;",
+                           "const float* f = (const float*)a.p + o / 2;"),
+    "bf16_reads_f16_table": ("for (int64_t j = 0; j < D; ++j) dst[j] = bf16_table[b[j]];",
+                             "for (int64_t j = 0; j < D; ++j) dst[j] = f16_table[b[j]];"),
 }
 
 
