@@ -28,19 +28,23 @@
  *   - Validation happens before anything is enqueued; on any error nothing
  *     is written and nothing is launched:
  *       MN_ERR_NULL      a required pointer is NULL
- *       MN_ERR_SHAPE     N < 1, or D outside [1, MN_MAX_COLS]
+ *       MN_ERR_SHAPE     N < 1, D outside [1, MN_MAX_COLS], N * D * 8 beyond
+ *                        INT64_MAX, or (forward) more than 2^31 - 1 tiles of
+ *                        rows (a tile holds at least 4 rows)
  *       MN_ERR_EPS       eps is not a positive finite float
  *       MN_ERR_ALIAS     an output's byte range overlaps an input's or
  *                        another output's ([meTile]: no in-place mutation)
  *       MN_ERR_WORKSPACE workspace NULL, smaller than
  *                        mn_norm_workspace_bytes(), or not 16-byte aligned
  *       MN_ERR_DEVICE    the HIP runtime rejected a launch
+ *       MN_ERR_DTYPE     a storage type outside mn_dtype (the *_ex calls)
  *   - Results are bitwise deterministic for a given (N, D), pointer
  *     alignment class and device: every reduction has a fixed order and no
  *     floating-point atomics are used.
- *   - Rows whose binary16 pointers are all 16-byte aligned with D % 8 == 0
- *     take the 128-bit vector kernels; any other call takes the element-wise
- *     kernels (same results up to fp32 summation order).
+ *   - Calls whose tensor pointers are all 16-byte aligned, with D % 8 == 0
+ *     for 16-bit storage or D % 4 == 0 for binary32, take the 128-bit vector
+ *     kernels; any other call takes the element-wise kernels (same formulas,
+ *     different fp32 summation order).
  */
 #ifndef MN_NORM_H
 #define MN_NORM_H
@@ -61,8 +65,16 @@ typedef enum {
     MN_ERR_EPS = 3,
     MN_ERR_ALIAS = 4,
     MN_ERR_WORKSPACE = 5,
-    MN_ERR_DEVICE = 6
+    MN_ERR_DEVICE = 6,
+    MN_ERR_DTYPE = 7
 } mn_status;
+
+/* Storage types of the *_ex entry points. Arithmetic is fp32 for all. */
+typedef enum {
+    MN_F16 = 0,   /* IEEE binary16 */
+    MN_BF16 = 1,  /* bfloat16: the upper 16 bits of an IEEE binary32 */
+    MN_F32 = 2    /* IEEE binary32 */
+} mn_dtype;
 
 typedef enum {
     MN_RMSNORM = 0,
@@ -146,6 +158,43 @@ mn_status mn_add_rmsnorm_backward(const mn_f16* X, const mn_f16* R, const mn_f16
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Storage types beyond binary16. [meTile] contract: storage may be FP16 or
+ * FP32 and the weight, bias and cotangents may each use either type, while
+ * statistics, accumulation and parameter gradients are FP32. These entry
+ * points take `act`, the storage type of the activations and cotangents
+ * (X, R, Y, H, dY, dH, dX), and `param`, the storage type of gamma and beta;
+ * each is MN_F16, MN_BF16 or MN_F32. Everything else -- formulas, saved fp32
+ * statistics, fp32 dgamma/dbeta, workspace, validation, determinism -- is
+ * exactly as for the binary16 calls above, which equal the *_ex calls with
+ * act = param = MN_F16. Results in 16-bit storage are rounded to nearest,
+ * ties to even; the fused add's H is the exact sum x + r rounded once to
+ * the activation type. Workspace sizes do not depend on the storage types.
+ * ------------------------------------------------------------------------- */
+mn_status mn_rmsnorm_forward_ex(const void* X, const void* gamma, void* Y, float* rstd,
+                                int64_t N, int64_t D, float eps, mn_dtype act, mn_dtype param,
+                                void* stream);
+mn_status mn_rmsnorm_backward_ex(const void* X, const void* gamma, const float* rstd,
+                                 const void* dY, void* dX, float* dgamma, int64_t N, int64_t D,
+                                 mn_dtype act, mn_dtype param, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+mn_status mn_layernorm_forward_ex(const void* X, const void* gamma, const void* beta, void* Y,
+                                  float* mean, float* rstd, int64_t N, int64_t D, float eps,
+                                  mn_dtype act, mn_dtype param, void* stream);
+mn_status mn_layernorm_backward_ex(const void* X, const void* gamma, const float* mean,
+                                   const float* rstd, const void* dY, void* dX, float* dgamma,
+                                   float* dbeta, int64_t N, int64_t D, mn_dtype act,
+                                   mn_dtype param, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+mn_status mn_add_rmsnorm_forward_ex(const void* X, const void* R, const void* gamma, void* H,
+                                    void* Y, float* rstd, int64_t N, int64_t D, float eps,
+                                    mn_dtype act, mn_dtype param, void* stream);
+mn_status mn_add_rmsnorm_backward_ex(const void* X, const void* R, const void* gamma,
+                                     const float* rstd, const void* dY, const void* dH, void* dX,
+                                     float* dgamma, int64_t N, int64_t D, mn_dtype act,
+                                     mn_dtype param, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* ---------------------------------------------------------------------------
  * Workspace and diagnostics.
  * ------------------------------------------------------------------------- */
 
@@ -183,8 +232,23 @@ mn_status mn_add_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* R, const m
                                        mn_f16* dX, int64_t N, int64_t D, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* Stage 1 with explicit storage types (see the *_ex calls above). */
+mn_status mn_rmsnorm_backward_rows_ex(const void* X, const void* gamma, const float* rstd,
+                                      const void* dY, void* dX, int64_t N, int64_t D,
+                                      mn_dtype act, mn_dtype param, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+mn_status mn_layernorm_backward_rows_ex(const void* X, const void* gamma, const float* mean,
+                                        const float* rstd, const void* dY, void* dX, int64_t N,
+                                        int64_t D, mn_dtype act, mn_dtype param,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+mn_status mn_add_rmsnorm_backward_rows_ex(const void* X, const void* R, const void* gamma,
+                                          const float* rstd, const void* dY, const void* dH,
+                                          void* dX, int64_t N, int64_t D, mn_dtype act,
+                                          mn_dtype param, void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
 /* Stage 2 (column reduce): dgamma[j] = sum over partial rows p of
- * partial[p][j] in ascending p order (dbeta likewise for LayerNorm; pass
+ * partial[p][j] in a fixed order (dbeta likewise for LayerNorm; pass
  * dbeta = NULL otherwise). Overwrites dgamma/dbeta. `kind`, N and D must be
  * those of the stage-1 call that filled `workspace`. */
 mn_status mn_norm_reduce_partials(mn_norm_kind kind, int64_t N, int64_t D,

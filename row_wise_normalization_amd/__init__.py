@@ -7,8 +7,10 @@ derives N and D from X, and raises ``MnError`` on a non-zero status. All
 arithmetic runs in the library's HIP kernels; there is no fallback: if the
 library is missing or cannot be loaded the call raises.
 
-The helpers without the ``mn_`` prefix allocate outputs and workspace with
-torch (device memory plumbing only) and call the same entry points.
+The ``mn_*_ex`` functions take float16, bfloat16 or float32 tensors (the
+activations' type from X, the parameters' from gamma). The helpers without
+the ``mn_`` prefix allocate outputs and workspace with torch (device memory
+plumbing only) and call the ``_ex`` entry points.
 """
 from __future__ import annotations
 
@@ -26,8 +28,12 @@ MAX_COLS = 8192
 
 STATUS = {
     0: "MN_OK", 1: "MN_ERR_NULL", 2: "MN_ERR_SHAPE", 3: "MN_ERR_EPS", 4: "MN_ERR_ALIAS",
-    5: "MN_ERR_WORKSPACE", 6: "MN_ERR_DEVICE",
+    5: "MN_ERR_WORKSPACE", 6: "MN_ERR_DEVICE", 7: "MN_ERR_DTYPE",
 }
+
+# mn_dtype codes for torch storage types
+MN_F16, MN_BF16, MN_F32 = 0, 1, 2
+DTYPE_CODE = {torch.float16: MN_F16, torch.bfloat16: MN_BF16, torch.float32: MN_F32}
 
 
 class MnError(RuntimeError):
@@ -39,6 +45,7 @@ class MnError(RuntimeError):
 _lib: Optional[ctypes.CDLL] = None
 
 _P = ctypes.c_void_p
+_C = ctypes.c_int
 _I64 = ctypes.c_int64
 _F = ctypes.c_float
 _SZ = ctypes.c_size_t
@@ -54,6 +61,17 @@ _SIGNATURES = {
     "mn_layernorm_backward_rows": [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
     "mn_add_rmsnorm_backward_rows": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
     "mn_norm_reduce_partials": [ctypes.c_int, _I64, _I64, _P, _SZ, _P, _P, _P],
+    "mn_rmsnorm_forward_ex": [_P, _P, _P, _P, _I64, _I64, _F, _C, _C, _P],
+    "mn_rmsnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ, _P],
+    "mn_layernorm_forward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _C, _C, _P],
+    "mn_layernorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ, _P],
+    "mn_add_rmsnorm_forward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _C, _C, _P],
+    "mn_add_rmsnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ,
+                                   _P],
+    "mn_rmsnorm_backward_rows_ex": [_P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ, _P],
+    "mn_layernorm_backward_rows_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ, _P],
+    "mn_add_rmsnorm_backward_rows_ex": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ,
+                                        _P],
 }
 
 
@@ -214,6 +232,102 @@ def mn_norm_reduce_partials(kind: int, N: int, D: int, workspace, dgamma, dbeta=
           _ws_bytes(workspace), _ptr(dgamma), _ptr(dbeta), _stream(stream))
 
 
+# --- the C entry points with explicit storage types ---------------------------
+# Activations and cotangents share one storage type (float16, bfloat16 or
+# float32, taken from X); gamma and beta share another (taken from gamma).
+
+def _types(X, gamma):
+    if X.dtype not in DTYPE_CODE or gamma.dtype not in DTYPE_CODE:
+        raise TypeError("storage types must be float16, bfloat16 or float32")
+    return DTYPE_CODE[X.dtype], DTYPE_CODE[gamma.dtype]
+
+
+def mn_rmsnorm_forward_ex(X, gamma, Y, rstd, eps: float, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, D)); _check_t("gamma", gamma, gamma.dtype, (D,))
+    _check_t("Y", Y, X.dtype, (N, D)); _check_t("rstd", rstd, F32, (N,))
+    _call("mn_rmsnorm_forward_ex", _ptr(X), _ptr(gamma), _ptr(Y), _ptr(rstd), N, D, float(eps),
+          act, par, _stream(stream))
+
+
+def mn_rmsnorm_backward_ex(X, gamma, rstd, dY, dX, dgamma, workspace, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, D)); _check_t("gamma", gamma, gamma.dtype, (D,))
+    _check_t("rstd", rstd, F32, (N,)); _check_t("dY", dY, X.dtype, (N, D))
+    _check_t("dX", dX, X.dtype, (N, D)); _check_t("dgamma", dgamma, F32, (D,))
+    _call("mn_rmsnorm_backward_ex", _ptr(X), _ptr(gamma), _ptr(rstd), _ptr(dY), _ptr(dX),
+          _ptr(dgamma), N, D, act, par, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def mn_layernorm_forward_ex(X, gamma, beta, Y, mean, rstd, eps: float, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, D)); _check_t("gamma", gamma, gamma.dtype, (D,))
+    _check_t("beta", beta, gamma.dtype, (D,)); _check_t("Y", Y, X.dtype, (N, D))
+    _check_t("mean", mean, F32, (N,)); _check_t("rstd", rstd, F32, (N,))
+    _call("mn_layernorm_forward_ex", _ptr(X), _ptr(gamma), _ptr(beta), _ptr(Y), _ptr(mean),
+          _ptr(rstd), N, D, float(eps), act, par, _stream(stream))
+
+
+def mn_layernorm_backward_ex(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, workspace, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, D)); _check_t("gamma", gamma, gamma.dtype, (D,))
+    _check_t("mean", mean, F32, (N,)); _check_t("rstd", rstd, F32, (N,))
+    _check_t("dY", dY, X.dtype, (N, D)); _check_t("dX", dX, X.dtype, (N, D))
+    _check_t("dgamma", dgamma, F32, (D,)); _check_t("dbeta", dbeta, F32, (D,))
+    _call("mn_layernorm_backward_ex", _ptr(X), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dY),
+          _ptr(dX), _ptr(dgamma), _ptr(dbeta), N, D, act, par, _ptr(workspace),
+          _ws_bytes(workspace), _stream(stream))
+
+
+def mn_add_rmsnorm_forward_ex(X, R, gamma, H_out, Y, rstd, eps: float, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, D)); _check_t("R", R, X.dtype, (N, D))
+    _check_t("gamma", gamma, gamma.dtype, (D,)); _check_t("H", H_out, X.dtype, (N, D))
+    _check_t("Y", Y, X.dtype, (N, D)); _check_t("rstd", rstd, F32, (N,))
+    _call("mn_add_rmsnorm_forward_ex", _ptr(X), _ptr(R), _ptr(gamma), _ptr(H_out), _ptr(Y),
+          _ptr(rstd), N, D, float(eps), act, par, _stream(stream))
+
+
+def mn_add_rmsnorm_backward_ex(X, R, gamma, rstd, dY, dH, dX, dgamma, workspace, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, D)); _check_t("R", R, X.dtype, (N, D))
+    _check_t("gamma", gamma, gamma.dtype, (D,)); _check_t("rstd", rstd, F32, (N,))
+    _check_t("dY", dY, X.dtype, (N, D)); _check_t("dH", dH, X.dtype, (N, D), optional=True)
+    _check_t("dX", dX, X.dtype, (N, D)); _check_t("dgamma", dgamma, F32, (D,))
+    _call("mn_add_rmsnorm_backward_ex", _ptr(X), _ptr(R), _ptr(gamma), _ptr(rstd), _ptr(dY),
+          _ptr(dH), _ptr(dX), _ptr(dgamma), N, D, act, par, _ptr(workspace),
+          _ws_bytes(workspace), _stream(stream))
+
+
+def mn_rmsnorm_backward_rows_ex(X, gamma, rstd, dY, dX, workspace, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _call("mn_rmsnorm_backward_rows_ex", _ptr(X), _ptr(gamma), _ptr(rstd), _ptr(dY), _ptr(dX),
+          N, D, act, par, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def mn_layernorm_backward_rows_ex(X, gamma, mean, rstd, dY, dX, workspace, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _call("mn_layernorm_backward_rows_ex", _ptr(X), _ptr(gamma), _ptr(mean), _ptr(rstd),
+          _ptr(dY), _ptr(dX), N, D, act, par, _ptr(workspace), _ws_bytes(workspace),
+          _stream(stream))
+
+
+def mn_add_rmsnorm_backward_rows_ex(X, R, gamma, rstd, dY, dH, dX, workspace, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _call("mn_add_rmsnorm_backward_rows_ex", _ptr(X), _ptr(R), _ptr(gamma), _ptr(rstd),
+          _ptr(dY), _ptr(dH), _ptr(dX), N, D, act, par, _ptr(workspace), _ws_bytes(workspace),
+          _stream(stream))
+
+
 def _ws_bytes(workspace: Optional[torch.Tensor]) -> int:
     if workspace is None:
         return 0
@@ -231,7 +345,7 @@ def rmsnorm_forward(X, gamma, eps: float = 1e-5, stream=None):
     N, D = _nd(X)
     Y = torch.empty_like(X)
     rstd = torch.empty(N, dtype=F32, device=X.device)
-    mn_rmsnorm_forward(X, gamma, Y, rstd, eps, stream)
+    mn_rmsnorm_forward_ex(X, gamma, Y, rstd, eps, stream)
     return Y, rstd
 
 
@@ -240,7 +354,7 @@ def rmsnorm_backward(X, gamma, rstd, dY, stream=None):
     dX = torch.empty_like(X)
     dgamma = torch.empty(D, dtype=F32, device=X.device)
     ws = new_workspace(MN_RMSNORM, N, D, X.device)
-    mn_rmsnorm_backward(X, gamma, rstd, dY, dX, dgamma, ws, stream)
+    mn_rmsnorm_backward_ex(X, gamma, rstd, dY, dX, dgamma, ws, stream)
     return dX, dgamma
 
 
@@ -249,7 +363,7 @@ def layernorm_forward(X, gamma, beta, eps: float = 1e-5, stream=None):
     Y = torch.empty_like(X)
     mean = torch.empty(N, dtype=F32, device=X.device)
     rstd = torch.empty(N, dtype=F32, device=X.device)
-    mn_layernorm_forward(X, gamma, beta, Y, mean, rstd, eps, stream)
+    mn_layernorm_forward_ex(X, gamma, beta, Y, mean, rstd, eps, stream)
     return Y, mean, rstd
 
 
@@ -259,7 +373,7 @@ def layernorm_backward(X, gamma, mean, rstd, dY, stream=None):
     dgamma = torch.empty(D, dtype=F32, device=X.device)
     dbeta = torch.empty(D, dtype=F32, device=X.device)
     ws = new_workspace(MN_LAYERNORM, N, D, X.device)
-    mn_layernorm_backward(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, ws, stream)
+    mn_layernorm_backward_ex(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, ws, stream)
     return dX, dgamma, dbeta
 
 
@@ -268,7 +382,7 @@ def add_rmsnorm_forward(X, R, gamma, eps: float = 1e-5, stream=None):
     Hs = torch.empty_like(X)
     Y = torch.empty_like(X)
     rstd = torch.empty(N, dtype=F32, device=X.device)
-    mn_add_rmsnorm_forward(X, R, gamma, Hs, Y, rstd, eps, stream)
+    mn_add_rmsnorm_forward_ex(X, R, gamma, Hs, Y, rstd, eps, stream)
     return Hs, Y, rstd
 
 
@@ -277,5 +391,5 @@ def add_rmsnorm_backward(X, R, gamma, rstd, dY, dH=None, stream=None):
     dX = torch.empty_like(X)
     dgamma = torch.empty(D, dtype=F32, device=X.device)
     ws = new_workspace(MN_ADD_RMSNORM, N, D, X.device)
-    mn_add_rmsnorm_backward(X, R, gamma, rstd, dY, dH, dX, dgamma, ws, stream)
+    mn_add_rmsnorm_backward_ex(X, R, gamma, rstd, dY, dH, dX, dgamma, ws, stream)
     return dX, dgamma

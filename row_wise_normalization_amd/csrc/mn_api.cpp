@@ -21,7 +21,7 @@ struct Span {
 Span span(const void* p, size_t bytes)
 {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    return Span{a, a + bytes};
+    return Span{a, p ? a + bytes : a};
 }
 
 bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
@@ -30,10 +30,12 @@ bool shape_ok(int64_t N, int64_t D)
 {
     if (N < 1 || D < 1 || D > MN_MAX_COLS) return false;
     // element offsets are formed in int64 and byte spans in uintptr_t
-    return N <= (INT64_MAX / 4) / D;
+    return N <= (INT64_MAX / 8) / D;
 }
 
 bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.0f; }
+
+bool dtype_ok(int t) { return t == MN_F16 || t == MN_BF16 || t == MN_F32; }
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -50,6 +52,10 @@ bool alias_free(const Span (&in)[NI], const Span (&out)[NO])
     }
     return true;
 }
+
+// 128-bit chunks need whole 16-byte chunks per row: D a multiple of 8
+// elements for the 16-bit storage types, of 4 for binary32.
+bool chunks_fit(int st, int64_t D) { return D % (st == mn::ST_F32 ? 4 : 8) == 0; }
 
 size_t workspace_bytes(int kind, int64_t N, int64_t D)
 {
@@ -72,40 +78,42 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 // Forward.
 // ---------------------------------------------------------------------------
 
-mn_status forward(int kind, const mn_f16* X, const mn_f16* R, const mn_f16* gamma,
-                  const mn_f16* beta, mn_f16* H, mn_f16* Y, float* mean, float* rstd,
-                  int64_t N, int64_t D, float eps, void* stream)
+mn_status forward(int kind, const void* X, const void* R, const void* gamma, const void* beta,
+                  void* H, void* Y, float* mean, float* rstd, int64_t N, int64_t D, float eps,
+                  int st, int pdt, void* stream)
 {
     if (!X || !gamma || !Y || !rstd) return MN_ERR_NULL;
     if (kind == mn::LN && (!beta || !mean)) return MN_ERR_NULL;
     if (kind == mn::ADD && (!R || !H)) return MN_ERR_NULL;
+    if (!dtype_ok(st) || !dtype_ok(pdt)) return MN_ERR_DTYPE;
     if (!shape_ok(N, D)) return MN_ERR_SHAPE;
     if (!eps_ok(eps)) return MN_ERR_EPS;
 
-    const size_t nd = (size_t)N * (size_t)D * 2u;
-    const Span in[] = {span(X, nd), span(R, R ? nd : 0), span(gamma, (size_t)D * 2u),
-                       span(beta, beta ? (size_t)D * 2u : 0)};
-    const Span out[] = {span(Y, nd), span(H, H ? nd : 0), span(rstd, (size_t)N * 4u),
-                        span(mean, mean ? (size_t)N * 4u : 0)};
+    const size_t nd = (size_t)N * (size_t)D * (size_t)mn::stor_bytes(st);
+    const size_t dp = (size_t)D * (size_t)mn::stor_bytes(pdt);
+    const Span in[] = {span(X, nd), span(R, nd), span(gamma, dp), span(beta, dp)};
+    const Span out[] = {span(Y, nd), span(H, nd), span(rstd, (size_t)N * 4u),
+                        span(mean, (size_t)N * 4u)};
     if (!alias_free(in, out)) return MN_ERR_ALIAS;
 
-    const bool vec_ok = (D % 8 == 0) && aligned16(X) && aligned16(R) && aligned16(gamma) &&
+    const bool vec_ok = chunks_fit(st, D) && aligned16(X) && aligned16(R) && aligned16(gamma) &&
                         aligned16(beta) && aligned16(Y) && aligned16(H);
-    const mn::FwdPlan plan = mn::plan_forward(kind, N, (int32_t)D, vec_ok);
+    const mn::FwdPlan plan = mn::plan_forward(kind, st, N, (int32_t)D, vec_ok);
+    if (plan.grid > INT32_MAX) return MN_ERR_SHAPE;  // one workgroup per tile of rows
     mn::FwdArgs a;
-    a.X = reinterpret_cast<const _Float16*>(X);
-    a.R = reinterpret_cast<const _Float16*>(R);
-    a.gamma = reinterpret_cast<const _Float16*>(gamma);
-    a.beta = reinterpret_cast<const _Float16*>(beta);
-    a.Y = reinterpret_cast<_Float16*>(Y);
-    a.H = reinterpret_cast<_Float16*>(H);
+    a.X = X;
+    a.R = R;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.Y = Y;
+    a.H = H;
     a.mean = mean;
     a.rstd = rstd;
     a.N = N;
     a.D = (int32_t)D;
+    a.pdt = pdt;
     a.eps = eps;
-    a.rows_per_block = plan.rows_per_block;
-    return device_status(mn::launch_forward(kind, plan, a, as_stream(stream)));
+    return device_status(mn::launch_forward(kind, st, plan, a, as_stream(stream)));
 }
 
 // ---------------------------------------------------------------------------
@@ -113,48 +121,52 @@ mn_status forward(int kind, const mn_f16* X, const mn_f16* R, const mn_f16* gamm
 // ---------------------------------------------------------------------------
 
 struct BwdIn {
-    const mn_f16 *X, *R, *gamma, *dY, *dH;
+    const void *X, *R, *gamma, *dY, *dH;
     const float *mean, *rstd;
-    mn_f16* dX;
+    void* dX;
 };
 
-mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, void* ws,
-                        size_t ws_bytes, const float* dgamma, const float* dbeta, void* stream)
+mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, int st, int pdt,
+                        void* ws, size_t ws_bytes, const float* dgamma, const float* dbeta,
+                        void* stream)
 {
     if (!b.X || !b.gamma || !b.dY || !b.rstd || !b.dX) return MN_ERR_NULL;
     if (kind == mn::LN && !b.mean) return MN_ERR_NULL;
     if (kind == mn::ADD && !b.R) return MN_ERR_NULL;
+    if (!dtype_ok(st) || !dtype_ok(pdt)) return MN_ERR_DTYPE;
     if (!shape_ok(N, D)) return MN_ERR_SHAPE;
     const size_t need = workspace_bytes(kind, N, D);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
 
-    const size_t nd = (size_t)N * (size_t)D * 2u;
-    const Span in[] = {span(b.X, nd), span(b.R, b.R ? nd : 0), span(b.gamma, (size_t)D * 2u),
-                       span(b.dY, nd), span(b.dH, b.dH ? nd : 0),
-                       span(b.mean, b.mean ? (size_t)N * 4u : 0), span(b.rstd, (size_t)N * 4u)};
-    const Span out[] = {span(b.dX, nd), span(ws, need),
-                        span(dgamma, dgamma ? (size_t)D * 4u : 0),
-                        span(dbeta, dbeta ? (size_t)D * 4u : 0)};
+    const size_t nd = (size_t)N * (size_t)D * (size_t)mn::stor_bytes(st);
+    const size_t dp = (size_t)D * (size_t)mn::stor_bytes(pdt);
+    const Span in[] = {span(b.X, nd), span(b.R, nd), span(b.gamma, dp), span(b.dY, nd),
+                       span(b.dH, nd), span(b.mean, (size_t)N * 4u),
+                       span(b.rstd, (size_t)N * 4u)};
+    const Span out[] = {span(b.dX, nd), span(ws, need), span(dgamma, (size_t)D * 4u),
+                        span(dbeta, (size_t)D * 4u)};
     if (!alias_free(in, out)) return MN_ERR_ALIAS;
 
-    const bool vec_ok = (D % 8 == 0) && aligned16(b.X) && aligned16(b.R) && aligned16(b.gamma) &&
-                        aligned16(b.dY) && aligned16(b.dH) && aligned16(b.dX);
-    const mn::BwdPlan plan = mn::plan_backward(kind, N, (int32_t)D, vec_ok);
+    const bool vec_ok = chunks_fit(st, D) && aligned16(b.X) && aligned16(b.R) &&
+                        aligned16(b.gamma) && aligned16(b.dY) && aligned16(b.dH) &&
+                        aligned16(b.dX);
+    const mn::BwdPlan plan = mn::plan_backward(kind, st, N, (int32_t)D, vec_ok);
     mn::BwdArgs a;
-    a.X = reinterpret_cast<const _Float16*>(b.X);
-    a.R = reinterpret_cast<const _Float16*>(b.R);
-    a.gamma = reinterpret_cast<const _Float16*>(b.gamma);
-    a.dY = reinterpret_cast<const _Float16*>(b.dY);
-    a.dH = reinterpret_cast<const _Float16*>(b.dH);
+    a.X = b.X;
+    a.R = b.R;
+    a.gamma = b.gamma;
+    a.dY = b.dY;
+    a.dH = b.dH;
     a.mean = b.mean;
     a.rstd = b.rstd;
-    a.dX = reinterpret_cast<_Float16*>(b.dX);
+    a.dX = b.dX;
     a.part_g = static_cast<float*>(ws);
     a.part_b = (kind == mn::LN) ? static_cast<float*>(ws) + plan.P * plan.Dp : nullptr;
     a.N = N;
     a.D = (int32_t)D;
     a.Dp = plan.Dp;
-    return device_status(mn::launch_backward_rows(kind, plan, a, as_stream(stream)));
+    a.pdt = pdt;
+    return device_status(mn::launch_backward_rows(kind, st, plan, a, as_stream(stream)));
 }
 
 mn_status reduce_partials(int kind, int64_t N, int64_t D, const void* ws, size_t ws_bytes,
@@ -167,7 +179,7 @@ mn_status reduce_partials(int kind, int64_t N, int64_t D, const void* ws, size_t
     if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
     const Span in[] = {span(ws, need)};
     const Span out[] = {span(dgamma, (size_t)D * 4u),
-                        span(kind == mn::LN ? dbeta : nullptr, kind == mn::LN ? (size_t)D * 4u : 0)};
+                        span(kind == mn::LN ? dbeta : nullptr, (size_t)D * 4u)};
     if (!alias_free(in, out)) return MN_ERR_ALIAS;
 
     mn::ReduceArgs a;
@@ -182,11 +194,11 @@ mn_status reduce_partials(int kind, int64_t N, int64_t D, const void* ws, size_t
 }
 
 mn_status backward(int kind, const BwdIn& b, float* dgamma, float* dbeta, int64_t N, int64_t D,
-                   void* ws, size_t ws_bytes, void* stream)
+                   int st, int pdt, void* ws, size_t ws_bytes, void* stream)
 {
     if (!dgamma || (kind == mn::LN && !dbeta)) return MN_ERR_NULL;
-    mn_status st = backward_rows(kind, b, N, D, ws, ws_bytes, dgamma, dbeta, stream);
-    if (st != MN_OK) return st;
+    mn_status s = backward_rows(kind, b, N, D, st, pdt, ws, ws_bytes, dgamma, dbeta, stream);
+    if (s != MN_OK) return s;
     return reduce_partials(kind, N, D, ws, ws_bytes, dgamma, dbeta, stream);
 }
 
@@ -194,25 +206,29 @@ mn_status backward(int kind, const BwdIn& b, float* dgamma, float* dbeta, int64_
 
 extern "C" {
 
+// --- binary16 entry points ---------------------------------------------------
+
 mn_status mn_rmsnorm_forward(const mn_f16* X, const mn_f16* gamma, mn_f16* Y, float* rstd,
                              int64_t N, int64_t D, float eps, void* stream)
 {
     return forward(mn::RMS, X, nullptr, gamma, nullptr, nullptr, Y, nullptr, rstd, N, D, eps,
-                   stream);
+                   MN_F16, MN_F16, stream);
 }
 
 mn_status mn_layernorm_forward(const mn_f16* X, const mn_f16* gamma, const mn_f16* beta,
                                mn_f16* Y, float* mean, float* rstd, int64_t N, int64_t D,
                                float eps, void* stream)
 {
-    return forward(mn::LN, X, nullptr, gamma, beta, nullptr, Y, mean, rstd, N, D, eps, stream);
+    return forward(mn::LN, X, nullptr, gamma, beta, nullptr, Y, mean, rstd, N, D, eps, MN_F16,
+                   MN_F16, stream);
 }
 
 mn_status mn_add_rmsnorm_forward(const mn_f16* X, const mn_f16* R, const mn_f16* gamma,
                                  mn_f16* H, mn_f16* Y, float* rstd, int64_t N, int64_t D,
                                  float eps, void* stream)
 {
-    return forward(mn::ADD, X, R, gamma, nullptr, H, Y, nullptr, rstd, N, D, eps, stream);
+    return forward(mn::ADD, X, R, gamma, nullptr, H, Y, nullptr, rstd, N, D, eps, MN_F16,
+                   MN_F16, stream);
 }
 
 mn_status mn_rmsnorm_backward(const mn_f16* X, const mn_f16* gamma, const float* rstd,
@@ -220,7 +236,8 @@ mn_status mn_rmsnorm_backward(const mn_f16* X, const mn_f16* gamma, const float*
                               void* workspace, size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
-    return backward(mn::RMS, b, dgamma, nullptr, N, D, workspace, workspace_bytes, stream);
+    return backward(mn::RMS, b, dgamma, nullptr, N, D, MN_F16, MN_F16, workspace,
+                    workspace_bytes, stream);
 }
 
 mn_status mn_layernorm_backward(const mn_f16* X, const mn_f16* gamma, const float* mean,
@@ -229,7 +246,8 @@ mn_status mn_layernorm_backward(const mn_f16* X, const mn_f16* gamma, const floa
                                 size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
-    return backward(mn::LN, b, dgamma, dbeta, N, D, workspace, workspace_bytes, stream);
+    return backward(mn::LN, b, dgamma, dbeta, N, D, MN_F16, MN_F16, workspace, workspace_bytes,
+                    stream);
 }
 
 mn_status mn_add_rmsnorm_backward(const mn_f16* X, const mn_f16* R, const mn_f16* gamma,
@@ -238,7 +256,8 @@ mn_status mn_add_rmsnorm_backward(const mn_f16* X, const mn_f16* R, const mn_f16
                                   void* workspace, size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
-    return backward(mn::ADD, b, dgamma, nullptr, N, D, workspace, workspace_bytes, stream);
+    return backward(mn::ADD, b, dgamma, nullptr, N, D, MN_F16, MN_F16, workspace,
+                    workspace_bytes, stream);
 }
 
 mn_status mn_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const float* rstd,
@@ -246,7 +265,8 @@ mn_status mn_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const f
                                    void* workspace, size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
-    return backward_rows(mn::RMS, b, N, D, workspace, workspace_bytes, nullptr, nullptr, stream);
+    return backward_rows(mn::RMS, b, N, D, MN_F16, MN_F16, workspace, workspace_bytes, nullptr,
+                         nullptr, stream);
 }
 
 mn_status mn_layernorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const float* mean,
@@ -255,7 +275,8 @@ mn_status mn_layernorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const
                                      void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
-    return backward_rows(mn::LN, b, N, D, workspace, workspace_bytes, nullptr, nullptr, stream);
+    return backward_rows(mn::LN, b, N, D, MN_F16, MN_F16, workspace, workspace_bytes, nullptr,
+                         nullptr, stream);
 }
 
 mn_status mn_add_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* R, const mn_f16* gamma,
@@ -264,8 +285,99 @@ mn_status mn_add_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* R, const m
                                        size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
-    return backward_rows(mn::ADD, b, N, D, workspace, workspace_bytes, nullptr, nullptr, stream);
+    return backward_rows(mn::ADD, b, N, D, MN_F16, MN_F16, workspace, workspace_bytes, nullptr,
+                         nullptr, stream);
 }
+
+// --- entry points with explicit storage types --------------------------------
+
+mn_status mn_rmsnorm_forward_ex(const void* X, const void* gamma, void* Y, float* rstd, int64_t N,
+                                int64_t D, float eps, mn_dtype act, mn_dtype param, void* stream)
+{
+    return forward(mn::RMS, X, nullptr, gamma, nullptr, nullptr, Y, nullptr, rstd, N, D, eps,
+                   act, param, stream);
+}
+
+mn_status mn_layernorm_forward_ex(const void* X, const void* gamma, const void* beta, void* Y,
+                                  float* mean, float* rstd, int64_t N, int64_t D, float eps,
+                                  mn_dtype act, mn_dtype param, void* stream)
+{
+    return forward(mn::LN, X, nullptr, gamma, beta, nullptr, Y, mean, rstd, N, D, eps, act, param,
+                   stream);
+}
+
+mn_status mn_add_rmsnorm_forward_ex(const void* X, const void* R, const void* gamma, void* H,
+                                    void* Y, float* rstd, int64_t N, int64_t D, float eps,
+                                    mn_dtype act, mn_dtype param, void* stream)
+{
+    return forward(mn::ADD, X, R, gamma, nullptr, H, Y, nullptr, rstd, N, D, eps, act, param,
+                   stream);
+}
+
+mn_status mn_rmsnorm_backward_ex(const void* X, const void* gamma, const float* rstd,
+                                 const void* dY, void* dX, float* dgamma, int64_t N, int64_t D,
+                                 mn_dtype act, mn_dtype param, void* workspace,
+                                 size_t workspace_bytes, void* stream)
+{
+    const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
+    return backward(mn::RMS, b, dgamma, nullptr, N, D, act, param, workspace, workspace_bytes,
+                    stream);
+}
+
+mn_status mn_layernorm_backward_ex(const void* X, const void* gamma, const float* mean,
+                                   const float* rstd, const void* dY, void* dX, float* dgamma,
+                                   float* dbeta, int64_t N, int64_t D, mn_dtype act,
+                                   mn_dtype param, void* workspace, size_t workspace_bytes,
+                                   void* stream)
+{
+    const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
+    return backward(mn::LN, b, dgamma, dbeta, N, D, act, param, workspace, workspace_bytes,
+                    stream);
+}
+
+mn_status mn_add_rmsnorm_backward_ex(const void* X, const void* R, const void* gamma,
+                                     const float* rstd, const void* dY, const void* dH, void* dX,
+                                     float* dgamma, int64_t N, int64_t D, mn_dtype act,
+                                     mn_dtype param, void* workspace, size_t workspace_bytes,
+                                     void* stream)
+{
+    const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
+    return backward(mn::ADD, b, dgamma, nullptr, N, D, act, param, workspace, workspace_bytes,
+                    stream);
+}
+
+mn_status mn_rmsnorm_backward_rows_ex(const void* X, const void* gamma, const float* rstd,
+                                      const void* dY, void* dX, int64_t N, int64_t D,
+                                      mn_dtype act, mn_dtype param, void* workspace,
+                                      size_t workspace_bytes, void* stream)
+{
+    const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
+    return backward_rows(mn::RMS, b, N, D, act, param, workspace, workspace_bytes, nullptr,
+                         nullptr, stream);
+}
+
+mn_status mn_layernorm_backward_rows_ex(const void* X, const void* gamma, const float* mean,
+                                        const float* rstd, const void* dY, void* dX, int64_t N,
+                                        int64_t D, mn_dtype act, mn_dtype param,
+                                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
+    return backward_rows(mn::LN, b, N, D, act, param, workspace, workspace_bytes, nullptr,
+                         nullptr, stream);
+}
+
+mn_status mn_add_rmsnorm_backward_rows_ex(const void* X, const void* R, const void* gamma,
+                                          const float* rstd, const void* dY, const void* dH,
+                                          void* dX, int64_t N, int64_t D, mn_dtype act,
+                                          mn_dtype param, void* workspace, size_t workspace_bytes,
+                                          void* stream)
+{
+    const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
+    return backward_rows(mn::ADD, b, N, D, act, param, workspace, workspace_bytes, nullptr,
+                         nullptr, stream);
+}
+
+// --- workspace, stage 2, diagnostics ----------------------------------------
 
 mn_status mn_norm_reduce_partials(mn_norm_kind kind, int64_t N, int64_t D, const void* workspace,
                                   size_t workspace_bytes, float* dgamma, float* dbeta,
@@ -289,6 +401,7 @@ const char* mn_status_string(mn_status s)
     case MN_ERR_ALIAS: return "an output overlaps an input or another output";
     case MN_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
     case MN_ERR_DEVICE: return "the HIP runtime rejected a launch";
+    case MN_ERR_DTYPE: return "unknown storage type";
     }
     return "unknown status";
 }

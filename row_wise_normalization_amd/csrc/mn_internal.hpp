@@ -9,37 +9,46 @@ namespace mn {
 
 enum Kind : int { RMS = 0, LN = 1, ADD = 2 };
 
-// Forward arguments. Pointers not used by a kind are null.
+// Storage types; the values match mn_dtype in mn_norm.h.
+enum Stor : int { ST_F16 = 0, ST_BF16 = 1, ST_F32 = 2 };
+
+inline int stor_bytes(int st) { return st == ST_F32 ? 4 : 2; }
+
+// Forward arguments. Pointers not used by a kind are null. Activations
+// (X, R, Y, H) share one storage type (a template parameter of the kernel);
+// gamma and beta share the parameter storage type `pdt`.
 struct FwdArgs {
-    const _Float16* X;
-    const _Float16* R;       // ADD
-    const _Float16* gamma;
-    const _Float16* beta;    // LN
-    _Float16* Y;
-    _Float16* H;             // ADD
+    const void* X;
+    const void* R;           // ADD
+    const void* gamma;
+    const void* beta;        // LN
+    void* Y;
+    void* H;                 // ADD
     float* mean;             // LN
     float* rstd;
     int64_t N;
     int32_t D;
+    int32_t pdt;             // storage type of gamma / beta
     float eps;
-    int64_t rows_per_block;  // contiguous rows owned by one workgroup
 };
 
-// Backward (stage 1) arguments.
+// Backward (stage 1) arguments. X, R, dY, dH, dX share the activation
+// storage type.
 struct BwdArgs {
-    const _Float16* X;
-    const _Float16* R;       // ADD
-    const _Float16* gamma;
-    const _Float16* dY;
-    const _Float16* dH;      // ADD, may be null (zero cotangent)
+    const void* X;
+    const void* R;           // ADD
+    const void* gamma;
+    const void* dY;
+    const void* dH;          // ADD, may be null (zero cotangent)
     const float* mean;       // LN
     const float* rstd;
-    _Float16* dX;
+    void* dX;
     float* part_g;           // [P][Dp] dgamma partials
     float* part_b;           // [P][Dp] dbeta partials (LN)
     int64_t N;
     int32_t D;
     int32_t Dp;              // partial row stride (D rounded up to 4)
+    int32_t pdt;             // storage type of gamma
 };
 
 // Column-reduce (stage 2) arguments.
@@ -63,8 +72,7 @@ struct Variant {
 
 struct FwdPlan {
     Variant v;
-    int64_t grid;
-    int64_t rows_per_block;
+    int64_t grid;            // one tile of (BLOCK / T) * U rows per workgroup
 };
 
 struct BwdPlan {
@@ -78,11 +86,12 @@ struct BwdPlan {
 int64_t bwd_partial_rows(int kind, int64_t N, int32_t D);
 int32_t partial_stride(int32_t D);
 
-FwdPlan plan_forward(int kind, int64_t N, int32_t D, bool vec_ok);
-BwdPlan plan_backward(int kind, int64_t N, int32_t D, bool vec_ok);
+FwdPlan plan_forward(int kind, int st, int64_t N, int32_t D, bool vec_ok);
+BwdPlan plan_backward(int kind, int st, int64_t N, int32_t D, bool vec_ok);
 
-hipError_t launch_forward(int kind, const FwdPlan& p, const FwdArgs& a, hipStream_t s);
-hipError_t launch_backward_rows(int kind, const BwdPlan& p, const BwdArgs& a, hipStream_t s);
+hipError_t launch_forward(int kind, int st, const FwdPlan& p, const FwdArgs& a, hipStream_t s);
+hipError_t launch_backward_rows(int kind, int st, const BwdPlan& p, const BwdArgs& a,
+                                hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 
 }  // namespace mn

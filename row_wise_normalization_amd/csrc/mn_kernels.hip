@@ -28,7 +28,8 @@ constexpr int kReduceCQ = 16;  // 64 columns per block, 64 segments
 //     inputs non-temporal loads (NT bit 1), except the LayerNorm forward,
 //     which measured slower with non-temporal loads.
 // Ids are unique within a kind; 8..10 are the element-wise variants (any D,
-// any alignment) shared by all kinds.
+// any alignment) shared by all kinds. Each row is instantiated for binary16,
+// bfloat16 and binary32 storage (binary32: see st_vec / st_cpt below).
 //
 //   id   T  VEC CPT  U  BLOCK  PF NT  max_d
 #define MN_FWD_RMS(X)                        \
@@ -106,72 +107,75 @@ hipError_t launch(Kernel k, dim3 grid, dim3 block, size_t shmem, hipStream_t s, 
     return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, shmem, s);
 }
 
-#define MN_FWD_CASE(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) \
-    case id:                                                 \
-        return launch(fwd_kernel<KIND, T, VEC, CPT, U, BLOCK, PF, NT>, grid, dim3(BLOCK), 0, s, a);
-#define MN_BWD_CASE(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) \
-    case id:                                                 \
-        return launch(bwd_kernel<KIND, T, VEC, CPT, U, BLOCK, PF, NT>, grid, dim3(BLOCK), p.shmem, s, a);
+// binary32 storage keeps 16-byte chunks: 4 elements per chunk and twice the
+// chunks per lane of the 16-bit shapes, so the row coverage T*CPT*VEC and
+// the bytes in flight per lane are unchanged.
+constexpr int st_vec(int st, int vec) { return (st == ST_F32 && vec == 8) ? 4 : vec; }
+constexpr int st_cpt(int st, int vec, int cpt) { return (st == ST_F32 && vec == 8) ? 2 * cpt : cpt; }
 
-template <int KIND> hipError_t launch_fwd_kind(const FwdPlan& p, const FwdArgs& a, hipStream_t s);
-template <int KIND> hipError_t launch_bwd_kind(const BwdPlan& p, const BwdArgs& a, hipStream_t s);
+#define MN_FWD_CASE(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD)                                  \
+    case id:                                                                                  \
+        return launch(fwd_kernel<KIND, ST, T, st_vec(ST, VEC), st_cpt(ST, VEC, CPT), U, BLOCK, \
+                                 PF, NT>,                                                     \
+                      grid, dim3(BLOCK), 0, s, a);
+#define MN_BWD_CASE(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD)                                  \
+    case id:                                                                                  \
+        return launch(bwd_kernel<KIND, ST, T, st_vec(ST, VEC), st_cpt(ST, VEC, CPT), U, BLOCK, \
+                                 PF, NT>,                                                     \
+                      grid, dim3(BLOCK), p.shmem, s, a);
 
-template <>
-hipError_t launch_fwd_kind<RMS>(const FwdPlan& p, const FwdArgs& a, hipStream_t s)
+template <int KIND, int ST>
+hipError_t launch_fwd(const FwdPlan& p, const FwdArgs& a, hipStream_t s)
 {
-    constexpr int KIND = RMS;
     const dim3 grid((unsigned)p.grid);
-    switch (p.v.id) { MN_FWD_RMS(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
+    if constexpr (KIND == RMS) {
+        switch (p.v.id) { MN_FWD_RMS(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
+    } else if constexpr (KIND == LN) {
+        switch (p.v.id) { MN_FWD_LN(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
+    } else {
+        switch (p.v.id) { MN_FWD_ADD(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
+    }
     return hipErrorInvalidValue;
 }
 
-template <>
-hipError_t launch_fwd_kind<LN>(const FwdPlan& p, const FwdArgs& a, hipStream_t s)
+template <int KIND, int ST>
+hipError_t launch_bwd(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
 {
-    constexpr int KIND = LN;
-    const dim3 grid((unsigned)p.grid);
-    switch (p.v.id) { MN_FWD_LN(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
-    return hipErrorInvalidValue;
-}
-
-template <>
-hipError_t launch_fwd_kind<ADD>(const FwdPlan& p, const FwdArgs& a, hipStream_t s)
-{
-    constexpr int KIND = ADD;
-    const dim3 grid((unsigned)p.grid);
-    switch (p.v.id) { MN_FWD_ADD(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
-    return hipErrorInvalidValue;
-}
-
-template <>
-hipError_t launch_bwd_kind<RMS>(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
-{
-    constexpr int KIND = RMS;
     const dim3 grid((unsigned)p.P);
-    switch (p.v.id) { MN_BWD_RMS(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
-    return hipErrorInvalidValue;
-}
-
-template <>
-hipError_t launch_bwd_kind<LN>(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
-{
-    constexpr int KIND = LN;
-    const dim3 grid((unsigned)p.P);
-    switch (p.v.id) { MN_BWD_LN(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
-    return hipErrorInvalidValue;
-}
-
-template <>
-hipError_t launch_bwd_kind<ADD>(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
-{
-    constexpr int KIND = ADD;
-    const dim3 grid((unsigned)p.P);
-    switch (p.v.id) { MN_BWD_ADD(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
+    if constexpr (KIND == RMS) {
+        switch (p.v.id) { MN_BWD_RMS(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
+    } else if constexpr (KIND == LN) {
+        switch (p.v.id) { MN_BWD_LN(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
+    } else {
+        switch (p.v.id) { MN_BWD_ADD(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
+    }
     return hipErrorInvalidValue;
 }
 
 #undef MN_FWD_CASE
 #undef MN_BWD_CASE
+
+template <int KIND>
+hipError_t launch_fwd_st(int st, const FwdPlan& p, const FwdArgs& a, hipStream_t s)
+{
+    switch (st) {
+    case ST_F16: return launch_fwd<KIND, ST_F16>(p, a, s);
+    case ST_BF16: return launch_fwd<KIND, ST_BF16>(p, a, s);
+    case ST_F32: return launch_fwd<KIND, ST_F32>(p, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int KIND>
+hipError_t launch_bwd_st(int st, const BwdPlan& p, const BwdArgs& a, hipStream_t s)
+{
+    switch (st) {
+    case ST_F16: return launch_bwd<KIND, ST_F16>(p, a, s);
+    case ST_BF16: return launch_bwd<KIND, ST_BF16>(p, a, s);
+    case ST_F32: return launch_bwd<KIND, ST_F32>(p, a, s);
+    }
+    return hipErrorInvalidValue;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -193,18 +197,19 @@ int64_t bwd_partial_rows(int kind, int64_t N, int32_t D)
     return N < bwd_blocks(kind, D) ? N : bwd_blocks(kind, D);
 }
 
-FwdPlan plan_forward(int kind, int64_t N, int32_t D, bool vec_ok)
+FwdPlan plan_forward(int kind, int st, int64_t N, int32_t D, bool vec_ok)
 {
+    (void)st;
     FwdPlan p;
     p.v = vec_ok ? pick(kFwdVec[kind], D) : pick(kFwdGen, D);
     // one tile of RPB*U rows per workgroup
-    p.rows_per_block = (int64_t)(p.v.BLOCK / p.v.T) * p.v.U;
-    p.grid = ceil_div(N, p.rows_per_block);
+    p.grid = ceil_div(N, (int64_t)(p.v.BLOCK / p.v.T) * p.v.U);
     return p;
 }
 
-BwdPlan plan_backward(int kind, int64_t N, int32_t D, bool vec_ok)
+BwdPlan plan_backward(int kind, int st, int64_t N, int32_t D, bool vec_ok)
 {
+    (void)st;
     BwdPlan p;
     p.v = vec_ok ? pick(kBwdVec[kind], D) : pick(kBwdGen, D);
     p.P = bwd_partial_rows(kind, N, D);
@@ -214,22 +219,23 @@ BwdPlan plan_backward(int kind, int64_t N, int32_t D, bool vec_ok)
     return p;
 }
 
-hipError_t launch_forward(int kind, const FwdPlan& p, const FwdArgs& a, hipStream_t s)
+hipError_t launch_forward(int kind, int st, const FwdPlan& p, const FwdArgs& a, hipStream_t s)
 {
     switch (kind) {
-    case RMS: return launch_fwd_kind<RMS>(p, a, s);
-    case LN: return launch_fwd_kind<LN>(p, a, s);
-    case ADD: return launch_fwd_kind<ADD>(p, a, s);
+    case RMS: return launch_fwd_st<RMS>(st, p, a, s);
+    case LN: return launch_fwd_st<LN>(st, p, a, s);
+    case ADD: return launch_fwd_st<ADD>(st, p, a, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_backward_rows(int kind, const BwdPlan& p, const BwdArgs& a, hipStream_t s)
+hipError_t launch_backward_rows(int kind, int st, const BwdPlan& p, const BwdArgs& a,
+                                hipStream_t s)
 {
     switch (kind) {
-    case RMS: return launch_bwd_kind<RMS>(p, a, s);
-    case LN: return launch_bwd_kind<LN>(p, a, s);
-    case ADD: return launch_bwd_kind<ADD>(p, a, s);
+    case RMS: return launch_bwd_st<RMS>(st, p, a, s);
+    case LN: return launch_bwd_st<LN>(st, p, a, s);
+    case ADD: return launch_bwd_st<ADD>(st, p, a, s);
     }
     return hipErrorInvalidValue;
 }

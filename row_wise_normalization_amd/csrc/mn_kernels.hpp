@@ -18,12 +18,11 @@
 //     the element-wise path for every other call.
 //   * Rows are processed in tiles of RPB*U rows (RPB row groups per
 //     workgroup, U rows per group per step). The forward gives each
-//     workgroup a contiguous range of rows (one tile in the shipped plans);
-//     the backward gives workgroup b the tiles b, b+P, b+2P, ..., so the
-//     workgroups in flight always cover one contiguous band of rows. With
-//     PF = 1 the loads of the next tile are issued before the current tile
-//     is reduced, so HBM reads stay in flight while a wave reduces and
-//     writes.
+//     workgroup exactly one tile; the backward gives workgroup b the tiles
+//     b, b+P, b+2P, ..., so the workgroups in flight always cover one
+//     contiguous band of rows. With PF = 1 (backward) the loads of the next
+//     tile are issued before the current tile is reduced, so HBM reads stay
+//     in flight while a wave reduces and writes.
 //   * Row sums are reduced inside a wave by DPP (quad permutes, half-row and
 //     row mirrors) and lane exchanges across 16-lane rows; row groups wider
 //     than a wave combine their per-wave sums through LDS in wave order.
@@ -44,58 +43,189 @@
 namespace mn {
 namespace kern {
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int VEC> struct HVec;
-template <> struct HVec<8> { typedef h8 type; };
-template <> struct HVec<1> { typedef _Float16 type; };
+// ---------------------------------------------------------------------------
+// Storage types. Activations use a template storage type ST: binary16
+// (_Float16), bfloat16 (__bf16; gfx950 converts with v_cvt_pk_bf16_f32,
+// round to nearest even) or binary32. A chunk is VEC consecutive elements,
+// 16 bytes for VEC = 8 (16-bit types) or VEC = 4 (binary32), or one element.
+// ---------------------------------------------------------------------------
 
-template <int VEC>
-__device__ __forceinline__ typename HVec<VEC>::type hzero()
+template <int ST> struct Elem;
+template <> struct Elem<ST_F16> { typedef _Float16 type; };
+template <> struct Elem<ST_BF16> { typedef __bf16 type; };
+template <> struct Elem<ST_F32> { typedef float type; };
+
+template <int ST, int VEC> struct Chunk {
+    typedef typename Elem<ST>::type E;
+    typedef E type __attribute__((ext_vector_type(VEC)));
+};
+template <int ST> struct Chunk<ST, 1> { typedef typename Elem<ST>::type type; };
+
+template <int ST, int VEC>
+__device__ __forceinline__ typename Chunk<ST, VEC>::type czero()
 {
-    typename HVec<VEC>::type z;
-    _Float16 s = (_Float16)0.0f;
-    z = s;  // splat for the vector type
+    typename Chunk<ST, VEC>::type z;
+    typename Elem<ST>::type s = (typename Elem<ST>::type)0.0f;
+    z = s;  // splat for vector types
     return z;
 }
 
-template <int VEC>
-__device__ __forceinline__ typename HVec<VEC>::type hload(const _Float16* p)
-{
-    return *reinterpret_cast<const typename HVec<VEC>::type*>(p);
-}
-
-// Load of a streamed input row (read once per launch); NT bit 1 marks it
+// Load of a streamed input chunk (read once per launch); NT bit 1 marks it
 // non-temporal so it does not displace reusable lines in the caches.
-template <int VEC, int NT>
-__device__ __forceinline__ typename HVec<VEC>::type sload(const _Float16* p)
+template <int ST, int VEC, int NT>
+__device__ __forceinline__ typename Chunk<ST, VEC>::type sload(const void* base, int64_t off)
 {
-    typedef typename HVec<VEC>::type HV;
-    if constexpr ((NT & 2) != 0) return __builtin_nontemporal_load(reinterpret_cast<const HV*>(p));
-    else return *reinterpret_cast<const HV*>(p);
+    typedef typename Chunk<ST, VEC>::type C;
+    const C* p = reinterpret_cast<const C*>(static_cast<const typename Elem<ST>::type*>(base) + off);
+    if constexpr ((NT & 2) != 0) return __builtin_nontemporal_load(p);
+    else return *p;
 }
 
-template <int VEC, int NT>
-__device__ __forceinline__ void hstore(_Float16* p, const typename HVec<VEC>::type& v)
+template <int ST, int VEC, int NT>
+__device__ __forceinline__ void cstore(void* base, int64_t off, const typename Chunk<ST, VEC>::type& v)
 {
-    typedef typename HVec<VEC>::type HV;
-    if constexpr ((NT & 1) != 0) __builtin_nontemporal_store(v, reinterpret_cast<HV*>(p));
-    else *reinterpret_cast<HV*>(p) = v;
+    typedef typename Chunk<ST, VEC>::type C;
+    C* p = reinterpret_cast<C*>(static_cast<typename Elem<ST>::type*>(base) + off);
+    if constexpr ((NT & 1) != 0) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+template <int ST, int VEC>
+__device__ __forceinline__ float cget(const typename Chunk<ST, VEC>::type& v, int e)
+{
+    if constexpr (VEC == 1) return (float)v;
+    else return (float)v[e];
+}
+
+// Round an fp32 value into a chunk element (round to nearest even).
+template <int ST, int VEC>
+__device__ __forceinline__ void cset(typename Chunk<ST, VEC>::type& v, int e, float f)
+{
+    typedef typename Elem<ST>::type E;
+    if constexpr (VEC == 1) v = (E)f;
+    else v[e] = (E)f;
+}
+
+// bfloat16 rounding of the exact sum a + b of two bfloat16 values. The fp32
+// sum s may itself be rounded; TwoSum recovers the exact remainder err with
+// a + b = s + err. Rounding s to bfloat16 rounds a + b correctly unless s
+// lies exactly halfway between two bfloat16 values (low 16 bits 0x8000) and
+// err != 0: then the exact sum is off that midpoint on the side of err.
+__device__ __forceinline__ __bf16 bf16_round_sum(float a, float b)
+{
+    const float s = a + b;
+    const float bb = s - a;
+    const float err = (a - (s - bb)) + (b - bb);
+    const unsigned u = __builtin_bit_cast(unsigned, s);
+    if ((u & 0xFFFFu) == 0x8000u && err != 0.0f && (u & 0x7F800000u) != 0x7F800000u) {
+        const bool away = (err > 0.0f) == (s > 0.0f);
+        const unsigned short h = (unsigned short)((u >> 16) + (away ? 1u : 0u));
+        return __builtin_bit_cast(__bf16, h);
+    }
+    return (__bf16)s;
+}
+
+// The fused add's H chunk: the sum x + r rounded once to the storage type.
+template <int ST, int VEC>
+__device__ __forceinline__ typename Chunk<ST, VEC>::type round_sum(
+    const typename Chunk<ST, VEC>::type& x, const typename Chunk<ST, VEC>::type& r)
+{
+    typedef typename Chunk<ST, VEC>::type C;
+    if constexpr (ST == ST_F16) {
+        return x + r;  // binary16 addition rounds the exact sum once
+    } else if constexpr (ST == ST_F32) {
+        return x + r;  // binary32 addition, likewise
+    } else {
+        C h;
+        if constexpr (VEC == 1) {
+            h = bf16_round_sum((float)x, (float)r);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) h[e] = bf16_round_sum((float)x[e], (float)r[e]);
+        }
+        return h;
+    }
+}
+
+// Parameters (gamma, beta) are read once per workgroup and widened to fp32
+// registers; their storage type pdt is a runtime value. Reading and widening
+// are separate steps: the loads are issued (under a uniform branch on pdt)
+// together with the first tile's loads, and widened after both are in
+// flight, so a workgroup waits for memory once, not once per parameter.
+//
+// PRaw holds one chunk as loaded: VEC binary32 words, or VEC 16-bit values
+// packed two per word (element e in the low half of word e/2 when e is even),
+// or, for VEC == 1, one 16-bit value in the low half of word 0.
+template <int VEC>
+struct PRaw {
+    uint32_t w[VEC];
+};
+
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+
+template <int VEC>
+__device__ __forceinline__ void load_param_raw(const void* base, int pdt, int off, PRaw<VEC>& r)
+{
+    if (pdt == ST_F32) {
+        const uint32_t* p = static_cast<const uint32_t*>(base) + off;
+        if constexpr (VEC % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < VEC / 4; ++q) {
+                const u4 v = *reinterpret_cast<const u4*>(p + 4 * q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r.w[4 * q + e] = v[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) r.w[e] = p[e];
+        }
+    } else {
+        const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+        if constexpr (VEC % 8 == 0) {
+#pragma unroll
+            for (int q = 0; q < VEC / 8; ++q) {
+                const u4 v = *reinterpret_cast<const u4*>(p + 8 * q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r.w[4 * q + e] = v[e];
+            }
+        } else if constexpr (VEC == 4) {
+            const u2 v = *reinterpret_cast<const u2*>(p);
+            r.w[0] = v[0];
+            r.w[1] = v[1];
+        } else {
+            static_assert(VEC == 1, "parameter chunks of 1, 4 or a multiple of 8 elements");
+            r.w[0] = p[0];
+        }
+    }
 }
 
 template <int VEC>
-__device__ __forceinline__ float hget(const typename HVec<VEC>::type& v, int e)
+__device__ __forceinline__ uint32_t param_half(const PRaw<VEC>& r, int e)
 {
-    if constexpr (VEC == 8) return (float)v[e];
-    else return (float)v;
+    return (VEC == 1) ? (r.w[0] & 0xFFFFu) : ((r.w[e / 2] >> (16 * (e & 1))) & 0xFFFFu);
 }
 
 template <int VEC>
-__device__ __forceinline__ void hset(typename HVec<VEC>::type& v, int e, float f)
+__device__ __forceinline__ void widen_param(const PRaw<VEC>& r, int pdt, bool valid,
+                                            float (&dst)[VEC])
 {
-    if constexpr (VEC == 8) v[e] = (_Float16)f;   // v_cvt_f16_f32: round to nearest even
-    else v = (_Float16)f;
+    // one uniform branch per chunk, each arm a straight run of conversions
+    if (pdt == ST_F32) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dst[e] = __uint_as_float(r.w[e]);
+    } else if (pdt == ST_BF16) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dst[e] = __uint_as_float(param_half(r, e) << 16);
+    } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            dst[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)param_half(r, e));
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dst[e] = valid ? dst[e] : 0.0f;
 }
 
 // Opaque register copy: afterwards the compiler cannot reuse fp32 values it
@@ -106,6 +236,17 @@ template <typename V>
 __device__ __forceinline__ void launder(V& v)
 {
     asm volatile("" : "+v"(v));
+}
+
+// Wait until every vector-memory operation issued so far has completed
+// (s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima). Placed just
+// before the next tile's loads are issued: the tile in registers is needed
+// next anyway, and the compiler then has nothing older to wait for, so its
+// own waits (it cannot count loads issued under divergent branches) no
+// longer also cover the loads that are meant to stay in flight.
+__device__ __forceinline__ void wait_vmem_all()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 // ---------------------------------------------------------------------------
@@ -179,21 +320,22 @@ struct RedBuf {
 // Forward: Y (and H), rstd (and mean).
 // ---------------------------------------------------------------------------
 
-template <int KIND, int T, int VEC, int CPT, int U, int BLOCK, int PF, int NT>
+template <int KIND, int ST, int T, int VEC, int CPT, int U, int BLOCK, int PF, int NT>
 __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
 {
-    typedef typename HVec<VEC>::type HV;
+    typedef typename Chunk<ST, VEC>::type HV;
     constexpr int RPB = BLOCK / T;
     constexpr int TILE = RPB * U;
     static_assert(BLOCK % T == 0, "block holds whole row groups");
+    static_assert(PF == 0, "the forward runs one tile per workgroup: nothing to prefetch");
     __shared__ float red[RedBuf<T, RPB, U>::size];
 
     const int tid = threadIdx.x;
     const int g = tid / T;
     const int l = tid % T;
     const int D = a.D;
-    const int64_t begin = (int64_t)blockIdx.x * a.rows_per_block;
-    const int64_t end = min(a.N, begin + a.rows_per_block);
+    const int64_t begin = (int64_t)blockIdx.x * TILE;
+    const int64_t end = a.N;
 
     int coff[CPT];
     bool cval[CPT];
@@ -203,11 +345,13 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
         cval[k] = coff[k] < D;
     }
 
-    HV gam[CPT], bet[CPT];
+    PRaw<VEC> graw[CPT], braw[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-        gam[k] = cval[k] ? hload<VEC>(a.gamma + coff[k]) : hzero<VEC>();
-        if constexpr (KIND == LN) bet[k] = cval[k] ? hload<VEC>(a.beta + coff[k]) : hzero<VEC>();
+        if (cval[k]) {
+            load_param_raw<VEC>(a.gamma, a.pdt, coff[k], graw[k]);
+            if constexpr (KIND == LN) load_param_raw<VEC>(a.beta, a.pdt, coff[k], braw[k]);
+        }
     }
 
     struct Tile {
@@ -222,21 +366,25 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 const bool ok = row < end && cval[k];
-                t.x[u][k] = ok ? sload<VEC, NT>(a.X + ro + coff[k]) : hzero<VEC>();
-                if constexpr (KIND == ADD) t.r[u][k] = ok ? sload<VEC, NT>(a.R + ro + coff[k]) : hzero<VEC>();
+                t.x[u][k] = ok ? sload<ST, VEC, NT>(a.X, ro + coff[k]) : czero<ST, VEC>();
+                if constexpr (KIND == ADD) t.r[u][k] = ok ? sload<ST, VEC, NT>(a.R, ro + coff[k]) : czero<ST, VEC>();
             }
         }
     };
 
     const float fD = (float)D;
     int phase = 0;
+    // parameter and tile loads are all in flight before the first wait
     Tile cur;
-    if constexpr (PF) load_tile(cur, begin);
-    for (int64_t base = begin; base < end; base += TILE) {
-        Tile nxt;
-        if constexpr (PF) load_tile(nxt, base + TILE);
-        else load_tile(cur, base);
-
+    load_tile(cur, begin);
+    float gam[CPT][VEC], bet[CPT][VEC];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        widen_param<VEC>(graw[k], a.pdt, cval[k], gam[k]);
+        if constexpr (KIND == LN) widen_param<VEC>(braw[k], a.pdt, cval[k], bet[k]);
+    }
+    {
+        const int64_t base = begin;
         int64_t row[U];
         bool rv[U];
 #pragma unroll
@@ -254,8 +402,8 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
             for (int k = 0; k < CPT; ++k)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    float v = hget<VEC>(cur.x[u][k], e);
-                    if constexpr (KIND == ADD) v += hget<VEC>(cur.r[u][k], e);
+                    float v = cget<ST, VEC>(cur.x[u][k], e);
+                    if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                     if constexpr (KIND == LN) acc += v;
                     else acc += v * v;
                 }
@@ -282,7 +430,7 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
                 for (int k = 0; k < CPT; ++k)
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        const float c = hget<VEC>(cur.x[u][k], e) - mu[u];
+                        const float c = cget<ST, VEC>(cur.x[u][k], e) - mu[u];
                         acc += cval[k] ? c * c : 0.0f;
                     }
                 s2[u] = acc;
@@ -311,24 +459,23 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
                 HV y;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    float v = hget<VEC>(cur.x[u][k], e);
-                    if constexpr (KIND == ADD) v += hget<VEC>(cur.r[u][k], e);
+                    float v = cget<ST, VEC>(cur.x[u][k], e);
+                    if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                     float o;
                     if constexpr (KIND == LN)
-                        o = (v - mu[u]) * rs[u] * hget<VEC>(gam[k], e) + hget<VEC>(bet[k], e);
+                        o = (v - mu[u]) * rs[u] * gam[k][e] + bet[k][e];
                     else
-                        o = v * rs[u] * hget<VEC>(gam[k], e);
-                    hset<VEC>(y, e, o);
+                        o = v * rs[u] * gam[k][e];
+                    cset<ST, VEC>(y, e, o);
                 }
-                hstore<VEC, NT>(a.Y + ro + coff[k], y);
+                cstore<ST, VEC, NT>(a.Y, ro + coff[k], y);
                 if constexpr (KIND == ADD) {
-                    // binary16 addition rounds the exact sum once (to nearest even)
-                    const HV h = cur.x[u][k] + cur.r[u][k];
-                    hstore<VEC, NT>(a.H + ro + coff[k], h);
+                    // the exact sum rounded once to the storage type
+                    const HV h = round_sum<ST, VEC>(cur.x[u][k], cur.r[u][k]);
+                    cstore<ST, VEC, NT>(a.H, ro + coff[k], h);
                 }
             }
         }
-        if constexpr (PF) cur = nxt;
     }
 }
 
@@ -336,10 +483,10 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
 // Backward stage 1: dX and per-workgroup parameter-gradient partials.
 // ---------------------------------------------------------------------------
 
-template <int KIND, int T, int VEC, int CPT, int U, int BLOCK, int PF, int NT>
+template <int KIND, int ST, int T, int VEC, int CPT, int U, int BLOCK, int PF, int NT>
 __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
 {
-    typedef typename HVec<VEC>::type HV;
+    typedef typename Chunk<ST, VEC>::type HV;
     constexpr int RPB = BLOCK / T;
     constexpr int TILE = RPB * U;
     constexpr int NR = (KIND == LN) ? 2 : 1;  // sums per row: c1 (and c2)
@@ -365,9 +512,10 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
         coff[k] = (k * T + l) * VEC;
         cval[k] = coff[k] < D;
     }
-    HV gam[CPT];
+    PRaw<VEC> graw[CPT];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) gam[k] = cval[k] ? hload<VEC>(a.gamma + coff[k]) : hzero<VEC>();
+    for (int k = 0; k < CPT; ++k)
+        if (cval[k]) load_param_raw<VEC>(a.gamma, a.pdt, coff[k], graw[k]);
 
     float accg[CPT][VEC], accb[CPT][VEC];
 #pragma unroll
@@ -393,9 +541,9 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 const bool ok = rok && cval[k];
-                t.x[u][k] = ok ? sload<VEC, NT>(a.X + ro + coff[k]) : hzero<VEC>();
-                if constexpr (KIND == ADD) t.r[u][k] = ok ? sload<VEC, NT>(a.R + ro + coff[k]) : hzero<VEC>();
-                t.dy[u][k] = ok ? sload<VEC, NT>(a.dY + ro + coff[k]) : hzero<VEC>();
+                t.x[u][k] = ok ? sload<ST, VEC, NT>(a.X, ro + coff[k]) : czero<ST, VEC>();
+                if constexpr (KIND == ADD) t.r[u][k] = ok ? sload<ST, VEC, NT>(a.R, ro + coff[k]) : czero<ST, VEC>();
+                t.dy[u][k] = ok ? sload<ST, VEC, NT>(a.dY, ro + coff[k]) : czero<ST, VEC>();
             }
         }
     };
@@ -405,11 +553,16 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
     Tile cur;
     const int64_t first = (int64_t)blockIdx.x * TILE;
     const int64_t stop = ntiles * TILE;  // uniform loop bound for the workgroup
-    if constexpr (PF) load_tile(cur, first);
+    load_tile(cur, first);
+    float gam[CPT][VEC];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) widen_param<VEC>(graw[k], a.pdt, cval[k], gam[k]);
     for (int64_t base = first; base < stop; base += tstride) {
         Tile nxt;
-        if constexpr (PF) load_tile(nxt, base + tstride);
-        else load_tile(cur, base);
+        if constexpr (PF) {
+            wait_vmem_all();
+            load_tile(nxt, base + tstride);
+        }
 
         // c1 = sum(g * xhat), c2 = sum(g), g = dY * gamma
         float c[U * NR];
@@ -420,10 +573,10 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
             for (int k = 0; k < CPT; ++k)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    float v = hget<VEC>(cur.x[u][k], e);
-                    if constexpr (KIND == ADD) v += hget<VEC>(cur.r[u][k], e);
+                    float v = cget<ST, VEC>(cur.x[u][k], e);
+                    if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                     const float xh = (v - cur.mu[u]) * cur.rs[u];
-                    const float gg = hget<VEC>(cur.dy[u][k], e) * hget<VEC>(gam[k], e);
+                    const float gg = cget<ST, VEC>(cur.dy[u][k], e) * gam[k][e];
                     a1 += gg * xh;
                     if constexpr (KIND == LN) a2 += gg;
                 }
@@ -452,30 +605,31 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 const bool ok = rok && cval[k];
-                HV dh = hzero<VEC>();
+                HV dh = czero<ST, VEC>();
                 if constexpr (KIND == ADD) {
-                    if (ok && a.dH != nullptr) dh = sload<VEC, NT>(a.dH + ro + coff[k]);
+                    if (ok && a.dH != nullptr) dh = sload<ST, VEC, NT>(a.dH, ro + coff[k]);
                 }
                 HV o;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    float v = hget<VEC>(cur.x[u][k], e);
-                    if constexpr (KIND == ADD) v += hget<VEC>(cur.r[u][k], e);
+                    float v = cget<ST, VEC>(cur.x[u][k], e);
+                    if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                     const float xh = (v - mu) * rs;
-                    const float dyv = hget<VEC>(cur.dy[u][k], e);
-                    const float gg = dyv * hget<VEC>(gam[k], e);
+                    const float dyv = cget<ST, VEC>(cur.dy[u][k], e);
+                    const float gg = dyv * gam[k][e];
                     float d;
                     if constexpr (KIND == LN) d = rs * (gg - c2 - xh * c1);
                     else d = rs * (gg - xh * c1);
-                    if constexpr (KIND == ADD) d += hget<VEC>(dh, e);
-                    hset<VEC>(o, e, d);
+                    if constexpr (KIND == ADD) d += cget<ST, VEC>(dh, e);
+                    cset<ST, VEC>(o, e, d);
                     accg[k][e] += dyv * xh;
                     if constexpr (KIND == LN) accb[k][e] += dyv;
                 }
-                if (ok) hstore<VEC, NT>(a.dX + ro + coff[k], o);
+                if (ok) cstore<ST, VEC, NT>(a.dX, ro + coff[k], o);
             }
         }
         if constexpr (PF) cur = nxt;
+        else if (base + tstride < stop) load_tile(cur, base + tstride);
     }
 
     // Fold the row groups of this workgroup in group order, then write the

@@ -18,10 +18,19 @@ def say(msg: str):
     sys.stdout.flush()
 
 
+_TORCH = {np.dtype(np.float16): torch.float16, np.dtype(np.uint16): torch.bfloat16,
+          np.dtype(np.float32): torch.float32}
+
+
 def dev(a: np.ndarray, offset: int = 0) -> torch.Tensor:
     """Upload ``a`` as a contiguous GPU tensor whose first element sits
-    ``offset`` elements past a 256-byte aligned allocation."""
-    t = torch.from_numpy(np.ascontiguousarray(a))
+    ``offset`` elements past a 256-byte aligned allocation (uint16 arrays
+    are bfloat16 bit patterns)."""
+    a = np.ascontiguousarray(a)
+    bf16 = a.dtype == np.uint16
+    t = torch.from_numpy(a.view(np.int16) if bf16 else a)
+    if bf16:
+        t = t.view(torch.bfloat16)
     if offset == 0:
         return t.to("cuda")
     buf = torch.empty(t.numel() + offset + 64, dtype=t.dtype, device="cuda")
@@ -39,41 +48,53 @@ def empty(shape, dtype, offset: int = 0) -> torch.Tensor:
 
 
 def host(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
-    return None if t is None else t.detach().cpu().numpy()
+    """Download a GPU tensor (bfloat16 comes back as uint16 bit patterns)."""
+    if t is None:
+        return None
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
 
 
 def run_gpu(kind: str, d: Dict[str, np.ndarray], eps: float, offset: int = 0,
-            use_dh: bool = True) -> Dict[str, np.ndarray]:
-    """Forward, then backward fed with the forward's own saved statistics."""
+            use_dh: bool = True, typed: Optional[bool] = None) -> Dict[str, np.ndarray]:
+    """Forward, then backward fed with the forward's own saved statistics.
+    fp16 inputs go through the fp16 entry points, other storage types (or
+    ``typed=True``) through the ``_ex`` entry points."""
     N, D = d["X"].shape
+    act = _TORCH[d["X"].dtype]
+    if typed is None:
+        typed = not (d["X"].dtype == np.float16 and d["gamma"].dtype == np.float16)
     X = dev(d["X"], offset)
     g = dev(d["gamma"], offset)
     dY = dev(d["dY"], offset)
     out: Dict[str, np.ndarray] = {}
-    Y = empty((N, D), torch.float16, offset)
+    Y = empty((N, D), act, offset)
     rstd = torch.empty(N, dtype=torch.float32, device="cuda")
-    dX = empty((N, D), torch.float16, offset)
+    dX = empty((N, D), act, offset)
     dgamma = torch.empty(D, dtype=torch.float32, device="cuda")
+    x = "_ex" if typed else ""
     if kind == "rms":
-        mn.mn_rmsnorm_forward(X, g, Y, rstd, eps)
+        getattr(mn, "mn_rmsnorm_forward" + x)(X, g, Y, rstd, eps)
         ws = mn.new_workspace(mn.MN_RMSNORM, N, D)
-        mn.mn_rmsnorm_backward(X, g, rstd, dY, dX, dgamma, ws)
+        getattr(mn, "mn_rmsnorm_backward" + x)(X, g, rstd, dY, dX, dgamma, ws)
     elif kind == "ln":
         b = dev(d["beta"], offset)
         mean = torch.empty(N, dtype=torch.float32, device="cuda")
         dbeta = torch.empty(D, dtype=torch.float32, device="cuda")
-        mn.mn_layernorm_forward(X, g, b, Y, mean, rstd, eps)
+        getattr(mn, "mn_layernorm_forward" + x)(X, g, b, Y, mean, rstd, eps)
         ws = mn.new_workspace(mn.MN_LAYERNORM, N, D)
-        mn.mn_layernorm_backward(X, g, mean, rstd, dY, dX, dgamma, dbeta, ws)
+        getattr(mn, "mn_layernorm_backward" + x)(X, g, mean, rstd, dY, dX, dgamma, dbeta, ws)
         out["mean"] = host(mean)
         out["dbeta"] = host(dbeta)
     elif kind == "add":
         R = dev(d["R"], offset)
         dH = dev(d["dH"], offset) if use_dh else None
-        Hs = empty((N, D), torch.float16, offset)
-        mn.mn_add_rmsnorm_forward(X, R, g, Hs, Y, rstd, eps)
+        Hs = empty((N, D), act, offset)
+        getattr(mn, "mn_add_rmsnorm_forward" + x)(X, R, g, Hs, Y, rstd, eps)
         ws = mn.new_workspace(mn.MN_ADD_RMSNORM, N, D)
-        mn.mn_add_rmsnorm_backward(X, R, g, rstd, dY, dH, dX, dgamma, ws)
+        getattr(mn, "mn_add_rmsnorm_backward" + x)(X, R, g, rstd, dY, dH, dX, dgamma, ws)
         out["H"] = host(Hs)
     else:
         raise ValueError(kind)
@@ -109,7 +130,7 @@ def reference(kind: str, d: Dict[str, np.ndarray], eps: float, rows: Optional[np
 
 
 def _f64(a):
-    return a.astype(np.float64)
+    return parity.as_f64(a)
 
 
 def cancel_scales(kind: str, d: Dict[str, np.ndarray], ref: Dict[str, np.ndarray],
@@ -122,17 +143,19 @@ def cancel_scales(kind: str, d: Dict[str, np.ndarray], ref: Dict[str, np.ndarray
         x = x + _f64(sub(d["R"]))
     rs = ref["rstd"][:, None]
     mu = ref["mean"][:, None] if kind == "ln" else 0.0
-    xh = (x - mu) * rs
+    # xhat = (x - mean) * rstd is formed from x and the fp32 mean, so its
+    # rounding error scales with |x| + |mean|, not with |x - mean|
+    xs = (np.abs(x) + np.abs(mu)) * rs
     g = _f64(sub(d["dY"])) * _f64(d["gamma"])[None, :]
-    A = np.abs(g * xh).mean(axis=1, keepdims=True)
-    sdx = rs * (np.abs(g) + np.abs(xh) * A)
+    A = (np.abs(g) * xs).mean(axis=1, keepdims=True)
+    sdx = rs * (np.abs(g) + xs * A)
     if kind == "ln":
         sdx = sdx + rs * np.abs(g).mean(axis=1, keepdims=True)
     if kind == "add" and use_dh:
         sdx = sdx + np.abs(_f64(sub(d["dH"])))
     sy = None
     if kind == "ln":
-        sy = np.abs(xh * _f64(d["gamma"])[None, :]) + np.abs(_f64(d["beta"]))[None, :]
+        sy = xs * np.abs(_f64(d["gamma"]))[None, :] + np.abs(_f64(d["beta"]))[None, :]
     return sdx, sy
 
 
@@ -142,27 +165,39 @@ def compare(kind: str, gpu: Dict[str, np.ndarray], ref: Dict[str, np.ndarray], w
             ) -> Dict[str, float]:
     """Check every element of the GPU outputs (restricted to ``rows``)
     against the oracle; returns the worst error per output. With ``inputs``
-    the fp32 cancellation allowance of parity.check_f16 applies; without it
-    every element must be within 2 ulp."""
+    the fp32 cancellation allowance of parity.check_out applies to 16-bit
+    outputs; without it every element must be within 2 ulp. float32 outputs
+    need ``inputs`` (their bound is relative to the fp32 terms)."""
     sel = (lambda a: a) if rows is None else (lambda a: a[rows])
     sdx = sy = None
     if inputs is not None:
         sdx, sy = cancel_scales(kind, inputs, ref, rows, use_dh)
+    if inputs is None and gpu["Y"].dtype == np.float32:
+        raise ValueError("float32 outputs are checked against the scale of their fp32 terms; "
+                         "pass the inputs")
     w: Dict[str, float] = {}
-    w["Y_ulp"], w["Y_fp32_admitted"] = parity.check_f16(sel(gpu["Y"]), ref["Y"], f"{what} Y",
+    w["Y_ulp"], w["Y_fp32_admitted"] = parity.check_out(sel(gpu["Y"]), ref["Y"], f"{what} Y",
                                                         scale=sy)
-    w["dX_ulp"], w["dX_fp32_admitted"] = parity.check_f16(sel(gpu["dX"]), ref["dX"],
+    w["dX_ulp"], w["dX_fp32_admitted"] = parity.check_out(sel(gpu["dX"]), ref["dX"],
                                                           f"{what} dX", scale=sdx)
     w["rstd_rel"] = parity.check_stat(sel(gpu["rstd"]), ref["rstd"], f"{what} rstd")
     w["dgamma"] = parity.check_grad(gpu["dgamma"], ref["dgamma"], f"{what} dgamma")
     if kind == "ln":
+        if inputs is not None:
+            # a mean near zero is a cancellation of fp32 terms of size mean|x|
+            sub = (lambda a: a) if rows is None else (lambda a: a[rows])
+            xa = np.abs(_f64(sub(inputs["X"]))).mean(axis=1)
+            mean_atol = np.maximum(mean_atol, parity.FP32_K * 2.0 ** -24 * xa)
         w["mean_rel"] = parity.check_stat(sel(gpu["mean"]), ref["mean"], f"{what} mean",
                                           atol=mean_atol)
         w["dbeta"] = parity.check_grad(gpu["dbeta"], ref["dbeta"], f"{what} dbeta")
     if kind == "add":
-        h = sel(gpu["H"]).view(np.uint16)
-        r = ref["H16"].view(np.uint16)
+        hg, hr = sel(gpu["H"]), ref["H16"]
+        assert hg.dtype == hr.dtype, f"{what} H: {hg.dtype} vs {hr.dtype}"
+        bits = np.uint32 if hg.dtype == np.float32 else np.uint16
+        sign = bits(0x80000000 if bits is np.uint32 else 0x8000)
+        h, r = hg.view(bits), hr.view(bits)
         # +0 and -0 are the same sum; otherwise H must be the exact rounded sum
-        same = (h == r) | (((h | r) & 0x7FFF) == 0)
-        assert same.all(), f"{what} H: {int((~same).sum())} elements differ from fp16(x + r)"
+        same = (h == r) | (((h | r) & ~sign) == 0)
+        assert same.all(), f"{what} H: {int((~same).sum())} elements differ from round(x + r)"
     return w

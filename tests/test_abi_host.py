@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings():
     L = mn.lib()
-    for code in range(7):
+    for code in range(8):
         assert len(L.mn_status_string(code)) > 0
     assert L.mn_last_device_error() == b""
 
@@ -115,6 +115,29 @@ def test_backward_validation():
                                    mn.workspace_bytes(mn.MN_LAYERNORM, N, D), S) == 1
     assert L.mn_add_rmsnorm_backward(A, NULL, B, C, Dp, NULL, E, F, N, D, W, ws, S) == 1
     assert L.mn_norm_reduce_partials(1, N, D, W, ws, F, NULL, S) == 1
+
+
+def test_typed_entry_points_validate_storage_types():
+    L = mn.lib()
+    f = ctypes.c_float(1e-5)
+    fwd = lambda act, par, **k: L.mn_rmsnorm_forward_ex(
+        k.get("X", A), B, k.get("Y", C), Dp, k.get("N", 16), k.get("D", 64), f, act, par, S)
+    for act in (mn.MN_F16, mn.MN_BF16, mn.MN_F32):
+        for par in (mn.MN_F16, mn.MN_BF16, mn.MN_F32):
+            assert fwd(act, par, N=0) == 2          # valid types reach the shape check
+    for bad in (-1, 3, 7):
+        assert fwd(bad, mn.MN_F16) == 7
+        assert fwd(mn.MN_F16, bad) == 7
+    # spans scale with the storage type: 16 x 64 float32 elements occupy 4096 bytes
+    assert fwd(mn.MN_F32, mn.MN_F32, Y=P(0x100000 + 16 * 64 * 4 - 4)) == 4
+    N, D = 16, 64
+    W = P(0xE0000000)
+    ws = mn.workspace_bytes(mn.MN_LAYERNORM, N, D)
+    assert L.mn_layernorm_backward_ex(A, B, P(0x30000000), C, Dp, E, F, G, N, D, 9, 0, W, ws,
+                                      S) == 7
+    assert L.mn_add_rmsnorm_backward_ex(A, B, C, Dp, E, NULL, F, G, N, D, 1, 4, W, ws, S) == 7
+    assert L.mn_add_rmsnorm_backward_rows_ex(A, B, C, Dp, E, NULL, F, N, D, 2, 2, W, 0, S) == 5
+    assert L.mn_layernorm_forward_ex(A, B, NULL, C, Dp, E, N, D, f, 1, 1, S) == 1
 
 
 def test_workspace_bytes():

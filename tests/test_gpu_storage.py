@@ -1,0 +1,113 @@
+"""bfloat16 and float32 storage through the typed (``_ex``) entry points,
+versus the fp64 oracle fed the same stored values.
+
+Activations/cotangents (X, R, dY, dH and the outputs Y, H, dX) share one
+storage type, gamma/beta another; every pairing of fp16, bf16 and float32 is
+run. The arithmetic is fp32 in every case, so only the rounding of the
+stored outputs differs: bf16 outputs are held to 2 bf16 ulp, float32 outputs
+to the fp32 evaluation bound (parity.check_out), and a stored H must equal
+round(x + r) in its own type.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_cases import compare, reference, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ["rms", "ln", "add"]
+STORAGE = ["f16", "bf16", "f32"]
+PAIRS = list(itertools.product(STORAGE, STORAGE))
+
+
+def _case(kind, N, D, seed, act, param):
+    return workloads.random_case(kind, N, D, seed, x_loc=0.5 if kind == "ln" else 0.0,
+                                 act=act, param=param)
+
+
+@pytest.mark.parametrize("D", [257, 1024, 4096, 8192])
+@pytest.mark.parametrize("act,param", PAIRS)
+@pytest.mark.parametrize("kind", KINDS)
+def test_storage_pairs(kind, act, param, D):
+    N = 300
+    say(f"[storage] {kind} act={act} param={param} N={N} D={D}")
+    d = _case(kind, N, D, 7000 + D, act, param)
+    w = compare(kind, run_gpu(kind, d, 1e-5), reference(kind, d, 1e-5),
+                f"{kind} {act}/{param} {N}x{D}", inputs=d)
+    say(f"[storage] {kind} act={act} param={param} D={D}: {w}")
+
+
+D_SWEEP = [1, 2, 3, 4, 7, 8, 63, 64, 127, 128, 200, 256, 260, 1000, 2048, 2056, 3000, 4095,
+           6000, 8191]
+
+
+@pytest.mark.parametrize("D", D_SWEEP)
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", KINDS)
+def test_storage_width_sweep(kind, act, D):
+    # several tiles and workgroup ranges plus a ragged tail of rows
+    N = 1023 if D <= 1024 else 333
+    say(f"[storage] sweep {kind} {act} N={N} D={D}")
+    d = _case(kind, N, D, 8000 + D, act, act)
+    compare(kind, run_gpu(kind, d, 1e-5), reference(kind, d, 1e-5), f"{kind} {act} {N}x{D}",
+            inputs=d)
+
+
+@pytest.mark.parametrize("D", [8, 128, 1024, 4096, 257])
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", KINDS)
+def test_storage_unaligned(kind, act, D):
+    # every tensor starts one element past a 16-byte boundary: element-wise kernels
+    N = 129
+    say(f"[storage] unaligned {kind} {act} N={N} D={D}")
+    d = _case(kind, N, D, 9000 + D, act, act)
+    compare(kind, run_gpu(kind, d, 1e-5, offset=1), reference(kind, d, 1e-5),
+            f"{kind} {act} {N}x{D} unaligned", inputs=d)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_typed_entry_points_match_fp16_ones(kind):
+    """With fp16 for both types the ``_ex`` entry points run the fp16 path."""
+    d = _case(kind, 500, 4096, 11, "f16", "f16")
+    a = run_gpu(kind, d, 1e-5, typed=False)
+    b = run_gpu(kind, d, 1e-5, typed=True)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_add_without_residual_cotangent_storage(act):
+    d = _case("add", 300, 1024, 12, act, "f32")
+    compare("add", run_gpu("add", d, 1e-5, use_dh=False),
+            reference("add", d, 1e-5, use_dh=False), f"add {act} dH=NULL", inputs=d,
+            use_dh=False)
+
+
+# Full-size shapes: bf16 activations with float32 parameters (the usual
+# mixed-precision training layout), and float32 throughout.
+FULL = [("rms_16384x4096", "bf16", "f32"), ("add_rms_32768x8192", "bf16", "f32"),
+        ("rms_1048576x128", "bf16", "bf16"), ("ln_16384x4096", "bf16", "f32"),
+        ("rms_16384x4096", "f32", "f32"), ("ln_16384x4096", "f32", "f32")]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,act,param", FULL)
+def test_full_size_storage(name, act, param):
+    w = workloads.WORKLOADS[name]
+    say(f"[storage] full {name} {act}/{param}: generating")
+    d = workloads.generate(w, act=act, param=param)
+    say(f"[storage] full {name} {act}/{param}: gpu")
+    gpu = run_gpu(w.kind, d, w.eps)
+    rows = workloads.sample_rows(w.N, 2048)
+    say(f"[storage] full {name} {act}/{param}: oracle on {len(rows)} rows")
+    ref = reference(w.kind, d, w.eps, rows=rows)
+    # bfloat16 keeps full relative precision down to 2^-126, so an output that
+    # is a deep cancellation of fp32 terms (dX near zero, LayerNorm y where
+    # gamma*xhat ~ -beta) can sit a few bf16 ulp off; those elements take the
+    # fp32 allowance, every other one the 2 ulp bound
+    inputs = d
+    worst = compare(w.kind, gpu, ref, f"{name} {act}/{param}", rows=rows, inputs=inputs)
+    say(f"[storage] full {name} {act}/{param}: worst {worst}")

@@ -14,9 +14,13 @@ Recipe (fixed, so that every run sees the same bits):
   Blocks are independent streams, so they are drawn on several threads and
   the values do not depend on the thread count; a smaller N yields a prefix
   of the same rows. Seed 0 unless a test says otherwise.
-* ``loc + scale * z`` is applied in float64, then the value is rounded
-  directly to fp16 (round to nearest, ties to even; numpy converts float64 to
-  float16 without passing through float32).
+* ``loc + scale * z`` is applied in float64, then the value is rounded to the
+  storage type, round to nearest, ties to even: fp16 directly from float64
+  (numpy converts float64 to float16 without passing through float32);
+  float32 directly; bfloat16 from the float32 value, by rounding its bit
+  pattern to the upper 16 bits (returned as uint16 bit patterns). The named
+  workloads are fp16 throughout; tests of the other storage types pass
+  ``act`` (X, R, dY, dH) and ``param`` (gamma, beta) to the generators.
 * The Llama-shape RMSNorm workload marks 1 % of its 4096 channels as outliers:
   41 channels drawn without replacement from ``default_rng(1)`` and sorted;
   those X columns are multiplied by 20 before rounding.
@@ -108,6 +112,24 @@ WORKLOADS: Dict[str, Workload] = {
 HEADLINE = "rms_16384x4096"
 
 
+# storage names -> numpy array type of the generated arrays (bfloat16 as bits)
+STORAGE = {"f16": np.float16, "bf16": np.uint16, "f32": np.float32}
+
+
+def to_storage(v: np.ndarray, storage: str) -> np.ndarray:
+    """Round float64 values to ``storage`` (see the recipe above)."""
+    if storage == "f16":
+        return v.astype(np.float16)
+    if storage == "f32":
+        return v.astype(np.float32)
+    if storage == "bf16":
+        u = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32)
+        # nearest, ties to even, on the 16 bits kept (the generated values are finite)
+        u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+        return u.astype(np.uint16)
+    raise ValueError(storage)
+
+
 def rows_per_chunk(D: int) -> int:
     return max(1, _CHUNK_ELEMS // max(int(D), 1))
 
@@ -125,7 +147,10 @@ def _fill_rows(seed: int, t: int, out: np.ndarray, spec: TensorSpec, outliers: n
         v += spec.loc
         if outliers.size:
             v[:, outliers] *= gain
-        out[r0:r1] = v  # float64 -> float16 assignment rounds to nearest even
+        if out.dtype == np.uint16:
+            out[r0:r1] = to_storage(v, "bf16")
+        else:
+            out[r0:r1] = v  # float64 -> float16/float32 assignment rounds to nearest even
 
     nblocks = (n + rows - 1) // rows
     if nblocks <= 1:
@@ -136,35 +161,40 @@ def _fill_rows(seed: int, t: int, out: np.ndarray, spec: TensorSpec, outliers: n
         list(ex.map(block, range(nblocks)))
 
 
-def generate(w: Workload, seed: int = 0, N: Optional[int] = None) -> Dict[str, np.ndarray]:
-    """Materialise every input tensor of ``w`` as contiguous fp16 numpy arrays.
+def generate(w: Workload, seed: int = 0, N: Optional[int] = None, act: str = "f16",
+             param: Optional[str] = None) -> Dict[str, np.ndarray]:
+    """Materialise every input tensor of ``w`` as contiguous numpy arrays:
+    per-row tensors in storage ``act``, gamma/beta in ``param`` (default:
+    ``act``); fp16 and float32 as such, bfloat16 as uint16 bit patterns.
 
     ``N`` overrides the row count (same distributions; the rows are a prefix
-    of the full workload's rows).
+    of the full workload's rows). The float64 draws do not depend on the
+    storage types, so the same seed gives the same values rounded differently.
     """
+    param = act if param is None else param
     n = w.N if N is None else int(N)
     outliers = w.outlier_channels()
     out: Dict[str, np.ndarray] = {}
     for t, spec in enumerate(w.tensors):
         if spec.per_row:
-            a = np.empty((n, w.D), dtype=np.float16)
+            a = np.empty((n, w.D), dtype=STORAGE[act])
             _fill_rows(seed, t, a, spec, outliers if spec.name == "X" else np.zeros(0, np.int64),
                        w.outlier_gain)
         else:
             z = np.random.default_rng([seed, t]).standard_normal(w.D)
-            a = (spec.loc + spec.scale * z).astype(np.float16)
+            a = to_storage(spec.loc + spec.scale * z, param)
         out[spec.name] = a
     return out
 
 
 def random_case(kind: str, N: int, D: int, seed: int, x_loc: float = 0.0, x_scale: float = 1.0,
                 dy_scale: float = 1.0, r_scale: float = 2.0, dh_scale: float = 0.5,
-                ) -> Dict[str, np.ndarray]:
+                act: str = "f16", param: Optional[str] = None) -> Dict[str, np.ndarray]:
     """Inputs for an arbitrary (kind, N, D) test case with the default recipe."""
     w = Workload(f"case_{kind}_{N}x{D}", kind, N, D, 1e-5,
                  _spec(kind, x=(x_loc, x_scale), dy=(0.0, dy_scale), r=(0.0, r_scale),
                        dh=(0.0, dh_scale)))
-    return generate(w, seed)
+    return generate(w, seed, act=act, param=param)
 
 
 def sample_rows(N: int, k: int, seed: int = 7) -> np.ndarray:
