@@ -37,7 +37,8 @@
  *       MN_ERR_WORKSPACE workspace NULL, smaller than
  *                        mn_norm_workspace_bytes(), or not 16-byte aligned
  *       MN_ERR_DEVICE    the HIP runtime rejected a launch
- *       MN_ERR_DTYPE     a storage type outside mn_dtype (the *_ex calls)
+ *       MN_ERR_DTYPE     a storage type outside mn_dtype, or a backward
+ *                        combination the *_ex calls do not provide
  *   - Results are bitwise deterministic for a given (N, D), pointer
  *     alignment class and device: every reduction has a fixed order and no
  *     floating-point atomics are used.
@@ -158,41 +159,49 @@ mn_status mn_add_rmsnorm_backward(const mn_f16* X, const mn_f16* R, const mn_f16
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Storage types beyond binary16. [meTile] contract: storage may be FP16 or
- * FP32 and the weight, bias and cotangents may each use either type, while
- * statistics, accumulation and parameter gradients are FP32. These entry
- * points take `act`, the storage type of the activations and cotangents
- * (X, R, Y, H, dY, dH, dX), and `param`, the storage type of gamma and beta;
- * each is MN_F16, MN_BF16 or MN_F32. Everything else -- formulas, saved fp32
- * statistics, fp32 dgamma/dbeta, workspace, validation, determinism -- is
- * exactly as for the binary16 calls above, which equal the *_ex calls with
- * act = param = MN_F16. Results in 16-bit storage are rounded to nearest,
+ * Storage types beyond binary16. The [meTile] normalization contract lets
+ * the source be FP16 or FP32 and lets weight, bias and cotangents each take
+ * either type, with statistics, accumulation and every returned gradient in
+ * FP32; this library adds bfloat16. The *_ex entry points take:
+ *   act    storage of the activations X, R and of the forward outputs Y, H
+ *   param  storage of gamma and beta (any of the three types)
+ *   cot    storage of the cotangents dY, dH            (backward only)
+ *   dxt    storage of dX (= dR)                       (backward only)
+ * each MN_F16, MN_BF16 or MN_F32. Backward combinations (act, cot, dxt):
+ *   act 16-bit (F16 or BF16): cot in {act, F32}, dxt in {act, F32};
+ *   act F32: cot any of the three, dxt F32.
+ * Anything else returns MN_ERR_DTYPE. Everything else -- formulas, saved
+ * fp32 statistics, fp32 dgamma/dbeta, workspace, validation, determinism --
+ * is exactly as for the binary16 calls above, which equal the *_ex calls
+ * with every type MN_F16. Results in 16-bit storage are rounded to nearest,
  * ties to even; the fused add's H is the exact sum x + r rounded once to
- * the activation type. Workspace sizes do not depend on the storage types.
+ * `act`. Workspace sizes do not depend on the storage types. The 128-bit
+ * vector kernels need D % 8 == 0 when `act` is 16-bit and D % 4 == 0 when it
+ * is MN_F32 (and 16-byte aligned pointers).
  * ------------------------------------------------------------------------- */
 mn_status mn_rmsnorm_forward_ex(const void* X, const void* gamma, void* Y, float* rstd,
                                 int64_t N, int64_t D, float eps, mn_dtype act, mn_dtype param,
                                 void* stream);
 mn_status mn_rmsnorm_backward_ex(const void* X, const void* gamma, const float* rstd,
                                  const void* dY, void* dX, float* dgamma, int64_t N, int64_t D,
-                                 mn_dtype act, mn_dtype param, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+                                 mn_dtype act, mn_dtype param, mn_dtype cot, mn_dtype dxt,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 mn_status mn_layernorm_forward_ex(const void* X, const void* gamma, const void* beta, void* Y,
                                   float* mean, float* rstd, int64_t N, int64_t D, float eps,
                                   mn_dtype act, mn_dtype param, void* stream);
 mn_status mn_layernorm_backward_ex(const void* X, const void* gamma, const float* mean,
                                    const float* rstd, const void* dY, void* dX, float* dgamma,
                                    float* dbeta, int64_t N, int64_t D, mn_dtype act,
-                                   mn_dtype param, void* workspace, size_t workspace_bytes,
-                                   void* stream);
+                                   mn_dtype param, mn_dtype cot, mn_dtype dxt, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 mn_status mn_add_rmsnorm_forward_ex(const void* X, const void* R, const void* gamma, void* H,
                                     void* Y, float* rstd, int64_t N, int64_t D, float eps,
                                     mn_dtype act, mn_dtype param, void* stream);
 mn_status mn_add_rmsnorm_backward_ex(const void* X, const void* R, const void* gamma,
                                      const float* rstd, const void* dY, const void* dH, void* dX,
                                      float* dgamma, int64_t N, int64_t D, mn_dtype act,
-                                     mn_dtype param, void* workspace, size_t workspace_bytes,
-                                     void* stream);
+                                     mn_dtype param, mn_dtype cot, mn_dtype dxt,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Workspace and diagnostics.
@@ -235,17 +244,18 @@ mn_status mn_add_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* R, const m
 /* Stage 1 with explicit storage types (see the *_ex calls above). */
 mn_status mn_rmsnorm_backward_rows_ex(const void* X, const void* gamma, const float* rstd,
                                       const void* dY, void* dX, int64_t N, int64_t D,
-                                      mn_dtype act, mn_dtype param, void* workspace,
-                                      size_t workspace_bytes, void* stream);
+                                      mn_dtype act, mn_dtype param, mn_dtype cot, mn_dtype dxt,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 mn_status mn_layernorm_backward_rows_ex(const void* X, const void* gamma, const float* mean,
                                         const float* rstd, const void* dY, void* dX, int64_t N,
-                                        int64_t D, mn_dtype act, mn_dtype param,
-                                        void* workspace, size_t workspace_bytes, void* stream);
+                                        int64_t D, mn_dtype act, mn_dtype param, mn_dtype cot,
+                                        mn_dtype dxt, void* workspace, size_t workspace_bytes,
+                                        void* stream);
 mn_status mn_add_rmsnorm_backward_rows_ex(const void* X, const void* R, const void* gamma,
                                           const float* rstd, const void* dY, const void* dH,
                                           void* dX, int64_t N, int64_t D, mn_dtype act,
-                                          mn_dtype param, void* workspace, size_t workspace_bytes,
-                                          void* stream);
+                                          mn_dtype param, mn_dtype cot, mn_dtype dxt,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stage 2 (column reduce): dgamma[j] = sum over partial rows p of
  * partial[p][j] in a fixed order (dbeta likewise for LayerNorm; pass

@@ -62,16 +62,18 @@ _SIGNATURES = {
     "mn_add_rmsnorm_backward_rows": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
     "mn_norm_reduce_partials": [ctypes.c_int, _I64, _I64, _P, _SZ, _P, _P, _P],
     "mn_rmsnorm_forward_ex": [_P, _P, _P, _P, _I64, _I64, _F, _C, _C, _P],
-    "mn_rmsnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ, _P],
+    "mn_rmsnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _C, _C, _P, _SZ, _P],
     "mn_layernorm_forward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _C, _C, _P],
-    "mn_layernorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ, _P],
+    "mn_layernorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _C, _C, _P,
+                                 _SZ, _P],
     "mn_add_rmsnorm_forward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _C, _C, _P],
-    "mn_add_rmsnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ,
-                                   _P],
-    "mn_rmsnorm_backward_rows_ex": [_P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ, _P],
-    "mn_layernorm_backward_rows_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ, _P],
-    "mn_add_rmsnorm_backward_rows_ex": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ,
-                                        _P],
+    "mn_add_rmsnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _C, _C,
+                                   _P, _SZ, _P],
+    "mn_rmsnorm_backward_rows_ex": [_P, _P, _P, _P, _P, _I64, _I64, _C, _C, _C, _C, _P, _SZ, _P],
+    "mn_layernorm_backward_rows_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _C, _C, _P,
+                                      _SZ, _P],
+    "mn_add_rmsnorm_backward_rows_ex": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _C, _C,
+                                        _P, _SZ, _P],
 }
 
 
@@ -236,10 +238,20 @@ def mn_norm_reduce_partials(kind: int, N: int, D: int, workspace, dgamma, dbeta=
 # Activations and cotangents share one storage type (float16, bfloat16 or
 # float32, taken from X); gamma and beta share another (taken from gamma).
 
+def _code(name, t):
+    if t.dtype not in DTYPE_CODE:
+        raise TypeError(f"{name}: storage must be float16, bfloat16 or float32, got {t.dtype}")
+    return DTYPE_CODE[t.dtype]
+
+
 def _types(X, gamma):
-    if X.dtype not in DTYPE_CODE or gamma.dtype not in DTYPE_CODE:
-        raise TypeError("storage types must be float16, bfloat16 or float32")
-    return DTYPE_CODE[X.dtype], DTYPE_CODE[gamma.dtype]
+    return _code("X", X), _code("gamma", gamma)
+
+
+def _bwd_types(X, gamma, dY, dX):
+    """(act, param, cot, dxt) from the tensors; the library rejects
+    combinations it does not provide (MN_ERR_DTYPE)."""
+    return _code("X", X), _code("gamma", gamma), _code("dY", dY), _code("dX", dX)
 
 
 def mn_rmsnorm_forward_ex(X, gamma, Y, rstd, eps: float, stream=None):
@@ -253,12 +265,12 @@ def mn_rmsnorm_forward_ex(X, gamma, Y, rstd, eps: float, stream=None):
 
 def mn_rmsnorm_backward_ex(X, gamma, rstd, dY, dX, dgamma, workspace, stream=None):
     N, D = _nd(X)
-    act, par = _types(X, gamma)
+    ty = _bwd_types(X, gamma, dY, dX)
     _check_t("X", X, X.dtype, (N, D)); _check_t("gamma", gamma, gamma.dtype, (D,))
-    _check_t("rstd", rstd, F32, (N,)); _check_t("dY", dY, X.dtype, (N, D))
-    _check_t("dX", dX, X.dtype, (N, D)); _check_t("dgamma", dgamma, F32, (D,))
+    _check_t("rstd", rstd, F32, (N,)); _check_t("dY", dY, dY.dtype, (N, D))
+    _check_t("dX", dX, dX.dtype, (N, D)); _check_t("dgamma", dgamma, F32, (D,))
     _call("mn_rmsnorm_backward_ex", _ptr(X), _ptr(gamma), _ptr(rstd), _ptr(dY), _ptr(dX),
-          _ptr(dgamma), N, D, act, par, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+          _ptr(dgamma), N, D, *ty, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
 
 
 def mn_layernorm_forward_ex(X, gamma, beta, Y, mean, rstd, eps: float, stream=None):
@@ -273,13 +285,13 @@ def mn_layernorm_forward_ex(X, gamma, beta, Y, mean, rstd, eps: float, stream=No
 
 def mn_layernorm_backward_ex(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, workspace, stream=None):
     N, D = _nd(X)
-    act, par = _types(X, gamma)
+    ty = _bwd_types(X, gamma, dY, dX)
     _check_t("X", X, X.dtype, (N, D)); _check_t("gamma", gamma, gamma.dtype, (D,))
     _check_t("mean", mean, F32, (N,)); _check_t("rstd", rstd, F32, (N,))
-    _check_t("dY", dY, X.dtype, (N, D)); _check_t("dX", dX, X.dtype, (N, D))
+    _check_t("dY", dY, dY.dtype, (N, D)); _check_t("dX", dX, dX.dtype, (N, D))
     _check_t("dgamma", dgamma, F32, (D,)); _check_t("dbeta", dbeta, F32, (D,))
     _call("mn_layernorm_backward_ex", _ptr(X), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dY),
-          _ptr(dX), _ptr(dgamma), _ptr(dbeta), N, D, act, par, _ptr(workspace),
+          _ptr(dX), _ptr(dgamma), _ptr(dbeta), N, D, *ty, _ptr(workspace),
           _ws_bytes(workspace), _stream(stream))
 
 
@@ -295,36 +307,36 @@ def mn_add_rmsnorm_forward_ex(X, R, gamma, H_out, Y, rstd, eps: float, stream=No
 
 def mn_add_rmsnorm_backward_ex(X, R, gamma, rstd, dY, dH, dX, dgamma, workspace, stream=None):
     N, D = _nd(X)
-    act, par = _types(X, gamma)
+    ty = _bwd_types(X, gamma, dY, dX)
     _check_t("X", X, X.dtype, (N, D)); _check_t("R", R, X.dtype, (N, D))
     _check_t("gamma", gamma, gamma.dtype, (D,)); _check_t("rstd", rstd, F32, (N,))
-    _check_t("dY", dY, X.dtype, (N, D)); _check_t("dH", dH, X.dtype, (N, D), optional=True)
-    _check_t("dX", dX, X.dtype, (N, D)); _check_t("dgamma", dgamma, F32, (D,))
+    _check_t("dY", dY, dY.dtype, (N, D)); _check_t("dH", dH, dY.dtype, (N, D), optional=True)
+    _check_t("dX", dX, dX.dtype, (N, D)); _check_t("dgamma", dgamma, F32, (D,))
     _call("mn_add_rmsnorm_backward_ex", _ptr(X), _ptr(R), _ptr(gamma), _ptr(rstd), _ptr(dY),
-          _ptr(dH), _ptr(dX), _ptr(dgamma), N, D, act, par, _ptr(workspace),
+          _ptr(dH), _ptr(dX), _ptr(dgamma), N, D, *ty, _ptr(workspace),
           _ws_bytes(workspace), _stream(stream))
 
 
 def mn_rmsnorm_backward_rows_ex(X, gamma, rstd, dY, dX, workspace, stream=None):
     N, D = _nd(X)
-    act, par = _types(X, gamma)
+    ty = _bwd_types(X, gamma, dY, dX)
     _call("mn_rmsnorm_backward_rows_ex", _ptr(X), _ptr(gamma), _ptr(rstd), _ptr(dY), _ptr(dX),
-          N, D, act, par, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+          N, D, *ty, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
 
 
 def mn_layernorm_backward_rows_ex(X, gamma, mean, rstd, dY, dX, workspace, stream=None):
     N, D = _nd(X)
-    act, par = _types(X, gamma)
+    ty = _bwd_types(X, gamma, dY, dX)
     _call("mn_layernorm_backward_rows_ex", _ptr(X), _ptr(gamma), _ptr(mean), _ptr(rstd),
-          _ptr(dY), _ptr(dX), N, D, act, par, _ptr(workspace), _ws_bytes(workspace),
+          _ptr(dY), _ptr(dX), N, D, *ty, _ptr(workspace), _ws_bytes(workspace),
           _stream(stream))
 
 
 def mn_add_rmsnorm_backward_rows_ex(X, R, gamma, rstd, dY, dH, dX, workspace, stream=None):
     N, D = _nd(X)
-    act, par = _types(X, gamma)
+    ty = _bwd_types(X, gamma, dY, dX)
     _call("mn_add_rmsnorm_backward_rows_ex", _ptr(X), _ptr(R), _ptr(gamma), _ptr(rstd),
-          _ptr(dY), _ptr(dH), _ptr(dX), N, D, act, par, _ptr(workspace), _ws_bytes(workspace),
+          _ptr(dY), _ptr(dH), _ptr(dX), N, D, *ty, _ptr(workspace), _ws_bytes(workspace),
           _stream(stream))
 
 
@@ -349,9 +361,9 @@ def rmsnorm_forward(X, gamma, eps: float = 1e-5, stream=None):
     return Y, rstd
 
 
-def rmsnorm_backward(X, gamma, rstd, dY, stream=None):
+def rmsnorm_backward(X, gamma, rstd, dY, stream=None, dx_dtype=None):
     N, D = _nd(X)
-    dX = torch.empty_like(X)
+    dX = torch.empty_like(X, dtype=dx_dtype or X.dtype)
     dgamma = torch.empty(D, dtype=F32, device=X.device)
     ws = new_workspace(MN_RMSNORM, N, D, X.device)
     mn_rmsnorm_backward_ex(X, gamma, rstd, dY, dX, dgamma, ws, stream)
@@ -367,9 +379,9 @@ def layernorm_forward(X, gamma, beta, eps: float = 1e-5, stream=None):
     return Y, mean, rstd
 
 
-def layernorm_backward(X, gamma, mean, rstd, dY, stream=None):
+def layernorm_backward(X, gamma, mean, rstd, dY, stream=None, dx_dtype=None):
     N, D = _nd(X)
-    dX = torch.empty_like(X)
+    dX = torch.empty_like(X, dtype=dx_dtype or X.dtype)
     dgamma = torch.empty(D, dtype=F32, device=X.device)
     dbeta = torch.empty(D, dtype=F32, device=X.device)
     ws = new_workspace(MN_LAYERNORM, N, D, X.device)
@@ -386,9 +398,9 @@ def add_rmsnorm_forward(X, R, gamma, eps: float = 1e-5, stream=None):
     return Hs, Y, rstd
 
 
-def add_rmsnorm_backward(X, R, gamma, rstd, dY, dH=None, stream=None):
+def add_rmsnorm_backward(X, R, gamma, rstd, dY, dH=None, stream=None, dx_dtype=None):
     N, D = _nd(X)
-    dX = torch.empty_like(X)
+    dX = torch.empty_like(X, dtype=dx_dtype or X.dtype)
     dgamma = torch.empty(D, dtype=F32, device=X.device)
     ws = new_workspace(MN_ADD_RMSNORM, N, D, X.device)
     mn_add_rmsnorm_backward_ex(X, R, gamma, rstd, dY, dH, dX, dgamma, ws, stream)

@@ -16,17 +16,24 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmn_norm.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["mn_kernels.hip", "mn_api.cpp"]
+# The kernel instances are split by activation storage type so that the
+# sources compile in parallel.
+SOURCES = ["mn_inst_f16.hip", "mn_inst_bf16.hip", "mn_inst_f32.hip", "mn_kernels.hip",
+           "mn_api.cpp"]
 ARCH = "gfx950"
 
 # Device-code flags. Packed fp32 instructions are disabled on purpose; no
 # fast-math and no denormal flushing (IEEE fp32 division and square root).
+# No implicit contraction: the kernels write every fused multiply-add they
+# use as fmaf, so each storage-type instance evaluates the same expressions
+# with the same roundings.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
     "-std=c++17",
     "-fPIC",
     "-Wall",
+    "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
@@ -39,18 +46,23 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; always rebuilds."""
+    """Compile every source (in parallel) and link the shared library; always
+    rebuilds."""
     objs = []
     build_dir = os.path.join(PKG, "_build")
     os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
+    procs = []
     for src in SOURCES:
         obj = os.path.join(build_dir, src + ".o")
         cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((src, subprocess.Popen(cmd)))
         objs.append(obj)
+    failed = [src for src, p in procs if p.wait() != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
     tmp = LIB_PATH + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -126,24 +126,35 @@ struct BwdIn {
     void* dX;
 };
 
-mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, int st, int pdt,
+// Storage types of one backward call: activations (X, R), parameters
+// (gamma), cotangents (dY, dH) and dX.
+struct BwdTypes {
+    int st, pdt, ct, ot;
+};
+
+mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, const BwdTypes& t,
                         void* ws, size_t ws_bytes, const float* dgamma, const float* dbeta,
                         void* stream)
 {
     if (!b.X || !b.gamma || !b.dY || !b.rstd || !b.dX) return MN_ERR_NULL;
     if (kind == mn::LN && !b.mean) return MN_ERR_NULL;
     if (kind == mn::ADD && !b.R) return MN_ERR_NULL;
-    if (!dtype_ok(st) || !dtype_ok(pdt)) return MN_ERR_DTYPE;
+    if (!dtype_ok(t.st) || !dtype_ok(t.pdt) || !dtype_ok(t.ct) || !dtype_ok(t.ot) ||
+        !mn::backward_types_supported(t.st, t.ct, t.ot))
+        return MN_ERR_DTYPE;
+    const int st = t.st;
     if (!shape_ok(N, D)) return MN_ERR_SHAPE;
     const size_t need = workspace_bytes(kind, N, D);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
 
     const size_t nd = (size_t)N * (size_t)D * (size_t)mn::stor_bytes(st);
-    const size_t dp = (size_t)D * (size_t)mn::stor_bytes(pdt);
-    const Span in[] = {span(b.X, nd), span(b.R, nd), span(b.gamma, dp), span(b.dY, nd),
-                       span(b.dH, nd), span(b.mean, (size_t)N * 4u),
+    const size_t ndc = (size_t)N * (size_t)D * (size_t)mn::stor_bytes(t.ct);
+    const size_t ndo = (size_t)N * (size_t)D * (size_t)mn::stor_bytes(t.ot);
+    const size_t dp = (size_t)D * (size_t)mn::stor_bytes(t.pdt);
+    const Span in[] = {span(b.X, nd), span(b.R, nd), span(b.gamma, dp), span(b.dY, ndc),
+                       span(b.dH, ndc), span(b.mean, (size_t)N * 4u),
                        span(b.rstd, (size_t)N * 4u)};
-    const Span out[] = {span(b.dX, nd), span(ws, need), span(dgamma, (size_t)D * 4u),
+    const Span out[] = {span(b.dX, ndo), span(ws, need), span(dgamma, (size_t)D * 4u),
                         span(dbeta, (size_t)D * 4u)};
     if (!alias_free(in, out)) return MN_ERR_ALIAS;
 
@@ -165,8 +176,9 @@ mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, int st, 
     a.N = N;
     a.D = (int32_t)D;
     a.Dp = plan.Dp;
-    a.pdt = pdt;
-    return device_status(mn::launch_backward_rows(kind, st, plan, a, as_stream(stream)));
+    a.pdt = t.pdt;
+    return device_status(
+        mn::launch_backward_rows(kind, st, t.ct, t.ot, plan, a, as_stream(stream)));
 }
 
 mn_status reduce_partials(int kind, int64_t N, int64_t D, const void* ws, size_t ws_bytes,
@@ -193,11 +205,13 @@ mn_status reduce_partials(int kind, int64_t N, int64_t D, const void* ws, size_t
     return device_status(mn::launch_reduce(a, as_stream(stream)));
 }
 
+const BwdTypes kF16{MN_F16, MN_F16, MN_F16, MN_F16};
+
 mn_status backward(int kind, const BwdIn& b, float* dgamma, float* dbeta, int64_t N, int64_t D,
-                   int st, int pdt, void* ws, size_t ws_bytes, void* stream)
+                   const BwdTypes& t, void* ws, size_t ws_bytes, void* stream)
 {
     if (!dgamma || (kind == mn::LN && !dbeta)) return MN_ERR_NULL;
-    mn_status s = backward_rows(kind, b, N, D, st, pdt, ws, ws_bytes, dgamma, dbeta, stream);
+    mn_status s = backward_rows(kind, b, N, D, t, ws, ws_bytes, dgamma, dbeta, stream);
     if (s != MN_OK) return s;
     return reduce_partials(kind, N, D, ws, ws_bytes, dgamma, dbeta, stream);
 }
@@ -236,8 +250,8 @@ mn_status mn_rmsnorm_backward(const mn_f16* X, const mn_f16* gamma, const float*
                               void* workspace, size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
-    return backward(mn::RMS, b, dgamma, nullptr, N, D, MN_F16, MN_F16, workspace,
-                    workspace_bytes, stream);
+    return backward(mn::RMS, b, dgamma, nullptr, N, D, kF16, workspace, workspace_bytes,
+                    stream);
 }
 
 mn_status mn_layernorm_backward(const mn_f16* X, const mn_f16* gamma, const float* mean,
@@ -246,7 +260,7 @@ mn_status mn_layernorm_backward(const mn_f16* X, const mn_f16* gamma, const floa
                                 size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
-    return backward(mn::LN, b, dgamma, dbeta, N, D, MN_F16, MN_F16, workspace, workspace_bytes,
+    return backward(mn::LN, b, dgamma, dbeta, N, D, kF16, workspace, workspace_bytes,
                     stream);
 }
 
@@ -256,8 +270,8 @@ mn_status mn_add_rmsnorm_backward(const mn_f16* X, const mn_f16* R, const mn_f16
                                   void* workspace, size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
-    return backward(mn::ADD, b, dgamma, nullptr, N, D, MN_F16, MN_F16, workspace,
-                    workspace_bytes, stream);
+    return backward(mn::ADD, b, dgamma, nullptr, N, D, kF16, workspace, workspace_bytes,
+                    stream);
 }
 
 mn_status mn_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const float* rstd,
@@ -265,7 +279,7 @@ mn_status mn_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const f
                                    void* workspace, size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
-    return backward_rows(mn::RMS, b, N, D, MN_F16, MN_F16, workspace, workspace_bytes, nullptr,
+    return backward_rows(mn::RMS, b, N, D, kF16, workspace, workspace_bytes, nullptr,
                          nullptr, stream);
 }
 
@@ -275,7 +289,7 @@ mn_status mn_layernorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const
                                      void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
-    return backward_rows(mn::LN, b, N, D, MN_F16, MN_F16, workspace, workspace_bytes, nullptr,
+    return backward_rows(mn::LN, b, N, D, kF16, workspace, workspace_bytes, nullptr,
                          nullptr, stream);
 }
 
@@ -285,7 +299,7 @@ mn_status mn_add_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* R, const m
                                        size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
-    return backward_rows(mn::ADD, b, N, D, MN_F16, MN_F16, workspace, workspace_bytes, nullptr,
+    return backward_rows(mn::ADD, b, N, D, kF16, workspace, workspace_bytes, nullptr,
                          nullptr, stream);
 }
 
@@ -316,65 +330,66 @@ mn_status mn_add_rmsnorm_forward_ex(const void* X, const void* R, const void* ga
 
 mn_status mn_rmsnorm_backward_ex(const void* X, const void* gamma, const float* rstd,
                                  const void* dY, void* dX, float* dgamma, int64_t N, int64_t D,
-                                 mn_dtype act, mn_dtype param, void* workspace,
-                                 size_t workspace_bytes, void* stream)
+                                 mn_dtype act, mn_dtype param, mn_dtype cot, mn_dtype dxt,
+                                 void* workspace, size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
-    return backward(mn::RMS, b, dgamma, nullptr, N, D, act, param, workspace, workspace_bytes,
-                    stream);
+    return backward(mn::RMS, b, dgamma, nullptr, N, D, BwdTypes{act, param, cot, dxt},
+                    workspace, workspace_bytes, stream);
 }
 
 mn_status mn_layernorm_backward_ex(const void* X, const void* gamma, const float* mean,
                                    const float* rstd, const void* dY, void* dX, float* dgamma,
                                    float* dbeta, int64_t N, int64_t D, mn_dtype act,
-                                   mn_dtype param, void* workspace, size_t workspace_bytes,
-                                   void* stream)
+                                   mn_dtype param, mn_dtype cot, mn_dtype dxt, void* workspace,
+                                   size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
-    return backward(mn::LN, b, dgamma, dbeta, N, D, act, param, workspace, workspace_bytes,
-                    stream);
+    return backward(mn::LN, b, dgamma, dbeta, N, D, BwdTypes{act, param, cot, dxt}, workspace,
+                    workspace_bytes, stream);
 }
 
 mn_status mn_add_rmsnorm_backward_ex(const void* X, const void* R, const void* gamma,
                                      const float* rstd, const void* dY, const void* dH, void* dX,
                                      float* dgamma, int64_t N, int64_t D, mn_dtype act,
-                                     mn_dtype param, void* workspace, size_t workspace_bytes,
-                                     void* stream)
+                                     mn_dtype param, mn_dtype cot, mn_dtype dxt,
+                                     void* workspace, size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
-    return backward(mn::ADD, b, dgamma, nullptr, N, D, act, param, workspace, workspace_bytes,
-                    stream);
+    return backward(mn::ADD, b, dgamma, nullptr, N, D, BwdTypes{act, param, cot, dxt},
+                    workspace, workspace_bytes, stream);
 }
 
 mn_status mn_rmsnorm_backward_rows_ex(const void* X, const void* gamma, const float* rstd,
                                       const void* dY, void* dX, int64_t N, int64_t D,
-                                      mn_dtype act, mn_dtype param, void* workspace,
-                                      size_t workspace_bytes, void* stream)
+                                      mn_dtype act, mn_dtype param, mn_dtype cot, mn_dtype dxt,
+                                      void* workspace, size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
-    return backward_rows(mn::RMS, b, N, D, act, param, workspace, workspace_bytes, nullptr,
-                         nullptr, stream);
+    return backward_rows(mn::RMS, b, N, D, BwdTypes{act, param, cot, dxt}, workspace,
+                         workspace_bytes, nullptr, nullptr, stream);
 }
 
 mn_status mn_layernorm_backward_rows_ex(const void* X, const void* gamma, const float* mean,
                                         const float* rstd, const void* dY, void* dX, int64_t N,
-                                        int64_t D, mn_dtype act, mn_dtype param,
-                                        void* workspace, size_t workspace_bytes, void* stream)
+                                        int64_t D, mn_dtype act, mn_dtype param, mn_dtype cot,
+                                        mn_dtype dxt, void* workspace, size_t workspace_bytes,
+                                        void* stream)
 {
     const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
-    return backward_rows(mn::LN, b, N, D, act, param, workspace, workspace_bytes, nullptr,
-                         nullptr, stream);
+    return backward_rows(mn::LN, b, N, D, BwdTypes{act, param, cot, dxt}, workspace,
+                         workspace_bytes, nullptr, nullptr, stream);
 }
 
 mn_status mn_add_rmsnorm_backward_rows_ex(const void* X, const void* R, const void* gamma,
                                           const float* rstd, const void* dY, const void* dH,
                                           void* dX, int64_t N, int64_t D, mn_dtype act,
-                                          mn_dtype param, void* workspace, size_t workspace_bytes,
-                                          void* stream)
+                                          mn_dtype param, mn_dtype cot, mn_dtype dxt,
+                                          void* workspace, size_t workspace_bytes, void* stream)
 {
     const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
-    return backward_rows(mn::ADD, b, N, D, act, param, workspace, workspace_bytes, nullptr,
-                         nullptr, stream);
+    return backward_rows(mn::ADD, b, N, D, BwdTypes{act, param, cot, dxt}, workspace,
+                         workspace_bytes, nullptr, nullptr, stream);
 }
 
 // --- workspace, stage 2, diagnostics ----------------------------------------
@@ -401,7 +416,7 @@ const char* mn_status_string(mn_status s)
     case MN_ERR_ALIAS: return "an output overlaps an input or another output";
     case MN_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
     case MN_ERR_DEVICE: return "the HIP runtime rejected a launch";
-    case MN_ERR_DTYPE: return "unknown storage type";
+    case MN_ERR_DTYPE: return "unknown storage type or unsupported combination";
     }
     return "unknown status";
 }

@@ -32,8 +32,8 @@ struct FwdArgs {
     float eps;
 };
 
-// Backward (stage 1) arguments. X, R, dY, dH, dX share the activation
-// storage type.
+// Backward (stage 1) arguments. X and R share the activation storage type,
+// dY and dH the cotangent storage type; dX has its own.
 struct BwdArgs {
     const void* X;
     const void* R;           // ADD
@@ -90,8 +90,10 @@ FwdPlan plan_forward(int kind, int st, int64_t N, int32_t D, bool vec_ok);
 BwdPlan plan_backward(int kind, int st, int64_t N, int32_t D, bool vec_ok);
 
 hipError_t launch_forward(int kind, int st, const FwdPlan& p, const FwdArgs& a, hipStream_t s);
-hipError_t launch_backward_rows(int kind, int st, const BwdPlan& p, const BwdArgs& a,
-                                hipStream_t s);
+// Backward storage combinations (activations st, cotangents ct, dX ot).
+bool backward_types_supported(int st, int ct, int ot);
+hipError_t launch_backward_rows(int kind, int st, int ct, int ot, const BwdPlan& p,
+                                const BwdArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 
 }  // namespace mn

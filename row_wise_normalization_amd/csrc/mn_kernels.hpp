@@ -405,7 +405,7 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
                     float v = cget<ST, VEC>(cur.x[u][k], e);
                     if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                     if constexpr (KIND == LN) acc += v;
-                    else acc += v * v;
+                    else acc = __builtin_fmaf(v, v, acc);
                 }
             s1[u] = acc;
         }
@@ -431,7 +431,7 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
                         const float c = cget<ST, VEC>(cur.x[u][k], e) - mu[u];
-                        acc += cval[k] ? c * c : 0.0f;
+                        acc = cval[k] ? __builtin_fmaf(c, c, acc) : acc;
                     }
                 s2[u] = acc;
             }
@@ -463,7 +463,7 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
                     if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                     float o;
                     if constexpr (KIND == LN)
-                        o = (v - mu[u]) * rs[u] * gam[k][e] + bet[k][e];
+                        o = __builtin_fmaf((v - mu[u]) * rs[u], gam[k][e], bet[k][e]);
                     else
                         o = v * rs[u] * gam[k][e];
                     cset<ST, VEC>(y, e, o);
@@ -483,10 +483,14 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
 // Backward stage 1: dX and per-workgroup parameter-gradient partials.
 // ---------------------------------------------------------------------------
 
-template <int KIND, int ST, int T, int VEC, int CPT, int U, int BLOCK, int PF, int NT>
+// Storage types: ST for X and R, CT for the cotangents dY and dH, OT for dX.
+template <int KIND, int ST, int CT, int OT, int T, int VEC, int CPT, int U, int BLOCK, int PF,
+          int NT>
 __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
 {
     typedef typename Chunk<ST, VEC>::type HV;
+    typedef typename Chunk<CT, VEC>::type CV;
+    typedef typename Chunk<OT, VEC>::type OV;
     constexpr int RPB = BLOCK / T;
     constexpr int TILE = RPB * U;
     constexpr int NR = (KIND == LN) ? 2 : 1;  // sums per row: c1 (and c2)
@@ -527,7 +531,8 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
         }
 
     struct Tile {
-        HV x[U][CPT], r[U][CPT], dy[U][CPT];
+        HV x[U][CPT], r[U][CPT];
+        CV dy[U][CPT];
         float rs[U], mu[U];
     };
     auto load_tile = [&](Tile& t, int64_t base) {
@@ -543,7 +548,7 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                 const bool ok = rok && cval[k];
                 t.x[u][k] = ok ? sload<ST, VEC, NT>(a.X, ro + coff[k]) : czero<ST, VEC>();
                 if constexpr (KIND == ADD) t.r[u][k] = ok ? sload<ST, VEC, NT>(a.R, ro + coff[k]) : czero<ST, VEC>();
-                t.dy[u][k] = ok ? sload<ST, VEC, NT>(a.dY, ro + coff[k]) : czero<ST, VEC>();
+                t.dy[u][k] = ok ? sload<CT, VEC, NT>(a.dY, ro + coff[k]) : czero<CT, VEC>();
             }
         }
     };
@@ -576,8 +581,8 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                     float v = cget<ST, VEC>(cur.x[u][k], e);
                     if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                     const float xh = (v - cur.mu[u]) * cur.rs[u];
-                    const float gg = cget<ST, VEC>(cur.dy[u][k], e) * gam[k][e];
-                    a1 += gg * xh;
+                    const float gg = cget<CT, VEC>(cur.dy[u][k], e) * gam[k][e];
+                    a1 = __builtin_fmaf(gg, xh, a1);
                     if constexpr (KIND == LN) a2 += gg;
                 }
             c[u * NR] = a1;
@@ -605,27 +610,28 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 const bool ok = rok && cval[k];
-                HV dh = czero<ST, VEC>();
+                CV dh = czero<CT, VEC>();
                 if constexpr (KIND == ADD) {
-                    if (ok && a.dH != nullptr) dh = sload<ST, VEC, NT>(a.dH, ro + coff[k]);
+                    if (ok && a.dH != nullptr) dh = sload<CT, VEC, NT>(a.dH, ro + coff[k]);
                 }
-                HV o;
+                OV o;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     float v = cget<ST, VEC>(cur.x[u][k], e);
                     if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                     const float xh = (v - mu) * rs;
-                    const float dyv = cget<ST, VEC>(cur.dy[u][k], e);
+                    const float dyv = cget<CT, VEC>(cur.dy[u][k], e);
                     const float gg = dyv * gam[k][e];
                     float d;
-                    if constexpr (KIND == LN) d = rs * (gg - c2 - xh * c1);
-                    else d = rs * (gg - xh * c1);
-                    if constexpr (KIND == ADD) d += cget<ST, VEC>(dh, e);
-                    cset<ST, VEC>(o, e, d);
-                    accg[k][e] += dyv * xh;
+                    if constexpr (KIND == LN) d = rs * __builtin_fmaf(-xh, c1, gg - c2);
+                    else if constexpr (KIND == ADD)
+                        d = __builtin_fmaf(rs, __builtin_fmaf(-xh, c1, gg), cget<CT, VEC>(dh, e));
+                    else d = rs * __builtin_fmaf(-xh, c1, gg);
+                    cset<OT, VEC>(o, e, d);
+                    accg[k][e] = __builtin_fmaf(dyv, xh, accg[k][e]);
                     if constexpr (KIND == LN) accb[k][e] += dyv;
                 }
-                if (ok) cstore<ST, VEC, NT>(a.dX, ro + coff[k], o);
+                if (ok) cstore<OT, VEC, NT>(a.dX, ro + coff[k], o);
             }
         }
         if constexpr (PF) cur = nxt;

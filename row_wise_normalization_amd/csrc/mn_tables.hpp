@@ -1,0 +1,106 @@
+// mn_tables.hpp -- the launch tables of the gfx950 normalization kernels:
+// which template instance serves which width and storage combination.
+// Shared by the planner (mn_kernels.hip) and the per-storage instance files
+// (mn_inst_*.hip), which define and instantiate the launchers.
+#pragma once
+
+#include "mn_internal.hpp"
+
+namespace mn {
+
+// ---------------------------------------------------------------------------
+// Variant tables.
+// ---------------------------------------------------------------------------
+
+// Variant tables, one per norm kind and direction; a row is chosen by the
+// smallest max_d >= D. Shapes come from timing sweeps on MI355X at
+// 16384x4096, 32768x8192 and 1048576x128:
+//   * the forward runs one tile per workgroup (many small workgroups keep
+//     the most reads in flight);
+//   * the backward runs 256 long-lived workgroups (each owns one partial
+//     row of dgamma and the tiles b, b+256, ...), prefetches its next tile
+//     and keeps two rows per row group in flight;
+//   * streamed outputs use non-temporal stores (NT bit 0) and streamed
+//     inputs non-temporal loads (NT bit 1), except the LayerNorm forward,
+//     which measured slower with non-temporal loads.
+// Ids are unique within a kind; 8..10 are the element-wise variants (any D,
+// any alignment) shared by all kinds. Each row is instantiated for every
+// storage combination (binary32 activations: see st_vec / st_cpt below).
+//
+//   id   T  VEC CPT  U  BLOCK  PF NT  max_d
+#define MN_FWD_RMS(X)                        \
+    X(0, 8, 8, 1, 4, 256, 0, 3, 64)          \
+    X(1, 16, 8, 1, 2, 256, 0, 3, 128)        \
+    X(2, 32, 8, 1, 2, 256, 0, 3, 256)        \
+    X(3, 64, 8, 1, 2, 256, 0, 3, 512)        \
+    X(4, 128, 8, 1, 1, 256, 0, 3, 1024)      \
+    X(5, 256, 8, 1, 1, 256, 0, 3, 2048)      \
+    X(6, 256, 8, 2, 1, 256, 0, 3, 4096)      \
+    X(7, 1024, 8, 1, 1, 1024, 0, 3, 8192)
+#define MN_FWD_LN(X)                         \
+    X(0, 8, 8, 1, 4, 256, 0, 1, 64)          \
+    X(1, 16, 8, 1, 2, 256, 0, 1, 128)        \
+    X(2, 32, 8, 1, 2, 256, 0, 1, 256)        \
+    X(3, 64, 8, 1, 2, 256, 0, 1, 512)        \
+    X(4, 128, 8, 1, 1, 256, 0, 1, 1024)      \
+    X(5, 256, 8, 1, 1, 256, 0, 1, 2048)      \
+    X(6, 256, 8, 2, 2, 256, 0, 1, 4096)      \
+    X(7, 1024, 8, 1, 1, 1024, 0, 1, 8192)
+#define MN_FWD_ADD(X) MN_FWD_RMS(X)
+#define MN_FWD_GEN(X)                        \
+    X(8, 64, 1, 16, 1, 256, 0, 1, 1024)      \
+    X(9, 256, 1, 16, 1, 256, 0, 1, 4096)     \
+    X(10, 512, 1, 16, 1, 512, 0, 1, 8192)
+
+#define MN_BWD_RMS(X)                        \
+    X(0, 8, 8, 1, 4, 256, 1, 3, 64)          \
+    X(1, 16, 8, 1, 4, 256, 1, 3, 128)        \
+    X(2, 32, 8, 1, 4, 256, 1, 3, 256)        \
+    X(3, 64, 8, 1, 2, 256, 1, 3, 512)        \
+    X(4, 128, 8, 1, 2, 512, 1, 3, 1024)      \
+    X(5, 256, 8, 1, 2, 512, 1, 3, 2048)      \
+    X(6, 512, 8, 1, 2, 512, 1, 3, 4096)      \
+    X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
+#define MN_BWD_LN(X)                         \
+    X(0, 8, 8, 1, 4, 256, 1, 3, 64)          \
+    X(1, 16, 8, 1, 4, 256, 1, 3, 128)        \
+    X(2, 32, 8, 1, 4, 256, 1, 3, 256)        \
+    X(3, 64, 8, 1, 2, 256, 1, 3, 512)        \
+    X(4, 64, 8, 2, 2, 256, 1, 3, 1024)       \
+    X(5, 128, 8, 2, 2, 512, 1, 3, 2048)      \
+    X(6, 256, 8, 2, 2, 512, 1, 3, 4096)      \
+    X(7, 512, 8, 2, 1, 512, 1, 3, 8192)
+#define MN_BWD_ADD(X) MN_BWD_RMS(X)
+#define MN_BWD_GEN(X)                        \
+    X(8, 64, 1, 16, 1, 256, 1, 1, 1024)      \
+    X(9, 256, 1, 16, 1, 256, 1, 1, 4096)     \
+    X(10, 512, 1, 16, 1, 512, 1, 1, 8192)
+
+// Storage combinations of the backward (X/R, dY/dH, dX), one list per
+// activation type: cotangents in the activation type or binary32 and dX in
+// the activation type or binary32; binary32 activations take cotangents of
+// any type and give a binary32 dX.
+#define MN_BWD_TYPES_F16(X)                                                     \
+    X(ST_F16, ST_F16, ST_F16) X(ST_F16, ST_F16, ST_F32) X(ST_F16, ST_F32, ST_F16) \
+    X(ST_F16, ST_F32, ST_F32)
+#define MN_BWD_TYPES_BF16(X)                                                         \
+    X(ST_BF16, ST_BF16, ST_BF16) X(ST_BF16, ST_BF16, ST_F32) X(ST_BF16, ST_F32, ST_BF16) \
+    X(ST_BF16, ST_F32, ST_F32)
+#define MN_BWD_TYPES_F32(X) \
+    X(ST_F32, ST_F32, ST_F32) X(ST_F32, ST_F16, ST_F32) X(ST_F32, ST_BF16, ST_F32)
+#define MN_BWD_TYPES(X) MN_BWD_TYPES_F16(X) MN_BWD_TYPES_BF16(X) MN_BWD_TYPES_F32(X)
+
+// binary32 storage keeps 16-byte chunks: 4 elements per chunk and twice the
+// chunks per lane of the 16-bit shapes, so the row coverage T*CPT*VEC and
+// the bytes in flight per lane are unchanged.
+constexpr int st_vec(int st, int vec) { return (st == ST_F32 && vec == 8) ? 4 : vec; }
+constexpr int st_cpt(int st, int vec, int cpt) { return (st == ST_F32 && vec == 8) ? 2 * cpt : cpt; }
+
+// Launch one planned forward / backward-stage-1 kernel; defined and
+// explicitly instantiated per activation storage type in mn_inst_*.hip.
+template <int KIND, int ST>
+hipError_t launch_fwd(const FwdPlan& p, const FwdArgs& a, hipStream_t s);
+template <int KIND, int ST, int CT, int OT>
+hipError_t launch_bwd(const BwdPlan& p, const BwdArgs& a, hipStream_t s);
+
+}  // namespace mn

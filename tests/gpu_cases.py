@@ -58,21 +58,25 @@ def host(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
 
 
 def run_gpu(kind: str, d: Dict[str, np.ndarray], eps: float, offset: int = 0,
-            use_dh: bool = True, typed: Optional[bool] = None) -> Dict[str, np.ndarray]:
+            use_dh: bool = True, typed: Optional[bool] = None,
+            dx_dtype: Optional[torch.dtype] = None) -> Dict[str, np.ndarray]:
     """Forward, then backward fed with the forward's own saved statistics.
-    fp16 inputs go through the fp16 entry points, other storage types (or
-    ``typed=True``) through the ``_ex`` entry points."""
+    All-fp16 cases go through the fp16 entry points, any other storage (or
+    ``typed=True``) through the ``_ex`` entry points; dX is stored in
+    ``dx_dtype`` (default: the activation type)."""
     N, D = d["X"].shape
     act = _TORCH[d["X"].dtype]
+    dxt = act if dx_dtype is None else dx_dtype
     if typed is None:
-        typed = not (d["X"].dtype == np.float16 and d["gamma"].dtype == np.float16)
+        typed = not (d["X"].dtype == np.float16 and d["gamma"].dtype == np.float16 and
+                     d["dY"].dtype == np.float16 and dxt == torch.float16)
     X = dev(d["X"], offset)
     g = dev(d["gamma"], offset)
     dY = dev(d["dY"], offset)
     out: Dict[str, np.ndarray] = {}
     Y = empty((N, D), act, offset)
     rstd = torch.empty(N, dtype=torch.float32, device="cuda")
-    dX = empty((N, D), act, offset)
+    dX = empty((N, D), dxt, offset)
     dgamma = torch.empty(D, dtype=torch.float32, device="cuda")
     x = "_ex" if typed else ""
     if kind == "rms":
@@ -172,7 +176,7 @@ def compare(kind: str, gpu: Dict[str, np.ndarray], ref: Dict[str, np.ndarray], w
     sdx = sy = None
     if inputs is not None:
         sdx, sy = cancel_scales(kind, inputs, ref, rows, use_dh)
-    if inputs is None and gpu["Y"].dtype == np.float32:
+    if inputs is None and np.float32 in (gpu["Y"].dtype, gpu["dX"].dtype):
         raise ValueError("float32 outputs are checked against the scale of their fp32 terms; "
                          "pass the inputs")
     w: Dict[str, float] = {}

@@ -133,11 +133,33 @@ def test_typed_entry_points_validate_storage_types():
     N, D = 16, 64
     W = P(0xE0000000)
     ws = mn.workspace_bytes(mn.MN_LAYERNORM, N, D)
-    assert L.mn_layernorm_backward_ex(A, B, P(0x30000000), C, Dp, E, F, G, N, D, 9, 0, W, ws,
-                                      S) == 7
-    assert L.mn_add_rmsnorm_backward_ex(A, B, C, Dp, E, NULL, F, G, N, D, 1, 4, W, ws, S) == 7
-    assert L.mn_add_rmsnorm_backward_rows_ex(A, B, C, Dp, E, NULL, F, N, D, 2, 2, W, 0, S) == 5
+    F16, BF16, F32 = mn.MN_F16, mn.MN_BF16, mn.MN_F32
+    lnb = lambda act, par, cot, dxt, ws=ws: L.mn_layernorm_backward_ex(
+        A, B, P(0x30000000), C, Dp, E, F, G, N, D, act, par, cot, dxt, W, ws, S)
+    assert lnb(9, F16, F16, F16) == 7
+    assert lnb(F16, 9, F16, F16) == 7
+    assert lnb(F16, F16, -1, F16) == 7
+    assert lnb(F16, F16, F16, 3) == 7
+    # the backward storage combinations provided (act, cot, dxt); a valid
+    # combination gets as far as the workspace check
+    provided = {(a, c, o) for a in (F16, BF16) for c in (a, F32) for o in (a, F32)}
+    provided |= {(F32, c, F32) for c in (F16, BF16, F32)}
+    for act in (F16, BF16, F32):
+        for cot in (F16, BF16, F32):
+            for dxt in (F16, BF16, F32):
+                want = 5 if (act, cot, dxt) in provided else 7
+                assert lnb(act, BF16, cot, dxt, ws=0) == want, (act, cot, dxt)
+    assert L.mn_add_rmsnorm_backward_ex(A, B, C, Dp, E, NULL, F, G, N, D, 1, 4, 1, 1, W, ws,
+                                        S) == 7
+    assert L.mn_add_rmsnorm_backward_rows_ex(A, B, C, Dp, E, NULL, F, N, D, 2, 2, 2, 2, W, 0,
+                                             S) == 5
+    assert L.mn_rmsnorm_backward_rows_ex(A, B, C, Dp, E, N, D, F16, F16, BF16, F16, W, 0, S) == 7
     assert L.mn_layernorm_forward_ex(A, B, NULL, C, Dp, E, N, D, f, 1, 1, S) == 1
+    # dX spans scale with its own storage type: a float32 dX of 16 x 64 covers
+    # 4096 bytes, so one starting 2 KiB before dY overlaps it
+    assert L.mn_rmsnorm_backward_rows_ex(A, B, C, P(0x60000000), P(0x60000000 - 2048), N, D,
+                                         F16, F16, F16, F32, W,
+                                         mn.workspace_bytes(mn.MN_RMSNORM, N, D), S) == 4
 
 
 def test_workspace_bytes():

@@ -1,17 +1,19 @@
 """bfloat16 and float32 storage through the typed (``_ex``) entry points,
 versus the fp64 oracle fed the same stored values.
 
-Activations/cotangents (X, R, dY, dH and the outputs Y, H, dX) share one
-storage type, gamma/beta another; every pairing of fp16, bf16 and float32 is
-run. The arithmetic is fp32 in every case, so only the rounding of the
-stored outputs differs: bf16 outputs are held to 2 bf16 ulp, float32 outputs
-to the fp32 evaluation bound (parity.check_out), and a stored H must equal
-round(x + r) in its own type.
+The activations X, R and forward outputs Y, H take one storage type, gamma
+and beta another (every pairing of fp16, bf16 and float32 is run), the
+cotangents dY, dH a third and dX a fourth (every backward combination the
+library provides is run). The arithmetic is fp32 in every case, so only the
+rounding of the stored outputs differs: bf16 outputs are held to 2 bf16 ulp,
+float32 outputs to the fp32 evaluation bound (parity.check_out), and a
+stored H must equal round(x + r) in its own type.
 """
 import itertools
 
 import numpy as np
 import pytest
+import torch
 
 import workloads
 from gpu_cases import compare, reference, run_gpu, say
@@ -23,9 +25,16 @@ STORAGE = ["f16", "bf16", "f32"]
 PAIRS = list(itertools.product(STORAGE, STORAGE))
 
 
-def _case(kind, N, D, seed, act, param):
+def _case(kind, N, D, seed, act, param, cot=None):
     return workloads.random_case(kind, N, D, seed, x_loc=0.5 if kind == "ln" else 0.0,
-                                 act=act, param=param)
+                                 act=act, param=param, cot=cot)
+
+
+TORCH = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+# backward storage combinations (act, cot, dX) the library provides
+BWD_TYPES = ([(a, c, o) for a in ("f16", "bf16") for c in (a, "f32") for o in (a, "f32")] +
+             [("f32", c, "f32") for c in ("f16", "bf16", "f32")])
 
 
 @pytest.mark.parametrize("D", [257, 1024, 4096, 8192])
@@ -68,6 +77,33 @@ def test_storage_unaligned(kind, act, D):
             f"{kind} {act} {N}x{D} unaligned", inputs=d)
 
 
+@pytest.mark.parametrize("D", [1024, 257])
+@pytest.mark.parametrize("act,cot,dxt", BWD_TYPES)
+@pytest.mark.parametrize("kind", KINDS)
+def test_cotangent_and_dx_types(kind, act, cot, dxt, D):
+    N = 300
+    say(f"[storage] {kind} act={act} cot={cot} dX={dxt} N={N} D={D}")
+    d = _case(kind, N, D, 10000 + D, act, "f32", cot)
+    gpu = run_gpu(kind, d, 1e-5, dx_dtype=TORCH[dxt])
+    assert gpu["dX"].dtype == workloads.STORAGE[dxt]
+    w = compare(kind, gpu, reference(kind, d, 1e-5), f"{kind} {act}/{cot}/{dxt} {N}x{D}",
+                inputs=d)
+    say(f"[storage] {kind} act={act} cot={cot} dX={dxt} D={D}: {w}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_float32_dx_is_the_unrounded_16bit_dx(kind):
+    """A float32 dX rounded to fp16 (nearest, ties to even) equals the fp16
+    dX of the same call: both are the same fp32 value, stored once as is and
+    once rounded."""
+    d = _case(kind, 200, 4096, 13, "f16", "f16")
+    a = run_gpu(kind, d, 1e-5)
+    b = run_gpu(kind, d, 1e-5, dx_dtype=torch.float32)
+    assert np.array_equal(b["dX"].astype(np.float16), a["dX"])
+    for k in ("Y", "rstd", "dgamma"):
+        assert np.array_equal(a[k], b[k]), k
+
+
 @pytest.mark.parametrize("kind", KINDS)
 def test_typed_entry_points_match_fp16_ones(kind):
     """With fp16 for both types the ``_ex`` entry points run the fp16 path."""
@@ -87,27 +123,34 @@ def test_add_without_residual_cotangent_storage(act):
 
 
 # Full-size shapes: bf16 activations with float32 parameters (the usual
-# mixed-precision training layout), and float32 throughout.
-FULL = [("rms_16384x4096", "bf16", "f32"), ("add_rms_32768x8192", "bf16", "f32"),
-        ("rms_1048576x128", "bf16", "bf16"), ("ln_16384x4096", "bf16", "f32"),
-        ("rms_16384x4096", "f32", "f32"), ("ln_16384x4096", "f32", "f32")]
+# mixed-precision training layout), float32 throughout, and fp16 storage
+# with float32 gradients (dX and the cotangents in float32 as well).
+FULL = [("rms_16384x4096", "bf16", "f32", "bf16", "bf16"),
+        ("add_rms_32768x8192", "bf16", "f32", "bf16", "bf16"),
+        ("rms_1048576x128", "bf16", "bf16", "bf16", "bf16"),
+        ("ln_16384x4096", "bf16", "f32", "bf16", "bf16"),
+        ("rms_16384x4096", "f32", "f32", "f32", "f32"),
+        ("ln_16384x4096", "f32", "f32", "f32", "f32"),
+        ("rms_16384x4096", "f16", "f16", "f16", "f32"),
+        ("ln_16384x4096", "f16", "f16", "f32", "f32")]
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name,act,param", FULL)
-def test_full_size_storage(name, act, param):
+@pytest.mark.parametrize("name,act,param,cot,dxt", FULL)
+def test_full_size_storage(name, act, param, cot, dxt):
     w = workloads.WORKLOADS[name]
-    say(f"[storage] full {name} {act}/{param}: generating")
-    d = workloads.generate(w, act=act, param=param)
-    say(f"[storage] full {name} {act}/{param}: gpu")
-    gpu = run_gpu(w.kind, d, w.eps)
+    say(f"[storage] full {name} {act}/{param}/{cot}/{dxt}: generating")
+    d = workloads.generate(w, act=act, param=param, cot=cot)
+    say(f"[storage] full {name} {act}/{param}/{cot}/{dxt}: gpu")
+    gpu = run_gpu(w.kind, d, w.eps, dx_dtype=TORCH[dxt])
     rows = workloads.sample_rows(w.N, 2048)
-    say(f"[storage] full {name} {act}/{param}: oracle on {len(rows)} rows")
+    say(f"[storage] full {name}: oracle on {len(rows)} rows")
     ref = reference(w.kind, d, w.eps, rows=rows)
     # bfloat16 keeps full relative precision down to 2^-126, so an output that
     # is a deep cancellation of fp32 terms (dX near zero, LayerNorm y where
     # gamma*xhat ~ -beta) can sit a few bf16 ulp off; those elements take the
     # fp32 allowance, every other one the 2 ulp bound
     inputs = d
-    worst = compare(w.kind, gpu, ref, f"{name} {act}/{param}", rows=rows, inputs=inputs)
-    say(f"[storage] full {name} {act}/{param}: worst {worst}")
+    worst = compare(w.kind, gpu, ref, f"{name} {act}/{param}/{cot}/{dxt}", rows=rows,
+                    inputs=inputs)
+    say(f"[storage] full {name}: worst {worst}")

@@ -20,7 +20,8 @@ Recipe (fixed, so that every run sees the same bits):
   float32 directly; bfloat16 from the float32 value, by rounding its bit
   pattern to the upper 16 bits (returned as uint16 bit patterns). The named
   workloads are fp16 throughout; tests of the other storage types pass
-  ``act`` (X, R, dY, dH) and ``param`` (gamma, beta) to the generators.
+  ``act`` (X, R), ``cot`` (dY, dH) and ``param`` (gamma, beta) to the
+  generators.
 * The Llama-shape RMSNorm workload marks 1 % of its 4096 channels as outliers:
   41 channels drawn without replacement from ``default_rng(1)`` and sorted;
   those X columns are multiplied by 20 before rounding.
@@ -162,22 +163,24 @@ def _fill_rows(seed: int, t: int, out: np.ndarray, spec: TensorSpec, outliers: n
 
 
 def generate(w: Workload, seed: int = 0, N: Optional[int] = None, act: str = "f16",
-             param: Optional[str] = None) -> Dict[str, np.ndarray]:
+             param: Optional[str] = None, cot: Optional[str] = None) -> Dict[str, np.ndarray]:
     """Materialise every input tensor of ``w`` as contiguous numpy arrays:
-    per-row tensors in storage ``act``, gamma/beta in ``param`` (default:
-    ``act``); fp16 and float32 as such, bfloat16 as uint16 bit patterns.
+    X and R in storage ``act``, the cotangents dY and dH in ``cot``, gamma
+    and beta in ``param`` (both default to ``act``); fp16 and float32 as
+    such, bfloat16 as uint16 bit patterns.
 
     ``N`` overrides the row count (same distributions; the rows are a prefix
     of the full workload's rows). The float64 draws do not depend on the
     storage types, so the same seed gives the same values rounded differently.
     """
     param = act if param is None else param
+    cot = act if cot is None else cot
     n = w.N if N is None else int(N)
     outliers = w.outlier_channels()
     out: Dict[str, np.ndarray] = {}
     for t, spec in enumerate(w.tensors):
         if spec.per_row:
-            a = np.empty((n, w.D), dtype=STORAGE[act])
+            a = np.empty((n, w.D), dtype=STORAGE[cot if spec.name in ("dY", "dH") else act])
             _fill_rows(seed, t, a, spec, outliers if spec.name == "X" else np.zeros(0, np.int64),
                        w.outlier_gain)
         else:
@@ -189,12 +192,13 @@ def generate(w: Workload, seed: int = 0, N: Optional[int] = None, act: str = "f1
 
 def random_case(kind: str, N: int, D: int, seed: int, x_loc: float = 0.0, x_scale: float = 1.0,
                 dy_scale: float = 1.0, r_scale: float = 2.0, dh_scale: float = 0.5,
-                act: str = "f16", param: Optional[str] = None) -> Dict[str, np.ndarray]:
+                act: str = "f16", param: Optional[str] = None, cot: Optional[str] = None
+                ) -> Dict[str, np.ndarray]:
     """Inputs for an arbitrary (kind, N, D) test case with the default recipe."""
     w = Workload(f"case_{kind}_{N}x{D}", kind, N, D, 1e-5,
                  _spec(kind, x=(x_loc, x_scale), dy=(0.0, dy_scale), r=(0.0, r_scale),
                        dh=(0.0, dh_scale)))
-    return generate(w, seed, act=act, param=param)
+    return generate(w, seed, act=act, param=param, cot=cot)
 
 
 def sample_rows(N: int, k: int, seed: int = 7) -> np.ndarray:
