@@ -34,21 +34,28 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
 KERNEL_SRCS = [os.path.join(ROOT, "row_wise_normalization_amd", "csrc", f)
-               for f in ("mn_kernels.hpp", "mn_kernels.hip")]
+               for f in ("mn_kernels.hpp", "mn_kernels.hip", "mn_tables.hpp", "mn_instances.hpp",
+                         "mn_inst_f16.hip", "mn_inst_bf16.hip", "mn_inst_f32.hip")]
+SIZE = {"f16": 2, "bf16": 2, "f32": 4}
 
 
-def alg_bytes(kind: str, N: int, D: int):
-    """Algorithmic bytes (each tensor read or written once) of the forward,
-    the backward row kernel and the column reduce."""
+def alg_bytes(kind: str, N: int, D: int, act: str = "f16", param: str = "f16",
+              cot: str = "f16", dxt: str = "f16"):
+    """Algorithmic bytes (each tensor read or written once) of the forward and
+    the backward (row kernel and column reduce together): activations X, R,
+    Y, H of `act`, gamma/beta of `param`, cotangents dY, dH of `cot`, dX of
+    `dxt`, fp32 statistics and parameter gradients."""
+    a, p, c, o = SIZE[act], SIZE[param], SIZE[cot], SIZE[dxt]
+    nd = N * D
     if kind == "rms":
-        fwd = 4 * N * D + 2 * D + 4 * N
-        bwd = 6 * N * D + 6 * D + 4 * N
+        fwd = 2 * a * nd + p * D + 4 * N                      # X, gamma -> Y, rstd
+        bwd = (a + c + o) * nd + (p + 4) * D + 4 * N          # X, dY, gamma, rstd -> dX, dgamma
     elif kind == "ln":
-        fwd = 4 * N * D + 4 * D + 8 * N
-        bwd = 6 * N * D + 10 * D + 8 * N
+        fwd = 2 * a * nd + 2 * p * D + 8 * N                  # + beta, mean
+        bwd = (a + c + o) * nd + (p + 8) * D + 8 * N          # + mean, dbeta
     else:
-        fwd = 8 * N * D + 2 * D + 4 * N
-        bwd = 10 * N * D + 6 * D + 4 * N
+        fwd = 4 * a * nd + p * D + 4 * N                      # X, R -> H, Y
+        bwd = (2 * a + 2 * c + o) * nd + (p + 4) * D + 4 * N  # X, R, dY, dH -> dX
     return fwd, bwd
 
 
@@ -127,12 +134,13 @@ class HipEvent:
             self._lib.hipEventDestroy(self.h)
 
 
-def cpu_baseline(w, d, budget_s: float):
+def cpu_baseline(w, d, budget_s: float, types=("f16",) * 4):
     """The oracle (single-threaded C, fp64) on this host: full forward and
-    backward passes over a bounded number of rows of the same workload."""
+    backward passes over all rows of the same workload, repeated until the
+    time budget is spent (at least once)."""
     import oracle
 
-    fwd_b, bwd_b = alg_bytes(w.kind, w.N, w.D)
+    fwd_b, bwd_b = alg_bytes(w.kind, w.N, w.D, *types)
     rows = w.N
     X, g, dY = d["X"], d["gamma"], d["dY"]
     t0 = time.perf_counter()
@@ -163,6 +171,76 @@ def cpu_baseline(w, d, budget_s: float):
     }
 
 
+# The shapes of the pages' binary32 LayerNorm forward timings (rows x width).
+PAGES_SHAPES = [(1, 127), (17, 257), (128, 1024), (64, 4096)]
+
+
+def pages_context(torch, mn):
+    """Binary32 LayerNorm forward at the shapes the pages time, measured the
+    way they describe their table: inputs resident on the device, output
+    preallocated, 100 ms of warmup, then the median over 11 windows of
+    100 ms of the host-wall time per synchronized call. Reported both
+    through the Python binding (tensor checks included) and as a direct
+    C-ABI call with prepared arguments, next to the device time per call
+    from events. Context only: the pages measure another GPU and API."""
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    L = mn.lib()
+    out = []
+    for N, D in PAGES_SHAPES:
+        d = workloads.random_case("ln", N, D, seed=0, x_loc=0.5, act="f32", param="f32")
+        X = torch.from_numpy(d["X"]).to(dev)
+        g = torch.from_numpy(d["gamma"]).to(dev)
+        b = torch.from_numpy(d["beta"]).to(dev)
+        Y = torch.empty_like(X)
+        mean = torch.empty(N, dtype=torch.float32, device=dev)
+        rstd = torch.empty(N, dtype=torch.float32, device=dev)
+        eps = 1e-5
+
+        def via_binding():
+            mn.mn_layernorm_forward_ex(X, g, b, Y, mean, rstd, eps, stream)
+
+        cargs = [ctypes.c_void_p(t.data_ptr()) for t in (X, g, b, Y, mean, rstd)]
+        craw = (N, D, ctypes.c_float(eps), mn.MN_F32, mn.MN_F32, ctypes.c_void_p(stream.cuda_stream))
+        fn = L.mn_layernorm_forward_ex
+
+        def direct():
+            if fn(*cargs, *craw) != 0:
+                raise RuntimeError("mn_layernorm_forward_ex failed")
+
+        def window(call, seconds=0.1):
+            n = 0
+            t0 = time.perf_counter()
+            while True:
+                call()
+                stream.synchronize()
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    return el / n
+
+        res = {"rows": N, "width": D}
+        for name, call in (("binding", via_binding), ("direct", direct)):
+            window(call)
+            res[f"host_wall_p50_us_{name}"] = round(
+                float(np.median([window(call) for _ in range(11)])) * 1e6, 3)
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(stream)
+        for _ in range(1000):
+            direct()
+        e1.record(stream)
+        stream.synchronize()
+        res["device_us_per_call_back_to_back"] = round(e0.elapsed_ms(e1), 3)
+        out.append(res)
+    print(json.dumps({
+        "metric": "host-wall us per binary32 LayerNorm forward call (p50 of 11 x 100 ms windows, "
+                  "synchronized calls)",
+        "unit": "us", "higher_is_better": False, "data": "synthetic", "dtype": "f32",
+        "shapes": out, "device": torch.cuda.get_device_name(dev),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +250,17 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
+    ap.add_argument("--act", default="f16", choices=sorted(SIZE),
+                    help="storage of X, R, Y, H (default fp16, the workloads' own)")
+    ap.add_argument("--param", default=None, choices=sorted(SIZE),
+                    help="storage of gamma, beta (default: --act)")
+    ap.add_argument("--cot", default=None, choices=sorted(SIZE),
+                    help="storage of dY, dH (default: --act)")
+    ap.add_argument("--dx", default=None, choices=sorted(SIZE),
+                    help="storage of dX (default: --act)")
+    ap.add_argument("--pages-context", action="store_true",
+                    help="instead of the training step: host-wall time of the binary32 "
+                         "LayerNorm forward at the shapes the pages time")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -183,22 +272,38 @@ def main():
     import torch
     import row_wise_normalization_amd as mn
 
+    if args.pages_context:
+        pages_context(torch, mn)
+        return
+
+    act = args.act
+    param = args.param or act
+    cot = args.cot or act
+    dxt = args.dx or act
+    typed = (act, param, cot, dxt) != ("f16",) * 4
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
     w = workloads.WORKLOADS[args.workload]
     N, D, kind = w.N, w.D, w.kind
     print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
-    d = workloads.generate(w)
+    d = workloads.generate(w, act=act, param=param, cot=cot)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
+    def upload(a):
+        if a.dtype == np.uint16:  # bfloat16 bit patterns
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
     S = max(2, args.sets)
-    up = {k: torch.from_numpy(v).to(dev) for k, v in d.items()}
+    up = {k: upload(v) for k, v in d.items()}
     sets = []
     for s in range(S):
         b = {"X": up["X"] if s == 0 else up["X"].clone(),
              "dY": up["dY"] if s == 0 else up["dY"].clone(),
-             "Y": torch.empty(N, D, dtype=torch.float16, device=dev),
-             "dX": torch.empty(N, D, dtype=torch.float16, device=dev),
+             "Y": torch.empty(N, D, dtype=tdt[act], device=dev),
+             "dX": torch.empty(N, D, dtype=tdt[dxt], device=dev),
              "rstd": torch.empty(N, dtype=torch.float32, device=dev),
              "dgamma": torch.empty(D, dtype=torch.float32, device=dev)}
         if kind == "ln":
@@ -207,36 +312,39 @@ def main():
         if kind == "add":
             b["R"] = up["R"] if s == 0 else up["R"].clone()
             b["dH"] = up["dH"] if s == 0 else up["dH"].clone()
-            b["H"] = torch.empty(N, D, dtype=torch.float16, device=dev)
+            b["H"] = torch.empty(N, D, dtype=tdt[act], device=dev)
         b["ws"] = mn.new_workspace({"rms": 0, "ln": 1, "add": 2}[kind], N, D, dev)
         sets.append(b)
     gamma = up["gamma"]
     beta = up.get("beta")
     kcode = {"rms": mn.MN_RMSNORM, "ln": mn.MN_LAYERNORM, "add": mn.MN_ADD_RMSNORM}[kind]
+    x = "_ex" if typed else ""
+    f_rms, f_ln, f_add = (getattr(mn, f"mn_{n}_forward{x}")
+                          for n in ("rmsnorm", "layernorm", "add_rmsnorm"))
+    b_rms, b_ln, b_add = (getattr(mn, f"mn_{n}_backward_rows{x}")
+                          for n in ("rmsnorm", "layernorm", "add_rmsnorm"))
 
     def fwd(b):
         if kind == "rms":
-            mn.mn_rmsnorm_forward(b["X"], gamma, b["Y"], b["rstd"], w.eps, stream)
+            f_rms(b["X"], gamma, b["Y"], b["rstd"], w.eps, stream)
         elif kind == "ln":
-            mn.mn_layernorm_forward(b["X"], gamma, beta, b["Y"], b["mean"], b["rstd"], w.eps, stream)
+            f_ln(b["X"], gamma, beta, b["Y"], b["mean"], b["rstd"], w.eps, stream)
         else:
-            mn.mn_add_rmsnorm_forward(b["X"], b["R"], gamma, b["H"], b["Y"], b["rstd"], w.eps, stream)
+            f_add(b["X"], b["R"], gamma, b["H"], b["Y"], b["rstd"], w.eps, stream)
 
     def bwd_rows(b):
         if kind == "rms":
-            mn.mn_rmsnorm_backward_rows(b["X"], gamma, b["rstd"], b["dY"], b["dX"], b["ws"], stream)
+            b_rms(b["X"], gamma, b["rstd"], b["dY"], b["dX"], b["ws"], stream)
         elif kind == "ln":
-            mn.mn_layernorm_backward_rows(b["X"], gamma, b["mean"], b["rstd"], b["dY"], b["dX"],
-                                          b["ws"], stream)
+            b_ln(b["X"], gamma, b["mean"], b["rstd"], b["dY"], b["dX"], b["ws"], stream)
         else:
-            mn.mn_add_rmsnorm_backward_rows(b["X"], b["R"], gamma, b["rstd"], b["dY"], b["dH"],
-                                            b["dX"], b["ws"], stream)
+            b_add(b["X"], b["R"], gamma, b["rstd"], b["dY"], b["dH"], b["dX"], b["ws"], stream)
 
     def reduce(b):
         mn.mn_norm_reduce_partials(kcode, N, D, b["ws"], b["dgamma"], b.get("dbeta"), stream)
 
     K, W = args.steps, args.warmup
-    fwd_b, bwd_b = alg_bytes(kind, N, D)
+    fwd_b, bwd_b = alg_bytes(kind, N, D, act, param, cot, dxt)
     # The dominant kernel (most algorithmic bytes per launch) is the backward
     # row kernel; the timed loop brackets only it with events, so that the
     # step wall time carries two event records per step.
@@ -293,14 +401,14 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(w.name, dom),
+        "traffic": measured_traffic(w.name, dom) if not typed else None,
     }
 
     cpu = None
     if args.cpu_budget > 0:
         print(f"[bench] cpu baseline (oracle, {args.cpu_budget:.0f} s budget)", file=sys.stderr,
               flush=True)
-        cpu = cpu_baseline(w, d, args.cpu_budget)
+        cpu = cpu_baseline(w, d, args.cpu_budget, (act, param, cot, dxt))
 
     line = {
         "metric": "achieved HBM GB/s (% of peak) + rows/s for norm fwd+bwd, RMSNorm 16384x4096",
@@ -316,7 +424,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": w.name, "N": N, "D": D, "eps": w.eps, "io_dtype": "f16",
+            "workload": w.name, "N": N, "D": D, "eps": w.eps, "io_dtype": act,
+            "param_dtype": param, "cotangent_dtype": cot, "dx_dtype": dxt,
             "norm": {"rms": "RMSNorm", "ln": "LayerNorm", "add": "fused add + RMSNorm"}[kind],
             "step": "forward + backward rows + column reduce", "buffer_sets": S,
         },
