@@ -93,6 +93,18 @@ class Oracle:
                                          _PD],
             "mno_add_rmsnorm_backward_t": [_VP, _VP, I, _VP, I, _VP, _VP, I, _I64, _I64, _DBL,
                                            _PD, _PD],
+            "mno_dyt_forward_t": [_VP, I, _DBL, _VP, _VP, I, _I64, _I64, _PD],
+            "mno_dyt_backward_t": [_VP, I, _DBL, _VP, I, _VP, I, _I64, _I64, _PD, _PD, _PD, _PD],
+            "mno_polynorm_forward_t": [_VP, I, _PD, _DBL, _I64, _I64, _DBL, _PD, _PD],
+            "mno_polynorm_backward_t": [_VP, I, _PD, _VP, I, _I64, _I64, _DBL, _PD, _PD, _PD],
+            "mno_modrms_forward_t": [_VP, I, _VP, I, _VP, _VP, I, _I64, _I64, _I64, _DBL, _PD,
+                                     _PD],
+            "mno_modrms_backward_t": [_VP, I, _VP, I, _VP, I, _VP, I, _I64, _I64, _I64, _DBL,
+                                      _PD, _PD, _PD, _PD],
+            "mno_groupnorm_forward_t": [_VP, I, _VP, _VP, I, _I64, _I64, _I64, _I64, _DBL, _PD,
+                                        _PD, _PD],
+            "mno_groupnorm_backward_t": [_VP, I, _VP, I, _VP, I, _I64, _I64, _I64, _I64, _DBL,
+                                         _PD, _PD, _PD],
         }
         for name, argtypes in sig.items():
             fn = getattr(lib, name)
@@ -243,6 +255,107 @@ class Oracle:
         self._check("add_rmsnorm_backward", self.lib.mno_add_rmsnorm_backward_t(
             x, r, tx, g, tg, dy, dh, ty, N, D, float(eps), self._out(dX), self._out(dg)))
         return dX, dg
+
+    # -- the other row-wise norms -------------------------------------------
+
+    def dyt_forward(self, X, alpha, gamma, beta, f64: bool = False):
+        """Dynamic Tanh: Y [N, D] = gamma * tanh(alpha * X) + beta, float64."""
+        N, D = _nd(X)
+        (x,), tx, k1 = self._group([X], f64)
+        (g, b), tg, k2 = self._group([gamma, beta], f64)
+        Y = np.empty((N, D))
+        self._check("dyt_forward", self.lib.mno_dyt_forward_t(
+            x, tx, float(alpha), g, b, tg, N, D, self._out(Y)))
+        return Y
+
+    def dyt_backward(self, X, alpha, gamma, dY, want_dx: bool = True, f64: bool = False):
+        """(dX or None, dalpha (float), dgamma [D], dbeta [D])."""
+        N, D = _nd(X)
+        (x,), tx, k1 = self._group([X], f64)
+        (g,), tg, k2 = self._group([gamma], f64)
+        (dy,), ty, k3 = self._group([dY], f64)
+        dX = np.empty((N, D)) if want_dx else None
+        da = np.empty(1); dg = np.empty(D); db = np.empty(D)
+        self._check("dyt_backward", self.lib.mno_dyt_backward_t(
+            x, tx, float(alpha), g, tg, dy, ty, N, D, self._out(dX), self._out(da),
+            self._out(dg), self._out(db)))
+        return dX, float(da[0]), dg, db
+
+    def polynorm_forward(self, X, w, b, eps, f64: bool = False):
+        """PolyNorm: (Y [N, D], rstd [N, 3]) with rstd[:, p-1] the p-th power's."""
+        N, D = _nd(X)
+        (x,), tx, k1 = self._group([X], f64)
+        wv = np.ascontiguousarray(w, dtype=np.float64).reshape(3)
+        Y = np.empty((N, D)); rstd = np.empty((N, 3))
+        self._check("polynorm_forward", self.lib.mno_polynorm_forward_t(
+            x, tx, self._out(wv), float(b), N, D, float(eps), self._out(Y), self._out(rstd)))
+        return Y, rstd
+
+    def polynorm_backward(self, X, w, dY, eps, want_dx: bool = True, f64: bool = False):
+        """(dX or None, dw [3], db (float))."""
+        N, D = _nd(X)
+        (x,), tx, k1 = self._group([X], f64)
+        (dy,), ty, k3 = self._group([dY], f64)
+        wv = np.ascontiguousarray(w, dtype=np.float64).reshape(3)
+        dX = np.empty((N, D)) if want_dx else None
+        dw = np.empty(3); db = np.empty(1)
+        self._check("polynorm_backward", self.lib.mno_polynorm_backward_t(
+            x, tx, self._out(wv), dy, ty, N, D, float(eps), self._out(dX), self._out(dw),
+            self._out(db)))
+        return dX, dw, float(db[0])
+
+    def modrms_forward(self, X, gamma, scale, shift, eps, f64: bool = False):
+        """Modulated RMSNorm with B = scale.shape[0] samples of N / B rows:
+        (Y [N, D], rstd [N])."""
+        N, D = _nd(X)
+        B = int(scale.shape[0])
+        (x,), tx, k1 = self._group([X], f64)
+        (g,), tg, k2 = self._group([gamma], f64)
+        (sc, sh), ts, k3 = self._group([scale, shift], f64)
+        Y = np.empty((N, D)); rstd = np.empty(N)
+        self._check("modrms_forward", self.lib.mno_modrms_forward_t(
+            x, tx, g, tg, sc, sh, ts, B, N, D, float(eps), self._out(Y), self._out(rstd)))
+        return Y, rstd
+
+    def modrms_backward(self, X, gamma, scale, dY, eps, want_dx: bool = True, f64: bool = False):
+        """(dX or None, dgamma [D], dscale [B, D], dshift [B, D])."""
+        N, D = _nd(X)
+        B = int(scale.shape[0])
+        (x,), tx, k1 = self._group([X], f64)
+        (g,), tg, k2 = self._group([gamma], f64)
+        (sc,), ts, k3 = self._group([scale], f64)
+        (dy,), ty, k4 = self._group([dY], f64)
+        dX = np.empty((N, D)) if want_dx else None
+        dg = np.empty(D); dsc = np.empty((B, D)); dsh = np.empty((B, D))
+        self._check("modrms_backward", self.lib.mno_modrms_backward_t(
+            x, tx, g, tg, sc, ts, dy, ty, B, N, D, float(eps), self._out(dX), self._out(dg),
+            self._out(dsc), self._out(dsh)))
+        return dX, dg, dsc, dsh
+
+    def groupnorm_forward(self, X, gamma, beta, groups, eps, f64: bool = False):
+        """GroupNorm on X [N, C, L]: (Y [N, C, L], mean [N, G], rstd [N, G])."""
+        N, C, L = (int(v) for v in X.shape)
+        (x,), tx, k1 = self._group([X], f64)
+        (g, b), tg, k2 = self._group([gamma, beta], f64)
+        Y = np.empty((N, C, L)); mean = np.empty((N, groups)); rstd = np.empty((N, groups))
+        self._check("groupnorm_forward", self.lib.mno_groupnorm_forward_t(
+            x, tx, g, b, tg, N, C, L, int(groups), float(eps), self._out(Y), self._out(mean),
+            self._out(rstd)))
+        return Y, mean, rstd
+
+    def groupnorm_backward(self, X, gamma, dY, groups, eps, want_dx: bool = True,
+                           f64: bool = False):
+        """(dX [N, C, L] or None, dgamma [C], dbeta [C])."""
+        N, C, L = (int(v) for v in X.shape)
+        (x,), tx, k1 = self._group([X], f64)
+        (g,), tg, k2 = self._group([gamma], f64)
+        (dy,), ty, k3 = self._group([dY], f64)
+        dX = np.empty((N, C, L)) if want_dx else None
+        dg = np.empty(C); db = np.empty(C)
+        self._check("groupnorm_backward", self.lib.mno_groupnorm_backward_t(
+            x, tx, g, tg, dy, ty, N, C, L, int(groups), float(eps), self._out(dX),
+            self._out(dg), self._out(db)))
+        return dX, dg, db
 
 
 _default: Optional[Oracle] = None

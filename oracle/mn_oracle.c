@@ -1,7 +1,8 @@
 /*
  * mn_oracle.c -- plain fp64 CPU oracle for the row-wise normalization
  * training pair (RMSNorm, LayerNorm, fused residual-add + RMSNorm; forward and
- * backward).
+ * backward), and for the other row-wise norms the [meTile] coverage
+ * inventory lists (Dynamic Tanh, PolyNorm, Modulated RMSNorm, GroupNorm).
  *
  * TEST INFRASTRUCTURE ONLY. Nothing in the product library links, includes or
  * calls this file; only the test suite, the smoke check and the benchmark's
@@ -26,13 +27,15 @@
  * formula with respect to its inputs and parameters (the [meTile] contract
  * ignores the rounding of casts and gives no epsilon gradient).
  *
- * Pins (tests/test_oracle_pins.py): torch fp64 layer_norm / rms_norm and
- * autograd on random inputs, central finite differences, closed forms for
- * constant and zero rows, the LayerNorm worked example of the [meTile]
- * contract, row invariants, the binary16 codec against numpy and the
- * bfloat16 codec against torch over every bit pattern, and agreement of the
- * typed entry points across storage types on values all types represent.
- * No function here is "parity unpinned".
+ * Pins (tests/test_oracle_pins.py): torch fp64 layer_norm / rms_norm /
+ * group_norm and autograd on random inputs, central finite differences,
+ * closed forms for constant and zero rows, the LayerNorm worked example of
+ * the [meTile] contract, row invariants, the binary16 codec against numpy
+ * and the bfloat16 codec against torch over every bit pattern, agreement of
+ * the typed entry points across storage types on values all types
+ * represent; for Dynamic Tanh its exponential form, odd symmetry, alpha = 0
+ * and saturation; for PolyNorm each power against torch rms_norm and
+ * linearity in its weights. No function here is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -567,4 +570,377 @@ int mno_add_rmsnorm_backward_t(const void* X, const void* R, int tx, const void*
     if (!type_ok(tx) || !type_ok(tg) || !type_ok(ty) || !R) return MNO_ERR_ARG;
     return rms_backward(opt(X, tx), opt(R, tx), opt(gamma, tg), opt(dY, ty), opt(dH, ty), N, D,
                         eps, dX, dgamma);
+}
+
+/* ===========================================================================
+ * The other row-wise normalizations the [meTile] coverage inventory lists as
+ * missing (section "Normalization", parity checklist): Dynamic Tanh,
+ * PolyNorm, Modulated RMSNorm and GroupNorm. The page names each with the
+ * gradients it must return but gives no formula; each function below states
+ * the published definition it writes out. Sums are in ascending order, row
+ * by row, as above; backward functions recompute their statistics in fp64.
+ * ======================================================================== */
+
+/* ---------------------------------------------------------------------------
+ * Dynamic Tanh (Zhu, Chen, He, LeCun and Liu, "Transformers without
+ * Normalization", 2025): an element-wise stand-in for a normalization layer,
+ *   y[i,j] = gamma[j] * tanh(alpha * x[i,j]) + beta[j]
+ * with a trainable scalar alpha. [meTile] lists its gradients as alpha,
+ * gamma and beta (and the input). With t = tanh(alpha x) and
+ * dt/dx = alpha (1 - t^2):
+ *   dX = dY * gamma * alpha * (1 - t^2)
+ *   dalpha = sum over all elements of dY * gamma * x * (1 - t^2)
+ *   dgamma[j] = sum_i dY * t,   dbeta[j] = sum_i dY.
+ * ------------------------------------------------------------------------- */
+
+static int dyt_forward(operand X, double alpha, operand G, operand B, int64_t N, int64_t D,
+                       double* Y)
+{
+    if (bad_shape(N, D)) return MNO_ERR_ARG;
+    fill_tables();
+    rows w;
+    if (!rows_alloc(&w, D)) { rows_free(&w); return MNO_ERR_MEM; }
+    get_row(G, 0, D, w.g);
+    get_row(B, 0, D, w.b);
+    for (int64_t i = 0; i < N; ++i) {
+        get_row(X, i, D, w.x);
+        for (int64_t j = 0; j < D; ++j) Y[i * D + j] = w.g[j] * tanh(alpha * w.x[j]) + w.b[j];
+    }
+    rows_free(&w);
+    return MNO_OK;
+}
+
+static int dyt_backward(operand X, double alpha, operand G, operand DY, int64_t N, int64_t D,
+                        double* dX, double* dalpha, double* dgamma, double* dbeta)
+{
+    if (bad_shape(N, D)) return MNO_ERR_ARG;
+    fill_tables();
+    rows w;
+    if (!rows_alloc(&w, D)) { rows_free(&w); return MNO_ERR_MEM; }
+    get_row(G, 0, D, w.g);
+    for (int64_t j = 0; j < D; ++j) { dgamma[j] = 0.0; dbeta[j] = 0.0; }
+    double da = 0.0;
+    for (int64_t i = 0; i < N; ++i) {
+        get_row(X, i, D, w.x);
+        get_row(DY, i, D, w.dy);
+        for (int64_t j = 0; j < D; ++j) {
+            double t = tanh(alpha * w.x[j]);
+            double s = 1.0 - t * t;
+            if (dX) dX[i * D + j] = w.dy[j] * w.g[j] * alpha * s;
+            da += w.dy[j] * w.g[j] * w.x[j] * s;
+            dgamma[j] += w.dy[j] * t;
+            dbeta[j] += w.dy[j];
+        }
+    }
+    *dalpha = da;
+    rows_free(&w);
+    return MNO_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * PolyNorm (Zhuo et al., "Polynomial Composition Activations", 2024): a sum
+ * of the RMS-normalised first three powers of the row,
+ *   y = w[0] * n1 + w[1] * n2 + w[2] * n3 + b,   n_p = x^p * r_p,
+ *   r_p = 1 / sqrt(mean_j((x_j^p)^2) + eps),
+ * with trainable scalars w[0..2] and b; w[p-1] weighs the p-th power, and
+ * eps enters as in RMSNorm (inside the square root). [meTile] asks for the
+ * input and parameter gradients. Each n_p is an RMSNorm of u = x^p with a
+ * scalar weight, so with g = dY:
+ *   dU_p = w[p-1] * r_p * (g - n_p * mean_j(g * n_p))
+ *   dX = sum_p p * x^(p-1) * dU_p
+ *   dw[p-1] = sum over all elements of g * n_p,   db = sum of g.
+ * The forward also returns the three r_p of each row (rstd[3 i + p - 1]).
+ * ------------------------------------------------------------------------- */
+
+static int poly_forward(operand X, const double* wp, double bias, int64_t N, int64_t D,
+                        double eps, double* Y, double* rstd)
+{
+    if (bad_shape(N, D)) return MNO_ERR_ARG;
+    fill_tables();
+    rows w;
+    if (!rows_alloc(&w, D)) { rows_free(&w); return MNO_ERR_MEM; }
+    for (int64_t i = 0; i < N; ++i) {
+        get_row(X, i, D, w.x);
+        double r[3];
+        for (int p = 1; p <= 3; ++p) {
+            for (int64_t j = 0; j < D; ++j) w.xh[j] = pow(w.x[j], (double)p);
+            r[p - 1] = rms_rstd(w.xh, D, eps);
+            if (rstd) rstd[3 * i + p - 1] = r[p - 1];
+        }
+        for (int64_t j = 0; j < D; ++j) {
+            double y = bias;
+            for (int p = 1; p <= 3; ++p) y += wp[p - 1] * (pow(w.x[j], (double)p) * r[p - 1]);
+            Y[i * D + j] = y;
+        }
+    }
+    rows_free(&w);
+    return MNO_OK;
+}
+
+static int poly_backward(operand X, const double* wp, operand DY, int64_t N, int64_t D,
+                         double eps, double* dX, double* dw, double* db)
+{
+    if (bad_shape(N, D)) return MNO_ERR_ARG;
+    fill_tables();
+    rows w;
+    if (!rows_alloc(&w, D)) { rows_free(&w); return MNO_ERR_MEM; }
+    double sw[3] = {0.0, 0.0, 0.0}, sb = 0.0;
+    for (int64_t i = 0; i < N; ++i) {
+        get_row(X, i, D, w.x);
+        get_row(DY, i, D, w.dy);
+        if (dX)
+            for (int64_t j = 0; j < D; ++j) dX[i * D + j] = 0.0;
+        for (int p = 1; p <= 3; ++p) {
+            for (int64_t j = 0; j < D; ++j) w.xh[j] = pow(w.x[j], (double)p);
+            double r = rms_rstd(w.xh, D, eps);
+            double c = 0.0;
+            for (int64_t j = 0; j < D; ++j) {
+                w.xh[j] *= r;                       /* n_p */
+                c += w.dy[j] * w.xh[j];
+                sw[p - 1] += w.dy[j] * w.xh[j];
+            }
+            c /= (double)D;
+            if (dX)
+                for (int64_t j = 0; j < D; ++j) {
+                    double du = wp[p - 1] * r * (w.dy[j] - w.xh[j] * c);
+                    dX[i * D + j] += (double)p * pow(w.x[j], (double)(p - 1)) * du;
+                }
+        }
+        for (int64_t j = 0; j < D; ++j) sb += w.dy[j];
+    }
+    for (int p = 0; p < 3; ++p) dw[p] = sw[p];
+    *db = sb;
+    rows_free(&w);
+    return MNO_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Modulated RMSNorm: RMSNorm whose output is modulated per sample by a
+ * broadcast scale and shift (the adaptive-norm modulation of conditioned
+ * transformers), rows grouped into B samples of S = N / B consecutive rows:
+ *   y[i,j] = gamma[j] * xhat[i,j] * (1 + scale[b,j]) + shift[b,j],
+ *   xhat = x * rstd (RMSNorm),  b = i / S.
+ * [meTile] asks for the input, weight and broadcast scale/shift gradients.
+ * With m[i,j] = gamma[j] (1 + scale[b,j]) the row is an RMSNorm with weight
+ * m, so with g = dY * m:
+ *   dX = rstd * (g - xhat * mean_j(g * xhat))
+ *   dgamma[j] = sum_i dY * xhat * (1 + scale[b,j])
+ *   dscale[b,j] = sum_{i in b} dY * xhat * gamma[j]
+ *   dshift[b,j] = sum_{i in b} dY.
+ * ------------------------------------------------------------------------- */
+
+static int modrms_forward(operand X, operand G, operand SC, operand SH, int64_t B, int64_t N,
+                          int64_t D, double eps, double* Y, double* rstd)
+{
+    if (bad_shape(N, D) || B < 1 || N % B != 0) return MNO_ERR_ARG;
+    fill_tables();
+    rows w;
+    if (!rows_alloc(&w, D)) { rows_free(&w); return MNO_ERR_MEM; }
+    const int64_t S = N / B;
+    get_row(G, 0, D, w.g);
+    for (int64_t i = 0; i < N; ++i) {
+        const int64_t b = i / S;
+        get_row(X, i, D, w.x);
+        get_row(SC, b, D, w.r);
+        get_row(SH, b, D, w.b);
+        double r = rms_rstd(w.x, D, eps);
+        rstd[i] = r;
+        for (int64_t j = 0; j < D; ++j)
+            Y[i * D + j] = w.g[j] * (w.x[j] * r) * (1.0 + w.r[j]) + w.b[j];
+    }
+    rows_free(&w);
+    return MNO_OK;
+}
+
+static int modrms_backward(operand X, operand G, operand SC, operand DY, int64_t B, int64_t N,
+                           int64_t D, double eps, double* dX, double* dgamma, double* dscale,
+                           double* dshift)
+{
+    if (bad_shape(N, D) || B < 1 || N % B != 0) return MNO_ERR_ARG;
+    fill_tables();
+    rows w;
+    if (!rows_alloc(&w, D)) { rows_free(&w); return MNO_ERR_MEM; }
+    const int64_t S = N / B;
+    get_row(G, 0, D, w.g);
+    for (int64_t j = 0; j < D; ++j) dgamma[j] = 0.0;
+    for (int64_t k = 0; k < B * D; ++k) { dscale[k] = 0.0; dshift[k] = 0.0; }
+    for (int64_t i = 0; i < N; ++i) {
+        const int64_t b = i / S;
+        get_row(X, i, D, w.x);
+        get_row(SC, b, D, w.r);
+        get_row(DY, i, D, w.dy);
+        double r = rms_rstd(w.x, D, eps);
+        double c1 = 0.0;
+        for (int64_t j = 0; j < D; ++j) {
+            w.xh[j] = w.x[j] * r;
+            c1 += w.dy[j] * w.g[j] * (1.0 + w.r[j]) * w.xh[j];
+        }
+        c1 /= (double)D;
+        if (dX)
+            for (int64_t j = 0; j < D; ++j)
+                dX[i * D + j] = r * (w.dy[j] * w.g[j] * (1.0 + w.r[j]) - w.xh[j] * c1);
+        for (int64_t j = 0; j < D; ++j) {
+            dgamma[j] += w.dy[j] * w.xh[j] * (1.0 + w.r[j]);
+            dscale[b * D + j] += w.dy[j] * w.xh[j] * w.g[j];
+            dshift[b * D + j] += w.dy[j];
+        }
+    }
+    rows_free(&w);
+    return MNO_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * GroupNorm (Wu and He, "Group Normalization", 2018) on X of shape
+ * [N, C, L] (L positions per channel, contiguous): the C channels form G
+ * groups of C / G consecutive channels; each (sample, group) slice of
+ * (C / G) * L contiguous values is centred by its mean and scaled by its
+ * rstd (population variance, eps inside the square root, as LayerNorm), and
+ * channel c then takes its own affine weight and bias:
+ *   y[n,c,l] = (x[n,c,l] - mean[n,g]) * rstd[n,g] * gamma[c] + beta[c].
+ * [meTile] asks for the group/channel layouts and the affine gradients. The
+ * backward is the LayerNorm backward over each slice with a per-channel
+ * weight (g = dY * gamma[c], M = (C / G) * L):
+ *   dX = rstd * (g - mean_M(g) - xhat * mean_M(g * xhat))
+ *   dgamma[c] = sum_{n,l} dY * xhat,   dbeta[c] = sum_{n,l} dY.
+ * mean and rstd are [N, G].
+ * ------------------------------------------------------------------------- */
+
+static int gn_forward(operand X, operand G, operand B, int64_t N, int64_t C, int64_t L,
+                      int64_t groups, double eps, double* Y, double* mean, double* rstd)
+{
+    if (N < 0 || C < 1 || L < 1 || groups < 1 || C % groups != 0) return MNO_ERR_ARG;
+    fill_tables();
+    const int64_t M = (C / groups) * L;
+    rows w;
+    if (!rows_alloc(&w, M > C ? M : C)) { rows_free(&w); return MNO_ERR_MEM; }
+    double* gam = malloc(sizeof(double) * (size_t)C);
+    double* bet = malloc(sizeof(double) * (size_t)C);
+    if (!gam || !bet) { free(gam); free(bet); rows_free(&w); return MNO_ERR_MEM; }
+    get_row(G, 0, C, gam);
+    get_row(B, 0, C, bet);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t g = 0; g < groups; ++g) {
+            const int64_t slice = n * groups + g;     /* row `slice` of [N*G, M] */
+            get_row(X, slice, M, w.x);
+            double mu, r;
+            ln_stats(w.x, M, eps, &mu, &r);
+            mean[slice] = mu;
+            rstd[slice] = r;
+            for (int64_t k = 0; k < M; ++k) {
+                const int64_t c = g * (C / groups) + k / L;
+                Y[slice * M + k] = (w.x[k] - mu) * r * gam[c] + bet[c];
+            }
+        }
+    free(gam); free(bet);
+    rows_free(&w);
+    return MNO_OK;
+}
+
+static int gn_backward(operand X, operand G, operand DY, int64_t N, int64_t C, int64_t L,
+                       int64_t groups, double eps, double* dX, double* dgamma, double* dbeta)
+{
+    if (N < 0 || C < 1 || L < 1 || groups < 1 || C % groups != 0) return MNO_ERR_ARG;
+    fill_tables();
+    const int64_t M = (C / groups) * L;
+    rows w;
+    if (!rows_alloc(&w, M > C ? M : C)) { rows_free(&w); return MNO_ERR_MEM; }
+    double* gam = malloc(sizeof(double) * (size_t)C);
+    if (!gam) { rows_free(&w); return MNO_ERR_MEM; }
+    get_row(G, 0, C, gam);
+    for (int64_t c = 0; c < C; ++c) { dgamma[c] = 0.0; dbeta[c] = 0.0; }
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t g = 0; g < groups; ++g) {
+            const int64_t slice = n * groups + g;
+            get_row(X, slice, M, w.x);
+            get_row(DY, slice, M, w.dy);
+            double mu, r;
+            ln_stats(w.x, M, eps, &mu, &r);
+            double c1 = 0.0, c2 = 0.0;
+            for (int64_t k = 0; k < M; ++k) {
+                const int64_t c = g * (C / groups) + k / L;
+                w.xh[k] = (w.x[k] - mu) * r;
+                c1 += w.dy[k] * gam[c] * w.xh[k];
+                c2 += w.dy[k] * gam[c];
+            }
+            c1 /= (double)M;
+            c2 /= (double)M;
+            for (int64_t k = 0; k < M; ++k) {
+                const int64_t c = g * (C / groups) + k / L;
+                if (dX) dX[slice * M + k] = r * (w.dy[k] * gam[c] - c2 - w.xh[k] * c1);
+                dgamma[c] += w.dy[k] * w.xh[k];
+                dbeta[c] += w.dy[k];
+            }
+        }
+    free(gam);
+    rows_free(&w);
+    return MNO_OK;
+}
+
+/* Typed entry points of the four (types as for the entry points above: tx
+ * for X, tg for gamma/beta, ts for scale/shift, ty for dY). */
+int mno_dyt_forward_t(const void* X, int tx, double alpha, const void* gamma, const void* beta,
+                      int tg, int64_t N, int64_t D, double* Y)
+{
+    if (!type_ok(tx) || !type_ok(tg)) return MNO_ERR_ARG;
+    return dyt_forward(opt(X, tx), alpha, opt(gamma, tg), opt(beta, tg), N, D, Y);
+}
+
+int mno_dyt_backward_t(const void* X, int tx, double alpha, const void* gamma, int tg,
+                       const void* dY, int ty, int64_t N, int64_t D, double* dX, double* dalpha,
+                       double* dgamma, double* dbeta)
+{
+    if (!type_ok(tx) || !type_ok(tg) || !type_ok(ty)) return MNO_ERR_ARG;
+    return dyt_backward(opt(X, tx), alpha, opt(gamma, tg), opt(dY, ty), N, D, dX, dalpha,
+                        dgamma, dbeta);
+}
+
+int mno_polynorm_forward_t(const void* X, int tx, const double* w, double b, int64_t N,
+                           int64_t D, double eps, double* Y, double* rstd)
+{
+    if (!type_ok(tx)) return MNO_ERR_ARG;
+    return poly_forward(opt(X, tx), w, b, N, D, eps, Y, rstd);
+}
+
+int mno_polynorm_backward_t(const void* X, int tx, const double* w, const void* dY, int ty,
+                            int64_t N, int64_t D, double eps, double* dX, double* dw, double* db)
+{
+    if (!type_ok(tx) || !type_ok(ty)) return MNO_ERR_ARG;
+    return poly_backward(opt(X, tx), w, opt(dY, ty), N, D, eps, dX, dw, db);
+}
+
+int mno_modrms_forward_t(const void* X, int tx, const void* gamma, int tg, const void* scale,
+                         const void* shift, int ts, int64_t B, int64_t N, int64_t D, double eps,
+                         double* Y, double* rstd)
+{
+    if (!type_ok(tx) || !type_ok(tg) || !type_ok(ts)) return MNO_ERR_ARG;
+    return modrms_forward(opt(X, tx), opt(gamma, tg), opt(scale, ts), opt(shift, ts), B, N, D,
+                          eps, Y, rstd);
+}
+
+int mno_modrms_backward_t(const void* X, int tx, const void* gamma, int tg, const void* scale,
+                          int ts, const void* dY, int ty, int64_t B, int64_t N, int64_t D,
+                          double eps, double* dX, double* dgamma, double* dscale,
+                          double* dshift)
+{
+    if (!type_ok(tx) || !type_ok(tg) || !type_ok(ts) || !type_ok(ty)) return MNO_ERR_ARG;
+    return modrms_backward(opt(X, tx), opt(gamma, tg), opt(scale, ts), opt(dY, ty), B, N, D,
+                           eps, dX, dgamma, dscale, dshift);
+}
+
+int mno_groupnorm_forward_t(const void* X, int tx, const void* gamma, const void* beta, int tg,
+                            int64_t N, int64_t C, int64_t L, int64_t G, double eps, double* Y,
+                            double* mean, double* rstd)
+{
+    if (!type_ok(tx) || !type_ok(tg)) return MNO_ERR_ARG;
+    return gn_forward(opt(X, tx), opt(gamma, tg), opt(beta, tg), N, C, L, G, eps, Y, mean,
+                      rstd);
+}
+
+int mno_groupnorm_backward_t(const void* X, int tx, const void* gamma, int tg, const void* dY,
+                             int ty, int64_t N, int64_t C, int64_t L, int64_t G, double eps,
+                             double* dX, double* dgamma, double* dbeta)
+{
+    if (!type_ok(tx) || !type_ok(tg) || !type_ok(ty)) return MNO_ERR_ARG;
+    return gn_backward(opt(X, tx), opt(gamma, tg), opt(dY, ty), N, C, L, G, eps, dX, dgamma,
+                       dbeta);
 }

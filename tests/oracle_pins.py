@@ -509,9 +509,179 @@ def pin_bf16_fused_sum(o):
     assert (S == o.bf16_to_f64(x) + o.bf16_to_f64(r)).all(), "S is not the exact sum"
 
 
+# ---------------------------------------------------------------------------
+# The other row-wise norms (Dynamic Tanh, PolyNorm, Modulated RMSNorm,
+# GroupNorm)
+# ---------------------------------------------------------------------------
+
+def pin_dyt(o):
+    rng = np.random.default_rng(31)
+    # closed forms: tanh through the exponential, odd symmetry, alpha = 0
+    N, D = 6, 77
+    x = rng.standard_normal((N, D)) * 1.5
+    g = 1 + 0.2 * rng.standard_normal(D)
+    b = 0.2 * rng.standard_normal(D)
+    for alpha in (0.5, 1.7):
+        Y = o.dyt_forward(x, alpha, g, b, f64=True)
+        e = np.exp(2 * alpha * x)
+        _close(Y, g[None, :] * (e - 1) / (e + 1) + b[None, :], 1e-13, 1e-15, "dyt via exp")
+        Ym = o.dyt_forward(-x, alpha, g, b, f64=True)
+        _close(Ym - b[None, :], -(Y - b[None, :]), 1e-14, 1e-16, "dyt odd symmetry")
+    Y0 = o.dyt_forward(x, 0.0, g, b, f64=True)
+    assert (Y0 == np.broadcast_to(b, (N, D))).all(), "dyt alpha = 0 must give beta"
+    dy = rng.standard_normal((N, D))
+    dX, da, dg, db = o.dyt_backward(x, 0.0, g, dy, f64=True)
+    assert (dX == 0).all() and (dg == 0).all(), "dyt alpha = 0: dX and dgamma vanish"
+    _close(da, (dy * g[None, :] * x).sum(), 1e-13, 1e-13, "dyt alpha = 0: dalpha")
+    _close(db, dy.sum(axis=0), 1e-14, 1e-14, "dyt dbeta = column sums")
+    # saturation: tanh(+-40) = +-1 in double, so y = beta +- gamma and dX = 0
+    xs = np.sign(rng.standard_normal((2, D))) * 40.0
+    Ys = o.dyt_forward(xs, 1.0, g, b, f64=True)
+    _close(Ys, np.sign(xs) * g[None, :] + b[None, :], 1e-15, 1e-15, "dyt saturation")
+    # central finite differences
+    for (n, d), alpha in (((2, 3), 0.8), ((3, 5), 1.3), ((1, 7), -0.6)):
+        x = rng.standard_normal((n, d))
+        g = 1 + 0.3 * rng.standard_normal(d)
+        b = 0.3 * rng.standard_normal(d)
+        dy = rng.standard_normal((n, d))
+        loss = lambda xx, aa, gg, bb: float((o.dyt_forward(xx, aa, gg, bb, f64=True) * dy).sum())
+        dX, da, dg, db = o.dyt_backward(x, alpha, g, dy, f64=True)
+        _fd_check(f"dyt dX {n}x{d}", lambda v: loss(v, alpha, g, b), x, dX)
+        _fd_check(f"dyt dgamma {n}x{d}", lambda v: loss(x, alpha, v, b), g, dg)
+        _fd_check(f"dyt dbeta {n}x{d}", lambda v: loss(x, alpha, g, v), b, db)
+        _fd_check(f"dyt dalpha {n}x{d}", lambda v: loss(x, float(v[0]), g, b),
+                  np.array([alpha]), np.array([da]))
+
+
+def pin_polynorm(o):
+    rng = np.random.default_rng(37)
+    eps = 1e-5
+    # each power on its own is torch's RMSNorm (no weight) of x^p
+    x = rng.standard_normal((5, 96)) + 0.1
+    for p in (1, 2, 3):
+        w = np.zeros(3); w[p - 1] = 1.0
+        Y, rstd = o.polynorm_forward(x, w, 0.0, eps, f64=True)
+        ref = F.rms_norm(torch.from_numpy(x ** p), (96,), eps=eps).numpy()
+        _close(Y, ref, 1e-12, 1e-14, f"polynorm power {p} vs torch rms_norm")
+        _close(rstd[:, p - 1], 1 / np.sqrt((x ** (2 * p)).mean(axis=1) + eps), 1e-13, 0,
+               f"polynorm rstd {p}")
+    # linear in (w, b)
+    w = np.array([0.3, -0.7, 1.1])
+    Y, _ = o.polynorm_forward(x, w, 0.25, eps, f64=True)
+    parts = [o.polynorm_forward(x, np.eye(3)[k], 0.0, eps, f64=True)[0] for k in range(3)]
+    _close(Y, sum(w[k] * parts[k] for k in range(3)) + 0.25, 1e-13, 1e-14, "polynorm linear")
+    dy = rng.standard_normal(x.shape)
+    dX, dw, db = o.polynorm_backward(x, w, dy, eps, f64=True)
+    _close(dw, [(dy * parts[k]).sum() for k in range(3)], 1e-12, 1e-12, "polynorm dw")
+    _close(db, dy.sum(), 1e-13, 1e-13, "polynorm db")
+    # central finite differences
+    for n, d in ((1, 1), (2, 3), (2, 6), (1, 9)):
+        x = rng.standard_normal((n, d)) + 0.2
+        w = rng.standard_normal(3)
+        dy = rng.standard_normal((n, d))
+        loss = lambda xx, ww, bb: float((o.polynorm_forward(xx, ww, bb, 1e-3, f64=True)[0]
+                                         * dy).sum())
+        dX, dw, db = o.polynorm_backward(x, w, dy, 1e-3, f64=True)
+        _fd_check(f"polynorm dX {n}x{d}", lambda v: loss(v, w, 0.1), x, dX)
+        _fd_check(f"polynorm dw {n}x{d}", lambda v: loss(x, v, 0.1), w, dw)
+        _fd_check(f"polynorm db {n}x{d}", lambda v: loss(x, w, float(v[0])), np.array([0.1]),
+                  np.array([db]))
+
+
+def pin_modrms(o):
+    rng = np.random.default_rng(41)
+    eps = 1e-5
+    B, S, D = 3, 4, 80
+    N = B * S
+    x = rng.standard_normal((N, D))
+    g = 1 + 0.1 * rng.standard_normal(D)
+    sc = 0.3 * rng.standard_normal((B, D))
+    sh = 0.3 * rng.standard_normal((B, D))
+    dy = rng.standard_normal((N, D))
+    zero = np.zeros((B, D))
+    # no modulation: torch's RMSNorm and its autograd
+    Y, rstd = o.modrms_forward(x, g, zero, zero, eps, f64=True)
+    tx = torch.from_numpy(x).requires_grad_(True)
+    tg = torch.from_numpy(g).requires_grad_(True)
+    ty = F.rms_norm(tx, (D,), tg, eps)
+    ty.backward(torch.from_numpy(dy))
+    _close(Y, ty.detach().numpy(), 1e-12, 1e-14, "modrms unmodulated Y")
+    dX, dg, dsc, dsh = o.modrms_backward(x, g, zero, dy, eps, f64=True)
+    _close(dX, tx.grad.numpy(), 1e-10, 1e-12, "modrms unmodulated dX")
+    _close(dg, tg.grad.numpy(), 1e-10, 1e-12, "modrms unmodulated dgamma")
+    # with modulation: torch RMSNorm times (1 + scale) plus shift, per sample
+    tx = torch.from_numpy(x).requires_grad_(True)
+    tg = torch.from_numpy(g).requires_grad_(True)
+    ts = torch.from_numpy(sc).requires_grad_(True)
+    th = torch.from_numpy(sh).requires_grad_(True)
+    rep = torch.arange(N) // S
+    ty = F.rms_norm(tx, (D,), tg, eps) * (1 + ts[rep]) + th[rep]
+    ty.backward(torch.from_numpy(dy))
+    Y, _ = o.modrms_forward(x, g, sc, sh, eps, f64=True)
+    dX, dg, dsc, dsh = o.modrms_backward(x, g, sc, dy, eps, f64=True)
+    _close(Y, ty.detach().numpy(), 1e-12, 1e-14, "modrms Y")
+    _close(dX, tx.grad.numpy(), 1e-10, 1e-12, "modrms dX")
+    _close(dg, tg.grad.numpy(), 1e-10, 1e-12, "modrms dgamma")
+    _close(dsc, ts.grad.numpy(), 1e-10, 1e-12, "modrms dscale")
+    _close(dsh, dy.reshape(B, S, D).sum(axis=1), 1e-13, 1e-13, "modrms dshift = sums per sample")
+    # central finite differences
+    for b_, s_, d in ((1, 1, 3), (2, 2, 3), (3, 1, 5)):
+        n = b_ * s_
+        x = rng.standard_normal((n, d))
+        g = 1 + 0.3 * rng.standard_normal(d)
+        sc = 0.4 * rng.standard_normal((b_, d))
+        sh = 0.4 * rng.standard_normal((b_, d))
+        dy = rng.standard_normal((n, d))
+        loss = lambda xx, gg, ss, hh: float((o.modrms_forward(xx, gg, ss, hh, 1e-3, f64=True)[0]
+                                             * dy).sum())
+        dX, dg, dsc, dsh = o.modrms_backward(x, g, sc, dy, 1e-3, f64=True)
+        _fd_check(f"modrms dX {n}x{d}", lambda v: loss(v, g, sc, sh), x, dX)
+        _fd_check(f"modrms dgamma {n}x{d}", lambda v: loss(x, v, sc, sh), g, dg)
+        _fd_check(f"modrms dscale {n}x{d}", lambda v: loss(x, g, v, sh), sc, dsc)
+        _fd_check(f"modrms dshift {n}x{d}", lambda v: loss(x, g, sc, v), sh, dsh)
+
+
+def pin_groupnorm(o):
+    rng = np.random.default_rng(43)
+    eps = 1e-5
+    for N, C, L, G in ((2, 8, 5, 4), (3, 6, 7, 1), (2, 6, 3, 6), (1, 12, 16, 3)):
+        x = rng.standard_normal((N, C, L)) + 0.3
+        g = 1 + 0.2 * rng.standard_normal(C)
+        b = 0.2 * rng.standard_normal(C)
+        dy = rng.standard_normal((N, C, L))
+        tx = torch.from_numpy(x).requires_grad_(True)
+        tg = torch.from_numpy(g).requires_grad_(True)
+        tb = torch.from_numpy(b).requires_grad_(True)
+        ty = F.group_norm(tx, G, tg, tb, eps)
+        ty.backward(torch.from_numpy(dy))
+        Y, mean, rstd = o.groupnorm_forward(x, g, b, G, eps, f64=True)
+        dX, dg, db = o.groupnorm_backward(x, g, dy, G, eps, f64=True)
+        what = f"groupnorm {N}x{C}x{L} G={G}"
+        _close(Y, ty.detach().numpy(), 1e-12, 1e-13, what + " Y")
+        sl = x.reshape(N, G, -1)
+        _close(mean, sl.mean(axis=2), 1e-13, 1e-15, what + " mean")
+        _close(rstd, 1 / np.sqrt(sl.var(axis=2) + eps), 1e-12, 0, what + " rstd")
+        _close(dX, tx.grad.numpy(), 1e-10, 1e-12, what + " dX")
+        _close(dg, tg.grad.numpy(), 1e-10, 1e-12, what + " dgamma")
+        _close(db, tb.grad.numpy(), 1e-12, 1e-12, what + " dbeta")
+    # central finite differences
+    for N, C, L, G in ((1, 2, 2, 1), (2, 4, 1, 2), (1, 3, 2, 3)):
+        x = rng.standard_normal((N, C, L))
+        g = 1 + 0.3 * rng.standard_normal(C)
+        b = 0.3 * rng.standard_normal(C)
+        dy = rng.standard_normal((N, C, L))
+        loss = lambda xx, gg, bb: float((o.groupnorm_forward(xx, gg, bb, G, 1e-3, f64=True)[0]
+                                         * dy).sum())
+        dX, dg, db = o.groupnorm_backward(x, g, dy, G, 1e-3, f64=True)
+        _fd_check(f"groupnorm dX {N}x{C}x{L}", lambda v: loss(v, g, b), x, dX)
+        _fd_check(f"groupnorm dgamma {N}x{C}x{L}", lambda v: loss(x, v, b), g, dg)
+        _fd_check(f"groupnorm dbeta {N}x{C}x{L}", lambda v: loss(x, g, v), b, db)
+
+
 ALL_PINS = [
     pin_codec_decode, pin_codec_encode, pin_torch_rmsnorm, pin_torch_layernorm,
     pin_torch_add_rmsnorm, pin_finite_differences, pin_constant_rows, pin_zero_rows,
     pin_worked_example, pin_invariants, pin_scaling, pin_fused_special_cases,
     pin_bf16_codec_decode, pin_bf16_codec_encode, pin_storage_types_agree, pin_bf16_fused_sum,
+    pin_dyt, pin_polynorm, pin_modrms, pin_groupnorm,
 ]

@@ -50,6 +50,28 @@ MUTANTS = {
                            "const float* f = (const float*)a.p + o / 2;"),
     "bf16_reads_f16_table": ("for (int64_t j = 0; j < D; ++j) dst[j] = bf16_table[b[j]];",
                              "for (int64_t j = 0; j < D; ++j) dst[j] = f16_table[b[j]];"),
+    "dyt_derivative_linear": ("double s = 1.0 - t * t;", "double s = 1.0 - t;"),
+    "dyt_dx_alpha_dropped": ("dX[i * D + j] = w.dy[j] * w.g[j] * alpha * s;",
+                             "dX[i * D + j] = w.dy[j] * w.g[j] * s;"),
+    "dyt_dalpha_gamma_dropped": ("da += w.dy[j] * w.g[j] * w.x[j] * s;",
+                                 "da += w.dy[j] * w.x[j] * s;"),
+    "poly_power_factor_dropped": ("dX[i * D + j] += (double)p * pow(w.x[j], (double)(p - 1)) * du;",
+                                  "dX[i * D + j] += pow(w.x[j], (double)(p - 1)) * du;"),
+    "poly_weights_reversed": ("y += wp[p - 1] * (pow(w.x[j], (double)p) * r[p - 1]);",
+                              "y += wp[3 - p] * (pow(w.x[j], (double)p) * r[p - 1]);"),
+    "modrms_scale_not_offset": ("Y[i * D + j] = w.g[j] * (w.x[j] * r) * (1.0 + w.r[j]) + w.b[j];",
+                                "Y[i * D + j] = w.g[j] * (w.x[j] * r) * w.r[j] + w.b[j];"),
+    "modrms_sample_interleaved": ("const int64_t b = i / S;\n        get_row(X, i, D, w.x);\n"
+                                  "        get_row(SC, b, D, w.r);\n        get_row(SH",
+                                  "const int64_t b = i % B;\n        get_row(X, i, D, w.x);\n"
+                                  "        get_row(SC, b, D, w.r);\n        get_row(SH"),
+    "modrms_dscale_unweighted": ("dscale[b * D + j] += w.dy[j] * w.xh[j] * w.g[j];",
+                                 "dscale[b * D + j] += w.dy[j] * w.xh[j];"),
+    "gn_gamma_by_group": ("Y[slice * M + k] = (w.x[k] - mu) * r * gam[c] + bet[c];",
+                          "Y[slice * M + k] = (w.x[k] - mu) * r * gam[g] + bet[c];"),
+    "gn_channel_stride": ("const int64_t c = g * (C / groups) + k / L;\n                if (dX)",
+                          "const int64_t c = g * (C / groups) + k % (C / groups);\n"
+                          "                if (dX)"),
 }
 
 
