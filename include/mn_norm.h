@@ -80,7 +80,10 @@ typedef enum {
 typedef enum {
     MN_RMSNORM = 0,
     MN_LAYERNORM = 1,
-    MN_ADD_RMSNORM = 2
+    MN_ADD_RMSNORM = 2,
+    MN_DYT = 3,          /* Dynamic Tanh */
+    MN_POLYNORM = 4,
+    MN_MOD_RMSNORM = 5   /* Modulated RMSNorm */
 } mn_norm_kind;
 
 /* [meTile] contract bound: 1..8192 columns. */
@@ -204,12 +207,83 @@ mn_status mn_add_rmsnorm_backward_ex(const void* X, const void* R, const void* g
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The other row-wise norms. The [meTile] coverage inventory (section
+ * "Normalization", parity checklist) lists Modulated RMSNorm, PolyNorm and
+ * Dynamic Tanh as missing there, naming the gradients each must return but
+ * not the formulas; these calls implement the published definitions below.
+ * Conventions are those of the *_ex calls above, except: the cotangent dY has
+ * the activation type `act`; dX has `dxt`, which is `act` or MN_F32; every
+ * parameter gradient is fp32 and is overwritten. Each backward runs its row
+ * kernel and its fixed-order parameter reduction on `stream`.
+ * ------------------------------------------------------------------------- */
+
+/* Dynamic Tanh (Zhu et al., "Transformers without Normalization", 2025):
+ *   Y[i,j] = gamma[j] * tanh(alpha * X[i,j]) + beta[j]
+ * alpha is one fp32 scalar in device memory; gamma, beta are [D] of `param`.
+ * No statistics are saved and there is no epsilon. Backward, with
+ * t = tanh(alpha x):
+ *   dX = dY * gamma * alpha * (1 - t^2)
+ *   dalpha[0] = sum_{i,j} dY * gamma * x * (1 - t^2)
+ *   dgamma[j] = sum_i dY * t,   dbeta[j] = sum_i dY
+ * Workspace: mn_norm_workspace_bytes(MN_DYT, N, D). */
+mn_status mn_dyt_forward_ex(const void* X, const float* alpha, const void* gamma,
+                            const void* beta, void* Y, int64_t N, int64_t D, mn_dtype act,
+                            mn_dtype param, void* stream);
+mn_status mn_dyt_backward_ex(const void* X, const float* alpha, const void* gamma, const void* dY,
+                             void* dX, float* dalpha, float* dgamma, float* dbeta, int64_t N,
+                             int64_t D, mn_dtype act, mn_dtype param, mn_dtype dxt,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* PolyNorm (Zhuo et al., "Polynomial Composition Activations", 2024): the
+ * RMS-normalised first three powers of each row, weighted, plus a bias,
+ *   Y = w1 * n1 + w2 * n2 + w3 * n3 + b,   n_p = X^p * rstd_p,
+ *   rstd_p = 1 / sqrt(mean_j(X^(2p)) + eps)   (per row).
+ * params = {w1, w2, w3, b}: four fp32 scalars in device memory. rstd is
+ * [N][3] fp32 (rstd_1, rstd_2, rstd_3 of each row), saved for the backward.
+ * Backward (g = dY):
+ *   dX = sum_p p * X^(p-1) * w_p * rstd_p * (g - n_p * mean_j(g * n_p))
+ *   dparams = {sum g*n1, sum g*n2, sum g*n3, sum g} over all elements.
+ * Workspace: mn_norm_workspace_bytes(MN_POLYNORM, N, D). */
+mn_status mn_polynorm_forward_ex(const void* X, const float* params, void* Y, float* rstd,
+                                 int64_t N, int64_t D, float eps, mn_dtype act, void* stream);
+mn_status mn_polynorm_backward_ex(const void* X, const float* params, const float* rstd,
+                                  const void* dY, void* dX, float* dparams, int64_t N, int64_t D,
+                                  mn_dtype act, mn_dtype dxt, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Modulated RMSNorm: RMSNorm modulated per sample by a broadcast scale and
+ * shift (the adaptive-norm modulation of conditioned transformers). The N
+ * rows form B samples of S = N / B consecutive rows (B must divide N,
+ * 1 <= B <= 4096); scale and shift are [B][D] of the activation type:
+ *   Y[i,j] = gamma[j] * xhat[i,j] * (1 + scale[b,j]) + shift[b,j],
+ *   xhat = X * rstd (RMSNorm, rstd [N] saved),  b = i / S.
+ * Backward, with m = gamma * (1 + scale) the weight the row sees:
+ *   dX = rstd * (dY*m - xhat * mean_j(dY*m*xhat))
+ *   dgamma[j] = sum_i dY * xhat * (1 + scale[b,j])
+ *   dscale[b,j] = sum_{i in b} dY * xhat * gamma[j]
+ *   dshift[b,j] = sum_{i in b} dY            (dscale, dshift [B][D] fp32)
+ * Workspace: mn_mod_rmsnorm_workspace_bytes(B, N, D). */
+mn_status mn_mod_rmsnorm_forward_ex(const void* X, const void* gamma, const void* scale,
+                                    const void* shift, void* Y, float* rstd, int64_t B,
+                                    int64_t N, int64_t D, float eps, mn_dtype act, mn_dtype param,
+                                    void* stream);
+mn_status mn_mod_rmsnorm_backward_ex(const void* X, const void* gamma, const void* scale,
+                                     const float* rstd, const void* dY, void* dX, float* dgamma,
+                                     float* dscale, float* dshift, int64_t B, int64_t N,
+                                     int64_t D, mn_dtype act, mn_dtype param, mn_dtype dxt,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+size_t mn_mod_rmsnorm_workspace_bytes(int64_t B, int64_t N, int64_t D);
+
+/* ---------------------------------------------------------------------------
  * Workspace and diagnostics.
  * ------------------------------------------------------------------------- */
 
 /* Bytes of device workspace the backward of `kind` needs at (N, D): the
- * per-block fp32 parameter-gradient partials (two arrays for LayerNorm).
- * Depends only on (kind, N, D). Returns 0 for invalid arguments. */
+ * per-block fp32 parameter-gradient partials (two arrays for LayerNorm and
+ * Dynamic Tanh, plus scalar partials for Dynamic Tanh and PolyNorm).
+ * Depends only on (kind, N, D). Returns 0 for invalid arguments and for
+ * MN_MOD_RMSNORM, whose size also depends on the sample count (see
+ * mn_mod_rmsnorm_workspace_bytes). */
 size_t mn_norm_workspace_bytes(mn_norm_kind kind, int64_t N, int64_t D);
 
 /* Static description of a status code. */
@@ -220,9 +294,9 @@ const char* mn_status_string(mn_status s);
 const char* mn_last_device_error(void);
 
 /* ---------------------------------------------------------------------------
- * The two stages of every backward, exported for callers that schedule them
- * separately (for instance to time the row kernel on its own, or to overlap
- * the parameter reduction with other work). Calling stage 1 then stage 2 on
+ * The two stages of the training-pair backward calls, exported for callers
+ * that schedule them separately (for instance to time the row kernel on its
+ * own, or to overlap the parameter reduction with other work). Calling stage 1 then stage 2 on
  * the same stream with the same workspace is exactly the corresponding
  * mn_*_backward call.
  *

@@ -24,6 +24,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmn_norm.so")
 
 MN_RMSNORM, MN_LAYERNORM, MN_ADD_RMSNORM = 0, 1, 2
+MN_DYT, MN_POLYNORM, MN_MOD_RMSNORM = 3, 4, 5
 MAX_COLS = 8192
 
 STATUS = {
@@ -74,6 +75,13 @@ _SIGNATURES = {
                                       _SZ, _P],
     "mn_add_rmsnorm_backward_rows_ex": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _C, _C,
                                         _P, _SZ, _P],
+    "mn_dyt_forward_ex": [_P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P],
+    "mn_dyt_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _C, _P, _SZ, _P],
+    "mn_polynorm_forward_ex": [_P, _P, _P, _P, _I64, _I64, _F, _C, _P],
+    "mn_polynorm_backward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _C, _C, _P, _SZ, _P],
+    "mn_mod_rmsnorm_forward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F, _C, _C, _P],
+    "mn_mod_rmsnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _C, _C,
+                                   _C, _P, _SZ, _P],
 }
 
 
@@ -93,6 +101,8 @@ def lib() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     L.mn_norm_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64]
     L.mn_norm_workspace_bytes.restype = _SZ
+    L.mn_mod_rmsnorm_workspace_bytes.argtypes = [_I64, _I64, _I64]
+    L.mn_mod_rmsnorm_workspace_bytes.restype = _SZ
     L.mn_status_string.argtypes = [ctypes.c_int]
     L.mn_status_string.restype = ctypes.c_char_p
     L.mn_last_device_error.argtypes = []
@@ -340,6 +350,79 @@ def mn_add_rmsnorm_backward_rows_ex(X, R, gamma, rstd, dY, dH, dX, workspace, st
           _stream(stream))
 
 
+# --- the other row-wise norms (activation-typed cotangents; dX in the
+# activation type or float32; fp32 parameter gradients) -----------------------
+
+def _scalar_t(name, t, n):
+    _check_t(name, t, F32, (n,))
+
+
+def mn_dyt_forward_ex(X, alpha, gamma, beta, Y, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, D)); _scalar_t("alpha", alpha, 1)
+    _check_t("gamma", gamma, gamma.dtype, (D,)); _check_t("beta", beta, gamma.dtype, (D,))
+    _check_t("Y", Y, X.dtype, (N, D))
+    _call("mn_dyt_forward_ex", _ptr(X), _ptr(alpha), _ptr(gamma), _ptr(beta), _ptr(Y), N, D,
+          act, par, _stream(stream))
+
+
+def mn_dyt_backward_ex(X, alpha, gamma, dY, dX, dalpha, dgamma, dbeta, workspace, stream=None):
+    N, D = _nd(X)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, D)); _scalar_t("alpha", alpha, 1)
+    _check_t("gamma", gamma, gamma.dtype, (D,)); _check_t("dY", dY, X.dtype, (N, D))
+    _check_t("dX", dX, dX.dtype, (N, D)); _scalar_t("dalpha", dalpha, 1)
+    _check_t("dgamma", dgamma, F32, (D,)); _check_t("dbeta", dbeta, F32, (D,))
+    _call("mn_dyt_backward_ex", _ptr(X), _ptr(alpha), _ptr(gamma), _ptr(dY), _ptr(dX),
+          _ptr(dalpha), _ptr(dgamma), _ptr(dbeta), N, D, act, par, _code("dX", dX),
+          _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def mn_polynorm_forward_ex(X, params, Y, rstd, eps: float, stream=None):
+    N, D = _nd(X)
+    _check_t("X", X, X.dtype, (N, D)); _scalar_t("params", params, 4)
+    _check_t("Y", Y, X.dtype, (N, D)); _check_t("rstd", rstd, F32, (N, 3))
+    _call("mn_polynorm_forward_ex", _ptr(X), _ptr(params), _ptr(Y), _ptr(rstd), N, D,
+          float(eps), _code("X", X), _stream(stream))
+
+
+def mn_polynorm_backward_ex(X, params, rstd, dY, dX, dparams, workspace, stream=None):
+    N, D = _nd(X)
+    _check_t("X", X, X.dtype, (N, D)); _scalar_t("params", params, 4)
+    _check_t("rstd", rstd, F32, (N, 3)); _check_t("dY", dY, X.dtype, (N, D))
+    _check_t("dX", dX, dX.dtype, (N, D)); _scalar_t("dparams", dparams, 4)
+    _call("mn_polynorm_backward_ex", _ptr(X), _ptr(params), _ptr(rstd), _ptr(dY), _ptr(dX),
+          _ptr(dparams), N, D, _code("X", X), _code("dX", dX), _ptr(workspace),
+          _ws_bytes(workspace), _stream(stream))
+
+
+def mn_mod_rmsnorm_forward_ex(X, gamma, scale, shift, Y, rstd, eps: float, stream=None):
+    N, D = _nd(X)
+    B = int(scale.shape[0])
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, D)); _check_t("gamma", gamma, gamma.dtype, (D,))
+    _check_t("scale", scale, X.dtype, (B, D)); _check_t("shift", shift, X.dtype, (B, D))
+    _check_t("Y", Y, X.dtype, (N, D)); _check_t("rstd", rstd, F32, (N,))
+    _call("mn_mod_rmsnorm_forward_ex", _ptr(X), _ptr(gamma), _ptr(scale), _ptr(shift), _ptr(Y),
+          _ptr(rstd), B, N, D, float(eps), act, par, _stream(stream))
+
+
+def mn_mod_rmsnorm_backward_ex(X, gamma, scale, rstd, dY, dX, dgamma, dscale, dshift, workspace,
+                               stream=None):
+    N, D = _nd(X)
+    B = int(scale.shape[0])
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, D)); _check_t("gamma", gamma, gamma.dtype, (D,))
+    _check_t("scale", scale, X.dtype, (B, D)); _check_t("rstd", rstd, F32, (N,))
+    _check_t("dY", dY, X.dtype, (N, D)); _check_t("dX", dX, dX.dtype, (N, D))
+    _check_t("dgamma", dgamma, F32, (D,)); _check_t("dscale", dscale, F32, (B, D))
+    _check_t("dshift", dshift, F32, (B, D))
+    _call("mn_mod_rmsnorm_backward_ex", _ptr(X), _ptr(gamma), _ptr(scale), _ptr(rstd), _ptr(dY),
+          _ptr(dX), _ptr(dgamma), _ptr(dscale), _ptr(dshift), B, N, D, act, par,
+          _code("dX", dX), _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
 def _ws_bytes(workspace: Optional[torch.Tensor]) -> int:
     if workspace is None:
         return 0
@@ -348,8 +431,14 @@ def _ws_bytes(workspace: Optional[torch.Tensor]) -> int:
 
 # --- allocating helpers -------------------------------------------------------
 
-def new_workspace(kind: int, N: int, D: int, device=None) -> torch.Tensor:
-    nbytes = max(16, workspace_bytes(kind, N, D))
+def mod_rmsnorm_workspace_bytes(B: int, N: int, D: int) -> int:
+    return int(lib().mn_mod_rmsnorm_workspace_bytes(int(B), int(N), int(D)))
+
+
+def new_workspace(kind: int, N: int, D: int, device=None, B: int = 1) -> torch.Tensor:
+    nb = mod_rmsnorm_workspace_bytes(B, N, D) if kind == MN_MOD_RMSNORM else workspace_bytes(
+        kind, N, D)
+    nbytes = max(16, nb)
     return torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=device or "cuda")
 
 
@@ -405,3 +494,57 @@ def add_rmsnorm_backward(X, R, gamma, rstd, dY, dH=None, stream=None, dx_dtype=N
     ws = new_workspace(MN_ADD_RMSNORM, N, D, X.device)
     mn_add_rmsnorm_backward_ex(X, R, gamma, rstd, dY, dH, dX, dgamma, ws, stream)
     return dX, dgamma
+
+
+def dyt_forward(X, alpha, gamma, beta, stream=None):
+    Y = torch.empty_like(X)
+    mn_dyt_forward_ex(X, alpha, gamma, beta, Y, stream)
+    return Y
+
+
+def dyt_backward(X, alpha, gamma, dY, stream=None, dx_dtype=None):
+    N, D = _nd(X)
+    dX = torch.empty_like(X, dtype=dx_dtype or X.dtype)
+    dalpha = torch.empty(1, dtype=F32, device=X.device)
+    dgamma = torch.empty(D, dtype=F32, device=X.device)
+    dbeta = torch.empty(D, dtype=F32, device=X.device)
+    ws = new_workspace(MN_DYT, N, D, X.device)
+    mn_dyt_backward_ex(X, alpha, gamma, dY, dX, dalpha, dgamma, dbeta, ws, stream)
+    return dX, dalpha, dgamma, dbeta
+
+
+def polynorm_forward(X, params, eps: float = 1e-5, stream=None):
+    N, D = _nd(X)
+    Y = torch.empty_like(X)
+    rstd = torch.empty(N, 3, dtype=F32, device=X.device)
+    mn_polynorm_forward_ex(X, params, Y, rstd, eps, stream)
+    return Y, rstd
+
+
+def polynorm_backward(X, params, rstd, dY, stream=None, dx_dtype=None):
+    N, D = _nd(X)
+    dX = torch.empty_like(X, dtype=dx_dtype or X.dtype)
+    dparams = torch.empty(4, dtype=F32, device=X.device)
+    ws = new_workspace(MN_POLYNORM, N, D, X.device)
+    mn_polynorm_backward_ex(X, params, rstd, dY, dX, dparams, ws, stream)
+    return dX, dparams
+
+
+def mod_rmsnorm_forward(X, gamma, scale, shift, eps: float = 1e-5, stream=None):
+    N, D = _nd(X)
+    Y = torch.empty_like(X)
+    rstd = torch.empty(N, dtype=F32, device=X.device)
+    mn_mod_rmsnorm_forward_ex(X, gamma, scale, shift, Y, rstd, eps, stream)
+    return Y, rstd
+
+
+def mod_rmsnorm_backward(X, gamma, scale, rstd, dY, stream=None, dx_dtype=None):
+    N, D = _nd(X)
+    B = int(scale.shape[0])
+    dX = torch.empty_like(X, dtype=dx_dtype or X.dtype)
+    dgamma = torch.empty(D, dtype=F32, device=X.device)
+    dscale = torch.empty(B, D, dtype=F32, device=X.device)
+    dshift = torch.empty(B, D, dtype=F32, device=X.device)
+    ws = new_workspace(MN_MOD_RMSNORM, N, D, X.device, B=B)
+    mn_mod_rmsnorm_backward_ex(X, gamma, scale, rstd, dY, dX, dgamma, dscale, dshift, ws, stream)
+    return dX, dgamma, dscale, dshift

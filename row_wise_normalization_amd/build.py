@@ -16,10 +16,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmn_norm.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-# The kernel instances are split by activation storage type so that the
-# sources compile in parallel.
-SOURCES = ["mn_inst_f16.hip", "mn_inst_bf16.hip", "mn_inst_f32.hip", "mn_kernels.hip",
-           "mn_api.cpp"]
+# The kernel instances are split by activation storage type and kind group
+# so that the sources compile in parallel.
+SOURCES = ["mn_inst_f16.hip", "mn_inst_bf16.hip", "mn_inst_f32.hip", "mn_inst_ext_f16.hip",
+           "mn_inst_ext_bf16.hip", "mn_inst_ext_f32.hip", "mn_kernels.hip", "mn_api.cpp"]
 ARCH = "gfx950"
 
 # Device-code flags. Packed fp32 instructions are disabled on purpose; no

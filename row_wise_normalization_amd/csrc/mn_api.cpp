@@ -57,12 +57,34 @@ bool alias_free(const Span (&in)[NI], const Span (&out)[NO])
 // elements for the 16-bit storage types, of 4 for binary32.
 bool chunks_fit(int st, int64_t D) { return D % (st == mn::ST_F32 ? 4 : 8) == 0; }
 
-size_t workspace_bytes(int kind, int64_t N, int64_t D)
+// Largest sample count of the Modulated RMSNorm (its backward keeps one set
+// of partial rows per sample).
+constexpr int64_t kMaxSamples = 4096;
+
+bool samples_ok(int kind, int64_t B, int64_t N)
 {
-    if (!shape_ok(N, D) || kind < 0 || kind > 2) return 0;
-    const int64_t P = mn::bwd_partial_rows(kind, N, (int32_t)D);
+    if (kind != mn::MOD) return true;
+    return B >= 1 && B <= kMaxSamples && N % B == 0;
+}
+
+int64_t partial_rows(int kind, int64_t N, int64_t D, int64_t B)
+{
+    if (kind == mn::MOD) return B * mn::mod_blocks_per_sample(B, N);
+    return mn::bwd_partial_rows(kind, N, (int32_t)D);
+}
+
+bool has_scalar_partials(int kind) { return kind == mn::DYT || kind == mn::POLY; }
+
+// Workspace: per-workgroup fp32 partial rows [P][Dp] for each per-column
+// parameter gradient, then (DYT, POLY) [P][4] scalar partials.
+size_t workspace_bytes(int kind, int64_t N, int64_t D, int64_t B = 1)
+{
+    if (!shape_ok(N, D) || kind < 0 || kind > mn::MOD || !samples_ok(kind, B, N)) return 0;
+    const int64_t P = partial_rows(kind, N, D, B);
     const int64_t Dp = mn::partial_stride((int32_t)D);
-    return (size_t)P * (size_t)Dp * sizeof(float) * (kind == mn::LN ? 2u : 1u);
+    size_t bytes = (size_t)P * (size_t)Dp * sizeof(float) * (size_t)mn::bwd_vector_partials(kind);
+    if (has_scalar_partials(kind)) bytes += (size_t)P * 4u * sizeof(float);
+    return bytes;
 }
 
 mn_status device_status(hipError_t e)
@@ -78,38 +100,69 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 // Forward.
 // ---------------------------------------------------------------------------
 
-mn_status forward(int kind, const void* X, const void* R, const void* gamma, const void* beta,
-                  void* H, void* Y, float* mean, float* rstd, int64_t N, int64_t D, float eps,
-                  int st, int pdt, void* stream)
-{
-    if (!X || !gamma || !Y || !rstd) return MN_ERR_NULL;
-    if (kind == mn::LN && (!beta || !mean)) return MN_ERR_NULL;
-    if (kind == mn::ADD && (!R || !H)) return MN_ERR_NULL;
-    if (!dtype_ok(st) || !dtype_ok(pdt)) return MN_ERR_DTYPE;
-    if (!shape_ok(N, D)) return MN_ERR_SHAPE;
-    if (!eps_ok(eps)) return MN_ERR_EPS;
+struct FwdIn {
+    const void* X = nullptr;
+    const void* R = nullptr;         // ADD
+    const void* gamma = nullptr;     // all but POLY
+    const void* beta = nullptr;      // LN, DYT
+    const float* alpha = nullptr;    // DYT
+    const float* poly = nullptr;     // POLY: w1, w2, w3, b
+    const void* scale = nullptr;     // MOD
+    const void* shift = nullptr;     // MOD
+    void* H = nullptr;               // ADD
+    void* Y = nullptr;
+    float* mean = nullptr;           // LN
+    float* rstd = nullptr;           // all but DYT (POLY: [N][3])
+    int64_t B = 1;                   // MOD: samples
+};
 
-    const size_t nd = (size_t)N * (size_t)D * (size_t)mn::stor_bytes(st);
+mn_status forward(int kind, const FwdIn& f, int64_t N, int64_t D, float eps, int st, int pdt,
+                  void* stream)
+{
+    if (!f.X || !f.Y) return MN_ERR_NULL;
+    if (kind != mn::POLY && !f.gamma) return MN_ERR_NULL;
+    if (kind != mn::DYT && !f.rstd) return MN_ERR_NULL;
+    if ((kind == mn::LN || kind == mn::DYT) && !f.beta) return MN_ERR_NULL;
+    if (kind == mn::LN && !f.mean) return MN_ERR_NULL;
+    if (kind == mn::ADD && (!f.R || !f.H)) return MN_ERR_NULL;
+    if (kind == mn::DYT && !f.alpha) return MN_ERR_NULL;
+    if (kind == mn::POLY && !f.poly) return MN_ERR_NULL;
+    if (kind == mn::MOD && (!f.scale || !f.shift)) return MN_ERR_NULL;
+    if (!dtype_ok(st) || !dtype_ok(pdt)) return MN_ERR_DTYPE;
+    if (!shape_ok(N, D) || !samples_ok(kind, f.B, N)) return MN_ERR_SHAPE;
+    if (kind != mn::DYT && !eps_ok(eps)) return MN_ERR_EPS;
+
+    const size_t es = (size_t)mn::stor_bytes(st);
+    const size_t nd = (size_t)N * (size_t)D * es;
     const size_t dp = (size_t)D * (size_t)mn::stor_bytes(pdt);
-    const Span in[] = {span(X, nd), span(R, nd), span(gamma, dp), span(beta, dp)};
-    const Span out[] = {span(Y, nd), span(H, nd), span(rstd, (size_t)N * 4u),
-                        span(mean, (size_t)N * 4u)};
+    const size_t bd = (kind == mn::MOD) ? (size_t)f.B * (size_t)D * es : 0;
+    const size_t nstat = (size_t)N * 4u * (kind == mn::POLY ? 3u : 1u);
+    const Span in[] = {span(f.X, nd), span(f.R, nd), span(f.gamma, dp), span(f.beta, dp),
+                       span(f.alpha, 4), span(f.poly, 16), span(f.scale, bd), span(f.shift, bd)};
+    const Span out[] = {span(f.Y, nd), span(f.H, nd), span(f.rstd, nstat),
+                        span(f.mean, (size_t)N * 4u)};
     if (!alias_free(in, out)) return MN_ERR_ALIAS;
 
-    const bool vec_ok = chunks_fit(st, D) && aligned16(X) && aligned16(R) && aligned16(gamma) &&
-                        aligned16(beta) && aligned16(Y) && aligned16(H);
+    const bool vec_ok = chunks_fit(st, D) && aligned16(f.X) && aligned16(f.R) &&
+                        aligned16(f.gamma) && aligned16(f.beta) && aligned16(f.Y) &&
+                        aligned16(f.H) && aligned16(f.scale) && aligned16(f.shift);
     const mn::FwdPlan plan = mn::plan_forward(kind, st, N, (int32_t)D, vec_ok);
     if (plan.grid > INT32_MAX) return MN_ERR_SHAPE;  // one workgroup per tile of rows
     mn::FwdArgs a;
-    a.X = X;
-    a.R = R;
-    a.gamma = gamma;
-    a.beta = beta;
-    a.Y = Y;
-    a.H = H;
-    a.mean = mean;
-    a.rstd = rstd;
+    a.X = f.X;
+    a.R = f.R;
+    a.gamma = f.gamma;
+    a.beta = f.beta;
+    a.alpha = f.alpha;
+    a.poly = f.poly;
+    a.scale = f.scale;
+    a.shift = f.shift;
+    a.Y = f.Y;
+    a.H = f.H;
+    a.mean = f.mean;
+    a.rstd = f.rstd;
     a.N = N;
+    a.S = (kind == mn::MOD) ? N / f.B : 0;
     a.D = (int32_t)D;
     a.pdt = pdt;
     a.eps = eps;
@@ -121,9 +174,26 @@ mn_status forward(int kind, const void* X, const void* R, const void* gamma, con
 // ---------------------------------------------------------------------------
 
 struct BwdIn {
-    const void *X, *R, *gamma, *dY, *dH;
-    const float *mean, *rstd;
-    void* dX;
+    const void* X = nullptr;
+    const void* R = nullptr;         // ADD
+    const void* gamma = nullptr;     // all but POLY
+    const void* dY = nullptr;
+    const void* dH = nullptr;        // ADD (may be NULL)
+    const float* mean = nullptr;     // LN
+    const float* rstd = nullptr;     // all but DYT
+    const float* alpha = nullptr;    // DYT
+    const float* poly = nullptr;     // POLY
+    const void* scale = nullptr;     // MOD
+    void* dX = nullptr;
+    int64_t B = 1;                   // MOD
+};
+
+// Parameter gradients (fp32).
+struct BwdOut {
+    float* dgamma = nullptr;         // all but POLY
+    float* dbeta = nullptr;          // LN, DYT; MOD: dscale [B][D]
+    float* dshift = nullptr;         // MOD [B][D]
+    float* dscalar = nullptr;        // DYT: dalpha [1]; POLY: d(w1, w2, w3, b) [4]
 };
 
 // Storage types of one backward call: activations (X, R), parameters
@@ -132,36 +202,58 @@ struct BwdTypes {
     int st, pdt, ct, ot;
 };
 
-mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, const BwdTypes& t,
-                        void* ws, size_t ws_bytes, const float* dgamma, const float* dbeta,
-                        void* stream)
+// Byte spans of the parameter-gradient outputs.
+void out_spans(int kind, const BwdOut& o, int64_t D, int64_t B, Span (&sp)[4])
 {
-    if (!b.X || !b.gamma || !b.dY || !b.rstd || !b.dX) return MN_ERR_NULL;
+    const size_t dv = (size_t)D * 4u;
+    const size_t bdv = (size_t)B * (size_t)D * 4u;
+    sp[0] = span(o.dgamma, dv);
+    sp[1] = span(o.dbeta, kind == mn::MOD ? bdv : dv);
+    sp[2] = span(o.dshift, bdv);
+    sp[3] = span(o.dscalar, kind == mn::POLY ? 16u : 4u);
+}
+
+mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, const BwdTypes& t,
+                        void* ws, size_t ws_bytes, const BwdOut& o, void* stream)
+{
+    if (!b.X || !b.dY || !b.dX) return MN_ERR_NULL;
+    if (kind != mn::POLY && !b.gamma) return MN_ERR_NULL;
+    if (kind != mn::DYT && !b.rstd) return MN_ERR_NULL;
     if (kind == mn::LN && !b.mean) return MN_ERR_NULL;
     if (kind == mn::ADD && !b.R) return MN_ERR_NULL;
+    if (kind == mn::DYT && !b.alpha) return MN_ERR_NULL;
+    if (kind == mn::POLY && !b.poly) return MN_ERR_NULL;
+    if (kind == mn::MOD && !b.scale) return MN_ERR_NULL;
     if (!dtype_ok(t.st) || !dtype_ok(t.pdt) || !dtype_ok(t.ct) || !dtype_ok(t.ot) ||
-        !mn::backward_types_supported(t.st, t.ct, t.ot))
+        !mn::backward_types_supported(kind, t.st, t.ct, t.ot))
         return MN_ERR_DTYPE;
+    if (!shape_ok(N, D) || !samples_ok(kind, b.B, N)) return MN_ERR_SHAPE;
     const int st = t.st;
-    if (!shape_ok(N, D)) return MN_ERR_SHAPE;
-    const size_t need = workspace_bytes(kind, N, D);
+    const size_t need = workspace_bytes(kind, N, D, b.B);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
 
-    const size_t nd = (size_t)N * (size_t)D * (size_t)mn::stor_bytes(st);
+    const size_t es = (size_t)mn::stor_bytes(st);
+    const size_t nd = (size_t)N * (size_t)D * es;
     const size_t ndc = (size_t)N * (size_t)D * (size_t)mn::stor_bytes(t.ct);
     const size_t ndo = (size_t)N * (size_t)D * (size_t)mn::stor_bytes(t.ot);
     const size_t dp = (size_t)D * (size_t)mn::stor_bytes(t.pdt);
+    const size_t bd = (kind == mn::MOD) ? (size_t)b.B * (size_t)D * es : 0;
+    const size_t nstat = (size_t)N * 4u * (kind == mn::POLY ? 3u : 1u);
     const Span in[] = {span(b.X, nd), span(b.R, nd), span(b.gamma, dp), span(b.dY, ndc),
-                       span(b.dH, ndc), span(b.mean, (size_t)N * 4u),
-                       span(b.rstd, (size_t)N * 4u)};
-    const Span out[] = {span(b.dX, ndo), span(ws, need), span(dgamma, (size_t)D * 4u),
-                        span(dbeta, (size_t)D * 4u)};
+                       span(b.dH, ndc), span(b.mean, (size_t)N * 4u), span(b.rstd, nstat),
+                       span(b.alpha, 4), span(b.poly, 16), span(b.scale, bd)};
+    Span ps[4];
+    out_spans(kind, o, D, b.B, ps);
+    const Span out[] = {span(b.dX, ndo), span(ws, need), ps[0], ps[1], ps[2], ps[3]};
     if (!alias_free(in, out)) return MN_ERR_ALIAS;
 
     const bool vec_ok = chunks_fit(st, D) && aligned16(b.X) && aligned16(b.R) &&
                         aligned16(b.gamma) && aligned16(b.dY) && aligned16(b.dH) &&
-                        aligned16(b.dX);
-    const mn::BwdPlan plan = mn::plan_backward(kind, st, N, (int32_t)D, vec_ok);
+                        aligned16(b.dX) && aligned16(b.scale);
+    const mn::BwdPlan plan = mn::plan_backward(kind, st, N, (int32_t)D, vec_ok, b.B);
+    float* w = static_cast<float*>(ws);
+    const int64_t PD = plan.P * plan.Dp;
+    const int nv = mn::bwd_vector_partials(kind);
     mn::BwdArgs a;
     a.X = b.X;
     a.R = b.R;
@@ -170,50 +262,148 @@ mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, const Bw
     a.dH = b.dH;
     a.mean = b.mean;
     a.rstd = b.rstd;
+    a.alpha = b.alpha;
+    a.poly = b.poly;
+    a.scale = b.scale;
     a.dX = b.dX;
-    a.part_g = static_cast<float*>(ws);
-    a.part_b = (kind == mn::LN) ? static_cast<float*>(ws) + plan.P * plan.Dp : nullptr;
+    a.part_g = nv > 0 ? w : nullptr;
+    a.part_b = nv > 1 ? w + PD : nullptr;
+    a.part_h = nv > 2 ? w + 2 * PD : nullptr;
+    a.part_a = has_scalar_partials(kind) ? w + nv * PD : nullptr;
     a.N = N;
+    a.S = (kind == mn::MOD) ? N / b.B : 0;
     a.D = (int32_t)D;
     a.Dp = plan.Dp;
     a.pdt = t.pdt;
+    a.Pb = plan.Pb;
     return device_status(
         mn::launch_backward_rows(kind, st, t.ct, t.ot, plan, a, as_stream(stream)));
 }
 
-mn_status reduce_partials(int kind, int64_t N, int64_t D, const void* ws, size_t ws_bytes,
-                          float* dgamma, float* dbeta, void* stream)
+// Stage 2 for every kind: the fixed-order column sums of the partial rows.
+mn_status reduce_partials(int kind, int64_t N, int64_t D, int64_t B, const void* ws,
+                          size_t ws_bytes, const BwdOut& o, void* stream)
 {
-    if (!dgamma || (kind == mn::LN && !dbeta)) return MN_ERR_NULL;
-    if (kind < 0 || kind > 2) return MN_ERR_SHAPE;
-    if (!shape_ok(N, D)) return MN_ERR_SHAPE;
-    const size_t need = workspace_bytes(kind, N, D);
+    if (kind < 0 || kind > mn::MOD) return MN_ERR_SHAPE;
+    if (kind != mn::POLY && !o.dgamma) return MN_ERR_NULL;
+    if ((kind == mn::LN || kind == mn::DYT || kind == mn::MOD) && !o.dbeta) return MN_ERR_NULL;
+    if (kind == mn::MOD && !o.dshift) return MN_ERR_NULL;
+    if (has_scalar_partials(kind) && !o.dscalar) return MN_ERR_NULL;
+    if (!shape_ok(N, D) || !samples_ok(kind, B, N)) return MN_ERR_SHAPE;
+    const size_t need = workspace_bytes(kind, N, D, B);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
+    Span ps[4];
+    out_spans(kind, o, D, B, ps);
     const Span in[] = {span(ws, need)};
-    const Span out[] = {span(dgamma, (size_t)D * 4u),
-                        span(kind == mn::LN ? dbeta : nullptr, (size_t)D * 4u)};
+    const Span out[] = {ps[0], ps[1], ps[2], ps[3]};
     if (!alias_free(in, out)) return MN_ERR_ALIAS;
 
-    mn::ReduceArgs a;
-    a.P = mn::bwd_partial_rows(kind, N, (int32_t)D);
-    a.Dp = mn::partial_stride((int32_t)D);
-    a.D = (int32_t)D;
-    a.part_g = static_cast<const float*>(ws);
-    a.part_b = (kind == mn::LN) ? static_cast<const float*>(ws) + a.P * a.Dp : nullptr;
-    a.dgamma = dgamma;
-    a.dbeta = (kind == mn::LN) ? dbeta : nullptr;
-    return device_status(mn::launch_reduce(a, as_stream(stream)));
+    const int64_t P = partial_rows(kind, N, D, B);
+    const int32_t Dp = mn::partial_stride((int32_t)D);
+    const int64_t PD = P * Dp;
+    const int nv = mn::bwd_vector_partials(kind);
+    const float* w = static_cast<const float*>(ws);
+    hipStream_t s = as_stream(stream);
+    if (nv > 0) {
+        mn::ReduceArgs a;
+        a.part_g = w;
+        a.part_b = (kind == mn::LN || kind == mn::DYT) ? w + PD : nullptr;
+        a.dgamma = o.dgamma;
+        a.dbeta = a.part_b ? o.dbeta : nullptr;
+        a.P = P;
+        a.D = (int32_t)D;
+        a.Dp = Dp;
+        a.groups = 1;
+        mn_status r = device_status(mn::launch_reduce(a, s));
+        if (r != MN_OK) return r;
+    }
+    if (kind == mn::MOD) {
+        // dscale and dshift: the partial rows of each sample's workgroups
+        mn::ReduceArgs a;
+        a.part_g = w + PD;
+        a.part_b = w + 2 * PD;
+        a.dgamma = o.dbeta;
+        a.dbeta = o.dshift;
+        a.P = P / B;
+        a.D = (int32_t)D;
+        a.Dp = Dp;
+        a.groups = (int32_t)B;
+        mn_status r = device_status(mn::launch_reduce(a, s));
+        if (r != MN_OK) return r;
+    }
+    if (has_scalar_partials(kind)) {
+        mn::ReduceArgs a;
+        a.part_g = w + nv * PD;
+        a.part_b = nullptr;
+        a.dgamma = o.dscalar;
+        a.dbeta = nullptr;
+        a.P = P;
+        a.D = kind == mn::POLY ? 4 : 1;
+        a.Dp = 4;
+        a.groups = 1;
+        mn_status r = device_status(mn::launch_reduce(a, s));
+        if (r != MN_OK) return r;
+    }
+    return MN_OK;
 }
 
 const BwdTypes kF16{MN_F16, MN_F16, MN_F16, MN_F16};
 
-mn_status backward(int kind, const BwdIn& b, float* dgamma, float* dbeta, int64_t N, int64_t D,
+mn_status backward(int kind, const BwdIn& b, const BwdOut& o, int64_t N, int64_t D,
                    const BwdTypes& t, void* ws, size_t ws_bytes, void* stream)
 {
-    if (!dgamma || (kind == mn::LN && !dbeta)) return MN_ERR_NULL;
-    mn_status s = backward_rows(kind, b, N, D, t, ws, ws_bytes, dgamma, dbeta, stream);
+    if (kind != mn::POLY && !o.dgamma) return MN_ERR_NULL;
+    if ((kind == mn::LN || kind == mn::DYT || kind == mn::MOD) && !o.dbeta) return MN_ERR_NULL;
+    if (kind == mn::MOD && !o.dshift) return MN_ERR_NULL;
+    if (has_scalar_partials(kind) && !o.dscalar) return MN_ERR_NULL;
+    mn_status s = backward_rows(kind, b, N, D, t, ws, ws_bytes, o, stream);
     if (s != MN_OK) return s;
-    return reduce_partials(kind, N, D, ws, ws_bytes, dgamma, dbeta, stream);
+    return reduce_partials(kind, N, D, b.B, ws, ws_bytes, o, stream);
+}
+
+}  // namespace
+
+namespace {
+
+FwdIn fwd_in(const void* X, const void* R, const void* gamma, const void* beta, void* H, void* Y,
+             float* mean, float* rstd)
+{
+    FwdIn f;
+    f.X = X;
+    f.R = R;
+    f.gamma = gamma;
+    f.beta = beta;
+    f.H = H;
+    f.Y = Y;
+    f.mean = mean;
+    f.rstd = rstd;
+    return f;
+}
+
+BwdIn bwd_in(const void* X, const void* R, const void* gamma, const void* dY, const void* dH,
+             const float* mean, const float* rstd, void* dX)
+{
+    BwdIn b;
+    b.X = X;
+    b.R = R;
+    b.gamma = gamma;
+    b.dY = dY;
+    b.dH = dH;
+    b.mean = mean;
+    b.rstd = rstd;
+    b.dX = dX;
+    return b;
+}
+
+BwdOut bwd_out(float* dgamma, float* dbeta = nullptr, float* dshift = nullptr,
+               float* dscalar = nullptr)
+{
+    BwdOut o;
+    o.dgamma = dgamma;
+    o.dbeta = dbeta;
+    o.dshift = dshift;
+    o.dscalar = dscalar;
+    return o;
 }
 
 }  // namespace
@@ -222,26 +412,27 @@ extern "C" {
 
 // --- binary16 entry points ---------------------------------------------------
 
+
 mn_status mn_rmsnorm_forward(const mn_f16* X, const mn_f16* gamma, mn_f16* Y, float* rstd,
                              int64_t N, int64_t D, float eps, void* stream)
 {
-    return forward(mn::RMS, X, nullptr, gamma, nullptr, nullptr, Y, nullptr, rstd, N, D, eps,
-                   MN_F16, MN_F16, stream);
+    return forward(mn::RMS, fwd_in(X, nullptr, gamma, nullptr, nullptr, Y, nullptr, rstd), N, D,
+                   eps, MN_F16, MN_F16, stream);
 }
 
 mn_status mn_layernorm_forward(const mn_f16* X, const mn_f16* gamma, const mn_f16* beta,
                                mn_f16* Y, float* mean, float* rstd, int64_t N, int64_t D,
                                float eps, void* stream)
 {
-    return forward(mn::LN, X, nullptr, gamma, beta, nullptr, Y, mean, rstd, N, D, eps, MN_F16,
-                   MN_F16, stream);
+    return forward(mn::LN, fwd_in(X, nullptr, gamma, beta, nullptr, Y, mean, rstd), N, D, eps,
+                   MN_F16, MN_F16, stream);
 }
 
 mn_status mn_add_rmsnorm_forward(const mn_f16* X, const mn_f16* R, const mn_f16* gamma,
                                  mn_f16* H, mn_f16* Y, float* rstd, int64_t N, int64_t D,
                                  float eps, void* stream)
 {
-    return forward(mn::ADD, X, R, gamma, nullptr, H, Y, nullptr, rstd, N, D, eps, MN_F16,
+    return forward(mn::ADD, fwd_in(X, R, gamma, nullptr, H, Y, nullptr, rstd), N, D, eps, MN_F16,
                    MN_F16, stream);
 }
 
@@ -249,9 +440,8 @@ mn_status mn_rmsnorm_backward(const mn_f16* X, const mn_f16* gamma, const float*
                               const mn_f16* dY, mn_f16* dX, float* dgamma, int64_t N, int64_t D,
                               void* workspace, size_t workspace_bytes, void* stream)
 {
-    const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
-    return backward(mn::RMS, b, dgamma, nullptr, N, D, kF16, workspace, workspace_bytes,
-                    stream);
+    return backward(mn::RMS, bwd_in(X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX),
+                    bwd_out(dgamma), N, D, kF16, workspace, workspace_bytes, stream);
 }
 
 mn_status mn_layernorm_backward(const mn_f16* X, const mn_f16* gamma, const float* mean,
@@ -259,9 +449,8 @@ mn_status mn_layernorm_backward(const mn_f16* X, const mn_f16* gamma, const floa
                                 float* dbeta, int64_t N, int64_t D, void* workspace,
                                 size_t workspace_bytes, void* stream)
 {
-    const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
-    return backward(mn::LN, b, dgamma, dbeta, N, D, kF16, workspace, workspace_bytes,
-                    stream);
+    return backward(mn::LN, bwd_in(X, nullptr, gamma, dY, nullptr, mean, rstd, dX),
+                    bwd_out(dgamma, dbeta), N, D, kF16, workspace, workspace_bytes, stream);
 }
 
 mn_status mn_add_rmsnorm_backward(const mn_f16* X, const mn_f16* R, const mn_f16* gamma,
@@ -269,18 +458,16 @@ mn_status mn_add_rmsnorm_backward(const mn_f16* X, const mn_f16* R, const mn_f16
                                   mn_f16* dX, float* dgamma, int64_t N, int64_t D,
                                   void* workspace, size_t workspace_bytes, void* stream)
 {
-    const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
-    return backward(mn::ADD, b, dgamma, nullptr, N, D, kF16, workspace, workspace_bytes,
-                    stream);
+    return backward(mn::ADD, bwd_in(X, R, gamma, dY, dH, nullptr, rstd, dX), bwd_out(dgamma), N,
+                    D, kF16, workspace, workspace_bytes, stream);
 }
 
 mn_status mn_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const float* rstd,
                                    const mn_f16* dY, mn_f16* dX, int64_t N, int64_t D,
                                    void* workspace, size_t workspace_bytes, void* stream)
 {
-    const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
-    return backward_rows(mn::RMS, b, N, D, kF16, workspace, workspace_bytes, nullptr,
-                         nullptr, stream);
+    return backward_rows(mn::RMS, bwd_in(X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX), N,
+                         D, kF16, workspace, workspace_bytes, BwdOut(), stream);
 }
 
 mn_status mn_layernorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const float* mean,
@@ -288,9 +475,8 @@ mn_status mn_layernorm_backward_rows(const mn_f16* X, const mn_f16* gamma, const
                                      int64_t D, void* workspace, size_t workspace_bytes,
                                      void* stream)
 {
-    const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
-    return backward_rows(mn::LN, b, N, D, kF16, workspace, workspace_bytes, nullptr,
-                         nullptr, stream);
+    return backward_rows(mn::LN, bwd_in(X, nullptr, gamma, dY, nullptr, mean, rstd, dX), N, D,
+                         kF16, workspace, workspace_bytes, BwdOut(), stream);
 }
 
 mn_status mn_add_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* R, const mn_f16* gamma,
@@ -298,9 +484,8 @@ mn_status mn_add_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* R, const m
                                        mn_f16* dX, int64_t N, int64_t D, void* workspace,
                                        size_t workspace_bytes, void* stream)
 {
-    const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
-    return backward_rows(mn::ADD, b, N, D, kF16, workspace, workspace_bytes, nullptr,
-                         nullptr, stream);
+    return backward_rows(mn::ADD, bwd_in(X, R, gamma, dY, dH, nullptr, rstd, dX), N, D, kF16,
+                         workspace, workspace_bytes, BwdOut(), stream);
 }
 
 // --- entry points with explicit storage types --------------------------------
@@ -308,24 +493,24 @@ mn_status mn_add_rmsnorm_backward_rows(const mn_f16* X, const mn_f16* R, const m
 mn_status mn_rmsnorm_forward_ex(const void* X, const void* gamma, void* Y, float* rstd, int64_t N,
                                 int64_t D, float eps, mn_dtype act, mn_dtype param, void* stream)
 {
-    return forward(mn::RMS, X, nullptr, gamma, nullptr, nullptr, Y, nullptr, rstd, N, D, eps,
-                   act, param, stream);
+    return forward(mn::RMS, fwd_in(X, nullptr, gamma, nullptr, nullptr, Y, nullptr, rstd), N, D,
+                   eps, act, param, stream);
 }
 
 mn_status mn_layernorm_forward_ex(const void* X, const void* gamma, const void* beta, void* Y,
                                   float* mean, float* rstd, int64_t N, int64_t D, float eps,
                                   mn_dtype act, mn_dtype param, void* stream)
 {
-    return forward(mn::LN, X, nullptr, gamma, beta, nullptr, Y, mean, rstd, N, D, eps, act, param,
-                   stream);
+    return forward(mn::LN, fwd_in(X, nullptr, gamma, beta, nullptr, Y, mean, rstd), N, D, eps,
+                   act, param, stream);
 }
 
 mn_status mn_add_rmsnorm_forward_ex(const void* X, const void* R, const void* gamma, void* H,
                                     void* Y, float* rstd, int64_t N, int64_t D, float eps,
                                     mn_dtype act, mn_dtype param, void* stream)
 {
-    return forward(mn::ADD, X, R, gamma, nullptr, H, Y, nullptr, rstd, N, D, eps, act, param,
-                   stream);
+    return forward(mn::ADD, fwd_in(X, R, gamma, nullptr, H, Y, nullptr, rstd), N, D, eps, act,
+                   param, stream);
 }
 
 mn_status mn_rmsnorm_backward_ex(const void* X, const void* gamma, const float* rstd,
@@ -333,9 +518,9 @@ mn_status mn_rmsnorm_backward_ex(const void* X, const void* gamma, const float* 
                                  mn_dtype act, mn_dtype param, mn_dtype cot, mn_dtype dxt,
                                  void* workspace, size_t workspace_bytes, void* stream)
 {
-    const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
-    return backward(mn::RMS, b, dgamma, nullptr, N, D, BwdTypes{act, param, cot, dxt},
-                    workspace, workspace_bytes, stream);
+    return backward(mn::RMS, bwd_in(X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX),
+                    bwd_out(dgamma), N, D, BwdTypes{act, param, cot, dxt}, workspace,
+                    workspace_bytes, stream);
 }
 
 mn_status mn_layernorm_backward_ex(const void* X, const void* gamma, const float* mean,
@@ -344,8 +529,8 @@ mn_status mn_layernorm_backward_ex(const void* X, const void* gamma, const float
                                    mn_dtype param, mn_dtype cot, mn_dtype dxt, void* workspace,
                                    size_t workspace_bytes, void* stream)
 {
-    const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
-    return backward(mn::LN, b, dgamma, dbeta, N, D, BwdTypes{act, param, cot, dxt}, workspace,
+    return backward(mn::LN, bwd_in(X, nullptr, gamma, dY, nullptr, mean, rstd, dX),
+                    bwd_out(dgamma, dbeta), N, D, BwdTypes{act, param, cot, dxt}, workspace,
                     workspace_bytes, stream);
 }
 
@@ -355,9 +540,8 @@ mn_status mn_add_rmsnorm_backward_ex(const void* X, const void* R, const void* g
                                      mn_dtype param, mn_dtype cot, mn_dtype dxt,
                                      void* workspace, size_t workspace_bytes, void* stream)
 {
-    const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
-    return backward(mn::ADD, b, dgamma, nullptr, N, D, BwdTypes{act, param, cot, dxt},
-                    workspace, workspace_bytes, stream);
+    return backward(mn::ADD, bwd_in(X, R, gamma, dY, dH, nullptr, rstd, dX), bwd_out(dgamma), N,
+                    D, BwdTypes{act, param, cot, dxt}, workspace, workspace_bytes, stream);
 }
 
 mn_status mn_rmsnorm_backward_rows_ex(const void* X, const void* gamma, const float* rstd,
@@ -365,9 +549,9 @@ mn_status mn_rmsnorm_backward_rows_ex(const void* X, const void* gamma, const fl
                                       mn_dtype act, mn_dtype param, mn_dtype cot, mn_dtype dxt,
                                       void* workspace, size_t workspace_bytes, void* stream)
 {
-    const BwdIn b{X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX};
-    return backward_rows(mn::RMS, b, N, D, BwdTypes{act, param, cot, dxt}, workspace,
-                         workspace_bytes, nullptr, nullptr, stream);
+    return backward_rows(mn::RMS, bwd_in(X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX), N,
+                         D, BwdTypes{act, param, cot, dxt}, workspace, workspace_bytes, BwdOut(),
+                         stream);
 }
 
 mn_status mn_layernorm_backward_rows_ex(const void* X, const void* gamma, const float* mean,
@@ -376,9 +560,9 @@ mn_status mn_layernorm_backward_rows_ex(const void* X, const void* gamma, const 
                                         mn_dtype dxt, void* workspace, size_t workspace_bytes,
                                         void* stream)
 {
-    const BwdIn b{X, nullptr, gamma, dY, nullptr, mean, rstd, dX};
-    return backward_rows(mn::LN, b, N, D, BwdTypes{act, param, cot, dxt}, workspace,
-                         workspace_bytes, nullptr, nullptr, stream);
+    return backward_rows(mn::LN, bwd_in(X, nullptr, gamma, dY, nullptr, mean, rstd, dX), N, D,
+                         BwdTypes{act, param, cot, dxt}, workspace, workspace_bytes, BwdOut(),
+                         stream);
 }
 
 mn_status mn_add_rmsnorm_backward_rows_ex(const void* X, const void* R, const void* gamma,
@@ -387,9 +571,75 @@ mn_status mn_add_rmsnorm_backward_rows_ex(const void* X, const void* R, const vo
                                           mn_dtype param, mn_dtype cot, mn_dtype dxt,
                                           void* workspace, size_t workspace_bytes, void* stream)
 {
-    const BwdIn b{X, R, gamma, dY, dH, nullptr, rstd, dX};
-    return backward_rows(mn::ADD, b, N, D, BwdTypes{act, param, cot, dxt}, workspace,
-                         workspace_bytes, nullptr, nullptr, stream);
+    return backward_rows(mn::ADD, bwd_in(X, R, gamma, dY, dH, nullptr, rstd, dX), N, D,
+                         BwdTypes{act, param, cot, dxt}, workspace, workspace_bytes, BwdOut(),
+                         stream);
+}
+
+// --- the other row-wise norms ------------------------------------------------
+
+mn_status mn_dyt_forward_ex(const void* X, const float* alpha, const void* gamma,
+                            const void* beta, void* Y, int64_t N, int64_t D, mn_dtype act,
+                            mn_dtype param, void* stream)
+{
+    FwdIn f = fwd_in(X, nullptr, gamma, beta, nullptr, Y, nullptr, nullptr);
+    f.alpha = alpha;
+    return forward(mn::DYT, f, N, D, 1.0f, act, param, stream);
+}
+
+mn_status mn_dyt_backward_ex(const void* X, const float* alpha, const void* gamma, const void* dY,
+                             void* dX, float* dalpha, float* dgamma, float* dbeta, int64_t N,
+                             int64_t D, mn_dtype act, mn_dtype param, mn_dtype dxt,
+                             void* workspace, size_t workspace_bytes, void* stream)
+{
+    BwdIn b = bwd_in(X, nullptr, gamma, dY, nullptr, nullptr, nullptr, dX);
+    b.alpha = alpha;
+    return backward(mn::DYT, b, bwd_out(dgamma, dbeta, nullptr, dalpha), N, D,
+                    BwdTypes{act, param, act, dxt}, workspace, workspace_bytes, stream);
+}
+
+mn_status mn_polynorm_forward_ex(const void* X, const float* params, void* Y, float* rstd,
+                                 int64_t N, int64_t D, float eps, mn_dtype act, void* stream)
+{
+    FwdIn f = fwd_in(X, nullptr, nullptr, nullptr, nullptr, Y, nullptr, rstd);
+    f.poly = params;
+    return forward(mn::POLY, f, N, D, eps, act, MN_F32, stream);
+}
+
+mn_status mn_polynorm_backward_ex(const void* X, const float* params, const float* rstd,
+                                  const void* dY, void* dX, float* dparams, int64_t N, int64_t D,
+                                  mn_dtype act, mn_dtype dxt, void* workspace,
+                                  size_t workspace_bytes, void* stream)
+{
+    BwdIn b = bwd_in(X, nullptr, nullptr, dY, nullptr, nullptr, rstd, dX);
+    b.poly = params;
+    return backward(mn::POLY, b, bwd_out(nullptr, nullptr, nullptr, dparams), N, D,
+                    BwdTypes{act, MN_F32, act, dxt}, workspace, workspace_bytes, stream);
+}
+
+mn_status mn_mod_rmsnorm_forward_ex(const void* X, const void* gamma, const void* scale,
+                                    const void* shift, void* Y, float* rstd, int64_t B,
+                                    int64_t N, int64_t D, float eps, mn_dtype act, mn_dtype param,
+                                    void* stream)
+{
+    FwdIn f = fwd_in(X, nullptr, gamma, nullptr, nullptr, Y, nullptr, rstd);
+    f.scale = scale;
+    f.shift = shift;
+    f.B = B;
+    return forward(mn::MOD, f, N, D, eps, act, param, stream);
+}
+
+mn_status mn_mod_rmsnorm_backward_ex(const void* X, const void* gamma, const void* scale,
+                                     const float* rstd, const void* dY, void* dX, float* dgamma,
+                                     float* dscale, float* dshift, int64_t B, int64_t N,
+                                     int64_t D, mn_dtype act, mn_dtype param, mn_dtype dxt,
+                                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    BwdIn b = bwd_in(X, nullptr, gamma, dY, nullptr, nullptr, rstd, dX);
+    b.scale = scale;
+    b.B = B;
+    return backward(mn::MOD, b, bwd_out(dgamma, dscale, dshift), N, D,
+                    BwdTypes{act, param, act, dxt}, workspace, workspace_bytes, stream);
 }
 
 // --- workspace, stage 2, diagnostics ----------------------------------------
@@ -398,12 +648,21 @@ mn_status mn_norm_reduce_partials(mn_norm_kind kind, int64_t N, int64_t D, const
                                   size_t workspace_bytes, float* dgamma, float* dbeta,
                                   void* stream)
 {
-    return reduce_partials((int)kind, N, D, workspace, workspace_bytes, dgamma, dbeta, stream);
+    // the split stages are exported for the training pair only
+    if ((int)kind < 0 || (int)kind > mn::ADD) return MN_ERR_SHAPE;
+    return reduce_partials((int)kind, N, D, 1, workspace, workspace_bytes,
+                           bwd_out(dgamma, kind == MN_LAYERNORM ? dbeta : nullptr), stream);
 }
 
 size_t mn_norm_workspace_bytes(mn_norm_kind kind, int64_t N, int64_t D)
 {
+    if (kind == MN_MOD_RMSNORM) return 0;  // depends on the sample count
     return workspace_bytes((int)kind, N, D);
+}
+
+size_t mn_mod_rmsnorm_workspace_bytes(int64_t B, int64_t N, int64_t D)
+{
+    return workspace_bytes(mn::MOD, N, D, B);
 }
 
 const char* mn_status_string(mn_status s)
@@ -411,7 +670,7 @@ const char* mn_status_string(mn_status s)
     switch (s) {
     case MN_OK: return "ok";
     case MN_ERR_NULL: return "a required pointer is NULL";
-    case MN_ERR_SHAPE: return "shape out of range: need N >= 1 and 1 <= D <= 8192";
+    case MN_ERR_SHAPE: return "shape out of range (N >= 1, 1 <= D <= 8192; samples divide N)";
     case MN_ERR_EPS: return "eps must be a positive finite float";
     case MN_ERR_ALIAS: return "an output overlaps an input or another output";
     case MN_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";

@@ -1,8 +1,9 @@
-// mn_instances.hpp -- definitions of the kernel launchers, included by
-// mn_inst_f16.hip, mn_inst_bf16.hip and mn_inst_f32.hip, each of which sets
-// MN_INST_ST (its activation storage type) and MN_INST_BWD_TYPES (the
-// backward storage combinations for it). Splitting the instances by storage
-// type lets the build compile them in parallel.
+// mn_instances.hpp -- definitions of the kernel launchers, included by the
+// mn_inst_*.hip files, each of which sets MN_INST_ST (its activation storage
+// type), MN_INST_KINDS (the kinds it instantiates, as X(kind) entries) and
+// MN_INST_BWD_TYPES (the backward storage combinations). Splitting the
+// instances by storage type and kind group lets the build compile them in
+// parallel.
 #pragma once
 
 #include "mn_kernels.hpp"
@@ -43,8 +44,14 @@ hipError_t launch_fwd(const FwdPlan& p, const FwdArgs& a, hipStream_t s)
         switch (p.v.id) { MN_FWD_RMS(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
     } else if constexpr (KIND == LN) {
         switch (p.v.id) { MN_FWD_LN(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
-    } else {
+    } else if constexpr (KIND == ADD) {
         switch (p.v.id) { MN_FWD_ADD(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
+    } else if constexpr (KIND == DYT) {
+        switch (p.v.id) { MN_FWD_DYT(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
+    } else if constexpr (KIND == POLY) {
+        switch (p.v.id) { MN_FWD_POLY(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
+    } else {
+        switch (p.v.id) { MN_FWD_MOD(MN_FWD_CASE) MN_FWD_GEN(MN_FWD_CASE) }
     }
     return hipErrorInvalidValue;
 }
@@ -57,8 +64,14 @@ hipError_t launch_bwd(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
         switch (p.v.id) { MN_BWD_RMS(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
     } else if constexpr (KIND == LN) {
         switch (p.v.id) { MN_BWD_LN(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
-    } else {
+    } else if constexpr (KIND == ADD) {
         switch (p.v.id) { MN_BWD_ADD(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
+    } else if constexpr (KIND == DYT) {
+        switch (p.v.id) { MN_BWD_DYT(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
+    } else if constexpr (KIND == POLY) {
+        switch (p.v.id) { MN_BWD_POLY(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
+    } else {
+        switch (p.v.id) { MN_BWD_MOD(MN_BWD_CASE) MN_BWD_GEN(MN_BWD_CASE) }
     }
     return hipErrorInvalidValue;
 }
@@ -66,15 +79,16 @@ hipError_t launch_bwd(const BwdPlan& p, const BwdArgs& a, hipStream_t s)
 #undef MN_FWD_CASE
 #undef MN_BWD_CASE
 
-template hipError_t launch_fwd<RMS, MN_INST_ST>(const FwdPlan&, const FwdArgs&, hipStream_t);
-template hipError_t launch_fwd<LN, MN_INST_ST>(const FwdPlan&, const FwdArgs&, hipStream_t);
-template hipError_t launch_fwd<ADD, MN_INST_ST>(const FwdPlan&, const FwdArgs&, hipStream_t);
+#define MN_INST_FWD(K) \
+    template hipError_t launch_fwd<K, MN_INST_ST>(const FwdPlan&, const FwdArgs&, hipStream_t);
+MN_INST_KINDS(MN_INST_FWD)
+#undef MN_INST_FWD
 
-#define MN_INST_BWD(S, C, O)                                                                  \
-    template hipError_t launch_bwd<RMS, S, C, O>(const BwdPlan&, const BwdArgs&, hipStream_t); \
-    template hipError_t launch_bwd<LN, S, C, O>(const BwdPlan&, const BwdArgs&, hipStream_t);  \
-    template hipError_t launch_bwd<ADD, S, C, O>(const BwdPlan&, const BwdArgs&, hipStream_t);
+#define MN_INST_BWD_KIND(K, S, C, O) \
+    template hipError_t launch_bwd<K, S, C, O>(const BwdPlan&, const BwdArgs&, hipStream_t);
+#define MN_INST_BWD(S, C, O) MN_INST_KINDS_BWD(MN_INST_BWD_KIND, S, C, O)
 MN_INST_BWD_TYPES(MN_INST_BWD)
 #undef MN_INST_BWD
+#undef MN_INST_BWD_KIND
 
 }  // namespace mn

@@ -7,7 +7,9 @@
 
 namespace mn {
 
-enum Kind : int { RMS = 0, LN = 1, ADD = 2 };
+// Norm kinds: the training pair (RMS, LN, ADD) and the other row-wise norms
+// (DYT: Dynamic Tanh, POLY: PolyNorm, MOD: Modulated RMSNorm).
+enum Kind : int { RMS = 0, LN = 1, ADD = 2, DYT = 3, POLY = 4, MOD = 5 };
 
 // Storage types; the values match mn_dtype in mn_norm.h.
 enum Stor : int { ST_F16 = 0, ST_BF16 = 1, ST_F32 = 2 };
@@ -15,18 +17,24 @@ enum Stor : int { ST_F16 = 0, ST_BF16 = 1, ST_F32 = 2 };
 inline int stor_bytes(int st) { return st == ST_F32 ? 4 : 2; }
 
 // Forward arguments. Pointers not used by a kind are null. Activations
-// (X, R, Y, H) share one storage type (a template parameter of the kernel);
-// gamma and beta share the parameter storage type `pdt`.
+// (X, R, Y, H, and MOD's scale and shift) share one storage type (a template
+// parameter of the kernel); gamma and beta share the parameter storage type
+// `pdt`.
 struct FwdArgs {
     const void* X;
     const void* R;           // ADD
-    const void* gamma;
-    const void* beta;        // LN
+    const void* gamma;       // all but POLY
+    const void* beta;        // LN, DYT
+    const float* alpha;      // DYT: the scalar alpha (device)
+    const float* poly;       // POLY: w1, w2, w3, b (device)
+    const void* scale;       // MOD: [B][D]
+    const void* shift;       // MOD: [B][D]
     void* Y;
     void* H;                 // ADD
     float* mean;             // LN
-    float* rstd;
+    float* rstd;             // [N] (POLY: [N][3])
     int64_t N;
+    int64_t S;               // MOD: rows per sample
     int32_t D;
     int32_t pdt;             // storage type of gamma / beta
     float eps;
@@ -37,29 +45,39 @@ struct FwdArgs {
 struct BwdArgs {
     const void* X;
     const void* R;           // ADD
-    const void* gamma;
+    const void* gamma;       // all but POLY
     const void* dY;
     const void* dH;          // ADD, may be null (zero cotangent)
     const float* mean;       // LN
-    const float* rstd;
+    const float* rstd;       // [N] (POLY: [N][3])
+    const float* alpha;      // DYT
+    const float* poly;       // POLY: w1, w2, w3, b
+    const void* scale;       // MOD: [B][D], activation storage type
     void* dX;
     float* part_g;           // [P][Dp] dgamma partials
-    float* part_b;           // [P][Dp] dbeta partials (LN)
+    float* part_b;           // [P][Dp] dbeta (LN, DYT) or dscale (MOD) partials
+    float* part_h;           // MOD: [P][Dp] dshift partials
+    float* part_a;           // DYT, POLY: [P][4] scalar partials
     int64_t N;
+    int64_t S;               // MOD: rows per sample
     int32_t D;
     int32_t Dp;              // partial row stride (D rounded up to 4)
     int32_t pdt;             // storage type of gamma
+    int32_t Pb;              // MOD: workgroups per sample (workgroup b serves sample b / Pb)
 };
 
-// Column-reduce (stage 2) arguments.
+// Column-reduce (stage 2) arguments: out_y[z * D + j] = sum over the P rows
+// p of part_y[(z * P + p) * Dp + j], for plane y = 0 (part_g -> dgamma) and
+// y = 1 (part_b -> dbeta, when part_b is not null) and group z < groups.
 struct ReduceArgs {
     const float* part_g;
-    const float* part_b;     // null unless LN
+    const float* part_b;     // null for a single plane
     float* dgamma;
     float* dbeta;
-    int64_t P;               // partial rows
+    int64_t P;               // partial rows per group
     int32_t D;
     int32_t Dp;
+    int32_t groups;
 };
 
 // Row-kernel variant: threads per row (T), elements per load (VEC, 8 or 1),
@@ -78,20 +96,24 @@ struct FwdPlan {
 struct BwdPlan {
     Variant v;
     int64_t P;               // workgroups == partial rows
+    int32_t Pb;              // MOD: workgroups per sample
     int32_t Dp;
     size_t shmem;            // dynamic LDS bytes of the block-level fold
 };
 
-// Partial-buffer geometry; depends only on (kind, N, D).
+// Partial-buffer geometry; depends only on (kind, N, D), and for MOD on the
+// sample count B.
 int64_t bwd_partial_rows(int kind, int64_t N, int32_t D);
+int32_t mod_blocks_per_sample(int64_t B, int64_t N);
+int bwd_vector_partials(int kind);
 int32_t partial_stride(int32_t D);
 
 FwdPlan plan_forward(int kind, int st, int64_t N, int32_t D, bool vec_ok);
-BwdPlan plan_backward(int kind, int st, int64_t N, int32_t D, bool vec_ok);
+BwdPlan plan_backward(int kind, int st, int64_t N, int32_t D, bool vec_ok, int64_t B = 1);
 
 hipError_t launch_forward(int kind, int st, const FwdPlan& p, const FwdArgs& a, hipStream_t s);
 // Backward storage combinations (activations st, cotangents ct, dX ot).
-bool backward_types_supported(int st, int ct, int ot);
+bool backward_types_supported(int kind, int st, int ct, int ot);
 hipError_t launch_backward_rows(int kind, int st, int ct, int ot, const BwdPlan& p,
                                 const BwdArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);

@@ -18,8 +18,10 @@ struct VariantRow {
 };
 
 #define MN_ROW(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) {{id, T, VEC, CPT, U, BLOCK}, MAXD},
-const VariantRow kFwdVec[3][8] = {{MN_FWD_RMS(MN_ROW)}, {MN_FWD_LN(MN_ROW)}, {MN_FWD_ADD(MN_ROW)}};
-const VariantRow kBwdVec[3][8] = {{MN_BWD_RMS(MN_ROW)}, {MN_BWD_LN(MN_ROW)}, {MN_BWD_ADD(MN_ROW)}};
+const VariantRow kFwdVec[6][8] = {{MN_FWD_RMS(MN_ROW)}, {MN_FWD_LN(MN_ROW)}, {MN_FWD_ADD(MN_ROW)},
+                                  {MN_FWD_DYT(MN_ROW)}, {MN_FWD_POLY(MN_ROW)}, {MN_FWD_MOD(MN_ROW)}};
+const VariantRow kBwdVec[6][8] = {{MN_BWD_RMS(MN_ROW)}, {MN_BWD_LN(MN_ROW)}, {MN_BWD_ADD(MN_ROW)},
+                                  {MN_BWD_DYT(MN_ROW)}, {MN_BWD_POLY(MN_ROW)}, {MN_BWD_MOD(MN_ROW)}};
 const VariantRow kFwdGen[] = {MN_FWD_GEN(MN_ROW)};
 const VariantRow kBwdGen[] = {MN_BWD_GEN(MN_ROW)};
 #undef MN_ROW
@@ -57,7 +59,11 @@ hipError_t launch_bwd_types(int st, int ct, int ot, const BwdPlan& p, const BwdA
 {
 #define MN_BWD_TYPE_CASE(S, C, O) \
     if (st == S && ct == C && ot == O) return launch_bwd<KIND, S, C, O>(p, a, s);
-    MN_BWD_TYPES(MN_BWD_TYPE_CASE)
+    if constexpr (KIND == RMS || KIND == LN || KIND == ADD) {
+        MN_BWD_TYPES(MN_BWD_TYPE_CASE)
+    } else {
+        MN_BWD_TYPES_EXT(MN_BWD_TYPE_CASE)
+    }
 #undef MN_BWD_TYPE_CASE
     return hipErrorInvalidValue;
 }
@@ -82,6 +88,27 @@ int64_t bwd_partial_rows(int kind, int64_t N, int32_t D)
     return N < bwd_blocks(kind, D) ? N : bwd_blocks(kind, D);
 }
 
+int32_t mod_blocks_per_sample(int64_t B, int64_t N)
+{
+    // 256 workgroups shared out over the samples (at least one each), never
+    // more per sample than it has rows
+    const int64_t S = N / B;
+    int64_t pb = B >= 256 ? 1 : 256 / B;
+    if (pb > S) pb = S;
+    return (int32_t)(pb < 1 ? 1 : pb);
+}
+
+int bwd_vector_partials(int kind)
+{
+    switch (kind) {
+    case LN:
+    case DYT: return 2;
+    case MOD: return 3;
+    case POLY: return 0;
+    default: return 1;
+    }
+}
+
 FwdPlan plan_forward(int kind, int st, int64_t N, int32_t D, bool vec_ok)
 {
     (void)st;
@@ -92,15 +119,16 @@ FwdPlan plan_forward(int kind, int st, int64_t N, int32_t D, bool vec_ok)
     return p;
 }
 
-BwdPlan plan_backward(int kind, int st, int64_t N, int32_t D, bool vec_ok)
+BwdPlan plan_backward(int kind, int st, int64_t N, int32_t D, bool vec_ok, int64_t B)
 {
     (void)st;
     BwdPlan p;
     p.v = vec_ok ? pick(kBwdVec[kind], D) : pick(kBwdGen, D);
-    p.P = bwd_partial_rows(kind, N, D);
+    p.Pb = (kind == MOD) ? mod_blocks_per_sample(B, N) : 0;
+    p.P = (kind == MOD) ? B * p.Pb : bwd_partial_rows(kind, N, D);
     p.Dp = partial_stride(D);
     const int rpb = p.v.BLOCK / p.v.T;
-    p.shmem = (rpb > 1) ? (size_t)D * sizeof(float) * (kind == LN ? 2 : 1) : 0;
+    p.shmem = (rpb > 1) ? (size_t)D * sizeof(float) * bwd_vector_partials(kind) : 0;
     return p;
 }
 
@@ -110,15 +138,22 @@ hipError_t launch_forward(int kind, int st, const FwdPlan& p, const FwdArgs& a, 
     case RMS: return launch_fwd_st<RMS>(st, p, a, s);
     case LN: return launch_fwd_st<LN>(st, p, a, s);
     case ADD: return launch_fwd_st<ADD>(st, p, a, s);
+    case DYT: return launch_fwd_st<DYT>(st, p, a, s);
+    case POLY: return launch_fwd_st<POLY>(st, p, a, s);
+    case MOD: return launch_fwd_st<MOD>(st, p, a, s);
     }
     return hipErrorInvalidValue;
 }
 
-bool backward_types_supported(int st, int ct, int ot)
+bool backward_types_supported(int kind, int st, int ct, int ot)
 {
 #define MN_BWD_TYPE_OK(S, C, O) \
     if (st == S && ct == C && ot == O) return true;
-    MN_BWD_TYPES(MN_BWD_TYPE_OK)
+    if (kind == RMS || kind == LN || kind == ADD) {
+        MN_BWD_TYPES(MN_BWD_TYPE_OK)
+    } else {
+        MN_BWD_TYPES_EXT(MN_BWD_TYPE_OK)
+    }
 #undef MN_BWD_TYPE_OK
     return false;
 }
@@ -130,13 +165,17 @@ hipError_t launch_backward_rows(int kind, int st, int ct, int ot, const BwdPlan&
     case RMS: return launch_bwd_types<RMS>(st, ct, ot, p, a, s);
     case LN: return launch_bwd_types<LN>(st, ct, ot, p, a, s);
     case ADD: return launch_bwd_types<ADD>(st, ct, ot, p, a, s);
+    case DYT: return launch_bwd_types<DYT>(st, ct, ot, p, a, s);
+    case POLY: return launch_bwd_types<POLY>(st, ct, ot, p, a, s);
+    case MOD: return launch_bwd_types<MOD>(st, ct, ot, p, a, s);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s)
 {
-    const dim3 grid((unsigned)ceil_div(a.Dp, 4 * kReduceCQ), a.part_b ? 2u : 1u);
+    const dim3 grid((unsigned)ceil_div(a.Dp, 4 * kReduceCQ), a.part_b ? 2u : 1u,
+                    (unsigned)(a.groups > 0 ? a.groups : 1));
     return launch(reduce_kernel<kReduceCQ>, grid, dim3(1024), 0, s, a);
 }
 

@@ -326,9 +326,12 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
     typedef typename Chunk<ST, VEC>::type HV;
     constexpr int RPB = BLOCK / T;
     constexpr int TILE = RPB * U;
+    // sums per row: none (DYT), three (POLY: sum of x^2, x^4, x^6), else one
+    constexpr int NS = (KIND == DYT) ? 0 : (KIND == POLY) ? 3 : 1;
+    constexpr int NSR = NS > 0 ? NS : 1;
     static_assert(BLOCK % T == 0, "block holds whole row groups");
     static_assert(PF == 0, "the forward runs one tile per workgroup: nothing to prefetch");
-    __shared__ float red[RedBuf<T, RPB, U>::size];
+    __shared__ float red[RedBuf<T, RPB, U * NSR>::size];
 
     const int tid = threadIdx.x;
     const int g = tid / T;
@@ -345,13 +348,21 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
         cval[k] = coff[k] < D;
     }
 
+    constexpr bool HAS_G = KIND != POLY;
+    constexpr bool HAS_B = KIND == LN || KIND == DYT;
     PRaw<VEC> graw[CPT], braw[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         if (cval[k]) {
-            load_param_raw<VEC>(a.gamma, a.pdt, coff[k], graw[k]);
-            if constexpr (KIND == LN) load_param_raw<VEC>(a.beta, a.pdt, coff[k], braw[k]);
+            if constexpr (HAS_G) load_param_raw<VEC>(a.gamma, a.pdt, coff[k], graw[k]);
+            if constexpr (HAS_B) load_param_raw<VEC>(a.beta, a.pdt, coff[k], braw[k]);
         }
+    }
+    float alpha = 0.0f, pw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (KIND == DYT) alpha = *a.alpha;
+    if constexpr (KIND == POLY) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pw[q] = a.poly[q];
     }
 
     struct Tile {
@@ -380,8 +391,8 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
     float gam[CPT][VEC], bet[CPT][VEC];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-        widen_param<VEC>(graw[k], a.pdt, cval[k], gam[k]);
-        if constexpr (KIND == LN) widen_param<VEC>(braw[k], a.pdt, cval[k], bet[k]);
+        if constexpr (HAS_G) widen_param<VEC>(graw[k], a.pdt, cval[k], gam[k]);
+        if constexpr (HAS_B) widen_param<VEC>(braw[k], a.pdt, cval[k], bet[k]);
     }
     {
         const int64_t base = begin;
@@ -393,32 +404,47 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
             rv[u] = row[u] < end;
         }
 
-        // First reduction: sum of squares (RMS, ADD) or plain sum (LN).
-        float s1[U];
+        // First reduction: sum of squares (RMS, ADD, MOD), plain sum (LN),
+        // sums of the second, fourth and sixth powers (POLY); none for DYT.
+        float s1[U * NSR];
+        if constexpr (NS > 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float acc = 0.0f;
+            for (int u = 0; u < U; ++u) {
+                float acc[NSR];
 #pragma unroll
-            for (int k = 0; k < CPT; ++k)
+                for (int q = 0; q < NSR; ++q) acc[q] = 0.0f;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    float v = cget<ST, VEC>(cur.x[u][k], e);
-                    if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
-                    if constexpr (KIND == LN) acc += v;
-                    else acc = __builtin_fmaf(v, v, acc);
-                }
-            s1[u] = acc;
-        }
-        row_sum<T, RPB, U>(s1, red, phase, g, l);
+                for (int k = 0; k < CPT; ++k)
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+                    for (int e = 0; e < VEC; ++e) {
+                        float v = cget<ST, VEC>(cur.x[u][k], e);
+                        if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
+                        if constexpr (KIND == LN) {
+                            acc[0] += v;
+                        } else if constexpr (KIND == POLY) {
+                            const float v2 = v * v;
+                            const float v3 = v2 * v;
+                            acc[0] = __builtin_fmaf(v, v, acc[0]);
+                            acc[1] = __builtin_fmaf(v2, v2, acc[1]);
+                            acc[2] = __builtin_fmaf(v3, v3, acc[2]);
+                        } else {
+                            acc[0] = __builtin_fmaf(v, v, acc[0]);
+                        }
+                    }
 #pragma unroll
-            for (int k = 0; k < CPT; ++k) {
-                launder(cur.x[u][k]);
-                if constexpr (KIND == ADD) launder(cur.r[u][k]);
+                for (int q = 0; q < NSR; ++q) s1[u * NSR + q] = acc[q];
             }
+            row_sum<T, RPB, U * NSR>(s1, red, phase, g, l);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < CPT; ++k) {
+                    launder(cur.x[u][k]);
+                    if constexpr (KIND == ADD) launder(cur.r[u][k]);
+                }
+        }
 
-        float mu[U], rs[U];
+        float mu[U], rs[U * NSR];
         if constexpr (KIND == LN) {
             // Second reduction: centred sum of squares from the registers.
             float s2[U];
@@ -438,34 +464,62 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
             row_sum<T, RPB, U>(s2, red, phase, g, l);
 #pragma unroll
             for (int u = 0; u < U; ++u) rs[u] = 1.0f / sqrtf(s2[u] / fD + a.eps);
-        } else {
+        } else if constexpr (NS > 0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 mu[u] = 0.0f;
-                rs[u] = 1.0f / sqrtf(s1[u] / fD + a.eps);
+#pragma unroll
+                for (int q = 0; q < NSR; ++q)
+                    rs[u * NSR + q] = 1.0f / sqrtf(s1[u * NSR + q] / fD + a.eps);
             }
         }
 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (l == 0 && rv[u]) {
-                a.rstd[row[u]] = rs[u];
-                if constexpr (KIND == LN) a.mean[row[u]] = mu[u];
+            if constexpr (NS > 0) {
+                if (l == 0 && rv[u]) {
+                    if constexpr (KIND == POLY) {
+#pragma unroll
+                        for (int q = 0; q < 3; ++q) a.rstd[row[u] * 3 + q] = rs[u * NSR + q];
+                    } else {
+                        a.rstd[row[u]] = rs[u];
+                    }
+                    if constexpr (KIND == LN) a.mean[row[u]] = mu[u];
+                }
             }
             const int64_t ro = row[u] * (int64_t)D;
+            const int64_t so = (KIND == MOD) ? (row[u] / a.S) * (int64_t)D : 0;
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 if (!(rv[u] && cval[k])) continue;
+                HV sc, sh;
+                if constexpr (KIND == MOD) {
+                    sc = sload<ST, VEC, 0>(a.scale, so + coff[k]);
+                    sh = sload<ST, VEC, 0>(a.shift, so + coff[k]);
+                }
                 HV y;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     float v = cget<ST, VEC>(cur.x[u][k], e);
                     if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                     float o;
-                    if constexpr (KIND == LN)
+                    if constexpr (KIND == LN) {
                         o = __builtin_fmaf((v - mu[u]) * rs[u], gam[k][e], bet[k][e]);
-                    else
+                    } else if constexpr (KIND == DYT) {
+                        o = __builtin_fmaf(gam[k][e], tanhf(alpha * v), bet[k][e]);
+                    } else if constexpr (KIND == POLY) {
+                        const float v2 = v * v;
+                        const float v3 = v2 * v;
+                        o = __builtin_fmaf(pw[0], v * rs[u * NSR],
+                                           __builtin_fmaf(pw[1], v2 * rs[u * NSR + 1],
+                                                          __builtin_fmaf(pw[2], v3 * rs[u * NSR + 2],
+                                                                         pw[3])));
+                    } else if constexpr (KIND == MOD) {
+                        o = __builtin_fmaf(v * rs[u] * gam[k][e], 1.0f + cget<ST, VEC>(sc, e),
+                                           cget<ST, VEC>(sh, e));
+                    } else {
                         o = v * rs[u] * gam[k][e];
+                    }
                     cset<ST, VEC>(y, e, o);
                 }
                 cstore<ST, VEC, NT>(a.Y, ro + coff[k], y);
@@ -483,7 +537,30 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
 // Backward stage 1: dX and per-workgroup parameter-gradient partials.
 // ---------------------------------------------------------------------------
 
-// Storage types: ST for X and R, CT for the cotangents dY and dH, OT for dX.
+// Sum of one value per lane over the whole workgroup in a fixed order: the
+// wave-level tree of group_sum, then the per-wave totals in wave order.
+// Every thread must call it (it has barriers); lane 0 of wave 0 gets the sum.
+template <int BLOCK>
+__device__ __forceinline__ float block_sum(float v, float* scratch)
+{
+    v = group_sum<64>(v);
+    if constexpr (BLOCK > 64) {
+        const int w = threadIdx.x >> 6;
+        __syncthreads();
+        if ((threadIdx.x & 63) == 0) scratch[w] = v;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float t = scratch[0];
+#pragma unroll
+            for (int ww = 1; ww < BLOCK / 64; ++ww) t += scratch[ww];
+            v = t;
+        }
+    }
+    return v;
+}
+
+// Storage types: ST for X and R (and MOD's scale), CT for the cotangents dY
+// and dH, OT for dX.
 template <int KIND, int ST, int CT, int OT, int T, int VEC, int CPT, int U, int BLOCK, int PF,
           int NT>
 __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
@@ -493,21 +570,43 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
     typedef typename Chunk<OT, VEC>::type OV;
     constexpr int RPB = BLOCK / T;
     constexpr int TILE = RPB * U;
-    constexpr int NR = (KIND == LN) ? 2 : 1;  // sums per row: c1 (and c2)
+    // sums per row: c1 (and c2 for LN; three for POLY; none for DYT)
+    constexpr int NR = (KIND == LN) ? 2 : (KIND == POLY) ? 3 : (KIND == DYT) ? 0 : 1;
+    constexpr int NRR = NR > 0 ? NR : 1;
+    // per-column partial arrays: dgamma (+ dbeta for LN and DYT, + dscale and
+    // dshift for MOD); POLY has only scalar parameters
+    constexpr int NV = (KIND == LN || KIND == DYT) ? 2 : (KIND == MOD) ? 3 : (KIND == POLY) ? 0 : 1;
+    // per-workgroup scalar partials: dalpha (DYT), dw1..dw3 and db (POLY)
+    constexpr int NSC = (KIND == DYT) ? 1 : (KIND == POLY) ? 4 : 0;
+    constexpr int NQ = (KIND == POLY) ? 3 : 1;  // saved rstd values per row
     static_assert(BLOCK % T == 0, "block holds whole row groups");
-    __shared__ float red[RedBuf<T, RPB, U * NR>::size];
-    extern __shared__ float fold[];           // [NR][D] when RPB > 1
+    __shared__ float red[RedBuf<T, RPB, U * NRR>::size];
+    __shared__ float wsum[BLOCK / 64 > 0 ? BLOCK / 64 : 1];
+    extern __shared__ float fold[];           // [NV][D] when RPB > 1
 
     const int tid = threadIdx.x;
     const int g = tid / T;
     const int l = tid % T;
     const int D = a.D;
     // Workgroup b owns tiles b, b + P, b + 2P, ... (P = gridDim.x): a fixed
-    // set of rows, so its dgamma partial is reproducible, while the P
-    // workgroups running together touch one contiguous band of rows.
-    const int64_t end = a.N;
-    const int64_t ntiles = (a.N + TILE - 1) / TILE;
-    const int64_t tstride = (int64_t)gridDim.x * TILE;
+    // set of rows, so its partials are reproducible, while the P workgroups
+    // running together touch one contiguous band of rows. For MOD the
+    // workgroups are split by sample: workgroup b serves sample b / Pb and
+    // owns the tiles b % Pb, b % Pb + Pb, ... of that sample's rows, so its
+    // dscale and dshift partials belong to one sample.
+    int64_t row0 = 0, end = a.N, first, stop, tstride;
+    if constexpr (KIND == MOD) {
+        const int64_t smp = blockIdx.x / a.Pb;
+        row0 = smp * a.S;
+        end = row0 + a.S;
+        first = row0 + (int64_t)(blockIdx.x % a.Pb) * TILE;
+        stop = row0 + (a.S + TILE - 1) / TILE * TILE;
+        tstride = (int64_t)a.Pb * TILE;
+    } else {
+        first = (int64_t)blockIdx.x * TILE;
+        stop = (a.N + TILE - 1) / TILE * TILE;  // uniform loop bound for the workgroup
+        tstride = (int64_t)gridDim.x * TILE;
+    }
 
     int coff[CPT];
     bool cval[CPT];
@@ -516,31 +615,50 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
         coff[k] = (k * T + l) * VEC;
         cval[k] = coff[k] < D;
     }
+    constexpr bool HAS_G = KIND != POLY;
     PRaw<VEC> graw[CPT];
+    HV scr[CPT];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k)
-        if (cval[k]) load_param_raw<VEC>(a.gamma, a.pdt, coff[k], graw[k]);
+    for (int k = 0; k < CPT; ++k) {
+        if constexpr (HAS_G)
+            if (cval[k]) load_param_raw<VEC>(a.gamma, a.pdt, coff[k], graw[k]);
+        if constexpr (KIND == MOD)
+            scr[k] = cval[k] ? sload<ST, VEC, 0>(a.scale, (row0 / a.S) * D + coff[k])
+                             : czero<ST, VEC>();
+    }
+    float alpha = 0.0f, pw[3] = {0.0f, 0.0f, 0.0f};
+    if constexpr (KIND == DYT) alpha = *a.alpha;
+    if constexpr (KIND == POLY) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) pw[q] = a.poly[q];
+    }
 
-    float accg[CPT][VEC], accb[CPT][VEC];
+    float accg[CPT][VEC], accb[CPT][VEC], acch[CPT][VEC], accs[NSC > 0 ? NSC : 1];
 #pragma unroll
     for (int k = 0; k < CPT; ++k)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             accg[k][e] = 0.0f;
             accb[k][e] = 0.0f;
+            acch[k][e] = 0.0f;
         }
+#pragma unroll
+    for (int q = 0; q < (NSC > 0 ? NSC : 1); ++q) accs[q] = 0.0f;
 
     struct Tile {
         HV x[U][CPT], r[U][CPT];
         CV dy[U][CPT];
-        float rs[U], mu[U];
+        float rs[U][NQ], mu[U];
     };
     auto load_tile = [&](Tile& t, int64_t base) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = base + u * RPB + g;
             const bool rok = row < end;
-            t.rs[u] = rok ? a.rstd[row] : 0.0f;
+            if constexpr (KIND != DYT) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) t.rs[u][q] = rok ? a.rstd[row * NQ + q] : 0.0f;
+            }
             t.mu[u] = (KIND == LN && rok) ? a.mean[row] : 0.0f;
             const int64_t ro = row * (int64_t)D;
 #pragma unroll
@@ -556,12 +674,23 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
     const float fD = (float)D;
     int phase = 0;
     Tile cur;
-    const int64_t first = (int64_t)blockIdx.x * TILE;
-    const int64_t stop = ntiles * TILE;  // uniform loop bound for the workgroup
     load_tile(cur, first);
-    float gam[CPT][VEC];
+    // gam: gamma; gef: the weight the row sees (MOD: gamma * (1 + scale) of
+    // this workgroup's sample, else gamma); scl: 1 + scale (MOD)
+    float gam[CPT][VEC], gef[CPT][VEC], scl[CPT][VEC];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) widen_param<VEC>(graw[k], a.pdt, cval[k], gam[k]);
+    for (int k = 0; k < CPT; ++k) {
+        if constexpr (HAS_G) widen_param<VEC>(graw[k], a.pdt, cval[k], gam[k]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if constexpr (KIND == MOD) {
+                scl[k][e] = 1.0f + cget<ST, VEC>(scr[k], e);
+                gef[k][e] = gam[k][e] * scl[k][e];
+            } else if constexpr (HAS_G) {
+                gef[k][e] = gam[k][e];
+            }
+        }
+    }
     for (int64_t base = first; base < stop; base += tstride) {
         Tile nxt;
         if constexpr (PF) {
@@ -569,42 +698,57 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
             load_tile(nxt, base + tstride);
         }
 
-        // c1 = sum(g * xhat), c2 = sum(g), g = dY * gamma
-        float c[U * NR];
+        // Row sums. RMS, ADD, MOD: c1 = sum(g * xhat) with g = dY * gamma
+        // (MOD: times 1 + scale); LN: also c2 = sum(g); POLY: sum(dY * n_p)
+        // for the three normalised powers n_p.
+        float c[U * NRR];
+        if constexpr (NR > 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float a1 = 0.0f, a2 = 0.0f;
+            for (int u = 0; u < U; ++u) {
+                float acc[NRR];
 #pragma unroll
-            for (int k = 0; k < CPT; ++k)
+                for (int q = 0; q < NRR; ++q) acc[q] = 0.0f;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    float v = cget<ST, VEC>(cur.x[u][k], e);
-                    if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
-                    const float xh = (v - cur.mu[u]) * cur.rs[u];
-                    const float gg = cget<CT, VEC>(cur.dy[u][k], e) * gam[k][e];
-                    a1 = __builtin_fmaf(gg, xh, a1);
-                    if constexpr (KIND == LN) a2 += gg;
-                }
-            c[u * NR] = a1;
-            if constexpr (KIND == LN) c[u * NR + 1] = a2;
-        }
-        row_sum<T, RPB, U * NR>(c, red, phase, g, l);
+                for (int k = 0; k < CPT; ++k)
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+                    for (int e = 0; e < VEC; ++e) {
+                        float v = cget<ST, VEC>(cur.x[u][k], e);
+                        if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
+                        const float dyv = cget<CT, VEC>(cur.dy[u][k], e);
+                        if constexpr (KIND == POLY) {
+                            const float v2 = v * v;
+                            acc[0] = __builtin_fmaf(dyv, v * cur.rs[u][0], acc[0]);
+                            acc[1] = __builtin_fmaf(dyv, v2 * cur.rs[u][1], acc[1]);
+                            acc[2] = __builtin_fmaf(dyv, v2 * v * cur.rs[u][2], acc[2]);
+                        } else {
+                            const float xh = (v - cur.mu[u]) * cur.rs[u][0];
+                            const float gg = dyv * gef[k][e];
+                            acc[0] = __builtin_fmaf(gg, xh, acc[0]);
+                            if constexpr (KIND == LN) acc[1] += gg;
+                        }
+                    }
 #pragma unroll
-            for (int k = 0; k < CPT; ++k) {
-                launder(cur.x[u][k]);
-                launder(cur.dy[u][k]);
-                if constexpr (KIND == ADD) launder(cur.r[u][k]);
+                for (int q = 0; q < NRR; ++q) c[u * NRR + q] = acc[q];
             }
+            row_sum<T, RPB, U * NRR>(c, red, phase, g, l);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < CPT; ++k) {
+                    launder(cur.x[u][k]);
+                    launder(cur.dy[u][k]);
+                    if constexpr (KIND == ADD) launder(cur.r[u][k]);
+                }
+        }
 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = base + u * RPB + g;
             const bool rok = row < end;
-            const float c1 = c[u * NR] / fD;
-            const float c2 = (KIND == LN) ? c[u * NR + 1] / fD : 0.0f;
-            const float rs = cur.rs[u];
+            const float c1 = (NR > 0) ? c[u * NRR] / fD : 0.0f;
+            const float c2 = (NR > 1) ? c[u * NRR + 1] / fD : 0.0f;
+            const float c3 = (NR > 2) ? c[u * NRR + 2] / fD : 0.0f;
+            const float rs = (KIND != DYT) ? cur.rs[u][0] : 0.0f;
             const float mu = cur.mu[u];
             const int64_t ro = row * (int64_t)D;
 #pragma unroll
@@ -619,17 +763,54 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                 for (int e = 0; e < VEC; ++e) {
                     float v = cget<ST, VEC>(cur.x[u][k], e);
                     if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
-                    const float xh = (v - mu) * rs;
                     const float dyv = cget<CT, VEC>(cur.dy[u][k], e);
-                    const float gg = dyv * gam[k][e];
                     float d;
-                    if constexpr (KIND == LN) d = rs * __builtin_fmaf(-xh, c1, gg - c2);
-                    else if constexpr (KIND == ADD)
-                        d = __builtin_fmaf(rs, __builtin_fmaf(-xh, c1, gg), cget<CT, VEC>(dh, e));
-                    else d = rs * __builtin_fmaf(-xh, c1, gg);
+                    if constexpr (KIND == DYT) {
+                        const float u = alpha * v;
+                        const float t = tanhf(u);
+                        // 1 - t^2 = 4 q (1 - q) with q = 1 / (exp(2|u|) + 1):
+                        // no cancellation where |t| is close to 1 (q -> 0
+                        // when the exponential overflows)
+                        const float q =
+                            __builtin_amdgcn_rcpf(__expf(2.0f * __builtin_fabsf(u)) + 1.0f);
+                        const float sd = 4.0f * q * (1.0f - q);
+                        const float gy = dyv * gam[k][e];
+                        d = gy * alpha * sd;
+                        accg[k][e] = __builtin_fmaf(dyv, t, accg[k][e]);
+                        accb[k][e] += dyv;
+                        accs[0] = __builtin_fmaf(gy * v, sd, accs[0]);
+                    } else if constexpr (KIND == POLY) {
+                        const float v2 = v * v;
+                        const float r1 = cur.rs[u][0], r2 = cur.rs[u][1], r3 = cur.rs[u][2];
+                        const float n1 = v * r1, n2 = v2 * r2, n3 = v2 * v * r3;
+                        const float t1 = pw[0] * r1 * __builtin_fmaf(-n1, c1, dyv);
+                        const float t2 = pw[1] * r2 * __builtin_fmaf(-n2, c2, dyv);
+                        const float t3 = pw[2] * r3 * __builtin_fmaf(-n3, c3, dyv);
+                        d = __builtin_fmaf(3.0f * v2, t3, __builtin_fmaf(2.0f * v, t2, t1));
+                        accs[0] = __builtin_fmaf(dyv, n1, accs[0]);
+                        accs[1] = __builtin_fmaf(dyv, n2, accs[1]);
+                        accs[2] = __builtin_fmaf(dyv, n3, accs[2]);
+                        accs[3] += dyv;
+                    } else {
+                        const float xh = (v - mu) * rs;
+                        const float gg = dyv * gef[k][e];
+                        if constexpr (KIND == LN) d = rs * __builtin_fmaf(-xh, c1, gg - c2);
+                        else if constexpr (KIND == ADD)
+                            d = __builtin_fmaf(rs, __builtin_fmaf(-xh, c1, gg), cget<CT, VEC>(dh, e));
+                        else d = rs * __builtin_fmaf(-xh, c1, gg);
+                        if constexpr (KIND == MOD) {
+                            // dgamma takes dY * xhat * (1 + scale), dscale
+                            // dY * xhat * gamma, dshift dY
+                            const float dx = dyv * xh;
+                            accg[k][e] = __builtin_fmaf(dx, scl[k][e], accg[k][e]);
+                            accb[k][e] = __builtin_fmaf(dx, gam[k][e], accb[k][e]);
+                            acch[k][e] += dyv;
+                        } else {
+                            accg[k][e] = __builtin_fmaf(dyv, xh, accg[k][e]);
+                            if constexpr (KIND == LN) accb[k][e] += dyv;
+                        }
+                    }
                     cset<OT, VEC>(o, e, d);
-                    accg[k][e] = __builtin_fmaf(dyv, xh, accg[k][e]);
-                    if constexpr (KIND == LN) accb[k][e] += dyv;
                 }
                 if (ok) cstore<OT, VEC, NT>(a.dX, ro + coff[k], o);
             }
@@ -639,45 +820,60 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
     }
 
     // Fold the row groups of this workgroup in group order, then write the
-    // workgroup's partial row.
-    float* pg = a.part_g + (int64_t)blockIdx.x * a.Dp;
-    float* pb = (KIND == LN) ? a.part_b + (int64_t)blockIdx.x * a.Dp : nullptr;
-    if constexpr (RPB == 1) {
+    // workgroup's partial rows.
+    if constexpr (NV > 0) {
+        float* pv[3] = {a.part_g + (int64_t)blockIdx.x * a.Dp,
+                        NV > 1 ? a.part_b + (int64_t)blockIdx.x * a.Dp : nullptr,
+                        NV > 2 ? a.part_h + (int64_t)blockIdx.x * a.Dp : nullptr};
+        if constexpr (RPB == 1) {
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            if (!cval[k]) continue;
+            for (int k = 0; k < CPT; ++k) {
+                if (!cval[k]) continue;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                pg[coff[k] + e] = accg[k][e];
-                if constexpr (KIND == LN) pb[coff[k] + e] = accb[k][e];
-            }
-        }
-    } else {
-        for (int gg = 0; gg < RPB; ++gg) {
-            if (g == gg) {
-#pragma unroll
-                for (int k = 0; k < CPT; ++k) {
-                    if (!cval[k]) continue;
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        const int j = coff[k] + e;
-                        fold[j] = (gg == 0) ? accg[k][e] : fold[j] + accg[k][e];
-                        if constexpr (KIND == LN)
-                            fold[D + j] = (gg == 0) ? accb[k][e] : fold[D + j] + accb[k][e];
-                    }
+                for (int e = 0; e < VEC; ++e) {
+                    pv[0][coff[k] + e] = accg[k][e];
+                    if constexpr (NV > 1) pv[1][coff[k] + e] = accb[k][e];
+                    if constexpr (NV > 2) pv[2][coff[k] + e] = acch[k][e];
                 }
             }
-            __syncthreads();
+        } else {
+            for (int gg = 0; gg < RPB; ++gg) {
+                if (g == gg) {
+#pragma unroll
+                    for (int k = 0; k < CPT; ++k) {
+                        if (!cval[k]) continue;
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) {
+                            const int j = coff[k] + e;
+                            fold[j] = (gg == 0) ? accg[k][e] : fold[j] + accg[k][e];
+                            if constexpr (NV > 1)
+                                fold[D + j] = (gg == 0) ? accb[k][e] : fold[D + j] + accb[k][e];
+                            if constexpr (NV > 2)
+                                fold[2 * D + j] = (gg == 0) ? acch[k][e] : fold[2 * D + j] + acch[k][e];
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+            for (int j = tid; j < D; j += BLOCK) {
+                pv[0][j] = fold[j];
+                if constexpr (NV > 1) pv[1][j] = fold[D + j];
+                if constexpr (NV > 2) pv[2][j] = fold[2 * D + j];
+            }
         }
-        for (int j = tid; j < D; j += BLOCK) {
-            pg[j] = fold[j];
-            if constexpr (KIND == LN) pb[j] = fold[D + j];
+    }
+    if constexpr (NSC > 0) {
+#pragma unroll
+        for (int q = 0; q < NSC; ++q) {
+            const float t = block_sum<BLOCK>(accs[q], wsum);
+            if (tid == 0) a.part_a[(int64_t)blockIdx.x * 4 + q] = t;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Backward stage 2: out[j] = sum over the P partial rows of partial[p][j].
+// Backward stage 2: out[j] = sum over the P partial rows of partial[p][j]
+// (per group z of P rows when there are several groups).
 // A block covers 4*CQ columns (one float4 per thread); its SEG = 1024/CQ
 // thread rows each sum one contiguous segment of the partial rows in
 // ascending order, then the SEG segment sums are combined by a fixed
@@ -691,8 +887,9 @@ __global__ void __launch_bounds__(1024) reduce_kernel(const ReduceArgs a)
     constexpr int SEG = 1024 / CQ;
     static_assert((SEG & (SEG - 1)) == 0, "segment count is a power of two");
     __shared__ f4 seg_sum[SEG][CQ];
-    const float* part = (blockIdx.y == 0) ? a.part_g : a.part_b;
-    float* out = (blockIdx.y == 0) ? a.dgamma : a.dbeta;
+    // group z: rows z*P .. z*P + P - 1 of the plane, into out[z*D ...]
+    const float* part = ((blockIdx.y == 0) ? a.part_g : a.part_b) + (int64_t)blockIdx.z * a.P * a.Dp;
+    float* out = ((blockIdx.y == 0) ? a.dgamma : a.dbeta) + (int64_t)blockIdx.z * a.D;
     const int q = threadIdx.x % CQ;
     const int s = threadIdx.x / CQ;
     const int c0 = (blockIdx.x * CQ + q) * 4;

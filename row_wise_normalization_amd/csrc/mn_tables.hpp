@@ -47,6 +47,11 @@ namespace mn {
     X(6, 256, 8, 2, 2, 256, 0, 1, 4096)      \
     X(7, 1024, 8, 1, 1, 1024, 0, 1, 8192)
 #define MN_FWD_ADD(X) MN_FWD_RMS(X)
+// the other norms: Dynamic Tanh and Modulated RMSNorm take the RMSNorm
+// shapes, PolyNorm (three sums per row) the LayerNorm ones
+#define MN_FWD_DYT(X) MN_FWD_RMS(X)
+#define MN_FWD_POLY(X) MN_FWD_LN(X)
+#define MN_FWD_MOD(X) MN_FWD_RMS(X)
 #define MN_FWD_GEN(X)                        \
     X(8, 64, 1, 16, 1, 256, 0, 1, 1024)      \
     X(9, 256, 1, 16, 1, 256, 0, 1, 4096)     \
@@ -71,6 +76,21 @@ namespace mn {
     X(6, 256, 8, 2, 2, 512, 1, 3, 4096)      \
     X(7, 512, 8, 2, 1, 512, 1, 3, 8192)
 #define MN_BWD_ADD(X) MN_BWD_RMS(X)
+// The other norms keep two or three per-column accumulators, or three row
+// sums, and (DYT) an inlined tanh per element: one row per group per step
+// keeps them within 128 VGPRs without spilling.
+#define MN_BWD_EXT(X)                        \
+    X(0, 8, 8, 1, 2, 256, 1, 3, 64)          \
+    X(1, 16, 8, 1, 2, 256, 1, 3, 128)        \
+    X(2, 32, 8, 1, 2, 256, 1, 3, 256)        \
+    X(3, 64, 8, 1, 1, 256, 1, 3, 512)        \
+    X(4, 128, 8, 1, 1, 512, 1, 3, 1024)      \
+    X(5, 256, 8, 1, 1, 512, 1, 3, 2048)      \
+    X(6, 512, 8, 1, 1, 512, 1, 3, 4096)      \
+    X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
+#define MN_BWD_DYT(X) MN_BWD_EXT(X)
+#define MN_BWD_POLY(X) MN_BWD_EXT(X)
+#define MN_BWD_MOD(X) MN_BWD_EXT(X)
 #define MN_BWD_GEN(X)                        \
     X(8, 64, 1, 16, 1, 256, 1, 1, 1024)      \
     X(9, 256, 1, 16, 1, 256, 1, 1, 4096)     \
@@ -90,6 +110,14 @@ namespace mn {
     X(ST_F32, ST_F32, ST_F32) X(ST_F32, ST_F16, ST_F32) X(ST_F32, ST_BF16, ST_F32)
 #define MN_BWD_TYPES(X) MN_BWD_TYPES_F16(X) MN_BWD_TYPES_BF16(X) MN_BWD_TYPES_F32(X)
 
+// The other norms (DYT, POLY, MOD): cotangents in the activation type, dX in
+// the activation type or binary32.
+#define MN_BWD_TYPES_EXT_F16(X) X(ST_F16, ST_F16, ST_F16) X(ST_F16, ST_F16, ST_F32)
+#define MN_BWD_TYPES_EXT_BF16(X) X(ST_BF16, ST_BF16, ST_BF16) X(ST_BF16, ST_BF16, ST_F32)
+#define MN_BWD_TYPES_EXT_F32(X) X(ST_F32, ST_F32, ST_F32)
+#define MN_BWD_TYPES_EXT(X) \
+    MN_BWD_TYPES_EXT_F16(X) MN_BWD_TYPES_EXT_BF16(X) MN_BWD_TYPES_EXT_F32(X)
+
 // binary32 storage keeps 16-byte chunks: 4 elements per chunk and twice the
 // chunks per lane of the 16-bit shapes, so the row coverage T*CPT*VEC and
 // the bytes in flight per lane are unchanged.
@@ -97,7 +125,8 @@ constexpr int st_vec(int st, int vec) { return (st == ST_F32 && vec == 8) ? 4 : 
 constexpr int st_cpt(int st, int vec, int cpt) { return (st == ST_F32 && vec == 8) ? 2 * cpt : cpt; }
 
 // Launch one planned forward / backward-stage-1 kernel; defined and
-// explicitly instantiated per activation storage type in mn_inst_*.hip.
+// explicitly instantiated per activation storage type and kind group in
+// mn_inst_*.hip.
 template <int KIND, int ST>
 hipError_t launch_fwd(const FwdPlan& p, const FwdArgs& a, hipStream_t s);
 template <int KIND, int ST, int CT, int OT>

@@ -172,7 +172,62 @@ def test_workspace_bytes():
             assert b > 0 and b % 16 == 0
             # at most 256 partial rows of round_up(D, 4) floats (two arrays for LayerNorm)
             assert b <= 256 * ((D + 3) // 4 * 4) * 4 * (2 if kind == mn.MN_LAYERNORM else 1)
-    assert mn.workspace_bytes(3, 16, 64) == 0
+    assert mn.workspace_bytes(6, 16, 64) == 0
+    # the other norms: Dynamic Tanh keeps two partial arrays plus scalars,
+    # PolyNorm only scalars, the Modulated RMSNorm sizes by its sample count
+    for N, D in ((1, 1), (17, 257), (16384, 4096)):
+        P = min(N, 256)
+        Dp = (D + 3) // 4 * 4
+        assert mn.workspace_bytes(mn.MN_DYT, N, D) == 2 * P * Dp * 4 + P * 16
+        assert mn.workspace_bytes(mn.MN_POLYNORM, N, D) == P * 16
+    assert mn.workspace_bytes(mn.MN_MOD_RMSNORM, 16, 64) == 0
+    assert mn.mod_rmsnorm_workspace_bytes(4, 16, 64) == 4 * 4 * 64 * 4 * 3  # 4 per sample (S = 4)
+    assert mn.mod_rmsnorm_workspace_bytes(8, 8192, 1024) == 8 * 32 * 1024 * 4 * 3
+    assert mn.mod_rmsnorm_workspace_bytes(3, 16, 64) == 0      # 3 does not divide 16
+    assert mn.mod_rmsnorm_workspace_bytes(0, 16, 64) == 0
+    assert mn.mod_rmsnorm_workspace_bytes(4097, 4097, 64) == 0
+
+
+def test_other_norms_validation():
+    L = mn.lib()
+    f = ctypes.c_float(1e-5)
+    F16, BF16, F32 = mn.MN_F16, mn.MN_BF16, mn.MN_F32
+    N, D = 16, 64
+    W = P(0xE0000000)
+    a_ = P(0x30000000)
+    # Dynamic Tanh: no epsilon; alpha, gamma, beta required
+    assert L.mn_dyt_forward_ex(A, NULL, B, C, Dp, N, D, F16, F16, S) == 1
+    assert L.mn_dyt_forward_ex(A, a_, B, NULL, Dp, N, D, F16, F16, S) == 1
+    assert L.mn_dyt_forward_ex(A, a_, B, C, A, N, D, F16, F16, S) == 4          # Y is X
+    assert L.mn_dyt_forward_ex(A, a_, B, C, Dp, N, D, F16, 5, S) == 7
+    ws = mn.workspace_bytes(mn.MN_DYT, N, D)
+    dyt_b = lambda act, dxt, ws=ws, da=G: L.mn_dyt_backward_ex(
+        A, a_, B, C, Dp, da, E, F, N, D, act, F16, dxt, W, ws, S)
+    assert dyt_b(F16, F16, da=NULL) == 1
+    assert dyt_b(F16, BF16) == 7                     # dX must be act or binary32
+    assert dyt_b(F32, F16) == 7
+    assert dyt_b(F16, F32, ws=ws - 1) == 5
+    assert dyt_b(BF16, BF16, ws=0) == 5
+    assert dyt_b(F16, F16, da=E) == 4                # dalpha inside dgamma
+    # PolyNorm: params and rstd required; eps checked
+    assert L.mn_polynorm_forward_ex(A, NULL, B, C, N, D, f, F16, S) == 1
+    assert L.mn_polynorm_forward_ex(A, a_, B, C, N, D, ctypes.c_float(0.0), F16, S) == 3
+    assert L.mn_polynorm_forward_ex(A, a_, B, P(0x20000000 + N * D * 2 - 4), N, D, f, F16,
+                                    S) == 4          # rstd [N][3] overlaps Y
+    wsp = mn.workspace_bytes(mn.MN_POLYNORM, N, D)
+    assert L.mn_polynorm_backward_ex(A, a_, C, Dp, E, NULL, N, D, F16, F16, W, wsp, S) == 1
+    assert L.mn_polynorm_backward_ex(A, a_, C, Dp, E, F, N, D, F16, F16, W, wsp - 1, S) == 5
+    # Modulated RMSNorm: B must divide N
+    assert L.mn_mod_rmsnorm_forward_ex(A, B, C, NULL, Dp, E, 4, N, D, f, F16, F16, S) == 1
+    assert L.mn_mod_rmsnorm_forward_ex(A, B, C, G, Dp, E, 3, N, D, f, F16, F16, S) == 2
+    assert L.mn_mod_rmsnorm_forward_ex(A, B, C, G, Dp, E, 0, N, D, f, F16, F16, S) == 2
+    wsm = mn.mod_rmsnorm_workspace_bytes(4, N, D)
+    mod_b = lambda **k: L.mn_mod_rmsnorm_backward_ex(
+        A, B, C, Dp, E, F, G, P(0x50000000), P(0x58000000), k.get("B", 4), N, D, F16, F16,
+        k.get("dxt", F16), W, k.get("ws", wsm), S)
+    assert mod_b(B=5) == 2
+    assert mod_b(ws=wsm - 16) == 5
+    assert mod_b(dxt=BF16) == 7
 
 
 def test_product_and_oracle_are_independent():

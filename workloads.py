@@ -22,6 +22,10 @@ Recipe (fixed, so that every run sees the same bits):
   workloads are fp16 throughout; tests of the other storage types pass
   ``act`` (X, R), ``cot`` (dY, dH) and ``param`` (gamma, beta) to the
   generators.
+* The Modulated RMSNorm's scale and shift are [B, D] tensors drawn like an
+  [N, D] one with B rows, in the activation storage type. The scalar
+  parameters (Dynamic Tanh's alpha, PolyNorm's weights and bias) are fixed
+  constants of the workload, not drawn.
 * The Llama-shape RMSNorm workload marks 1 % of its 4096 channels as outliers:
   41 channels drawn without replacement from ``default_rng(1)`` and sorted;
   those X columns are multiplied by 20 before rounding.
@@ -51,12 +55,13 @@ class TensorSpec:
     per_row: bool          # True: shape [N, D]; False: shape [D]
     loc: float = 0.0
     scale: float = 1.0
+    per_sample: bool = False   # shape [B, D] (the Modulated RMSNorm's scale and shift)
 
 
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str              # "rms", "ln" or "add"
+    kind: str              # "rms", "ln", "add", "dyt", "poly" or "mod"
     N: int
     D: int
     eps: float
@@ -65,6 +70,8 @@ class Workload:
     outlier_gain: float = 1.0
     outlier_seed: int = 1
     note: str = ""
+    B: int = 1             # "mod": samples (N / B rows each)
+    scalars: Tuple[float, ...] = ()   # "dyt": (alpha,); "poly": (w1, w2, w3, b)
 
     def outlier_channels(self) -> np.ndarray:
         if self.outlier_frac <= 0.0:
@@ -74,7 +81,8 @@ class Workload:
         return np.sort(rng.choice(self.D, k, replace=False))
 
 
-def _spec(kind: str, x=(0.0, 1.0), dy=(0.0, 1.0), r=(0.0, 2.0), dh=(0.0, 0.01)):
+def _spec(kind: str, x=(0.0, 1.0), dy=(0.0, 1.0), r=(0.0, 2.0), dh=(0.0, 0.01),
+          mod=(0.0, 0.1)):
     """Tensor list in draw order for one kind of norm."""
     X = TensorSpec("X", True, *x)
     G = TensorSpec("gamma", False, 1.0, 0.1)
@@ -82,11 +90,23 @@ def _spec(kind: str, x=(0.0, 1.0), dy=(0.0, 1.0), r=(0.0, 2.0), dh=(0.0, 0.01)):
     DY = TensorSpec("dY", True, *dy)
     if kind == "rms":
         return (X, G, DY)
-    if kind == "ln":
+    if kind in ("ln", "dyt"):
         return (X, G, B, DY)
     if kind == "add":
         return (X, TensorSpec("R", True, *r), G, DY, TensorSpec("dH", True, *dh))
+    if kind == "poly":
+        return (X, DY)
+    if kind == "mod":
+        return (X, G, TensorSpec("scale", False, *mod, per_sample=True),
+                TensorSpec("shift", False, *mod, per_sample=True), DY)
     raise ValueError(kind)
+
+
+# Fixed scalar parameters of the other norms: Dynamic Tanh's alpha (the
+# initial value its paper uses), and PolyNorm's weights near their usual
+# initial 1/3 with a small bias.
+DYT_ALPHA = (0.5,)
+POLY_PARAMS = (0.35, 0.3, 0.25, 0.05)
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -106,6 +126,13 @@ WORKLOADS: Dict[str, Workload] = {
                  note="per-head QK-norm, B=8 x H=32 x S=4096 rows of 128"),
         Workload("ln_16384x4096", "ln", 16384, 4096, 1e-5, _spec("ln", x=(0.5, 1.0)),
                  note="supplemental LayerNorm at the Llama shape, offset-mean distributions"),
+        Workload("dyt_16384x4096", "dyt", 16384, 4096, 0.0, _spec("dyt"), scalars=DYT_ALPHA,
+                 note="Dynamic Tanh in place of the norm at the Llama shape"),
+        Workload("poly_16384x4096", "poly", 16384, 4096, 1e-5, _spec("poly"),
+                 scalars=POLY_PARAMS, note="PolyNorm on 16384 tokens of width 4096"),
+        Workload("mod_rms_16384x3072", "mod", 16384, 3072, 1e-6, _spec("mod"), B=8,
+                 note="Modulated RMSNorm: 8 samples x 2048 tokens of width 3072 (a "
+                      "conditioned-transformer block)"),
     )
 }
 
@@ -179,7 +206,10 @@ def generate(w: Workload, seed: int = 0, N: Optional[int] = None, act: str = "f1
     outliers = w.outlier_channels()
     out: Dict[str, np.ndarray] = {}
     for t, spec in enumerate(w.tensors):
-        if spec.per_row:
+        if spec.per_sample:
+            a = np.empty((w.B, w.D), dtype=STORAGE[act])
+            _fill_rows(seed, t, a, spec, np.zeros(0, np.int64), 1.0)
+        elif spec.per_row:
             a = np.empty((n, w.D), dtype=STORAGE[cot if spec.name in ("dY", "dH") else act])
             _fill_rows(seed, t, a, spec, outliers if spec.name == "X" else np.zeros(0, np.int64),
                        w.outlier_gain)
@@ -192,12 +222,13 @@ def generate(w: Workload, seed: int = 0, N: Optional[int] = None, act: str = "f1
 
 def random_case(kind: str, N: int, D: int, seed: int, x_loc: float = 0.0, x_scale: float = 1.0,
                 dy_scale: float = 1.0, r_scale: float = 2.0, dh_scale: float = 0.5,
-                act: str = "f16", param: Optional[str] = None, cot: Optional[str] = None
-                ) -> Dict[str, np.ndarray]:
-    """Inputs for an arbitrary (kind, N, D) test case with the default recipe."""
+                act: str = "f16", param: Optional[str] = None, cot: Optional[str] = None,
+                B: int = 1, mod_scale: float = 0.1) -> Dict[str, np.ndarray]:
+    """Inputs for an arbitrary (kind, N, D) test case with the default recipe
+    (B samples for "mod"; the scalar parameters are not drawn)."""
     w = Workload(f"case_{kind}_{N}x{D}", kind, N, D, 1e-5,
                  _spec(kind, x=(x_loc, x_scale), dy=(0.0, dy_scale), r=(0.0, r_scale),
-                       dh=(0.0, dh_scale)))
+                       dh=(0.0, dh_scale), mod=(0.0, mod_scale)), B=B)
     return generate(w, seed, act=act, param=param, cot=cot)
 
 
