@@ -40,7 +40,7 @@ SIZE = {"f16": 2, "bf16": 2, "f32": 4}
 
 
 def alg_bytes(kind: str, N: int, D: int, act: str = "f16", param: str = "f16",
-              cot: str = "f16", dxt: str = "f16"):
+              cot: str = "f16", dxt: str = "f16", B: int = 1):
     """Algorithmic bytes (each tensor read or written once) of the forward and
     the backward (row kernel and column reduce together): activations X, R,
     Y, H of `act`, gamma/beta of `param`, cotangents dY, dH of `cot`, dX of
@@ -53,6 +53,15 @@ def alg_bytes(kind: str, N: int, D: int, act: str = "f16", param: str = "f16",
     elif kind == "ln":
         fwd = 2 * a * nd + 2 * p * D + 8 * N                  # + beta, mean
         bwd = (a + c + o) * nd + (p + 8) * D + 8 * N          # + mean, dbeta
+    elif kind == "dyt":
+        fwd = 2 * a * nd + 2 * p * D + 4                      # X, gamma, beta, alpha -> Y
+        bwd = (a + c + o) * nd + (p + 8) * D + 8              # -> dX, dgamma, dbeta, dalpha
+    elif kind == "poly":
+        fwd = 2 * a * nd + 16 + 12 * N                        # X, params -> Y, rstd [N][3]
+        bwd = (a + c + o) * nd + 32 + 12 * N                  # + rstd -> dX, dparams
+    elif kind == "mod":
+        fwd = 2 * a * nd + p * D + 2 * a * B * D + 4 * N      # + scale, shift [B][D]
+        bwd = (a + c + o) * nd + (p + 4) * D + (a + 8) * B * D + 4 * N
     else:
         fwd = 4 * a * nd + p * D + 4 * N                      # X, R -> H, Y
         bwd = (2 * a + 2 * c + o) * nd + (p + 4) * D + 4 * N  # X, R, dY, dH -> dX
@@ -140,13 +149,22 @@ def cpu_baseline(w, d, budget_s: float, types=("f16",) * 4):
     time budget is spent (at least once)."""
     import oracle
 
-    fwd_b, bwd_b = alg_bytes(w.kind, w.N, w.D, *types)
+    fwd_b, bwd_b = alg_bytes(w.kind, w.N, w.D, *types, B=w.B)
     rows = w.N
-    X, g, dY = d["X"], d["gamma"], d["dY"]
+    X, g, dY = d["X"], d.get("gamma"), d["dY"]
     t0 = time.perf_counter()
     reps = 0
     while True:
-        if w.kind == "rms":
+        if w.kind == "dyt":
+            oracle.dyt_forward(X, w.scalars[0], g, d["beta"])
+            oracle.dyt_backward(X, w.scalars[0], g, dY)
+        elif w.kind == "poly":
+            oracle.polynorm_forward(X, w.scalars[:3], w.scalars[3], w.eps)
+            oracle.polynorm_backward(X, w.scalars[:3], dY, w.eps)
+        elif w.kind == "mod":
+            oracle.modrms_forward(X, g, d["scale"], d["shift"], w.eps)
+            oracle.modrms_backward(X, g, d["scale"], dY, w.eps)
+        elif w.kind == "rms":
             oracle.rmsnorm_forward(X, g, w.eps)
             oracle.rmsnorm_backward(X, g, dY, w.eps)
         elif w.kind == "ln":
@@ -241,6 +259,123 @@ def pages_context(torch, mn):
     }), flush=True)
 
 
+NORM_NAMES = {"rms": "RMSNorm", "ln": "LayerNorm", "add": "fused add + RMSNorm",
+              "dyt": "Dynamic Tanh", "poly": "PolyNorm", "mod": "Modulated RMSNorm"}
+
+
+def bench_other(args, w, torch, mn, act, param, dxt):
+    """Dynamic Tanh, PolyNorm or Modulated RMSNorm: one step is the forward of
+    one batch and the whole backward (row kernel and parameter reduction) of
+    another, with rotating buffer sets as for the training pair; events
+    bracket the forward and the backward call separately."""
+    N, D, kind = w.N, w.D, w.kind
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+    print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
+    d = workloads.generate(w, act=act, param=param)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def upload(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    up = {k: upload(v) for k, v in d.items()}
+    scal = torch.tensor(np.asarray(w.scalars, np.float32), device=dev)
+    S = max(2, args.sets)
+    kcode = {"dyt": mn.MN_DYT, "poly": mn.MN_POLYNORM, "mod": mn.MN_MOD_RMSNORM}[kind]
+    sets = []
+    for s in range(S):
+        b = {"X": up["X"] if s == 0 else up["X"].clone(),
+             "dY": up["dY"] if s == 0 else up["dY"].clone(),
+             "Y": torch.empty(N, D, dtype=tdt[act], device=dev),
+             "dX": torch.empty(N, D, dtype=tdt[dxt], device=dev),
+             "ws": mn.new_workspace(kcode, N, D, dev, B=w.B)}
+        if kind == "dyt":
+            b.update(da=torch.empty(1, dtype=torch.float32, device=dev),
+                     dg=torch.empty(D, dtype=torch.float32, device=dev),
+                     db=torch.empty(D, dtype=torch.float32, device=dev))
+        elif kind == "poly":
+            b.update(rstd=torch.empty(N, 3, dtype=torch.float32, device=dev),
+                     dp=torch.empty(4, dtype=torch.float32, device=dev))
+        else:
+            b.update(rstd=torch.empty(N, dtype=torch.float32, device=dev),
+                     dg=torch.empty(D, dtype=torch.float32, device=dev),
+                     dsc=torch.empty(w.B, D, dtype=torch.float32, device=dev),
+                     dsh=torch.empty(w.B, D, dtype=torch.float32, device=dev))
+        sets.append(b)
+
+    def fwd(b):
+        if kind == "dyt":
+            mn.mn_dyt_forward_ex(b["X"], scal, up["gamma"], up["beta"], b["Y"], stream)
+        elif kind == "poly":
+            mn.mn_polynorm_forward_ex(b["X"], scal, b["Y"], b["rstd"], w.eps, stream)
+        else:
+            mn.mn_mod_rmsnorm_forward_ex(b["X"], up["gamma"], up["scale"], up["shift"], b["Y"],
+                                         b["rstd"], w.eps, stream)
+
+    def bwd(b):
+        if kind == "dyt":
+            mn.mn_dyt_backward_ex(b["X"], scal, up["gamma"], b["dY"], b["dX"], b["da"], b["dg"],
+                                  b["db"], b["ws"], stream)
+        elif kind == "poly":
+            mn.mn_polynorm_backward_ex(b["X"], scal, b["rstd"], b["dY"], b["dX"], b["dp"],
+                                       b["ws"], stream)
+        else:
+            mn.mn_mod_rmsnorm_backward_ex(b["X"], up["gamma"], up["scale"], b["rstd"], b["dY"],
+                                          b["dX"], b["dg"], b["dsc"], b["dsh"], b["ws"], stream)
+
+    K, W = args.steps, args.warmup
+    fwd_b, bwd_b = alg_bytes(kind, N, D, act, param, act, dxt, B=w.B)
+    for b in sets:
+        fwd(b)
+    for k in range(W):
+        fwd(sets[k % S]); bwd(sets[(k - 1) % S])
+    torch.cuda.synchronize()
+    ev = [[HipEvent() for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for k in range(K):
+        e = ev[k]
+        e[0].record(stream); fwd(sets[(W + k) % S]); e[1].record(stream)
+        bwd(sets[(W + k - 1) % S]); e[2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    fwd_ms = float(np.mean([e[0].elapsed_ms(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_ms(e[2]) for e in ev]))
+    gbs = (fwd_b + bwd_b) / (ms_step * 1e-3) / 1e9
+    achieved = bwd_b / (bwd_ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_budget > 0:
+        print(f"[bench] cpu baseline (oracle, {args.cpu_budget:.0f} s budget)", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(w, d, args.cpu_budget, (act, param, act, dxt))
+    line = {
+        "metric": f"achieved HBM GB/s (% of peak) + rows/s for norm fwd+bwd, "
+                  f"{NORM_NAMES[kind]} {N}x{D}",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "N": N, "D": D, "eps": w.eps, "io_dtype": act,
+                   "param_dtype": param, "dx_dtype": dxt, "norm": NORM_NAMES[kind],
+                   "samples": w.B, "scalars": list(w.scalars),
+                   "step": "forward + backward (row kernel and parameter reduction)",
+                   "buffer_sets": S},
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(N / (ms_step * 1e-3), 1),
+        "kernels_ms": {"forward": round(fwd_ms, 5), "backward": round(bwd_ms, 5)},
+        "kernel_gbs": {"forward": round(fwd_b / (fwd_ms * 1e-3) / 1e9, 1),
+                       "backward": round(bwd_b / (bwd_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "kernel": "backward (row kernel + reduce)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +420,9 @@ def main():
 
     w = workloads.WORKLOADS[args.workload]
     N, D, kind = w.N, w.D, w.kind
+    if kind in ("dyt", "poly", "mod"):
+        bench_other(args, w, torch, mn, act, param, dxt)
+        return
     print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
     d = workloads.generate(w, act=act, param=param, cot=cot)
     dev = torch.device("cuda", 0)
@@ -426,7 +564,7 @@ def main():
         "config": {
             "workload": w.name, "N": N, "D": D, "eps": w.eps, "io_dtype": act,
             "param_dtype": param, "cotangent_dtype": cot, "dx_dtype": dxt,
-            "norm": {"rms": "RMSNorm", "ln": "LayerNorm", "add": "fused add + RMSNorm"}[kind],
+            "norm": NORM_NAMES[kind],
             "step": "forward + backward rows + column reduce", "buffer_sets": S,
         },
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
