@@ -249,6 +249,25 @@ __device__ __forceinline__ void wait_vmem_all()
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// tanh(u) from one exponential and one reciprocal: with
+// q = 1 / (exp(2|u|) + 1), tanh(|u|) = 1 - 2q, and 1 - tanh(u)^2 = 4q(1 - q)
+// (returned in `sd`; it keeps its relative precision where |tanh| is close
+// to 1, and q -> 0 when the exponential overflows). Below |u| = 1/16 the
+// difference 1 - 2q loses relative precision, so there tanh comes from its
+// odd Taylor series u - u^3/3 + 2u^5/15, whose first omitted term is below
+// 2^-32 |u|. The relative error of the returned tanh stays below about
+// 2^-18 -- far inside a 16-bit ulp, not a binary32 one.
+__device__ __forceinline__ float tanh_q(float u, float& sd)
+{
+    const float a = __builtin_fabsf(u);
+    const float q = __builtin_amdgcn_rcpf(__expf(2.0f * a) + 1.0f);
+    sd = 4.0f * q * (1.0f - q);
+    const float u2 = u * u;
+    const float small = u * __builtin_fmaf(u2, __builtin_fmaf(u2, 2.0f / 15.0f, -1.0f / 3.0f), 1.0f);
+    const float big = __builtin_copysignf(__builtin_fmaf(-2.0f, q, 1.0f), u);
+    return a < 0.0625f ? small : big;
+}
+
 // ---------------------------------------------------------------------------
 // Wave-level sums.
 // ---------------------------------------------------------------------------
@@ -497,6 +516,13 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
                     sc = sload<ST, VEC, 0>(a.scale, so + coff[k]);
                     sh = sload<ST, VEC, 0>(a.shift, so + coff[k]);
                 }
+                // POLY: y = b + v (w1 r1 + v (w2 r2 + v w3 r3)), Horner form
+                float k1 = 0.0f, k2 = 0.0f, k3 = 0.0f;
+                if constexpr (KIND == POLY) {
+                    k1 = pw[0] * rs[u * NSR];
+                    k2 = pw[1] * rs[u * NSR + 1];
+                    k3 = pw[2] * rs[u * NSR + 2];
+                }
                 HV y;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
@@ -506,14 +532,19 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
                     if constexpr (KIND == LN) {
                         o = __builtin_fmaf((v - mu[u]) * rs[u], gam[k][e], bet[k][e]);
                     } else if constexpr (KIND == DYT) {
-                        o = __builtin_fmaf(gam[k][e], tanhf(alpha * v), bet[k][e]);
+                        // 16-bit outputs take the one-exponential tanh; binary32
+                        // outputs the library's
+                        float t;
+                        if constexpr (ST == ST_F32) {
+                            t = tanhf(alpha * v);
+                        } else {
+                            float sd_unused;
+                            t = tanh_q(alpha * v, sd_unused);
+                        }
+                        o = __builtin_fmaf(gam[k][e], t, bet[k][e]);
                     } else if constexpr (KIND == POLY) {
-                        const float v2 = v * v;
-                        const float v3 = v2 * v;
-                        o = __builtin_fmaf(pw[0], v * rs[u * NSR],
-                                           __builtin_fmaf(pw[1], v2 * rs[u * NSR + 1],
-                                                          __builtin_fmaf(pw[2], v3 * rs[u * NSR + 2],
-                                                                         pw[3])));
+                        o = __builtin_fmaf(v, __builtin_fmaf(v, __builtin_fmaf(v, k3, k2), k1),
+                                           pw[3]);
                     } else if constexpr (KIND == MOD) {
                         o = __builtin_fmaf(v * rs[u] * gam[k][e], 1.0f + cget<ST, VEC>(sc, e),
                                            cget<ST, VEC>(sh, e));
@@ -571,7 +602,8 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
     constexpr int RPB = BLOCK / T;
     constexpr int TILE = RPB * U;
     // sums per row: c1 (and c2 for LN; three for POLY; none for DYT)
-    constexpr int NR = (KIND == LN) ? 2 : (KIND == POLY) ? 3 : (KIND == DYT) ? 0 : 1;
+    // POLY's four: sum(dY * x^p) for p = 1, 2, 3 and sum(dY)
+    constexpr int NR = (KIND == LN) ? 2 : (KIND == POLY) ? 4 : (KIND == DYT) ? 0 : 1;
     constexpr int NRR = NR > 0 ? NR : 1;
     // per-column partial arrays: dgamma (+ dbeta for LN and DYT, + dscale and
     // dshift for MOD); POLY has only scalar parameters
@@ -672,6 +704,7 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
     };
 
     const float fD = (float)D;
+    const float invD = 1.0f / fD;
     int phase = 0;
     Tile cur;
     load_tile(cur, first);
@@ -717,9 +750,10 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                         const float dyv = cget<CT, VEC>(cur.dy[u][k], e);
                         if constexpr (KIND == POLY) {
                             const float v2 = v * v;
-                            acc[0] = __builtin_fmaf(dyv, v * cur.rs[u][0], acc[0]);
-                            acc[1] = __builtin_fmaf(dyv, v2 * cur.rs[u][1], acc[1]);
-                            acc[2] = __builtin_fmaf(dyv, v2 * v * cur.rs[u][2], acc[2]);
+                            acc[0] = __builtin_fmaf(dyv, v, acc[0]);
+                            acc[1] = __builtin_fmaf(dyv, v2, acc[1]);
+                            acc[2] = __builtin_fmaf(dyv, v2 * v, acc[2]);
+                            acc[3] += dyv;
                         } else {
                             const float xh = (v - cur.mu[u]) * cur.rs[u][0];
                             const float gg = dyv * gef[k][e];
@@ -745,12 +779,38 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
         for (int u = 0; u < U; ++u) {
             const int64_t row = base + u * RPB + g;
             const bool rok = row < end;
-            const float c1 = (NR > 0) ? c[u * NRR] / fD : 0.0f;
-            const float c2 = (NR > 1) ? c[u * NRR + 1] / fD : 0.0f;
-            const float c3 = (NR > 2) ? c[u * NRR + 2] / fD : 0.0f;
+            // (POLY divides by multiplying with 1/D: its four row means per
+            // row would otherwise cost as much as its element work)
+            const float c1 = (KIND == POLY) ? c[u * NRR] * invD : (NR > 0) ? c[u * NRR] / fD : 0.0f;
+            const float c2 = (KIND == POLY) ? c[u * NRR + 1] * invD
+                                            : (NR > 1) ? c[u * NRR + 1] / fD : 0.0f;
+            const float c3 = (KIND == POLY) ? c[u * NRR + 2] * invD : 0.0f;
             const float rs = (KIND != DYT) ? cur.rs[u][0] : 0.0f;
             const float mu = cur.mu[u];
             const int64_t ro = row * (int64_t)D;
+            // POLY: with S_p = sum(dY x^p) and n_p = x^p r_p, mean(dY n_p) =
+            // r_p S_p / D, and
+            //   dX = dY (A1 + x (A2 + x A3)) - x (B1 + x^2 (B2 + x^2 B3)),
+            //   A_p = p w_p r_p,  B_p = p w_p r_p^2 mean(dY n_p).
+            // The row's shares of dw_p (r_p S_p) and db (S_0) are added once,
+            // by the row group's first lane.
+            float A1 = 0.0f, A2 = 0.0f, A3 = 0.0f, B1 = 0.0f, B2 = 0.0f, B3 = 0.0f;
+            if constexpr (KIND == POLY) {
+                const float r1 = cur.rs[u][0], r2 = cur.rs[u][1], r3 = cur.rs[u][2];
+                const float m1 = r1 * c1, m2 = r2 * c2, m3 = r3 * c3;
+                A1 = pw[0] * r1;
+                A2 = 2.0f * pw[1] * r2;
+                A3 = 3.0f * pw[2] * r3;
+                B1 = A1 * r1 * m1;
+                B2 = A2 * r2 * m2;
+                B3 = A3 * r3 * m3;
+                if (l == 0) {
+                    accs[0] = __builtin_fmaf(r1, c[u * NRR], accs[0]);
+                    accs[1] = __builtin_fmaf(r2, c[u * NRR + 1], accs[1]);
+                    accs[2] = __builtin_fmaf(r3, c[u * NRR + 2], accs[2]);
+                    accs[3] += c[u * NRR + 3];
+                }
+            }
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 const bool ok = rok && cval[k];
@@ -766,14 +826,10 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                     const float dyv = cget<CT, VEC>(cur.dy[u][k], e);
                     float d;
                     if constexpr (KIND == DYT) {
-                        const float u = alpha * v;
-                        const float t = tanhf(u);
-                        // 1 - t^2 = 4 q (1 - q) with q = 1 / (exp(2|u|) + 1):
-                        // no cancellation where |t| is close to 1 (q -> 0
-                        // when the exponential overflows)
-                        const float q =
-                            __builtin_amdgcn_rcpf(__expf(2.0f * __builtin_fabsf(u)) + 1.0f);
-                        const float sd = 4.0f * q * (1.0f - q);
+                        // dX needs only 1 - t^2 (accurate from tanh_q); t
+                        // enters only the dgamma sums
+                        float sd;
+                        const float t = tanh_q(alpha * v, sd);
                         const float gy = dyv * gam[k][e];
                         d = gy * alpha * sd;
                         accg[k][e] = __builtin_fmaf(dyv, t, accg[k][e]);
@@ -781,16 +837,9 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                         accs[0] = __builtin_fmaf(gy * v, sd, accs[0]);
                     } else if constexpr (KIND == POLY) {
                         const float v2 = v * v;
-                        const float r1 = cur.rs[u][0], r2 = cur.rs[u][1], r3 = cur.rs[u][2];
-                        const float n1 = v * r1, n2 = v2 * r2, n3 = v2 * v * r3;
-                        const float t1 = pw[0] * r1 * __builtin_fmaf(-n1, c1, dyv);
-                        const float t2 = pw[1] * r2 * __builtin_fmaf(-n2, c2, dyv);
-                        const float t3 = pw[2] * r3 * __builtin_fmaf(-n3, c3, dyv);
-                        d = __builtin_fmaf(3.0f * v2, t3, __builtin_fmaf(2.0f * v, t2, t1));
-                        accs[0] = __builtin_fmaf(dyv, n1, accs[0]);
-                        accs[1] = __builtin_fmaf(dyv, n2, accs[1]);
-                        accs[2] = __builtin_fmaf(dyv, n3, accs[2]);
-                        accs[3] += dyv;
+                        const float P = __builtin_fmaf(v, __builtin_fmaf(v, A3, A2), A1);
+                        const float Q = __builtin_fmaf(v2, __builtin_fmaf(v2, B3, B2), B1);
+                        d = __builtin_fmaf(dyv, P, -(v * Q));
                     } else {
                         const float xh = (v - mu) * rs;
                         const float gg = dyv * gef[k][e];

@@ -23,6 +23,12 @@ namespace mn {
 //   * streamed outputs use non-temporal stores (NT bit 0) and streamed
 //     inputs non-temporal loads (NT bit 1), except the LayerNorm forward,
 //     which measured slower with non-temporal loads.
+// Rows 12 and 13 fit two common widths between the powers of two exactly
+// (5120 columns, and 6144 in the forward: row groups of 10 and 12 waves,
+// one workgroup per row group); they measured 2-12 % faster there than the
+// next power-of-two row. At 3072 columns, and for the 6144-column backward,
+// exact-fit rows measured slower than the next power-of-two row (whose idle
+// lanes cost no bandwidth), so those widths keep it.
 // Ids are unique within a kind; 8..10 are the element-wise variants (any D,
 // any alignment) shared by all kinds. Each row is instantiated for every
 // storage combination (binary32 activations: see st_vec / st_cpt below).
@@ -36,6 +42,8 @@ namespace mn {
     X(4, 128, 8, 1, 1, 256, 0, 3, 1024)      \
     X(5, 256, 8, 1, 1, 256, 0, 3, 2048)      \
     X(6, 256, 8, 2, 1, 256, 0, 3, 4096)      \
+    X(12, 640, 8, 1, 1, 640, 0, 3, 5120)     \
+    X(13, 768, 8, 1, 1, 768, 0, 3, 6144)     \
     X(7, 1024, 8, 1, 1, 1024, 0, 3, 8192)
 #define MN_FWD_LN(X)                         \
     X(0, 8, 8, 1, 4, 256, 0, 1, 64)          \
@@ -45,6 +53,8 @@ namespace mn {
     X(4, 128, 8, 1, 1, 256, 0, 1, 1024)      \
     X(5, 256, 8, 1, 1, 256, 0, 1, 2048)      \
     X(6, 256, 8, 2, 2, 256, 0, 1, 4096)      \
+    X(12, 640, 8, 1, 1, 640, 0, 1, 5120)     \
+    X(13, 768, 8, 1, 1, 768, 0, 1, 6144)     \
     X(7, 1024, 8, 1, 1, 1024, 0, 1, 8192)
 #define MN_FWD_ADD(X) MN_FWD_RMS(X)
 // the other norms: Dynamic Tanh and Modulated RMSNorm take the RMSNorm
@@ -65,6 +75,7 @@ namespace mn {
     X(4, 128, 8, 1, 2, 512, 1, 3, 1024)      \
     X(5, 256, 8, 1, 2, 512, 1, 3, 2048)      \
     X(6, 512, 8, 1, 2, 512, 1, 3, 4096)      \
+    X(12, 640, 8, 1, 2, 640, 1, 3, 5120)     \
     X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
 #define MN_BWD_LN(X)                         \
     X(0, 8, 8, 1, 4, 256, 1, 3, 64)          \
@@ -74,6 +85,7 @@ namespace mn {
     X(4, 64, 8, 2, 2, 256, 1, 3, 1024)       \
     X(5, 128, 8, 2, 2, 512, 1, 3, 2048)      \
     X(6, 256, 8, 2, 2, 512, 1, 3, 4096)      \
+    X(12, 320, 8, 2, 2, 320, 1, 3, 5120)     \
     X(7, 512, 8, 2, 1, 512, 1, 3, 8192)
 #define MN_BWD_ADD(X) MN_BWD_RMS(X)
 // The other norms keep two or three per-column accumulators, or three row
@@ -87,9 +99,21 @@ namespace mn {
     X(4, 128, 8, 1, 1, 512, 1, 3, 1024)      \
     X(5, 256, 8, 1, 1, 512, 1, 3, 2048)      \
     X(6, 512, 8, 1, 1, 512, 1, 3, 4096)      \
+    X(12, 640, 8, 1, 1, 640, 1, 3, 5120)     \
     X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
+// PolyNorm reduces four sums per row for little arithmetic per element, so
+// it takes two chunks per lane (half the lanes per row) to amortise them.
+#define MN_BWD_POLY(X)                       \
+    X(0, 8, 8, 1, 2, 256, 1, 3, 64)          \
+    X(1, 16, 8, 1, 2, 256, 1, 3, 128)        \
+    X(2, 32, 8, 1, 2, 256, 1, 3, 256)        \
+    X(3, 64, 8, 1, 1, 256, 1, 3, 512)        \
+    X(4, 64, 8, 2, 1, 256, 1, 3, 1024)       \
+    X(5, 128, 8, 2, 1, 512, 1, 3, 2048)      \
+    X(6, 256, 8, 2, 1, 512, 1, 3, 4096)      \
+    X(12, 320, 8, 2, 1, 320, 1, 3, 5120)     \
+    X(7, 512, 8, 2, 1, 512, 1, 3, 8192)
 #define MN_BWD_DYT(X) MN_BWD_EXT(X)
-#define MN_BWD_POLY(X) MN_BWD_EXT(X)
 #define MN_BWD_MOD(X) MN_BWD_EXT(X)
 #define MN_BWD_GEN(X)                        \
     X(8, 64, 1, 16, 1, 256, 1, 1, 1024)      \

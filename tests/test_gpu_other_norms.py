@@ -30,7 +30,8 @@ def test_small_every_element(kind, N, D):
     say(f"[other] {kind} {N}x{D}: {w}")
 
 
-D_SWEEP = [1, 2, 7, 8, 64, 127, 128, 256, 1000, 1024, 2048, 2056, 4095, 4096, 6000, 8191, 8192]
+D_SWEEP = [1, 2, 7, 8, 64, 127, 128, 256, 1000, 1024, 2048, 2056, 3072, 4095, 4096, 5120, 6000,
+           6144, 8191, 8192]
 
 
 @pytest.mark.parametrize("D", D_SWEEP)

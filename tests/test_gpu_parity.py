@@ -31,7 +31,7 @@ def test_small_workload_every_element(name):
 
 
 D_SWEEP = [1, 2, 7, 8, 16, 63, 64, 127, 128, 200, 256, 257, 512, 1000, 1024, 2048, 2056, 3000,
-           4095, 4096, 6000, 8191, 8192]
+           3072, 4095, 4096, 5000, 5120, 6000, 6144, 8191, 8192]
 
 
 @pytest.mark.parametrize("D", D_SWEEP)

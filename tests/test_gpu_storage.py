@@ -49,8 +49,8 @@ def test_storage_pairs(kind, act, param, D):
     say(f"[storage] {kind} act={act} param={param} D={D}: {w}")
 
 
-D_SWEEP = [1, 2, 3, 4, 7, 8, 63, 64, 127, 128, 200, 256, 260, 1000, 2048, 2056, 3000, 4095,
-           6000, 8191]
+D_SWEEP = [1, 2, 3, 4, 7, 8, 63, 64, 127, 128, 200, 256, 260, 1000, 2048, 2056, 3000, 3072,
+           4095, 5120, 6000, 6144, 8191]
 
 
 @pytest.mark.parametrize("D", D_SWEEP)
