@@ -105,6 +105,8 @@ class Oracle:
                                         _PD, _PD],
             "mno_groupnorm_backward_t": [_VP, I, _VP, I, _VP, I, _I64, _I64, _I64, _I64, _DBL,
                                          _PD, _PD, _PD],
+            "mno_rmsnorm_gemv_t": [_VP, I, _VP, I, _VP, I, _I64, _I64, _I64, _DBL, _PD],
+            "mno_layernorm_gemv_t": [_VP, I, _VP, _VP, I, _VP, I, _I64, _I64, _I64, _DBL, _PD],
         }
         for name, argtypes in sig.items():
             fn = getattr(lib, name)
@@ -356,6 +358,26 @@ class Oracle:
             x, tx, g, tg, dy, ty, N, C, L, int(groups), float(eps), self._out(dX),
             self._out(dg), self._out(db)))
         return dX, dg, db
+
+    # -- fused normalization + GEMV (inference) ---------------------------------
+
+    def norm_gemv(self, X, gamma, W, eps, beta=None, f64: bool = False):
+        """Y [M, N] = Norm(X) @ W: RMSNorm, or LayerNorm when beta is given;
+        float64, the normalised rows unrounded."""
+        M, K = _nd(X)
+        N = int(W.shape[1])
+        (x,), tx, k1 = self._group([X], f64)
+        (g, b), tg, k2 = self._group([gamma, beta], f64)
+        (w,), tw, k3 = self._group([W], f64)
+        Y = np.empty((M, N))
+        if beta is None:
+            rc = self.lib.mno_rmsnorm_gemv_t(x, tx, g, tg, w, tw, M, N, K, float(eps),
+                                             self._out(Y))
+        else:
+            rc = self.lib.mno_layernorm_gemv_t(x, tx, g, b, tg, w, tw, M, N, K, float(eps),
+                                               self._out(Y))
+        self._check("norm_gemv", rc)
+        return Y
 
 
 _default: Optional[Oracle] = None

@@ -1,8 +1,9 @@
 /*
  * mn_oracle.c -- plain fp64 CPU oracle for the row-wise normalization
  * training pair (RMSNorm, LayerNorm, fused residual-add + RMSNorm; forward and
- * backward), and for the other row-wise norms the [meTile] coverage
- * inventory lists (Dynamic Tanh, PolyNorm, Modulated RMSNorm, GroupNorm).
+ * backward), for the other row-wise norms the [meTile] coverage inventory
+ * lists (Dynamic Tanh, PolyNorm, Modulated RMSNorm, GroupNorm), and for the
+ * inference-only fused normalization + GEMV of [tensorcore].
  *
  * TEST INFRASTRUCTURE ONLY. Nothing in the product library links, includes or
  * calls this file; only the test suite, the smoke check and the benchmark's
@@ -943,4 +944,58 @@ int mno_groupnorm_backward_t(const void* X, int tx, const void* gamma, int tg, c
     if (!type_ok(tx) || !type_ok(tg) || !type_ok(ty)) return MNO_ERR_ARG;
     return gn_backward(opt(X, tx), opt(gamma, tg), opt(dY, ty), N, C, L, G, eps, dX, dgamma,
                        dbeta);
+}
+
+/* ---------------------------------------------------------------------------
+ * Fused normalization + GEMV ([tensorcore] "Fused Norm + GEMV"): for an
+ * inference batch X [M, K] (M small), Y [M, N] = Norm(X) @ W with W [K, N]
+ * row-major and Norm the RMSNorm (gamma) or LayerNorm (gamma, beta) of each
+ * row over its K columns, exactly as the forward functions above; the
+ * normalised rows are not rounded to a storage type before the product (the
+ * fused kernel never stores them). No statistics are returned. Sums over k
+ * are in ascending order.
+ * ------------------------------------------------------------------------- */
+
+static int norm_gemv(int ln, operand X, operand G, operand B, operand W, int64_t M, int64_t N,
+                     int64_t K, double eps, double* Y)
+{
+    if (bad_shape(M, K) || N < 1) return MNO_ERR_ARG;
+    fill_tables();
+    double* xn = malloc(sizeof(double) * (size_t)(M > 0 ? M : 1) * (size_t)K);
+    double *mean = malloc(sizeof(double) * (size_t)(M > 0 ? M : 1)),
+           *rstd = malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+    double* wrow = malloc(sizeof(double) * (size_t)N);
+    if (!xn || !mean || !rstd || !wrow) {
+        free(xn); free(mean); free(rstd); free(wrow);
+        return MNO_ERR_MEM;
+    }
+    int rc = ln ? ln_forward(X, G, B, M, K, eps, xn, mean, rstd)
+                : rms_forward(X, opt(NULL, X.type), G, M, K, eps, NULL, xn, rstd);
+    if (rc == MNO_OK) {
+        for (int64_t i = 0; i < M * N; ++i) Y[i] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            get_row(W, k, N, wrow);
+            for (int64_t m = 0; m < M; ++m) {
+                const double a = xn[m * K + k];
+                for (int64_t n = 0; n < N; ++n) Y[m * N + n] += a * wrow[n];
+            }
+        }
+    }
+    free(xn); free(mean); free(rstd); free(wrow);
+    return rc;
+}
+
+int mno_rmsnorm_gemv_t(const void* X, int tx, const void* gamma, int tg, const void* W, int tw,
+                       int64_t M, int64_t N, int64_t K, double eps, double* Y)
+{
+    if (!type_ok(tx) || !type_ok(tg) || !type_ok(tw)) return MNO_ERR_ARG;
+    return norm_gemv(0, opt(X, tx), opt(gamma, tg), opt(NULL, tg), opt(W, tw), M, N, K, eps, Y);
+}
+
+int mno_layernorm_gemv_t(const void* X, int tx, const void* gamma, const void* beta, int tg,
+                         const void* W, int tw, int64_t M, int64_t N, int64_t K, double eps,
+                         double* Y)
+{
+    if (!type_ok(tx) || !type_ok(tg) || !type_ok(tw)) return MNO_ERR_ARG;
+    return norm_gemv(1, opt(X, tx), opt(gamma, tg), opt(beta, tg), opt(W, tw), M, N, K, eps, Y);
 }

@@ -678,10 +678,43 @@ def pin_groupnorm(o):
         _fd_check(f"groupnorm dbeta {N}x{C}x{L}", lambda v: loss(x, g, v), b, db)
 
 
+def pin_norm_gemv(o):
+    rng = np.random.default_rng(47)
+    eps = 1e-5
+    for M, K, N in ((1, 1, 1), (3, 64, 40), (4, 257, 33), (2, 1024, 96)):
+        X = rng.standard_normal((M, K)).astype(np.float16)
+        g = (1 + 0.1 * rng.standard_normal(K)).astype(np.float16)
+        b = (0.1 * rng.standard_normal(K)).astype(np.float16)
+        W = (rng.standard_normal((K, N)) / np.sqrt(K)).astype(np.float16)
+        tx, tg, tb, tw = (torch.from_numpy(a.astype(np.float64)) for a in (X, g, b, W))
+        ref = F.rms_norm(tx, (K,), tg, eps) @ tw
+        _close(o.norm_gemv(X, g, W, eps), ref.numpy(), 1e-12, 1e-13, f"rms gemv {M}x{K}x{N}")
+        ref = F.layer_norm(tx, (K,), tg, tb, eps) @ tw
+        _close(o.norm_gemv(X, g, W, eps, beta=b), ref.numpy(), 1e-12, 1e-13,
+               f"ln gemv {M}x{K}x{N}")
+    # an identity W returns the normalised rows; a column selector picks one
+    M, K = 3, 48
+    X = rng.standard_normal((M, K))
+    g = 1 + 0.2 * rng.standard_normal(K)
+    b = 0.2 * rng.standard_normal(K)
+    tx, tg, tb = (torch.from_numpy(a) for a in (X, g, b))
+    _close(o.norm_gemv(X, g, np.eye(K), eps, f64=True),
+           F.rms_norm(tx, (K,), tg, eps).numpy(), 1e-13, 1e-15, "rms gemv identity")
+    sel = np.zeros((K, 5)); sel[[7, 0, 47, 20, 7], range(5)] = 1.0
+    _close(o.norm_gemv(X, g, sel, eps, beta=b, f64=True),
+           F.layer_norm(tx, (K,), tg, tb, eps).numpy()[:, [7, 0, 47, 20, 7]], 1e-13, 1e-15,
+           "ln gemv column selector")
+    # linear in W
+    W1 = rng.standard_normal((K, 9)); W2 = rng.standard_normal((K, 9))
+    _close(o.norm_gemv(X, g, W1 + 2 * W2, eps, f64=True),
+           o.norm_gemv(X, g, W1, eps, f64=True) + 2 * o.norm_gemv(X, g, W2, eps, f64=True),
+           1e-12, 1e-12, "gemv linear in W")
+
+
 ALL_PINS = [
     pin_codec_decode, pin_codec_encode, pin_torch_rmsnorm, pin_torch_layernorm,
     pin_torch_add_rmsnorm, pin_finite_differences, pin_constant_rows, pin_zero_rows,
     pin_worked_example, pin_invariants, pin_scaling, pin_fused_special_cases,
     pin_bf16_codec_decode, pin_bf16_codec_encode, pin_storage_types_agree, pin_bf16_fused_sum,
-    pin_dyt, pin_polynorm, pin_modrms, pin_groupnorm,
+    pin_dyt, pin_polynorm, pin_modrms, pin_groupnorm, pin_norm_gemv,
 ]

@@ -69,6 +69,9 @@ MUTANTS = {
                                  "dscale[b * D + j] += w.dy[j] * w.xh[j];"),
     "gn_gamma_by_group": ("Y[slice * M + k] = (w.x[k] - mu) * r * gam[c] + bet[c];",
                           "Y[slice * M + k] = (w.x[k] - mu) * r * gam[g] + bet[c];"),
+    "gemv_layernorm_as_rms": ("int rc = ln ? ln_forward(X, G, B, M, K, eps, xn, mean, rstd)",
+                              "int rc = 0 ? ln_forward(X, G, B, M, K, eps, xn, mean, rstd)"),
+    "gemv_w_row_off_by_one": ("get_row(W, k, N, wrow);", "get_row(W, (k + 1) % K, N, wrow);"),
     "gn_channel_stride": ("const int64_t c = g * (C / groups) + k / L;\n                if (dX)",
                           "const int64_t c = g * (C / groups) + k % (C / groups);\n"
                           "                if (dX)"),
