@@ -68,6 +68,14 @@ def alg_bytes(kind: str, N: int, D: int, act: str = "f16", param: str = "f16",
     return fwd, bwd
 
 
+def gemv_bytes(M: int, K: int, N: int, act: str = "f16", param: str = "f16", ln: bool = False):
+    """Algorithmic bytes of one fused norm + GEMV call: X [M, K], gamma (and
+    beta) [K], W [K, N] read once, Y [M, N] written once; the fp32 partials
+    of the K slices are workspace and not counted."""
+    a, p = SIZE[act], SIZE[param]
+    return a * (M * K + K * N + M * N) + p * K * (2 if ln else 1)
+
+
 def kernel_hash() -> str:
     """Hash of the kernel sources (templates and launch tables)."""
     h = hashlib.sha256()
@@ -260,7 +268,91 @@ def pages_context(torch, mn):
 
 
 NORM_NAMES = {"rms": "RMSNorm", "ln": "LayerNorm", "add": "fused add + RMSNorm",
-              "dyt": "Dynamic Tanh", "poly": "PolyNorm", "mod": "Modulated RMSNorm"}
+              "dyt": "Dynamic Tanh", "poly": "PolyNorm", "mod": "Modulated RMSNorm",
+              "rms_gemv": "fused RMSNorm + GEMV", "ln_gemv": "fused LayerNorm + GEMV"}
+
+
+def bench_gemv(args, w, torch, mn, act, param):
+    """Fused RMSNorm / LayerNorm + GEMV (inference): one step is one fused
+    call Y = Norm(X) @ W. Several copies of W rotate (each step reads a
+    different one, more bytes than the Infinity Cache holds), events bracket
+    every call on the launch stream."""
+    M, K, N = w.N, w.D, w.Nout
+    ln = w.kind == "ln_gemv"
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+    print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
+    d = workloads.generate(w, act=act, param=param)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def upload(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    up = {k: upload(v) for k, v in d.items()}
+    S = max(4, args.sets)
+    nb = mn.norm_gemv_workspace_bytes(M, N, K)
+    sets = [{"X": up["X"].clone(), "W": up["W"] if s == 0 else up["W"].clone(),
+             "Y": torch.empty(M, N, dtype=tdt[act], device=dev),
+             "ws": torch.empty(nb // 4, dtype=torch.float32, device=dev)} for s in range(S)]
+    beta = up.get("beta")
+
+    def call(b):
+        mn.mn_fused_norm_gemv_ex(b["X"], up["gamma"], b["W"], b["Y"], w.eps, b["ws"],
+                                 beta=beta, stream=stream)
+
+    Ks, Wu = args.steps, args.warmup
+    nbytes = gemv_bytes(M, K, N, act, param, ln)
+    for k in range(Wu):
+        call(sets[k % S])
+    torch.cuda.synchronize()
+    ev = [(HipEvent(), HipEvent()) for _ in range(Ks)]
+    t0 = time.perf_counter()
+    for k in range(Ks):
+        ev[k][0].record(stream); call(sets[(Wu + k) % S]); ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / Ks
+    call_ms = float(np.mean([a.elapsed_ms(b) for a, b in ev]))
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        print(f"[bench] cpu baseline (oracle, {args.cpu_budget:.0f} s budget)", file=sys.stderr,
+              flush=True)
+        t = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.norm_gemv(d["X"], d["gamma"], d["W"], w.eps, beta=d.get("beta"))
+            reps += 1
+            el = time.perf_counter() - t
+            if el >= args.cpu_budget:
+                break
+        cpu = {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s",
+               "calls_per_s": round(reps / el, 3), "cores": 1, "kind": "oracle",
+               "sample": f"{reps} full {M}x{K}x{N} calls ({el:.1f} s), single-threaded C fp64"}
+    line = {
+        "metric": f"achieved HBM GB/s (% of peak) for the fused norm + GEMV, "
+                  f"{NORM_NAMES[w.kind]} {M}x{K} @ {K}x{N}",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": Ks, "warmup": Wu,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "K": K, "N": N, "eps": w.eps, "io_dtype": act,
+                   "param_dtype": param, "norm": NORM_NAMES[w.kind],
+                   "step": "one fused call (GEMV kernel + K-slice reduce)", "weight_sets": S},
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "calls_per_s": round(1e3 / ms_step, 1),
+        "kernels_ms": {"fused_call": round(call_ms, 5)},
+        "roofline": {"bound": "hbm", "kernel": "fused call (GEMV + K-slice reduce)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line), flush=True)
 
 
 def bench_other(args, w, torch, mn, act, param, dxt):
@@ -422,6 +514,9 @@ def main():
     N, D, kind = w.N, w.D, w.kind
     if kind in ("dyt", "poly", "mod"):
         bench_other(args, w, torch, mn, act, param, dxt)
+        return
+    if kind in ("rms_gemv", "ln_gemv"):
+        bench_gemv(args, w, torch, mn, act, param)
         return
     print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
     d = workloads.generate(w, act=act, param=param, cot=cot)

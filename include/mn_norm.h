@@ -275,6 +275,40 @@ mn_status mn_mod_rmsnorm_backward_ex(const void* X, const void* gamma, const voi
 size_t mn_mod_rmsnorm_workspace_bytes(int64_t B, int64_t N, int64_t D);
 
 /* ---------------------------------------------------------------------------
+ * Fused normalization + GEMV for small inference batches. [tensorcore]
+ * "Fused Norm + GEMV": Y = Norm(X, gamma[, beta]) @ W, the normalisation
+ * applied in registers during the product instead of writing the normalised
+ * rows out; the fused path returns no statistics and has no backward.
+ *   X [M][K] (1 <= M <= 8), W [K][N] row-major, Y [M][N]: storage `act`
+ *   (MN_F16 or MN_BF16); gamma, beta [K] of `param`; fp32 arithmetic.
+ *   Norm is the RMSNorm or LayerNorm forward above over each row of X (the
+ *   normalised rows are not rounded to a storage type); Y is rounded once.
+ * The workspace (mn_norm_gemv_workspace_bytes(M, N, K), 16-byte aligned)
+ * holds the row statistics and fp32 partial products over slices of K; the
+ * sums run in a fixed order, so Y is bitwise reproducible. The normalisation
+ * is applied to the sums (rstd, and LayerNorm's mean through the column sums
+ * of gamma*W and beta*W) rather than to each X element; the results agree
+ * with the element-wise form to fp32 rounding. Validation as elsewhere (MN_ERR_SHAPE for M
+ * outside [1, 8], N < 1 or K < 1).
+ * ------------------------------------------------------------------------- */
+mn_status mn_fused_rmsnorm_gemv(const mn_f16* X, const mn_f16* gamma, const mn_f16* W, mn_f16* Y,
+                                int64_t M, int64_t N, int64_t K, float eps, void* workspace,
+                                size_t workspace_bytes, void* stream);
+mn_status mn_fused_layernorm_gemv(const mn_f16* X, const mn_f16* gamma, const mn_f16* beta,
+                                  const mn_f16* W, mn_f16* Y, int64_t M, int64_t N, int64_t K,
+                                  float eps, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+mn_status mn_fused_rmsnorm_gemv_ex(const void* X, const void* gamma, const void* W, void* Y,
+                                   int64_t M, int64_t N, int64_t K, float eps, mn_dtype act,
+                                   mn_dtype param, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+mn_status mn_fused_layernorm_gemv_ex(const void* X, const void* gamma, const void* beta,
+                                     const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+                                     float eps, mn_dtype act, mn_dtype param, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+size_t mn_norm_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* ---------------------------------------------------------------------------
  * Workspace and diagnostics.
  * ------------------------------------------------------------------------- */
 

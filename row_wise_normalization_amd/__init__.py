@@ -82,6 +82,11 @@ _SIGNATURES = {
     "mn_mod_rmsnorm_forward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F, _C, _C, _P],
     "mn_mod_rmsnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _C, _C,
                                    _C, _P, _SZ, _P],
+    "mn_fused_rmsnorm_gemv": [_P, _P, _P, _P, _I64, _I64, _I64, _F, _P, _SZ, _P],
+    "mn_fused_layernorm_gemv": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _F, _P, _SZ, _P],
+    "mn_fused_rmsnorm_gemv_ex": [_P, _P, _P, _P, _I64, _I64, _I64, _F, _C, _C, _P, _SZ, _P],
+    "mn_fused_layernorm_gemv_ex": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _F, _C, _C, _P, _SZ,
+                                   _P],
 }
 
 
@@ -103,6 +108,8 @@ def lib() -> ctypes.CDLL:
     L.mn_norm_workspace_bytes.restype = _SZ
     L.mn_mod_rmsnorm_workspace_bytes.argtypes = [_I64, _I64, _I64]
     L.mn_mod_rmsnorm_workspace_bytes.restype = _SZ
+    L.mn_norm_gemv_workspace_bytes.argtypes = [_I64, _I64, _I64]
+    L.mn_norm_gemv_workspace_bytes.restype = _SZ
     L.mn_status_string.argtypes = [ctypes.c_int]
     L.mn_status_string.restype = ctypes.c_char_p
     L.mn_last_device_error.argtypes = []
@@ -548,3 +555,36 @@ def mod_rmsnorm_backward(X, gamma, scale, rstd, dY, stream=None, dx_dtype=None):
     ws = new_workspace(MN_MOD_RMSNORM, N, D, X.device, B=B)
     mn_mod_rmsnorm_backward_ex(X, gamma, scale, rstd, dY, dX, dgamma, dscale, dshift, ws, stream)
     return dX, dgamma, dscale, dshift
+
+
+# --- fused normalization + GEMV (inference) -------------------------------------
+
+def norm_gemv_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().mn_norm_gemv_workspace_bytes(int(M), int(N), int(K)))
+
+
+def mn_fused_norm_gemv_ex(X, gamma, W, Y, eps: float, workspace, beta=None, stream=None):
+    """Y [M, N] = Norm(X [M, K]) @ W [K, N]; LayerNorm when beta is given."""
+    M, K = _nd(X)
+    N = int(W.shape[1])
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (M, K)); _check_t("gamma", gamma, gamma.dtype, (K,))
+    _check_t("beta", beta, gamma.dtype, (K,), optional=True)
+    _check_t("W", W, X.dtype, (K, N)); _check_t("Y", Y, X.dtype, (M, N))
+    if beta is None:
+        _call("mn_fused_rmsnorm_gemv_ex", _ptr(X), _ptr(gamma), _ptr(W), _ptr(Y), M, N, K,
+              float(eps), act, par, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+    else:
+        _call("mn_fused_layernorm_gemv_ex", _ptr(X), _ptr(gamma), _ptr(beta), _ptr(W), _ptr(Y),
+              M, N, K, float(eps), act, par, _ptr(workspace), _ws_bytes(workspace),
+              _stream(stream))
+
+
+def fused_norm_gemv(X, gamma, W, eps: float = 1e-5, beta=None, stream=None):
+    M, K = _nd(X)
+    N = int(W.shape[1])
+    Y = torch.empty(M, N, dtype=X.dtype, device=X.device)
+    nb = max(16, norm_gemv_workspace_bytes(M, N, K))
+    ws = torch.empty(nb // 4 + 4, dtype=torch.float32, device=X.device)
+    mn_fused_norm_gemv_ex(X, gamma, W, Y, eps, ws, beta, stream)
+    return Y

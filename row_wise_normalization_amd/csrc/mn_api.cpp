@@ -349,6 +349,64 @@ mn_status reduce_partials(int kind, int64_t N, int64_t D, int64_t B, const void*
 
 const BwdTypes kF16{MN_F16, MN_F16, MN_F16, MN_F16};
 
+// ---------------------------------------------------------------------------
+// Fused normalization + GEMV.
+// ---------------------------------------------------------------------------
+
+bool gemv_shape_ok(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 1 || M > mn::kGemvMaxM || N < 1 || K < 1) return false;
+    return N <= INT32_MAX / 8 && K <= INT32_MAX / 8 && K <= (INT64_MAX / 8) / N;
+}
+
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (!gemv_shape_ok(M, N, K)) return 0;
+    const mn::GemvPlan p = mn::plan_gemv(M, N, K, N % 8 == 0);
+    const mn::GemvPlan q = mn::plan_gemv(M, N, K, false);
+    const int64_t S = p.S > q.S ? p.S : q.S;  // either load path
+    // statistics, then S slices of M + 2 partial rows (LayerNorm's two extra)
+    return sizeof(float) * ((size_t)mn::kGemvStatFloats + (size_t)S * (size_t)(M + 2) * (size_t)N);
+}
+
+mn_status norm_gemv(bool ln, const void* X, const void* gamma, const void* beta, const void* W,
+                    void* Y, int64_t M, int64_t N, int64_t K, float eps, int st, int pdt,
+                    void* ws, size_t ws_bytes, void* stream)
+{
+    if (!X || !gamma || !W || !Y || (ln && !beta)) return MN_ERR_NULL;
+    if (!dtype_ok(st) || !dtype_ok(pdt) || st == MN_F32) return MN_ERR_DTYPE;
+    if (!gemv_shape_ok(M, N, K)) return MN_ERR_SHAPE;
+    if (!eps_ok(eps)) return MN_ERR_EPS;
+    const size_t need = gemv_workspace_bytes(M, N, K);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
+    const size_t es = (size_t)mn::stor_bytes(st);
+    const size_t kp = (size_t)K * (size_t)mn::stor_bytes(pdt);
+    const Span in[] = {span(X, (size_t)M * K * es), span(gamma, kp), span(beta, kp),
+                       span(W, (size_t)K * N * es)};
+    const Span out[] = {span(Y, (size_t)M * N * es), span(ws, need)};
+    if (!alias_free(in, out)) return MN_ERR_ALIAS;
+
+    const bool vec_ok = N % 8 == 0 && aligned16(W);
+    const mn::GemvPlan plan = mn::plan_gemv(M, N, K, vec_ok);
+    mn::GemvArgs a;
+    a.X = X;
+    a.gamma = gamma;
+    a.beta = ln ? beta : nullptr;
+    a.W = W;
+    a.stats = static_cast<float*>(ws);
+    a.part = static_cast<float*>(ws) + mn::kGemvStatFloats;
+    a.Y = Y;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.pdt = pdt;
+    a.eps = eps;
+    a.KB = plan.KB;
+    a.S = plan.S;
+    a.NB = plan.NB;
+    return device_status(mn::launch_gemv(st, ln, plan, a, as_stream(stream)));
+}
+
 mn_status backward(int kind, const BwdIn& b, const BwdOut& o, int64_t N, int64_t D,
                    const BwdTypes& t, void* ws, size_t ws_bytes, void* stream)
 {
@@ -640,6 +698,48 @@ mn_status mn_mod_rmsnorm_backward_ex(const void* X, const void* gamma, const voi
     b.B = B;
     return backward(mn::MOD, b, bwd_out(dgamma, dscale, dshift), N, D,
                     BwdTypes{act, param, act, dxt}, workspace, workspace_bytes, stream);
+}
+
+// --- fused normalization + GEMV (inference) ---------------------------------
+
+mn_status mn_fused_rmsnorm_gemv(const mn_f16* X, const mn_f16* gamma, const mn_f16* W, mn_f16* Y,
+                                int64_t M, int64_t N, int64_t K, float eps, void* workspace,
+                                size_t workspace_bytes, void* stream)
+{
+    return norm_gemv(false, X, gamma, nullptr, W, Y, M, N, K, eps, MN_F16, MN_F16, workspace,
+                     workspace_bytes, stream);
+}
+
+mn_status mn_fused_layernorm_gemv(const mn_f16* X, const mn_f16* gamma, const mn_f16* beta,
+                                  const mn_f16* W, mn_f16* Y, int64_t M, int64_t N, int64_t K,
+                                  float eps, void* workspace, size_t workspace_bytes,
+                                  void* stream)
+{
+    return norm_gemv(true, X, gamma, beta, W, Y, M, N, K, eps, MN_F16, MN_F16, workspace,
+                     workspace_bytes, stream);
+}
+
+mn_status mn_fused_rmsnorm_gemv_ex(const void* X, const void* gamma, const void* W, void* Y,
+                                   int64_t M, int64_t N, int64_t K, float eps, mn_dtype act,
+                                   mn_dtype param, void* workspace, size_t workspace_bytes,
+                                   void* stream)
+{
+    return norm_gemv(false, X, gamma, nullptr, W, Y, M, N, K, eps, act, param, workspace,
+                     workspace_bytes, stream);
+}
+
+mn_status mn_fused_layernorm_gemv_ex(const void* X, const void* gamma, const void* beta,
+                                     const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+                                     float eps, mn_dtype act, mn_dtype param, void* workspace,
+                                     size_t workspace_bytes, void* stream)
+{
+    return norm_gemv(true, X, gamma, beta, W, Y, M, N, K, eps, act, param, workspace,
+                     workspace_bytes, stream);
+}
+
+size_t mn_norm_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    return gemv_workspace_bytes(M, N, K);
 }
 
 // --- workspace, stage 2, diagnostics ----------------------------------------

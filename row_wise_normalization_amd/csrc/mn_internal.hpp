@@ -118,4 +118,34 @@ hipError_t launch_backward_rows(int kind, int st, int ct, int ot, const BwdPlan&
                                 const BwdArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 
+// Fused normalization + GEMV (inference): Y [M][N] = Norm(X [M][K]) @ W [K][N].
+constexpr int kGemvMaxKB = 512;  // rows of W per tile (LDS slice of the product rows)
+constexpr int kGemvMaxM = 8;
+constexpr int kGemvStatFloats = 64;  // workspace head: {mean, rstd} per X row
+
+struct GemvArgs {
+    const void* X;           // [M][K], storage type of the launch
+    const void* gamma;       // [K], type pdt
+    const void* beta;        // [K], type pdt (LayerNorm) or null
+    const void* W;           // [K][N], storage type of the launch
+    float* stats;            // [M][2] row statistics (workspace head)
+    float* part;             // [S][RE][N] fp32 partial products, RE = M (+2 LayerNorm)
+    void* Y;                 // [M][N], storage type of the launch
+    int32_t M, N, K, pdt;
+    float eps;
+    int32_t KB;              // W rows per tile
+    int32_t S;               // K slices = ceil(K / KB)
+    int32_t NB;              // column blocks
+};
+
+struct GemvPlan {
+    bool vec;                // 16-byte W loads (N % 8 == 0, aligned)
+    int32_t MM;              // rows instantiated: 1, 2, 4 or 8 >= M
+    int32_t NB, KB, S;
+    int64_t grid;
+};
+
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, bool vec_ok);
+hipError_t launch_gemv(int st, bool ln, const GemvPlan& p, const GemvArgs& a, hipStream_t s);
+
 }  // namespace mn

@@ -228,6 +228,14 @@ __device__ __forceinline__ void widen_param(const PRaw<VEC>& r, int pdt, bool va
     for (int e = 0; e < VEC; ++e) dst[e] = valid ? dst[e] : 0.0f;
 }
 
+// One parameter element of runtime storage type pdt, widened to fp32.
+__device__ __forceinline__ void load_scalar_param(const void* base, int pdt, int64_t i, float& v)
+{
+    if (pdt == ST_F32) v = static_cast<const float*>(base)[i];
+    else if (pdt == ST_BF16) v = (float)static_cast<const __bf16*>(base)[i];
+    else v = (float)static_cast<const _Float16*>(base)[i];
+}
+
 // Opaque register copy: afterwards the compiler cannot reuse fp32 values it
 // derived from `v` earlier, so packed fp16 registers are widened again where
 // needed instead of keeping every fp32 temporary live across a reduction

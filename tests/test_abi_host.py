@@ -230,6 +230,38 @@ def test_other_norms_validation():
     assert mod_b(dxt=BF16) == 7
 
 
+def test_fused_gemv_validation_and_workspace():
+    L = mn.lib()
+    f = ctypes.c_float(1e-5)
+    F16, BF16, F32 = mn.MN_F16, mn.MN_BF16, mn.MN_F32
+    # 64 floats of row statistics, then S slices of M + 2 fp32 partial rows;
+    # one tile per workgroup, K slices halve from 512 rows until there are 512
+    # tiles or the slices reach 64 rows; S is the larger of the 16-byte path
+    # (128-column tiles) and the element-wise path (64-column tiles)
+    ws = lambda S, M, N: 4 * (64 + S * (M + 2) * N)
+    assert mn.norm_gemv_workspace_bytes(4, 4096, 4096) == ws(16, 4, 4096)
+    assert mn.norm_gemv_workspace_bytes(1, 14336, 4096) == ws(8, 1, 14336)
+    assert mn.norm_gemv_workspace_bytes(4, 12288, 4096) == ws(8, 4, 12288)
+    assert mn.norm_gemv_workspace_bytes(2, 7, 100) == ws(2, 2, 7)
+    for bad in ((0, 8, 8), (9, 8, 8), (1, 0, 8), (1, 8, 0)):
+        assert mn.norm_gemv_workspace_bytes(*bad) == 0
+    M, N, K = 4, 64, 128
+    ws = mn.norm_gemv_workspace_bytes(M, N, K)
+    W = P(0xE0000000)
+    rms = lambda X=A, g=B, Wt=C, Y=Dp, M=M, act=F16, par=F16, ws_=W, nb=ws, eps=f: \
+        L.mn_fused_rmsnorm_gemv_ex(X, g, Wt, Y, M, N, K, eps, act, par, ws_, nb, S)
+    assert rms(X=NULL) == 1 and rms(Wt=NULL) == 1 and rms(ws_=NULL) == 5
+    assert rms(M=0) == 2 and rms(M=9) == 2
+    assert rms(eps=ctypes.c_float(0.0)) == 3
+    assert rms(Y=A) == 4                                   # Y is X
+    assert rms(Y=P(0x40000000 + K * N * 2 - 2)) == 4        # Y overlaps W's last element
+    assert rms(nb=ws - 4) == 5
+    assert rms(act=F32) == 7 and rms(par=5) == 7
+    assert L.mn_fused_layernorm_gemv_ex(A, B, NULL, C, Dp, M, N, K, f, F16, F16, W, ws, S) == 1
+    assert L.mn_fused_layernorm_gemv(A, B, E, C, Dp, M, N, K, f, W, ws - 1, S) == 5
+    assert L.mn_fused_rmsnorm_gemv(A, B, C, Dp, M, N, K, f, W, 0, S) == 5
+
+
 def test_product_and_oracle_are_independent():
     """Neither side imports, includes or links the other."""
     pkg = os.path.join(ROOT, "row_wise_normalization_amd")

@@ -1,0 +1,91 @@
+"""Fused RMSNorm / LayerNorm + GEMV ([tensorcore] "Fused Norm + GEMV"): the
+HIP path against the fp64 oracle on every output element (tolerances in
+tests/gpu_gemv.py)."""
+import numpy as np
+import pytest
+import torch
+
+import parity
+import workloads
+import row_wise_normalization_amd as mn
+from gpu_cases import dev, say
+from gpu_gemv import case as _case, compare, reference, run
+
+pytestmark = pytest.mark.gpu
+
+
+SHAPES = [(1, 1, 1), (1, 64, 8), (2, 257, 130), (3, 1000, 1000), (4, 4096, 4096),
+          (5, 2048, 520), (8, 1024, 2056), (1, 3000, 7), (4, 300, 4104), (6, 8192, 512)]
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_every_element(M, K, N, ln):
+    say(f"[gemv] {'ln' if ln else 'rms'} M={M} K={K} N={N}")
+    d = _case(M, K, N, 10 + M + K, ln)
+    w = compare(run(d, 1e-5, ln), reference(d, 1e-5, ln), d, 1e-5, ln, f"{M}x{K}x{N}")
+    say(f"[gemv] {M}x{K}x{N}: {w}")
+
+
+@pytest.mark.parametrize("act,param", [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f32"),
+                                       ("f16", "bf16")])
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+def test_storage_types(act, param, ln):
+    M, K, N = 4, 1024, 1032
+    d = _case(M, K, N, 77, ln, act=act, param=param)
+    compare(run(d, 1e-5, ln), reference(d, 1e-5, ln), d, 1e-5, ln, f"{act}/{param}")
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+def test_unaligned(ln):
+    """Operands one element past an aligned address take the element-wise path."""
+    M, K, N = 3, 512, 1024
+    d = _case(M, K, N, 5, ln)
+    compare(run(d, 1e-5, ln, offset=1), reference(d, 1e-5, ln), d, 1e-5, ln, "unaligned")
+
+
+def test_large_mean_layernorm():
+    """Rows with a mean 20 times their spread: the shifted sums and the
+    centred statistics keep the result to the bar."""
+    d = _case(4, 4096, 1024, 6, True, x_loc=20.0)
+    compare(run(d, 1e-5, True), reference(d, 1e-5, True), d, 1e-5, True, "mean 20")
+
+
+def test_deterministic_and_row_independent():
+    """Bitwise repeatable, and an output row does not depend on the other rows
+    of the batch (each row's statistics and sums are its own)."""
+    d = _case(4, 4096, 2048, 8, False)
+    a = run(d, 1e-5, False)
+    assert np.array_equal(a.view(np.uint16), run(d, 1e-5, False).view(np.uint16))
+    one = {k: (v[1:2] if k == "X" else v) for k, v in d.items()}
+    assert np.array_equal(a[1:2].view(np.uint16), run(one, 1e-5, False).view(np.uint16))
+
+
+def test_matches_separate_norm_then_matmul():
+    """The pages validate the fusion against the separate norm forward and a
+    GEMM: the same rms_scaled bound against our RMSNorm forward (fp16 rows)
+    followed by a float32 matmul."""
+    M, K, N = 4, 4096, 4096
+    d = _case(M, K, N, 9, False)
+    X, g, W = dev(d["X"]), dev(d["gamma"]), dev(d["W"])
+    Yn = torch.empty_like(X)
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    mn.mn_rmsnorm_forward(X, g, Yn, rstd, 1e-5)
+    sep = (Yn.float() @ W.float()).cpu().numpy().astype(np.float64)
+    fused = parity.as_f64(run(d, 1e-5, False))
+    rms = float(np.sqrt(np.mean((fused - sep) ** 2)) / np.sqrt(np.mean(sep ** 2)))
+    say(f"[gemv] fused vs separate rms_scaled {rms:.2e}")
+    assert rms <= 5e-3
+
+
+FULL = ["rms_gemv_4x4096x12288", "ln_gemv_4x4096x12288", "rms_gemv_1x4096x14336"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size(name):
+    w = workloads.WORKLOADS[name]
+    ln = w.kind == "ln_gemv"
+    say(f"[gemv] full {name}")
+    d = workloads.generate(w)
+    r = compare(run(d, w.eps, ln), reference(d, w.eps, ln), d, w.eps, ln, name)
+    say(f"[gemv] full {name}: {r}")

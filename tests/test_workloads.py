@@ -44,7 +44,8 @@ def test_shapes_and_dtypes():
         for spec in w.tensors:
             a = d[spec.name]
             assert a.dtype == np.float16 and a.flags.c_contiguous
-            want = (w.B, w.D) if spec.per_sample else (3, w.D) if spec.per_row else (w.D,)
+            want = ((w.D, w.Nout) if spec.matrix else (w.B, w.D) if spec.per_sample
+                    else (3, w.D) if spec.per_row else (w.D,))
             assert a.shape == want, (name, spec.name)
 
 

@@ -26,6 +26,9 @@ Recipe (fixed, so that every run sees the same bits):
   [N, D] one with B rows, in the activation storage type. The scalar
   parameters (Dynamic Tanh's alpha, PolyNorm's weights and bias) are fixed
   constants of the workload, not drawn.
+* The fused norm + GEMV workloads draw X as an [M, K] tensor (M = N rows,
+  K = D) and the weight W as a [K, Nout] tensor drawn like an [N, D] one with
+  K rows, N(0, 0.02^2), in the activation storage type.
 * The Llama-shape RMSNorm workload marks 1 % of its 4096 channels as outliers:
   41 channels drawn without replacement from ``default_rng(1)`` and sorted;
   those X columns are multiplied by 20 before rounding.
@@ -56,12 +59,13 @@ class TensorSpec:
     loc: float = 0.0
     scale: float = 1.0
     per_sample: bool = False   # shape [B, D] (the Modulated RMSNorm's scale and shift)
+    matrix: bool = False       # shape [D, Nout] (the fused GEMV's weight W)
 
 
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str              # "rms", "ln", "add", "dyt", "poly" or "mod"
+    kind: str              # "rms", "ln", "add", "dyt", "poly", "mod", "rms_gemv", "ln_gemv"
     N: int
     D: int
     eps: float
@@ -72,6 +76,7 @@ class Workload:
     note: str = ""
     B: int = 1             # "mod": samples (N / B rows each)
     scalars: Tuple[float, ...] = ()   # "dyt": (alpha,); "poly": (w1, w2, w3, b)
+    Nout: int = 0          # "*_gemv": output columns (N rows of X are the batch M, D is K)
 
     def outlier_channels(self) -> np.ndarray:
         if self.outlier_frac <= 0.0:
@@ -82,7 +87,7 @@ class Workload:
 
 
 def _spec(kind: str, x=(0.0, 1.0), dy=(0.0, 1.0), r=(0.0, 2.0), dh=(0.0, 0.01),
-          mod=(0.0, 0.1)):
+          mod=(0.0, 0.1), w=(0.0, 0.02)):
     """Tensor list in draw order for one kind of norm."""
     X = TensorSpec("X", True, *x)
     G = TensorSpec("gamma", False, 1.0, 0.1)
@@ -99,6 +104,11 @@ def _spec(kind: str, x=(0.0, 1.0), dy=(0.0, 1.0), r=(0.0, 2.0), dh=(0.0, 0.01),
     if kind == "mod":
         return (X, G, TensorSpec("scale", False, *mod, per_sample=True),
                 TensorSpec("shift", False, *mod, per_sample=True), DY)
+    W = TensorSpec("W", False, *w, matrix=True)
+    if kind == "rms_gemv":
+        return (X, G, W)
+    if kind == "ln_gemv":
+        return (X, G, B, W)
     raise ValueError(kind)
 
 
@@ -133,6 +143,15 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("mod_rms_16384x3072", "mod", 16384, 3072, 1e-6, _spec("mod"), B=8,
                  note="Modulated RMSNorm: 8 samples x 2048 tokens of width 3072 (a "
                       "conditioned-transformer block)"),
+        Workload("rms_gemv_4x4096x12288", "rms_gemv", 4, 4096, 1e-5, _spec("rms_gemv"),
+                 Nout=12288, note="decode step: RMSNorm of 4 tokens of width 4096 fused "
+                                  "into the fused Q/K/V projection (3 x 4096 columns)"),
+        Workload("ln_gemv_4x4096x12288", "ln_gemv", 4, 4096, 1e-5,
+                 _spec("ln_gemv", x=(0.5, 1.0)), Nout=12288,
+                 note="the same decode projection behind a LayerNorm, offset-mean X"),
+        Workload("rms_gemv_1x4096x14336", "rms_gemv", 1, 4096, 1e-5, _spec("rms_gemv"),
+                 Nout=14336, note="single-token decode: RMSNorm into an MLP up projection "
+                                  "(4096 -> 14336)"),
     )
 }
 
@@ -206,7 +225,10 @@ def generate(w: Workload, seed: int = 0, N: Optional[int] = None, act: str = "f1
     outliers = w.outlier_channels()
     out: Dict[str, np.ndarray] = {}
     for t, spec in enumerate(w.tensors):
-        if spec.per_sample:
+        if spec.matrix:
+            a = np.empty((w.D, w.Nout), dtype=STORAGE[act])
+            _fill_rows(seed, t, a, spec, np.zeros(0, np.int64), 1.0)
+        elif spec.per_sample:
             a = np.empty((w.B, w.D), dtype=STORAGE[act])
             _fill_rows(seed, t, a, spec, np.zeros(0, np.int64), 1.0)
         elif spec.per_row:
@@ -223,12 +245,15 @@ def generate(w: Workload, seed: int = 0, N: Optional[int] = None, act: str = "f1
 def random_case(kind: str, N: int, D: int, seed: int, x_loc: float = 0.0, x_scale: float = 1.0,
                 dy_scale: float = 1.0, r_scale: float = 2.0, dh_scale: float = 0.5,
                 act: str = "f16", param: Optional[str] = None, cot: Optional[str] = None,
-                B: int = 1, mod_scale: float = 0.1) -> Dict[str, np.ndarray]:
+                B: int = 1, mod_scale: float = 0.1, Nout: int = 0,
+                w_scale: float = 0.02) -> Dict[str, np.ndarray]:
     """Inputs for an arbitrary (kind, N, D) test case with the default recipe
-    (B samples for "mod"; the scalar parameters are not drawn)."""
+    (B samples for "mod", Nout output columns for "*_gemv"; the scalar
+    parameters are not drawn)."""
     w = Workload(f"case_{kind}_{N}x{D}", kind, N, D, 1e-5,
                  _spec(kind, x=(x_loc, x_scale), dy=(0.0, dy_scale), r=(0.0, r_scale),
-                       dh=(0.0, dh_scale), mod=(0.0, mod_scale)), B=B)
+                       dh=(0.0, dh_scale), mod=(0.0, mod_scale), w=(0.0, w_scale)), B=B,
+                 Nout=Nout)
     return generate(w, seed, act=act, param=param, cot=cot)
 
 
