@@ -644,7 +644,8 @@ def main():
         cpu = cpu_baseline(w, d, args.cpu_budget, (act, param, cot, dxt))
 
     line = {
-        "metric": "achieved HBM GB/s (% of peak) + rows/s for norm fwd+bwd, RMSNorm 16384x4096",
+        "metric": f"achieved HBM GB/s (% of peak) + rows/s for norm fwd+bwd, "
+                  f"{NORM_NAMES[kind]} {N}x{D}",
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
