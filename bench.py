@@ -40,7 +40,7 @@ SIZE = {"f16": 2, "bf16": 2, "f32": 4}
 
 
 def alg_bytes(kind: str, N: int, D: int, act: str = "f16", param: str = "f16",
-              cot: str = "f16", dxt: str = "f16", B: int = 1):
+              cot: str = "f16", dxt: str = "f16", B: int = 1, C: int = 0, G: int = 0):
     """Algorithmic bytes (each tensor read or written once) of the forward and
     the backward (row kernel and column reduce together): activations X, R,
     Y, H of `act`, gamma/beta of `param`, cotangents dY, dH of `cot`, dX of
@@ -62,6 +62,9 @@ def alg_bytes(kind: str, N: int, D: int, act: str = "f16", param: str = "f16",
     elif kind == "mod":
         fwd = 2 * a * nd + p * D + 2 * a * B * D + 4 * N      # + scale, shift [B][D]
         bwd = (a + c + o) * nd + (p + 4) * D + (a + 8) * B * D + 4 * N
+    elif kind == "gn":                                        # N samples of D = C * L values
+        fwd = 2 * a * nd + 2 * p * C + 8 * N * G              # X, gamma, beta -> Y, mean, rstd
+        bwd = (a + c + o) * nd + p * C + 8 * N * G + 8 * C    # -> dX, dgamma, dbeta
     else:
         fwd = 4 * a * nd + p * D + 4 * N                      # X, R -> H, Y
         bwd = (2 * a + 2 * c + o) * nd + (p + 4) * D + 4 * N  # X, R, dY, dH -> dX
@@ -157,7 +160,7 @@ def cpu_baseline(w, d, budget_s: float, types=("f16",) * 4):
     time budget is spent (at least once)."""
     import oracle
 
-    fwd_b, bwd_b = alg_bytes(w.kind, w.N, w.D, *types, B=w.B)
+    fwd_b, bwd_b = alg_bytes(w.kind, w.N, w.D, *types, B=w.B, C=w.channels, G=w.groups)
     rows = w.N
     X, g, dY = d["X"], d.get("gamma"), d["dY"]
     t0 = time.perf_counter()
@@ -172,6 +175,10 @@ def cpu_baseline(w, d, budget_s: float, types=("f16",) * 4):
         elif w.kind == "mod":
             oracle.modrms_forward(X, g, d["scale"], d["shift"], w.eps)
             oracle.modrms_backward(X, g, d["scale"], dY, w.eps)
+        elif w.kind == "gn":
+            shp = (w.N, w.channels, w.D // w.channels)
+            oracle.groupnorm_forward(X.reshape(shp), g, d["beta"], w.groups, w.eps)
+            oracle.groupnorm_backward(X.reshape(shp), g, dY.reshape(shp), w.groups, w.eps)
         elif w.kind == "rms":
             oracle.rmsnorm_forward(X, g, w.eps)
             oracle.rmsnorm_backward(X, g, dY, w.eps)
@@ -269,7 +276,8 @@ def pages_context(torch, mn):
 
 NORM_NAMES = {"rms": "RMSNorm", "ln": "LayerNorm", "add": "fused add + RMSNorm",
               "dyt": "Dynamic Tanh", "poly": "PolyNorm", "mod": "Modulated RMSNorm",
-              "rms_gemv": "fused RMSNorm + GEMV", "ln_gemv": "fused LayerNorm + GEMV"}
+              "rms_gemv": "fused RMSNorm + GEMV", "ln_gemv": "fused LayerNorm + GEMV",
+              "gn": "GroupNorm"}
 
 
 def bench_gemv(args, w, torch, mn, act, param):
@@ -356,11 +364,13 @@ def bench_gemv(args, w, torch, mn, act, param):
 
 
 def bench_other(args, w, torch, mn, act, param, dxt):
-    """Dynamic Tanh, PolyNorm or Modulated RMSNorm: one step is the forward of
-    one batch and the whole backward (row kernel and parameter reduction) of
-    another, with rotating buffer sets as for the training pair; events
-    bracket the forward and the backward call separately."""
+    """Dynamic Tanh, PolyNorm, Modulated RMSNorm or GroupNorm: one step is the
+    forward of one batch and the whole backward (row kernel and parameter
+    reduction) of another, with rotating buffer sets as for the training
+    pair; events bracket the forward and the backward call separately."""
     N, D, kind = w.N, w.D, w.kind
+    C, G = w.channels, w.groups
+    shp = (N, C, D // C) if kind == "gn" else (N, D)
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
     print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
     d = workloads.generate(w, act=act, param=param)
@@ -376,15 +386,24 @@ def bench_other(args, w, torch, mn, act, param, dxt):
     up = {k: upload(v) for k, v in d.items()}
     scal = torch.tensor(np.asarray(w.scalars, np.float32), device=dev)
     S = max(2, args.sets)
-    kcode = {"dyt": mn.MN_DYT, "poly": mn.MN_POLYNORM, "mod": mn.MN_MOD_RMSNORM}[kind]
     sets = []
     for s in range(S):
-        b = {"X": up["X"] if s == 0 else up["X"].clone(),
-             "dY": up["dY"] if s == 0 else up["dY"].clone(),
-             "Y": torch.empty(N, D, dtype=tdt[act], device=dev),
-             "dX": torch.empty(N, D, dtype=tdt[dxt], device=dev),
-             "ws": mn.new_workspace(kcode, N, D, dev, B=w.B)}
-        if kind == "dyt":
+        b = {"X": (up["X"] if s == 0 else up["X"].clone()).view(shp),
+             "dY": (up["dY"] if s == 0 else up["dY"].clone()).view(shp),
+             "Y": torch.empty(shp, dtype=tdt[act], device=dev),
+             "dX": torch.empty(shp, dtype=tdt[dxt], device=dev)}
+        if kind == "gn":
+            b["ws"] = torch.empty(mn.groupnorm_workspace_bytes(N, C) // 4, dtype=torch.float32,
+                                  device=dev)
+        else:
+            kcode = {"dyt": mn.MN_DYT, "poly": mn.MN_POLYNORM, "mod": mn.MN_MOD_RMSNORM}[kind]
+            b["ws"] = mn.new_workspace(kcode, N, D, dev, B=w.B)
+        if kind == "gn":
+            b.update(mean=torch.empty(N, G, dtype=torch.float32, device=dev),
+                     rstd=torch.empty(N, G, dtype=torch.float32, device=dev),
+                     dg=torch.empty(C, dtype=torch.float32, device=dev),
+                     db=torch.empty(C, dtype=torch.float32, device=dev))
+        elif kind == "dyt":
             b.update(da=torch.empty(1, dtype=torch.float32, device=dev),
                      dg=torch.empty(D, dtype=torch.float32, device=dev),
                      db=torch.empty(D, dtype=torch.float32, device=dev))
@@ -399,7 +418,10 @@ def bench_other(args, w, torch, mn, act, param, dxt):
         sets.append(b)
 
     def fwd(b):
-        if kind == "dyt":
+        if kind == "gn":
+            mn.mn_groupnorm_forward_ex(b["X"], up["gamma"], up["beta"], b["Y"], b["mean"],
+                                       b["rstd"], G, w.eps, stream)
+        elif kind == "dyt":
             mn.mn_dyt_forward_ex(b["X"], scal, up["gamma"], up["beta"], b["Y"], stream)
         elif kind == "poly":
             mn.mn_polynorm_forward_ex(b["X"], scal, b["Y"], b["rstd"], w.eps, stream)
@@ -408,7 +430,10 @@ def bench_other(args, w, torch, mn, act, param, dxt):
                                          b["rstd"], w.eps, stream)
 
     def bwd(b):
-        if kind == "dyt":
+        if kind == "gn":
+            mn.mn_groupnorm_backward_ex(b["X"], up["gamma"], b["mean"], b["rstd"], b["dY"],
+                                        b["dX"], b["dg"], b["db"], G, b["ws"], stream)
+        elif kind == "dyt":
             mn.mn_dyt_backward_ex(b["X"], scal, up["gamma"], b["dY"], b["dX"], b["da"], b["dg"],
                                   b["db"], b["ws"], stream)
         elif kind == "poly":
@@ -419,7 +444,7 @@ def bench_other(args, w, torch, mn, act, param, dxt):
                                           b["dX"], b["dg"], b["dsc"], b["dsh"], b["ws"], stream)
 
     K, W = args.steps, args.warmup
-    fwd_b, bwd_b = alg_bytes(kind, N, D, act, param, act, dxt, B=w.B)
+    fwd_b, bwd_b = alg_bytes(kind, N, D, act, param, act, dxt, B=w.B, C=C, G=G)
     for b in sets:
         fwd(b)
     for k in range(W):
@@ -445,13 +470,13 @@ def bench_other(args, w, torch, mn, act, param, dxt):
         cpu = cpu_baseline(w, d, args.cpu_budget, (act, param, act, dxt))
     line = {
         "metric": f"achieved HBM GB/s (% of peak) + rows/s for norm fwd+bwd, "
-                  f"{NORM_NAMES[kind]} {N}x{D}",
+                  f"{NORM_NAMES[kind]} {'x'.join(str(v) for v in shp)}",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "N": N, "D": D, "eps": w.eps, "io_dtype": act,
                    "param_dtype": param, "dx_dtype": dxt, "norm": NORM_NAMES[kind],
-                   "samples": w.B, "scalars": list(w.scalars),
+                   "samples": w.B, "scalars": list(w.scalars), "channels": C, "groups": G,
                    "step": "forward + backward (row kernel and parameter reduction)",
                    "buffer_sets": S},
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -512,7 +537,7 @@ def main():
 
     w = workloads.WORKLOADS[args.workload]
     N, D, kind = w.N, w.D, w.kind
-    if kind in ("dyt", "poly", "mod"):
+    if kind in ("dyt", "poly", "mod", "gn"):
         bench_other(args, w, torch, mn, act, param, dxt)
         return
     if kind in ("rms_gemv", "ln_gemv"):

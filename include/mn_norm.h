@@ -275,6 +275,37 @@ mn_status mn_mod_rmsnorm_backward_ex(const void* X, const void* gamma, const voi
 size_t mn_mod_rmsnorm_workspace_bytes(int64_t B, int64_t N, int64_t D);
 
 /* ---------------------------------------------------------------------------
+ * GroupNorm. [meTile] "Normalization" lists GroupNorm among the missing
+ * row-wise norms, with group/channel layouts and affine gradients; the
+ * formula is the published one (Wu and He, "Group Normalization"):
+ *   X, Y, dY, dX [N][C][L] (L positions per channel, contiguous), C = G * Cg;
+ *   the (sample n, group g) slice is the Cg * L contiguous values of
+ *   channels g*Cg .. g*Cg + Cg - 1 of sample n; mean and rstd [N][G] fp32
+ *   (population variance, eps inside the square root, as LayerNorm);
+ *   y = (x - mean) * rstd * gamma[c] + beta[c]  (gamma, beta [C] of `param`);
+ *   dgamma[c] = sum over n, l of dY * xhat, dbeta[c] = sum of dY (fp32 [C]).
+ * Storage: X, Y, dY in `act`; dX in `act` or MN_F32 (`dxt`). One workgroup
+ * holds a slice in registers (at most 1024 lanes; each channel row padded to
+ * its lane layout), which covers slices up to 65,536 values when L is a
+ * power of two from 64 to 16,384 (16-bit storage; 32,768 in binary32) and up
+ * to 16,384 values for L that is not a multiple of the 16-byte chunk or
+ * unaligned rows. Shapes that do not fit return MN_ERR_SHAPE, as do
+ * C % G != 0, zero sizes and L above 16,384. The backward workspace
+ * (mn_groupnorm_workspace_bytes(N, C), 16-byte aligned) holds per-sample
+ * fp32 partials of dgamma and dbeta, added in fixed order by a second kernel.
+ * ------------------------------------------------------------------------- */
+mn_status mn_groupnorm_forward_ex(const void* X, const void* gamma, const void* beta, void* Y,
+                                  float* mean, float* rstd, int64_t N, int64_t C, int64_t L,
+                                  int64_t G, float eps, mn_dtype act, mn_dtype param,
+                                  void* stream);
+mn_status mn_groupnorm_backward_ex(const void* X, const void* gamma, const float* mean,
+                                   const float* rstd, const void* dY, void* dX, float* dgamma,
+                                   float* dbeta, int64_t N, int64_t C, int64_t L, int64_t G,
+                                   mn_dtype act, mn_dtype param, mn_dtype dxt, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+size_t mn_groupnorm_workspace_bytes(int64_t N, int64_t C);
+
+/* ---------------------------------------------------------------------------
  * Fused normalization + GEMV for small inference batches. [tensorcore]
  * "Fused Norm + GEMV": Y = Norm(X, gamma[, beta]) @ W, the normalisation
  * applied in registers during the product instead of writing the normalised

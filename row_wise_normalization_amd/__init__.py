@@ -82,6 +82,9 @@ _SIGNATURES = {
     "mn_mod_rmsnorm_forward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F, _C, _C, _P],
     "mn_mod_rmsnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _C, _C,
                                    _C, _P, _SZ, _P],
+    "mn_groupnorm_forward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _C, _C, _P],
+    "mn_groupnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _C, _C,
+                                 _C, _P, _SZ, _P],
     "mn_fused_rmsnorm_gemv": [_P, _P, _P, _P, _I64, _I64, _I64, _F, _P, _SZ, _P],
     "mn_fused_layernorm_gemv": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _F, _P, _SZ, _P],
     "mn_fused_rmsnorm_gemv_ex": [_P, _P, _P, _P, _I64, _I64, _I64, _F, _C, _C, _P, _SZ, _P],
@@ -108,6 +111,8 @@ def lib() -> ctypes.CDLL:
     L.mn_norm_workspace_bytes.restype = _SZ
     L.mn_mod_rmsnorm_workspace_bytes.argtypes = [_I64, _I64, _I64]
     L.mn_mod_rmsnorm_workspace_bytes.restype = _SZ
+    L.mn_groupnorm_workspace_bytes.argtypes = [_I64, _I64]
+    L.mn_groupnorm_workspace_bytes.restype = _SZ
     L.mn_norm_gemv_workspace_bytes.argtypes = [_I64, _I64, _I64]
     L.mn_norm_gemv_workspace_bytes.restype = _SZ
     L.mn_status_string.argtypes = [ctypes.c_int]
@@ -428,6 +433,42 @@ def mn_mod_rmsnorm_backward_ex(X, gamma, scale, rstd, dY, dX, dgamma, dscale, ds
     _call("mn_mod_rmsnorm_backward_ex", _ptr(X), _ptr(gamma), _ptr(scale), _ptr(rstd), _ptr(dY),
           _ptr(dX), _ptr(dgamma), _ptr(dscale), _ptr(dshift), B, N, D, act, par,
           _code("dX", dX), _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def _ncl(X: torch.Tensor) -> Tuple[int, int, int]:
+    if X.dim() != 3:
+        raise ValueError(f"GroupNorm X must be [N, C, L], got shape {tuple(X.shape)}")
+    return int(X.shape[0]), int(X.shape[1]), int(X.shape[2])
+
+
+def mn_groupnorm_forward_ex(X, gamma, beta, Y, mean, rstd, groups: int, eps: float, stream=None):
+    """GroupNorm of X [N, C, L] over `groups` groups of C / groups channels."""
+    N, C, L = _ncl(X)
+    G = int(groups)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, C, L)); _check_t("gamma", gamma, gamma.dtype, (C,))
+    _check_t("beta", beta, gamma.dtype, (C,)); _check_t("Y", Y, X.dtype, (N, C, L))
+    _check_t("mean", mean, F32, (N, G)); _check_t("rstd", rstd, F32, (N, G))
+    _call("mn_groupnorm_forward_ex", _ptr(X), _ptr(gamma), _ptr(beta), _ptr(Y), _ptr(mean),
+          _ptr(rstd), N, C, L, G, float(eps), act, par, _stream(stream))
+
+
+def mn_groupnorm_backward_ex(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, groups: int, workspace,
+                             stream=None):
+    N, C, L = _ncl(X)
+    G = int(groups)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, C, L)); _check_t("gamma", gamma, gamma.dtype, (C,))
+    _check_t("mean", mean, F32, (N, G)); _check_t("rstd", rstd, F32, (N, G))
+    _check_t("dY", dY, X.dtype, (N, C, L)); _check_t("dX", dX, dX.dtype, (N, C, L))
+    _check_t("dgamma", dgamma, F32, (C,)); _check_t("dbeta", dbeta, F32, (C,))
+    _call("mn_groupnorm_backward_ex", _ptr(X), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dY),
+          _ptr(dX), _ptr(dgamma), _ptr(dbeta), N, C, L, G, act, par, _code("dX", dX),
+          _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def groupnorm_workspace_bytes(N: int, C: int) -> int:
+    return int(lib().mn_groupnorm_workspace_bytes(int(N), int(C)))
 
 
 def _ws_bytes(workspace: Optional[torch.Tensor]) -> int:

@@ -407,6 +407,118 @@ mn_status norm_gemv(bool ln, const void* X, const void* gamma, const void* beta,
     return device_status(mn::launch_gemv(st, ln, plan, a, as_stream(stream)));
 }
 
+// ---------------------------------------------------------------------------
+// GroupNorm.
+// ---------------------------------------------------------------------------
+
+int64_t gn_cp(int64_t C) { return (C + 3) / 4 * 4; }
+
+bool gn_shape_ok(int64_t N, int64_t C, int64_t L, int64_t G)
+{
+    if (N < 1 || C < 1 || L < 1 || G < 1 || C % G != 0) return false;
+    if (C > INT32_MAX / 4 || L > INT32_MAX) return false;
+    return N <= (INT64_MAX / 4) / C / L;
+}
+
+size_t gn_workspace_bytes(int64_t N, int64_t C)
+{
+    if (N < 1 || C < 1 || C > INT32_MAX / 4 || N > (INT64_MAX / 16) / gn_cp(C)) return 0;
+    return 2 * sizeof(float) * (size_t)N * (size_t)gn_cp(C);
+}
+
+bool gn_vec_ok(int st, int64_t L, const void* a, const void* b, const void* c = nullptr,
+               const void* d = nullptr)
+{
+    return chunks_fit(st, L) && aligned16(a) && aligned16(b) && aligned16(c) && aligned16(d);
+}
+
+mn_status groupnorm_forward(const void* X, const void* gamma, const void* beta, void* Y,
+                            float* mean, float* rstd, int64_t N, int64_t C, int64_t L, int64_t G,
+                            float eps, int st, int pdt, void* stream)
+{
+    if (!X || !gamma || !beta || !Y || !mean || !rstd) return MN_ERR_NULL;
+    if (!dtype_ok(st) || !dtype_ok(pdt)) return MN_ERR_DTYPE;
+    if (!gn_shape_ok(N, C, L, G)) return MN_ERR_SHAPE;
+    const bool vec = gn_vec_ok(st, L, X, Y);
+    mn::GnPlan plan;
+    if (!mn::plan_groupnorm(st, N, C, L, G, vec, plan)) return MN_ERR_SHAPE;
+    if (!eps_ok(eps)) return MN_ERR_EPS;
+    const size_t es = (size_t)mn::stor_bytes(st), ps = (size_t)mn::stor_bytes(pdt);
+    const size_t nx = (size_t)N * (size_t)C * (size_t)L;
+    const Span in[] = {span(X, nx * es), span(gamma, (size_t)C * ps), span(beta, (size_t)C * ps)};
+    const Span out[] = {span(Y, nx * es), span(mean, (size_t)(N * G) * 4),
+                        span(rstd, (size_t)(N * G) * 4)};
+    if (!alias_free(in, out)) return MN_ERR_ALIAS;
+    mn::GnArgs a{};
+    a.X = X;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.Y = Y;
+    a.mean = mean;
+    a.rstd = rstd;
+    a.C = (int32_t)C;
+    a.L = (int32_t)L;
+    a.G = (int32_t)G;
+    a.Cg = (int32_t)(C / G);
+    a.Cp = (int32_t)gn_cp(C);
+    a.pdt = pdt;
+    a.eps = eps;
+    return device_status(mn::launch_gn_fwd(st, plan, a, as_stream(stream)));
+}
+
+mn_status groupnorm_backward(const void* X, const void* gamma, const float* mean,
+                             const float* rstd, const void* dY, void* dX, float* dgamma,
+                             float* dbeta, int64_t N, int64_t C, int64_t L, int64_t G, int st,
+                             int pdt, int ot, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!X || !gamma || !mean || !rstd || !dY || !dX || !dgamma || !dbeta) return MN_ERR_NULL;
+    if (!dtype_ok(st) || !dtype_ok(pdt) || !(ot == st || ot == MN_F32)) return MN_ERR_DTYPE;
+    if (!gn_shape_ok(N, C, L, G)) return MN_ERR_SHAPE;
+    const bool vec = gn_vec_ok(st, L, X, dY, dX);
+    mn::GnPlan plan;
+    if (!mn::plan_groupnorm(st, N, C, L, G, vec, plan)) return MN_ERR_SHAPE;
+    const size_t need = gn_workspace_bytes(N, C);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
+    const size_t es = (size_t)mn::stor_bytes(st), ps = (size_t)mn::stor_bytes(pdt);
+    const size_t os = (size_t)mn::stor_bytes(ot);
+    const size_t nx = (size_t)N * (size_t)C * (size_t)L;
+    const Span in[] = {span(X, nx * es), span(gamma, (size_t)C * ps),
+                       span(mean, (size_t)(N * G) * 4), span(rstd, (size_t)(N * G) * 4),
+                       span(dY, nx * es)};
+    const Span out[] = {span(dX, nx * os), span(dgamma, (size_t)C * 4),
+                        span(dbeta, (size_t)C * 4), span(ws, need)};
+    if (!alias_free(in, out)) return MN_ERR_ALIAS;
+    mn::GnArgs a{};
+    a.X = X;
+    a.gamma = gamma;
+    a.dY = dY;
+    a.dX = dX;
+    a.mean = const_cast<float*>(mean);
+    a.rstd = const_cast<float*>(rstd);
+    a.part_g = static_cast<float*>(ws);
+    a.part_b = static_cast<float*>(ws) + N * gn_cp(C);
+    a.C = (int32_t)C;
+    a.L = (int32_t)L;
+    a.G = (int32_t)G;
+    a.Cg = (int32_t)(C / G);
+    a.Cp = (int32_t)gn_cp(C);
+    a.pdt = pdt;
+    hipStream_t s = as_stream(stream);
+    hipError_t e = mn::launch_gn_bwd(st, ot, plan, a, s);
+    if (e != hipSuccess) return device_status(e);
+    // dgamma, dbeta: the N per-sample partial rows, added in fixed order
+    mn::ReduceArgs r{};
+    r.part_g = a.part_g;
+    r.part_b = a.part_b;
+    r.dgamma = dgamma;
+    r.dbeta = dbeta;
+    r.P = N;
+    r.D = (int32_t)C;
+    r.Dp = a.Cp;
+    r.groups = 1;
+    return device_status(mn::launch_reduce(r, s));
+}
+
 mn_status backward(int kind, const BwdIn& b, const BwdOut& o, int64_t N, int64_t D,
                    const BwdTypes& t, void* ws, size_t ws_bytes, void* stream)
 {
@@ -699,6 +811,28 @@ mn_status mn_mod_rmsnorm_backward_ex(const void* X, const void* gamma, const voi
     return backward(mn::MOD, b, bwd_out(dgamma, dscale, dshift), N, D,
                     BwdTypes{act, param, act, dxt}, workspace, workspace_bytes, stream);
 }
+
+// --- GroupNorm ---------------------------------------------------------------
+
+mn_status mn_groupnorm_forward_ex(const void* X, const void* gamma, const void* beta, void* Y,
+                                  float* mean, float* rstd, int64_t N, int64_t C, int64_t L,
+                                  int64_t G, float eps, mn_dtype act, mn_dtype param,
+                                  void* stream)
+{
+    return groupnorm_forward(X, gamma, beta, Y, mean, rstd, N, C, L, G, eps, act, param, stream);
+}
+
+mn_status mn_groupnorm_backward_ex(const void* X, const void* gamma, const float* mean,
+                                   const float* rstd, const void* dY, void* dX, float* dgamma,
+                                   float* dbeta, int64_t N, int64_t C, int64_t L, int64_t G,
+                                   mn_dtype act, mn_dtype param, mn_dtype dxt, void* workspace,
+                                   size_t workspace_bytes, void* stream)
+{
+    return groupnorm_backward(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, N, C, L, G, act,
+                              param, dxt, workspace, workspace_bytes, stream);
+}
+
+size_t mn_groupnorm_workspace_bytes(int64_t N, int64_t C) { return gn_workspace_bytes(N, C); }
 
 // --- fused normalization + GEMV (inference) ---------------------------------
 

@@ -1,0 +1,66 @@
+// mn_gn_instances.hpp -- GroupNorm launchers, included by mn_gn_{f16,bf16,f32}.hip,
+// each of which instantiates them for its activation storage type.
+#pragma once
+
+#include "mn_groupnorm.hpp"
+#include "mn_tables.hpp"
+
+namespace mn {
+namespace {
+
+template <typename Kernel>
+hipError_t gn_launch(Kernel k, const GnPlan& p, const GnArgs& a, hipStream_t s)
+{
+    void* args[] = {const_cast<GnArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)p.grid),
+                           dim3((unsigned)p.block), args, 0, s);
+}
+
+}  // namespace
+
+// only the shapes within the register budget are instantiated
+#define MN_GN_FWD_U(SH, T, VEC, CPT, UL, U)                                                  \
+    case SH * 4 + UL:                                                                        \
+        if constexpr (gn_fits(ST, VEC, CPT, U))                                              \
+            return gn_launch(                                                                \
+                kern::gn_fwd_kernel<ST, T, st_vec(ST, VEC), st_cpt(ST, VEC, CPT), U>, p, a, s); \
+        else                                                                                 \
+            return hipErrorInvalidValue;
+#define MN_GN_BWD_U(SH, T, VEC, CPT, UL, U)                                                  \
+    case SH * 4 + UL:                                                                        \
+        if constexpr (gn_fits(ST, VEC, CPT, U))                                              \
+            return gn_launch(                                                                \
+                kern::gn_bwd_kernel<ST, OT, T, st_vec(ST, VEC), st_cpt(ST, VEC, CPT), U>, p, a, \
+                s);                                                                          \
+        else                                                                                 \
+            return hipErrorInvalidValue;
+#define MN_GN_US(M, SH, T, VEC, CPT) \
+    M(SH, T, VEC, CPT, 0, 1) M(SH, T, VEC, CPT, 1, 2) M(SH, T, VEC, CPT, 2, 4) M(SH, T, VEC, CPT, 3, 8)
+#define MN_GN_FWD_VEC(SH, T, CPT, MAXL) MN_GN_US(MN_GN_FWD_U, SH, T, 8, CPT)
+#define MN_GN_FWD_ELEM(SH, T, CPT, MAXL) MN_GN_US(MN_GN_FWD_U, SH, T, 1, CPT)
+#define MN_GN_BWD_VEC(SH, T, CPT, MAXL) MN_GN_US(MN_GN_BWD_U, SH, T, 8, CPT)
+#define MN_GN_BWD_ELEM(SH, T, CPT, MAXL) MN_GN_US(MN_GN_BWD_U, SH, T, 1, CPT)
+
+template <int ST>
+hipError_t launch_gn_fwd_t(const GnPlan& p, const GnArgs& a, hipStream_t s)
+{
+    switch (p.id) { MN_GN_VEC_SHAPES(MN_GN_FWD_VEC) MN_GN_ELEM_SHAPES(MN_GN_FWD_ELEM) }
+    return hipErrorInvalidValue;
+}
+
+template <int ST, int OT>
+hipError_t launch_gn_bwd_t(const GnPlan& p, const GnArgs& a, hipStream_t s)
+{
+    switch (p.id) { MN_GN_VEC_SHAPES(MN_GN_BWD_VEC) MN_GN_ELEM_SHAPES(MN_GN_BWD_ELEM) }
+    return hipErrorInvalidValue;
+}
+
+#undef MN_GN_FWD_U
+#undef MN_GN_BWD_U
+#undef MN_GN_US
+#undef MN_GN_FWD_VEC
+#undef MN_GN_FWD_ELEM
+#undef MN_GN_BWD_VEC
+#undef MN_GN_BWD_ELEM
+
+}  // namespace mn

@@ -118,6 +118,34 @@ hipError_t launch_backward_rows(int kind, int st, int ct, int ot, const BwdPlan&
                                 const BwdArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 
+// GroupNorm over X [N][C][L]: G groups of Cg = C / G consecutive channels;
+// one workgroup per (sample, group) slice of Cg rows of L values.
+struct GnArgs {
+    const void* X;           // [N][C][L], storage type of the launch
+    const void* gamma;       // [C], type pdt
+    const void* beta;        // [C], type pdt (forward)
+    const void* dY;          // [N][C][L] (backward)
+    void* Y;                 // forward output
+    void* dX;                // backward output, type OT of the launch
+    float* mean;             // [N][G]
+    float* rstd;             // [N][G]
+    float* part_g;           // [N][Cp] per-sample sums of dY * xhat per channel
+    float* part_b;           // [N][Cp] per-sample sums of dY per channel
+    int32_t C, L, G, Cg, Cp, pdt;
+    float eps;
+};
+
+struct GnPlan {
+    int id;                  // launch shape (T, VEC, CPT, U)
+    int32_t block;           // threads: a multiple of 64, at most 1024
+    int64_t grid;            // N * G
+};
+
+// false when the slice does not fit one workgroup's registers
+bool plan_groupnorm(int st, int64_t N, int64_t C, int64_t L, int64_t G, bool vec_ok, GnPlan& p);
+hipError_t launch_gn_fwd(int st, const GnPlan& p, const GnArgs& a, hipStream_t s);
+hipError_t launch_gn_bwd(int st, int ot, const GnPlan& p, const GnArgs& a, hipStream_t s);
+
 // Fused normalization + GEMV (inference): Y [M][N] = Norm(X [M][K]) @ W [K][N].
 constexpr int kGemvMaxKB = 512;  // rows of W per tile (LDS slice of the product rows)
 constexpr int kGemvMaxM = 8;

@@ -60,6 +60,8 @@ F = P(0xA0000000)
 G = P(0xC0000000)
 NULL = None
 S = None  # stream
+C_ = P(0x50000000)
+G_ = P(0x58000000)
 
 
 def rms_fwd(X=A, g=B, Y=C, r=Dp, N=16, D=64, eps=1e-5):
@@ -228,6 +230,36 @@ def test_other_norms_validation():
     assert mod_b(B=5) == 2
     assert mod_b(ws=wsm - 16) == 5
     assert mod_b(dxt=BF16) == 7
+
+
+def test_groupnorm_validation_and_workspace():
+    L_ = mn.lib()
+    f = ctypes.c_float(1e-5)
+    F16, BF16, F32 = mn.MN_F16, mn.MN_BF16, mn.MN_F32
+    # per-sample partial rows of dgamma and dbeta, C rounded up to 4
+    assert mn.groupnorm_workspace_bytes(32, 320) == 2 * 4 * 32 * 320
+    assert mn.groupnorm_workspace_bytes(3, 10) == 2 * 4 * 3 * 12
+    assert mn.groupnorm_workspace_bytes(0, 8) == 0 and mn.groupnorm_workspace_bytes(2, 0) == 0
+    N, C, L, G = 2, 8, 64, 2
+    mean, rstd = P(0x30000000), P(0x38000000)
+    fwd = lambda X=A, g=B, b=C_, Y=Dp, N=N, C=C, L=L, G=G, eps=f, act=F16, par=F16: \
+        L_.mn_groupnorm_forward_ex(X, g, b, Y, mean, rstd, N, C, L, G, eps, act, par, S)
+    assert fwd(b=NULL) == 1 and fwd(Y=NULL) == 1
+    assert fwd(G=3) == 2                        # 3 does not divide 8
+    assert fwd(G=0) == 2 and fwd(N=0) == 2 and fwd(L=0) == 2
+    assert fwd(L=16392) == 2                    # rows longer than 16,384
+    assert fwd(C=2560, L=1024, G=32) == 2       # an 81,920-value slice does not fit
+    assert fwd(eps=ctypes.c_float(-1.0)) == 3
+    assert fwd(Y=A) == 4                        # Y is X
+    assert fwd(act=7) == 7 and fwd(par=9) == 7
+    ws = mn.groupnorm_workspace_bytes(N, C)
+    W = P(0xE0000000)
+    bwd = lambda dxt=F16, act=F16, nb=ws, ws_=W, dX=E: L_.mn_groupnorm_backward_ex(
+        A, B, mean, rstd, Dp, dX, F, G_, N, C, L, G, act, F16, dxt, ws_, nb, S)
+    assert bwd(dxt=BF16) == 7                   # dX is the activation type or binary32
+    assert bwd(act=F32, dxt=F16) == 7
+    assert bwd(nb=ws - 4) == 5 and bwd(ws_=NULL) == 5
+    assert bwd(dX=Dp) == 4                      # dX is dY
 
 
 def test_fused_gemv_validation_and_workspace():

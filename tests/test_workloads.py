@@ -45,6 +45,7 @@ def test_shapes_and_dtypes():
             a = d[spec.name]
             assert a.dtype == np.float16 and a.flags.c_contiguous
             want = ((w.D, w.Nout) if spec.matrix else (w.B, w.D) if spec.per_sample
+                    else (w.channels,) if spec.per_channel
                     else (3, w.D) if spec.per_row else (w.D,))
             assert a.shape == want, (name, spec.name)
 

@@ -29,6 +29,8 @@ Recipe (fixed, so that every run sees the same bits):
 * The fused norm + GEMV workloads draw X as an [M, K] tensor (M = N rows,
   K = D) and the weight W as a [K, Nout] tensor drawn like an [N, D] one with
   K rows, N(0, 0.02^2), in the activation storage type.
+* GroupNorm draws X and dY as [N, C * L] tensors (one row per sample, viewed
+  as [N, C, L]) and gamma, beta as [C] vectors.
 * The Llama-shape RMSNorm workload marks 1 % of its 4096 channels as outliers:
   41 channels drawn without replacement from ``default_rng(1)`` and sorted;
   those X columns are multiplied by 20 before rounding.
@@ -60,6 +62,7 @@ class TensorSpec:
     scale: float = 1.0
     per_sample: bool = False   # shape [B, D] (the Modulated RMSNorm's scale and shift)
     matrix: bool = False       # shape [D, Nout] (the fused GEMV's weight W)
+    per_channel: bool = False  # shape [C] (GroupNorm's gamma and beta)
 
 
 @dataclass(frozen=True)
@@ -77,6 +80,8 @@ class Workload:
     B: int = 1             # "mod": samples (N / B rows each)
     scalars: Tuple[float, ...] = ()   # "dyt": (alpha,); "poly": (w1, w2, w3, b)
     Nout: int = 0          # "*_gemv": output columns (N rows of X are the batch M, D is K)
+    channels: int = 0      # "gn": C (rows of X are samples of C * L values, D = C * L)
+    groups: int = 0        # "gn": G
 
     def outlier_channels(self) -> np.ndarray:
         if self.outlier_frac <= 0.0:
@@ -104,6 +109,9 @@ def _spec(kind: str, x=(0.0, 1.0), dy=(0.0, 1.0), r=(0.0, 2.0), dh=(0.0, 0.01),
     if kind == "mod":
         return (X, G, TensorSpec("scale", False, *mod, per_sample=True),
                 TensorSpec("shift", False, *mod, per_sample=True), DY)
+    if kind == "gn":
+        return (X, TensorSpec("gamma", False, 1.0, 0.1, per_channel=True),
+                TensorSpec("beta", False, 0.0, 0.1, per_channel=True), DY)
     W = TensorSpec("W", False, *w, matrix=True)
     if kind == "rms_gemv":
         return (X, G, W)
@@ -143,6 +151,10 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("mod_rms_16384x3072", "mod", 16384, 3072, 1e-6, _spec("mod"), B=8,
                  note="Modulated RMSNorm: 8 samples x 2048 tokens of width 3072 (a "
                       "conditioned-transformer block)"),
+        Workload("gn_32x320x4096_g32", "gn", 32, 320 * 4096, 1e-5, _spec("gn", x=(0.5, 1.0)),
+                 channels=320, groups=32,
+                 note="GroupNorm of a diffusion U-Net's first stage: 32 images, 320 channels "
+                      "of 64 x 64 positions, 32 groups"),
         Workload("rms_gemv_4x4096x12288", "rms_gemv", 4, 4096, 1e-5, _spec("rms_gemv"),
                  Nout=12288, note="decode step: RMSNorm of 4 tokens of width 4096 fused "
                                   "into the fused Q/K/V projection (3 x 4096 columns)"),
@@ -225,7 +237,10 @@ def generate(w: Workload, seed: int = 0, N: Optional[int] = None, act: str = "f1
     outliers = w.outlier_channels()
     out: Dict[str, np.ndarray] = {}
     for t, spec in enumerate(w.tensors):
-        if spec.matrix:
+        if spec.per_channel:
+            z = np.random.default_rng([seed, t]).standard_normal(w.channels)
+            a = to_storage(spec.loc + spec.scale * z, param)
+        elif spec.matrix:
             a = np.empty((w.D, w.Nout), dtype=STORAGE[act])
             _fill_rows(seed, t, a, spec, np.zeros(0, np.int64), 1.0)
         elif spec.per_sample:
@@ -246,14 +261,15 @@ def random_case(kind: str, N: int, D: int, seed: int, x_loc: float = 0.0, x_scal
                 dy_scale: float = 1.0, r_scale: float = 2.0, dh_scale: float = 0.5,
                 act: str = "f16", param: Optional[str] = None, cot: Optional[str] = None,
                 B: int = 1, mod_scale: float = 0.1, Nout: int = 0,
-                w_scale: float = 0.02) -> Dict[str, np.ndarray]:
+                w_scale: float = 0.02, channels: int = 0,
+                groups: int = 0) -> Dict[str, np.ndarray]:
     """Inputs for an arbitrary (kind, N, D) test case with the default recipe
     (B samples for "mod", Nout output columns for "*_gemv"; the scalar
     parameters are not drawn)."""
     w = Workload(f"case_{kind}_{N}x{D}", kind, N, D, 1e-5,
                  _spec(kind, x=(x_loc, x_scale), dy=(0.0, dy_scale), r=(0.0, r_scale),
                        dh=(0.0, dh_scale), mod=(0.0, mod_scale), w=(0.0, w_scale)), B=B,
-                 Nout=Nout)
+                 Nout=Nout, channels=channels, groups=groups)
     return generate(w, seed, act=act, param=param, cot=cot)
 
 
