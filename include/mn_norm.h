@@ -287,9 +287,9 @@ size_t mn_mod_rmsnorm_workspace_bytes(int64_t B, int64_t N, int64_t D);
  * Storage: X, Y, dY in `act`; dX in `act` or MN_F32 (`dxt`). One workgroup
  * holds a slice in registers (at most 1024 lanes; each channel row padded to
  * its lane layout), which covers slices up to 65,536 values when L is a
- * power of two from 64 to 16,384 (16-bit storage; 32,768 in binary32) and up
- * to 16,384 values for L that is not a multiple of the 16-byte chunk or
- * unaligned rows. Shapes that do not fit return MN_ERR_SHAPE, as do
+ * power of two from 64 to 8,192 and 32,768 at L = 16,384 (16-bit storage;
+ * half as many in binary32), and up to 16,384 values for L that is not a
+ * multiple of the 16-byte chunk or unaligned rows. Shapes that do not fit return MN_ERR_SHAPE, as do
  * C % G != 0, zero sizes and L above 16,384. The backward workspace
  * (mn_groupnorm_workspace_bytes(N, C), 16-byte aligned) holds per-sample
  * fp32 partials of dgamma and dbeta, added in fixed order by a second kernel.

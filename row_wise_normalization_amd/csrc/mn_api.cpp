@@ -904,7 +904,7 @@ const char* mn_status_string(mn_status s)
     switch (s) {
     case MN_OK: return "ok";
     case MN_ERR_NULL: return "a required pointer is NULL";
-    case MN_ERR_SHAPE: return "shape out of range (N >= 1, 1 <= D <= 8192; samples divide N)";
+    case MN_ERR_SHAPE: return "shape out of range for this entry point (its declaration states the bounds)";
     case MN_ERR_EPS: return "eps must be a positive finite float";
     case MN_ERR_ALIAS: return "an output overlaps an input or another output";
     case MN_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";

@@ -20,22 +20,24 @@ hipError_t gn_launch(Kernel k, const GnPlan& p, const GnArgs& a, hipStream_t s)
 
 // only the shapes within the register budget are instantiated
 #define MN_GN_FWD_U(SH, T, VEC, CPT, UL, U)                                                  \
-    case SH * 4 + UL:                                                                        \
-        if constexpr (gn_fits(ST, VEC, CPT, U))                                              \
+    case SH * 8 + UL:                                                                        \
+        if constexpr (gn_fits(ST, VEC, T, CPT, U))                                              \
             return gn_launch(                                                                \
                 kern::gn_fwd_kernel<ST, T, st_vec(ST, VEC), st_cpt(ST, VEC, CPT), U>, p, a, s); \
         else                                                                                 \
             return hipErrorInvalidValue;
 #define MN_GN_BWD_U(SH, T, VEC, CPT, UL, U)                                                  \
-    case SH * 4 + UL:                                                                        \
-        if constexpr (gn_fits(ST, VEC, CPT, U))                                              \
+    case SH * 8 + UL:                                                                        \
+        if constexpr (gn_fits(ST, VEC, T, CPT, U))                                              \
             return gn_launch(                                                                \
                 kern::gn_bwd_kernel<ST, OT, T, st_vec(ST, VEC), st_cpt(ST, VEC, CPT), U>, p, a, \
                 s);                                                                          \
         else                                                                                 \
             return hipErrorInvalidValue;
-#define MN_GN_US(M, SH, T, VEC, CPT) \
-    M(SH, T, VEC, CPT, 0, 1) M(SH, T, VEC, CPT, 1, 2) M(SH, T, VEC, CPT, 2, 4) M(SH, T, VEC, CPT, 3, 8)
+#define MN_GN_US(M, SH, T, VEC, CPT)                                                      \
+    M(SH, T, VEC, CPT, 0, 1) M(SH, T, VEC, CPT, 1, 2) M(SH, T, VEC, CPT, 2, 3)            \
+    M(SH, T, VEC, CPT, 3, 4) M(SH, T, VEC, CPT, 4, 5) M(SH, T, VEC, CPT, 5, 6)            \
+    M(SH, T, VEC, CPT, 6, 7) M(SH, T, VEC, CPT, 7, 8)
 #define MN_GN_FWD_VEC(SH, T, CPT, MAXL) MN_GN_US(MN_GN_FWD_U, SH, T, 8, CPT)
 #define MN_GN_FWD_ELEM(SH, T, CPT, MAXL) MN_GN_US(MN_GN_FWD_U, SH, T, 1, CPT)
 #define MN_GN_BWD_VEC(SH, T, CPT, MAXL) MN_GN_US(MN_GN_BWD_U, SH, T, 8, CPT)

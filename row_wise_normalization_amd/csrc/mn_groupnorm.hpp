@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(kGnMaxBlock) gn_bwd_kernel(const GnArgs a)
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             t.x[u][k] = sload<ST, VEC, 2>(a.X, t.off(u, k));
-            dy[u][k] = sload<ST, VEC, 2>(a.dY, t.off(u, k));
+            dy[u][k] = sload<ST, VEC, 0>(a.dY, t.off(u, k));
         }
     float gam[U];
 #pragma unroll
@@ -201,10 +201,7 @@ __global__ void __launch_bounds__(kGnMaxBlock) gn_bwd_kernel(const GnArgs a)
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            launder(t.x[u][k]);
-            launder(dy[u][k]);
-        }
+        for (int k = 0; k < CPT; ++k) launder(t.x[u][k]);
     int phase = 0;
     row_sum<T, RMAX, 2 * U>(v, red, phase, gi, l);
 
@@ -235,17 +232,23 @@ __global__ void __launch_bounds__(kGnMaxBlock) gn_bwd_kernel(const GnArgs a)
     }
     const float fM = (float)a.Cg * (float)a.L;
     const float c1 = A / fM, c2 = B / fM;
+    // dY again (this workgroup read it moments ago: a cache hit), so that
+    // it does not hold registers across the reductions
+    HV dy2[U][CPT];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) dy2[u][k] = sload<ST, VEC, 0>(a.dY, t.off(u, k));
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             launder(t.x[u][k]);
-            launder(dy[u][k]);
             OV o;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 const float xh = (cget<ST, VEC>(t.x[u][k], e) - mu) * rs;
-                const float gg = cget<ST, VEC>(dy[u][k], e) * gam[u];
+                const float gg = cget<ST, VEC>(dy2[u][k], e) * gam[u];
                 cset<OT, VEC>(o, e, rs * __builtin_fmaf(-xh, c1, gg - c2));
             }
             if (t.ok(u, k)) cstore<OT, VEC, 1>(a.dX, t.off(u, k), o);
@@ -275,14 +278,19 @@ namespace mn {
     X(9, 64, 4, 256)         \
     X(10, 256, 8, 2048)      \
     X(11, 1024, 16, 16384)
-// Rows per row group U: 1, 2, 4 or 8, kept within the register budget: the
-// backward holds U * CPT chunks of X and of dY per lane (16-byte chunks: at
-// most 8 of each for 16-bit storage, 4 for binary32, whose chunks are twice
-// as many; element chunks: at most 16 of each). A launch id is
-// shape * 4 + log2(U).
-constexpr bool gn_fits(int st, int vec, int cpt, int u)
+// Rows per row group U: 1 to 8, kept within the register budget of a
+// 1024-lane workgroup (128 VGPRs): the backward holds U * CPT chunks of X per
+// lane across its reductions and as many of dY in its last pass. 16-byte
+// chunks: at most 10 for rows of up to 256 lanes, 8 for 512 lanes and 4 for
+// 1024 lanes (whose cross-wave row sums take more registers), halved for
+// binary32, whose chunks are twice as many; element chunks: at most 16. A
+// launch id is shape * 8 + U - 1.
+constexpr bool gn_fits(int st, int vec, int t, int cpt, int u)
 {
-    return vec == 1 ? u * cpt <= 16 : u * cpt <= (st == ST_F32 ? 4 : 8);
+    if (u > 8) return false;
+    if (vec == 1) return u * cpt <= 16;
+    const int lim = t >= 1024 ? 4 : t >= 512 ? 8 : 10;
+    return u * cpt <= (st == ST_F32 ? lim / 2 : lim);
 }
 
 template <int ST, int OT>

@@ -249,6 +249,7 @@ def test_groupnorm_validation_and_workspace():
     assert fwd(G=0) == 2 and fwd(N=0) == 2 and fwd(L=0) == 2
     assert fwd(L=16392) == 2                    # rows longer than 16,384
     assert fwd(C=2560, L=1024, G=32) == 2       # an 81,920-value slice does not fit
+    assert fwd(C=16, L=16384, G=4) == 2         # 65,536 values at L = 16,384 do not fit
     assert fwd(eps=ctypes.c_float(-1.0)) == 3
     assert fwd(Y=A) == 4                        # Y is X
     assert fwd(act=7) == 7 and fwd(par=9) == 7

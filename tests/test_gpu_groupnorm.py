@@ -16,9 +16,9 @@ pytestmark = pytest.mark.gpu
 # up to the 65,536-value limit
 SHAPES = [
     (2, 4, 8, 2), (3, 6, 64, 3), (4, 64, 256, 32), (2, 320, 1024, 32), (1, 128, 4096, 32),
-    (2, 64, 8192, 16), (1, 16, 16384, 4), (2, 1280, 64, 32), (1, 128, 1024, 2),
+    (2, 64, 8192, 16), (1, 8, 16384, 4), (2, 1280, 64, 32), (1, 128, 1024, 2),
     (3, 40, 1000, 4), (2, 32, 49, 8), (2, 12, 100, 3), (1, 7, 13, 7), (2, 8, 512, 1),
-    (2, 16, 2048, 16), (5, 96, 120, 6),
+    (2, 16, 2048, 16), (5, 96, 120, 6), (1, 64, 2048, 2),
 ]
 
 
