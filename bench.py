@@ -33,9 +33,26 @@ import numpy as np  # noqa: E402
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
-KERNEL_SRCS = [os.path.join(ROOT, "row_wise_normalization_amd", "csrc", f)
-               for f in ("mn_kernels.hpp", "mn_kernels.hip", "mn_tables.hpp", "mn_instances.hpp",
-                         "mn_inst_f16.hip", "mn_inst_bf16.hip", "mn_inst_f32.hip")]
+_CSRC = os.path.join(ROOT, "row_wise_normalization_amd", "csrc")
+# the kernel sources behind each kind's launches (the row-kernel templates,
+# launch tables and planner, and the kind's own instance files)
+_ROW = ("mn_kernels.hpp", "mn_kernels.hip", "mn_tables.hpp", "mn_instances.hpp")
+KERNEL_SRCS = {
+    "pair": _ROW + ("mn_inst_f16.hip", "mn_inst_bf16.hip", "mn_inst_f32.hip"),
+    "other": _ROW + ("mn_inst_ext_f16.hip", "mn_inst_ext_bf16.hip", "mn_inst_ext_f32.hip"),
+    "gn": ("mn_kernels.hpp", "mn_kernels.hip", "mn_tables.hpp", "mn_groupnorm.hpp",
+           "mn_gn_instances.hpp", "mn_gn_plan.hip", "mn_gn_f16.hip", "mn_gn_bf16.hip",
+           "mn_gn_f32.hip"),
+    "gemv": ("mn_kernels.hpp", "mn_gemv.hip"),
+}
+
+
+def _src_group(kind: str) -> str:
+    if kind in ("rms", "ln", "add"):
+        return "pair"
+    if kind in ("dyt", "poly", "mod"):
+        return "other"
+    return "gn" if kind == "gn" else "gemv"
 SIZE = {"f16": 2, "bf16": 2, "f32": 4}
 
 
@@ -79,11 +96,11 @@ def gemv_bytes(M: int, K: int, N: int, act: str = "f16", param: str = "f16", ln:
     return a * (M * K + K * N + M * N) + p * K * (2 if ln else 1)
 
 
-def kernel_hash() -> str:
-    """Hash of the kernel sources (templates and launch tables)."""
+def kernel_hash(kind: str = "rms") -> str:
+    """Hash of the kernel sources behind `kind`'s launches."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
+    for name in KERNEL_SRCS[_src_group(kind)]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -96,7 +113,7 @@ def measured_traffic(workload: str, kernel: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != kernel_hash():
+    if t.get("kernel_source_sha256_16") != kernel_hash(workloads.WORKLOADS[workload].kind):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -356,7 +373,10 @@ def bench_gemv(args, w, torch, mn, act, param):
         "kernels_ms": {"fused_call": round(call_ms, 5)},
         "roofline": {"bound": "hbm", "kernel": "fused call (GEMV + K-slice reduce)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (measured_traffic(w.name, "gemv")
+                                 if (act, param) == ("f16", "f16") else None),
+                     "traffic_kernel": "gemv"},
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
     }
@@ -486,7 +506,10 @@ def bench_other(args, w, torch, mn, act, param, dxt):
                        "backward": round(bwd_b / (bwd_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "kernel": "backward (row kernel + reduce)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (measured_traffic(w.name, "backward_rows")
+                                 if (act, param, dxt) == ("f16",) * 3 else None),
+                     "traffic_kernel": "backward_rows"},
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
     }
