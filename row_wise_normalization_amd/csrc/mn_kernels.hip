@@ -18,7 +18,7 @@ struct VariantRow {
 };
 
 #define MN_ROW(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) {{id, T, VEC, CPT, U, BLOCK}, MAXD},
-const VariantRow kFwdVec[6][10] = {{MN_FWD_RMS(MN_ROW)}, {MN_FWD_LN(MN_ROW)}, {MN_FWD_ADD(MN_ROW)},
+const VariantRow kFwdVec[6][11] = {{MN_FWD_RMS(MN_ROW)}, {MN_FWD_LN(MN_ROW)}, {MN_FWD_ADD(MN_ROW)},
                                   {MN_FWD_DYT(MN_ROW)}, {MN_FWD_POLY(MN_ROW)}, {MN_FWD_MOD(MN_ROW)}};
 const VariantRow kBwdVec[6][9] = {{MN_BWD_RMS(MN_ROW)}, {MN_BWD_LN(MN_ROW)}, {MN_BWD_ADD(MN_ROW)},
                                   {MN_BWD_DYT(MN_ROW)}, {MN_BWD_POLY(MN_ROW)}, {MN_BWD_MOD(MN_ROW)}};
@@ -29,9 +29,10 @@ const VariantRow kBwdGen[] = {MN_BWD_GEN(MN_ROW)};
 template <size_t K>
 Variant pick(const VariantRow (&t)[K], int32_t D)
 {
+    // tables shorter than the array end in zero rows (max_d 0), never picked
     for (size_t i = 0; i < K; ++i)
         if (D <= t[i].max_d) return t[i].v;
-    return t[K - 1].v;
+    return t[0].v;
 }
 
 template <typename Kernel, typename Args>

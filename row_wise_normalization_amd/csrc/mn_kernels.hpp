@@ -395,17 +395,23 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
     struct Tile {
         HV x[U][CPT];
         HV r[U][CPT];
+        HV sc[U][CPT], sh[U][CPT];   // MOD: the row's sample's scale and shift
     };
     auto load_tile = [&](Tile& t, int64_t base) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = base + u * RPB + g;
             const int64_t ro = row * (int64_t)D;
+            const int64_t so = (KIND == MOD) ? (row / a.S) * (int64_t)D : 0;
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 const bool ok = row < end && cval[k];
                 t.x[u][k] = ok ? sload<ST, VEC, NT>(a.X, ro + coff[k]) : czero<ST, VEC>();
                 if constexpr (KIND == ADD) t.r[u][k] = ok ? sload<ST, VEC, NT>(a.R, ro + coff[k]) : czero<ST, VEC>();
+                if constexpr (KIND == MOD) {
+                    t.sc[u][k] = ok ? sload<ST, VEC, 0>(a.scale, so + coff[k]) : czero<ST, VEC>();
+                    t.sh[u][k] = ok ? sload<ST, VEC, 0>(a.shift, so + coff[k]) : czero<ST, VEC>();
+                }
             }
         }
     };
@@ -515,15 +521,9 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
                 }
             }
             const int64_t ro = row[u] * (int64_t)D;
-            const int64_t so = (KIND == MOD) ? (row[u] / a.S) * (int64_t)D : 0;
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 if (!(rv[u] && cval[k])) continue;
-                HV sc, sh;
-                if constexpr (KIND == MOD) {
-                    sc = sload<ST, VEC, 0>(a.scale, so + coff[k]);
-                    sh = sload<ST, VEC, 0>(a.shift, so + coff[k]);
-                }
                 // POLY: y = b + v (w1 r1 + v (w2 r2 + v w3 r3)), Horner form
                 float k1 = 0.0f, k2 = 0.0f, k3 = 0.0f;
                 if constexpr (KIND == POLY) {
@@ -554,8 +554,9 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
                         o = __builtin_fmaf(v, __builtin_fmaf(v, __builtin_fmaf(v, k3, k2), k1),
                                            pw[3]);
                     } else if constexpr (KIND == MOD) {
-                        o = __builtin_fmaf(v * rs[u] * gam[k][e], 1.0f + cget<ST, VEC>(sc, e),
-                                           cget<ST, VEC>(sh, e));
+                        o = __builtin_fmaf(v * rs[u] * gam[k][e],
+                                           1.0f + cget<ST, VEC>(cur.sc[u][k], e),
+                                           cget<ST, VEC>(cur.sh[u][k], e));
                     } else {
                         o = v * rs[u] * gam[k][e];
                     }
