@@ -20,7 +20,7 @@ struct VariantRow {
 #define MN_ROW(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) {{id, T, VEC, CPT, U, BLOCK}, MAXD},
 const VariantRow kFwdVec[6][11] = {{MN_FWD_RMS(MN_ROW)}, {MN_FWD_LN(MN_ROW)}, {MN_FWD_ADD(MN_ROW)},
                                   {MN_FWD_DYT(MN_ROW)}, {MN_FWD_POLY(MN_ROW)}, {MN_FWD_MOD(MN_ROW)}};
-const VariantRow kBwdVec[6][9] = {{MN_BWD_RMS(MN_ROW)}, {MN_BWD_LN(MN_ROW)}, {MN_BWD_ADD(MN_ROW)},
+const VariantRow kBwdVec[6][10] = {{MN_BWD_RMS(MN_ROW)}, {MN_BWD_LN(MN_ROW)}, {MN_BWD_ADD(MN_ROW)},
                                   {MN_BWD_DYT(MN_ROW)}, {MN_BWD_POLY(MN_ROW)}, {MN_BWD_MOD(MN_ROW)}};
 const VariantRow kFwdGen[] = {MN_FWD_GEN(MN_ROW)};
 const VariantRow kBwdGen[] = {MN_BWD_GEN(MN_ROW)};

@@ -115,21 +115,12 @@ namespace mn {
     X(12, 320, 8, 2, 2, 320, 1, 3, 5120)     \
     X(7, 512, 8, 2, 1, 512, 1, 3, 8192)
 #define MN_BWD_ADD(X) MN_BWD_RMS(X)
-// The other norms keep two or three per-column accumulators, or three row
+// The other norms keep two or three per-column accumulators, or four row
 // sums, and (DYT) an inlined tanh per element: one row per group per step
 // keeps them within 128 VGPRs without spilling.
-#define MN_BWD_EXT(X)                        \
-    X(0, 8, 8, 1, 2, 256, 1, 3, 64)          \
-    X(1, 16, 8, 1, 2, 256, 1, 3, 128)        \
-    X(2, 32, 8, 1, 2, 256, 1, 3, 256)        \
-    X(3, 64, 8, 1, 1, 256, 1, 3, 512)        \
-    X(4, 128, 8, 1, 1, 512, 1, 3, 1024)      \
-    X(5, 256, 8, 1, 1, 512, 1, 3, 2048)      \
-    X(6, 512, 8, 1, 1, 512, 1, 3, 4096)      \
-    X(12, 640, 8, 1, 1, 640, 1, 3, 5120)     \
-    X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
 // PolyNorm reduces four sums per row for little arithmetic per element, so
-// it takes two chunks per lane (half the lanes per row) to amortise them.
+// it takes several chunks per lane (fewer lanes per row) to amortise them.
+// At 4096 columns 128 lanes x 4 chunks measured 13 % faster than 256 x 2.
 #define MN_BWD_POLY(X)                       \
     X(0, 8, 8, 1, 2, 256, 1, 3, 64)          \
     X(1, 16, 8, 1, 2, 256, 1, 3, 128)        \
@@ -137,11 +128,34 @@ namespace mn {
     X(3, 64, 8, 1, 1, 256, 1, 3, 512)        \
     X(4, 64, 8, 2, 1, 256, 1, 3, 1024)       \
     X(5, 128, 8, 2, 1, 512, 1, 3, 2048)      \
-    X(6, 256, 8, 2, 1, 512, 1, 3, 4096)      \
+    X(6, 128, 8, 4, 1, 512, 1, 3, 4096)      \
     X(12, 320, 8, 2, 1, 320, 1, 3, 5120)     \
     X(7, 512, 8, 2, 1, 512, 1, 3, 8192)
-#define MN_BWD_DYT(X) MN_BWD_EXT(X)
-#define MN_BWD_MOD(X) MN_BWD_EXT(X)
+// Dynamic Tanh at 4096 columns: 256 lanes x 2 chunks, two row groups per
+// workgroup (4 % faster than one 512-lane group).
+#define MN_BWD_DYT(X)                        \
+    X(0, 8, 8, 1, 2, 256, 1, 3, 64)          \
+    X(1, 16, 8, 1, 2, 256, 1, 3, 128)        \
+    X(2, 32, 8, 1, 2, 256, 1, 3, 256)        \
+    X(3, 64, 8, 1, 1, 256, 1, 3, 512)        \
+    X(4, 128, 8, 1, 1, 512, 1, 3, 1024)      \
+    X(5, 256, 8, 1, 1, 512, 1, 3, 2048)      \
+    X(6, 256, 8, 2, 1, 512, 1, 3, 4096)      \
+    X(12, 640, 8, 1, 1, 640, 1, 3, 5120)     \
+    X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
+// Modulated RMSNorm: an exact fit of 3072 columns, 128 lanes x 3 chunks
+// (19 % faster than the 4096-column row of 512 lanes).
+#define MN_BWD_MOD(X)                        \
+    X(0, 8, 8, 1, 2, 256, 1, 3, 64)          \
+    X(1, 16, 8, 1, 2, 256, 1, 3, 128)        \
+    X(2, 32, 8, 1, 2, 256, 1, 3, 256)        \
+    X(3, 64, 8, 1, 1, 256, 1, 3, 512)        \
+    X(4, 128, 8, 1, 1, 512, 1, 3, 1024)      \
+    X(5, 256, 8, 1, 1, 512, 1, 3, 2048)      \
+    X(14, 128, 8, 3, 1, 256, 1, 3, 3072)     \
+    X(6, 512, 8, 1, 1, 512, 1, 3, 4096)      \
+    X(12, 640, 8, 1, 1, 640, 1, 3, 5120)     \
+    X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
 #define MN_BWD_GEN(X)                        \
     X(8, 64, 1, 16, 1, 256, 1, 1, 1024)      \
     X(9, 256, 1, 16, 1, 256, 1, 1, 4096)     \
