@@ -32,10 +32,15 @@
 
 namespace mn {
 
-// tiles wanted per launch: about two workgroups per CU
-constexpr int64_t kGemvTileTarget = 512;
-// rows per wave load of the 16-byte path (tiles of 64 * 8 / 4 = 128 columns)
+// Tile shapes of the 16-byte path, from timing sweeps at 4096 x 12288 and
+// 4096 x 14336 (K x N): four rows of 128 columns per wave load, and tiles
+// halved along K until there are about two per CU; for one or two X rows and
+// wide W, one row of 512 columns per wave load in fewer, longer tiles (8 %
+// faster at M = 1, N = 14336; slower at M = 4, whose product rows need more
+// registers per column, and at N = 4096, which leaves too few tiles).
 constexpr int kGemvRpwVec = 4;
+constexpr int64_t kGemvTileTarget = 512;
+constexpr int64_t kGemvWideTileTarget = 192;
 
 namespace kern {
 
@@ -314,18 +319,27 @@ template <int ST, int VEC, bool LNF, int RPW>
 hipError_t launch_gemv_mm(int mm, dim3 grid, hipStream_t s, const GemvArgs& a)
 {
     const dim3 block(kern::kGemvBlock);
+    // the wide 16-byte tiles serve one or two X rows only
+    constexpr bool ALL = !(VEC == 8 && RPW == 1);
     switch (mm) {
     case 1: return launch_k(kern::gemv_kernel<ST, VEC, 1, LNF, RPW, 8>, grid, block, s, a);
     case 2: return launch_k(kern::gemv_kernel<ST, VEC, 2, LNF, RPW, 8>, grid, block, s, a);
-    case 4: return launch_k(kern::gemv_kernel<ST, VEC, 4, LNF, RPW, 8>, grid, block, s, a);
-    case 8: return launch_k(kern::gemv_kernel<ST, VEC, 8, LNF, RPW, 4>, grid, block, s, a);
+    case 4:
+        if constexpr (ALL) return launch_k(kern::gemv_kernel<ST, VEC, 4, LNF, RPW, 8>, grid, block, s, a);
+        break;
+    case 8:
+        if constexpr (ALL) return launch_k(kern::gemv_kernel<ST, VEC, 8, LNF, RPW, 4>, grid, block, s, a);
+        break;
     }
     return hipErrorInvalidValue;
 }
 
 template <int ST>
-hipError_t launch_gemv_st(bool ln, bool vec, int mm, dim3 grid, hipStream_t s, const GemvArgs& a)
+hipError_t launch_gemv_st(bool ln, bool vec, int rpw, int mm, dim3 grid, hipStream_t s,
+                          const GemvArgs& a)
 {
+    if (vec && rpw == 1) return ln ? launch_gemv_mm<ST, 8, true, 1>(mm, grid, s, a)
+                                   : launch_gemv_mm<ST, 8, false, 1>(mm, grid, s, a);
     if (vec) return ln ? launch_gemv_mm<ST, 8, true, kGemvRpwVec>(mm, grid, s, a)
                        : launch_gemv_mm<ST, 8, false, kGemvRpwVec>(mm, grid, s, a);
     return ln ? launch_gemv_mm<ST, 1, true, 1>(mm, grid, s, a)
@@ -338,17 +352,21 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, bool vec_ok)
 {
     GemvPlan p;
     p.vec = vec_ok;
-    const int64_t cols = vec_ok ? 64 * 8 / kGemvRpwVec : 64;
+    p.MM = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+    const bool wide = vec_ok && p.MM <= 2 &&
+                      ((N + 511) / 512) * ((K + kGemvMaxKB - 1) / kGemvMaxKB) >= kGemvWideTileTarget;
+    p.rpw = vec_ok && !wide ? kGemvRpwVec : 1;
+    const int64_t cols = (vec_ok ? 64 * 8 : 64) / p.rpw;
+    const int64_t target = wide ? kGemvWideTileTarget : kGemvTileTarget;
     p.NB = (int32_t)((N + cols - 1) / cols);
     // One tile per workgroup. Slices of K are halved from the LDS maximum
     // until there are enough tiles to keep every CU busy (each slice adds
     // rows of fp32 partials to write and read back), down to 64 rows.
     int64_t KB = kGemvMaxKB;
-    while (KB > 64 && (int64_t)p.NB * ((K + KB - 1) / KB) < kGemvTileTarget) KB /= 2;
+    while (KB > 64 && (int64_t)p.NB * ((K + KB - 1) / KB) < target) KB /= 2;
     p.KB = (int32_t)KB;
     p.S = (int32_t)((K + KB - 1) / KB);
     p.grid = M + (int64_t)p.NB * p.S;
-    p.MM = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
     return p;
 }
 
@@ -357,8 +375,8 @@ hipError_t launch_gemv(int st, bool ln, const GemvPlan& p, const GemvArgs& a, hi
     const dim3 grid((unsigned)p.grid);
     hipError_t e = hipErrorInvalidValue;
     switch (st) {
-    case ST_F16: e = launch_gemv_st<ST_F16>(ln, p.vec, p.MM, grid, s, a); break;
-    case ST_BF16: e = launch_gemv_st<ST_BF16>(ln, p.vec, p.MM, grid, s, a); break;
+    case ST_F16: e = launch_gemv_st<ST_F16>(ln, p.vec, p.rpw, p.MM, grid, s, a); break;
+    case ST_BF16: e = launch_gemv_st<ST_BF16>(ln, p.vec, p.rpw, p.MM, grid, s, a); break;
     }
     if (e != hipSuccess) return e;
     const int64_t MN = (int64_t)a.M * a.N;

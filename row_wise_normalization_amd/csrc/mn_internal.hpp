@@ -169,6 +169,7 @@ struct GemvArgs {
 struct GemvPlan {
     bool vec;                // 16-byte W loads (N % 8 == 0, aligned)
     int32_t MM;              // rows instantiated: 1, 2, 4 or 8 >= M
+    int32_t rpw;             // W rows per wave load (tile columns 64 * VEC / rpw)
     int32_t NB, KB, S;
     int64_t grid;
 };

@@ -269,8 +269,9 @@ def test_fused_gemv_validation_and_workspace():
     F16, BF16, F32 = mn.MN_F16, mn.MN_BF16, mn.MN_F32
     # 64 floats of row statistics, then S slices of M + 2 fp32 partial rows;
     # one tile per workgroup, K slices halve from 512 rows until there are 512
-    # tiles or the slices reach 64 rows; S is the larger of the 16-byte path
-    # (128-column tiles) and the element-wise path (64-column tiles)
+    # tiles (192 for the wide 512-column tiles of one or two X rows) or the
+    # slices reach 64 rows; S is the larger of the 16-byte path (128-column
+    # or wide tiles) and the element-wise path (64-column tiles)
     ws = lambda S, M, N: 4 * (64 + S * (M + 2) * N)
     assert mn.norm_gemv_workspace_bytes(4, 4096, 4096) == ws(16, 4, 4096)
     assert mn.norm_gemv_workspace_bytes(1, 14336, 4096) == ws(8, 1, 14336)

@@ -14,8 +14,11 @@ from gpu_gemv import case as _case, compare, reference, run
 pytestmark = pytest.mark.gpu
 
 
+# the last two take the wide tiles of one or two X rows (a ragged last tile,
+# and K not a multiple of the slice)
 SHAPES = [(1, 1, 1), (1, 64, 8), (2, 257, 130), (3, 1000, 1000), (4, 4096, 4096),
-          (5, 2048, 520), (8, 1024, 2056), (1, 3000, 7), (4, 300, 4104), (6, 8192, 512)]
+          (5, 2048, 520), (8, 1024, 2056), (1, 3000, 7), (4, 300, 4104), (6, 8192, 512),
+          (2, 4096, 12296), (1, 5000, 16384)]
 
 
 @pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
