@@ -19,6 +19,7 @@ SHAPES = [
     (2, 64, 8192, 16), (1, 8, 16384, 4), (2, 1280, 64, 32), (1, 128, 1024, 2),
     (3, 40, 1000, 4), (2, 32, 49, 8), (2, 12, 100, 3), (1, 7, 13, 7), (2, 8, 512, 1),
     (2, 16, 2048, 16), (5, 96, 120, 6), (1, 64, 2048, 2),
+    (3, 1, 1, 1), (2, 3, 1, 3), (4, 2, 8, 1),   # one-value slices, L = 1, the smallest vector row
 ]
 
 
