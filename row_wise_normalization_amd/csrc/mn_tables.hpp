@@ -26,9 +26,12 @@ namespace mn {
 // Rows 12 and 13 fit two common widths between the powers of two exactly
 // (5120 columns, and 6144 in the forward: row groups of 10 and 12 waves,
 // one workgroup per row group); they measured 2-12 % faster there than the
-// next power-of-two row. At 3072 columns, and for the 6144-column backward,
-// exact-fit rows measured slower than the next power-of-two row (whose idle
-// lanes cost no bandwidth), so those widths keep it.
+// next power-of-two row. At 3072 columns the backward takes an exact fit
+// with several chunks per lane (row 14: 192 lanes x 2 chunks for RMSNorm,
+// 128 lanes x 3 chunks for LayerNorm; 20 % and 8 % faster than the
+// 4096-column rows), while one chunk per lane over 384 lanes measured slower
+// than the 4096-column row; the forward keeps the 4096-column row there (the
+// exact fits were within 2 %), and the 6144-column backward the 8192 one.
 // Ids are unique within a kind; 8..10 are the element-wise variants (any D,
 // any alignment) shared by all kinds. Each row is instantiated for every
 // storage combination (binary32 activations: see st_vec / st_cpt below).
@@ -101,6 +104,7 @@ namespace mn {
     X(3, 64, 8, 1, 2, 256, 1, 3, 512)        \
     X(4, 128, 8, 1, 2, 512, 1, 3, 1024)      \
     X(5, 256, 8, 1, 2, 512, 1, 3, 2048)      \
+    X(14, 192, 8, 2, 1, 384, 1, 3, 3072)     \
     X(6, 512, 8, 1, 2, 512, 1, 3, 4096)      \
     X(12, 640, 8, 1, 2, 640, 1, 3, 5120)     \
     X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
@@ -111,6 +115,7 @@ namespace mn {
     X(3, 64, 8, 1, 2, 256, 1, 3, 512)        \
     X(4, 64, 8, 2, 2, 256, 1, 3, 1024)       \
     X(5, 128, 8, 2, 2, 512, 1, 3, 2048)      \
+    X(14, 128, 8, 3, 1, 256, 1, 3, 3072)     \
     X(6, 256, 8, 2, 2, 512, 1, 3, 4096)      \
     X(12, 320, 8, 2, 2, 320, 1, 3, 5120)     \
     X(7, 512, 8, 2, 1, 512, 1, 3, 8192)
