@@ -26,12 +26,15 @@ namespace mn {
 // Rows 12 and 13 fit two common widths between the powers of two exactly
 // (5120 columns, and 6144 in the forward: row groups of 10 and 12 waves,
 // one workgroup per row group); they measured 2-12 % faster there than the
-// next power-of-two row. At 3072 columns the backward takes an exact fit
-// with several chunks per lane (row 14: 192 lanes x 2 chunks for RMSNorm,
-// 128 lanes x 3 chunks for LayerNorm; 20 % and 8 % faster than the
-// 4096-column rows), while one chunk per lane over 384 lanes measured slower
-// than the 4096-column row; the forward keeps the 4096-column row there (the
-// exact fits were within 2 %), and the 6144-column backward the 8192 one.
+// next power-of-two row. Backward shapes away from 4096 columns come from a
+// sweep at 64 M elements per call: at 3072 columns exact fits with several
+// chunks per lane (RMSNorm 192 lanes x 2, LayerNorm 128 x 3; 20 % and 8 %
+// faster than the 4096-column rows, where one chunk over 384 lanes was
+// slower), at 5120 one row per group (RMSNorm, 7 %) and 128 lanes x 5 chunks
+// (LayerNorm, 24 %), for the LayerNorm at 2048 and 8192 one row per group in
+// larger workgroups (3 % and 7 %); the 6144-column backward keeps the 8192
+// row (exact fits within 2.5 %). The forward keeps the power-of-two rows at
+// 3072 (exact fits within 2 %).
 // Ids are unique within a kind; 8..10 are the element-wise variants (any D,
 // any alignment) shared by all kinds. Each row is instantiated for every
 // storage combination (binary32 activations: see st_vec / st_cpt below).
@@ -106,7 +109,7 @@ namespace mn {
     X(5, 256, 8, 1, 2, 512, 1, 3, 2048)      \
     X(14, 192, 8, 2, 1, 384, 1, 3, 3072)     \
     X(6, 512, 8, 1, 2, 512, 1, 3, 4096)      \
-    X(12, 640, 8, 1, 2, 640, 1, 3, 5120)     \
+    X(12, 640, 8, 1, 1, 640, 1, 3, 5120)     \
     X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
 #define MN_BWD_LN(X)                         \
     X(0, 8, 8, 1, 4, 256, 1, 3, 64)          \
@@ -114,11 +117,11 @@ namespace mn {
     X(2, 32, 8, 1, 4, 256, 1, 3, 256)        \
     X(3, 64, 8, 1, 2, 256, 1, 3, 512)        \
     X(4, 64, 8, 2, 2, 256, 1, 3, 1024)       \
-    X(5, 128, 8, 2, 2, 512, 1, 3, 2048)      \
+    X(5, 128, 8, 2, 1, 512, 1, 3, 2048)      \
     X(14, 128, 8, 3, 1, 256, 1, 3, 3072)     \
     X(6, 256, 8, 2, 2, 512, 1, 3, 4096)      \
-    X(12, 320, 8, 2, 2, 320, 1, 3, 5120)     \
-    X(7, 512, 8, 2, 1, 512, 1, 3, 8192)
+    X(12, 128, 8, 5, 1, 256, 1, 3, 5120)     \
+    X(7, 512, 8, 2, 1, 1024, 1, 3, 8192)
 #define MN_BWD_ADD(X) MN_BWD_RMS(X)
 // The other norms keep two or three per-column accumulators, or four row
 // sums, and (DYT) an inlined tanh per element: one row per group per step
