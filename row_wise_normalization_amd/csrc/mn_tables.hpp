@@ -24,17 +24,19 @@ namespace mn {
 //     inputs non-temporal loads (NT bit 1), except the LayerNorm forward,
 //     which measured slower with non-temporal loads.
 // Rows 12 and 13 fit two common widths between the powers of two exactly
-// (5120 columns, and 6144 in the forward: row groups of 10 and 12 waves,
-// one workgroup per row group); they measured 2-12 % faster there than the
-// next power-of-two row. Backward shapes away from 4096 columns come from a
+// (5120 columns, and 6144 in the forward), faster there than the next
+// power-of-two row. Backward shapes away from 4096 columns come from a
 // sweep at 64 M elements per call: at 3072 columns exact fits with several
 // chunks per lane (RMSNorm 192 lanes x 2, LayerNorm 128 x 3; 20 % and 8 %
 // faster than the 4096-column rows, where one chunk over 384 lanes was
 // slower), at 5120 one row per group (RMSNorm, 7 %) and 128 lanes x 5 chunks
 // (LayerNorm, 24 %), for the LayerNorm at 2048 and 8192 one row per group in
 // larger workgroups (3 % and 7 %); the 6144-column backward keeps the 8192
-// row (exact fits within 2.5 %). The forward keeps the power-of-two rows at
-// 3072 (exact fits within 2 %).
+// row (exact fits within 2.5 %). The forward likewise prefers fewer lanes
+// per row with more chunks per lane away from 4096 columns (4 to 8 waves per
+// workgroup, one or two rows per group): 6-29 % faster than rows of 640 to
+// 1024 lanes at 2048, 5120, 6144 and 8192 columns; it keeps the power-of-two
+// rows at 3072 (exact fits within 2 %).
 // Ids are unique within a kind; 8..10 are the element-wise variants (any D,
 // any alignment) shared by all kinds. Each row is instantiated for every
 // storage combination (binary32 activations: see st_vec / st_cpt below).
@@ -46,23 +48,36 @@ namespace mn {
     X(2, 32, 8, 1, 2, 256, 0, 3, 256)        \
     X(3, 64, 8, 1, 2, 256, 0, 3, 512)        \
     X(4, 128, 8, 1, 1, 256, 0, 3, 1024)      \
-    X(5, 256, 8, 1, 1, 256, 0, 3, 2048)      \
+    X(5, 256, 8, 1, 2, 256, 0, 3, 2048)      \
     X(6, 256, 8, 2, 1, 256, 0, 3, 4096)      \
-    X(12, 640, 8, 1, 1, 640, 0, 3, 5120)     \
-    X(13, 768, 8, 1, 1, 768, 0, 3, 6144)     \
-    X(7, 1024, 8, 1, 1, 1024, 0, 3, 8192)
+    X(12, 320, 8, 2, 1, 320, 0, 3, 5120)     \
+    X(13, 384, 8, 2, 1, 384, 0, 3, 6144)     \
+    X(7, 256, 8, 4, 1, 256, 0, 3, 8192)
 #define MN_FWD_LN(X)                         \
     X(0, 8, 8, 1, 4, 256, 0, 1, 64)          \
     X(1, 16, 8, 1, 2, 256, 0, 1, 128)        \
     X(2, 32, 8, 1, 2, 256, 0, 1, 256)        \
     X(3, 64, 8, 1, 2, 256, 0, 1, 512)        \
     X(4, 128, 8, 1, 1, 256, 0, 1, 1024)      \
-    X(5, 256, 8, 1, 1, 256, 0, 1, 2048)      \
+    X(5, 64, 8, 4, 1, 256, 0, 1, 2048)      \
     X(6, 256, 8, 2, 2, 256, 0, 1, 4096)      \
-    X(12, 640, 8, 1, 1, 640, 0, 1, 5120)     \
-    X(13, 768, 8, 1, 1, 768, 0, 1, 6144)     \
-    X(7, 1024, 8, 1, 1, 1024, 0, 1, 8192)
-#define MN_FWD_ADD(X) MN_FWD_RMS(X)
+    X(12, 128, 8, 5, 1, 256, 0, 1, 5120)     \
+    X(13, 256, 8, 3, 1, 256, 0, 1, 6144)     \
+    X(7, 256, 8, 4, 1, 256, 0, 1, 8192)
+// The fused add (two inputs and two outputs per element) keeps rows of up to
+// 1024 lanes away from 4096 columns: at 8192 the 256-lane row measured 4 %
+// slower than the 1024-lane one.
+#define MN_FWD_ADD(X)                        \
+    X(0, 8, 8, 1, 4, 256, 0, 3, 64)          \
+    X(1, 16, 8, 1, 2, 256, 0, 3, 128)        \
+    X(2, 32, 8, 1, 2, 256, 0, 3, 256)        \
+    X(3, 64, 8, 1, 2, 256, 0, 3, 512)        \
+    X(4, 128, 8, 1, 1, 256, 0, 3, 1024)      \
+    X(5, 256, 8, 1, 1, 256, 0, 3, 2048)      \
+    X(6, 256, 8, 2, 1, 256, 0, 3, 4096)      \
+    X(12, 640, 8, 1, 1, 640, 0, 3, 5120)     \
+    X(13, 768, 8, 1, 1, 768, 0, 3, 6144)     \
+    X(7, 1024, 8, 1, 1, 1024, 0, 3, 8192)
 // The other norms. PolyNorm (three sums per row) takes the LayerNorm shapes.
 // Dynamic Tanh (two parameter vectors, no reduction) and Modulated RMSNorm
 // (the sample's scale and shift rows with each tile) take the RMSNorm shapes
@@ -77,11 +92,11 @@ namespace mn {
     X(2, 32, 8, 1, 2, 256, 0, 3, 256)        \
     X(3, 64, 8, 1, 2, 256, 0, 3, 512)        \
     X(4, 128, 8, 1, 1, 256, 0, 3, 1024)      \
-    X(5, 256, 8, 1, 1, 256, 0, 3, 2048)      \
+    X(5, 256, 8, 1, 2, 256, 0, 3, 2048)      \
     X(6, 512, 8, 1, 2, 512, 0, 3, 4096)      \
-    X(12, 640, 8, 1, 1, 640, 0, 3, 5120)     \
-    X(13, 768, 8, 1, 1, 768, 0, 3, 6144)     \
-    X(7, 1024, 8, 1, 1, 1024, 0, 3, 8192)
+    X(12, 320, 8, 2, 1, 320, 0, 3, 5120)     \
+    X(13, 384, 8, 2, 1, 384, 0, 3, 6144)     \
+    X(7, 256, 8, 4, 1, 256, 0, 3, 8192)
 #define MN_FWD_POLY(X) MN_FWD_LN(X)
 #define MN_FWD_MOD(X)                        \
     X(0, 8, 8, 1, 4, 256, 0, 3, 64)          \
@@ -89,12 +104,12 @@ namespace mn {
     X(2, 32, 8, 1, 2, 256, 0, 3, 256)        \
     X(3, 64, 8, 1, 2, 256, 0, 3, 512)        \
     X(4, 128, 8, 1, 1, 256, 0, 3, 1024)      \
-    X(5, 256, 8, 1, 1, 256, 0, 3, 2048)      \
+    X(5, 256, 8, 1, 2, 256, 0, 3, 2048)      \
     X(14, 128, 8, 3, 2, 256, 0, 3, 3072)     \
     X(6, 256, 8, 2, 1, 256, 0, 3, 4096)      \
-    X(12, 640, 8, 1, 1, 640, 0, 3, 5120)     \
-    X(13, 768, 8, 1, 1, 768, 0, 3, 6144)     \
-    X(7, 1024, 8, 1, 1, 1024, 0, 3, 8192)
+    X(12, 320, 8, 2, 1, 320, 0, 3, 5120)     \
+    X(13, 384, 8, 2, 1, 384, 0, 3, 6144)     \
+    X(7, 256, 8, 4, 1, 256, 0, 3, 8192)
 #define MN_FWD_GEN(X)                        \
     X(8, 64, 1, 16, 1, 256, 0, 1, 1024)      \
     X(9, 256, 1, 16, 1, 256, 0, 1, 4096)     \
