@@ -35,8 +35,10 @@ namespace mn {
 // row (exact fits within 2.5 %). The forward likewise prefers fewer lanes
 // per row with more chunks per lane away from 4096 columns (4 to 8 waves per
 // workgroup, one or two rows per group): 6-29 % faster than rows of 640 to
-// 1024 lanes at 2048, 5120, 6144 and 8192 columns; it keeps the power-of-two
-// rows at 3072 (exact fits within 2 %).
+// 1024 lanes at 2048, 5120, 6144 and 8192 columns, and 32 lanes x 4 chunks at
+// 1024 columns (7-13 %); it keeps the power-of-two rows at 3072 (exact fits
+// within 2 %). At 512 columns the backward takes two row groups of 64 lanes
+// per workgroup (9 %).
 // Ids are unique within a kind; 8..10 are the element-wise variants (any D,
 // any alignment) shared by all kinds. Each row is instantiated for every
 // storage combination (binary32 activations: see st_vec / st_cpt below).
@@ -47,7 +49,7 @@ namespace mn {
     X(1, 16, 8, 1, 2, 256, 0, 3, 128)        \
     X(2, 32, 8, 1, 2, 256, 0, 3, 256)        \
     X(3, 64, 8, 1, 2, 256, 0, 3, 512)        \
-    X(4, 128, 8, 1, 1, 256, 0, 3, 1024)      \
+    X(4, 32, 8, 4, 1, 256, 0, 3, 1024)      \
     X(5, 256, 8, 1, 2, 256, 0, 3, 2048)      \
     X(6, 256, 8, 2, 1, 256, 0, 3, 4096)      \
     X(12, 320, 8, 2, 1, 320, 0, 3, 5120)     \
@@ -58,7 +60,7 @@ namespace mn {
     X(1, 16, 8, 1, 2, 256, 0, 1, 128)        \
     X(2, 32, 8, 1, 2, 256, 0, 1, 256)        \
     X(3, 64, 8, 1, 2, 256, 0, 1, 512)        \
-    X(4, 128, 8, 1, 1, 256, 0, 1, 1024)      \
+    X(4, 32, 8, 4, 1, 256, 0, 1, 1024)      \
     X(5, 64, 8, 4, 1, 256, 0, 1, 2048)      \
     X(6, 256, 8, 2, 2, 256, 0, 1, 4096)      \
     X(12, 128, 8, 5, 1, 256, 0, 1, 5120)     \
@@ -91,7 +93,7 @@ namespace mn {
     X(1, 16, 8, 1, 2, 256, 0, 3, 128)        \
     X(2, 32, 8, 1, 2, 256, 0, 3, 256)        \
     X(3, 64, 8, 1, 2, 256, 0, 3, 512)        \
-    X(4, 128, 8, 1, 1, 256, 0, 3, 1024)      \
+    X(4, 32, 8, 4, 1, 256, 0, 3, 1024)      \
     X(5, 256, 8, 1, 2, 256, 0, 3, 2048)      \
     X(6, 512, 8, 1, 2, 512, 0, 3, 4096)      \
     X(12, 320, 8, 2, 1, 320, 0, 3, 5120)     \
@@ -103,7 +105,7 @@ namespace mn {
     X(1, 16, 8, 1, 2, 256, 0, 3, 128)        \
     X(2, 32, 8, 1, 2, 256, 0, 3, 256)        \
     X(3, 64, 8, 1, 2, 256, 0, 3, 512)        \
-    X(4, 128, 8, 1, 1, 256, 0, 3, 1024)      \
+    X(4, 32, 8, 4, 1, 256, 0, 3, 1024)      \
     X(5, 256, 8, 1, 2, 256, 0, 3, 2048)      \
     X(14, 128, 8, 3, 2, 256, 0, 3, 3072)     \
     X(6, 256, 8, 2, 1, 256, 0, 3, 4096)      \
@@ -119,7 +121,7 @@ namespace mn {
     X(0, 8, 8, 1, 4, 256, 1, 3, 64)          \
     X(1, 16, 8, 1, 4, 256, 1, 3, 128)        \
     X(2, 32, 8, 1, 4, 256, 1, 3, 256)        \
-    X(3, 64, 8, 1, 2, 256, 1, 3, 512)        \
+    X(3, 64, 8, 1, 2, 512, 1, 3, 512)        \
     X(4, 128, 8, 1, 2, 512, 1, 3, 1024)      \
     X(5, 256, 8, 1, 2, 512, 1, 3, 2048)      \
     X(14, 192, 8, 2, 1, 384, 1, 3, 3072)     \
@@ -130,7 +132,7 @@ namespace mn {
     X(0, 8, 8, 1, 4, 256, 1, 3, 64)          \
     X(1, 16, 8, 1, 4, 256, 1, 3, 128)        \
     X(2, 32, 8, 1, 4, 256, 1, 3, 256)        \
-    X(3, 64, 8, 1, 2, 256, 1, 3, 512)        \
+    X(3, 64, 8, 1, 2, 512, 1, 3, 512)        \
     X(4, 64, 8, 2, 2, 256, 1, 3, 1024)       \
     X(5, 128, 8, 2, 1, 512, 1, 3, 2048)      \
     X(14, 128, 8, 3, 1, 256, 1, 3, 3072)     \
