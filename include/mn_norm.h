@@ -315,12 +315,18 @@ size_t mn_groupnorm_workspace_bytes(int64_t N, int64_t C);
  *   Norm is the RMSNorm or LayerNorm forward above over each row of X (the
  *   normalised rows are not rounded to a storage type); Y is rounded once.
  * The workspace (mn_norm_gemv_workspace_bytes(M, N, K), 16-byte aligned)
- * holds the row statistics and fp32 partial products over slices of K; the
- * sums run in a fixed order, so Y is bitwise reproducible. The normalisation
+ * holds the row statistics, a fixed area of arrival counters (one per
+ * column tile) and fp32 partial products over slices of K. It must be
+ * zero-filled before its
+ * first use and kept for this entry point (with any M, N, K): every call
+ * leaves its counters at zero again, and the other words need no contents.
+ * Calls that share a workspace must not overlap (one stream, or events
+ * between streams). The sums over the slices run in ascending order,
+ * whichever workgroup performs them, so Y is bitwise reproducible. The normalisation
  * is applied to the sums (rstd, and LayerNorm's mean through the column sums
  * of gamma*W and beta*W) rather than to each X element; the results agree
  * with the element-wise form to fp32 rounding. Validation as elsewhere (MN_ERR_SHAPE for M
- * outside [1, 8], N < 1 or K < 1).
+ * outside [1, 8], N outside [1, 1048576] or K < 1).
  * ------------------------------------------------------------------------- */
 mn_status mn_fused_rmsnorm_gemv(const mn_f16* X, const mn_f16* gamma, const mn_f16* W, mn_f16* Y,
                                 int64_t M, int64_t N, int64_t K, float eps, void* workspace,

@@ -605,7 +605,9 @@ def norm_gemv_workspace_bytes(M: int, N: int, K: int) -> int:
 
 
 def mn_fused_norm_gemv_ex(X, gamma, W, Y, eps: float, workspace, beta=None, stream=None):
-    """Y [M, N] = Norm(X [M, K]) @ W [K, N]; LayerNorm when beta is given."""
+    """Y [M, N] = Norm(X [M, K]) @ W [K, N]; LayerNorm when beta is given.
+    `workspace` is zero-filled before its first use and may then be reused
+    by later calls (each call leaves it reusable)."""
     M, K = _nd(X)
     N = int(W.shape[1])
     act, par = _types(X, gamma)
@@ -626,6 +628,6 @@ def fused_norm_gemv(X, gamma, W, eps: float = 1e-5, beta=None, stream=None):
     N = int(W.shape[1])
     Y = torch.empty(M, N, dtype=X.dtype, device=X.device)
     nb = max(16, norm_gemv_workspace_bytes(M, N, K))
-    ws = torch.empty(nb // 4 + 4, dtype=torch.float32, device=X.device)
+    ws = torch.zeros(nb // 4 + 4, dtype=torch.float32, device=X.device)
     mn_fused_norm_gemv_ex(X, gamma, W, Y, eps, ws, beta, stream)
     return Y

@@ -355,7 +355,7 @@ const BwdTypes kF16{MN_F16, MN_F16, MN_F16, MN_F16};
 
 bool gemv_shape_ok(int64_t M, int64_t N, int64_t K)
 {
-    if (M < 1 || M > mn::kGemvMaxM || N < 1 || K < 1) return false;
+    if (M < 1 || M > mn::kGemvMaxM || N < 1 || K < 1 || N > 64 * mn::kGemvCountWords) return false;
     return N <= INT32_MAX / 8 && K <= INT32_MAX / 8 && K <= (INT64_MAX / 8) / N;
 }
 
@@ -365,8 +365,10 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
     const mn::GemvPlan p = mn::plan_gemv(M, N, K, N % 8 == 0);
     const mn::GemvPlan q = mn::plan_gemv(M, N, K, false);
     const int64_t S = p.S > q.S ? p.S : q.S;  // either load path
-    // statistics, then S slices of M + 2 partial rows (LayerNorm's two extra)
-    return sizeof(float) * ((size_t)mn::kGemvStatFloats + (size_t)S * (size_t)(M + 2) * (size_t)N);
+    // statistics, the tiles' arrival counters, then S slices of M + 2 partial
+    // rows (LayerNorm's two extra)
+    return sizeof(float) * ((size_t)mn::kGemvStatFloats + (size_t)mn::kGemvCountWords +
+                            (size_t)S * (size_t)(M + 2) * (size_t)N);
 }
 
 mn_status norm_gemv(bool ln, const void* X, const void* gamma, const void* beta, const void* W,
@@ -394,7 +396,8 @@ mn_status norm_gemv(bool ln, const void* X, const void* gamma, const void* beta,
     a.beta = ln ? beta : nullptr;
     a.W = W;
     a.stats = static_cast<float*>(ws);
-    a.part = static_cast<float*>(ws) + mn::kGemvStatFloats;
+    a.cnt = reinterpret_cast<uint32_t*>(static_cast<float*>(ws) + mn::kGemvStatFloats);
+    a.part = static_cast<float*>(ws) + mn::kGemvStatFloats + mn::kGemvCountWords;
     a.Y = Y;
     a.M = (int32_t)M;
     a.N = (int32_t)N;

@@ -24,10 +24,25 @@
 // U loads in flight per wave). A tile block stages its KB rows of the product
 // rows in LDS, streams its W rows into per-lane fp32 accumulators, adds the
 // lanes of a column across the wave (butterfly) and the four waves in order,
-// and writes one partial row per product row: part[ks][r][n]. A second kernel
-// adds the S partials of every output in ascending ks order, applies the
-// statistics and rounds once to the storage type, so the result is bitwise
-// reproducible.
+// and writes one partial row per product row: part[ks][r][n].
+//
+// No second launch adds the partials. Every block that wrote something a
+// tile's outputs need (its S slices, and the M statistics blocks for every
+// tile) increments the tile's arrival counter once its stores have
+// completed; the block whose increment completes the count adds the S
+// partials of each output in ascending ks order, applies the statistics,
+// rounds once to the storage type and sets the counter back to zero. The
+// order of the sums does not depend on which block performs them, so the
+// result is bitwise reproducible, and no block waits for another.
+//
+// The hand-off needs no cache maintenance: the partials and statistics are
+// stored at device scope (written through to the level that every XCD
+// reads), each wave waits for its stores to complete before the barrier
+// that precedes the increment, and the finishing block loads them at device
+// scope, which never returns a stale line of its own XCD's L2. Agent-scope
+// release and acquire fences would instead write back and invalidate the
+// XCD's whole L2 once per wave, at a cost far above the separate reduce
+// launch this replaces (measured: 4-5 times slower calls).
 #include "mn_kernels.hpp"
 
 namespace mn {
@@ -46,6 +61,20 @@ namespace kern {
 
 constexpr int kGemvBlock = 256;   // four waves
 constexpr int kGemvWaves = kGemvBlock / 64;
+
+// Device-scope store and load of a value handed from one workgroup to
+// another (see the hand-off above).
+__device__ __forceinline__ void put_dev(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_dev(const float* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// This wave's stores have completed (s_waitcnt vmcnt(0), the other counters
+// left unconstrained; stores count in vmcnt on this architecture).
+__device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Statistics of X row m = blockIdx.x: {mean (LayerNorm) or 0, rstd}.
 template <int ST, bool LNF>
@@ -74,8 +103,8 @@ __device__ void gemv_row_stats(const GemvArgs& a)
     }
     q = block_sum<kGemvBlock>(q, wsum);
     if (threadIdx.x == 0) {
-        a.stats[2 * m] = mu;
-        a.stats[2 * m + 1] = 1.0f / sqrtf(q / (float)K + a.eps);
+        put_dev(&a.stats[2 * m], mu);
+        put_dev(&a.stats[2 * m + 1], 1.0f / sqrtf(q / (float)K + a.eps));
     }
 }
 
@@ -94,6 +123,72 @@ __device__ __forceinline__ float param_any(const void* base, int pdt, int k)
     return f32 ? vf : (pdt == ST_BF16 ? vb : vh);
 }
 
+// Y[m][n] of column tile cb from the S partials (ks ascending) and the row
+// statistics; called by the block that completed the tile's count.
+template <int ST, bool LNF, int TC>
+__device__ void gemv_finish(const GemvArgs& a, int cb)
+{
+    typedef typename Elem<ST>::type E;
+    const int M = a.M, N = a.N;
+    const int RE = M + (LNF ? 2 : 0);
+    const int64_t step = (int64_t)RE * N;
+    for (int i = threadIdx.x; i < M * TC; i += kGemvBlock) {
+        const int m = i / TC;
+        const int n = cb * TC + i % TC;
+        if (n >= N) continue;
+        // statistics first, so their loads overlap the partials'
+        const float rs = get_dev(&a.stats[2 * m + 1]);
+        const float d = LNF ? get_dev(&a.stats[2 * m]) -
+                                  (float)static_cast<const E*>(a.X)[(int64_t)m * a.K]
+                            : 0.0f;
+        const float* pa = a.part + (int64_t)m * N + n;
+        const float* pg = a.part + (int64_t)M * N + n;
+        const float* pb = a.part + (int64_t)(M + 1) * N + n;
+        float sa = 0.0f, sg = 0.0f, sb = 0.0f;
+        int k = 0;
+        for (; k + 8 <= a.S; k += 8) {
+            float va[8], vg[8], vb[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                va[j] = get_dev(pa + (k + j) * step);
+                if (LNF) {
+                    vg[j] = get_dev(pg + (k + j) * step);
+                    vb[j] = get_dev(pb + (k + j) * step);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                sa += va[j];
+                if (LNF) {
+                    sg += vg[j];
+                    sb += vb[j];
+                }
+            }
+        }
+        for (; k < a.S; ++k) {
+            sa += get_dev(pa + k * step);
+            if (LNF) {
+                sg += get_dev(pg + k * step);
+                sb += get_dev(pb + k * step);
+            }
+        }
+        float y;
+        if (LNF) {
+            y = __builtin_fmaf(rs, __builtin_fmaf(-d, sg, sa), sb);
+        } else {
+            y = rs * sa;
+        }
+        static_cast<E*>(a.Y)[(int64_t)m * N + n] = (E)y;
+    }
+}
+
+// Counter of tile cb back to zero for the next call, by the block that
+// finished the tile.
+__device__ __forceinline__ void gemv_reset(const GemvArgs& a, int cb)
+{
+    __hip_atomic_store(&a.cnt[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int ST, int VEC, int MM, bool LNF, int RPW, int U>
 __global__ void __launch_bounds__(kGemvBlock) gemv_kernel(const GemvArgs a)
 {
@@ -110,13 +205,34 @@ __global__ void __launch_bounds__(kGemvBlock) gemv_kernel(const GemvArgs a)
     __shared__ float4 lds4[LF / 4];
     float* const lds = reinterpret_cast<float*>(lds4);
 
+    __shared__ int s_count;
     const int M = a.M;
+    const int tid = threadIdx.x;
+    const unsigned arrivals = (unsigned)(a.S + M);
     if ((int)blockIdx.x < M) {
         gemv_row_stats<ST, LNF>(a);
+        // count the statistics in on every tile, and finish the tiles whose
+        // count this block completes
+        stores_done();
+        __syncthreads();
+        int* const done = reinterpret_cast<int*>(lds);
+        for (int base = 0; base < a.NB; base += kGemvBlock) {
+            if (tid == 0) s_count = 0;
+            __syncthreads();
+            const int cb = base + tid;
+            if (cb < a.NB && atomicAdd(&a.cnt[cb], 1u) == arrivals - 1)
+                done[atomicAdd(&s_count, 1)] = cb;
+            __syncthreads();
+            const int nd = s_count;
+            for (int j = 0; j < nd; ++j) {
+                gemv_finish<ST, LNF, TC>(a, done[j]);
+                if (tid == 0) gemv_reset(a, done[j]);
+            }
+            __syncthreads();
+        }
         return;
     }
     const int t = (int)blockIdx.x - M;
-    const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int rg = lane / LPR;
@@ -243,65 +359,19 @@ __global__ void __launch_bounds__(kGemvBlock) gemv_kernel(const GemvArgs a)
             float s = lds[p * TC + c];
 #pragma unroll
             for (int ww = 1; ww < NW; ++ww) s += lds[(ww * R + p) * TC + c];
-            a.part[((int64_t)ks * RE + pr) * N + n] = s;
+            put_dev(&a.part[((int64_t)ks * RE + pr) * N + n], s);
         }
     }
-}
-
-// Y[m][n] from the S partials (ks ascending) and the row statistics.
-template <int ST, bool LNF>
-__global__ void __launch_bounds__(256) gemv_reduce_kernel(const GemvArgs a)
-{
-    typedef typename Elem<ST>::type E;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int M = a.M, N = a.N;
-    if (i >= (int64_t)M * N) return;
-    const int m = (int)(i / N);
-    const int n = (int)(i - (int64_t)m * N);
-    // statistics first, so their loads overlap the partials'
-    const float rs = a.stats[2 * m + 1];
-    const float d = LNF ? a.stats[2 * m] - (float)static_cast<const E*>(a.X)[(int64_t)m * a.K]
-                        : 0.0f;
-    const int RE = M + (LNF ? 2 : 0);
-    const int64_t step = (int64_t)RE * N;
-    const float* pa = a.part + (int64_t)m * N + n;
-    const float* pg = a.part + (int64_t)M * N + n;
-    const float* pb = a.part + (int64_t)(M + 1) * N + n;
-    float sa = 0.0f, sg = 0.0f, sb = 0.0f;
-    int k = 0;
-    for (; k + 8 <= a.S; k += 8) {
-        float va[8], vg[8], vb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            va[j] = pa[(k + j) * step];
-            if (LNF) {
-                vg[j] = pg[(k + j) * step];
-                vb[j] = pb[(k + j) * step];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            sa += va[j];
-            if (LNF) {
-                sg += vg[j];
-                sb += vb[j];
-            }
-        }
+    // count the slice in once its stores have completed; the block that
+    // completes the tile's count adds the tile's partials
+    stores_done();
+    __syncthreads();
+    if (tid == 0) s_count = atomicAdd(&a.cnt[cb], 1u) == arrivals - 1;
+    __syncthreads();
+    if (s_count) {
+        gemv_finish<ST, LNF, TC>(a, cb);
+        if (tid == 0) gemv_reset(a, cb);
     }
-    for (; k < a.S; ++k) {
-        sa += pa[k * step];
-        if (LNF) {
-            sg += pg[k * step];
-            sb += pb[k * step];
-        }
-    }
-    float y;
-    if (LNF) {
-        y = __builtin_fmaf(rs, __builtin_fmaf(-d, sg, sa), sb);
-    } else {
-        y = rs * sa;
-    }
-    static_cast<E*>(a.Y)[i] = (E)y;
 }
 
 }  // namespace kern
@@ -378,19 +448,7 @@ hipError_t launch_gemv(int st, bool ln, const GemvPlan& p, const GemvArgs& a, hi
     case ST_F16: e = launch_gemv_st<ST_F16>(ln, p.vec, p.rpw, p.MM, grid, s, a); break;
     case ST_BF16: e = launch_gemv_st<ST_BF16>(ln, p.vec, p.rpw, p.MM, grid, s, a); break;
     }
-    if (e != hipSuccess) return e;
-    const int64_t MN = (int64_t)a.M * a.N;
-    const dim3 rgrid((unsigned)((MN + 255) / 256));
-    const dim3 rb(256);
-    switch (st) {
-    case ST_F16:
-        return ln ? launch_k(kern::gemv_reduce_kernel<ST_F16, true>, rgrid, rb, s, a)
-                  : launch_k(kern::gemv_reduce_kernel<ST_F16, false>, rgrid, rb, s, a);
-    case ST_BF16:
-        return ln ? launch_k(kern::gemv_reduce_kernel<ST_BF16, true>, rgrid, rb, s, a)
-                  : launch_k(kern::gemv_reduce_kernel<ST_BF16, false>, rgrid, rb, s, a);
-    }
-    return hipErrorInvalidValue;
+    return e;
 }
 
 }  // namespace mn

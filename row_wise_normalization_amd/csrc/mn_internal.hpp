@@ -150,6 +150,10 @@ hipError_t launch_gn_bwd(int st, int ot, const GnPlan& p, const GnArgs& a, hipSt
 constexpr int kGemvMaxKB = 512;  // rows of W per tile (LDS slice of the product rows)
 constexpr int kGemvMaxM = 8;
 constexpr int kGemvStatFloats = 64;  // workspace head: {mean, rstd} per X row
+// Arrival counters after the statistics, one per column tile (tiles are at
+// least 64 columns wide), in an area of fixed size so that no shape's
+// partials ever land on another shape's counters: N <= 64 * kGemvCountWords.
+constexpr int64_t kGemvCountWords = 16384;
 
 struct GemvArgs {
     const void* X;           // [M][K], storage type of the launch
@@ -157,6 +161,7 @@ struct GemvArgs {
     const void* beta;        // [K], type pdt (LayerNorm) or null
     const void* W;           // [K][N], storage type of the launch
     float* stats;            // [M][2] row statistics (workspace head)
+    uint32_t* cnt;           // [NB] arrival counters, zero between calls
     float* part;             // [S][RE][N] fp32 partial products, RE = M (+2 LayerNorm)
     void* Y;                 // [M][N], storage type of the launch
     int32_t M, N, K, pdt;

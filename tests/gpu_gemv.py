@@ -31,11 +31,22 @@ def run(d, eps, ln, offset=0):
     M, K = X.shape
     N = W.shape[1]
     Y = empty((M, N), X.dtype, offset)
-    nb = max(16, mn.norm_gemv_workspace_bytes(M, N, K))
-    ws = torch.empty(nb // 4, dtype=torch.float32, device="cuda")
-    mn.mn_fused_norm_gemv_ex(X, g, W, Y, eps, ws, beta=b)
+    mn.mn_fused_norm_gemv_ex(X, g, W, Y, eps, workspace(M, N, K), beta=b)
     torch.cuda.synchronize()
     return host(Y)
+
+
+_WS = [None]
+
+
+def workspace(M, N, K):
+    """One zero-filled workspace kept across calls (any shape, RMSNorm or
+    LayerNorm), as the entry point allows: every call must leave its arrival
+    counters at zero for the next."""
+    nb = max(16, mn.norm_gemv_workspace_bytes(M, N, K))
+    if _WS[0] is None or _WS[0].numel() * 4 < nb:
+        _WS[0] = torch.zeros(max(nb // 4, 1 << 20), dtype=torch.float32, device="cuda")
+    return _WS[0]
 
 
 def reference(d, eps, ln):

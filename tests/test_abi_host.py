@@ -267,18 +267,21 @@ def test_fused_gemv_validation_and_workspace():
     L = mn.lib()
     f = ctypes.c_float(1e-5)
     F16, BF16, F32 = mn.MN_F16, mn.MN_BF16, mn.MN_F32
-    # 64 floats of row statistics, then S slices of M + 2 fp32 partial rows;
-    # one tile per workgroup, K slices halve from 512 rows until there are 512
+    # 64 floats of row statistics, 16384 arrival counters (one per column
+    # tile, tiles at least 64 columns wide), then S slices of M + 2 fp32
+    # partial rows; one
+    # tile per workgroup, K slices halve from 512 rows until there are 512
     # tiles (192 for the wide 512-column tiles of one or two X rows) or the
     # slices reach 64 rows; S is the larger of the 16-byte path (128-column
     # or wide tiles) and the element-wise path (64-column tiles)
-    ws = lambda S, M, N: 4 * (64 + S * (M + 2) * N)
+    ws = lambda S, M, N: 4 * (64 + 16384 + S * (M + 2) * N)
     assert mn.norm_gemv_workspace_bytes(4, 4096, 4096) == ws(16, 4, 4096)
     assert mn.norm_gemv_workspace_bytes(1, 14336, 4096) == ws(8, 1, 14336)
     assert mn.norm_gemv_workspace_bytes(4, 12288, 4096) == ws(8, 4, 12288)
     assert mn.norm_gemv_workspace_bytes(2, 7, 100) == ws(2, 2, 7)
-    for bad in ((0, 8, 8), (9, 8, 8), (1, 0, 8), (1, 8, 0)):
+    for bad in ((0, 8, 8), (9, 8, 8), (1, 0, 8), (1, 8, 0), (1, 64 * 16384 + 1, 8)):
         assert mn.norm_gemv_workspace_bytes(*bad) == 0
+    assert mn.norm_gemv_workspace_bytes(1, 64 * 16384, 8) > 0
     M, N, K = 4, 64, 128
     ws = mn.norm_gemv_workspace_bytes(M, N, K)
     W = P(0xE0000000)

@@ -9,7 +9,7 @@ import parity
 import workloads
 import row_wise_normalization_amd as mn
 from gpu_cases import dev, say
-from gpu_gemv import case as _case, compare, reference, run
+from gpu_gemv import case as _case, compare, reference, run, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +62,17 @@ def test_deterministic_and_row_independent():
     assert np.array_equal(a.view(np.uint16), run(d, 1e-5, False).view(np.uint16))
     one = {k: (v[1:2] if k == "X" else v) for k, v in d.items()}
     assert np.array_equal(a[1:2].view(np.uint16), run(one, 1e-5, False).view(np.uint16))
+
+
+def test_counters_back_at_zero():
+    """Each call leaves every word of the shared workspace's counter area
+    (16384 words after the 64 of statistics) at zero: the block that
+    finishes a column tile resets its counter."""
+    for M, K, N, ln in ((4, 4096, 12288, False), (3, 1000, 1000, True), (1, 5000, 16384, False)):
+        d = _case(M, K, N, 3, ln)
+        run(d, 1e-5, ln)
+        ws = workspace(M, N, K)[:64 + 16384].view(torch.int32).cpu()
+        assert not ws[64:].any(), f"{M}x{K}x{N}: counters left {ws[64:].nonzero().flatten()[:8]}"
 
 
 def test_matches_separate_norm_then_matmul():
