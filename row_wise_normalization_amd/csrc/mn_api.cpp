@@ -444,7 +444,7 @@ mn_status groupnorm_forward(const void* X, const void* gamma, const void* beta, 
     if (!gn_shape_ok(N, C, L, G)) return MN_ERR_SHAPE;
     const bool vec = gn_vec_ok(st, L, X, Y);
     mn::GnPlan plan;
-    if (!mn::plan_groupnorm(st, N, C, L, G, vec, plan)) return MN_ERR_SHAPE;
+    if (!mn::plan_groupnorm(st, N, C, L, G, vec, true, plan)) return MN_ERR_SHAPE;
     if (!eps_ok(eps)) return MN_ERR_EPS;
     const size_t es = (size_t)mn::stor_bytes(st), ps = (size_t)mn::stor_bytes(pdt);
     const size_t nx = (size_t)N * (size_t)C * (size_t)L;
@@ -479,7 +479,7 @@ mn_status groupnorm_backward(const void* X, const void* gamma, const float* mean
     if (!gn_shape_ok(N, C, L, G)) return MN_ERR_SHAPE;
     const bool vec = gn_vec_ok(st, L, X, dY, dX);
     mn::GnPlan plan;
-    if (!mn::plan_groupnorm(st, N, C, L, G, vec, plan)) return MN_ERR_SHAPE;
+    if (!mn::plan_groupnorm(st, N, C, L, G, vec, false, plan)) return MN_ERR_SHAPE;
     const size_t need = gn_workspace_bytes(N, C);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
     const size_t es = (size_t)mn::stor_bytes(st), ps = (size_t)mn::stor_bytes(pdt);

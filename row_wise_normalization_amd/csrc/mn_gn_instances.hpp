@@ -20,8 +20,8 @@ hipError_t gn_launch(Kernel k, const GnPlan& p, const GnArgs& a, hipStream_t s)
 
 // only the shapes within the register budget are instantiated
 #define MN_GN_FWD_U(SH, T, VEC, CPT, UL, U)                                                  \
-    case SH * 8 + UL:                                                                        \
-        if constexpr (gn_fits(ST, VEC, T, CPT, U))                                              \
+    case SH * kGnFwdMaxU + UL:                                                               \
+        if constexpr (gn_fits_fwd(ST, VEC, T, CPT, U))                                          \
             return gn_launch(                                                                \
                 kern::gn_fwd_kernel<ST, T, st_vec(ST, VEC), st_cpt(ST, VEC, CPT), U>, p, a, s); \
         else                                                                                 \
@@ -38,8 +38,13 @@ hipError_t gn_launch(Kernel k, const GnPlan& p, const GnArgs& a, hipStream_t s)
     M(SH, T, VEC, CPT, 0, 1) M(SH, T, VEC, CPT, 1, 2) M(SH, T, VEC, CPT, 2, 3)            \
     M(SH, T, VEC, CPT, 3, 4) M(SH, T, VEC, CPT, 4, 5) M(SH, T, VEC, CPT, 5, 6)            \
     M(SH, T, VEC, CPT, 6, 7) M(SH, T, VEC, CPT, 7, 8)
-#define MN_GN_FWD_VEC(SH, T, CPT, MAXL) MN_GN_US(MN_GN_FWD_U, SH, T, 8, CPT)
-#define MN_GN_FWD_ELEM(SH, T, CPT, MAXL) MN_GN_US(MN_GN_FWD_U, SH, T, 1, CPT)
+#define MN_GN_US16(M, SH, T, VEC, CPT)                                                    \
+    MN_GN_US(M, SH, T, VEC, CPT)                                                          \
+    M(SH, T, VEC, CPT, 8, 9) M(SH, T, VEC, CPT, 9, 10) M(SH, T, VEC, CPT, 10, 11)         \
+    M(SH, T, VEC, CPT, 11, 12) M(SH, T, VEC, CPT, 12, 13) M(SH, T, VEC, CPT, 13, 14)      \
+    M(SH, T, VEC, CPT, 14, 15) M(SH, T, VEC, CPT, 15, 16)
+#define MN_GN_FWD_VEC(SH, T, CPT, MAXL) MN_GN_US16(MN_GN_FWD_U, SH, T, 8, CPT)
+#define MN_GN_FWD_ELEM(SH, T, CPT, MAXL) MN_GN_US16(MN_GN_FWD_U, SH, T, 1, CPT)
 #define MN_GN_BWD_VEC(SH, T, CPT, MAXL) MN_GN_US(MN_GN_BWD_U, SH, T, 8, CPT)
 #define MN_GN_BWD_ELEM(SH, T, CPT, MAXL) MN_GN_US(MN_GN_BWD_U, SH, T, 1, CPT)
 
@@ -60,6 +65,7 @@ hipError_t launch_gn_bwd_t(const GnPlan& p, const GnArgs& a, hipStream_t s)
 #undef MN_GN_FWD_U
 #undef MN_GN_BWD_U
 #undef MN_GN_US
+#undef MN_GN_US16
 #undef MN_GN_FWD_VEC
 #undef MN_GN_FWD_ELEM
 #undef MN_GN_BWD_VEC

@@ -16,7 +16,8 @@ constexpr GnShape kGnElem[] = {MN_GN_ELEM_SHAPES(MN_GN_ROW)};
 
 }  // namespace
 
-bool plan_groupnorm(int st, int64_t N, int64_t C, int64_t L, int64_t G, bool vec_ok, GnPlan& p)
+bool plan_groupnorm(int st, int64_t N, int64_t C, int64_t L, int64_t G, bool vec_ok, bool fwd,
+                    GnPlan& p)
 {
     if (N < 1 || C < 1 || L < 1 || G < 1 || C % G != 0) return false;
     const int64_t Cg = C / G;
@@ -52,7 +53,37 @@ bool plan_groupnorm(int st, int64_t N, int64_t C, int64_t L, int64_t G, bool vec
     p.id = sh->id * 8 + best - 1;
     p.block = (int32_t)best_block;
     p.grid = N * G;
-    return p.grid <= INT32_MAX;
+    if (p.grid > INT32_MAX) return false;
+    if (!fwd) return true;
+    // The forward (same shapes as the backward) holds fewer registers per
+    // row: the fewest padding rows again, then lanes that fill their waves,
+    // then the smallest workgroup. At 32 x 320 x 4096 (G = 32) one row group
+    // of 256 lanes per 10 x 4096 slice (four slices per CU, all 1024 in one
+    // round) ran 16 % ahead of two row groups of 512 lanes (three per CU).
+    int fb = -1;
+    int64_t fb_waste = 0, fb_block = 0, fb_lanes = 0;
+    for (int U = 1; U <= kGnFwdMaxU; ++U) {
+        if (!gn_fits_fwd(st, vec, sh->T, sh->CPT, U)) break;
+        const int64_t rpb = (Cg + U - 1) / U;
+        const int64_t lanes = rpb * sh->T;
+        const int64_t block = (lanes + 63) / 64 * 64;
+        if (block > 1024) continue;
+        const int64_t waste = rpb * U - Cg;
+        // busy lanes per 64: a shortfall below one wave counts against
+        const bool fuller = lanes * fb_block > fb_lanes * block;
+        const bool same_fill = lanes * fb_block == fb_lanes * block;
+        const bool better = fb < 0 || waste < fb_waste ||
+                            (waste == fb_waste && (fuller || (same_fill && block < fb_block)));
+        if (better) {
+            fb = U;
+            fb_waste = waste;
+            fb_block = block;
+            fb_lanes = lanes;
+        }
+    }
+    p.id = sh->id * kGnFwdMaxU + fb - 1;
+    p.block = (int32_t)fb_block;
+    return true;
 }
 
 hipError_t launch_gn_fwd(int st, const GnPlan& p, const GnArgs& a, hipStream_t s)

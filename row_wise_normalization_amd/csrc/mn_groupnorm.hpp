@@ -70,6 +70,10 @@ template <int ST, int T, int VEC, int CPT, int U>
 __device__ __forceinline__ void gn_map(GnSlice<ST, T, VEC, CPT, U>& t, const GnArgs& a, int s,
                                        int gi, int l, int rpb)
 {
+    // Rows of at least a wave: every lane of a wave is in the same row group,
+    // so its rows (and their gamma and beta) are wave-uniform and live in
+    // scalar registers.
+    if (T >= 64) gi = __builtin_amdgcn_readfirstlane(gi);
     t.base = (int64_t)s * a.Cg * a.L;
     t.l = l;
     t.L = a.L;
@@ -290,6 +294,21 @@ constexpr bool gn_fits(int st, int vec, int t, int cpt, int u)
     if (u > 8) return false;
     if (vec == 1) return u * cpt <= 16;
     const int lim = t >= 1024 ? 4 : t >= 512 ? 8 : 10;
+    return u * cpt <= (st == ST_F32 ? lim / 2 : lim);
+}
+
+// The forward holds only X across its reductions, so its rows per row group
+// go up to 16 and, for rows of 64 to 256 lanes, 20 chunks per lane (80 VGPRs
+// of fp16 data; a row group is then wave-uniform, so gamma, beta and the row
+// indices sit in scalar registers), which lets one row group of 256 lanes
+// hold a whole 10 x 4096 slice; rows of fewer than 64 lanes keep per-lane
+// row indices and stop at 12 chunks. Forward launch ids are shape * 16 + U - 1.
+constexpr int kGnFwdMaxU = 16;
+constexpr bool gn_fits_fwd(int st, int vec, int t, int cpt, int u)
+{
+    if (u > kGnFwdMaxU) return false;
+    if (vec == 1) return u * cpt <= 16;
+    const int lim = t >= 1024 ? 4 : t >= 512 ? 8 : t >= 64 ? 20 : 12;
     return u * cpt <= (st == ST_F32 ? lim / 2 : lim);
 }
 

@@ -141,8 +141,10 @@ struct GnPlan {
     int64_t grid;            // N * G
 };
 
-// false when the slice does not fit one workgroup's registers
-bool plan_groupnorm(int st, int64_t N, int64_t C, int64_t L, int64_t G, bool vec_ok, GnPlan& p);
+// false when the slice does not fit one workgroup's registers (the same
+// shapes for both directions; the forward plan may hold more rows per lane)
+bool plan_groupnorm(int st, int64_t N, int64_t C, int64_t L, int64_t G, bool vec_ok, bool fwd,
+                    GnPlan& p);
 hipError_t launch_gn_fwd(int st, const GnPlan& p, const GnArgs& a, hipStream_t s);
 hipError_t launch_gn_bwd(int st, int ot, const GnPlan& p, const GnArgs& a, hipStream_t s);
 
