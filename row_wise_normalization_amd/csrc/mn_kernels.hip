@@ -110,13 +110,15 @@ int bwd_vector_partials(int kind)
     }
 }
 
-FwdPlan plan_forward(int kind, int st, int64_t N, int32_t D, bool vec_ok)
+FwdPlan plan_forward(int kind, int st, int64_t N, int32_t D, bool vec_ok, int64_t B)
 {
     (void)st;
     FwdPlan p;
     p.v = vec_ok ? pick(kFwdVec[kind], D) : pick(kFwdGen, D);
-    // one tile of RPB*U rows per workgroup
-    p.grid = ceil_div(N, (int64_t)(p.v.BLOCK / p.v.T) * p.v.U);
+    // one tile of RPB*U rows per workgroup; MOD: whole tiles per sample (B
+    // samples of N / B rows)
+    const int64_t tile = (int64_t)(p.v.BLOCK / p.v.T) * p.v.U;
+    p.grid = (kind == MOD) ? B * ceil_div(N / B, tile) : ceil_div(N, tile);
     return p;
 }
 

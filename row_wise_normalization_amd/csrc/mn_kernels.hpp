@@ -364,8 +364,17 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
     const int g = tid / T;
     const int l = tid % T;
     const int D = a.D;
-    const int64_t begin = (int64_t)blockIdx.x * TILE;
-    const int64_t end = a.N;
+    // MOD: tiles are sample-major (each sample's S rows start a new tile), so
+    // a tile never spans two samples and its rows share one scale and shift
+    // row, loaded once per lane
+    int64_t begin = (int64_t)blockIdx.x * TILE, end = a.N, soff = 0;
+    if constexpr (KIND == MOD) {
+        const int64_t tps = (a.S + TILE - 1) / TILE;
+        const int64_t smp = (int64_t)blockIdx.x / tps;
+        begin = smp * a.S + ((int64_t)blockIdx.x - smp * tps) * TILE;
+        end = (smp + 1) * a.S;
+        soff = smp * (int64_t)a.D;
+    }
 
     int coff[CPT];
     bool cval[CPT];
@@ -395,23 +404,25 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
     struct Tile {
         HV x[U][CPT];
         HV r[U][CPT];
-        HV sc[U][CPT], sh[U][CPT];   // MOD: the row's sample's scale and shift
+        HV sc[CPT], sh[CPT];   // MOD: the tile's sample's scale and shift
     };
     auto load_tile = [&](Tile& t, int64_t base) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = base + u * RPB + g;
             const int64_t ro = row * (int64_t)D;
-            const int64_t so = (KIND == MOD) ? (row / a.S) * (int64_t)D : 0;
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 const bool ok = row < end && cval[k];
                 t.x[u][k] = ok ? sload<ST, VEC, NT>(a.X, ro + coff[k]) : czero<ST, VEC>();
                 if constexpr (KIND == ADD) t.r[u][k] = ok ? sload<ST, VEC, NT>(a.R, ro + coff[k]) : czero<ST, VEC>();
-                if constexpr (KIND == MOD) {
-                    t.sc[u][k] = ok ? sload<ST, VEC, 0>(a.scale, so + coff[k]) : czero<ST, VEC>();
-                    t.sh[u][k] = ok ? sload<ST, VEC, 0>(a.shift, so + coff[k]) : czero<ST, VEC>();
-                }
+            }
+        }
+        if constexpr (KIND == MOD) {
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                t.sc[k] = cval[k] ? sload<ST, VEC, 0>(a.scale, soff + coff[k]) : czero<ST, VEC>();
+                t.sh[k] = cval[k] ? sload<ST, VEC, 0>(a.shift, soff + coff[k]) : czero<ST, VEC>();
             }
         }
     };
@@ -555,8 +566,8 @@ __global__ void __launch_bounds__(BLOCK) fwd_kernel(const FwdArgs a)
                                            pw[3]);
                     } else if constexpr (KIND == MOD) {
                         o = __builtin_fmaf(v * rs[u] * gam[k][e],
-                                           1.0f + cget<ST, VEC>(cur.sc[u][k], e),
-                                           cget<ST, VEC>(cur.sh[u][k], e));
+                                           1.0f + cget<ST, VEC>(cur.sc[k], e),
+                                           cget<ST, VEC>(cur.sh[k], e));
                     } else {
                         o = v * rs[u] * gam[k][e];
                     }

@@ -73,6 +73,13 @@ def test_mod_samples(B, N):
     compare("mod", run("mod", d, 1e-5), reference("mod", d, 1e-5), d, f"mod B={B} N={N}")
 
 
+def test_mod_ragged_samples_at_benchmark_width():
+    """Samples of 101 rows at 3072 columns: tiles are laid out per sample, so
+    every sample ends in a part-filled tile."""
+    d = workloads.random_case("mod", 6 * 101, 3072, 510, B=6)
+    compare("mod", run("mod", d, 1e-5), reference("mod", d, 1e-5), d, "mod B=6 N=606 D=3072")
+
+
 def test_mod_without_modulation_is_rmsnorm():
     """scale = shift = 0 gives the RMSNorm outputs of the training-pair path."""
     from gpu_cases import run_gpu
