@@ -49,12 +49,15 @@ namespace mn {
 
 // Tile shapes of the 16-byte path, from timing sweeps at 4096 x 12288 and
 // 4096 x 14336 (K x N): four rows of 128 columns per wave load, and tiles
-// halved along K until there are about two per CU; for one or two X rows and
-// wide W, one row of 512 columns per wave load in fewer, longer tiles (8 %
-// faster at M = 1, N = 14336; slower at M = 4, whose product rows need more
-// registers per column, and at N = 4096, which leaves too few tiles).
+// halved along K until there is about one per CU (with the K slices added
+// inside the launch, fewer and longer slices beat two tiles per CU: 16 %
+// faster at 4 x 4096 @ 4096 x 4096, equal at N = 12288); for one or two X
+// rows and wide W, one row of 512 columns per wave load in fewer, longer
+// tiles (8 % faster at M = 1, N = 14336; slower at M = 4, whose product rows
+// need more registers per column, and at N = 4096, which leaves too few
+// tiles).
 constexpr int kGemvRpwVec = 4;
-constexpr int64_t kGemvTileTarget = 512;
+constexpr int64_t kGemvTileTarget = 256;
 constexpr int64_t kGemvWideTileTarget = 192;
 
 namespace kern {
@@ -389,13 +392,15 @@ template <int ST, int VEC, bool LNF, int RPW>
 hipError_t launch_gemv_mm(int mm, dim3 grid, hipStream_t s, const GemvArgs& a)
 {
     const dim3 block(kern::kGemvBlock);
-    // the wide 16-byte tiles serve one or two X rows only
+    // the wide 16-byte tiles serve one or two X rows only; W loads in flight
+    // per register set: 8 for one or two X rows, 4 from three (5-9 % faster
+    // at M = 4 than 8, whose registers cost waves)
     constexpr bool ALL = !(VEC == 8 && RPW == 1);
     switch (mm) {
     case 1: return launch_k(kern::gemv_kernel<ST, VEC, 1, LNF, RPW, 8>, grid, block, s, a);
     case 2: return launch_k(kern::gemv_kernel<ST, VEC, 2, LNF, RPW, 8>, grid, block, s, a);
     case 4:
-        if constexpr (ALL) return launch_k(kern::gemv_kernel<ST, VEC, 4, LNF, RPW, 8>, grid, block, s, a);
+        if constexpr (ALL) return launch_k(kern::gemv_kernel<ST, VEC, 4, LNF, RPW, 4>, grid, block, s, a);
         break;
     case 8:
         if constexpr (ALL) return launch_k(kern::gemv_kernel<ST, VEC, 8, LNF, RPW, 4>, grid, block, s, a);

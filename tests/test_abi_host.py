@@ -269,13 +269,14 @@ def test_fused_gemv_validation_and_workspace():
     F16, BF16, F32 = mn.MN_F16, mn.MN_BF16, mn.MN_F32
     # 64 floats of row statistics, 16384 arrival counters (one per column
     # tile, tiles at least 64 columns wide), then S slices of M + 2 fp32
-    # partial rows; one
-    # tile per workgroup, K slices halve from 512 rows until there are 512
-    # tiles (192 for the wide 512-column tiles of one or two X rows) or the
-    # slices reach 64 rows; S is the larger of the 16-byte path (128-column
-    # or wide tiles) and the element-wise path (64-column tiles)
+    # partial rows; one tile per workgroup, K slices halve from 512 rows
+    # until there are 256 tiles (192 for the wide 512-column tiles of one or
+    # two X rows) or the slices reach 64 rows; S is the larger of the 16-byte
+    # path (128-column or wide tiles) and the element-wise path (64-column
+    # tiles)
     ws = lambda S, M, N: 4 * (64 + 16384 + S * (M + 2) * N)
-    assert mn.norm_gemv_workspace_bytes(4, 4096, 4096) == ws(16, 4, 4096)
+    assert mn.norm_gemv_workspace_bytes(4, 4096, 4096) == ws(8, 4, 4096)
+    assert mn.norm_gemv_workspace_bytes(4, 1024, 4096) == ws(32, 4, 1024)
     assert mn.norm_gemv_workspace_bytes(1, 14336, 4096) == ws(8, 1, 14336)
     assert mn.norm_gemv_workspace_bytes(4, 12288, 4096) == ws(8, 4, 12288)
     assert mn.norm_gemv_workspace_bytes(2, 7, 100) == ws(2, 2, 7)
