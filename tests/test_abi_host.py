@@ -172,16 +172,18 @@ def test_workspace_bytes():
         for N, D in ((1, 1), (17, 257), (16384, 4096), (1048576, 128), (32768, 8192)):
             b = mn.workspace_bytes(kind, N, D)
             assert b > 0 and b % 16 == 0
-            # at most 256 partial rows of round_up(D, 4) floats (two arrays for LayerNorm)
-            assert b <= 256 * ((D + 3) // 4 * 4) * 4 * (2 if kind == mn.MN_LAYERNORM else 1)
+            # at most 256 partial rows of round_up(D, 4) floats (two arrays for
+            # LayerNorm), 512 for RMSNorm rows of up to 4096 columns
+            P = 512 if kind == mn.MN_RMSNORM and D <= 4096 else 256
+            assert b == min(N, P) * ((D + 3) // 4 * 4) * 4 * (2 if kind == mn.MN_LAYERNORM else 1)
     assert mn.workspace_bytes(6, 16, 64) == 0
     # the other norms: Dynamic Tanh keeps two partial arrays plus scalars,
     # PolyNorm only scalars, the Modulated RMSNorm sizes by its sample count
-    for N, D in ((1, 1), (17, 257), (16384, 4096)):
+    for N, D in ((1, 1), (17, 257), (16384, 4096), (16384, 8192)):
         P = min(N, 256)
         Dp = (D + 3) // 4 * 4
         assert mn.workspace_bytes(mn.MN_DYT, N, D) == 2 * P * Dp * 4 + P * 16
-        assert mn.workspace_bytes(mn.MN_POLYNORM, N, D) == P * 16
+        assert mn.workspace_bytes(mn.MN_POLYNORM, N, D) == min(N, 512 if D <= 4096 else 256) * 16
     assert mn.workspace_bytes(mn.MN_MOD_RMSNORM, 16, 64) == 0
     assert mn.mod_rmsnorm_workspace_bytes(4, 16, 64) == 4 * 4 * 64 * 4 * 3  # 4 per sample (S = 4)
     assert mn.mod_rmsnorm_workspace_bytes(8, 8192, 1024) == 8 * 32 * 1024 * 4 * 3

@@ -82,8 +82,12 @@ def test_fused_special_cases():
     say(f"[contract] fused(R=0) vs rmsnorm dX: {int((diff > 0).sum())} elements differ, "
         f"max {float((diff / ulp).max()):.1f} ulp")
     assert (diff <= ulp).all()
+    # the RMSNorm backward splits the rows over twice the workgroups of the
+    # fused one at this width, so its fp32 column sums run in another order:
+    # each of the 777 terms is O(1), and the two orders differ by a few units
+    # of 2^-24 times the column's sum of magnitudes (about 500)
     parity.check_grad(a["dgamma"], r["dgamma"].astype(np.float64), "fused(R=0) dgamma",
-                      atol=1e-6, rtol=1e-6)
+                      atol=5e-5, rtol=1e-5)
     # dY = 0: dX = dH exactly (as values; a zero may change sign)
     b = run_gpu("add", dict(d, dY=Z), 1e-5)
     assert (b["dX"].astype(np.float64) == d["dH"].astype(np.float64)).all()
