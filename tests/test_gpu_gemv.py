@@ -64,6 +64,17 @@ def test_deterministic_and_row_independent():
     assert np.array_equal(a[1:2].view(np.uint16), run(one, 1e-5, False).view(np.uint16))
 
 
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+def test_long_rows_few_columns(ln):
+    """K = 131072 against one 64-column tile: 256 short K slices finish while
+    the statistics workgroup still sums its long row, so the statistics
+    workgroup is usually the one that completes the tile and adds its
+    partials."""
+    M, K, N = 1, 131072, 64
+    d = _case(M, K, N, 12, ln)
+    compare(run(d, 1e-5, ln), reference(d, 1e-5, ln), d, 1e-5, ln, f"{M}x{K}x{N}")
+
+
 def test_counters_back_at_zero():
     """Each call leaves every word of the shared workspace's counter area
     (16384 words after the 64 of statistics) at zero: the block that
