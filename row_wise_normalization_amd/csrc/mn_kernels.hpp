@@ -276,6 +276,21 @@ __device__ __forceinline__ float tanh_q(float u, float& sd)
     return a < 0.0625f ? small : big;
 }
 
+// The backward's tanh: 1 - tanh(u)^2 exactly as tanh_q (it scales dX), but
+// tanh itself only enters the dgamma column sums, where a relative error of
+// 2^-15 per term is far below what the fp32 sums can show. So below
+// |u| = 1/128, where 1 - 2q would lose more than that, tanh(u) is u itself
+// (relative error u^2/3 < 2^-15.6), with no polynomial: the Dynamic Tanh
+// backward ran about 10 % faster at 16384 x 4096 than with tanh_q.
+__device__ __forceinline__ float tanh_for_sums(float u, float& sd)
+{
+    const float a = __builtin_fabsf(u);
+    const float q = __builtin_amdgcn_rcpf(__expf(2.0f * a) + 1.0f);
+    sd = 4.0f * q * (1.0f - q);
+    const float big = __builtin_copysignf(__builtin_fmaf(-2.0f, q, 1.0f), u);
+    return a < 0.0078125f ? u : big;
+}
+
 // ---------------------------------------------------------------------------
 // Wave-level sums.
 // ---------------------------------------------------------------------------
@@ -846,10 +861,10 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                     const float dyv = cget<CT, VEC>(cur.dy[u][k], e);
                     float d;
                     if constexpr (KIND == DYT) {
-                        // dX needs only 1 - t^2 (accurate from tanh_q); t
-                        // enters only the dgamma sums
+                        // dX needs only 1 - t^2; t enters only the dgamma
+                        // sums
                         float sd;
-                        const float t = tanh_q(alpha * v, sd);
+                        const float t = tanh_for_sums(alpha * v, sd);
                         const float gy = dyv * gam[k][e];
                         d = gy * alpha * sd;
                         accg[k][e] = __builtin_fmaf(dyv, t, accg[k][e]);

@@ -80,6 +80,16 @@ def test_mod_ragged_samples_at_benchmark_width():
     compare("mod", run("mod", d, 1e-5), reference("mod", d, 1e-5), d, "mod B=6 N=606 D=3072")
 
 
+@pytest.mark.parametrize("x_scale", [1e-3, 0.02])
+def test_dyt_small_arguments(x_scale):
+    """alpha * x around and below the 1/128 switch of the kernel's tanh, with
+    beta = 0 so that every output is as small as tanh itself: relative
+    accuracy on both sides of the switch."""
+    d = workloads.random_case("dyt", 256, 1024, 520, x_scale=x_scale)
+    d["beta"][:] = 0
+    compare("dyt", run("dyt", d, 1e-5), reference("dyt", d, 1e-5), d, f"dyt x~{x_scale}")
+
+
 def test_mod_without_modulation_is_rmsnorm():
     """scale = shift = 0 gives the RMSNorm outputs of the training-pair path."""
     from gpu_cases import run_gpu
