@@ -393,17 +393,20 @@ hipError_t launch_gemv_mm(int mm, dim3 grid, hipStream_t s, const GemvArgs& a)
 {
     const dim3 block(kern::kGemvBlock);
     // the wide 16-byte tiles serve one or two X rows only; W loads in flight
-    // per register set: 8 for one or two X rows, 4 from three (5-9 % faster
-    // at M = 4 than 8, whose registers cost waves)
+    // per register set: 8 for one or two X rows, 4 for RMSNorm at three or
+    // four, 2 for LayerNorm there (two more product rows) and for five to
+    // eight (fewer loads in flight, more waves: 5-9 % faster at M = 4 with
+    // 4 than 8, and 4-11 % faster at M = 8 and for LayerNorm at M = 4 with 2
+    // than 4, at N = 12288)
     constexpr bool ALL = !(VEC == 8 && RPW == 1);
     switch (mm) {
     case 1: return launch_k(kern::gemv_kernel<ST, VEC, 1, LNF, RPW, 8>, grid, block, s, a);
     case 2: return launch_k(kern::gemv_kernel<ST, VEC, 2, LNF, RPW, 8>, grid, block, s, a);
     case 4:
-        if constexpr (ALL) return launch_k(kern::gemv_kernel<ST, VEC, 4, LNF, RPW, 4>, grid, block, s, a);
+        if constexpr (ALL) return launch_k(kern::gemv_kernel<ST, VEC, 4, LNF, RPW, LNF ? 2 : 4>, grid, block, s, a);
         break;
     case 8:
-        if constexpr (ALL) return launch_k(kern::gemv_kernel<ST, VEC, 8, LNF, RPW, 4>, grid, block, s, a);
+        if constexpr (ALL) return launch_k(kern::gemv_kernel<ST, VEC, 8, LNF, RPW, 2>, grid, block, s, a);
         break;
     }
     return hipErrorInvalidValue;
