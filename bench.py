@@ -5,10 +5,12 @@
 One step is one pass of the whole training pair over one batch: the forward
 (Y, rstd) of one batch and the backward (dX, dgamma, via the row kernel and
 the column reduce) of one batch. Inputs are resident in HBM before timing.
-Several buffer sets rotate so that no kernel reads data another kernel of
-the same step has just touched: step k runs the forward on set k mod S and
-the backward on set (k - 1) mod S (whose forward ran one step earlier),
-which keeps the Infinity Cache from serving re-reads.
+Several buffer sets rotate so that no kernel reads data another kernel has
+touched recently: step k runs the forward on set k mod S and the backward on
+set (k + S/2) mod S (S >= 4), whose forward ran S/2 steps earlier, with more
+than the Infinity Cache's 256 MB of traffic in between. (A backward on the
+set forwarded one step earlier was measured re-reading part of it from that
+cache when the forward's loads allocate there.)
 
 Printed: one JSON line with the whole-step throughput (algorithmic HBM bytes
 per second: every tensor read or written once, workspace excluded), rows/s,
@@ -94,6 +96,11 @@ def gemv_bytes(M: int, K: int, N: int, act: str = "f16", param: str = "f16", ln:
     of the K slices are workspace and not counted."""
     a, p = SIZE[act], SIZE[param]
     return a * (M * K + K * N + M * N) + p * K * (2 if ln else 1)
+
+
+def back_set(k: int, S: int) -> int:
+    """Buffer set of step k's backward: the one forwarded S/2 steps ago."""
+    return (k + S // 2) % S
 
 
 def kernel_hash(kind: str = "rms") -> str:
@@ -406,7 +413,7 @@ def bench_other(args, w, torch, mn, act, param, dxt):
 
     up = {k: upload(v) for k, v in d.items()}
     scal = torch.tensor(np.asarray(w.scalars, np.float32), device=dev)
-    S = max(2, args.sets)
+    S = max(4, args.sets)
     sets = []
     for s in range(S):
         b = {"X": (up["X"] if s == 0 else up["X"].clone()).view(shp),
@@ -469,14 +476,14 @@ def bench_other(args, w, torch, mn, act, param, dxt):
     for b in sets:
         fwd(b)
     for k in range(W):
-        fwd(sets[k % S]); bwd(sets[(k - 1) % S])
+        fwd(sets[k % S]); bwd(sets[back_set(k, S)])
     torch.cuda.synchronize()
     ev = [[HipEvent() for _ in range(3)] for _ in range(K)]
     t0 = time.perf_counter()
     for k in range(K):
         e = ev[k]
         e[0].record(stream); fwd(sets[(W + k) % S]); e[1].record(stream)
-        bwd(sets[(W + k - 1) % S]); e[2].record(stream)
+        bwd(sets[back_set(W + k, S)]); e[2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
@@ -578,7 +585,7 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    S = max(2, args.sets)
+    S = max(4, args.sets)
     up = {k: upload(v) for k, v in d.items()}
     sets = []
     for s in range(S):
@@ -634,7 +641,7 @@ def main():
 
     def step(k, rows_events=None):
         f = sets[k % S]
-        bk = sets[(k - 1) % S]
+        bk = sets[back_set(k, S)]
         fwd(f)
         if rows_events: rows_events[0].record(stream)
         bwd_rows(bk)
@@ -660,7 +667,7 @@ def main():
     dg = [[HipEvent() for _ in range(4)] for _ in range(K)]
     for k in range(K):
         f = sets[k % S]
-        bk = sets[(k - 1) % S]
+        bk = sets[back_set(k, S)]
         dg[k][0].record(stream); fwd(f); dg[k][1].record(stream); bwd_rows(bk)
         dg[k][2].record(stream); reduce(bk); dg[k][3].record(stream)
     torch.cuda.synchronize()
