@@ -75,6 +75,26 @@ def test_long_rows_few_columns(ln):
     compare(run(d, 1e-5, ln), reference(d, 1e-5, ln), d, 1e-5, ln, f"{M}x{K}x{N}")
 
 
+@pytest.mark.parametrize("M,K,N,ln", [(4, 4096, 12288, False), (4, 4096, 12288, True),
+                                     (1, 4096, 14336, False), (8, 1024, 4096, True),
+                                     (1, 131072, 64, False)])
+def test_repeated_calls_bitwise(M, K, N, ln):
+    """400 back-to-back calls through one workspace give the first call's bits
+    every time: every workgroup that completes a tile reads every partial and
+    statistic it needs, whichever XCD wrote them."""
+    d = _case(M, K, N, 21, ln)
+    X, g, W = dev(d["X"]), dev(d["gamma"]), dev(d["W"])
+    b = dev(d["beta"]) if ln else None
+    ws = workspace(M, N, K)
+    ys = [torch.empty(M, N, dtype=X.dtype, device="cuda") for _ in range(400)]
+    for y in ys:
+        mn.mn_fused_norm_gemv_ex(X, g, W, y, 1e-5, ws, beta=b)
+    torch.cuda.synchronize()
+    first = ys[0].view(torch.int16)
+    bad = [i for i, y in enumerate(ys) if not torch.equal(y.view(torch.int16), first)]
+    assert not bad, f"{M}x{K}x{N}: calls {bad[:8]} differ from the first"
+
+
 def test_counters_back_at_zero():
     """Each call leaves every word of the shared workspace's counter area
     (16384 words after the 64 of statistics) at zero: the block that
