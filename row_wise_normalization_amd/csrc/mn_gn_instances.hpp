@@ -16,6 +16,23 @@ hipError_t gn_launch(Kernel k, const GnPlan& p, const GnArgs& a, hipStream_t s)
                            dim3((unsigned)p.block), args, 0, s);
 }
 
+// The backward stages its first dY chunks in LDS, at most kGnStageBytes per
+// workgroup (16-byte chunks only; `chunks` per lane in this instance). At
+// 32 x 320 x 4096 (G = 32), 32 KB (four of a lane's ten chunks) took the
+// backward from 55.5 to 51.2 us; larger stages gained little more.
+constexpr int64_t kGnStageBytes = 32 * 1024;
+
+template <typename Kernel>
+hipError_t gn_launch_bwd(Kernel k, const GnPlan& p, GnArgs a, hipStream_t s, int chunks,
+                         bool stage)
+{
+    const int64_t fit = kGnStageBytes / (16 * (int64_t)p.block);
+    a.sk = stage ? (int32_t)(fit < chunks ? fit : chunks) : 0;
+    void* args[] = {&a};
+    return hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)p.grid),
+                           dim3((unsigned)p.block), args, (size_t)a.sk * 16 * p.block, s);
+}
+
 }  // namespace
 
 // only the shapes within the register budget are instantiated
@@ -29,9 +46,9 @@ hipError_t gn_launch(Kernel k, const GnPlan& p, const GnArgs& a, hipStream_t s)
 #define MN_GN_BWD_U(SH, T, VEC, CPT, UL, U)                                                  \
     case SH * 8 + UL:                                                                        \
         if constexpr (gn_fits(ST, VEC, T, CPT, U))                                              \
-            return gn_launch(                                                                \
+            return gn_launch_bwd(                                                            \
                 kern::gn_bwd_kernel<ST, OT, T, st_vec(ST, VEC), st_cpt(ST, VEC, CPT), U>, p, a, \
-                s);                                                                          \
+                s, U * st_cpt(ST, VEC, CPT), VEC == 8);                                      \
         else                                                                                 \
             return hipErrorInvalidValue;
 #define MN_GN_US(M, SH, T, VEC, CPT)                                                      \

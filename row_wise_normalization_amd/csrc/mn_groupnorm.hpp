@@ -19,8 +19,10 @@
 //             [N][C] partials of dgamma and dbeta; the slice sums
 //             A = sum_c gamma[c] P_c, B = sum_c gamma[c] Q_c in channel-row
 //             group order; dX = rstd * (gamma[c] dY - B / M - xhat A / M),
-//             M = Cg * L. A second kernel (the column reduce) adds the N
-//             partial rows of dgamma and dbeta in fixed order.
+//             M = Cg * L, with dY for this last pass partly from LDS (the
+//             first chunks of each lane, staged after the first pass) and
+//             partly read again. A second kernel (the column reduce) adds
+//             the N partial rows of dgamma and dbeta in fixed order.
 // Every load is unconditional (row and column indices past the slice are
 // clamped; their values are masked out), every sum has a fixed order.
 #pragma once
@@ -169,6 +171,10 @@ __global__ void __launch_bounds__(kGnMaxBlock) gn_bwd_kernel(const GnArgs a)
     const int n = s / a.G;
     const int grp = s % a.G;
 
+    // dY staging: the first a.sk chunks of each lane, lane-private 16-byte
+    // slots [chunk][lane] (16-byte chunks only)
+    extern __shared__ u4 gn_stage[];
+    constexpr bool STAGE = sizeof(HV) == 16;
     GnSlice<ST, T, VEC, CPT, U> t;
     gn_map(t, a, s, gi, l, rpb);
     HV dy[U][CPT];
@@ -201,6 +207,14 @@ __global__ void __launch_bounds__(kGnMaxBlock) gn_bwd_kernel(const GnArgs a)
             }
         v[2 * u] = p;
         v[2 * u + 1] = q;
+    }
+    if constexpr (STAGE) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int k = 0; k < CPT; ++k)
+                if (u * CPT + k < a.sk)
+                    gn_stage[(u * CPT + k) * blockDim.x + tid] = __builtin_bit_cast(u4, dy[u][k]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -236,13 +250,23 @@ __global__ void __launch_bounds__(kGnMaxBlock) gn_bwd_kernel(const GnArgs a)
     }
     const float fM = (float)a.Cg * (float)a.L;
     const float c1 = A / fM, c2 = B / fM;
-    // dY again (this workgroup read it moments ago: a cache hit), so that
-    // it does not hold registers across the reductions
+    // dY again rather than held in registers across the reductions: the
+    // staged chunks from LDS, the rest from memory (this workgroup read them
+    // moments ago: mostly Infinity Cache hits)
     HV dy2[U][CPT];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) dy2[u][k] = sload<ST, VEC, 0>(a.dY, t.off(u, k));
+        for (int k = 0; k < CPT; ++k) {
+            if constexpr (STAGE) {
+                if (u * CPT + k < a.sk)
+                    dy2[u][k] = __builtin_bit_cast(HV, gn_stage[(u * CPT + k) * blockDim.x + tid]);
+                else
+                    dy2[u][k] = sload<ST, VEC, 0>(a.dY, t.off(u, k));
+            } else {
+                dy2[u][k] = sload<ST, VEC, 0>(a.dY, t.off(u, k));
+            }
+        }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll

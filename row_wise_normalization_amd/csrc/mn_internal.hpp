@@ -133,6 +133,7 @@ struct GnArgs {
     float* part_b;           // [N][Cp] per-sample sums of dY per channel
     int32_t C, L, G, Cg, Cp, pdt;
     float eps;
+    int32_t sk;              // backward: dY chunks per lane staged in LDS (the first sk)
 };
 
 struct GnPlan {
