@@ -294,7 +294,8 @@ __device__ __forceinline__ float tanh_for_sums(float u, float& sd)
 {
     const float a = __builtin_fabsf(u);
     const float q = __builtin_amdgcn_rcpf(exp_twice(a) + 1.0f);
-    sd = 4.0f * q * (1.0f - q);
+    const float q4 = 4.0f * q;                 // exact
+    sd = __builtin_fmaf(-q4, q, q4);           // 4q(1 - q), one rounding
     const float big = __builtin_copysignf(__builtin_fmaf(-2.0f, q, 1.0f), u);
     return a < 0.0078125f ? u : big;
 }
@@ -874,10 +875,11 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                         float sd;
                         const float t = tanh_for_sums(alpha * v, sd);
                         const float gy = dyv * gam[k][e];
-                        d = gy * alpha * sd;
+                        const float gs = gy * sd;
+                        d = gs * alpha;
                         accg[k][e] = __builtin_fmaf(dyv, t, accg[k][e]);
                         accb[k][e] += dyv;
-                        accs[0] = __builtin_fmaf(gy * v, sd, accs[0]);
+                        accs[0] = __builtin_fmaf(gs, v, accs[0]);
                     } else if constexpr (KIND == POLY) {
                         const float v2 = v * v;
                         const float P = __builtin_fmaf(v, __builtin_fmaf(v, A3, A2), A1);
