@@ -23,6 +23,7 @@ import workloads
 import row_wise_normalization_amd as mn
 from gpu_cases import dev, empty, host, say
 
+
 def run(d, eps, ln, offset=0):
     X = dev(d["X"], offset)
     g = dev(d["gamma"], offset)
