@@ -31,3 +31,12 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    import record
+    lines = record.summary()
+    if lines:
+        terminalreporter.write_sep("-", "parity record")
+        for ln in lines:
+            terminalreporter.write_line(ln)

@@ -8,6 +8,7 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
+import every_row
 import oracle
 import parity
 import row_wise_normalization_amd as mn
@@ -107,29 +108,40 @@ def run_gpu(kind: str, d: Dict[str, np.ndarray], eps: float, offset: int = 0,
     return out
 
 
-def reference(kind: str, d: Dict[str, np.ndarray], eps: float, rows: Optional[np.ndarray] = None,
-              use_dh: bool = True) -> Dict[str, np.ndarray]:
-    """Oracle results: per-row outputs for ``rows`` (all rows when None) and
-    parameter gradients over all rows."""
+def reference(kind: str, d: Dict[str, np.ndarray], eps: float, rows=None,
+              use_dh: bool = True, per_row: bool = True, grads: bool = True
+              ) -> Dict[str, np.ndarray]:
+    """Oracle results: per-row outputs for ``rows`` (all rows when None; an
+    index array or a slice) and parameter gradients over all rows. Either
+    half can be left out (``per_row``, ``grads``)."""
     sub = (lambda a: a) if rows is None else (lambda a: np.ascontiguousarray(a[rows]))
     X, dY = d["X"], d["dY"]
     o: Dict[str, np.ndarray] = {}
     if kind == "rms":
-        o["Y"], o["rstd"] = oracle.rmsnorm_forward(sub(X), d["gamma"], eps)
-        o["dX"], _ = oracle.rmsnorm_backward(sub(X), d["gamma"], sub(dY), eps)
-        _, o["dgamma"] = oracle.rmsnorm_backward(X, d["gamma"], dY, eps, want_dx=False)
+        if per_row:
+            o["Y"], o["rstd"] = oracle.rmsnorm_forward(sub(X), d["gamma"], eps)
+            o["dX"], _ = oracle.rmsnorm_backward(sub(X), d["gamma"], sub(dY), eps)
+        if grads:
+            _, o["dgamma"] = oracle.rmsnorm_backward(X, d["gamma"], dY, eps, want_dx=False)
     elif kind == "ln":
-        o["Y"], o["mean"], o["rstd"] = oracle.layernorm_forward(sub(X), d["gamma"], d["beta"], eps)
-        o["dX"], _, _ = oracle.layernorm_backward(sub(X), d["gamma"], sub(dY), eps)
-        _, o["dgamma"], o["dbeta"] = oracle.layernorm_backward(X, d["gamma"], dY, eps,
-                                                               want_dx=False)
+        if per_row:
+            o["Y"], o["mean"], o["rstd"] = oracle.layernorm_forward(sub(X), d["gamma"],
+                                                                   d["beta"], eps)
+            o["dX"], _, _ = oracle.layernorm_backward(sub(X), d["gamma"], sub(dY), eps)
+        if grads:
+            _, o["dgamma"], o["dbeta"] = oracle.layernorm_backward(X, d["gamma"], dY, eps,
+                                                                   want_dx=False)
     elif kind == "add":
         R = d["R"]
         dH = d["dH"] if use_dh else None
-        _, o["H16"], o["Y"], o["rstd"] = oracle.add_rmsnorm_forward(sub(X), sub(R), d["gamma"], eps)
-        o["dX"], _ = oracle.add_rmsnorm_backward(sub(X), sub(R), d["gamma"], sub(dY),
-                                                 None if dH is None else sub(dH), eps)
-        _, o["dgamma"] = oracle.add_rmsnorm_backward(X, R, d["gamma"], dY, dH, eps, want_dx=False)
+        if per_row:
+            _, o["H16"], o["Y"], o["rstd"] = oracle.add_rmsnorm_forward(sub(X), sub(R),
+                                                                        d["gamma"], eps)
+            o["dX"], _ = oracle.add_rmsnorm_backward(sub(X), sub(R), d["gamma"], sub(dY),
+                                                     None if dH is None else sub(dH), eps)
+        if grads:
+            _, o["dgamma"] = oracle.add_rmsnorm_backward(X, R, d["gamma"], dY, dH, eps,
+                                                         want_dx=False)
     return o
 
 
@@ -164,28 +176,35 @@ def cancel_scales(kind: str, d: Dict[str, np.ndarray], ref: Dict[str, np.ndarray
 
 
 def compare(kind: str, gpu: Dict[str, np.ndarray], ref: Dict[str, np.ndarray], what: str,
-            rows: Optional[np.ndarray] = None, mean_atol: float = 0.0,
-            inputs: Optional[Dict[str, np.ndarray]] = None, use_dh: bool = True
-            ) -> Dict[str, float]:
-    """Check every element of the GPU outputs (restricted to ``rows``)
-    against the oracle; returns the worst error per output. With ``inputs``
-    the fp32 cancellation allowance of parity.check_out applies to 16-bit
-    outputs; without it every element must be within 2 ulp. float32 outputs
-    need ``inputs`` (their bound is relative to the fp32 terms)."""
+            rows=None, mean_atol: float = 0.0,
+            inputs: Optional[Dict[str, np.ndarray]] = None, use_dh: bool = True,
+            per_row: bool = True, grads: bool = True) -> Dict[str, float]:
+    """Check every element of the GPU outputs (restricted to ``rows``, an
+    index array or a slice) against the oracle; returns the worst error per
+    output and, for 16-bit outputs, how many elements only the fp32
+    cancellation allowance admitted. With ``inputs`` that allowance of
+    parity.check_out applies; without it every element must be within
+    2 ulp. float32 outputs need ``inputs`` (their bound is relative to the
+    fp32 terms). ``per_row`` and ``grads`` select the halves to check."""
     sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    w: Dict[str, float] = {}
+    if grads:
+        w["dgamma"] = parity.check_grad(gpu["dgamma"], ref["dgamma"], f"{what} dgamma")
+        if kind == "ln":
+            w["dbeta"] = parity.check_grad(gpu["dbeta"], ref["dbeta"], f"{what} dbeta")
+    if not per_row:
+        return w
     sdx = sy = None
     if inputs is not None:
         sdx, sy = cancel_scales(kind, inputs, ref, rows, use_dh)
     if inputs is None and np.float32 in (gpu["Y"].dtype, gpu["dX"].dtype):
         raise ValueError("float32 outputs are checked against the scale of their fp32 terms; "
                          "pass the inputs")
-    w: Dict[str, float] = {}
     w["Y_ulp"], w["Y_fp32_admitted"] = parity.check_out(sel(gpu["Y"]), ref["Y"], f"{what} Y",
                                                         scale=sy)
     w["dX_ulp"], w["dX_fp32_admitted"] = parity.check_out(sel(gpu["dX"]), ref["dX"],
                                                           f"{what} dX", scale=sdx)
     w["rstd_rel"] = parity.check_stat(sel(gpu["rstd"]), ref["rstd"], f"{what} rstd")
-    w["dgamma"] = parity.check_grad(gpu["dgamma"], ref["dgamma"], f"{what} dgamma")
     if kind == "ln":
         if inputs is not None:
             # a mean near zero is a cancellation of fp32 terms of size mean|x|
@@ -194,7 +213,6 @@ def compare(kind: str, gpu: Dict[str, np.ndarray], ref: Dict[str, np.ndarray], w
             mean_atol = np.maximum(mean_atol, parity.FP32_K * 2.0 ** -24 * xa)
         w["mean_rel"] = parity.check_stat(sel(gpu["mean"]), ref["mean"], f"{what} mean",
                                           atol=mean_atol)
-        w["dbeta"] = parity.check_grad(gpu["dbeta"], ref["dbeta"], f"{what} dbeta")
     if kind == "add":
         hg, hr = sel(gpu["H"]), ref["H16"]
         assert hg.dtype == hr.dtype, f"{what} H: {hg.dtype} vs {hr.dtype}"
@@ -204,4 +222,24 @@ def compare(kind: str, gpu: Dict[str, np.ndarray], ref: Dict[str, np.ndarray], w
         # +0 and -0 are the same sum; otherwise H must be the exact rounded sum
         same = (h == r) | (((h | r) & ~sign) == 0)
         assert same.all(), f"{what} H: {int((~same).sum())} elements differ from round(x + r)"
+    return w
+
+
+def compare_every_row(kind: str, gpu: Dict[str, np.ndarray], d: Dict[str, np.ndarray],
+                      eps: float, what: str, inputs: Optional[Dict[str, np.ndarray]] = None,
+                      use_dh: bool = True) -> Dict[str, float]:
+    """compare() over every row of a full-size call: the oracle runs on
+    blocks of rows (bounded host memory, several blocks at a time), the
+    parameter gradients once over all rows. Returns the worst error per
+    output, the admitted counts summed over the blocks and ``rows_checked``."""
+    N, D = d["X"].shape
+    ref_g = reference(kind, d, eps, use_dh=use_dh, per_row=False)
+    w = compare(kind, gpu, ref_g, what, per_row=False)
+
+    def block(rows):
+        ref = reference(kind, d, eps, rows=rows, use_dh=use_dh, grads=False)
+        return compare(kind, gpu, ref, what, rows=rows, inputs=inputs, use_dh=use_dh,
+                       grads=False)
+
+    w.update(every_row.run_blocks(N, D, block))
     return w

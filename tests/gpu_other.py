@@ -16,6 +16,7 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
+import every_row
 import oracle
 import parity
 import workloads
@@ -84,32 +85,44 @@ def run(kind: str, d: Dict[str, np.ndarray], eps: float, offset: int = 0,
 
 
 def reference(kind: str, d: Dict[str, np.ndarray], eps: float, rows=None, alpha: float = ALPHA,
-              params=POLY) -> Dict[str, np.ndarray]:
-    """Oracle results: per-row outputs for ``rows`` (all when None) and
-    parameter gradients over all rows."""
+              params=POLY, per_row: bool = True, grads: bool = True) -> Dict[str, np.ndarray]:
+    """Oracle results: per-row outputs for ``rows`` (all when None; an index
+    array, or a slice that for "mod" lies inside one sample) and parameter
+    gradients over all rows. Either half can be left out."""
     sub = (lambda a: a) if rows is None else (lambda a: np.ascontiguousarray(a[rows]))
     X, dY = d["X"], d["dY"]
     o: Dict[str, np.ndarray] = {}
     if kind == "dyt":
-        o["Y"] = oracle.dyt_forward(sub(X), alpha, d["gamma"], d["beta"])
-        o["dX"] = oracle.dyt_backward(sub(X), alpha, d["gamma"], sub(dY))[0]
-        _, da, o["dgamma"], o["dbeta"] = oracle.dyt_backward(X, alpha, d["gamma"], dY,
-                                                             want_dx=False)
-        o["dalpha"] = np.array([da])
+        if per_row:
+            o["Y"] = oracle.dyt_forward(sub(X), alpha, d["gamma"], d["beta"])
+            o["dX"] = oracle.dyt_backward(sub(X), alpha, d["gamma"], sub(dY))[0]
+        if grads:
+            _, da, o["dgamma"], o["dbeta"] = oracle.dyt_backward(X, alpha, d["gamma"], dY,
+                                                                 want_dx=False)
+            o["dalpha"] = np.array([da])
     elif kind == "poly":
         w, b = np.asarray(params[:3], np.float64), float(params[3])
-        o["Y"], o["rstd"] = oracle.polynorm_forward(sub(X), w, b, eps)
-        o["dX"] = oracle.polynorm_backward(sub(X), w, sub(dY), eps)[0]
-        _, dw, db = oracle.polynorm_backward(X, w, dY, eps, want_dx=False)
-        o["dparams"] = np.concatenate([dw, [db]])
+        if per_row:
+            o["Y"], o["rstd"] = oracle.polynorm_forward(sub(X), w, b, eps)
+            o["dX"] = oracle.polynorm_backward(sub(X), w, sub(dY), eps)[0]
+        if grads:
+            _, dw, db = oracle.polynorm_backward(X, w, dY, eps, want_dx=False)
+            o["dparams"] = np.concatenate([dw, [db]])
     elif kind == "mod":
-        if rows is None:
+        S = X.shape[0] // d["scale"].shape[0]
+        if per_row and rows is None:
             o["Y"], o["rstd"] = oracle.modrms_forward(X, d["gamma"], d["scale"], d["shift"], eps)
             o["dX"] = oracle.modrms_backward(X, d["gamma"], d["scale"], dY, eps)[0]
-        else:
+        elif per_row and isinstance(rows, slice):
+            # a block of rows of one sample: that sample's scale and shift
+            b = rows.start // S
+            assert (rows.stop - 1) // S == b, "a row block must lie inside one sample"
+            sci, shi = d["scale"][b:b + 1], d["shift"][b:b + 1]
+            o["Y"], o["rstd"] = oracle.modrms_forward(sub(X), d["gamma"], sci, shi, eps)
+            o["dX"] = oracle.modrms_backward(sub(X), d["gamma"], sci, sub(dY), eps)[0]
+        elif per_row:
             # per-row outputs of sampled rows: one row at a time with its sample's
             # scale and shift
-            S = X.shape[0] // d["scale"].shape[0]
             Ys, rs, dXs = [], [], []
             for i in rows:
                 b = i // S
@@ -119,8 +132,9 @@ def reference(kind: str, d: Dict[str, np.ndarray], eps: float, rows=None, alpha:
                 Ys.append(y[0]); rs.append(r[0])
                 dXs.append(oracle.modrms_backward(xi, d["gamma"], sci, dyi, eps)[0][0])
             o["Y"], o["rstd"], o["dX"] = np.array(Ys), np.array(rs), np.array(dXs)
-        _, o["dgamma"], o["dscale"], o["dshift"] = oracle.modrms_backward(
-            X, d["gamma"], d["scale"], dY, eps, want_dx=False)
+        if grads:
+            _, o["dgamma"], o["dscale"], o["dshift"] = oracle.modrms_backward(
+                X, d["gamma"], d["scale"], dY, eps, want_dx=False)
     return o
 
 
@@ -147,7 +161,12 @@ def scales(kind: str, d, ref, rows=None, alpha: float = ALPHA, params=POLY):
         return sy, sdx
     # mod
     S = d["X"].shape[0] // d["scale"].shape[0]
-    idx = np.arange(d["X"].shape[0]) if rows is None else np.asarray(rows)
+    if rows is None:
+        idx = np.arange(d["X"].shape[0])
+    elif isinstance(rows, slice):
+        idx = np.arange(rows.start, rows.stop)
+    else:
+        idx = np.asarray(rows)
     smp = idx // S
     sc = _f64(d["scale"])[smp]
     sh = _f64(d["shift"])[smp]
@@ -169,28 +188,58 @@ def grad_scalar(gpu, ref, what, terms: int, mag: float):
 
 
 def compare(kind: str, gpu, ref, d, what: str, rows=None, strict: bool = False,
-            alpha: float = ALPHA, params=POLY) -> Dict[str, float]:
+            alpha: float = ALPHA, params=POLY, per_row: bool = True,
+            grads: bool = True) -> Dict[str, float]:
     sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    w: Dict[str, float] = {}
+    n = d["X"].size
+    if grads:
+        if kind == "dyt":
+            w["dgamma"] = parity.check_grad(gpu["dgamma"], ref["dgamma"], f"{what} dgamma")
+            w["dbeta"] = parity.check_grad(gpu["dbeta"], ref["dbeta"], f"{what} dbeta")
+            mag = float(np.abs(_f64(d["dY"]) * _f64(d["X"])).mean() *
+                        np.abs(_f64(d["gamma"])).max())
+            w["dalpha"] = grad_scalar(gpu["dalpha"], ref["dalpha"], f"{what} dalpha", n, mag)
+        elif kind == "poly":
+            mag = float(np.abs(_f64(d["dY"])).mean())
+            w["dparams"] = grad_scalar(gpu["dparams"], ref["dparams"], f"{what} dparams", n,
+                                       mag)
+        else:
+            w["dgamma"] = parity.check_grad(gpu["dgamma"], ref["dgamma"], f"{what} dgamma")
+            w["dscale"] = parity.check_grad(gpu["dscale"], ref["dscale"], f"{what} dscale")
+            w["dshift"] = parity.check_grad(gpu["dshift"], ref["dshift"], f"{what} dshift")
+    if not per_row:
+        return w
     sy, sdx = scales(kind, d, ref, rows, alpha, params)
     if strict and gpu["Y"].dtype != np.float32:
         sy = sdx = None
-    w: Dict[str, float] = {}
     w["Y"], w["Y_admitted"] = parity.check_out(sel(gpu["Y"]), ref["Y"], f"{what} Y", scale=sy)
     w["dX"], w["dX_admitted"] = parity.check_out(sel(gpu["dX"]), ref["dX"], f"{what} dX",
                                                  scale=sdx)
-    n = d["X"].size
-    if kind == "dyt":
-        w["dgamma"] = parity.check_grad(gpu["dgamma"], ref["dgamma"], f"{what} dgamma")
-        w["dbeta"] = parity.check_grad(gpu["dbeta"], ref["dbeta"], f"{what} dbeta")
-        mag = float(np.abs(_f64(d["dY"]) * _f64(d["X"])).mean() * np.abs(_f64(d["gamma"])).max())
-        w["dalpha"] = grad_scalar(gpu["dalpha"], ref["dalpha"], f"{what} dalpha", n, mag)
-    elif kind == "poly":
+    if kind != "dyt":
         w["rstd"] = parity.check_stat(sel(gpu["rstd"]), ref["rstd"], f"{what} rstd")
-        mag = float(np.abs(_f64(d["dY"])).mean())
-        w["dparams"] = grad_scalar(gpu["dparams"], ref["dparams"], f"{what} dparams", n, mag)
-    else:
-        w["rstd"] = parity.check_stat(sel(gpu["rstd"]), ref["rstd"], f"{what} rstd")
-        w["dgamma"] = parity.check_grad(gpu["dgamma"], ref["dgamma"], f"{what} dgamma")
-        w["dscale"] = parity.check_grad(gpu["dscale"], ref["dscale"], f"{what} dscale")
-        w["dshift"] = parity.check_grad(gpu["dshift"], ref["dshift"], f"{what} dshift")
+    return w
+
+
+def compare_every_row(kind: str, gpu, d, eps: float, what: str, strict: bool = False,
+                      alpha: float = ALPHA, params=POLY) -> Dict[str, float]:
+    """compare() over every row of a full-size call, the oracle on blocks of
+    rows (for "mod" blocks never straddle two samples); parameter gradients
+    once over all rows."""
+    N, D = d["X"].shape
+    w = compare(kind, gpu, reference(kind, d, eps, alpha=alpha, params=params, per_row=False),
+                d, what, per_row=False, alpha=alpha, params=params)
+    align = 1
+    if kind == "mod":
+        S = N // d["scale"].shape[0]
+        # blocks of whole samples, or of a divisor of the sample's rows
+        rows = max(1, every_row.BLOCK_ELEMS // D)
+        align = S if rows >= S else max(r for r in range(1, rows + 1) if S % r == 0)
+
+    def block(rows):
+        ref = reference(kind, d, eps, rows=rows, alpha=alpha, params=params, grads=False)
+        return compare(kind, gpu, ref, d, what, rows=rows, strict=strict, alpha=alpha,
+                       params=params, grads=False)
+
+    w.update(every_row.run_blocks(N, D, block, align=align))
     return w

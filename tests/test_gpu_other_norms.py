@@ -4,9 +4,10 @@ import numpy as np
 import pytest
 import torch
 
+import record
 import workloads
 from gpu_cases import say
-from gpu_other import compare, reference, run
+from gpu_other import compare, compare_every_row, reference, run
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +41,9 @@ def test_width_sweep(kind, D):
     N = 1020 if D <= 1024 else 332      # several tiles and a ragged tail
     say(f"[other] sweep {kind} N={N} D={D}")
     d = _case(kind, N, D, 200 + D)
-    compare(kind, run(kind, d, 1e-5), reference(kind, d, 1e-5), d, f"{kind} {N}x{D}")
+    w = compare(kind, run(kind, d, 1e-5), reference(kind, d, 1e-5), d, f"{kind} {N}x{D}")
+    record.admitted(f"other sweep {kind} {N}x{D}", w["Y_admitted"] + w["dX_admitted"],
+                    2 * N * D)
 
 
 @pytest.mark.parametrize("act,dxt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"),
@@ -118,13 +121,16 @@ FULL = ["dyt_16384x4096", "poly_16384x4096", "mod_rms_16384x3072"]
 @pytest.mark.slow
 @pytest.mark.parametrize("name", FULL)
 def test_full_size(name):
+    """Every row of the full-size workload."""
     w = workloads.WORKLOADS[name]
     say(f"[other] full {name}: generating")
     d = workloads.generate(w)
     say(f"[other] full {name}: gpu")
     gpu = run(w.kind, d, w.eps)
-    rows = workloads.sample_rows(w.N, 2048)
-    say(f"[other] full {name}: oracle on {len(rows)} rows")
-    ref = reference(w.kind, d, w.eps, rows=rows)
-    worst = compare(w.kind, gpu, ref, d, name, rows=rows)
-    say(f"[other] full {name}: {worst}")
+    say(f"[other] full {name}: oracle on every row")
+    r = compare_every_row(w.kind, gpu, d, w.eps, name)
+    n = r.get('Y_admitted', 0) + r.get('dX_admitted', 0)
+    msg = f"full {name}: rows checked = {r['rows_checked']} of {w.N}, admitted = {n}"
+    say(f"[other] {msg}; worst {r}")
+    record.line(msg)
+    assert r["rows_checked"] == w.N
