@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 import torch
 
+import parity
 import record
 import workloads
 from gpu_cases import say
@@ -42,8 +43,9 @@ def test_width_sweep(kind, D):
     say(f"[other] sweep {kind} N={N} D={D}")
     d = _case(kind, N, D, 200 + D)
     w = compare(kind, run(kind, d, 1e-5), reference(kind, d, 1e-5), d, f"{kind} {N}x{D}")
-    record.admitted(f"other sweep {kind} {N}x{D}", w["Y_admitted"] + w["dX_admitted"],
-                    2 * N * D)
+    n = w["Y_admitted"] + w["dX_admitted"]
+    record.admitted(f"other sweep {kind} {N}x{D}", n, 2 * N * D)
+    assert n <= parity.allowance_bound(D, "f16") * 2 * N * D, f"{kind} {N}x{D}: {n} admitted"
 
 
 @pytest.mark.parametrize("act,dxt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"),
@@ -134,3 +136,4 @@ def test_full_size(name):
     say(f"[other] {msg}; worst {r}")
     record.line(msg)
     assert r["rows_checked"] == w.N
+    assert n == 0

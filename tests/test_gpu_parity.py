@@ -8,15 +8,17 @@ The backward is fed the statistics saved by the GPU forward, as in training.
 The named workloads are held to 2 ulp on every element with no allowance.
 The sweeps may admit an element whose exact value is a cancellation of much
 larger fp32 terms (parity.check_out); how many were admitted is printed for
-every case, and from 16 columns on none may be: there the row sums c1, c2
-are means of many independent terms, so a dX near zero needs a small
-g = dY*gamma and the fp32 terms are as small as the result.
+every case and bounded by parity.allowance_bound: from 16 columns on none
+may be, since the row sums c1, c2 are then means of many independent terms,
+so a dX near zero needs a small g = dY*gamma and the fp32 terms are as small
+as the result.
 """
 import numpy as np
 import pytest
 
 import workloads
 import every_row
+import parity
 import record
 from gpu_cases import compare, compare_every_row, reference, run_gpu, say
 
@@ -33,22 +35,15 @@ def admitted(w):
     return int(w.get("Y_fp32_admitted", 0)) + int(w.get("dX_fp32_admitted", 0))
 
 
-# Widths from which no element may need the allowance; below it at most
-# ADMIT_FRAC of the elements may.
-ADMIT_FREE_D = 16
-ADMIT_FRAC = 1e-2
-
-
-def check_admitted(w, N, D, what):
-    """Record and print the admitted count; from ADMIT_FREE_D columns on it
-    must be zero, below that bounded."""
+def check_admitted(w, N, D, what, storage="f16"):
+    """Record and print the admitted count and hold it to
+    parity.allowance_bound (zero for fp16 from 16 columns on)."""
     n = admitted(w)
     say(f"[parity] {what}: admitted {n} (Y {w.get('Y_fp32_admitted', 0)}, "
         f"dX {w.get('dX_fp32_admitted', 0)})")
     record.admitted(what, n, 2 * N * D)
-    if D >= ADMIT_FREE_D:
-        assert n == 0, f"{what}: {n} elements needed the fp32 cancellation allowance"
-    assert n <= ADMIT_FRAC * 2 * N * D, f"{what}: {n} elements needed the allowance"
+    bound = parity.allowance_bound(D, storage) * 2 * N * D
+    assert n <= bound, f"{what}: {n} elements needed the fp32 cancellation allowance"
 
 
 @pytest.mark.parametrize("name", ["rms_17x257", "ln_128x1024"])

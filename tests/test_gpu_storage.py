@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import parity
 import record
 import workloads
 from gpu_cases import compare_every_row, compare, reference, run_gpu, say
@@ -32,6 +33,15 @@ def _case(kind, N, D, seed, act, param, cot=None):
 
 
 TORCH = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _admitted(w, N, D, act, what):
+    """Record the elements the fp32 cancellation allowance admitted and hold
+    them to parity.allowance_bound (binary32 outputs take no allowance)."""
+    n = w["Y_fp32_admitted"] + w["dX_fp32_admitted"]
+    record.admitted(what, n, 2 * N * D)
+    if act != "f32":
+        assert n <= parity.allowance_bound(D, act) * 2 * N * D, f"{what}: {n} admitted"
 
 # backward storage combinations (act, cot, dX) the library provides
 BWD_TYPES = ([(a, c, o) for a in ("f16", "bf16") for c in (a, "f32") for o in (a, "f32")] +
@@ -64,8 +74,7 @@ def test_storage_width_sweep(kind, act, D):
     d = _case(kind, N, D, 8000 + D, act, act)
     w = compare(kind, run_gpu(kind, d, 1e-5), reference(kind, d, 1e-5),
                 f"{kind} {act} {N}x{D}", inputs=d)
-    record.admitted(f"storage sweep {kind} {act} {N}x{D}",
-                    w["Y_fp32_admitted"] + w["dX_fp32_admitted"], 2 * N * D)
+    _admitted(w, N, D, act, f"storage sweep {kind} {act} {N}x{D}")
 
 
 @pytest.mark.parametrize("D", [8, 128, 1024, 4096, 257])
@@ -78,8 +87,7 @@ def test_storage_unaligned(kind, act, D):
     d = _case(kind, N, D, 9000 + D, act, act)
     w = compare(kind, run_gpu(kind, d, 1e-5, offset=1), reference(kind, d, 1e-5),
                 f"{kind} {act} {N}x{D} unaligned", inputs=d)
-    record.admitted(f"storage unaligned {kind} {act} {N}x{D}",
-                    w["Y_fp32_admitted"] + w["dX_fp32_admitted"], 2 * N * D)
+    _admitted(w, N, D, act, f"storage unaligned {kind} {act} {N}x{D}")
 
 
 @pytest.mark.parametrize("D", [1024, 257])
@@ -161,3 +169,4 @@ def test_full_size_storage(name, act, param, cot, dxt):
     say(f"[storage] {msg}; worst {r}")
     record.line(msg)
     assert r["rows_checked"] == w.N
+    assert n <= parity.allowance_bound(w.D, act) * 2 * w.N * w.D
