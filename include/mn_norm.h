@@ -410,6 +410,27 @@ mn_status mn_norm_reduce_partials(mn_norm_kind kind, int64_t N, int64_t D,
                                   const void* workspace, size_t workspace_bytes,
                                   float* dgamma, float* dbeta, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * RMSNorm backward without a caller workspace, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, validation, kernels and
+ * results as mn_rmsnorm_backward (bitwise), minus `workspace`: the dgamma
+ * partial rows go to a fixed array of mn_noalloc_scratch_bytes() bytes
+ * (8 MiB, enough for every valid N, D) that the library holds on each
+ * device it runs on until the process ends; a shape needing more would
+ * return MN_ERR_WORKSPACE. The call allocates nothing. Its first call on a
+ * device looks up that device's copy of the array (the device of `stream`,
+ * or the current one for the null stream); a failure there returns
+ * MN_ERR_DEVICE. All calls on one device share its array, so two such calls
+ * that may run at the same time on one device (different streams without
+ * ordering between them) race and give wrong dgamma: order them, or use the
+ * workspace entry point. Nothing in the array needs clearing between calls.
+ * ------------------------------------------------------------------------- */
+mn_status mn_rmsnorm_backward_noalloc(const mn_f16* X, const mn_f16* gamma, const float* rstd,
+                                      const mn_f16* dY, mn_f16* dX, float* dgamma,
+                                      int64_t N, int64_t D, void* stream);
+size_t mn_noalloc_scratch_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif

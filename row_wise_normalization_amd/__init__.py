@@ -54,6 +54,7 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "mn_rmsnorm_forward": [_P, _P, _P, _P, _I64, _I64, _F, _P],
     "mn_rmsnorm_backward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
+    "mn_rmsnorm_backward_noalloc": [_P, _P, _P, _P, _P, _P, _I64, _I64, _P],
     "mn_layernorm_forward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P],
     "mn_layernorm_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P],
     "mn_add_rmsnorm_forward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P],
@@ -115,6 +116,8 @@ def lib() -> ctypes.CDLL:
     L.mn_groupnorm_workspace_bytes.restype = _SZ
     L.mn_norm_gemv_workspace_bytes.argtypes = [_I64, _I64, _I64]
     L.mn_norm_gemv_workspace_bytes.restype = _SZ
+    L.mn_noalloc_scratch_bytes.argtypes = []
+    L.mn_noalloc_scratch_bytes.restype = _SZ
     L.mn_status_string.argtypes = [ctypes.c_int]
     L.mn_status_string.restype = ctypes.c_char_p
     L.mn_last_device_error.argtypes = []
@@ -193,6 +196,21 @@ def mn_rmsnorm_backward(X, gamma, rstd, dY, dX, dgamma, workspace, stream=None):
     _check_t("dX", dX, H, (N, D)); _check_t("dgamma", dgamma, F32, (D,))
     _call("mn_rmsnorm_backward", _ptr(X), _ptr(gamma), _ptr(rstd), _ptr(dY), _ptr(dX),
           _ptr(dgamma), N, D, _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def mn_rmsnorm_backward_noalloc(X, gamma, rstd, dY, dX, dgamma, stream=None):
+    """mn_rmsnorm_backward with the library's fixed device scratch array in
+    place of a workspace (see include/mn_norm.h); allocates nothing."""
+    N, D = _nd(X)
+    _check_t("X", X, H, (N, D)); _check_t("gamma", gamma, H, (D,))
+    _check_t("rstd", rstd, F32, (N,)); _check_t("dY", dY, H, (N, D))
+    _check_t("dX", dX, H, (N, D)); _check_t("dgamma", dgamma, F32, (D,))
+    _call("mn_rmsnorm_backward_noalloc", _ptr(X), _ptr(gamma), _ptr(rstd), _ptr(dY), _ptr(dX),
+          _ptr(dgamma), N, D, _stream(stream))
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().mn_noalloc_scratch_bytes())
 
 
 def mn_layernorm_forward(X, gamma, beta, Y, mean, rstd, eps: float, stream=None):

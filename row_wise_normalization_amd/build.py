@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 # so that the sources compile in parallel.
 SOURCES = ["mn_inst_f16.hip", "mn_inst_bf16.hip", "mn_inst_f32.hip", "mn_inst_ext_f16.hip",
            "mn_inst_ext_bf16.hip", "mn_inst_ext_f32.hip", "mn_gn_f16.hip", "mn_gn_bf16.hip",
-           "mn_gn_f32.hip", "mn_gn_plan.hip", "mn_gemv.hip", "mn_kernels.hip", "mn_api.cpp"]
+           "mn_gn_f32.hip", "mn_gn_plan.hip", "mn_gemv.hip", "mn_kernels.hip", "mn_noalloc.hip",
+           "mn_api.cpp"]
 ARCH = "gfx950"
 
 # Device-code flags. Packed fp32 instructions are disabled on purpose; no

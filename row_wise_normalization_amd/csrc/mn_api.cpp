@@ -96,6 +96,16 @@ mn_status device_status(hipError_t e)
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+}  // namespace
+
+namespace mn {
+// MN_ERR_DEVICE with the runtime's text kept for mn_last_device_error (for
+// the other translation units of the library).
+mn_status record_device_error(hipError_t e) { return device_status(e); }
+}  // namespace mn
+
+namespace {
+
 // ---------------------------------------------------------------------------
 // Forward.
 // ---------------------------------------------------------------------------

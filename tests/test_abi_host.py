@@ -316,3 +316,24 @@ def test_product_and_oracle_are_independent():
             with open(os.path.join(ROOT, "oracle", fn)) as f:
                 src = f.read()
             assert "row_wise_normalization_amd" not in src and "mn_norm.h" not in src, fn
+
+
+def test_noalloc_validation_and_scratch_size():
+    """The no-allocation RMSNorm backward validates before touching a device,
+    and its fixed scratch array holds the partial rows of every valid shape."""
+    L = mn.lib()
+    cap = mn.noalloc_scratch_bytes()
+    assert cap == 8 << 20
+    call = lambda **k: L.mn_rmsnorm_backward_noalloc(
+        k.get("X", A), k.get("g", B), k.get("r", C), k.get("dY", Dp), k.get("dX", E),
+        k.get("dg", F), k.get("N", 16), k.get("D", 64), S)
+    assert call(X=NULL) == 1
+    assert call(dg=NULL) == 1
+    assert call(N=0) == 2
+    assert call(D=0) == 2
+    assert call(D=8193) == 2
+    worst = 0
+    for D in range(1, 8193):
+        for N in (1, 255, 256, 511, 512, 513, 1 << 20):
+            worst = max(worst, mn.workspace_bytes(mn.MN_RMSNORM, N, D))
+    assert 0 < worst <= cap
