@@ -70,21 +70,27 @@ typedef enum {
     MN_ERR_DTYPE = 7
 } mn_status;
 
-/* Storage types of the *_ex entry points. Arithmetic is fp32 for all. */
-typedef enum {
+/* Storage types of the *_ex entry points. Arithmetic is fp32 for all.
+ * mn_dtype and mn_norm_kind are plain 32-bit integers (the size of an enum
+ * argument on every supported ABI) with named values, so that any value a
+ * caller passes is well defined in the library and an unknown one returns
+ * MN_ERR_DTYPE (MN_ERR_SHAPE, or 0 bytes, for an unknown kind). */
+typedef int32_t mn_dtype;
+enum {
     MN_F16 = 0,   /* IEEE binary16 */
     MN_BF16 = 1,  /* bfloat16: the upper 16 bits of an IEEE binary32 */
     MN_F32 = 2    /* IEEE binary32 */
-} mn_dtype;
+};
 
-typedef enum {
+typedef int32_t mn_norm_kind;
+enum {
     MN_RMSNORM = 0,
     MN_LAYERNORM = 1,
     MN_ADD_RMSNORM = 2,
     MN_DYT = 3,          /* Dynamic Tanh */
     MN_POLYNORM = 4,
     MN_MOD_RMSNORM = 5   /* Modulated RMSNorm */
-} mn_norm_kind;
+};
 
 /* [meTile] contract bound: 1..8192 columns. */
 #define MN_MAX_COLS 8192

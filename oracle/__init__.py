@@ -31,12 +31,13 @@ _I64 = ctypes.c_int64
 _DBL = ctypes.c_double
 
 
-def compile_library(src: str, out: str) -> str:
+def compile_library(src: str, out: str, extra_flags=()) -> str:
     """gcc build: no fast-math and no FMA contraction, so every operation in
-    the oracle is one IEEE double rounding."""
+    the oracle is one IEEE double rounding. ``extra_flags`` adds options (the
+    sanitizer builds of the tests)."""
     tmp = out + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+           "-fno-fast-math", "-Wall", "-Wextra", *extra_flags, "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

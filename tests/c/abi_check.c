@@ -54,6 +54,32 @@ int main(void)
     EXPECT(mn_add_rmsnorm_backward(X, NULL, G, r, dY, NULL, dX, dg, N, D, ws, need, NULL),
            MN_ERR_NULL);
     EXPECT(mn_norm_reduce_partials(MN_LAYERNORM, N, D, ws, 2 * need, dg, NULL, NULL), MN_ERR_NULL);
+    /* explicit storage types */
+    EXPECT(mn_rmsnorm_forward_ex(X, G, Y, r, N, D, 1e-5f, (mn_dtype)7, MN_F16, NULL),
+           MN_ERR_DTYPE);
+    EXPECT(mn_layernorm_backward_ex(X, G, r, r + 4096, dY, dX, dg, dg + 8192, N, D, MN_BF16,
+                                    MN_F32, MN_F16, MN_BF16, ws, 2 * need, NULL),
+           MN_ERR_DTYPE);
+    EXPECT(mn_add_rmsnorm_forward_ex(X, dY, G, X, Y, r, N, D, 1e-5f, MN_F16, MN_F16, NULL),
+           MN_ERR_ALIAS);
+    /* the other norms, GroupNorm, the fused GEMV */
+    EXPECT(mn_dyt_forward_ex(X, NULL, G, G, Y, N, D, MN_F16, MN_F16, NULL), MN_ERR_NULL);
+    EXPECT(mn_polynorm_forward_ex(X, r, Y, r + 4096, N, D, 0.0f, MN_F16, NULL), MN_ERR_EPS);
+    EXPECT(mn_mod_rmsnorm_forward_ex(X, G, dY, dX, Y, r, 3, N, D, 1e-5f, MN_F16, MN_F16, NULL),
+           MN_ERR_SHAPE);
+    EXPECT(mn_groupnorm_forward_ex(X, G, G + 4096, Y, r, r + 4096, 2, 64, 256, 7, 1e-5f, MN_F16,
+                                   MN_F16, NULL),
+           MN_ERR_SHAPE);
+    if (mn_groupnorm_workspace_bytes(2, 64) == 0) ++failures;
+    if (mn_norm_gemv_workspace_bytes(4, 4096, 4096) == 0) ++failures;
+    EXPECT(mn_fused_rmsnorm_gemv(X, G, dY, Y, 9, 4096, 4096, 1e-5f, ws,
+                                 mn_norm_gemv_workspace_bytes(4, 4096, 4096), NULL),
+           MN_ERR_SHAPE);
+    /* the no-allocation backward: argument errors before any device call */
+    EXPECT(mn_rmsnorm_backward_noalloc(X, G, r, dY, dX, NULL, N, D, NULL), MN_ERR_NULL);
+    EXPECT(mn_rmsnorm_backward_noalloc(X, G, r, dY, dX, dg, N, 0, NULL), MN_ERR_SHAPE);
+    if (mn_noalloc_scratch_bytes() < mn_norm_workspace_bytes(MN_RMSNORM, 1 << 20, 4096))
+        ++failures;
     if (strlen(mn_status_string(MN_ERR_DEVICE)) == 0) ++failures;
     if (failures) {
         fprintf(stderr, "%d failures\n", failures);
