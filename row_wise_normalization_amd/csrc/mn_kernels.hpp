@@ -634,8 +634,37 @@ __device__ __forceinline__ float block_sum(float v, float* scratch)
     return v;
 }
 
+// Constants kept in registers where the compiler cannot see their values:
+// a -0 addend turns a product x * b into fma(x, b, -0), which is the rounded
+// product bitwise (sign of zero included) but, unlike a multiply, takes a
+// 16-bit x as a mixed-precision operand (v_fma_mix_f32: the conversion to
+// fp32 costs no instruction); likewise x + c as fma(x, 1, c). With visible
+// constants the compiler folds both back into a conversion and a multiply
+// or an add.
+struct MixConst {
+    float nz, one;
+};
+
+__device__ __forceinline__ MixConst mix_const()
+{
+    MixConst m{-0.0f, 1.0f};
+    asm volatile("" : "+v"(m.nz), "+v"(m.one));
+    return m;
+}
+
 // Storage types: ST for X and R (and MOD's scale), CT for the cotangents dY
 // and dH, OT for dX.
+//
+// Arithmetic per element (the row-constant factors are formed once per row;
+// every product of a 16-bit input is a mixed-precision fma, see MixConst):
+//   RMS, ADD, MOD (v = x, or x + r for ADD; w = gamma, or gamma * (1 + scale)
+//   for MOD's sample; g = dY w): the row sum S = sum_j g v, so c1 =
+//   mean(g xhat) = rstd S / D; then dX = rstd (g - xhat c1) [+ dH, in the
+//   last fma] with xhat = v rstd.
+//   LN: xhat = (x - mean) rstd, c1 = mean(g xhat), c2 = mean(g), dX =
+//   rstd (g - c2 - xhat c1), in this order (exact zeros stay exact).
+// The row means multiply by the rounded 1/D (one ulp of fp32 from a
+// division at most).
 template <int KIND, int ST, int CT, int OT, int T, int VEC, int CPT, int U, int BLOCK, int PF,
           int NT>
 __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
@@ -655,6 +684,8 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
     // per-workgroup scalar partials: dalpha (DYT), dw1..dw3 and db (POLY)
     constexpr int NSC = (KIND == DYT) ? 1 : (KIND == POLY) ? 4 : 0;
     constexpr int NQ = (KIND == POLY) ? 3 : 1;  // saved rstd values per row
+    // the kinds whose row sum is S = sum(dY w v)
+    constexpr bool RMSLIKE = KIND == RMS || KIND == ADD || KIND == MOD;
     static_assert(BLOCK % T == 0, "block holds whole row groups");
     __shared__ float red[RedBuf<T, RPB, U * NRR>::size];
     __shared__ float wsum[BLOCK / 64 > 0 ? BLOCK / 64 : 1];
@@ -708,6 +739,7 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
 #pragma unroll
         for (int q = 0; q < 3; ++q) pw[q] = a.poly[q];
     }
+    const MixConst mc = mix_const();
 
     float accg[CPT][VEC], accb[CPT][VEC], acch[CPT][VEC], accs[NSC > 0 ? NSC : 1];
 #pragma unroll
@@ -721,10 +753,24 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
 #pragma unroll
     for (int q = 0; q < (NSC > 0 ? NSC : 1); ++q) accs[q] = 0.0f;
 
+    // RMS, LN, ADD and MOD load every chunk unconditionally: a row past the
+    // end reads the last row again and a column past D the row's first
+    // chunk. Their terms vanish where they could reach a result: the row's
+    // rstd (and so xhat and dY * rstd) is 0 past the end, gamma is 0 past D,
+    // and the plain sums of dY (LN's dbeta, MOD's dshift) take a 0/1 row
+    // mask. Nothing is stored for them, and their row sums are not used.
+    // (Zero-filling the registers of masked loads instead cost about one
+    // instruction per element.) DYT and POLY sum dY and x without such a
+    // factor and keep the masked loads.
+    constexpr bool CLAMP = RMSLIKE || KIND == LN;
+    int coffc[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) coffc[k] = cval[k] ? coff[k] : 0;
+
     struct Tile {
         HV x[U][CPT], r[U][CPT];
         CV dy[U][CPT];
-        float rs[U][NQ], mu[U];
+        float rs[U][NQ], mu[U], rm[U];
     };
     auto load_tile = [&](Tile& t, int64_t base) {
 #pragma unroll
@@ -736,48 +782,45 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                 for (int q = 0; q < NQ; ++q) t.rs[u][q] = rok ? a.rstd[row * NQ + q] : 0.0f;
             }
             t.mu[u] = (KIND == LN && rok) ? a.mean[row] : 0.0f;
-            const int64_t ro = row * (int64_t)D;
+            t.rm[u] = rok ? 1.0f : 0.0f;
+            if constexpr (CLAMP) {
+                const int64_t ro = (rok ? row : end - 1) * (int64_t)D;
 #pragma unroll
-            for (int k = 0; k < CPT; ++k) {
-                const bool ok = rok && cval[k];
-                t.x[u][k] = ok ? sload<ST, VEC, NT>(a.X, ro + coff[k]) : czero<ST, VEC>();
-                if constexpr (KIND == ADD) t.r[u][k] = ok ? sload<ST, VEC, NT>(a.R, ro + coff[k]) : czero<ST, VEC>();
-                t.dy[u][k] = ok ? sload<CT, VEC, NT>(a.dY, ro + coff[k]) : czero<CT, VEC>();
+                for (int k = 0; k < CPT; ++k) {
+                    t.x[u][k] = sload<ST, VEC, NT>(a.X, ro + coffc[k]);
+                    if constexpr (KIND == ADD) t.r[u][k] = sload<ST, VEC, NT>(a.R, ro + coffc[k]);
+                    t.dy[u][k] = sload<CT, VEC, NT>(a.dY, ro + coffc[k]);
+                }
+            } else {
+                const int64_t ro = row * (int64_t)D;
+#pragma unroll
+                for (int k = 0; k < CPT; ++k) {
+                    const bool ok = rok && cval[k];
+                    t.x[u][k] = ok ? sload<ST, VEC, NT>(a.X, ro + coff[k]) : czero<ST, VEC>();
+                    t.dy[u][k] = ok ? sload<CT, VEC, NT>(a.dY, ro + coff[k]) : czero<CT, VEC>();
+                }
             }
         }
     };
 
-    const float fD = (float)D;
-    const float invD = 1.0f / fD;
+    const float invD = 1.0f / (float)D;
     int phase = 0;
-    Tile cur;
-    load_tile(cur, first);
     // gam: gamma; gef: the weight the row sees (MOD: gamma * (1 + scale) of
     // this workgroup's sample, else gamma); scl: 1 + scale (MOD)
     float gam[CPT][VEC], gef[CPT][VEC], scl[CPT][VEC];
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-        if constexpr (HAS_G) widen_param<VEC>(graw[k], a.pdt, cval[k], gam[k]);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            if constexpr (KIND == MOD) {
-                scl[k][e] = 1.0f + cget<ST, VEC>(scr[k], e);
-                gef[k][e] = gam[k][e] * scl[k][e];
-            } else if constexpr (HAS_G) {
-                gef[k][e] = gam[k][e];
-            }
-        }
-    }
-    for (int64_t base = first; base < stop; base += tstride) {
-        Tile nxt;
-        if constexpr (PF) {
-            wait_vmem_all();
-            load_tile(nxt, base + tstride);
-        }
 
-        // Row sums. RMS, ADD, MOD: c1 = sum(g * xhat) with g = dY * gamma
-        // (MOD: times 1 + scale); LN: also c2 = sum(g); POLY: sum(dY * n_p)
-        // for the three normalised powers n_p.
+    // The row value v: x, or for ADD the sum x + r rounded once to fp32.
+    auto value = [&](const Tile& t, int u, int k, int e) -> float {
+        if constexpr (KIND == ADD)
+            return __builtin_fmaf(cget<ST, VEC>(t.x[u][k], e), mc.one, cget<ST, VEC>(t.r[u][k], e));
+        else
+            return cget<ST, VEC>(t.x[u][k], e);
+    };
+
+    // One tile: the row sums, then dX and the parameter-gradient terms.
+    auto process = [&](Tile& cur, int64_t base) {
+        // Row sums. RMS, ADD, MOD: S = sum(dY w v); LN: sum(g xhat) and
+        // sum(g); POLY: sum(dY x^p) for p = 1..3 and sum(dY).
         float c[U * NRR];
         if constexpr (NR > 0) {
 #pragma unroll
@@ -785,24 +828,28 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                 float acc[NRR];
 #pragma unroll
                 for (int q = 0; q < NRR; ++q) acc[q] = 0.0f;
+                const float nmu = -cur.mu[u];
 #pragma unroll
                 for (int k = 0; k < CPT; ++k)
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        float v = cget<ST, VEC>(cur.x[u][k], e);
-                        if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                         const float dyv = cget<CT, VEC>(cur.dy[u][k], e);
                         if constexpr (KIND == POLY) {
+                            const float v = cget<ST, VEC>(cur.x[u][k], e);
                             const float v2 = v * v;
                             acc[0] = __builtin_fmaf(dyv, v, acc[0]);
                             acc[1] = __builtin_fmaf(dyv, v2, acc[1]);
                             acc[2] = __builtin_fmaf(dyv, v2 * v, acc[2]);
                             acc[3] += dyv;
-                        } else {
-                            const float xh = (v - cur.mu[u]) * cur.rs[u][0];
-                            const float gg = dyv * gef[k][e];
+                        } else if constexpr (KIND == LN) {
+                            const float xh = (__builtin_fmaf(cget<ST, VEC>(cur.x[u][k], e),
+                                                             mc.one, nmu) * cur.rs[u][0]);
+                            const float gg = __builtin_fmaf(dyv, gef[k][e], mc.nz);
                             acc[0] = __builtin_fmaf(gg, xh, acc[0]);
-                            if constexpr (KIND == LN) acc[1] += gg;
+                            acc[1] += gg;
+                        } else {
+                            const float gg = __builtin_fmaf(dyv, gef[k][e], mc.nz);
+                            acc[0] = __builtin_fmaf(gg, value(cur, u, k, e), acc[0]);
                         }
                     }
 #pragma unroll
@@ -823,14 +870,16 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
         for (int u = 0; u < U; ++u) {
             const int64_t row = base + u * RPB + g;
             const bool rok = row < end;
-            // (POLY divides by multiplying with 1/D: its four row means per
-            // row would otherwise cost as much as its element work)
-            const float c1 = (KIND == POLY) ? c[u * NRR] * invD : (NR > 0) ? c[u * NRR] / fD : 0.0f;
-            const float c2 = (KIND == POLY) ? c[u * NRR + 1] * invD
-                                            : (NR > 1) ? c[u * NRR + 1] / fD : 0.0f;
-            const float c3 = (KIND == POLY) ? c[u * NRR + 2] * invD : 0.0f;
             const float rs = (KIND != DYT) ? cur.rs[u][0] : 0.0f;
-            const float mu = cur.mu[u];
+            // row constants
+            float c1 = 0.0f, c2 = 0.0f;
+            if constexpr (RMSLIKE) {
+                c1 = rs * (c[u * NRR] * invD);                  // mean(g xhat) = rstd S / D
+            } else if constexpr (KIND == LN) {
+                c1 = c[u * NRR] * invD;
+                c2 = c[u * NRR + 1] * invD;
+            }
+            const float nmu = -cur.mu[u];
             const int64_t ro = row * (int64_t)D;
             // POLY: with S_p = sum(dY x^p) and n_p = x^p r_p, mean(dY n_p) =
             // r_p S_p / D, and
@@ -840,6 +889,8 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
             // by the row group's first lane.
             float A1 = 0.0f, A2 = 0.0f, A3 = 0.0f, B1 = 0.0f, B2 = 0.0f, B3 = 0.0f;
             if constexpr (KIND == POLY) {
+                const float c1 = c[u * NRR] * invD, c2 = c[u * NRR + 1] * invD;
+                const float c3 = c[u * NRR + 2] * invD;
                 const float r1 = cur.rs[u][0], r2 = cur.rs[u][1], r3 = cur.rs[u][2];
                 const float m1 = r1 * c1, m2 = r2 * c2, m3 = r3 * c3;
                 A1 = pw[0] * r1;
@@ -865,13 +916,12 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                 OV o;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    float v = cget<ST, VEC>(cur.x[u][k], e);
-                    if constexpr (KIND == ADD) v += cget<ST, VEC>(cur.r[u][k], e);
                     const float dyv = cget<CT, VEC>(cur.dy[u][k], e);
                     float d;
                     if constexpr (KIND == DYT) {
                         // dX needs only 1 - t^2; t enters only the dgamma
                         // sums
+                        const float v = cget<ST, VEC>(cur.x[u][k], e);
                         float sd;
                         const float t = tanh_for_sums(alpha * v, sd);
                         const float gy = dyv * gam[k][e];
@@ -881,27 +931,40 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                         accb[k][e] += dyv;
                         accs[0] = __builtin_fmaf(gs, v, accs[0]);
                     } else if constexpr (KIND == POLY) {
+                        const float v = cget<ST, VEC>(cur.x[u][k], e);
                         const float v2 = v * v;
                         const float P = __builtin_fmaf(v, __builtin_fmaf(v, A3, A2), A1);
                         const float Q = __builtin_fmaf(v2, __builtin_fmaf(v2, B3, B2), B1);
                         d = __builtin_fmaf(dyv, P, -(v * Q));
+                    } else if constexpr (KIND == LN) {
+                        // (x - mean) rstd and rstd (g - c2 - xhat c1) as
+                        // written: a constant row gives xhat = 0 and, with
+                        // D = 1, g - c2 = 0 exactly
+                        const float xh = (__builtin_fmaf(cget<ST, VEC>(cur.x[u][k], e), mc.one,
+                                                         nmu) * rs);
+                        const float gg = __builtin_fmaf(dyv, gam[k][e], mc.nz);
+                        d = rs * __builtin_fmaf(-xh, c1, gg - c2);
+                        accg[k][e] = __builtin_fmaf(dyv, xh, accg[k][e]);
+                        accb[k][e] = __builtin_fmaf(dyv, cur.rm[u], accb[k][e]);
                     } else {
-                        const float xh = (v - mu) * rs;
-                        const float gg = dyv * gef[k][e];
-                        if constexpr (KIND == LN) d = rs * __builtin_fmaf(-xh, c1, gg - c2);
-                        else if constexpr (KIND == ADD)
-                            d = __builtin_fmaf(rs, __builtin_fmaf(-xh, c1, gg), cget<CT, VEC>(dh, e));
-                        else d = rs * __builtin_fmaf(-xh, c1, gg);
+                        // RMS, ADD, MOD: rstd (g - xhat c1), for ADD with dH
+                        // in the last fma (a dX that cancels dH against the
+                        // norm term is rounded once)
+                        const float v = value(cur, u, k, e);
+                        const float xh = (KIND == ADD) ? v * rs : __builtin_fmaf(v, rs, mc.nz);
+                        const float gg = __builtin_fmaf(dyv, gef[k][e], mc.nz);
+                        const float in = __builtin_fmaf(-xh, c1, gg);
+                        if constexpr (KIND == ADD) d = __builtin_fmaf(rs, in, cget<CT, VEC>(dh, e));
+                        else d = rs * in;
                         if constexpr (KIND == MOD) {
                             // dgamma takes dY * xhat * (1 + scale), dscale
                             // dY * xhat * gamma, dshift dY
-                            const float dx = dyv * xh;
+                            const float dx = __builtin_fmaf(dyv, xh, mc.nz);
                             accg[k][e] = __builtin_fmaf(dx, scl[k][e], accg[k][e]);
                             accb[k][e] = __builtin_fmaf(dx, gam[k][e], accb[k][e]);
-                            acch[k][e] += dyv;
+                            acch[k][e] = __builtin_fmaf(dyv, cur.rm[u], acch[k][e]);
                         } else {
                             accg[k][e] = __builtin_fmaf(dyv, xh, accg[k][e]);
-                            if constexpr (KIND == LN) accb[k][e] += dyv;
                         }
                     }
                     cset<OT, VEC>(o, e, d);
@@ -909,8 +972,51 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                 if (ok) cstore<OT, VEC, NT>(a.dX, ro + coff[k], o);
             }
         }
-        if constexpr (PF) cur = nxt;
-        else if (base + tstride < stop) load_tile(cur, base + tstride);
+    };
+
+    // Two tile buffers in turn: while one is reduced and written, the
+    // other's loads are in flight, with no register copies between them.
+    // Where registers are scarce (1024-lane workgroups, whose waves may hold
+    // at most 128 VGPRs, and the element-wise variants) the loop keeps one
+    // body and copies the prefetched tile instead, which the compiler
+    // schedules in fewer registers.
+    constexpr bool PINGPONG = VEC > 1 && BLOCK < 1024;
+    Tile ta;
+    load_tile(ta, first);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        if constexpr (HAS_G) widen_param<VEC>(graw[k], a.pdt, cval[k], gam[k]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if constexpr (KIND == MOD) {
+                scl[k][e] = 1.0f + cget<ST, VEC>(scr[k], e);
+                gef[k][e] = gam[k][e] * scl[k][e];
+            } else if constexpr (HAS_G) {
+                gef[k][e] = gam[k][e];
+            }
+        }
+    }
+    static_assert(PF == 1, "the backward prefetches the next tile");
+    if constexpr (PINGPONG) {
+        Tile tb;
+        for (int64_t base = first; base < stop; base += 2 * tstride) {
+            wait_vmem_all();
+            load_tile(tb, base + tstride);
+            process(ta, base);
+            const int64_t b2 = base + tstride;
+            if (b2 >= stop) break;
+            wait_vmem_all();
+            load_tile(ta, b2 + tstride);
+            process(tb, b2);
+        }
+    } else {
+        for (int64_t base = first; base < stop; base += tstride) {
+            Tile nxt;
+            wait_vmem_all();
+            load_tile(nxt, base + tstride);
+            process(ta, base);
+            ta = nxt;
+        }
     }
 
     // Fold the row groups of this workgroup in group order, then write the
