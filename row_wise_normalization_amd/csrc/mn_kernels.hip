@@ -72,14 +72,17 @@ hipError_t launch_bwd_types(int st, int ct, int ot, const BwdPlan& p, const BwdA
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Workgroups (= partial rows) of the backward, never more than there are
-// rows: one long-lived workgroup per CU of the 256, or two for RMSNorm and
-// PolyNorm rows of up to 4096 columns (timing at 16384 x 4096: backward rows
-// 3 % faster for RMSNorm, 5 % for PolyNorm, the column reduce reading twice
-// the partials; LayerNorm, Dynamic Tanh and the fused add at 8192 columns
-// were slower or unchanged with two).
+// rows: one long-lived workgroup per CU of the 256, or two for RMSNorm rows
+// of up to 3072 columns and PolyNorm rows of up to 4096 (5 % faster for
+// PolyNorm at 16384 x 4096; LayerNorm, Dynamic Tanh and the fused add at
+// 8192 columns were slower or unchanged with two). At 4096 columns RMSNorm
+// takes one workgroup per CU with three rows per step: timed as whole steps
+// (forward, backward, column reduce on rotating buffers), 0.7 % faster than
+// two workgroups of two rows, with half the partial rows to reduce.
 int64_t bwd_blocks(int kind, int32_t D)
 {
-    return ((kind == RMS || kind == POLY) && D <= 4096) ? 512 : 256;
+    if (kind == RMS) return D <= 3072 ? 512 : 256;
+    return (kind == POLY && D <= 4096) ? 512 : 256;
 }
 
 }  // namespace

@@ -661,8 +661,9 @@ __device__ __forceinline__ MixConst mix_const()
 //   for MOD's sample; g = dY w): the row sum S = sum_j g v, so c1 =
 //   mean(g xhat) = rstd S / D; then dX = rstd (g - xhat c1) [+ dH, in the
 //   last fma] with xhat = v rstd.
-//   LN: xhat = (x - mean) rstd, c1 = mean(g xhat), c2 = mean(g), dX =
-//   rstd (g - c2 - xhat c1), in this order (exact zeros stay exact).
+//   LN: c1 = mean(g xhat) = rstd mean(g (x - mean)), c2 = mean(g), and
+//   dX = rstd (g - c2 - xhat c1) with xhat = (x - mean) rstd, in this order
+//   (exact zeros stay exact).
 // The row means multiply by the rounded 1/D (one ulp of fp32 from a
 // division at most).
 template <int KIND, int ST, int CT, int OT, int T, int VEC, int CPT, int U, int BLOCK, int PF,
@@ -842,10 +843,11 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                             acc[2] = __builtin_fmaf(dyv, v2 * v, acc[2]);
                             acc[3] += dyv;
                         } else if constexpr (KIND == LN) {
-                            const float xh = (__builtin_fmaf(cget<ST, VEC>(cur.x[u][k], e),
-                                                             mc.one, nmu) * cur.rs[u][0]);
+                            // sum(g (x - mean)); times rstd once per row
+                            const float t = __builtin_fmaf(cget<ST, VEC>(cur.x[u][k], e), mc.one,
+                                                           nmu);
                             const float gg = __builtin_fmaf(dyv, gef[k][e], mc.nz);
-                            acc[0] = __builtin_fmaf(gg, xh, acc[0]);
+                            acc[0] = __builtin_fmaf(gg, t, acc[0]);
                             acc[1] += gg;
                         } else {
                             const float gg = __builtin_fmaf(dyv, gef[k][e], mc.nz);
@@ -876,8 +878,8 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
             if constexpr (RMSLIKE) {
                 c1 = rs * (c[u * NRR] * invD);                  // mean(g xhat) = rstd S / D
             } else if constexpr (KIND == LN) {
-                c1 = c[u * NRR] * invD;
-                c2 = c[u * NRR + 1] * invD;
+                c1 = rs * (c[u * NRR] * invD);                  // mean(g xhat)
+                c2 = c[u * NRR + 1] * invD;                     // mean(g)
             }
             const float nmu = -cur.mu[u];
             const int64_t ro = row * (int64_t)D;

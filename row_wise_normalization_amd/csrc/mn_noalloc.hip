@@ -21,7 +21,7 @@ mn_status record_device_error(hipError_t e);  // mn_api.cpp
 
 namespace {
 
-// Largest RMSNorm partial-row area: at most 512 rows of up to 4096 columns
+// Largest RMSNorm partial-row area: at most 512 rows of up to 3072 columns
 // or 256 rows of up to 8192 columns, 8 MiB (checked against
 // mn_norm_workspace_bytes for every shape by the host tests).
 constexpr size_t kScratchBytes = (size_t)8 << 20;

@@ -139,7 +139,7 @@ namespace mn {
     X(4, 128, 8, 1, 2, 512, 1, 3, 1024)      \
     X(5, 256, 8, 1, 2, 512, 1, 3, 2048)      \
     X(14, 192, 8, 2, 1, 384, 1, 3, 3072)     \
-    X(6, 512, 8, 1, 2, 512, 1, 3, 4096)      \
+    X(6, 512, 8, 1, 3, 512, 1, 3, 4096)      \
     X(12, 640, 8, 1, 1, 640, 1, 3, 5120)     \
     X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
 #define MN_BWD_LN(X)                         \
@@ -153,7 +153,19 @@ namespace mn {
     X(6, 256, 8, 2, 2, 512, 1, 3, 4096)      \
     X(12, 128, 8, 5, 1, 256, 1, 3, 5120)     \
     X(7, 512, 8, 2, 1, 1024, 1, 3, 8192)
-#define MN_BWD_ADD(X) MN_BWD_RMS(X)
+// The fused add keeps two rows per group at 4096 columns (its four streams
+// per element hold more registers).
+#define MN_BWD_ADD(X)                        \
+    X(0, 8, 8, 1, 4, 256, 1, 3, 64)          \
+    X(1, 16, 8, 1, 4, 256, 1, 3, 128)        \
+    X(2, 32, 8, 1, 4, 256, 1, 3, 256)        \
+    X(3, 64, 8, 1, 2, 512, 1, 3, 512)        \
+    X(4, 128, 8, 1, 2, 512, 1, 3, 1024)      \
+    X(5, 256, 8, 1, 2, 512, 1, 3, 2048)      \
+    X(14, 192, 8, 2, 1, 384, 1, 3, 3072)     \
+    X(6, 512, 8, 1, 2, 512, 1, 3, 4096)      \
+    X(12, 640, 8, 1, 1, 640, 1, 3, 5120)     \
+    X(7, 1024, 8, 1, 1, 1024, 1, 3, 8192)
 // The other norms keep two or three per-column accumulators, or four row
 // sums, and (DYT) an inlined tanh per element: one row per group per step
 // keeps them within 128 VGPRs without spilling.

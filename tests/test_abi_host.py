@@ -173,8 +173,8 @@ def test_workspace_bytes():
             b = mn.workspace_bytes(kind, N, D)
             assert b > 0 and b % 16 == 0
             # at most 256 partial rows of round_up(D, 4) floats (two arrays for
-            # LayerNorm), 512 for RMSNorm rows of up to 4096 columns
-            P = 512 if kind == mn.MN_RMSNORM and D <= 4096 else 256
+            # LayerNorm), 512 for RMSNorm rows of up to 3072 columns
+            P = 512 if kind == mn.MN_RMSNORM and D <= 3072 else 256
             assert b == min(N, P) * ((D + 3) // 4 * 4) * 4 * (2 if kind == mn.MN_LAYERNORM else 1)
     assert mn.workspace_bytes(6, 16, 64) == 0
     # the other norms: Dynamic Tanh keeps two partial arrays plus scalars,

@@ -55,7 +55,8 @@ def _one(N, D, seed, stream=None):
 
 
 def test_noalloc_matches_workspace_entry_point_in_sequence():
-    _one(16384, 4096, 1)                    # fills the whole 8 MiB array
+    _one(2048, 8192, 1)                     # fills the whole 8 MiB array
+    _one(16384, 4096, 5)                    # the headline shape
     _one(1000, 1024, 2)                     # smaller: stale partials must not leak
     _one(129, 257, 3)                       # element-wise path
     _one(3, 8192, 4, stream=torch.cuda.Stream())   # fewer rows than workgroups, own stream
