@@ -178,53 +178,111 @@ class HipEvent:
             self._lib.hipEventDestroy(self.h)
 
 
-def cpu_baseline(w, d, budget_s: float, types=("f16",) * 4):
-    """The oracle (single-threaded C, fp64) on this host: full forward and
-    backward passes over all rows of the same workload, repeated until the
-    time budget is spent (at least once)."""
+def _oracle_pass(w, d, lo: int, hi: int):
+    """The oracle's forward and backward over rows lo..hi-1 of the workload
+    (for the Modulated RMSNorm whole samples, for GroupNorm samples);
+    returns the parameter gradients of those rows."""
     import oracle
 
+    X, g, dY = d["X"][lo:hi], d.get("gamma"), d["dY"][lo:hi]
+    if w.kind == "dyt":
+        oracle.dyt_forward(X, w.scalars[0], g, d["beta"])
+        return oracle.dyt_backward(X, w.scalars[0], g, dY)[2]
+    if w.kind == "poly":
+        oracle.polynorm_forward(X, w.scalars[:3], w.scalars[3], w.eps)
+        return oracle.polynorm_backward(X, w.scalars[:3], dY, w.eps)[1]
+    if w.kind == "mod":
+        S = w.N // w.B
+        sc, sh = d["scale"][lo // S:hi // S], d["shift"][lo // S:hi // S]
+        oracle.modrms_forward(X, g, sc, sh, w.eps)
+        return oracle.modrms_backward(X, g, sc, dY, w.eps)[1]
+    if w.kind == "gn":
+        shp = (hi - lo, w.channels, w.D // w.channels)
+        oracle.groupnorm_forward(X.reshape(shp), g, d["beta"], w.groups, w.eps)
+        return oracle.groupnorm_backward(X.reshape(shp), g, dY.reshape(shp), w.groups, w.eps)[1]
+    if w.kind == "rms":
+        oracle.rmsnorm_forward(X, g, w.eps)
+        return oracle.rmsnorm_backward(X, g, dY, w.eps)[1]
+    if w.kind == "ln":
+        oracle.layernorm_forward(X, g, d["beta"], w.eps)
+        return oracle.layernorm_backward(X, g, dY, w.eps)[1]
+    R = d["R"][lo:hi]
+    oracle.add_rmsnorm_forward(X, R, g, w.eps)
+    return oracle.add_rmsnorm_backward(X, R, g, dY, d["dH"][lo:hi], w.eps)[1]
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads() -> int:
+    """Host threads for the threaded baseline: the CPUs this process may run
+    on, at most 16 (one GPU's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(w, d, budget_s: float, types=("f16",) * 4):
+    """The oracle (C, fp64) on this host, timed on full forward + backward
+    passes over all rows of the same workload: first on one core (a third of
+    the budget), then with the rows split into static contiguous chunks over
+    cpu_threads() host threads (the oracle's ctypes calls release the
+    interpreter lock), the chunks' parameter gradients added in chunk order;
+    each repeated until its share of the budget is spent (at least once).
+    The threaded figure is the reported value, the one-core one sits beside
+    it."""
+    from concurrent.futures import ThreadPoolExecutor
+
     fwd_b, bwd_b = alg_bytes(w.kind, w.N, w.D, *types, B=w.B, C=w.channels, G=w.groups)
-    rows = w.N
-    X, g, dY = d["X"], d.get("gamma"), d["dY"]
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        if w.kind == "dyt":
-            oracle.dyt_forward(X, w.scalars[0], g, d["beta"])
-            oracle.dyt_backward(X, w.scalars[0], g, dY)
-        elif w.kind == "poly":
-            oracle.polynorm_forward(X, w.scalars[:3], w.scalars[3], w.eps)
-            oracle.polynorm_backward(X, w.scalars[:3], dY, w.eps)
-        elif w.kind == "mod":
-            oracle.modrms_forward(X, g, d["scale"], d["shift"], w.eps)
-            oracle.modrms_backward(X, g, d["scale"], dY, w.eps)
-        elif w.kind == "gn":
-            shp = (w.N, w.channels, w.D // w.channels)
-            oracle.groupnorm_forward(X.reshape(shp), g, d["beta"], w.groups, w.eps)
-            oracle.groupnorm_backward(X.reshape(shp), g, dY.reshape(shp), w.groups, w.eps)
-        elif w.kind == "rms":
-            oracle.rmsnorm_forward(X, g, w.eps)
-            oracle.rmsnorm_backward(X, g, dY, w.eps)
-        elif w.kind == "ln":
-            oracle.layernorm_forward(X, g, d["beta"], w.eps)
-            oracle.layernorm_backward(X, g, dY, w.eps)
-        else:
-            oracle.add_rmsnorm_forward(X, d["R"], g, w.eps)
-            oracle.add_rmsnorm_backward(X, d["R"], g, dY, d["dH"], w.eps)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per = el / reps
+    align = w.N // w.B if w.kind == "mod" else 1
+
+    def timed(fn, budget):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    reps1, el1 = timed(lambda: _oracle_pass(w, d, 0, w.N), budget_s / 3)
+    T = cpu_threads()
+    per = -(-w.N // T)
+    per = -(-per // align) * align
+    chunks = [(lo, min(w.N, lo + per)) for lo in range(0, w.N, per)]
+    with ThreadPoolExecutor(T) as ex:
+        def threaded():
+            parts = list(ex.map(lambda c: _oracle_pass(w, d, c[0], c[1]), chunks))
+            total = parts[0]
+            for p in parts[1:]:
+                total = total + p
+            return total
+        repsT, elT = timed(threaded, budget_s - budget_s / 3)
+    one = el1 / reps1
+    many = elT / repsT
     return {
-        "value": round((fwd_b + bwd_b) / per / 1e9, 4),
+        "value": round((fwd_b + bwd_b) / many / 1e9, 4),
         "unit": "GB/s",
-        "rows_per_s": round(rows / per, 1),
-        "cores": 1,
+        "rows_per_s": round(w.N / many, 1),
+        "cores": T,
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
-        "sample": f"{reps} full forward+backward passes over all {w.N}x{w.D} rows "
-                  f"({el:.1f} s), single-threaded C fp64",
+        "sample": f"{repsT} full forward+backward passes over all {w.N}x{w.D} rows in "
+                  f"{len(chunks)} contiguous row chunks on {T} threads ({elT:.1f} s), C fp64",
+        "single_core": {"value": round((fwd_b + bwd_b) / one / 1e9, 4), "unit": "GB/s",
+                        "rows_per_s": round(w.N / one, 1),
+                        "sample": f"{reps1} full passes on one thread ({el1:.1f} s)"},
     }
 
 
@@ -296,6 +354,172 @@ def pages_context(torch, mn):
         "unit": "us", "higher_is_better": False, "data": "synthetic", "dtype": "f32",
         "shapes": out, "device": torch.cuda.get_device_name(dev),
     }), flush=True)
+
+
+# --- rocprofv3 summaries ------------------------------------------------------
+
+# Kernel-name fragments -> (label, which algorithmic byte count applies).
+PROFILE_KERNELS = (("gn_fwd_kernel", "forward"), ("gn_bwd_kernel", "backward_rows"),
+                   ("fwd_kernel", "forward"), ("bwd_kernel", "backward_rows"),
+                   ("reduce_kernel", "reduce_partials"), ("gemv_kernel", "gemv"))
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _csvs(root: str, suffix: str):
+    """Every CSV under `root` whose name ends with `suffix` (rocprofv3 puts
+    them in the output directory or in host/process subdirectories)."""
+    import glob
+    return sorted(glob.glob(os.path.join(root, "**", f"*{suffix}"), recursive=True))
+
+
+def _read_csv(path: str):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def profile_commands(workload: str, prefix: str, extra: str = "--cpu-budget 0"):
+    """The three rocprofv3 runs a summary is made from (run from /tmp with
+    TMPDIR=/tmp; R is the repository root)."""
+    b = f"python3 $R/bench.py --workload {workload}"
+    return [
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d {prefix}_trace -o trace -- "
+        f"{b} {extra}",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {prefix}_fetch -o fetch -- "
+        f"{b} --steps 4 --warmup 2 --cpu-budget 0",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {prefix}_write -o write -- "
+        f"{b} --steps 4 --warmup 2 --cpu-budget 0",
+        f"python3 $R/bench.py --workload {workload} --summarize-profile {prefix}",
+    ]
+
+
+def summarize_profile(workload: str, prefix: str, out_dir: str = None):
+    """Turn the three rocprofv3 runs of profile_commands() into
+    profiles/traffic_<workload>.json and profiles/<workload>_trace_and_traffic.md.
+
+    HBM bytes per launch come from the TCC counters FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, summed over the channels). They are
+    calibrated against the HIP runtime's own device copy kernel, which
+    bench.py issues when it clones its largest inputs (a copy of known size:
+    N * D elements, or the weight matrix for the fused GEMV): the factor is
+    the copied bytes over the counter's KiB * 1024. On gfx950 FETCH_SIZE
+    reads half the copied bytes (factor about 2.0) and WRITE_SIZE all of
+    them (factor 1.0)."""
+    import statistics
+    w = workloads.WORKLOADS[workload]
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    stats_p = _csvs(prefix + "_trace", "kernel_stats.csv")
+    trace_p = _csvs(prefix + "_trace", "kernel_trace.csv")
+    fetch_p = _csvs(prefix + "_fetch", "counter_collection.csv")
+    write_p = _csvs(prefix + "_write", "counter_collection.csv")
+    if not (stats_p and fetch_p and write_p):
+        raise SystemExit(f"rocprofv3 CSVs not found under {prefix}_trace/_fetch/_write")
+    stats = _read_csv(stats_p[0])
+
+    def counter(paths, name):
+        d = {}
+        for p in paths:
+            for r in _read_csv(p):
+                if r.get("Counter_Name") == name:
+                    d.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return d
+
+    fetch = counter(fetch_p, "FETCH_SIZE")
+    write = counter(write_p, "WRITE_SIZE")
+    gemv = w.kind.endswith("gemv")
+    copy_bytes = w.D * w.Nout * SIZE["f16"] if gemv else w.N * w.D * SIZE["f16"]
+
+    def calib(d):
+        vals = [v for k, vs in d.items() if k.startswith(COPY_KERNEL) for v in vs]
+        top = max(vals)
+        return statistics.median([v for v in vals if v > 0.9 * top])
+
+    cf, cw = calib(fetch), calib(write)
+    sf, sw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    if gemv:
+        alg = {"gemv": gemv_bytes(w.N, w.D, w.Nout, ln=w.kind == "ln_gemv")}
+    else:
+        fb, bb = alg_bytes(w.kind, w.N, w.D, B=w.B, C=w.channels, G=w.groups)
+        alg = {"forward": fb, "backward_rows": bb, "reduce_partials": None}
+    # resources of each kernel from the per-dispatch trace (first dispatch)
+    res = {}
+    for p in trace_p:
+        for r in _read_csv(p):
+            n = r.get("Kernel_Name", "")
+            if n and n not in res:
+                res[n] = {k: r[k] for k in ("VGPR_Count", "Accum_VGPR_Count", "SGPR_Count",
+                                            "LDS_Block_Size", "Scratch_Size", "Workgroup_Size_X",
+                                            "Grid_Size_X") if k in r}
+    # the compiler's resource usage of each kernel, recorded by the build
+    built = {}
+    rpath = os.path.join(ROOT, "row_wise_normalization_amd", "_build", "kernel_resources.json")
+    if os.path.exists(rpath):
+        with open(rpath) as f:
+            built = json.load(f)
+    out = {"workload": workload, "kernel_source_sha256_16": kernel_hash(w.kind),
+           "calibration": {"kernel": COPY_KERNEL, "bytes_read": copy_bytes,
+                           "bytes_written": copy_bytes, "FETCH_SIZE_KiB_median": cf,
+                           "WRITE_SIZE_KiB_median": cw, "fetch_scale": sf, "write_scale": sw},
+           "commands": profile_commands(workload, "$R/gpurun_out/prof_" + workload),
+           "kernels": {}}
+    for s in stats:
+        n = s["Name"]
+        label = next((lab for frag, lab in PROFILE_KERNELS if frag in n), None)
+        if label is None or label not in alg:
+            continue
+        fv, wv = fetch.get(n, []), write.get(n, [])
+        fr = statistics.median(fv) * 1024 * sf if fv else None
+        wr = statistics.median(wv) * 1024 * sw if wv else None
+        avg_ns = float(s["AverageNs"])
+        a = alg[label]
+        out["kernels"][label] = {
+            "name": n, "calls": int(s["Calls"]), "avg_ns": avg_ns, "min_ns": int(s["MinNs"]),
+            "max_ns": int(s["MaxNs"]), "fetch_bytes_per_launch": fr,
+            "write_bytes_per_launch": wr,
+            "hbm_bytes_per_launch": (fr + wr) if fr is not None and wr is not None else None,
+            "algorithmic_bytes_per_launch": a,
+            "algorithmic_GBps_at_avg": (a / (avg_ns * 1e-9) / 1e9) if a else None,
+            "resources": res.get(n, {}),
+            "compiler_resources": built.get(n, {}),
+        }
+    with open(os.path.join(out_dir, f"traffic_{workload}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    with open(stats_p[0]) as f:
+        stats_text = f.read().strip()
+    md = [f"# {workload}: rocprofv3 kernel trace and HBM traffic", "",
+          f"Kernel sources: sha256[:16] = `{out['kernel_source_sha256_16']}` (the kernel templates, "
+          "launch tables and instance files, as hashed by bench.py).", "",
+          "## Commands (run from /tmp with TMPDIR=/tmp; R = repository root)", "", "```",
+          *out["commands"], "```", "", "## Kernel statistics (trace_kernel_stats.csv)", "", "```",
+          stats_text, "```", "", "## HBM traffic per launch (FETCH_SIZE, WRITE_SIZE)", "",
+          f"Calibration: the runtime's device copy `{COPY_KERNEL}` of {copy_bytes:,} bytes reads "
+          f"FETCH_SIZE = {cf:.1f} KiB and WRITE_SIZE = {cw:.1f} KiB per dispatch, so FETCH_SIZE is "
+          f"scaled by {sf:.4f} and WRITE_SIZE by {sw:.4f} to bytes.", "",
+          "| kernel | avg us | algorithmic bytes | fetched bytes | written bytes | measured / "
+          "algorithmic | algorithmic GB/s at avg |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for label, k in out["kernels"].items():
+        a, h, r = k["algorithmic_bytes_per_launch"], k["hbm_bytes_per_launch"], k["resources"]
+        alg_s = f"{a:,}" if a else "-"
+        ratio = f"{h / a:.4f}" if a and h else "-"
+        gbs = f"{k['algorithmic_GBps_at_avg']:.0f}" if a else "-"
+        fetched = f"{k['fetch_bytes_per_launch'] or 0:,.0f}"
+        written = f"{k['write_bytes_per_launch'] or 0:,.0f}"
+        md.append(f"| {label} (`{k['name'].split('(')[0]}`) | {k['avg_ns'] / 1000:.2f} | {alg_s} | "
+                  f"{fetched} | {written} | {ratio} | {gbs} |")
+    md += ["", "## Kernel resources (compiler remarks at build time; launch shape from the trace)",
+           "", "| kernel | VGPRs | AGPRs | SGPRs | LDS bytes / block | scratch bytes / lane | "
+           "occupancy (waves / SIMD) | workgroup | grid |", "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for label, k in out["kernels"].items():
+        c, r = k["compiler_resources"], k["resources"]
+        md.append(f"| {label} | {c.get('VGPRs', '?')} | {c.get('AGPRs', '?')} | "
+                  f"{c.get('TotalSGPRs', '?')} | {c.get('LDS Size [bytes/block]', '?')} | "
+                  f"{c.get('ScratchSize [bytes/lane]', '?')} | "
+                  f"{c.get('Occupancy [waves/SIMD]', '?')} | {r.get('Workgroup_Size_X', '?')} | "
+                  f"{r.get('Grid_Size_X', '?')} |")
+    md.append("")
+    with open(os.path.join(out_dir, f"{workload}_trace_and_traffic.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
 
 
 NORM_NAMES = {"rms": "RMSNorm", "ln": "LayerNorm", "add": "fused add + RMSNorm",
@@ -541,6 +765,9 @@ def main():
                     help="storage of dY, dH (default: --act)")
     ap.add_argument("--dx", default=None, choices=sorted(SIZE),
                     help="storage of dX (default: --act)")
+    ap.add_argument("--summarize-profile", metavar="PREFIX", default=None,
+                    help="instead of running: summarize the rocprofv3 runs PREFIX_trace, "
+                         "PREFIX_fetch and PREFIX_write of --workload into profiles/")
     ap.add_argument("--pages-context", action="store_true",
                     help="instead of the training step: host-wall time of the binary32 "
                          "LayerNorm forward at the shapes the pages time")
@@ -551,6 +778,10 @@ def main():
               "is row-local, so a multi-GPU run is this single-GPU path on each GPU's rows plus "
               "one dgamma all-reduce, which is not implemented here", file=sys.stderr)
         sys.exit(2)
+
+    if args.summarize_profile:
+        summarize_profile(args.workload, args.summarize_profile)
+        return
 
     import torch
     import row_wise_normalization_amd as mn
@@ -663,6 +894,52 @@ def main():
     ms_step = (t1 - t0) * 1e3 / K
     rows_ms = float(np.mean([a.elapsed_ms(b) for a, b in ev]))
 
+    # Launch-bound workloads (under 64 MB per step): back-to-back device
+    # throughput, 1000 steps enqueued without synchronizing, once issued from
+    # Python (host-issue bound) and once replayed from a HIP graph of 100
+    # steps (device bound), events around each.
+    b2b = None
+    if fwd_b + bwd_b < (64 << 20):
+        nb = 1000
+        e0, e1 = HipEvent(), HipEvent()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for k in range(nb):
+            step(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_us = e0.elapsed_ms(e1) * 1e3 / nb
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            step_stream = stream
+            stream = side
+            for k in range(4):
+                step(k)
+            side.synchronize()
+            with torch.cuda.graph(graph, stream=side):
+                for k in range(100):
+                    step(k)
+            stream = step_stream
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(stream)
+        for _ in range(nb // 100):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_ms(e1) * 1e3 / nb
+        b2b = {"steps": nb, "eager_us_per_step": round(eager_us, 3),
+               "graph_us_per_step": round(graph_us, 3),
+               "graph_rows_per_s": round(N / (graph_us * 1e-6), 1),
+               "graph_GBps": round((fwd_b + bwd_b) / (graph_us * 1e-6) / 1e9, 1),
+               "note": "1000 forward + backward steps back to back between two events: issued "
+                       "from Python one call at a time, and replayed from a captured HIP graph "
+                       "of 100 steps"}
+
     # Diagnostic pass (not the timed region): every kernel bracketed.
     dg = [[HipEvent() for _ in range(4)] for _ in range(K)]
     for k in range(K):
@@ -731,6 +1008,8 @@ def main():
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
     }
+    if b2b is not None:
+        line["back_to_back"] = b2b
     print(json.dumps(line), flush=True)
 
 

@@ -4,6 +4,7 @@ Usage: python -m row_wise_normalization_amd.build  (or call build()).
 """
 from __future__ import annotations
 
+import json
 import os
 import shutil
 import subprocess
@@ -47,9 +48,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmn_norm.so)")
 
 
+RESOURCES = os.path.join(PKG, "_build", "kernel_resources.json")
+
+
+def _resources(remarks: str):
+    """Per-kernel resource usage from the compiler's
+    kernel-resource-usage remarks: {mangled name: {field: value}}."""
+    out, cur = {}, None
+    for line in remarks.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].split("[-Rpass", 1)[0].strip()
+        if body.startswith("Function Name:"):
+            cur = body.split(":", 1)[1].strip()
+            out[cur] = {}
+        elif cur and ":" in body:
+            k, v = body.split(":", 1)
+            out[cur][k.strip()] = v.strip()
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source (in parallel) and link the shared library; always
-    rebuilds."""
+    rebuilds. The compiler's per-kernel resource usage (VGPRs, AGPRs, LDS,
+    scratch, occupancy) is kept in _build/kernel_resources.json, keyed by
+    the demangled kernel name, for the profile summaries."""
     objs = []
     build_dir = os.path.join(PKG, "_build")
     os.makedirs(build_dir, exist_ok=True)
@@ -57,14 +80,27 @@ def build(verbose: bool = False) -> str:
     procs = []
     for src in SOURCES:
         obj = os.path.join(build_dir, src + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-I", INCLUDE,
+               "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd)))
+        procs.append((src, subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True)))
         objs.append(obj)
-    failed = [src for src, p in procs if p.wait() != 0]
+    failed, resources = [], {}
+    for src, p in procs:
+        _, err = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(err)
+            failed.append(src)
+        else:
+            resources.update(_resources(err))
     if failed:
         raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
+    names = list(resources)
+    dem = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True)
+    pretty = dem.stdout.splitlines() if dem.returncode == 0 else names
+    with open(RESOURCES, "w") as f:
+        json.dump({d: resources[m] for m, d in zip(names, pretty)}, f, indent=0)
     tmp = LIB_PATH + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
