@@ -56,11 +56,18 @@ def test_large_mean_layernorm():
 
 def test_deterministic_and_row_independent():
     """Bitwise repeatable, and an output row does not depend on the other rows
-    of the batch (each row's statistics and sums are its own)."""
+    of the batch (each row's statistics and sums are its own). Another input
+    runs through the shared workspace between the repeats, so a repeat that
+    read a stale partial or statistic of its own earlier call could not pass
+    by reading the same bits again."""
     d = _case(4, 4096, 2048, 8, False)
+    other = _case(4, 4096, 2048, 9, False)
     a = run(d, 1e-5, False)
+    b = run(other, 1e-5, False)
+    assert not np.array_equal(a.view(np.uint16), b.view(np.uint16))
     assert np.array_equal(a.view(np.uint16), run(d, 1e-5, False).view(np.uint16))
     one = {k: (v[1:2] if k == "X" else v) for k, v in d.items()}
+    run(other, 1e-5, False)
     assert np.array_equal(a[1:2].view(np.uint16), run(one, 1e-5, False).view(np.uint16))
 
 
@@ -79,20 +86,26 @@ def test_long_rows_few_columns(ln):
                                      (1, 4096, 14336, False), (8, 1024, 4096, True),
                                      (1, 131072, 64, False)])
 def test_repeated_calls_bitwise(M, K, N, ln):
-    """400 back-to-back calls through one workspace give the first call's bits
-    every time: every workgroup that completes a tile reads every partial and
-    statistic it needs, whichever XCD wrote them."""
-    d = _case(M, K, N, 21, ln)
-    X, g, W = dev(d["X"]), dev(d["gamma"]), dev(d["W"])
-    b = dev(d["beta"]) if ln else None
+    """400 back-to-back calls through one workspace, two different inputs in
+    turn (other X rows, gamma, beta and W): every call gives the bits of the
+    first call on its own input. A workgroup that completed a tile from a
+    partial or statistic not yet visible would read the other input's value
+    left in the workspace by the call before, and differ."""
+    sets = []
+    for seed in (21, 22):
+        d = _case(M, K, N, seed, ln)
+        sets.append((dev(d["X"]), dev(d["gamma"]), dev(d["W"]),
+                     dev(d["beta"]) if ln else None))
     ws = workspace(M, N, K)
-    ys = [torch.empty(M, N, dtype=X.dtype, device="cuda") for _ in range(400)]
-    for y in ys:
+    ys = [torch.empty(M, N, dtype=sets[0][0].dtype, device="cuda") for _ in range(400)]
+    for i, y in enumerate(ys):
+        X, g, W, b = sets[i % 2]
         mn.mn_fused_norm_gemv_ex(X, g, W, y, 1e-5, ws, beta=b)
     torch.cuda.synchronize()
-    first = ys[0].view(torch.int16)
-    bad = [i for i, y in enumerate(ys) if not torch.equal(y.view(torch.int16), first)]
-    assert not bad, f"{M}x{K}x{N}: calls {bad[:8]} differ from the first"
+    first = [ys[0].view(torch.int16), ys[1].view(torch.int16)]
+    assert not torch.equal(first[0], first[1])
+    bad = [i for i, y in enumerate(ys) if not torch.equal(y.view(torch.int16), first[i % 2])]
+    assert not bad, f"{M}x{K}x{N}: calls {bad[:8]} differ from the first call on their input"
 
 
 def test_counters_back_at_zero():
