@@ -43,8 +43,8 @@ KERNEL_SRCS = {
     "pair": _ROW + ("mn_inst_f16.hip", "mn_inst_bf16.hip", "mn_inst_f32.hip"),
     "other": _ROW + ("mn_inst_ext_f16.hip", "mn_inst_ext_bf16.hip", "mn_inst_ext_f32.hip"),
     "gn": ("mn_kernels.hpp", "mn_kernels.hip", "mn_tables.hpp", "mn_groupnorm.hpp",
-           "mn_gn_instances.hpp", "mn_gn_plan.hip", "mn_gn_f16.hip", "mn_gn_bf16.hip",
-           "mn_gn_f32.hip"),
+           "mn_gn_instances.hpp", "mn_gn_plan.hip", "mn_gn_fwd_f16.hip", "mn_gn_bwd_f16.hip",
+           "mn_gn_fwd_bf16.hip", "mn_gn_bwd_bf16.hip", "mn_gn_fwd_f32.hip", "mn_gn_bwd_f32.hip"),
     "gemv": ("mn_kernels.hpp", "mn_gemv.hip"),
 }
 
@@ -645,7 +645,7 @@ def bench_other(args, w, torch, mn, act, param, dxt):
              "Y": torch.empty(shp, dtype=tdt[act], device=dev),
              "dX": torch.empty(shp, dtype=tdt[dxt], device=dev)}
         if kind == "gn":
-            b["ws"] = torch.empty(mn.groupnorm_workspace_bytes(N, C) // 4, dtype=torch.float32,
+            b["ws"] = torch.empty(mn.groupnorm_workspace_bytes(N, C, D // C, G) // 4, dtype=torch.float32,
                                   device=dev)
         else:
             kcode = {"dyt": mn.MN_DYT, "poly": mn.MN_POLYNORM, "mod": mn.MN_MOD_RMSNORM}[kind]

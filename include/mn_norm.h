@@ -290,15 +290,18 @@ size_t mn_mod_rmsnorm_workspace_bytes(int64_t B, int64_t N, int64_t D);
  *   (population variance, eps inside the square root, as LayerNorm);
  *   y = (x - mean) * rstd * gamma[c] + beta[c]  (gamma, beta [C] of `param`);
  *   dgamma[c] = sum over n, l of dY * xhat, dbeta[c] = sum of dY (fp32 [C]).
- * Storage: X, Y, dY in `act`; dX in `act` or MN_F32 (`dxt`). One workgroup
- * holds a slice in registers (at most 1024 lanes; each channel row padded to
- * its lane layout), which covers slices up to 65,536 values when L is a
- * power of two from 64 to 8,192 and 32,768 at L = 16,384 (16-bit storage;
- * half as many in binary32), and up to 16,384 values for L that is not a
- * multiple of the 16-byte chunk or unaligned rows. Shapes that do not fit return MN_ERR_SHAPE, as do
- * C % G != 0, zero sizes and L above 16,384. The backward workspace
- * (mn_groupnorm_workspace_bytes(N, C), 16-byte aligned) holds per-sample
- * fp32 partials of dgamma and dbeta, added in fixed order by a second kernel.
+ * Storage: X, Y, dY in `act`; dX in `act` or MN_F32 (`dxt`). Any shape with
+ * C % G == 0 and positive sizes is accepted (slices of up to 2^31 - 1 values,
+ * L up to 2^30 - 1): a slice that fits one workgroup's registers is handled
+ * by one kernel per direction; a larger one is split over many workgroups,
+ * with its statistics (forward) or its channel and slice sums (backward)
+ * combined in fixed order between launches. The split forward keeps its
+ * per-chunk statistics in Y until it writes Y. The backward workspace
+ * (mn_groupnorm_workspace_bytes(N, C, L, G) bytes, 16-byte aligned; no
+ * initial contents needed) holds the per-sample fp32 partials of dgamma and
+ * dbeta, added in fixed order by a second kernel, and the split path's
+ * sums. Errors: MN_ERR_SHAPE for C % G != 0, zero sizes or sizes beyond
+ * those bounds; otherwise as the row-wise norms.
  * ------------------------------------------------------------------------- */
 mn_status mn_groupnorm_forward_ex(const void* X, const void* gamma, const void* beta, void* Y,
                                   float* mean, float* rstd, int64_t N, int64_t C, int64_t L,
@@ -309,7 +312,7 @@ mn_status mn_groupnorm_backward_ex(const void* X, const void* gamma, const float
                                    float* dbeta, int64_t N, int64_t C, int64_t L, int64_t G,
                                    mn_dtype act, mn_dtype param, mn_dtype dxt, void* workspace,
                                    size_t workspace_bytes, void* stream);
-size_t mn_groupnorm_workspace_bytes(int64_t N, int64_t C);
+size_t mn_groupnorm_workspace_bytes(int64_t N, int64_t C, int64_t L, int64_t G);
 
 /* ---------------------------------------------------------------------------
  * Fused normalization + GEMV for small inference batches. [tensorcore]

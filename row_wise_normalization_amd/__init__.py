@@ -112,7 +112,7 @@ def lib() -> ctypes.CDLL:
     L.mn_norm_workspace_bytes.restype = _SZ
     L.mn_mod_rmsnorm_workspace_bytes.argtypes = [_I64, _I64, _I64]
     L.mn_mod_rmsnorm_workspace_bytes.restype = _SZ
-    L.mn_groupnorm_workspace_bytes.argtypes = [_I64, _I64]
+    L.mn_groupnorm_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
     L.mn_groupnorm_workspace_bytes.restype = _SZ
     L.mn_norm_gemv_workspace_bytes.argtypes = [_I64, _I64, _I64]
     L.mn_norm_gemv_workspace_bytes.restype = _SZ
@@ -485,8 +485,8 @@ def mn_groupnorm_backward_ex(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, groups
           _ptr(workspace), _ws_bytes(workspace), _stream(stream))
 
 
-def groupnorm_workspace_bytes(N: int, C: int) -> int:
-    return int(lib().mn_groupnorm_workspace_bytes(int(N), int(C)))
+def groupnorm_workspace_bytes(N: int, C: int, L: int, G: int) -> int:
+    return int(lib().mn_groupnorm_workspace_bytes(int(N), int(C), int(L), int(G)))
 
 
 def _ws_bytes(workspace: Optional[torch.Tensor]) -> int:

@@ -433,16 +433,35 @@ bool gn_shape_ok(int64_t N, int64_t C, int64_t L, int64_t G)
     return N <= (INT64_MAX / 4) / C / L;
 }
 
-size_t gn_workspace_bytes(int64_t N, int64_t C)
+size_t gn_workspace_bytes(int64_t N, int64_t C, int64_t L, int64_t G)
 {
-    if (N < 1 || C < 1 || C > INT32_MAX / 4 || N > (INT64_MAX / 16) / gn_cp(C)) return 0;
-    return 2 * sizeof(float) * (size_t)N * (size_t)gn_cp(C);
+    if (!gn_shape_ok(N, C, L, G)) return 0;
+    const int64_t f = mn::gn_workspace_floats(N, C, L, G);
+    return f > 0 ? (size_t)f * sizeof(float) : 0;
 }
 
 bool gn_vec_ok(int st, int64_t L, const void* a, const void* b, const void* c = nullptr,
                const void* d = nullptr)
 {
     return chunks_fit(st, L) && aligned16(a) && aligned16(b) && aligned16(c) && aligned16(d);
+}
+
+void gn_common(mn::GnArgs& a, const mn::GnPlan& plan, int64_t N, int64_t C, int64_t L,
+               int64_t G)
+{
+    a.S = N * G;
+    a.C = (int32_t)C;
+    a.L = (int32_t)L;
+    a.G = (int32_t)G;
+    a.Cg = (int32_t)(C / G);
+    a.Cp = (int32_t)gn_cp(C);
+    if (plan.split) {
+        a.units = plan.units;
+        a.Kr = plan.Kr;
+        a.UL = plan.UL;
+        a.Kf = plan.Kf;
+        a.FL = plan.FL;
+    }
 }
 
 mn_status groupnorm_forward(const void* X, const void* gamma, const void* beta, void* Y,
@@ -454,7 +473,7 @@ mn_status groupnorm_forward(const void* X, const void* gamma, const void* beta, 
     if (!gn_shape_ok(N, C, L, G)) return MN_ERR_SHAPE;
     const bool vec = gn_vec_ok(st, L, X, Y);
     mn::GnPlan plan;
-    if (!mn::plan_groupnorm(st, N, C, L, G, vec, true, plan)) return MN_ERR_SHAPE;
+    if (!mn::plan_groupnorm(st, st, pdt, N, C, L, G, vec, true, plan)) return MN_ERR_SHAPE;
     if (!eps_ok(eps)) return MN_ERR_EPS;
     const size_t es = (size_t)mn::stor_bytes(st), ps = (size_t)mn::stor_bytes(pdt);
     const size_t nx = (size_t)N * (size_t)C * (size_t)L;
@@ -469,13 +488,18 @@ mn_status groupnorm_forward(const void* X, const void* gamma, const void* beta, 
     a.Y = Y;
     a.mean = mean;
     a.rstd = rstd;
-    a.C = (int32_t)C;
-    a.L = (int32_t)L;
-    a.G = (int32_t)G;
-    a.Cg = (int32_t)(C / G);
-    a.Cp = (int32_t)gn_cp(C);
     a.pdt = pdt;
     a.eps = eps;
+    gn_common(a, plan, N, C, L, G);
+    if (plan.split) {
+        // the chunk statistics go into Y (16-byte aligned within it) until
+        // the apply pass overwrites it
+        const uintptr_t y = reinterpret_cast<uintptr_t>(Y);
+        const uintptr_t st16 = (y + 15) & ~(uintptr_t)15;
+        const size_t need = (size_t)(st16 - y) + 8 * (size_t)(N * G) * (size_t)plan.Kf;
+        if (need > nx * es) return MN_ERR_SHAPE;
+        a.stat = reinterpret_cast<float*>(st16);
+    }
     return device_status(mn::launch_gn_fwd(st, plan, a, as_stream(stream)));
 }
 
@@ -489,8 +513,9 @@ mn_status groupnorm_backward(const void* X, const void* gamma, const float* mean
     if (!gn_shape_ok(N, C, L, G)) return MN_ERR_SHAPE;
     const bool vec = gn_vec_ok(st, L, X, dY, dX);
     mn::GnPlan plan;
-    if (!mn::plan_groupnorm(st, N, C, L, G, vec, false, plan)) return MN_ERR_SHAPE;
-    const size_t need = gn_workspace_bytes(N, C);
+    if (!mn::plan_groupnorm(st, ot, pdt, N, C, L, G, vec, false, plan)) return MN_ERR_SHAPE;
+    const size_t need = gn_workspace_bytes(N, C, L, G);
+    if (need == 0) return MN_ERR_SHAPE;
     if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
     const size_t es = (size_t)mn::stor_bytes(st), ps = (size_t)mn::stor_bytes(pdt);
     const size_t os = (size_t)mn::stor_bytes(ot);
@@ -508,13 +533,17 @@ mn_status groupnorm_backward(const void* X, const void* gamma, const float* mean
     a.dX = dX;
     a.mean = const_cast<float*>(mean);
     a.rstd = const_cast<float*>(rstd);
-    a.part_g = static_cast<float*>(ws);
-    a.part_b = static_cast<float*>(ws) + N * gn_cp(C);
-    a.C = (int32_t)C;
-    a.L = (int32_t)L;
-    a.G = (int32_t)G;
-    a.Cg = (int32_t)(C / G);
-    a.Cp = (int32_t)gn_cp(C);
+    gn_common(a, plan, N, C, L, G);
+    // workspace: part_g, part_b [N][Cp]; then (split path) unit_p, unit_q
+    // [N * C * Kr] and the slice sums [N * G][2]
+    float* w = static_cast<float*>(ws);
+    a.part_g = w;
+    a.part_b = w + N * a.Cp;
+    if (plan.split) {
+        a.unit_p = w + 2 * N * a.Cp;
+        a.unit_q = a.unit_p + plan.units;
+        a.slice_ab = a.unit_q + plan.units;
+    }
     a.pdt = pdt;
     hipStream_t s = as_stream(stream);
     hipError_t e = mn::launch_gn_bwd(st, ot, plan, a, s);
@@ -845,7 +874,10 @@ mn_status mn_groupnorm_backward_ex(const void* X, const void* gamma, const float
                               param, dxt, workspace, workspace_bytes, stream);
 }
 
-size_t mn_groupnorm_workspace_bytes(int64_t N, int64_t C) { return gn_workspace_bytes(N, C); }
+size_t mn_groupnorm_workspace_bytes(int64_t N, int64_t C, int64_t L, int64_t G)
+{
+    return gn_workspace_bytes(N, C, L, G);
+}
 
 // --- fused normalization + GEMV (inference) ---------------------------------
 

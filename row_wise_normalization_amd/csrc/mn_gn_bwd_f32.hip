@@ -1,7 +1,6 @@
-// GroupNorm launchers for f32 activations.
+// GroupNorm backward launchers for f32 activations.
 #include "mn_gn_instances.hpp"
 
 namespace mn {
-template hipError_t launch_gn_fwd_t<ST_F32>(const GnPlan&, const GnArgs&, hipStream_t);
 template hipError_t launch_gn_bwd_t<ST_F32, ST_F32>(const GnPlan&, const GnArgs&, hipStream_t);
 }  // namespace mn

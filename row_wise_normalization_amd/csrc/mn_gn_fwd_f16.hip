@@ -1,0 +1,6 @@
+// GroupNorm forward launchers for f16 activations.
+#include "mn_gn_instances.hpp"
+
+namespace mn {
+template hipError_t launch_gn_fwd_t<ST_F16>(const GnPlan&, const GnArgs&, hipStream_t);
+}  // namespace mn

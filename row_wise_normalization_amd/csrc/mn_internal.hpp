@@ -119,7 +119,15 @@ hipError_t launch_backward_rows(int kind, int st, int ct, int ot, const BwdPlan&
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 
 // GroupNorm over X [N][C][L]: G groups of Cg = C / G consecutive channels;
-// one workgroup per (sample, group) slice of Cg rows of L values.
+// the (sample, group) slice s = n * G + g is Cg * L contiguous values.
+//
+// Slices that fit one workgroup's registers take one kernel per direction
+// (persistent workgroups, one slice at a time, the next slice's loads in
+// flight). Larger slices take the split path: the forward as per-chunk
+// statistics, a fixed-order merge per slice and an apply pass; the backward
+// as per-chunk channel sums, a per-slice merge (dgamma, dbeta partials and
+// the slice sums) and an apply pass. A chunk ("unit") of the split path's
+// row kernels is up to kGnUnitIt chunks per lane of one channel row.
 struct GnArgs {
     const void* X;           // [N][C][L], storage type of the launch
     const void* gamma;       // [C], type pdt
@@ -131,21 +139,39 @@ struct GnArgs {
     float* rstd;             // [N][G]
     float* part_g;           // [N][Cp] per-sample sums of dY * xhat per channel
     float* part_b;           // [N][Cp] per-sample sums of dY per channel
+    // split path
+    float* unit_p;           // backward: [N * C * Kr] per-unit sums of dY * xhat
+    float* unit_q;           // backward: [N * C * Kr] per-unit sums of dY
+    float* slice_ab;         // backward: [N * G][2] the slice sums A, B
+    float* stat;             // forward: [N * G * Kf][2] per-chunk mean and M2
+    int64_t S;               // slices, N * G
+    int64_t units;           // row units, N * C * Kr
     int32_t C, L, G, Cg, Cp, pdt;
+    int32_t Kr;              // row units per channel row
+    int32_t UL;              // values per row unit (the last one of a row may be shorter)
+    int32_t Kf;              // statistics chunks per slice
+    int32_t FL;              // values per statistics chunk (the last one may be shorter)
     float eps;
-    int32_t sk;              // backward: dY chunks per lane staged in LDS (the first sk)
 };
 
 struct GnPlan {
-    int id;                  // launch shape (T, VEC, CPT, U)
-    int32_t block;           // threads: a multiple of 64, at most 1024
-    int64_t grid;            // N * G
+    bool split;              // the split path (slice larger than one workgroup)
+    int id;                  // register path: launch shape (T, VEC, CPT, U, prefetch);
+                             // split path: 1 for 16-byte chunks, 0 element-wise
+    int32_t block;           // register path: threads, a multiple of 64, at most 1024
+    int64_t grid;            // register path: persistent workgroups, at most N * G
+    int tid;                 // split path: lanes per row unit, 8 << tid
+    int32_t Kr, UL, Kf, FL;  // split path geometry (see GnArgs)
+    int64_t units;
 };
 
-// false when the slice does not fit one workgroup's registers (the same
-// shapes for both directions; the forward plan may hold more rows per lane)
-bool plan_groupnorm(int st, int64_t N, int64_t C, int64_t L, int64_t G, bool vec_ok, bool fwd,
-                    GnPlan& p);
+// Plans either path for a valid shape (false only when a count exceeds the
+// launch limits; `ot` is the dX type, the activation type for the forward;
+// `pdt` the gamma / beta type); the workspace is gn_workspace_floats(N, C, L, G) floats
+// for both paths.
+bool plan_groupnorm(int st, int ot, int pdt, int64_t N, int64_t C, int64_t L, int64_t G,
+                    bool vec_ok, bool fwd, GnPlan& p);
+int64_t gn_workspace_floats(int64_t N, int64_t C, int64_t L, int64_t G);
 hipError_t launch_gn_fwd(int st, const GnPlan& p, const GnArgs& a, hipStream_t s);
 hipError_t launch_gn_bwd(int st, int ot, const GnPlan& p, const GnArgs& a, hipStream_t s);
 

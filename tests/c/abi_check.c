@@ -70,7 +70,7 @@ int main(void)
     EXPECT(mn_groupnorm_forward_ex(X, G, G + 4096, Y, r, r + 4096, 2, 64, 256, 7, 1e-5f, MN_F16,
                                    MN_F16, NULL),
            MN_ERR_SHAPE);
-    if (mn_groupnorm_workspace_bytes(2, 64) == 0) ++failures;
+    if (mn_groupnorm_workspace_bytes(2, 64, 256, 8) == 0) ++failures;
     if (mn_norm_gemv_workspace_bytes(4, 4096, 4096) == 0) ++failures;
     EXPECT(mn_fused_rmsnorm_gemv(X, G, dY, Y, 9, 4096, 4096, 1e-5f, ws,
                                  mn_norm_gemv_workspace_bytes(4, 4096, 4096), NULL),

@@ -46,7 +46,7 @@ def run(d, G: int, eps: float, offset: int = 0, dx_dtype: Optional[torch.dtype] 
     mn.mn_groupnorm_forward_ex(X, g, b, Y, mean, rstd, G, eps)
     dg = torch.empty(C, dtype=torch.float32, device="cuda")
     db = torch.empty(C, dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(16, mn.groupnorm_workspace_bytes(N, C)) // 4, dtype=torch.float32,
+    ws = torch.empty(max(16, mn.groupnorm_workspace_bytes(N, C, L, G)) // 4, dtype=torch.float32,
                      device="cuda")
     mn.mn_groupnorm_backward_ex(X, g, mean, rstd, dY, dX, dg, db, G, ws)
     torch.cuda.synchronize()

@@ -238,10 +238,15 @@ def test_groupnorm_validation_and_workspace():
     L_ = mn.lib()
     f = ctypes.c_float(1e-5)
     F16, BF16, F32 = mn.MN_F16, mn.MN_BF16, mn.MN_F32
-    # per-sample partial rows of dgamma and dbeta, C rounded up to 4
-    assert mn.groupnorm_workspace_bytes(32, 320) == 2 * 4 * 32 * 320
-    assert mn.groupnorm_workspace_bytes(3, 10) == 2 * 4 * 3 * 12
-    assert mn.groupnorm_workspace_bytes(0, 8) == 0 and mn.groupnorm_workspace_bytes(2, 0) == 0
+    # per-sample partial rows of dgamma and dbeta (C rounded up to 4), the
+    # split path's per-unit channel sums (units of at least 8192 values) and
+    # its slice sums
+    ws = lambda N, C, L, G: 2 * 4 * N * ((C + 3) // 4 * 4 + C * -(-L // 8192) + G)
+    assert mn.groupnorm_workspace_bytes(32, 320, 4096, 32) == ws(32, 320, 4096, 32)
+    assert mn.groupnorm_workspace_bytes(3, 10, 7, 5) == 2 * 4 * 3 * (12 + 10 + 5)
+    assert mn.groupnorm_workspace_bytes(1, 128, 262144, 32) == 2 * 4 * (128 + 128 * 32 + 32)
+    for bad in ((0, 8, 8, 1), (2, 0, 8, 1), (2, 8, 0, 1), (2, 8, 8, 0), (2, 8, 8, 3)):
+        assert mn.groupnorm_workspace_bytes(*bad) == 0
     N, C, L, G = 2, 8, 64, 2
     mean, rstd = P(0x30000000), P(0x38000000)
     fwd = lambda X=A, g=B, b=C_, Y=Dp, N=N, C=C, L=L, G=G, eps=f, act=F16, par=F16: \
@@ -249,13 +254,12 @@ def test_groupnorm_validation_and_workspace():
     assert fwd(b=NULL) == 1 and fwd(Y=NULL) == 1
     assert fwd(G=3) == 2                        # 3 does not divide 8
     assert fwd(G=0) == 2 and fwd(N=0) == 2 and fwd(L=0) == 2
-    assert fwd(L=16392) == 2                    # rows longer than 16,384
-    assert fwd(C=2560, L=1024, G=32) == 2       # an 81,920-value slice does not fit
-    assert fwd(C=16, L=16384, G=4) == 2         # 65,536 values at L = 16,384 do not fit
+    assert fwd(L=1 << 30) == 2                  # rows of 2^30 values or more
+    assert fwd(C=4096, L=1 << 20, G=1) == 2     # a slice of 2^32 values
     assert fwd(eps=ctypes.c_float(-1.0)) == 3
     assert fwd(Y=A) == 4                        # Y is X
     assert fwd(act=7) == 7 and fwd(par=9) == 7
-    ws = mn.groupnorm_workspace_bytes(N, C)
+    ws = mn.groupnorm_workspace_bytes(N, C, L, G)
     W = P(0xE0000000)
     bwd = lambda dxt=F16, act=F16, nb=ws, ws_=W, dX=E: L_.mn_groupnorm_backward_ex(
         A, B, mean, rstd, Dp, dX, F, G_, N, C, L, G, act, F16, dxt, ws_, nb, S)

@@ -183,8 +183,12 @@ def test_other_norm_guards(kind, N, D, off):
 
 # (N, C, L, G, offset): the vector path at several lane shapes, the
 # element-wise path (L not a multiple of 8), unaligned tensors, G = C
+# the last three take the split path (slices beyond one workgroup), on
+# 16-byte chunks, element-wise with several units per channel row, and with
+# many short channel rows
 GN_SHAPES = [(2, 64, 256, 8, 0), (2, 12, 100, 3, 0), (3, 32, 4096, 32, 0), (2, 40, 64, 4, 1),
-             (1, 16, 8, 16, 0), (4, 320, 1024, 32, 0)]
+             (1, 16, 8, 16, 0), (4, 320, 1024, 32, 0), (2, 32, 16384, 2, 0),
+             (1, 8, 20001, 1, 1), (2, 3000, 9, 1, 0)]
 
 
 @pytest.mark.parametrize("N,C,L,G,off", GN_SHAPES)
@@ -198,7 +202,7 @@ def test_groupnorm_guards(N, C, L, G, off):
             "dX": Guarded((N, C, L), torch.float16, off),
             "mean": Guarded((N, G), torch.float32), "rstd": Guarded((N, G), torch.float32),
             "dgamma": Guarded((C,), torch.float32), "dbeta": Guarded((C,), torch.float32),
-            "ws": workspace(mn.groupnorm_workspace_bytes(N, C))}
+            "ws": workspace(mn.groupnorm_workspace_bytes(N, C, L, G))}
     before = snapshot(ins)
     o = {k: v.t for k, v in outs.items()}
     i = {k: v.t for k, v in ins.items()}
