@@ -114,7 +114,16 @@ mn_status mn_rmsnorm_forward(const mn_f16* X, const mn_f16* gamma, mn_f16* Y, fl
  * forward. dgamma is reduced in two fixed-order stages through `workspace`
  * (caller-owned device memory of at least
  * mn_norm_workspace_bytes(MN_RMSNORM, N, D) bytes, contents on entry
- * ignored, clobbered on exit). */
+ * ignored, clobbered on exit). For small problems (N * round_up(D, 4) up
+ * to 131,072, rows of up to 5120 columns) both stages run in one launch:
+ * the last workgroup to finish
+ * its partial row adds them all, in the same order as the second stage
+ * (bitwise the same dgamma), found through an epoch and per-workgroup flags
+ * kept at the end of the workspace. These words need no clearing: a
+ * workgroup reduces early only if every flag not yet written already holds
+ * the 64-bit epoch word + 1, which neither cleared memory nor the words left
+ * by earlier calls of the same shape do. The same holds for the
+ * LayerNorm and fused-add backwards and their typed (_ex) forms. */
 mn_status mn_rmsnorm_backward(const mn_f16* X, const mn_f16* gamma, const float* rstd,
                               const mn_f16* dY, mn_f16* dX, float* dgamma,
                               int64_t N, int64_t D, void* workspace, size_t workspace_bytes,
@@ -360,11 +369,20 @@ size_t mn_norm_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Bytes of device workspace the backward of `kind` needs at (N, D): the
  * per-block fp32 parameter-gradient partials (two arrays for LayerNorm and
- * Dynamic Tanh, plus scalar partials for Dynamic Tanh and PolyNorm).
+ * Dynamic Tanh, plus scalar partials for Dynamic Tanh and PolyNorm), and for
+ * the one-launch backward of small RMSNorm, LayerNorm and fused-add
+ * problems 528 bytes of hand-off words.
  * Depends only on (kind, N, D). Returns 0 for invalid arguments and for
  * MN_MOD_RMSNORM, whose size also depends on the sample count (see
  * mn_mod_rmsnorm_workspace_bytes). */
 size_t mn_norm_workspace_bytes(mn_norm_kind kind, int64_t N, int64_t D);
+
+/* Kernel launches of the full backward of `kind` at (N, D), for any storage
+ * types and pointer alignment: 1 where the parameter-gradient reduction runs
+ * inside the row launch (RMSNorm, LayerNorm and the fused add with
+ * N * round_up(D, 4) <= 131,072 and D <= 5120), 2 otherwise (row kernel,
+ * then the fixed-order column reduce); 0 for an invalid kind or shape. */
+int mn_norm_backward_launches(mn_norm_kind kind, int64_t N, int64_t D);
 
 /* Static description of a status code. */
 const char* mn_status_string(mn_status s);
@@ -424,7 +442,8 @@ mn_status mn_norm_reduce_partials(mn_norm_kind kind, int64_t N, int64_t D,
  * allocate device memory (code under stream capture, tight serving loops,
  * harnesses that forbid hipMalloc). Same arguments, validation, kernels and
  * results as mn_rmsnorm_backward (bitwise), minus `workspace`: the dgamma
- * partial rows go to a fixed array of mn_noalloc_scratch_bytes() bytes
+ * partial rows (and, for small problems, the one-launch hand-off words) go
+ * to a fixed array of mn_noalloc_scratch_bytes() bytes
  * (8 MiB, enough for every valid N, D) that the library holds on each
  * device it runs on until the process ends; a shape needing more would
  * return MN_ERR_WORKSPACE. The call allocates nothing. Its first call on a

@@ -110,6 +110,8 @@ def lib() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     L.mn_norm_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64]
     L.mn_norm_workspace_bytes.restype = _SZ
+    L.mn_norm_backward_launches.argtypes = [ctypes.c_int, _I64, _I64]
+    L.mn_norm_backward_launches.restype = ctypes.c_int
     L.mn_mod_rmsnorm_workspace_bytes.argtypes = [_I64, _I64, _I64]
     L.mn_mod_rmsnorm_workspace_bytes.restype = _SZ
     L.mn_groupnorm_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
@@ -177,6 +179,10 @@ H, F32 = torch.float16, torch.float32
 
 def workspace_bytes(kind: int, N: int, D: int) -> int:
     return int(lib().mn_norm_workspace_bytes(int(kind), int(N), int(D)))
+
+
+def backward_launches(kind: int, N: int, D: int) -> int:
+    return int(lib().mn_norm_backward_launches(int(kind), int(N), int(D)))
 
 
 # --- the C entry points ------------------------------------------------------

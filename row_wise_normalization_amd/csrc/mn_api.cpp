@@ -76,7 +76,8 @@ int64_t partial_rows(int kind, int64_t N, int64_t D, int64_t B)
 bool has_scalar_partials(int kind) { return kind == mn::DYT || kind == mn::POLY; }
 
 // Workspace: per-workgroup fp32 partial rows [P][Dp] for each per-column
-// parameter gradient, then (DYT, POLY) [P][4] scalar partials.
+// parameter gradient, then (DYT, POLY) [P][4] scalar partials, then (small
+// problems of RMS, LN, ADD, whose backward is one launch) the hand-off words.
 size_t workspace_bytes(int kind, int64_t N, int64_t D, int64_t B = 1)
 {
     if (!shape_ok(N, D) || kind < 0 || kind > mn::MOD || !samples_ok(kind, B, N)) return 0;
@@ -84,6 +85,7 @@ size_t workspace_bytes(int kind, int64_t N, int64_t D, int64_t B = 1)
     const int64_t Dp = mn::partial_stride((int32_t)D);
     size_t bytes = (size_t)P * (size_t)Dp * sizeof(float) * (size_t)mn::bwd_vector_partials(kind);
     if (has_scalar_partials(kind)) bytes += (size_t)P * 4u * sizeof(float);
+    if (mn::bwd_small(kind, N, (int32_t)D)) bytes += mn::kSmallSyncBytes;
     return bytes;
 }
 
@@ -223,8 +225,12 @@ void out_spans(int kind, const BwdOut& o, int64_t D, int64_t B, Span (&sp)[4])
     sp[3] = span(o.dscalar, kind == mn::POLY ? 16u : 4u);
 }
 
+// `one_launch` (the full backward): for a small problem (mn::bwd_one_launch)
+// the row launch adds the partial rows itself and writes dgamma (dbeta);
+// *done says whether it did.
 mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, const BwdTypes& t,
-                        void* ws, size_t ws_bytes, const BwdOut& o, void* stream)
+                        void* ws, size_t ws_bytes, const BwdOut& o, void* stream,
+                        bool one_launch = false, bool* done = nullptr)
 {
     if (!b.X || !b.dY || !b.dX) return MN_ERR_NULL;
     if (kind != mn::POLY && !b.gamma) return MN_ERR_NULL;
@@ -286,6 +292,16 @@ mn_status backward_rows(int kind, const BwdIn& b, int64_t N, int64_t D, const Bw
     a.Dp = plan.Dp;
     a.pdt = t.pdt;
     a.Pb = plan.Pb;
+    a.sync = nullptr;
+    a.dgamma = nullptr;
+    a.dbeta = nullptr;
+    one_launch = one_launch && mn::bwd_one_launch(kind, N, (int32_t)D) && plan.v.BLOCK < 1024;
+    if (done) *done = one_launch;
+    if (one_launch) {
+        a.sync = reinterpret_cast<uint64_t*>(w + nv * PD);
+        a.dgamma = o.dgamma;
+        a.dbeta = kind == mn::LN ? o.dbeta : nullptr;
+    }
     return device_status(
         mn::launch_backward_rows(kind, st, t.ct, t.ot, plan, a, as_stream(stream)));
 }
@@ -568,8 +584,9 @@ mn_status backward(int kind, const BwdIn& b, const BwdOut& o, int64_t N, int64_t
     if ((kind == mn::LN || kind == mn::DYT || kind == mn::MOD) && !o.dbeta) return MN_ERR_NULL;
     if (kind == mn::MOD && !o.dshift) return MN_ERR_NULL;
     if (has_scalar_partials(kind) && !o.dscalar) return MN_ERR_NULL;
-    mn_status s = backward_rows(kind, b, N, D, t, ws, ws_bytes, o, stream);
-    if (s != MN_OK) return s;
+    bool one = false;
+    mn_status s = backward_rows(kind, b, N, D, t, ws, ws_bytes, o, stream, true, &one);
+    if (s != MN_OK || one) return s;
     return reduce_partials(kind, N, D, b.B, ws, ws_bytes, o, stream);
 }
 
@@ -937,6 +954,13 @@ size_t mn_norm_workspace_bytes(mn_norm_kind kind, int64_t N, int64_t D)
 {
     if (kind == MN_MOD_RMSNORM) return 0;  // depends on the sample count
     return workspace_bytes((int)kind, N, D);
+}
+
+int mn_norm_backward_launches(mn_norm_kind kind, int64_t N, int64_t D)
+{
+    if (kind == MN_MOD_RMSNORM) return shape_ok(N, D) ? 2 : 0;
+    if (workspace_bytes((int)kind, N, D) == 0) return 0;
+    return mn::bwd_one_launch((int)kind, N, (int32_t)D) ? 1 : 2;
 }
 
 size_t mn_mod_rmsnorm_workspace_bytes(int64_t B, int64_t N, int64_t D)

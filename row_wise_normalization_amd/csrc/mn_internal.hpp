@@ -64,6 +64,11 @@ struct BwdArgs {
     int32_t Dp;              // partial row stride (D rounded up to 4)
     int32_t pdt;             // storage type of gamma
     int32_t Pb;              // MOD: workgroups per sample (workgroup b serves sample b / Pb)
+    // one-launch backward of small problems (null otherwise): the hand-off
+    // words [epoch][flag per workgroup] and the parameter gradients
+    uint64_t* sync;
+    float* dgamma;
+    float* dbeta;            // LN
 };
 
 // Column-reduce (stage 2) arguments: out_y[z * D + j] = sum over the P rows
@@ -104,6 +109,20 @@ struct BwdPlan {
 // Partial-buffer geometry; depends only on (kind, N, D), and for MOD on the
 // sample count B.
 int64_t bwd_partial_rows(int kind, int64_t N, int32_t D);
+// Small problems of RMSNorm, LayerNorm and the fused add (N * Dp at most
+// 8 * kSmallPartialFloats): at most kSmallMaxP partial rows, added inside
+// the row launch by the workgroup that finds every partial row written, so
+// that the whole backward is one launch. The workspace then ends with the
+// hand-off words: an epoch and one flag per workgroup (kSmallSyncBytes).
+constexpr int64_t kSmallPartialFloats = 16384;
+constexpr int64_t kSmallMaxP = 64;
+constexpr size_t kSmallSyncBytes = (8 * (1 + kSmallMaxP) + 15) / 16 * 16;
+bool bwd_small(int kind, int64_t N, int32_t D);
+// The full backward is one launch for small problems whose rows have at most
+// kSmallMaxD columns (every row variant up to that width has fewer than 1024
+// lanes, the variants that carry the in-kernel reduce).
+constexpr int32_t kSmallMaxD = 5120;
+bool bwd_one_launch(int kind, int64_t N, int32_t D);
 int32_t mod_blocks_per_sample(int64_t B, int64_t N);
 int bwd_vector_partials(int kind);
 int32_t partial_stride(int32_t D);

@@ -11,6 +11,9 @@ namespace {
 using kern::reduce_kernel;
 
 constexpr int kReduceCQ = 16;  // 64 columns per block, 64 segments
+// the one-launch backward adds its partial rows in this kernel's order,
+// which for at most 64 rows is one row per segment
+static_assert(1024 / kReduceCQ == kSmallMaxP, "one-launch reduce order");
 
 struct VariantRow {
     Variant v;
@@ -89,8 +92,39 @@ int64_t bwd_blocks(int kind, int32_t D)
 
 int32_t partial_stride(int32_t D) { return (D + 3) & ~3; }
 
+bool bwd_small(int kind, int64_t N, int32_t D)
+{
+    return (kind == RMS || kind == LN || kind == ADD) &&
+           N * (int64_t)partial_stride(D) <= kSmallPartialFloats * 8;
+}
+
+bool bwd_one_launch(int kind, int64_t N, int32_t D)
+{
+    return bwd_small(kind, N, D) && D <= kSmallMaxD;
+}
+
+// every row variant that serves widths up to kSmallMaxD has fewer than 1024
+// lanes (the one-launch reduce is compiled into those only)
+#define MN_SMALL_OK(id, T, VEC, CPT, U, BLOCK, PF, NT, MAXD) \
+    static_assert(MAXD > kSmallMaxD || BLOCK < 1024, "one-launch row variant");
+MN_BWD_RMS(MN_SMALL_OK)
+MN_BWD_LN(MN_SMALL_OK)
+MN_BWD_ADD(MN_SMALL_OK)
+MN_BWD_GEN(MN_SMALL_OK)
+#undef MN_SMALL_OK
+
 int64_t bwd_partial_rows(int kind, int64_t N, int32_t D)
 {
+    // Small problems: about eight rows per workgroup, rounded up to a power
+    // of two (the one-launch reduce then needs no masking of absent rows;
+    // workgroups past the last tile write zero rows, as they do whenever
+    // there are fewer tiles than workgroups), at most 64 workgroups.
+    if (bwd_small(kind, N, D)) {
+        const int64_t k = (N + 7) / 8;
+        int64_t p = 1;
+        while (p < k && p < kSmallMaxP) p *= 2;
+        return p;
+    }
     return N < bwd_blocks(kind, D) ? N : bwd_blocks(kind, D);
 }
 

@@ -652,6 +652,128 @@ __device__ __forceinline__ MixConst mix_const()
     return m;
 }
 
+// ---------------------------------------------------------------------------
+// The end of the one-launch backward of a small problem: each workgroup,
+// once its partial rows are stored device-coherently, sets its flag to this
+// call's epoch + 1 and reads every flag; a workgroup that finds them all set
+// adds the P partial rows (P = gridDim.x, a power of two up to 64) in the
+// column-reduce kernel's order, so dgamma (dbeta) is bitwise that of the
+// two-launch backward.
+//
+// Nothing waits on another workgroup: the last flag to be stored is followed
+// by its own workgroup's reads, which see every flag (each flag is stored
+// only after its workgroup's partial rows completed, and read only after the
+// reader's own flag completed); any other workgroup that also sees them all
+// writes the same values. Every workgroup reads the epoch before storing its
+// flag, so the epoch, advanced by the reducer for the next call, changes
+// only after all have read it; calls on one stream run in order.
+//
+// The column-reduce kernel sums 64 segments, here one row each (0 past P),
+// each from 0.0f, then pairwise (h = 32, 16, .., 1). P is a power of two on
+// this path, and the levels h >= P add +0 to a value that is never -0, so
+// they change nothing: the P-leaf tree gives the same bits. A lane holds
+// NV x P x W values (W adjacent columns of each plane, one 4 W-byte load per
+// row). The loads
+// are device-coherent (scope bit sc1 of the buffer load: no line of the
+// XCD's own L2 is returned), so no cache invalidation precedes them. Their
+// byte offset walks in a vector register so that the P row offsets are not
+// all held in scalar registers (which spilled them into a vector register
+// of every kernel that carries this path).
+// ---------------------------------------------------------------------------
+constexpr int kBufferSc1 = 16;             // cache-policy operand: sc1
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+template <int P, int W, int BLOCK, int NV>
+__device__ __forceinline__ void small_rows_sum(const BwdArgs& a, int D, int tid)
+{
+    static_assert(W == 1 || W == 2 || W == 4, "load width");
+    __amdgpu_buffer_rsrc_t r[NV];
+#pragma unroll
+    for (int y = 0; y < NV; ++y)
+        r[y] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(y == 0 ? a.part_g : a.part_b),
+                                                 0, P * a.Dp * (int)sizeof(float), kBufferWord3);
+#pragma unroll 1
+    for (int c = tid * W; c < D; c += BLOCK * W) {
+        // both planes' loads are issued before either is added
+        float v[NV][P][W];
+        uint32_t off = (uint32_t)c * sizeof(float);
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+#pragma unroll
+            for (int y = 0; y < NV; ++y) {
+                float x[W];
+                if constexpr (W == 4) {
+                    const f4 t = __builtin_bit_cast(
+                        f4, __builtin_amdgcn_raw_buffer_load_b128(r[y], off, 0, kBufferSc1));
+                    x[0] = t[0]; x[1] = t[1]; x[2] = t[2]; x[3] = t[3];
+                } else if constexpr (W == 2) {
+                    typedef float f2 __attribute__((ext_vector_type(2)));
+                    const f2 t = __builtin_bit_cast(
+                        f2, __builtin_amdgcn_raw_buffer_load_b64(r[y], off, 0, kBufferSc1));
+                    x[0] = t[0]; x[1] = t[1];
+                } else {
+                    x[0] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(r[y], off, 0, kBufferSc1));
+                }
+#pragma unroll
+                for (int e = 0; e < W; ++e) v[y][q][e] = 0.0f + x[e];
+            }
+            off += (uint32_t)a.Dp * sizeof(float);
+            asm volatile("" : "+v"(off));  // no instruction: keeps off in a VGPR
+        }
+#pragma unroll
+        for (int y = 0; y < NV; ++y) {
+#pragma unroll
+            for (int h = P / 2; h > 0; h /= 2)
+#pragma unroll
+                for (int q = 0; q < h; ++q)
+#pragma unroll
+                    for (int e = 0; e < W; ++e) v[y][q][e] = v[y][q][e] + v[y][q + h][e];
+            float* out = y == 0 ? a.dgamma : a.dbeta;
+#pragma unroll
+            for (int e = 0; e < W; ++e)
+                if (c + e < D) out[c + e] = v[y][0][e];
+        }
+    }
+}
+
+template <int BLOCK, int NV>
+__device__ __forceinline__ void small_backward_reduce(const BwdArgs& a, int D, int tid)
+{
+    __shared__ int s_all;
+    const int P = (int)gridDim.x;
+    uint64_t e = 0;
+    if (tid < 64)
+        e = __hip_atomic_load(&a.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's partial rows (and the epoch) are in
+    __syncthreads();
+    if (tid < 64) {
+        if (tid == 0)
+            __hip_atomic_store(&a.sync[1 + blockIdx.x], e + 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the flag is stored
+        const bool set = tid >= P || __hip_atomic_load(&a.sync[1 + tid], __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT) == e + 1;
+        const uint64_t unset = __ballot(!set);
+        if (tid == 0) {
+            s_all = unset == 0;
+            if (unset == 0)
+                __hip_atomic_store(&a.sync[0], e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+    if (!s_all) return;
+    switch (P) {
+    case 1: small_rows_sum<1, 4, BLOCK, NV>(a, D, tid); break;
+    case 2: small_rows_sum<2, 4, BLOCK, NV>(a, D, tid); break;
+    case 4: small_rows_sum<4, 4, BLOCK, NV>(a, D, tid); break;
+    case 8: small_rows_sum<8, 4, BLOCK, NV>(a, D, tid); break;
+    case 16: small_rows_sum<16, 4, BLOCK, NV>(a, D, tid); break;
+    case 32: small_rows_sum<32, 2, BLOCK, NV>(a, D, tid); break;
+    case 64: small_rows_sum<64, 1, BLOCK, NV>(a, D, tid); break;
+    }
+}
+
 // Storage types: ST for X and R (and MOD's scale), CT for the cotangents dY
 // and dH, OT for dX.
 //
@@ -1021,9 +1143,16 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
         }
     }
 
+    // One-launch backward of a small problem (RMS, LN, ADD with a.sync set;
+    // not in 1024-lane variants, whose 128 VGPRs the reduce would exceed).
+    constexpr bool kOneLaunch = BLOCK < 1024 && NV > 0 && NV <= 2 && NSC == 0 && KIND != MOD;
+    const bool one_launch = kOneLaunch && a.sync != nullptr;
+
     // Fold the row groups of this workgroup in group order, then write the
-    // workgroup's partial rows.
-    if constexpr (NV > 0) {
+    // workgroup's partial rows: plain (write-back cached, 16-byte) stores, or
+    // on the one-launch path device-coherent ones, written through to the
+    // level every XCD reads.
+    auto write_partials = [&](auto put) {
         float* pv[3] = {a.part_g + (int64_t)blockIdx.x * a.Dp,
                         NV > 1 ? a.part_b + (int64_t)blockIdx.x * a.Dp : nullptr,
                         NV > 2 ? a.part_h + (int64_t)blockIdx.x * a.Dp : nullptr};
@@ -1033,12 +1162,21 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                 if (!cval[k]) continue;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    pv[0][coff[k] + e] = accg[k][e];
-                    if constexpr (NV > 1) pv[1][coff[k] + e] = accb[k][e];
-                    if constexpr (NV > 2) pv[2][coff[k] + e] = acch[k][e];
+                    put(&pv[0][coff[k] + e], accg[k][e]);
+                    if constexpr (NV > 1) put(&pv[1][coff[k] + e], accb[k][e]);
+                    if constexpr (NV > 2) put(&pv[2][coff[k] + e], acch[k][e]);
                 }
             }
         } else {
+            for (int j = tid; j < D; j += BLOCK) {
+                put(&pv[0][j], fold[j]);
+                if constexpr (NV > 1) put(&pv[1][j], fold[D + j]);
+                if constexpr (NV > 2) put(&pv[2][j], fold[2 * D + j]);
+            }
+        }
+    };
+    if constexpr (NV > 0) {
+        if constexpr (RPB > 1) {
             for (int gg = 0; gg < RPB; ++gg) {
                 if (g == gg) {
 #pragma unroll
@@ -1057,12 +1195,16 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
                 }
                 __syncthreads();
             }
-            for (int j = tid; j < D; j += BLOCK) {
-                pv[0][j] = fold[j];
-                if constexpr (NV > 1) pv[1][j] = fold[D + j];
-                if constexpr (NV > 2) pv[2][j] = fold[2 * D + j];
-            }
         }
+        if (one_launch)
+            write_partials([](float* q, float v) {
+                __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            });
+        else
+            write_partials([](float* q, float v) { *q = v; });
+    }
+    if constexpr (kOneLaunch) {
+        if (one_launch) small_backward_reduce<BLOCK, NV>(a, D, tid);
     }
     if constexpr (NSC > 0) {
 #pragma unroll

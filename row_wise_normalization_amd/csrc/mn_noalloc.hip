@@ -1,8 +1,9 @@
 // mn_noalloc.hip -- the RMSNorm backward for callers that cannot allocate
 // device memory (code under stream capture, tight serving loops, harnesses
-// that forbid hipMalloc): the same two kernels as mn_rmsnorm_backward, with
-// the per-workgroup dgamma partial rows in a fixed device array of this
-// library instead of a caller workspace.
+// that forbid hipMalloc): the same kernels as mn_rmsnorm_backward, with the
+// per-workgroup dgamma partial rows (and the hand-off words of the one-launch
+// backward of small problems) in a fixed device array of this library
+// instead of a caller workspace.
 //
 // The array lives in each device's copy of the code object until the
 // process ends. Host code never passes the array's own name to a kernel: in

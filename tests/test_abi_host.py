@@ -173,9 +173,16 @@ def test_workspace_bytes():
             b = mn.workspace_bytes(kind, N, D)
             assert b > 0 and b % 16 == 0
             # at most 256 partial rows of round_up(D, 4) floats (two arrays for
-            # LayerNorm), 512 for RMSNorm rows of up to 3072 columns
-            P = 512 if kind == mn.MN_RMSNORM and D <= 3072 else 256
-            assert b == min(N, P) * ((D + 3) // 4 * 4) * 4 * (2 if kind == mn.MN_LAYERNORM else 1)
+            # LayerNorm), 512 for RMSNorm rows of up to 3072 columns; small
+            # problems (N * Dp <= 131072) one partial row per eight rows (at
+            # most 64) and the one-launch hand-off words (an epoch and 64
+            # flags, 528 bytes)
+            Dp = (D + 3) // 4 * 4
+            small = N * Dp <= 131072
+            P = min(1 << ((N + 7) // 8 - 1).bit_length(), 64) if small else min(
+                N, 512 if kind == mn.MN_RMSNORM and D <= 3072 else 256)
+            planes = 2 if kind == mn.MN_LAYERNORM else 1
+            assert b == P * Dp * 4 * planes + (528 if small else 0)
     assert mn.workspace_bytes(6, 16, 64) == 0
     # the other norms: Dynamic Tanh keeps two partial arrays plus scalars,
     # PolyNorm only scalars, the Modulated RMSNorm sizes by its sample count
@@ -190,6 +197,27 @@ def test_workspace_bytes():
     assert mn.mod_rmsnorm_workspace_bytes(3, 16, 64) == 0      # 3 does not divide 16
     assert mn.mod_rmsnorm_workspace_bytes(0, 16, 64) == 0
     assert mn.mod_rmsnorm_workspace_bytes(4097, 4097, 64) == 0
+
+
+def test_backward_launches():
+    """One launch for small RMSNorm, LayerNorm and fused-add problems (at most
+    131,072 partial values, rows of at most 5120 columns), else the row kernel
+    and the column reduce."""
+    pair = (mn.MN_RMSNORM, mn.MN_LAYERNORM, mn.MN_ADD_RMSNORM)
+    for kind in pair:
+        assert mn.backward_launches(kind, 17, 257) == 1
+        assert mn.backward_launches(kind, 128, 1024) == 1       # exactly 131,072
+        assert mn.backward_launches(kind, 129, 1024) == 2
+        assert mn.backward_launches(kind, 25, 5120) == 1
+        assert mn.backward_launches(kind, 16, 5121) == 2        # wider than 5120
+        assert mn.backward_launches(kind, 1, 8192) == 2
+        assert mn.backward_launches(kind, 16384, 4096) == 2
+        assert mn.backward_launches(kind, 0, 64) == 0
+        assert mn.backward_launches(kind, 4, 8193) == 0
+    for kind in (mn.MN_DYT, mn.MN_POLYNORM, mn.MN_MOD_RMSNORM):
+        assert mn.backward_launches(kind, 17, 257) == 2
+    assert mn.backward_launches(6, 16, 64) == 0
+    assert mn.backward_launches(-1, 16, 64) == 0
 
 
 def test_other_norms_validation():

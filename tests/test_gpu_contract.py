@@ -132,8 +132,12 @@ def test_no_writes_outside_outputs():
         assert (h[:guard] == 7).all() and (h[-guard:] == 7).all(), f"write outside {name}"
 
 
-def test_two_stage_backward_equals_full_call():
-    N, D = 1000, 2048
+# the first shape takes the two-launch backward; the small ones take the
+# one-launch backward (the row launch adds its partial rows itself), the last
+# a 1024-lane variant, which keeps two launches with few partial rows
+@pytest.mark.parametrize("N,D", [(1000, 2048), (17, 257), (128, 1024), (500, 256), (3, 5),
+                                 (16, 8192)])
+def test_two_stage_backward_equals_full_call(N, D):
     for kind in ("rms", "ln", "add"):
         d = workloads.random_case(kind, N, D, seed=13)
         full = run_gpu(kind, d, 1e-5)
@@ -184,3 +188,93 @@ def test_error_returns_on_device():
         mn.mn_rmsnorm_forward(X, g, Y, rstd, float("nan"))
     torch.cuda.synchronize()
     assert (Y == 3.0).all()
+
+
+def _small_backward(kind, d, ws):
+    """The full backward of one case through workspace `ws` (forward first,
+    for the statistics); returns (dX, dgamma, dbeta) on the host."""
+    N, D = d["X"].shape
+    X, g, dY = dev(d["X"]), dev(d["gamma"]), dev(d["dY"])
+    dX = torch.empty_like(X)
+    dg = torch.empty(D, dtype=torch.float32, device="cuda")
+    db = torch.empty(D, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(N, dtype=torch.float32, device="cuda")
+    if kind == "rms":
+        mn.mn_rmsnorm_forward(X, g, torch.empty_like(X), rstd, 1e-5)
+        mn.mn_rmsnorm_backward(X, g, rstd, dY, dX, dg, ws)
+    elif kind == "ln":
+        mean = torch.empty(N, dtype=torch.float32, device="cuda")
+        mn.mn_layernorm_forward(X, g, dev(d["beta"]), torch.empty_like(X), mean, rstd, 1e-5)
+        mn.mn_layernorm_backward(X, g, mean, rstd, dY, dX, dg, db, ws)
+    else:
+        R, dH = dev(d["R"]), dev(d["dH"])
+        mn.mn_add_rmsnorm_forward(X, R, g, torch.empty_like(X), torch.empty_like(X), rstd, 1e-5)
+        mn.mn_add_rmsnorm_backward(X, R, g, rstd, dY, dH, dX, dg, ws)
+    torch.cuda.synchronize()
+    return dX.cpu().numpy(), dg.cpu().numpy(), db.cpu().numpy()
+
+
+@pytest.mark.parametrize("kind,N,D", [("rms", 17, 257), ("ln", 128, 1024), ("add", 500, 256),
+                                      ("ln", 3, 5), ("rms", 64, 2048)])
+def test_one_launch_backward_through_a_reused_workspace(kind, N, D):
+    """The one-launch backward hands the partial rows over through flags and
+    an epoch kept in the workspace: a workspace of random bytes, then calls
+    alternating two inputs through it, each equal bitwise to its input's
+    result through a fresh zero-filled workspace."""
+    code = {"rms": mn.MN_RMSNORM, "ln": mn.MN_LAYERNORM, "add": mn.MN_ADD_RMSNORM}[kind]
+    cases = [workloads.random_case(kind, N, D, seed=s) for s in (31, 32)]
+    fresh = []
+    for d in cases:
+        ws = mn.new_workspace(code, N, D)
+        ws.zero_()
+        fresh.append(_small_backward(kind, d, ws))
+    ws = mn.new_workspace(code, N, D)
+    ws.view(torch.int32).random_()
+    for i in range(6):
+        got = _small_backward(kind, cases[i % 2], ws)
+        for a, b, name in zip(fresh[i % 2], got, ("dX", "dgamma", "dbeta")):
+            if name != "dbeta" or kind == "ln":
+                _same(a, b, f"{kind} {N}x{D} call {i} {name}")
+
+
+def test_one_launch_backward_replayed_from_a_graph():
+    """A captured one-launch backward replayed with new inputs copied in
+    between replays: every replay equals the eager result of its input."""
+    N, D = 128, 1024
+    cases = [workloads.random_case("ln", N, D, seed=s) for s in (41, 42, 43)]
+    eager = []
+    for d in cases:
+        ws = mn.new_workspace(mn.MN_LAYERNORM, N, D)
+        eager.append(_small_backward("ln", d, ws))
+    X, g, dY = dev(cases[0]["X"]), dev(cases[0]["gamma"]), dev(cases[0]["dY"])
+    mean = torch.empty(N, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(N, dtype=torch.float32, device="cuda")
+    Y = torch.empty_like(X)
+    dX = torch.empty_like(X)
+    dg = torch.empty(D, dtype=torch.float32, device="cuda")
+    db = torch.empty(D, dtype=torch.float32, device="cuda")
+    ws = mn.new_workspace(mn.MN_LAYERNORM, N, D)
+    beta = dev(cases[0]["beta"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mn.mn_layernorm_forward(X, g, beta, Y, mean, rstd, 1e-5)
+        mn.mn_layernorm_backward(X, g, mean, rstd, dY, dX, dg, db, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mn.mn_layernorm_forward(X, g, beta, Y, mean, rstd, 1e-5)
+        mn.mn_layernorm_backward(X, g, mean, rstd, dY, dX, dg, db, ws)
+    for i in range(6):
+        d = cases[i % 3]
+        X.copy_(dev(d["X"]))
+        g.copy_(dev(d["gamma"]))
+        beta.copy_(dev(d["beta"]))
+        dY.copy_(dev(d["dY"]))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b, name in zip(eager[i % 3], (dX.cpu().numpy(), dg.cpu().numpy(), db.cpu().numpy()),
+                              ("dX", "dgamma", "dbeta")):
+            _same(a, b, f"graph replay {i} {name}")
