@@ -388,9 +388,14 @@ bool gemv_shape_ok(int64_t M, int64_t N, int64_t K)
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (!gemv_shape_ok(M, N, K)) return 0;
-    const mn::GemvPlan p = mn::plan_gemv(M, N, K, N % 8 == 0);
-    const mn::GemvPlan q = mn::plan_gemv(M, N, K, false);
-    const int64_t S = p.S > q.S ? p.S : q.S;  // either load path
+    // the largest slice count of any load path (16-byte, with or without the
+    // matrix-core tiles, or element-wise)
+    int64_t S = mn::plan_gemv(M, N, K, false, false, false).S;
+    for (int f16 = 0; f16 < 2; ++f16)
+        for (int ln = 0; ln < 2; ++ln) {
+            const int64_t s = mn::plan_gemv(M, N, K, N % 8 == 0, f16, ln).S;
+            S = s > S ? s : S;
+        }
     // statistics, the tiles' arrival counters, then S slices of M + 2 partial
     // rows (LayerNorm's two extra)
     return sizeof(float) * ((size_t)mn::kGemvStatFloats + (size_t)mn::kGemvCountWords +
@@ -415,7 +420,7 @@ mn_status norm_gemv(bool ln, const void* X, const void* gamma, const void* beta,
     if (!alias_free(in, out)) return MN_ERR_ALIAS;
 
     const bool vec_ok = N % 8 == 0 && aligned16(W);
-    const mn::GemvPlan plan = mn::plan_gemv(M, N, K, vec_ok);
+    const mn::GemvPlan plan = mn::plan_gemv(M, N, K, vec_ok, st == MN_F16, ln);
     mn::GemvArgs a;
     a.X = X;
     a.gamma = gamma;

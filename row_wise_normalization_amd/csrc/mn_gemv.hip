@@ -3,9 +3,12 @@
 // the normalised rows applied in registers, never written to memory).
 //
 // The product is bound by reading W once (K*N elements; M <= 8 rows of X are
-// tiny), so it runs on the vector ALUs: per W element M fused multiply-adds,
-// far below the ALU rate at HBM speed, and an MFMA tile would need W in its
-// operand layout (a transposing LDS pass) for no gain at M <= 8.
+// tiny). Per W element it takes M (+2 for LayerNorm) multiply-adds: for
+// RMSNorm in binary16 on the matrix cores (16x16x16 products, W's operand
+// layout formed by byte permutes in registers, no LDS pass; see the
+// matrix-core tiles below), otherwise on the vector ALUs (LayerNorm,
+// bfloat16, unaligned operands, and the wide tiles of one or two rows
+// against a wide W).
 //
 // The normalisation is factored out of the product. With xc = x - c (c = 0
 // for RMSNorm; for LayerNorm c is the row's first element, a shift that
@@ -206,6 +209,67 @@ __device__ __forceinline__ void gemv_reset(const GemvArgs& a, int cb)
     __hip_atomic_store(&a.cnt[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Blocks 0..M-1: the statistics of row blockIdx.x, then the count on every
+// tile, finishing the tiles whose count this block completes. `done` is
+// kGemvBlock ints of shared scratch.
+template <int ST, bool LNF, int TC>
+__device__ void gemv_stats_block(const GemvArgs& a, int* done, int& s_count)
+{
+    const int tid = threadIdx.x;
+    const unsigned arrivals = (unsigned)(a.S + a.M);
+    gemv_row_stats<ST, LNF>(a);
+    stores_done();
+    __syncthreads();
+    for (int base = 0; base < a.NB; base += kGemvBlock) {
+        if (tid == 0) s_count = 0;
+        __syncthreads();
+        const int cb = base + tid;
+        if (cb < a.NB && atomicAdd(&a.cnt[cb], 1u) == arrivals - 1)
+            done[atomicAdd(&s_count, 1)] = cb;
+        __syncthreads();
+        const int nd = s_count;
+        for (int j = 0; j < nd; ++j) {
+            gemv_finish<ST, LNF, TC>(a, done[j]);
+            if (tid == 0) gemv_reset(a, done[j]);
+        }
+        __syncthreads();
+    }
+}
+
+// End of a tile block: the wave sums are in lds[(wave * R + p) * TC + c]
+// (p < R: the product rows, then g and b for LayerNorm); the waves are added
+// in order into the slice's partial rows, the slice is counted in once its
+// stores have completed, and the block that completes the tile's count adds
+// the tile's partials.
+template <int ST, int MM, bool LNF, int TC>
+__device__ void gemv_tile_end(const GemvArgs& a, const float* lds, int cb, int ks, int& s_count)
+{
+    constexpr int R = MM + (LNF ? 2 : 0);
+    const int M = a.M, N = a.N, tid = threadIdx.x;
+    const unsigned arrivals = (unsigned)(a.S + M);
+    const int RE = M + (LNF ? 2 : 0);   // partial rows written per slice
+    for (int i = tid; i < RE * TC; i += kGemvBlock) {
+        const int pr = i / TC;
+        const int c = i % TC;
+        const int n = cb * TC + c;
+        if (n < N) {
+            const int p = pr < M ? pr : MM + (pr - M);
+            float s = lds[p * TC + c];
+#pragma unroll
+            for (int ww = 1; ww < kGemvWaves; ++ww) s += lds[(ww * R + p) * TC + c];
+            put_dev(&a.part[((int64_t)ks * RE + pr) * N + n], s);
+        }
+    }
+    stores_done();
+    __syncthreads();
+    if (tid == 0) s_count = atomicAdd(&a.cnt[cb], 1u) == arrivals - 1;
+    __syncthreads();
+    if (s_count) {
+        gemv_finish<ST, LNF, TC>(a, cb);
+        if (tid == 0) gemv_reset(a, cb);
+    }
+}
+
 template <int ST, int VEC, int MM, bool LNF, int RPW, int U>
 __global__ void __launch_bounds__(kGemvBlock) gemv_kernel(const GemvArgs a)
 {
@@ -225,28 +289,8 @@ __global__ void __launch_bounds__(kGemvBlock) gemv_kernel(const GemvArgs a)
     __shared__ int s_count;
     const int M = a.M;
     const int tid = threadIdx.x;
-    const unsigned arrivals = (unsigned)(a.S + M);
     if ((int)blockIdx.x < M) {
-        gemv_row_stats<ST, LNF>(a);
-        // count the statistics in on every tile, and finish the tiles whose
-        // count this block completes
-        stores_done();
-        __syncthreads();
-        int* const done = reinterpret_cast<int*>(lds);
-        for (int base = 0; base < a.NB; base += kGemvBlock) {
-            if (tid == 0) s_count = 0;
-            __syncthreads();
-            const int cb = base + tid;
-            if (cb < a.NB && atomicAdd(&a.cnt[cb], 1u) == arrivals - 1)
-                done[atomicAdd(&s_count, 1)] = cb;
-            __syncthreads();
-            const int nd = s_count;
-            for (int j = 0; j < nd; ++j) {
-                gemv_finish<ST, LNF, TC>(a, done[j]);
-                if (tid == 0) gemv_reset(a, done[j]);
-            }
-            __syncthreads();
-        }
+        gemv_stats_block<ST, LNF, TC>(a, reinterpret_cast<int*>(lds), s_count);
         return;
     }
     const int t = (int)blockIdx.x - M;
@@ -366,29 +410,213 @@ __global__ void __launch_bounds__(kGemvBlock) gemv_kernel(const GemvArgs a)
             for (int e = 0; e < VEC; ++e) lds[(wave * R + p) * TC + cl * VEC + e] = acc[p][e];
     }
     __syncthreads();
-    const int RE = M + (LNF ? 2 : 0);   // partial rows written per slice
-    for (int i = tid; i < RE * TC; i += kGemvBlock) {
-        const int pr = i / TC;
-        const int c = i % TC;
-        const int n = cb * TC + c;
-        if (n < N) {
-            const int p = pr < M ? pr : MM + (pr - M);
-            float s = lds[p * TC + c];
+    gemv_tile_end<ST, MM, LNF, TC>(a, lds, cb, ks, s_count);
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core tiles (binary16 X and W, the 16-byte path, at most eight
+// product rows). The product of a tile is an MFMA product
+//   D[m][n] += sum_k A[m][k] B[k][n]   (v_mfma_f32_16x16x16_f16, fp32 sums)
+// with B = 16 rows x 16 columns of W and A = the product rows of X over the
+// same 16 rows. W is read exactly as the vector-ALU kernel reads it (16-byte
+// loads of 8 columns) and its elements are exact in binary16; the product
+// rows are fp32 values, so each is split into two binary16 rows, hi = f16(v)
+// and lo = f16(v - hi), after scaling the row of the tile by a power of two
+// that puts its largest magnitude in [2^14, 2^15) (no overflow; the split
+// keeps about 22 bits, the products are exact and the sums fp32). A holds
+// hi and lo of product row r as its rows 2r and 2r + 1, so 2 R <= 16.
+//
+// Lane layout of the 16x16x16 product (lane l): A[l % 16][4 (l / 16) + i],
+// B[4 (l / 16) + i][l % 16] and D[4 (l / 16) + i][l % 16], i = 0..3. A lane
+// loads rows 4 (l / 16) .. + 3 of a 16-row step at columns 8 (l % 16) .. + 7
+// and forms from them the B operands of eight products, one per column j of
+// its eight (two byte permutes each): product j covers the tile columns
+// 8 c + j, c = 0..15. Its D rows 4 (l / 16) + i are then hi and lo of the
+// product rows 2 (l / 16) and 2 (l / 16) + 1, added and scaled back.
+// ---------------------------------------------------------------------------
+constexpr int kMfmaTC = 128;                 // tile columns: 16 lanes x 8
+constexpr int kMfmaKP = kGemvMaxKB + 8;      // LDS row pitch of A, in halves
+constexpr int kBufNt = 2;                    // buffer cache policy: nt
+constexpr int kBufWord3 = 0x00020000;        // raw buffer, 32-bit data format
+constexpr uint32_t kBufOut = 0x80000000u;    // offset past every tile: reads 0
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float mf4 __attribute__((ext_vector_type(4)));
+typedef uint32_t wq __attribute__((ext_vector_type(4)));
+
+template <int MM, bool LNF, int U>
+__global__ void __launch_bounds__(kGemvBlock) gemv_mfma_kernel(const GemvArgs a)
+{
+    constexpr int R = MM + (LNF ? 2 : 0);
+    static_assert(2 * R <= 16, "hi and lo rows of every product row fit the A operand");
+    constexpr int NW = kGemvWaves;
+    constexpr int TC = kMfmaTC;
+    constexpr int KP = kMfmaKP;
+    constexpr int AB = 16 * KP * 2;          // A rows in LDS, bytes
+    constexpr int SB = NW * R * TC * 4;      // wave sums, bytes
+    __shared__ float4 lds4[(AB > SB ? AB : SB) / 16];
+    __shared__ float s_max[NW][R];
+    __shared__ int s_sh[R];
+    __shared__ int s_count;
+    _Float16* const la = reinterpret_cast<_Float16*>(lds4);
+    float* const lds = reinterpret_cast<float*>(lds4);
+
+    const int M = a.M;
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x < M) {
+        gemv_stats_block<ST_F16, LNF, TC>(a, reinterpret_cast<int*>(lds), s_count);
+        return;
+    }
+    const int t = (int)blockIdx.x - M;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cg = lane & 15;                // column group: tile columns 8 cg .. + 7
+    const int kg = lane >> 4;                // rows 4 kg .. + 3 of each 16-row step
+    const int N = a.N, K = a.K;
+    const int cb = t % a.NB;
+    const int ks = t / a.NB;
+    const int k0 = ks * a.KB;
+    const int kn = min(a.KB, K - k0);
+    // the tile's W through a buffer resource: rows at or past kn read as 0;
+    // columns past N (ragged last tile) repeat the last 8 and are not stored
+    const _Float16* wt = static_cast<const _Float16*>(a.W) + (int64_t)k0 * N + (int64_t)cb * TC;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<_Float16*>(wt), 0, (int)((int64_t)kn * N * 2), kBufWord3);
+    const int colc = min(cb * TC + 8 * cg, N - 8) - cb * TC;
+    auto woff = [&](int rr) -> uint32_t {
+        return rr < kn ? (uint32_t)(((int64_t)rr * N + colc) * 2) : kBufOut;
+    };
+    const int nb = (kn - 16 * wave + 16 * NW - 1) / (16 * NW);   // 16-row steps of the wave
+    auto load_step = [&](wq (&w)[4], int s) {
+        const int rb = 16 * (wave + NW * s) + 4 * kg;
 #pragma unroll
-            for (int ww = 1; ww < NW; ++ww) s += lds[(ww * R + p) * TC + c];
-            put_dev(&a.part[((int64_t)ks * RE + pr) * N + n], s);
+        for (int r = 0; r < 4; ++r)
+            w[r] = __builtin_bit_cast(wq, __builtin_amdgcn_raw_buffer_load_b128(wr, woff(rb + r), 0, kBufNt));
+    };
+
+    // first steps of W in flight while the A rows are formed
+    wq wa[U][4], wb[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_step(wa[u], u);
+
+    // product rows of the tile (rows past kn are 0), their scales, and the
+    // hi / lo rows of A in LDS: la[m * KP + k]
+    int sh[R];
+    {
+        constexpr int IT = kGemvMaxKB / kGemvBlock;
+        const _Float16* X = static_cast<const _Float16*>(a.X);
+        float v[IT][R];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int k = tid + it * kGemvBlock;
+            const int kk = k0 + min(k, kn - 1);
+            const float g = param_any(a.gamma, a.pdt, kk);
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                const int64_t row = (int64_t)min(m, M - 1) * K;
+                const float c = LNF ? (float)X[row] : 0.0f;
+                v[it][m] = ((float)X[row + kk] - c) * g;
+            }
+            if (LNF) {
+                v[it][MM] = g;
+                v[it][MM + 1] = param_any(a.beta, a.pdt, kk);
+            }
+            if (k >= kn)
+#pragma unroll
+                for (int r = 0; r < R; ++r) v[it][r] = 0.0f;
+        }
+        // largest magnitude of each row over the tile
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int it = 0; it < IT; ++it) mx = fmaxf(mx, fabsf(v[it][r]));
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            if (lane == 0) s_max[wave][r] = mx;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float mx = s_max[0][r];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_max[w][r]);
+            // finite and nonzero: 2^sh puts the largest in [2^14, 2^15)
+            const bool scale = mx > 0.0f && mx <= 3.40282347e38f;
+            int ex = 0;
+            if (scale) frexpf(mx, &ex);
+            sh[r] = scale ? 15 - ex : 0;
+            if (tid == r) s_sh[r] = sh[r];
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int k = tid + it * kGemvBlock;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float vs = ldexpf(v[it][r], sh[r]);
+                const _Float16 hi = (_Float16)vs;
+                const float hf = (float)hi;
+                // a non-finite value keeps its hi part only (no inf - inf)
+                const _Float16 lo = (hf - hf == 0.0f) ? (_Float16)(vs - hf) : (_Float16)0.0f;
+                la[(2 * r) * KP + k] = hi;
+                la[(2 * r + 1) * KP + k] = lo;
+            }
+#pragma unroll
+            for (int m = 2 * R; m < 16; ++m) la[m * KP + k] = (_Float16)0.0f;
         }
     }
-    // count the slice in once its stores have completed; the block that
-    // completes the tile's count adds the tile's partials
-    stores_done();
     __syncthreads();
-    if (tid == 0) s_count = atomicAdd(&a.cnt[cb], 1u) == arrivals - 1;
-    __syncthreads();
-    if (s_count) {
-        gemv_finish<ST, LNF, TC>(a, cb);
-        if (tid == 0) gemv_reset(a, cb);
+
+    mf4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = mf4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto mma_step = [&](const wq (&w)[4], int s) {
+        const int kb = 16 * (wave + NW * s) + 4 * kg;
+        const h4 af = *reinterpret_cast<const h4*>(&la[cg * KP + kb]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int d = j >> 1;
+            uint32_t b0, b1;
+            if (j & 1) {
+                b0 = (w[0][d] >> 16) | (w[1][d] & 0xFFFF0000u);
+                b1 = (w[2][d] >> 16) | (w[3][d] & 0xFFFF0000u);
+            } else {
+                b0 = (w[0][d] & 0xFFFFu) | (w[1][d] << 16);
+                b1 = (w[2][d] & 0xFFFFu) | (w[3][d] << 16);
+            }
+            typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+            const h4 bf = __builtin_bit_cast(h4, u2{b0, b1});
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(af, bf, acc[j], 0, 0, 0);
+        }
+    };
+    // two register sets in turn: the next steps are in flight while one is used
+    for (int s = 0; s < nb; s += 2 * U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_step(wb[u], s + U + u);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (s + u < nb) mma_step(wa[u], s + u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_step(wa[u], s + 2 * U + u);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (s + U + u < nb) mma_step(wb[u], s + U + u);
     }
+
+    // hi + lo of product rows 2 kg and 2 kg + 1, scaled back, as wave sums
+    __syncthreads();  // the A rows are reused below
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = 2 * kg + h;
+        if (r < R) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                lds[(wave * R + r) * TC + 8 * cg + j] =
+                    ldexpf(acc[j][2 * h] + acc[j][2 * h + 1], -s_sh[r]);
+        }
+    }
+    __syncthreads();
+    gemv_tile_end<ST_F16, MM, LNF, TC>(a, lds, cb, ks, s_count);
 }
 
 }  // namespace kern
@@ -426,6 +654,18 @@ hipError_t launch_gemv_mm(int mm, dim3 grid, hipStream_t s, const GemvArgs& a)
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_gemv_mfma(int mm, dim3 grid, hipStream_t s, const GemvArgs& a)
+{
+    const dim3 block(kern::kGemvBlock);
+    switch (mm) {
+    case 1: return launch_k(kern::gemv_mfma_kernel<1, false, 2>, grid, block, s, a);
+    case 2: return launch_k(kern::gemv_mfma_kernel<2, false, 2>, grid, block, s, a);
+    case 4: return launch_k(kern::gemv_mfma_kernel<4, false, 2>, grid, block, s, a);
+    case 8: return launch_k(kern::gemv_mfma_kernel<8, false, 2>, grid, block, s, a);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int ST>
 hipError_t launch_gemv_st(bool ln, bool vec, int rpw, int mm, dim3 grid, hipStream_t s,
                           const GemvArgs& a)
@@ -440,13 +680,18 @@ hipError_t launch_gemv_st(bool ln, bool vec, int rpw, int mm, dim3 grid, hipStre
 
 }  // namespace
 
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, bool vec_ok)
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, bool vec_ok, bool f16, bool ln)
 {
     GemvPlan p;
     p.vec = vec_ok;
     p.MM = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
     const bool wide = vec_ok && p.MM <= 2 &&
                       ((N + 511) / 512) * ((K + kGemvMaxKB - 1) / kGemvMaxKB) >= kGemvWideTileTarget;
+    // matrix-core tiles (128 columns): RMSNorm in binary16 with 16-byte
+    // loads, not the shapes the wide vector-ALU tiles serve (faster for one or
+    // two X rows). LayerNorm's six product rows at four X rows measured 1-5 %
+    // slower on them (its longer tile set-up), so it keeps the vector ALUs.
+    p.mfma = vec_ok && f16 && !ln && !wide && 2 * p.MM <= 16;
     p.rpw = vec_ok && !wide ? kGemvRpwVec : 1;
     const int64_t cols = (vec_ok ? 64 * 8 : 64) / p.rpw;
     const int64_t target = wide ? kGemvWideTileTarget : kGemvTileTarget;
@@ -465,6 +710,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, bool vec_ok)
 hipError_t launch_gemv(int st, bool ln, const GemvPlan& p, const GemvArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)p.grid);
+    if (p.mfma) return ln ? hipErrorInvalidValue : launch_gemv_mfma(p.MM, grid, s, a);
     hipError_t e = hipErrorInvalidValue;
     switch (st) {
     case ST_F16: e = launch_gemv_st<ST_F16>(ln, p.vec, p.rpw, p.MM, grid, s, a); break;

@@ -221,13 +221,14 @@ struct GemvArgs {
 
 struct GemvPlan {
     bool vec;                // 16-byte W loads (N % 8 == 0, aligned)
+    bool mfma;               // matrix-core tiles (binary16, 128 columns)
     int32_t MM;              // rows instantiated: 1, 2, 4 or 8 >= M
     int32_t rpw;             // W rows per wave load (tile columns 64 * VEC / rpw)
     int32_t NB, KB, S;
     int64_t grid;
 };
 
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, bool vec_ok);
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, bool vec_ok, bool f16, bool ln);
 hipError_t launch_gemv(int st, bool ln, const GemvPlan& p, const GemvArgs& a, hipStream_t s);
 
 }  // namespace mn

@@ -47,6 +47,27 @@ def test_unaligned(ln):
     compare(run(d, 1e-5, ln, offset=1), reference(d, 1e-5, ln), d, 1e-5, ln, "unaligned")
 
 
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("M", [3, 4, 8])
+@pytest.mark.parametrize("xs,gs", [(2.0 ** 12, 2.0 ** 4), (2.0 ** -12, 2.0 ** -6)],
+                         ids=["large", "small"])
+def test_product_row_range(M, ln, xs, gs):
+    """X and gamma scaled by powers of two (exact in binary16): products of
+    the shifted rows and gamma far above the binary16 range, or deep in its
+    subnormals. The normalised result is the same function of the stored
+    inputs; the matrix-core tiles (RMSNorm in binary16) rescale each product
+    row of a tile by a power of two before splitting it into two binary16
+    rows, and the vector-ALU tiles (LayerNorm) keep it in fp32."""
+    d = _case(M, 1024, 1040, 31 + M, ln)
+    d["X"] = (d["X"].astype(np.float64) * xs).astype(np.float16)
+    d["gamma"] = (d["gamma"].astype(np.float64) * gs).astype(np.float16)
+    if ln:
+        d["beta"] = (d["beta"].astype(np.float64) * gs).astype(np.float16)
+    assert np.isfinite(d["X"].astype(np.float64)).all()
+    w = compare(run(d, 1e-5, ln), reference(d, 1e-5, ln), d, 1e-5, ln, f"range {xs} {gs}")
+    say(f"[gemv] range M={M} xs={xs} gs={gs}: {w}")
+
+
 def test_large_mean_layernorm():
     """Rows with a mean 20 times their spread: the shifted sums and the
     centred statistics keep the result to the bar."""
