@@ -361,7 +361,8 @@ def pages_context(torch, mn):
 # Kernel-name fragments -> (label, which algorithmic byte count applies).
 PROFILE_KERNELS = (("gn_fwd_kernel", "forward"), ("gn_bwd_kernel", "backward_rows"),
                    ("fwd_kernel", "forward"), ("bwd_kernel", "backward_rows"),
-                   ("reduce_kernel", "reduce_partials"), ("gemv_kernel", "gemv"))
+                   ("reduce_kernel", "reduce_partials"), ("gemv_mfma_kernel", "gemv"),
+                   ("gemv_kernel", "gemv"))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
