@@ -101,78 +101,6 @@ __device__ __forceinline__ void gstore(void* base, uint32_t off, const typename 
     else *p = v;
 }
 
-// Buffer resources for the register path: a slice of one tensor as a raw
-// buffer (base address and size in bytes in four scalar registers, word 3
-// the gfx9 raw-buffer format), so that every chunk load and store takes the
-// slice base from scalar registers and one 32-bit offset register. With
-// plain global addresses the compiler kept a 64-bit address per chunk
-// across the reductions, which spilled the backward. An offset past the
-// size reads 0 and drops a store: a chunk that is not to be written is
-// stored at byte offset kNoStore instead of under a branch, so that every
-// memory instruction of the loop is issued unconditionally and the compiler
-// can count them (with a store under a divergent branch it waits for all of
-// them, the prefetch included). kNoStore is a byte offset: scaled by an
-// element size it would wrap to 0.
-constexpr int kRawBufferWord3 = 0x00020000;
-constexpr uint32_t kNoStore = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void* p, int64_t byte_off,
-                                                            uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(static_cast<const char*>(p) + byte_off), 0, (int)bytes, kRawBufferWord3);
-}
-
-// cache policy: 2 marks a non-temporal access
-// `off` is the lane's element offset, `soff` a wave-uniform one (scalar).
-template <int ST, int VEC, int NT>
-__device__ __forceinline__ typename Chunk<ST, VEC>::type bload(__amdgpu_buffer_rsrc_t r,
-                                                               uint32_t off, uint32_t soff)
-{
-    typedef typename Chunk<ST, VEC>::type C;
-    constexpr int aux = (NT & 2) ? 2 : 0;
-    constexpr uint32_t es = sizeof(typename Elem<ST>::type);
-    const uint32_t b = off * es, sb = soff * es;
-    if constexpr (sizeof(C) == 16) {
-        return __builtin_bit_cast(C, __builtin_amdgcn_raw_buffer_load_b128(r, b, sb, aux));
-    } else if constexpr (sizeof(C) == 4) {
-        return __builtin_bit_cast(C, __builtin_amdgcn_raw_buffer_load_b32(r, b, sb, aux));
-    } else {
-        static_assert(sizeof(C) == 2, "chunk of 2, 4 or 16 bytes");
-        return __builtin_bit_cast(C, __builtin_amdgcn_raw_buffer_load_b16(r, b, sb, aux));
-    }
-}
-
-// `ok` false: the store is dropped (byte offset kNoStore). The whole offset
-// goes in the offset register and the scalar offset is the constant 0: a
-// store of more than 8 bytes with a scalar-register offset needs a wait
-// state before the next write of its data registers, which this compiler
-// did not insert (the next chunk's fp32 temporaries then replaced the first
-// words of the stored data).
-template <int ST, int VEC, int NT>
-__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff,
-                                       bool ok, const typename Chunk<ST, VEC>::type& v)
-{
-    typedef typename Chunk<ST, VEC>::type C;
-    constexpr int aux = (NT & 1) ? 2 : 0;
-    constexpr uint32_t es = sizeof(typename Elem<ST>::type);
-    const uint32_t b = ok ? (off + soff) * es : kNoStore;
-    constexpr uint32_t sb = 0;
-    if constexpr (sizeof(C) == 32) {
-        // binary32 dX from a 16-bit chunk of 8: two 16-byte stores
-        typedef unsigned int u8v __attribute__((ext_vector_type(8)));
-        const u8v w = __builtin_bit_cast(u8v, v);
-        __builtin_amdgcn_raw_buffer_store_b128(u4{w[0], w[1], w[2], w[3]}, r, b, sb, aux);
-        __builtin_amdgcn_raw_buffer_store_b128(u4{w[4], w[5], w[6], w[7]}, r, b + 16, sb, aux);
-    } else if constexpr (sizeof(C) == 16) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, b, sb, aux);
-    } else if constexpr (sizeof(C) == 4) {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, b, sb, aux);
-    } else {
-        static_assert(sizeof(C) == 2, "chunk of 2, 4, 16 or 32 bytes");
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, b, sb, aux);
-    }
-}
 
 // A parameter element of PW bytes (binary32, or binary16 / bfloat16), loaded
 // raw in one instruction without a branch (a load in the arms of a branch

@@ -31,8 +31,10 @@ namespace mn {
 // faster than the 4096-column rows, where one chunk over 384 lanes was
 // slower), at 5120 one row per group (RMSNorm, 7 %) and 128 lanes x 5 chunks
 // (LayerNorm, 24 %), for the LayerNorm at 2048 and 8192 one row per group in
-// larger workgroups (3 % and 7 %); the 6144-column backward keeps the 8192
-// row (exact fits within 2.5 %). The forward likewise prefers fewer lanes
+// larger workgroups (3 % and 7 %), at 4096 one 512-lane row group with two
+// rows per step (1 % faster than two 256-lane groups of two chunks once its
+// dX stores went through a buffer resource); the 6144-column backward keeps
+// the 8192 row (exact fits within 2.5 %). The forward likewise prefers fewer lanes
 // per row with more chunks per lane away from 4096 columns (4 to 8 waves per
 // workgroup, one or two rows per group): 6-29 % faster than rows of 640 to
 // 1024 lanes at 2048, 5120, 6144 and 8192 columns, and 32 lanes x 4 chunks at
@@ -150,7 +152,7 @@ namespace mn {
     X(4, 64, 8, 2, 2, 256, 1, 3, 1024)       \
     X(5, 128, 8, 2, 1, 512, 1, 3, 2048)      \
     X(14, 128, 8, 3, 1, 256, 1, 3, 3072)     \
-    X(6, 256, 8, 2, 2, 512, 1, 3, 4096)      \
+    X(6, 512, 8, 1, 2, 512, 1, 3, 4096)      \
     X(12, 128, 8, 5, 1, 256, 1, 3, 5120)     \
     X(7, 512, 8, 2, 1, 1024, 1, 3, 8192)
 // The fused add keeps two rows per group at 4096 columns (its four streams
