@@ -329,48 +329,21 @@ mn_status reduce_partials(int kind, int64_t N, int64_t D, int64_t B, const void*
     const int64_t PD = P * Dp;
     const int nv = mn::bwd_vector_partials(kind);
     const float* w = static_cast<const float*>(ws);
-    hipStream_t s = as_stream(stream);
-    if (nv > 0) {
-        mn::ReduceArgs a;
-        a.part_g = w;
-        a.part_b = (kind == mn::LN || kind == mn::DYT) ? w + PD : nullptr;
-        a.dgamma = o.dgamma;
-        a.dbeta = a.part_b ? o.dbeta : nullptr;
-        a.P = P;
-        a.D = (int32_t)D;
-        a.Dp = Dp;
-        a.groups = 1;
-        mn_status r = device_status(mn::launch_reduce(a, s));
-        if (r != MN_OK) return r;
-    }
+    // every parameter gradient of the call in one launch, one plane each
+    mn::ReduceArgs a{};
+    auto add = [&](const float* part, float* out, int64_t rows, int32_t d, int32_t dp,
+                   int32_t groups) {
+        a.plane[a.planes++] = mn::ReducePlane{part, out, rows, d, dp, groups};
+    };
+    if (nv > 0) add(w, o.dgamma, P, (int32_t)D, Dp, 1);
+    if (kind == mn::LN || kind == mn::DYT) add(w + PD, o.dbeta, P, (int32_t)D, Dp, 1);
     if (kind == mn::MOD) {
         // dscale and dshift: the partial rows of each sample's workgroups
-        mn::ReduceArgs a;
-        a.part_g = w + PD;
-        a.part_b = w + 2 * PD;
-        a.dgamma = o.dbeta;
-        a.dbeta = o.dshift;
-        a.P = P / B;
-        a.D = (int32_t)D;
-        a.Dp = Dp;
-        a.groups = (int32_t)B;
-        mn_status r = device_status(mn::launch_reduce(a, s));
-        if (r != MN_OK) return r;
+        add(w + PD, o.dbeta, P / B, (int32_t)D, Dp, (int32_t)B);
+        add(w + 2 * PD, o.dshift, P / B, (int32_t)D, Dp, (int32_t)B);
     }
-    if (has_scalar_partials(kind)) {
-        mn::ReduceArgs a;
-        a.part_g = w + nv * PD;
-        a.part_b = nullptr;
-        a.dgamma = o.dscalar;
-        a.dbeta = nullptr;
-        a.P = P;
-        a.D = kind == mn::POLY ? 4 : 1;
-        a.Dp = 4;
-        a.groups = 1;
-        mn_status r = device_status(mn::launch_reduce(a, s));
-        if (r != MN_OK) return r;
-    }
-    return MN_OK;
+    if (has_scalar_partials(kind)) add(w + nv * PD, o.dscalar, P, kind == mn::POLY ? 4 : 1, 4, 1);
+    return device_status(mn::launch_reduce(a, as_stream(stream)));
 }
 
 const BwdTypes kF16{MN_F16, MN_F16, MN_F16, MN_F16};
@@ -571,14 +544,9 @@ mn_status groupnorm_backward(const void* X, const void* gamma, const float* mean
     if (e != hipSuccess) return device_status(e);
     // dgamma, dbeta: the N per-sample partial rows, added in fixed order
     mn::ReduceArgs r{};
-    r.part_g = a.part_g;
-    r.part_b = a.part_b;
-    r.dgamma = dgamma;
-    r.dbeta = dbeta;
-    r.P = N;
-    r.D = (int32_t)C;
-    r.Dp = a.Cp;
-    r.groups = 1;
+    r.plane[0] = mn::ReducePlane{a.part_g, dgamma, N, (int32_t)C, a.Cp, 1};
+    r.plane[1] = mn::ReducePlane{a.part_b, dbeta, N, (int32_t)C, a.Cp, 1};
+    r.planes = 2;
     return device_status(mn::launch_reduce(r, s));
 }
 

@@ -71,18 +71,22 @@ struct BwdArgs {
     float* dbeta;            // LN
 };
 
-// Column-reduce (stage 2) arguments: out_y[z * D + j] = sum over the P rows
-// p of part_y[(z * P + p) * Dp + j], for plane y = 0 (part_g -> dgamma) and
-// y = 1 (part_b -> dbeta, when part_b is not null) and group z < groups.
-struct ReduceArgs {
-    const float* part_g;
-    const float* part_b;     // null for a single plane
-    float* dgamma;
-    float* dbeta;
+// Column-reduce (stage 2) arguments. One launch reduces up to
+// kReduceMaxPlanes planes, each of its own shape: for plane y and group
+// z < groups, out[z * D + j] = sum over the P rows p of
+// part[(z * P + p) * Dp + j].
+struct ReducePlane {
+    const float* part;
+    float* out;
     int64_t P;               // partial rows per group
     int32_t D;
-    int32_t Dp;
+    int32_t Dp;              // partial row stride (a multiple of 4)
     int32_t groups;
+};
+constexpr int kReduceMaxPlanes = 3;
+struct ReduceArgs {
+    ReducePlane plane[kReduceMaxPlanes];
+    int32_t planes;
 };
 
 // Row-kernel variant: threads per row (T), elements per load (VEC, 8 or 1),

@@ -2,6 +2,8 @@
 // kernels: picks the launch-table row for a call (tables in mn_tables.hpp),
 // sizes its grid, and dispatches to the instance for its storage types
 // (instantiated in mn_inst_*.hip); also launches the stage-2 reduce.
+#include <algorithm>
+
 #include "mn_kernels.hpp"
 #include "mn_tables.hpp"
 
@@ -216,8 +218,15 @@ hipError_t launch_backward_rows(int kind, int st, int ct, int ot, const BwdPlan&
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s)
 {
-    const dim3 grid((unsigned)ceil_div(a.Dp, 4 * kReduceCQ), a.part_b ? 2u : 1u,
-                    (unsigned)(a.groups > 0 ? a.groups : 1));
+    if (a.planes < 1 || a.planes > kReduceMaxPlanes) return hipErrorInvalidValue;
+    int64_t gx = 1, gz = 1;
+    for (int y = 0; y < a.planes; ++y) {
+        const ReducePlane& pl = a.plane[y];
+        if (pl.Dp % 4 != 0 || pl.D > pl.Dp || pl.P < 1 || pl.groups < 1) return hipErrorInvalidValue;
+        gx = std::max(gx, ceil_div(pl.Dp, 4 * kReduceCQ));
+        gz = std::max(gz, (int64_t)pl.groups);
+    }
+    const dim3 grid((unsigned)gx, (unsigned)a.planes, (unsigned)gz);
     return launch(reduce_kernel<kReduceCQ>, grid, dim3(1024), 0, s, a);
 }
 

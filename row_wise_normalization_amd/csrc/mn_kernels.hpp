@@ -1329,7 +1329,8 @@ __global__ void __launch_bounds__(BLOCK) bwd_kernel(const BwdArgs a)
 
 // ---------------------------------------------------------------------------
 // Backward stage 2: out[j] = sum over the P partial rows of partial[p][j]
-// (per group z of P rows when there are several groups).
+// (per group z of P rows when there are several groups), for every plane of
+// the launch (blockIdx.y; a parameter gradient each, all in one launch).
 // A block covers 4*CQ columns (one float4 per thread); its SEG = 1024/CQ
 // thread rows each sum one contiguous segment of the partial rows in
 // ascending order, then the SEG segment sums are combined by a fixed
@@ -1343,20 +1344,26 @@ __global__ void __launch_bounds__(1024) reduce_kernel(const ReduceArgs a)
     constexpr int SEG = 1024 / CQ;
     static_assert((SEG & (SEG - 1)) == 0, "segment count is a power of two");
     __shared__ f4 seg_sum[SEG][CQ];
+    // the plane by constant indices (a dynamic index would copy the
+    // arguments to scratch memory)
+    const ReducePlane pl = blockIdx.y == 0 ? a.plane[0] : blockIdx.y == 1 ? a.plane[1] : a.plane[2];
+    // the grid covers the largest plane: blocks past this one's columns or
+    // groups have nothing to do (a whole block returns, before any barrier)
+    if ((int)blockIdx.z >= pl.groups || (int)blockIdx.x * 4 * CQ >= pl.Dp) return;
     // group z: rows z*P .. z*P + P - 1 of the plane, into out[z*D ...]
-    const float* part = ((blockIdx.y == 0) ? a.part_g : a.part_b) + (int64_t)blockIdx.z * a.P * a.Dp;
-    float* out = ((blockIdx.y == 0) ? a.dgamma : a.dbeta) + (int64_t)blockIdx.z * a.D;
+    const float* part = pl.part + (int64_t)blockIdx.z * pl.P * pl.Dp;
+    float* out = pl.out + (int64_t)blockIdx.z * pl.D;
     const int q = threadIdx.x % CQ;
     const int s = threadIdx.x / CQ;
     const int c0 = (blockIdx.x * CQ + q) * 4;
-    const int64_t per = (a.P + SEG - 1) / SEG;
-    const int64_t p0 = min(a.P, (int64_t)s * per);
-    const int64_t p1 = min(a.P, p0 + per);
+    const int64_t per = (pl.P + SEG - 1) / SEG;
+    const int64_t p0 = min(pl.P, (int64_t)s * per);
+    const int64_t p1 = min(pl.P, p0 + per);
     f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (c0 < a.Dp) {
+    if (c0 < pl.Dp) {
         const float* src = part + c0;
 #pragma unroll 8
-        for (int64_t p = p0; p < p1; ++p) acc += *reinterpret_cast<const f4*>(src + p * a.Dp);
+        for (int64_t p = p0; p < p1; ++p) acc += *reinterpret_cast<const f4*>(src + p * pl.Dp);
     }
     seg_sum[s][q] = acc;
     __syncthreads();
@@ -1365,11 +1372,11 @@ __global__ void __launch_bounds__(1024) reduce_kernel(const ReduceArgs a)
         if (s < st) seg_sum[s][q] = seg_sum[s][q] + seg_sum[s + st][q];
         __syncthreads();
     }
-    if (s == 0 && c0 < a.D) {
+    if (s == 0 && c0 < pl.D) {
         const f4 t = seg_sum[0][q];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (c0 + e < a.D) out[c0 + e] = t[e];
+            if (c0 + e < pl.D) out[c0 + e] = t[e];
     }
 }
 

@@ -21,8 +21,9 @@ namespace mn {
 //     row of dgamma and the tiles b, b+256, ...), prefetches its next tile
 //     and keeps two rows per row group in flight;
 //   * streamed outputs use non-temporal stores (NT bit 0) and streamed
-//     inputs non-temporal loads (NT bit 1), except the LayerNorm forward,
-//     which measured slower with non-temporal loads.
+//     inputs non-temporal loads (NT bit 1), except the LayerNorm forward
+//     away from 4096 columns, which measured slower with non-temporal loads
+//     (at 4096 they measured 1 % faster in a same-box A/B).
 // Rows 12 and 13 fit two common widths between the powers of two exactly
 // (5120 columns, and 6144 in the forward), faster there than the next
 // power-of-two row. Backward shapes away from 4096 columns come from a
@@ -64,7 +65,7 @@ namespace mn {
     X(3, 64, 8, 1, 2, 256, 0, 1, 512)        \
     X(4, 32, 8, 4, 1, 256, 0, 1, 1024)      \
     X(5, 64, 8, 4, 1, 256, 0, 1, 2048)      \
-    X(6, 256, 8, 2, 2, 256, 0, 1, 4096)      \
+    X(6, 256, 8, 2, 2, 256, 0, 3, 4096)      \
     X(12, 128, 8, 5, 1, 256, 0, 1, 5120)     \
     X(13, 256, 8, 3, 1, 256, 0, 1, 6144)     \
     X(7, 256, 8, 4, 1, 256, 0, 1, 8192)
@@ -104,7 +105,7 @@ namespace mn {
 // PolyNorm: the LayerNorm shapes (three sums per row), but with non-temporal
 // loads as well as stores, and 128 lanes x 4 chunks at 4096 columns: a width
 // sweep measured them 4-15 % faster than the LayerNorm rows at 1024-8192
-// columns (LayerNorm itself measured slower with non-temporal loads).
+// columns.
 #define MN_FWD_POLY(X)                       \
     X(0, 8, 8, 1, 4, 256, 0, 3, 64)          \
     X(1, 16, 8, 1, 2, 256, 0, 3, 128)        \
