@@ -45,11 +45,14 @@ KERNEL_SRCS = {
     "gn": ("mn_kernels.hpp", "mn_kernels.hip", "mn_tables.hpp", "mn_groupnorm.hpp",
            "mn_gn_instances.hpp", "mn_gn_plan.hip", "mn_gn_fwd_f16.hip", "mn_gn_bwd_f16.hip",
            "mn_gn_fwd_bf16.hip", "mn_gn_bwd_bf16.hip", "mn_gn_fwd_f32.hip", "mn_gn_bwd_f32.hip"),
+    "gnl": ("mn_kernels.hpp", "mn_kernels.hip", "mn_gnl.hip"),
     "gemv": ("mn_kernels.hpp", "mn_gemv.hip"),
 }
 
 
-def _src_group(kind: str) -> str:
+def _src_group(kind: str, layout: str = "ncl") -> str:
+    if kind == "gn" and layout == "nlc":
+        return "gnl"
     if kind in ("rms", "ln", "add"):
         return "pair"
     if kind in ("dyt", "poly", "mod"):
@@ -103,10 +106,10 @@ def back_set(k: int, S: int) -> int:
     return (k + S // 2) % S
 
 
-def kernel_hash(kind: str = "rms") -> str:
+def kernel_hash(kind: str = "rms", layout: str = "ncl") -> str:
     """Hash of the kernel sources behind `kind`'s launches."""
     h = hashlib.sha256()
-    for name in KERNEL_SRCS[_src_group(kind)]:
+    for name in KERNEL_SRCS[_src_group(kind, layout)]:
         with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -120,7 +123,8 @@ def measured_traffic(workload: str, kernel: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != kernel_hash(workloads.WORKLOADS[workload].kind):
+    w = workloads.WORKLOADS[workload]
+    if t.get("kernel_source_sha256_16") != kernel_hash(w.kind, w.layout):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -359,7 +363,10 @@ def pages_context(torch, mn):
 # --- rocprofv3 summaries ------------------------------------------------------
 
 # Kernel-name fragments -> (label, which algorithmic byte count applies).
-PROFILE_KERNELS = (("gn_fwd_kernel", "forward"), ("gn_bwd_kernel", "backward_rows"),
+PROFILE_KERNELS = (("gnl_sum_kernel<0", "forward_sums"), ("gnl_stats_kernel", "forward_stats"),
+                   ("gnl_apply_kernel<0", "forward_apply"), ("gnl_sum_kernel<1", "backward_sums"),
+                   ("gnl_merge_kernel", "backward_merge"), ("gnl_apply_kernel<1", "backward_apply"),
+                   ("gn_fwd_kernel", "forward"), ("gn_bwd_kernel", "backward_rows"),
                    ("fwd_kernel", "forward"), ("bwd_kernel", "backward_rows"),
                    ("reduce_kernel", "reduce_partials"), ("gemv_mfma_kernel", "gemv"),
                    ("gemv_kernel", "gemv"))
@@ -439,6 +446,12 @@ def summarize_profile(workload: str, prefix: str, out_dir: str = None):
     sf, sw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
     if gemv:
         alg = {"gemv": gemv_bytes(w.N, w.D, w.Nout, ln=w.kind == "ln_gemv")}
+    elif w.layout == "nlc":
+        # channels-last GroupNorm: each direction is three kernels; the
+        # algorithmic bytes belong to the direction, not to one of them
+        alg = {k: None for k in ("forward_sums", "forward_stats", "forward_apply",
+                                 "backward_sums", "backward_merge", "backward_apply",
+                                 "reduce_partials")}
     else:
         fb, bb = alg_bytes(w.kind, w.N, w.D, B=w.B, C=w.channels, G=w.groups)
         alg = {"forward": fb, "backward_rows": bb, "reduce_partials": None}
@@ -457,7 +470,7 @@ def summarize_profile(workload: str, prefix: str, out_dir: str = None):
     if os.path.exists(rpath):
         with open(rpath) as f:
             built = json.load(f)
-    out = {"workload": workload, "kernel_source_sha256_16": kernel_hash(w.kind),
+    out = {"workload": workload, "kernel_source_sha256_16": kernel_hash(w.kind, w.layout),
            "calibration": {"kernel": COPY_KERNEL, "bytes_read": copy_bytes,
                            "bytes_written": copy_bytes, "FETCH_SIZE_KiB_median": cf,
                            "WRITE_SIZE_KiB_median": cw, "fetch_scale": sf, "write_scale": sw},
@@ -623,10 +636,17 @@ def bench_other(args, w, torch, mn, act, param, dxt):
     pair; events bracket the forward and the backward call separately."""
     N, D, kind = w.N, w.D, w.kind
     C, G = w.channels, w.groups
-    shp = (N, C, D // C) if kind == "gn" else (N, D)
+    nlc = kind == "gn" and w.layout == "nlc"
+    shp = ((N, D // C, C) if nlc else (N, C, D // C)) if kind == "gn" else (N, D)
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
     print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
     d = workloads.generate(w, act=act, param=param)
+    # the device copy of a channels-last workload holds X and dY transposed;
+    # the oracle's CPU baseline keeps the channels-first arrays
+    dd = dict(d)
+    if nlc:
+        for k in ("X", "dY"):
+            dd[k] = np.ascontiguousarray(d[k].reshape(N, C, D // C).swapaxes(1, 2))
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -636,7 +656,7 @@ def bench_other(args, w, torch, mn, act, param, dxt):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    up = {k: upload(v) for k, v in d.items()}
+    up = {k: upload(v) for k, v in dd.items()}
     scal = torch.tensor(np.asarray(w.scalars, np.float32), device=dev)
     S = max(4, args.sets)
     sets = []
@@ -646,8 +666,9 @@ def bench_other(args, w, torch, mn, act, param, dxt):
              "Y": torch.empty(shp, dtype=tdt[act], device=dev),
              "dX": torch.empty(shp, dtype=tdt[dxt], device=dev)}
         if kind == "gn":
-            b["ws"] = torch.empty(mn.groupnorm_workspace_bytes(N, C, D // C, G) // 4, dtype=torch.float32,
-                                  device=dev)
+            nb = (mn.groupnorm_nlc_workspace_bytes(N, D // C, C, G) if nlc
+                  else mn.groupnorm_workspace_bytes(N, C, D // C, G))
+            b["ws"] = torch.empty(nb // 4, dtype=torch.float32, device=dev)
         else:
             kcode = {"dyt": mn.MN_DYT, "poly": mn.MN_POLYNORM, "mod": mn.MN_MOD_RMSNORM}[kind]
             b["ws"] = mn.new_workspace(kcode, N, D, dev, B=w.B)
@@ -671,7 +692,10 @@ def bench_other(args, w, torch, mn, act, param, dxt):
         sets.append(b)
 
     def fwd(b):
-        if kind == "gn":
+        if nlc:
+            mn.mn_groupnorm_nlc_forward_ex(b["X"], up["gamma"], up["beta"], b["Y"], b["mean"],
+                                           b["rstd"], G, w.eps, b["ws"], stream)
+        elif kind == "gn":
             mn.mn_groupnorm_forward_ex(b["X"], up["gamma"], up["beta"], b["Y"], b["mean"],
                                        b["rstd"], G, w.eps, stream)
         elif kind == "dyt":
@@ -683,7 +707,10 @@ def bench_other(args, w, torch, mn, act, param, dxt):
                                          b["rstd"], w.eps, stream)
 
     def bwd(b):
-        if kind == "gn":
+        if nlc:
+            mn.mn_groupnorm_nlc_backward_ex(b["X"], up["gamma"], b["mean"], b["rstd"], b["dY"],
+                                            b["dX"], b["dg"], b["db"], G, b["ws"], stream)
+        elif kind == "gn":
             mn.mn_groupnorm_backward_ex(b["X"], up["gamma"], b["mean"], b["rstd"], b["dY"],
                                         b["dX"], b["dg"], b["db"], G, b["ws"], stream)
         elif kind == "dyt":
@@ -730,6 +757,7 @@ def bench_other(args, w, torch, mn, act, param, dxt):
         "config": {"workload": w.name, "N": N, "D": D, "eps": w.eps, "io_dtype": act,
                    "param_dtype": param, "dx_dtype": dxt, "norm": NORM_NAMES[kind],
                    "samples": w.B, "scalars": list(w.scalars), "channels": C, "groups": G,
+                   "layout": w.layout if kind == "gn" else None,
                    "step": "forward + backward (row kernel and parameter reduction)",
                    "buffer_sets": S},
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),

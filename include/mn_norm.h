@@ -324,6 +324,38 @@ mn_status mn_groupnorm_backward_ex(const void* X, const void* gamma, const float
 size_t mn_groupnorm_workspace_bytes(int64_t N, int64_t C, int64_t L, int64_t G);
 
 /* ---------------------------------------------------------------------------
+ * GroupNorm over channels-last activations. [meTile] "Normalization" asks
+ * for GroupNorm's group and channel layouts; this is the same operation as
+ * mn_groupnorm_*_ex (same groups, statistics, affine and gradients) over
+ * X, Y, dY, dX [N][L][C]: the C channels of a position contiguous (the NHWC
+ * layout of image activations), position l of channel c of sample n at
+ * (n * L + l) * C + c. mean and rstd [N][G] fp32; gamma, beta [C] of `param`;
+ * dgamma, dbeta [C] fp32; dX in `act` or MN_F32 (`dxt`).
+ * Both directions take a workspace of mn_groupnorm_nlc_workspace_bytes(N, L,
+ * C, G) bytes, 16-byte aligned, no initial contents needed: per-chunk
+ * channel sums of the position chunks each workgroup streams, combined per
+ * (sample, group) in fixed order by a second kernel (the forward's in
+ * binary64, from sums shifted by each channel's value at position 0), then
+ * an apply pass; the backward's per-sample dgamma and dbeta partials are
+ * added in fixed order by the column-reduce kernel. X (and dY) are read
+ * twice. Calls with C a multiple of 8 (binary32: 4) and every tensor
+ * pointer 16-byte aligned take 16-byte chunks of channels; others go
+ * channel by channel. Accepted shapes: those of mn_groupnorm_*_ex, with C
+ * up to 16,776,960. Errors: as mn_groupnorm_*_ex, plus MN_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------- */
+mn_status mn_groupnorm_nlc_forward_ex(const void* X, const void* gamma, const void* beta, void* Y,
+                                      float* mean, float* rstd, int64_t N, int64_t L, int64_t C,
+                                      int64_t G, float eps, mn_dtype act, mn_dtype param,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+mn_status mn_groupnorm_nlc_backward_ex(const void* X, const void* gamma, const float* mean,
+                                       const float* rstd, const void* dY, void* dX,
+                                       float* dgamma, float* dbeta, int64_t N, int64_t L,
+                                       int64_t C, int64_t G, mn_dtype act, mn_dtype param,
+                                       mn_dtype dxt, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+size_t mn_groupnorm_nlc_workspace_bytes(int64_t N, int64_t L, int64_t C, int64_t G);
+
+/* ---------------------------------------------------------------------------
  * Fused normalization + GEMV for small inference batches. [tensorcore]
  * "Fused Norm + GEMV": Y = Norm(X, gamma[, beta]) @ W, the normalisation
  * applied in registers during the product instead of writing the normalised

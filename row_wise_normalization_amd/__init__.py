@@ -86,6 +86,10 @@ _SIGNATURES = {
     "mn_groupnorm_forward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _C, _C, _P],
     "mn_groupnorm_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _C, _C,
                                  _C, _P, _SZ, _P],
+    "mn_groupnorm_nlc_forward_ex": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _C, _C,
+                                    _P, _SZ, _P],
+    "mn_groupnorm_nlc_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _C,
+                                     _C, _C, _P, _SZ, _P],
     "mn_fused_rmsnorm_gemv": [_P, _P, _P, _P, _I64, _I64, _I64, _F, _P, _SZ, _P],
     "mn_fused_layernorm_gemv": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _F, _P, _SZ, _P],
     "mn_fused_rmsnorm_gemv_ex": [_P, _P, _P, _P, _I64, _I64, _I64, _F, _C, _C, _P, _SZ, _P],
@@ -116,6 +120,8 @@ def lib() -> ctypes.CDLL:
     L.mn_mod_rmsnorm_workspace_bytes.restype = _SZ
     L.mn_groupnorm_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
     L.mn_groupnorm_workspace_bytes.restype = _SZ
+    L.mn_groupnorm_nlc_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
+    L.mn_groupnorm_nlc_workspace_bytes.restype = _SZ
     L.mn_norm_gemv_workspace_bytes.argtypes = [_I64, _I64, _I64]
     L.mn_norm_gemv_workspace_bytes.restype = _SZ
     L.mn_noalloc_scratch_bytes.argtypes = []
@@ -493,6 +499,45 @@ def mn_groupnorm_backward_ex(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, groups
 
 def groupnorm_workspace_bytes(N: int, C: int, L: int, G: int) -> int:
     return int(lib().mn_groupnorm_workspace_bytes(int(N), int(C), int(L), int(G)))
+
+
+def _nlc(X: torch.Tensor) -> Tuple[int, int, int]:
+    if X.dim() != 3:
+        raise ValueError(f"channels-last GroupNorm X must be [N, L, C], got shape {tuple(X.shape)}")
+    return int(X.shape[0]), int(X.shape[1]), int(X.shape[2])
+
+
+def mn_groupnorm_nlc_forward_ex(X, gamma, beta, Y, mean, rstd, groups: int, eps: float, workspace,
+                                stream=None):
+    """GroupNorm of channels-last X [N, L, C] over `groups` groups of C / groups
+    channels."""
+    N, L, C = _nlc(X)
+    G = int(groups)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, L, C)); _check_t("gamma", gamma, gamma.dtype, (C,))
+    _check_t("beta", beta, gamma.dtype, (C,)); _check_t("Y", Y, X.dtype, (N, L, C))
+    _check_t("mean", mean, F32, (N, G)); _check_t("rstd", rstd, F32, (N, G))
+    _call("mn_groupnorm_nlc_forward_ex", _ptr(X), _ptr(gamma), _ptr(beta), _ptr(Y), _ptr(mean),
+          _ptr(rstd), N, L, C, G, float(eps), act, par, _ptr(workspace), _ws_bytes(workspace),
+          _stream(stream))
+
+
+def mn_groupnorm_nlc_backward_ex(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, groups: int,
+                                 workspace, stream=None):
+    N, L, C = _nlc(X)
+    G = int(groups)
+    act, par = _types(X, gamma)
+    _check_t("X", X, X.dtype, (N, L, C)); _check_t("gamma", gamma, gamma.dtype, (C,))
+    _check_t("mean", mean, F32, (N, G)); _check_t("rstd", rstd, F32, (N, G))
+    _check_t("dY", dY, X.dtype, (N, L, C)); _check_t("dX", dX, dX.dtype, (N, L, C))
+    _check_t("dgamma", dgamma, F32, (C,)); _check_t("dbeta", dbeta, F32, (C,))
+    _call("mn_groupnorm_nlc_backward_ex", _ptr(X), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dY),
+          _ptr(dX), _ptr(dgamma), _ptr(dbeta), N, L, C, G, act, par, _code("dX", dX),
+          _ptr(workspace), _ws_bytes(workspace), _stream(stream))
+
+
+def groupnorm_nlc_workspace_bytes(N: int, L: int, C: int, G: int) -> int:
+    return int(lib().mn_groupnorm_nlc_workspace_bytes(int(N), int(L), int(C), int(G)))
 
 
 def _ws_bytes(workspace: Optional[torch.Tensor]) -> int:

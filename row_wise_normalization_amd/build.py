@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["mn_inst_f16.hip", "mn_inst_bf16.hip", "mn_inst_f32.hip", "mn_inst_ext_f16.hip",
            "mn_inst_ext_bf16.hip", "mn_inst_ext_f32.hip", "mn_gn_fwd_f16.hip", "mn_gn_bwd_f16.hip",
            "mn_gn_fwd_bf16.hip", "mn_gn_bwd_bf16.hip", "mn_gn_fwd_f32.hip", "mn_gn_bwd_f32.hip",
-           "mn_gn_plan.hip", "mn_gemv.hip", "mn_kernels.hip", "mn_noalloc.hip", "mn_api.cpp"]
+           "mn_gn_plan.hip", "mn_gnl.hip", "mn_gemv.hip", "mn_kernels.hip", "mn_noalloc.hip", "mn_api.cpp"]
 ARCH = "gfx950"
 
 # Device-code flags. Packed fp32 instructions are disabled on purpose; no

@@ -550,6 +550,120 @@ mn_status groupnorm_backward(const void* X, const void* gamma, const float* mean
     return device_status(mn::launch_reduce(r, s));
 }
 
+// GroupNorm over channels-last X [N][L][C]: the launch limits (grid y
+// covers ceil(C / 256) channel blocks of the element-wise path, grid x the
+// N * J position chunks) on top of the channels-first shape bounds.
+bool gnl_shape_ok(int64_t N, int64_t L, int64_t C, int64_t G)
+{
+    if (!gn_shape_ok(N, C, L, G)) return false;
+    if ((C + 255) / 256 > 65535) return false;
+    return N * (int64_t)mn::gnl_chunks(N, L) <= (int64_t)UINT32_MAX && N * G <= (int64_t)UINT32_MAX;
+}
+
+size_t gnl_workspace_bytes(int64_t N, int64_t L, int64_t C, int64_t G)
+{
+    if (!gnl_shape_ok(N, L, C, G)) return 0;
+    return (size_t)mn::gnl_workspace_floats(N, L, C, G) * sizeof(float);
+}
+
+void gnl_common(mn::GnlArgs& a, int st, bool vec_ok, int& vec, int64_t N, int64_t L, int64_t C,
+                int64_t G, void* ws)
+{
+    a.N = N;
+    a.L = (int32_t)L;
+    a.C = (int32_t)C;
+    a.G = (int32_t)G;
+    a.Cg = (int32_t)(C / G);
+    a.Cp = (int32_t)gn_cp(C);
+    a.J = mn::gnl_chunks(N, L);
+    mn::gnl_geometry(st, vec_ok, a, vec);
+    // workspace: sa, sb [N][J][C]; then part_g, part_b [N][Cp]; ab [N * G][2]
+    float* w = static_cast<float*>(ws);
+    const int64_t njc = N * (int64_t)a.J * C;
+    a.sa = w;
+    a.sb = w + njc;
+    a.part_g = w + 2 * njc;
+    a.part_b = a.part_g + N * a.Cp;
+    a.ab = a.part_b + N * a.Cp;
+}
+
+mn_status groupnorm_nlc_forward(const void* X, const void* gamma, const void* beta, void* Y,
+                                float* mean, float* rstd, int64_t N, int64_t L, int64_t C,
+                                int64_t G, float eps, int st, int pdt, void* ws, size_t ws_bytes,
+                                void* stream)
+{
+    if (!X || !gamma || !beta || !Y || !mean || !rstd) return MN_ERR_NULL;
+    if (!dtype_ok(st) || !dtype_ok(pdt)) return MN_ERR_DTYPE;
+    if (!gnl_shape_ok(N, L, C, G)) return MN_ERR_SHAPE;
+    if (!eps_ok(eps)) return MN_ERR_EPS;
+    const size_t need = gnl_workspace_bytes(N, L, C, G);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
+    const size_t es = (size_t)mn::stor_bytes(st), ps = (size_t)mn::stor_bytes(pdt);
+    const size_t nx = (size_t)N * (size_t)C * (size_t)L;
+    const Span in[] = {span(X, nx * es), span(gamma, (size_t)C * ps), span(beta, (size_t)C * ps)};
+    const Span out[] = {span(Y, nx * es), span(mean, (size_t)(N * G) * 4),
+                        span(rstd, (size_t)(N * G) * 4), span(ws, need)};
+    if (!alias_free(in, out)) return MN_ERR_ALIAS;
+    mn::GnlArgs a{};
+    a.X = X;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.Y = Y;
+    a.mean = mean;
+    a.rstd = rstd;
+    a.pdt = pdt;
+    a.eps = eps;
+    int vec = 1;
+    gnl_common(a, st,
+               chunks_fit(st, C) && aligned16(X) && aligned16(Y) && aligned16(gamma) &&
+                   aligned16(beta),
+               vec, N, L, C, G, ws);
+    return device_status(mn::launch_gnl_fwd(st, vec, a, as_stream(stream)));
+}
+
+mn_status groupnorm_nlc_backward(const void* X, const void* gamma, const float* mean,
+                                 const float* rstd, const void* dY, void* dX, float* dgamma,
+                                 float* dbeta, int64_t N, int64_t L, int64_t C, int64_t G, int st,
+                                 int pdt, int ot, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!X || !gamma || !mean || !rstd || !dY || !dX || !dgamma || !dbeta) return MN_ERR_NULL;
+    if (!dtype_ok(st) || !dtype_ok(pdt) || !(ot == st || ot == MN_F32)) return MN_ERR_DTYPE;
+    if (!gnl_shape_ok(N, L, C, G)) return MN_ERR_SHAPE;
+    const size_t need = gnl_workspace_bytes(N, L, C, G);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MN_ERR_WORKSPACE;
+    const size_t es = (size_t)mn::stor_bytes(st), ps = (size_t)mn::stor_bytes(pdt);
+    const size_t os = (size_t)mn::stor_bytes(ot);
+    const size_t nx = (size_t)N * (size_t)C * (size_t)L;
+    const Span in[] = {span(X, nx * es), span(gamma, (size_t)C * ps),
+                       span(mean, (size_t)(N * G) * 4), span(rstd, (size_t)(N * G) * 4),
+                       span(dY, nx * es)};
+    const Span out[] = {span(dX, nx * os), span(dgamma, (size_t)C * 4),
+                        span(dbeta, (size_t)C * 4), span(ws, need)};
+    if (!alias_free(in, out)) return MN_ERR_ALIAS;
+    mn::GnlArgs a{};
+    a.X = X;
+    a.gamma = gamma;
+    a.dY = dY;
+    a.dX = dX;
+    a.mean = const_cast<float*>(mean);
+    a.rstd = const_cast<float*>(rstd);
+    a.pdt = pdt;
+    int vec = 1;
+    gnl_common(a, st,
+               chunks_fit(st, C) && aligned16(X) && aligned16(dY) && aligned16(dX) &&
+                   aligned16(gamma),
+               vec, N, L, C, G, ws);
+    hipStream_t s = as_stream(stream);
+    hipError_t e = mn::launch_gnl_bwd(st, ot, vec, a, s);
+    if (e != hipSuccess) return device_status(e);
+    // dgamma, dbeta: the N per-sample partial rows, added in fixed order
+    mn::ReduceArgs r{};
+    r.plane[0] = mn::ReducePlane{a.part_g, dgamma, N, (int32_t)C, a.Cp, 1};
+    r.plane[1] = mn::ReducePlane{a.part_b, dbeta, N, (int32_t)C, a.Cp, 1};
+    r.planes = 2;
+    return device_status(mn::launch_reduce(r, s));
+}
+
 mn_status backward(int kind, const BwdIn& b, const BwdOut& o, int64_t N, int64_t D,
                    const BwdTypes& t, void* ws, size_t ws_bytes, void* stream)
 {
@@ -867,6 +981,31 @@ mn_status mn_groupnorm_backward_ex(const void* X, const void* gamma, const float
 size_t mn_groupnorm_workspace_bytes(int64_t N, int64_t C, int64_t L, int64_t G)
 {
     return gn_workspace_bytes(N, C, L, G);
+}
+
+mn_status mn_groupnorm_nlc_forward_ex(const void* X, const void* gamma, const void* beta, void* Y,
+                                      float* mean, float* rstd, int64_t N, int64_t L, int64_t C,
+                                      int64_t G, float eps, mn_dtype act, mn_dtype param,
+                                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    return groupnorm_nlc_forward(X, gamma, beta, Y, mean, rstd, N, L, C, G, eps, act, param,
+                                 workspace, workspace_bytes, stream);
+}
+
+mn_status mn_groupnorm_nlc_backward_ex(const void* X, const void* gamma, const float* mean,
+                                       const float* rstd, const void* dY, void* dX,
+                                       float* dgamma, float* dbeta, int64_t N, int64_t L,
+                                       int64_t C, int64_t G, mn_dtype act, mn_dtype param,
+                                       mn_dtype dxt, void* workspace, size_t workspace_bytes,
+                                       void* stream)
+{
+    return groupnorm_nlc_backward(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, N, L, C, G, act,
+                                  param, dxt, workspace, workspace_bytes, stream);
+}
+
+size_t mn_groupnorm_nlc_workspace_bytes(int64_t N, int64_t L, int64_t C, int64_t G)
+{
+    return gnl_workspace_bytes(N, L, C, G);
 }
 
 // --- fused normalization + GEMV (inference) ---------------------------------

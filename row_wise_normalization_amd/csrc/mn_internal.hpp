@@ -198,6 +198,40 @@ int64_t gn_workspace_floats(int64_t N, int64_t C, int64_t L, int64_t G);
 hipError_t launch_gn_fwd(int st, const GnPlan& p, const GnArgs& a, hipStream_t s);
 hipError_t launch_gn_bwd(int st, int ot, const GnPlan& p, const GnArgs& a, hipStream_t s);
 
+// GroupNorm over channels-last X [N][L][C] (C contiguous per position): a
+// sums pass over position chunks, a per-(sample, group) merge, an apply
+// pass (mn_gnl.hip). The workspace is gnl_workspace_floats(N, L, C, G)
+// floats: sa, sb [N][J][C] chunk sums, then (backward) part_g, part_b
+// [N][Cp] and ab [N * G][2].
+struct GnlArgs {
+    const void* X;           // [N][L][C], storage type of the launch
+    const void* gamma;       // [C], type pdt
+    const void* beta;        // [C], type pdt (forward)
+    const void* dY;          // [N][L][C] (backward)
+    void* Y;                 // forward output
+    void* dX;                // backward output, type OT of the launch
+    float* mean;             // [N][G]
+    float* rstd;             // [N][G]
+    float* sa;               // [N][J][C] chunk sums (see mn_gnl.hip)
+    float* sb;               // [N][J][C]
+    float* part_g;           // backward: [N][Cp] per-sample sums of dY * xhat
+    float* part_b;           // backward: [N][Cp] per-sample sums of dY
+    float* ab;               // backward: [N * G][2] the group sums A, B
+    int64_t N;
+    int32_t L, C, G, Cg, Cp, pdt;
+    int32_t J;               // position chunks per sample
+    int32_t LC;              // positions per chunk (the last one may be shorter)
+    int32_t CK;              // chunks of VEC channels per position
+    float eps;
+};
+int32_t gnl_chunks(int64_t N, int64_t L);
+int64_t gnl_workspace_floats(int64_t N, int64_t L, int64_t C, int64_t G);
+// VEC (8 for 16-bit, 4 for binary32 storage, when C is a multiple of it and
+// every activation pointer is 16-byte aligned; else 1) and the derived CK, LC.
+void gnl_geometry(int st, bool vec_ok, GnlArgs& a, int& vec);
+hipError_t launch_gnl_fwd(int st, int vec, const GnlArgs& a, hipStream_t s);
+hipError_t launch_gnl_bwd(int st, int ot, int vec, const GnlArgs& a, hipStream_t s);
+
 // Fused normalization + GEMV (inference): Y [M][N] = Norm(X [M][K]) @ W [K][N].
 constexpr int kGemvMaxKB = 512;  // rows of W per tile (LDS slice of the product rows)
 constexpr int kGemvMaxM = 8;

@@ -73,6 +73,21 @@ int main(void)
                                    MN_F16, NULL),
            MN_ERR_SHAPE);
     if (mn_groupnorm_workspace_bytes(2, 64, 256, 8) == 0) ++failures;
+    /* channels-last GroupNorm: groups must divide C; the workspace is checked */
+    {
+        const size_t gw = mn_groupnorm_nlc_workspace_bytes(2, 256, 64, 8);
+        if (gw == 0 || gw % 16 != 0 || mn_groupnorm_nlc_workspace_bytes(2, 256, 64, 7) != 0)
+            ++failures;
+        EXPECT(mn_groupnorm_nlc_forward_ex(X, G, G + 4096, Y, r, r + 4096, 2, 256, 64, 7, 1e-5f,
+                                           MN_F16, MN_F16, ws, gw, NULL),
+               MN_ERR_SHAPE);
+        EXPECT(mn_groupnorm_nlc_forward_ex(X, G, G + 4096, Y, r, r + 4096, 2, 256, 64, 8, 1e-5f,
+                                           MN_F16, MN_F16, ws, gw - 16, NULL),
+               MN_ERR_WORKSPACE);
+        EXPECT(mn_groupnorm_nlc_backward_ex(X, G, r, r + 4096, dY, dY, dg, dg + 8192, 2, 256, 64,
+                                            8, MN_F16, MN_F16, MN_F16, ws, gw, NULL),
+               MN_ERR_ALIAS);
+    }
     if (mn_norm_gemv_workspace_bytes(4, 4096, 4096) == 0) ++failures;
     EXPECT(mn_fused_rmsnorm_gemv(X, G, dY, Y, 9, 4096, 4096, 1e-5f, ws,
                                  mn_norm_gemv_workspace_bytes(4, 4096, 4096), NULL),

@@ -213,6 +213,35 @@ def test_groupnorm_guards(N, C, L, G, off):
     verify(outs, ins, before, what)
 
 
+# Channels-last GroupNorm (X [N, L, C]): 16-byte chunks with several rows
+# per pass and with two channel blocks, the element-wise path (C not a
+# multiple of 8, and unaligned tensors), G = C, one position
+GNL_SHAPES = [(2, 320, 1000, 32, 0), (1, 2560, 40, 32, 0), (2, 300, 50, 10, 0),
+              (2, 64, 256, 8, 1), (2, 16, 128, 16, 0), (3, 8, 1, 1, 0)]
+
+
+@pytest.mark.parametrize("N,C,L,G,off", GNL_SHAPES)
+def test_groupnorm_nlc_guards(N, C, L, G, off):
+    what = f"groupnorm nlc {N}x{L}x{C} G={G}+{off}"
+    d = workloads.random_case("gn", N, C * L, 90 + L, x_loc=0.5, channels=C, groups=G)
+    d["X"] = np.ascontiguousarray(d["X"].reshape(N, C, L).swapaxes(1, 2))
+    d["dY"] = np.ascontiguousarray(d["dY"].reshape(N, C, L).swapaxes(1, 2))
+    ins = {k: upload(v, off) for k, v in d.items()}
+    outs = {"Y": Guarded((N, L, C), torch.float16, off),
+            "dX": Guarded((N, L, C), torch.float16, off),
+            "mean": Guarded((N, G), torch.float32), "rstd": Guarded((N, G), torch.float32),
+            "dgamma": Guarded((C,), torch.float32), "dbeta": Guarded((C,), torch.float32),
+            "ws": workspace(mn.groupnorm_nlc_workspace_bytes(N, L, C, G))}
+    before = snapshot(ins)
+    o = {k: v.t for k, v in outs.items()}
+    i = {k: v.t for k, v in ins.items()}
+    mn.mn_groupnorm_nlc_forward_ex(i["X"], i["gamma"], i["beta"], o["Y"], o["mean"], o["rstd"],
+                                   G, 1e-5, o["ws"])
+    mn.mn_groupnorm_nlc_backward_ex(i["X"], i["gamma"], o["mean"], o["rstd"], i["dY"], o["dX"],
+                                    o["dgamma"], o["dbeta"], G, o["ws"])
+    verify(outs, ins, before, what)
+
+
 @pytest.mark.parametrize("M,K,N,off", [(4, 4096, 12288, 0), (3, 1000, 1032, 0), (1, 4096, 14336, 0),
                                        (8, 512, 100, 1), (2, 64, 4099, 0)])
 @pytest.mark.parametrize("ln", [False, True])

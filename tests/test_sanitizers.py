@@ -6,7 +6,7 @@
 * A copy of the oracle with one planted heap overflow must be reported, so
   the gate above is known to be live.
 * The library's host code -- argument validation (mn_api.cpp), the launch
-  planners (mn_kernels.hip, mn_gn_plan.hip) and the no-allocation entry point
+  planners (mn_kernels.hip, mn_gn_plan.hip, mn_gnl.hip) and the no-allocation entry point
   (mn_noalloc.hip) -- is rebuilt with the sanitizers on the host side only
   (device code untouched) and linked with the other objects of the normal
   build; the plain-C caller tests/c/abi_check.c, built with the sanitizers,
@@ -89,7 +89,7 @@ def test_planted_heap_overflow_is_reported(tmp_path):
 HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
 # sources holding the host-side validation and planning
-HOST_SOURCES = ["mn_api.cpp", "mn_kernels.hip", "mn_gn_plan.hip", "mn_noalloc.hip"]
+HOST_SOURCES = ["mn_api.cpp", "mn_kernels.hip", "mn_gn_plan.hip", "mn_gnl.hip", "mn_noalloc.hip"]
 
 
 @pytest.mark.skipif(not os.path.exists(mn.LIB_PATH), reason="libmn_norm.so not built")

@@ -82,6 +82,8 @@ class Workload:
     Nout: int = 0          # "*_gemv": output columns (N rows of X are the batch M, D is K)
     channels: int = 0      # "gn": C (rows of X are samples of C * L values, D = C * L)
     groups: int = 0        # "gn": G
+    layout: str = "ncl"    # "gn": "ncl" channels-first, "nlc" channels-last (the
+                           # generated values are the channels-first ones, transposed)
 
     def outlier_channels(self) -> np.ndarray:
         if self.outlier_frac <= 0.0:
@@ -155,6 +157,10 @@ WORKLOADS: Dict[str, Workload] = {
                  channels=320, groups=32,
                  note="GroupNorm of a diffusion U-Net's first stage: 32 images, 320 channels "
                       "of 64 x 64 positions, 32 groups"),
+        Workload("gn_nlc_32x4096x320_g32", "gn", 32, 320 * 4096, 1e-5, _spec("gn", x=(0.5, 1.0)),
+                 channels=320, groups=32, layout="nlc",
+                 note="the same GroupNorm on channels-last activations (32 images of 64 x 64 "
+                      "positions, 320 channels each, 32 groups)"),
         Workload("rms_gemv_4x4096x12288", "rms_gemv", 4, 4096, 1e-5, _spec("rms_gemv"),
                  Nout=12288, note="decode step: RMSNorm of 4 tokens of width 4096 fused "
                                   "into the fused Q/K/V projection (3 x 4096 columns)"),
