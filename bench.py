@@ -101,6 +101,29 @@ def gemv_bytes(M: int, K: int, N: int, act: str = "f16", param: str = "f16", ln:
     return a * (M * K + K * N + M * N) + p * K * (2 if ln else 1)
 
 
+# Untimed steps before the counted warm-up: the GPU idles while the host
+# generates the inputs, and its clocks take longer to come back up than a
+# few steps last (20 timed steps after 5 warm-up steps measured 1-2 % below
+# 200 after 50 on one box).
+SETTLE_S = 0.2
+
+
+def settle(run_step, torch) -> int:
+    """Run untimed steps for at least SETTLE_S seconds; returns their count."""
+    t0, n = time.perf_counter(), 0
+    while True:
+        for _ in range(8):
+            run_step(n)
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= SETTLE_S:
+            return n
+
+
+WARMUP_NOTE = (f"the counted warm-up steps follow {SETTLE_S} s of untimed steps (clocks settle "
+               "after the host-side input generation)")
+
+
 def back_set(k: int, S: int) -> int:
     """Buffer set of step k's backward: the one forwarded S/2 steps ago."""
     return (k + S // 2) % S
@@ -575,6 +598,7 @@ def bench_gemv(args, w, torch, mn, act, param):
 
     Ks, Wu = args.steps, args.warmup
     nbytes = gemv_bytes(M, K, N, act, param, ln)
+    settle(lambda k: call(sets[k % S]), torch)
     for k in range(Wu):
         call(sets[k % S])
     torch.cuda.synchronize()
@@ -607,7 +631,7 @@ def bench_gemv(args, w, torch, mn, act, param):
     line = {
         "metric": f"achieved HBM GB/s (% of peak) for the fused norm + GEMV, "
                   f"{NORM_NAMES[w.kind]} {M}x{K} @ {K}x{N}",
-        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": Ks, "warmup": Wu,
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": Ks, "warmup": Wu, "warmup_note": WARMUP_NOTE,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "M": M, "K": K, "N": N, "eps": w.eps, "io_dtype": act,
@@ -727,6 +751,7 @@ def bench_other(args, w, torch, mn, act, param, dxt):
     fwd_b, bwd_b = alg_bytes(kind, N, D, act, param, act, dxt, B=w.B, C=C, G=G)
     for b in sets:
         fwd(b)
+    settle(lambda k: (fwd(sets[k % S]), bwd(sets[back_set(k, S)])), torch)
     for k in range(W):
         fwd(sets[k % S]); bwd(sets[back_set(k, S)])
     torch.cuda.synchronize()
@@ -751,7 +776,7 @@ def bench_other(args, w, torch, mn, act, param, dxt):
     line = {
         "metric": f"achieved HBM GB/s (% of peak) + rows/s for norm fwd+bwd, "
                   f"{NORM_NAMES[kind]} {'x'.join(str(v) for v in shp)}",
-        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W, "warmup_note": WARMUP_NOTE,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "N": N, "D": D, "eps": w.eps, "io_dtype": act,
@@ -929,6 +954,7 @@ def main():
     print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
     for b in sets:
         fwd(b)
+    settle(step, torch)
     for k in range(W):
         step(k)
     torch.cuda.synchronize()
@@ -1031,6 +1057,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
+        "warmup_note": WARMUP_NOTE,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
