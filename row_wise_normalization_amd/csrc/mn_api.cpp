@@ -158,7 +158,7 @@ mn_status forward(int kind, const FwdIn& f, int64_t N, int64_t D, float eps, int
     const bool vec_ok = chunks_fit(st, D) && aligned16(f.X) && aligned16(f.R) &&
                         aligned16(f.gamma) && aligned16(f.beta) && aligned16(f.Y) &&
                         aligned16(f.H) && aligned16(f.scale) && aligned16(f.shift);
-    const mn::FwdPlan plan = mn::plan_forward(kind, st, N, (int32_t)D, vec_ok, f.B);
+    const mn::FwdPlan plan = mn::plan_forward(kind, st, pdt, N, (int32_t)D, vec_ok, f.B);
     if (plan.grid > INT32_MAX) return MN_ERR_SHAPE;  // one workgroup per tile of rows
     mn::FwdArgs a;
     a.X = f.X;

@@ -131,7 +131,7 @@ int32_t mod_blocks_per_sample(int64_t B, int64_t N);
 int bwd_vector_partials(int kind);
 int32_t partial_stride(int32_t D);
 
-FwdPlan plan_forward(int kind, int st, int64_t N, int32_t D, bool vec_ok, int64_t B);
+FwdPlan plan_forward(int kind, int st, int pdt, int64_t N, int32_t D, bool vec_ok, int64_t B);
 BwdPlan plan_backward(int kind, int st, int64_t N, int32_t D, bool vec_ok, int64_t B = 1);
 
 hipError_t launch_forward(int kind, int st, const FwdPlan& p, const FwdArgs& a, hipStream_t s);

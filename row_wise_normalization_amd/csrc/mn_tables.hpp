@@ -42,6 +42,11 @@ namespace mn {
 // 1024 columns (7-13 %); it keeps the power-of-two rows at 3072 (exact fits
 // within 2 %). At 512 columns the backward takes two row groups of 64 lanes
 // per workgroup (9 %).
+// RMSNorm forward row 15 (max_d 0, so never chosen by width) is row 6 with
+// two rows per workgroup: the planner takes it instead of row 6 when 16-bit
+// activations come with binary32 gamma, whose chunks per lane are twice as
+// wide (bf16 with fp32 gamma: 50.0 -> 46.8 us at 16384 x 4096; fp16 gamma
+// measured 1 % slower with it).
 // Ids are unique within a kind; 8..10 are the element-wise variants (any D,
 // any alignment) shared by all kinds. Each row is instantiated for every
 // storage combination (binary32 activations: see st_vec / st_cpt below).
@@ -57,7 +62,8 @@ namespace mn {
     X(6, 256, 8, 2, 1, 256, 0, 3, 4096)      \
     X(12, 320, 8, 2, 1, 320, 0, 3, 5120)     \
     X(13, 384, 8, 2, 1, 384, 0, 3, 6144)     \
-    X(7, 256, 8, 4, 1, 256, 0, 3, 8192)
+    X(7, 256, 8, 4, 1, 256, 0, 3, 8192)      \
+    X(15, 256, 8, 2, 2, 256, 0, 3, 0)
 #define MN_FWD_LN(X)                         \
     X(0, 8, 8, 1, 4, 256, 0, 1, 64)          \
     X(1, 16, 8, 1, 2, 256, 0, 1, 128)        \
