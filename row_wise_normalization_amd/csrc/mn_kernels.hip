@@ -155,10 +155,10 @@ FwdPlan plan_forward(int kind, int st, int pdt, int64_t N, int32_t D, bool vec_o
 {
     FwdPlan p;
     p.v = vec_ok ? pick(kFwdVec[kind], D) : pick(kFwdGen, D);
-    // 16-bit activations with binary32 gamma: two rows per workgroup at 4096
-    // columns (the RMSNorm table's row 15)
-    if (kind == RMS && vec_ok && p.v.id == 6 && st != ST_F32 && pdt == ST_F32)
-        for (const VariantRow& r : kFwdVec[RMS])
+    // 16-bit activations with binary32 parameters: twice the rows per
+    // workgroup at 4096 columns (row 15 of the RMSNorm and LayerNorm tables)
+    if ((kind == RMS || kind == LN) && vec_ok && p.v.id == 6 && st != ST_F32 && pdt == ST_F32)
+        for (const VariantRow& r : kFwdVec[kind])
             if (r.v.id == 15) p.v = r.v;
     // one tile of RPB*U rows per workgroup; MOD: whole tiles per sample (B
     // samples of N / B rows)

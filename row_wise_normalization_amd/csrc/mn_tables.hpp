@@ -42,11 +42,12 @@ namespace mn {
 // 1024 columns (7-13 %); it keeps the power-of-two rows at 3072 (exact fits
 // within 2 %). At 512 columns the backward takes two row groups of 64 lanes
 // per workgroup (9 %).
-// RMSNorm forward row 15 (max_d 0, so never chosen by width) is row 6 with
-// two rows per workgroup: the planner takes it instead of row 6 when 16-bit
-// activations come with binary32 gamma, whose chunks per lane are twice as
-// wide (bf16 with fp32 gamma: 50.0 -> 46.8 us at 16384 x 4096; fp16 gamma
-// measured 1 % slower with it).
+// Forward row 15 of RMSNorm and of LayerNorm (max_d 0, so never chosen by
+// width) is row 6 with twice the rows per workgroup: the planner takes it
+// instead of row 6 when 16-bit activations come with binary32 parameters,
+// whose chunks per lane are twice as wide (at 16384 x 4096: RMSNorm 50.0 ->
+// 46.8 us, LayerNorm 53.6 -> 48.8 us; with 16-bit parameters both measured
+// 1-2 % slower with it).
 // Ids are unique within a kind; 8..10 are the element-wise variants (any D,
 // any alignment) shared by all kinds. Each row is instantiated for every
 // storage combination (binary32 activations: see st_vec / st_cpt below).
@@ -74,7 +75,8 @@ namespace mn {
     X(6, 256, 8, 2, 2, 256, 0, 3, 4096)      \
     X(12, 128, 8, 5, 1, 256, 0, 1, 5120)     \
     X(13, 256, 8, 3, 1, 256, 0, 1, 6144)     \
-    X(7, 256, 8, 4, 1, 256, 0, 1, 8192)
+    X(7, 256, 8, 4, 1, 256, 0, 1, 8192)      \
+    X(15, 256, 8, 2, 4, 256, 0, 3, 0)
 // The fused add (two inputs and two outputs per element) keeps rows of up to
 // 1024 lanes away from 4096 columns: at 8192 the 256-lane row measured 4 %
 // slower than the 1024-lane one.
