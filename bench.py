@@ -389,6 +389,11 @@ def pages_context(torch, mn):
 PROFILE_KERNELS = (("gnl_sum_kernel<0", "forward_sums"), ("gnl_stats_kernel", "forward_stats"),
                    ("gnl_apply_kernel<0", "forward_apply"), ("gnl_sum_kernel<1", "backward_sums"),
                    ("gnl_merge_kernel", "backward_merge"), ("gnl_apply_kernel<1", "backward_apply"),
+                   ("gn_chunk_stats_kernel", "forward_stats"),
+                   ("gn_stats_merge_kernel", "forward_merge"), ("gn_unit_y_kernel", "forward_apply"),
+                   ("gn_unit_sums_kernel", "backward_sums"),
+                   ("gn_unit_merge_kernel", "backward_merge"),
+                   ("gn_unit_dx_kernel", "backward_apply"),
                    ("gn_fwd_kernel", "forward"), ("gn_bwd_kernel", "backward_rows"),
                    ("fwd_kernel", "forward"), ("bwd_kernel", "backward_rows"),
                    ("reduce_kernel", "reduce_partials"), ("gemv_mfma_kernel", "gemv"),
@@ -478,6 +483,11 @@ def summarize_profile(workload: str, prefix: str, out_dir: str = None):
     else:
         fb, bb = alg_bytes(w.kind, w.N, w.D, B=w.B, C=w.channels, G=w.groups)
         alg = {"forward": fb, "backward_rows": bb, "reduce_partials": None}
+        if w.kind == "gn":
+            # slices larger than one workgroup holds: three kernels per
+            # direction, the algorithmic bytes again the direction's
+            alg.update({k: None for k in ("forward_stats", "forward_merge", "forward_apply",
+                                          "backward_sums", "backward_merge", "backward_apply")})
     # resources of each kernel from the per-dispatch trace (first dispatch)
     res = {}
     for p in trace_p:

@@ -526,10 +526,15 @@ struct GnUnit {
     int c0;              // first column of this lane's values in the row
     int L;
 
+    // REV: workgroups take the units from the last one back, so that a pass
+    // re-reading X first reads what the pass before it read last (and may
+    // still find it in the memory-side cache)
+    template <bool REV = false>
     __device__ __forceinline__ void map(const GnArgs& a, int gi, int l)
     {
         constexpr int RG = kGnUnitBlock / T;
-        const int64_t uu = (int64_t)blockIdx.x * RG + gi;
+        const int64_t bx = REV ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
+        const int64_t uu = bx * RG + gi;
         uok = uu < a.units;
         u = uok ? uu : a.units - 1;
         q = u / a.Kr;
@@ -561,10 +566,11 @@ __global__ void __launch_bounds__(kGnUnitBlock) gn_unit_sums_kernel(const GnArgs
     const void* xr = at<ST>(a.X, w.q * w.L);
     const void* dr = at<ST>(a.dY, w.q * w.L);
     HV x[IT], dy[IT];
+    // plain (temporal) loads: the dX pass reads X and dY again
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-        x[i] = gload<ST, VEC, 2>(xr, w.off(i));
-        dy[i] = gload<ST, VEC, 2>(dr, w.off(i));
+        x[i] = gload<ST, VEC, 0>(xr, w.off(i));
+        dy[i] = gload<ST, VEC, 0>(dr, w.off(i));
     }
     float v[2] = {0.0f, 0.0f};
 #pragma unroll
@@ -675,9 +681,10 @@ __global__ void __launch_bounds__(kGnUnitBlock) gn_chunk_stats_kernel(const GnAr
     const int cnt = (int)min((int64_t)a.FL, M - first);
     const void* xc = at<ST>(a.X, s * M + first);
     HV x[IT];
+    // plain (temporal) loads: the y pass reads X again, from the last unit back
 #pragma unroll
     for (int i = 0; i < IT; ++i)
-        x[i] = gload<ST, VEC, 2>(xc, (uint32_t)min((i * kGnUnitBlock + (int)threadIdx.x) * VEC,
+        x[i] = gload<ST, VEC, 0>(xc, (uint32_t)min((i * kGnUnitBlock + (int)threadIdx.x) * VEC,
                                                   cnt - VEC));
     float s1 = 0.0f;
 #pragma unroll
@@ -773,7 +780,7 @@ __global__ void __launch_bounds__(kGnUnitBlock) gn_unit_y_kernel(const GnArgs a)
     constexpr int IT = gn_unit_it<VEC>();
     const int gi = threadIdx.x / T, l = threadIdx.x % T;
     GnUnit<T, VEC> w;
-    w.map(a, gi, l);
+    w.template map<true>(a, gi, l);
     const void* xr = at<ST>(a.X, w.q * w.L);
     void* yr = at<ST>(a.Y, w.q * w.L);
     HV x[IT];

@@ -157,6 +157,10 @@ WORKLOADS: Dict[str, Workload] = {
                  channels=320, groups=32,
                  note="GroupNorm of a diffusion U-Net's first stage: 32 images, 320 channels "
                       "of 64 x 64 positions, 32 groups"),
+        Workload("gn_32x320x16384_g32", "gn", 32, 320 * 16384, 1e-5, _spec("gn", x=(0.5, 1.0)),
+                 channels=320, groups=32,
+                 note="the same GroupNorm at 128 x 128 positions: slices of 163,840 values, "
+                      "more than one workgroup holds in registers"),
         Workload("gn_nlc_32x4096x320_g32", "gn", 32, 320 * 4096, 1e-5, _spec("gn", x=(0.5, 1.0)),
                  channels=320, groups=32, layout="nlc",
                  note="the same GroupNorm on channels-last activations (32 images of 64 x 64 "
