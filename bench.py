@@ -138,9 +138,11 @@ def kernel_hash(kind: str = "rms", layout: str = "ncl") -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kernel: str):
+def measured_traffic(workload: str, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
-    only if it was taken on the current kernel source."""
+    only if it was taken on the current kernel source; `kernel` is a label,
+    or a tuple of labels whose bytes are added (a direction that runs as
+    several kernels)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -149,8 +151,27 @@ def measured_traffic(workload: str, kernel: str):
     w = workloads.WORKLOADS[workload]
     if t.get("kernel_source_sha256_16") != kernel_hash(w.kind, w.layout):
         return None
-    k = t.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    names = (kernel,) if isinstance(kernel, str) else tuple(kernel)
+    vals = [t.get("kernels", {}).get(n, {}).get("hbm_bytes_per_launch") for n in names]
+    return None if any(v is None for v in vals) else sum(vals)
+
+
+# GroupNorm backwards that run as three kernels and the column reduce (the
+# channels-last layout, and slices larger than one workgroup holds)
+GN_MULTI_BACKWARD = ("backward_sums", "backward_merge", "backward_apply", "reduce_partials")
+
+
+def backward_traffic_labels(workload: str):
+    """The profile labels whose HBM bytes make up one backward call's traffic
+    in bench_other's roofline: the row kernel, or every kernel of a
+    multi-kernel GroupNorm backward."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if os.path.exists(path):
+        with open(path) as f:
+            ks = json.load(f).get("kernels", {})
+        if "backward_rows" not in ks and all(k in ks for k in GN_MULTI_BACKWARD):
+            return GN_MULTI_BACKWARD
+    return "backward_rows"
 
 
 class HipEvent:
@@ -783,6 +804,7 @@ def bench_other(args, w, torch, mn, act, param, dxt):
         print(f"[bench] cpu baseline (oracle, {args.cpu_budget:.0f} s budget)", file=sys.stderr,
               flush=True)
         cpu = cpu_baseline(w, d, args.cpu_budget, (act, param, act, dxt))
+    tlab = backward_traffic_labels(w.name)
     line = {
         "metric": f"achieved HBM GB/s (% of peak) + rows/s for norm fwd+bwd, "
                   f"{NORM_NAMES[kind]} {'x'.join(str(v) for v in shp)}",
@@ -800,12 +822,14 @@ def bench_other(args, w, torch, mn, act, param, dxt):
         "kernels_ms": {"forward": round(fwd_ms, 5), "backward": round(bwd_ms, 5)},
         "kernel_gbs": {"forward": round(fwd_b / (fwd_ms * 1e-3) / 1e9, 1),
                        "backward": round(bwd_b / (bwd_ms * 1e-3) / 1e9, 1)},
-        "roofline": {"bound": "hbm", "kernel": "backward (row kernel + reduce)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("backward (row kernel + reduce)" if isinstance(tlab, str)
+                                else "backward (sums, merge and apply kernels + reduce)"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (measured_traffic(w.name, "backward_rows")
+                     "traffic": (measured_traffic(w.name, tlab)
                                  if (act, param, dxt) == ("f16",) * 3 else None),
-                     "traffic_kernel": "backward_rows"},
+                     "traffic_kernel": tlab if isinstance(tlab, str) else " + ".join(tlab)},
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
     }
