@@ -69,3 +69,22 @@ def test_summary_of_synthetic_counters(tmp_path):
     assert "| backward_rows |" in md
     # bench's roofline reads the measured traffic back while the source hash matches
     assert bench.measured_traffic.__code__.co_argcount == 2
+
+
+def test_multi_kernel_groupnorm_backward_traffic():
+    """A GroupNorm backward that runs as sums, merge and apply kernels plus the
+    column reduce (the channels-last layout, and slices beyond one workgroup)
+    reports the summed counter bytes of all four in its roofline; a one-kernel
+    backward reports its row kernel's."""
+    for wl in ("gn_nlc_32x4096x320_g32", "gn_32x320x16384_g32"):
+        labels = bench.backward_traffic_labels(wl)
+        assert labels == bench.GN_MULTI_BACKWARD, wl
+        with open(os.path.join(bench.ROOT, "profiles", f"traffic_{wl}.json")) as f:
+            ks = json.load(f)["kernels"]
+        want = sum(ks[k]["hbm_bytes_per_launch"] for k in labels)
+        assert bench.measured_traffic(wl, labels) == want
+        # X and dY are fetched twice, dX written once
+        w = workloads.WORKLOADS[wl]
+        assert want > 1.5 * bench.alg_bytes("gn", w.N, w.D, C=w.channels, G=w.groups)[1]
+    assert bench.backward_traffic_labels("gn_32x320x4096_g32") == "backward_rows"
+    assert bench.backward_traffic_labels("rms_16384x4096") == "backward_rows"
